@@ -1,0 +1,552 @@
+// api.hip -- host side of libgr: argument validation, workspace carving, launch
+// planning and the call sequences of the C ABI declared in include/gr.h.
+//
+// Every host-checkable condition is checked before the first launch, so a call
+// that fails enqueues nothing.  The library keeps no per-row state: continuous
+// batching (Leone, intro; tinyllm, Status: continuous admission, variable-length
+// batched decode) is just a different B, block table and ctx_lens on the next call.
+#include <atomic>
+#include <cstring>
+
+#include "gr_internal.h"
+#include "attn_internal.h"
+
+namespace gr {
+
+hipError_t launch_dequant(int kind, const void* blocks, int64_t n, float* out, hipStream_t st);
+hipError_t launch_gather(int kv_dtype, int D, const void* pool, int is_v, const int32_t* bt, const int32_t* ctx,
+                         int B, int max_blocks, int n_kv_heads, int max_ctx, float* out, hipStream_t st);
+
+namespace {
+
+thread_local int t_last_hip_error = 0;
+std::atomic<int> g_dev_state[64];  // 0 unknown, 1 gfx950, -1 other
+
+gr_status check_launch(hipError_t e) {
+  if (e != hipSuccess) {
+    t_last_hip_error = (int)e;
+    return GR_ERR_LAUNCH;
+  }
+  return GR_OK;
+}
+
+gr_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GR_ERR_DEVICE;
+  int st = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t pr;
+    if (hipGetDeviceProperties(&pr, dev) != hipSuccess) return GR_ERR_DEVICE;
+    st = std::strncmp(pr.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_dev_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? GR_OK : GR_ERR_DEVICE;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool wtype_ok(int t) { return t == GR_W_Q4_K || t == GR_W_Q6_K; }
+bool kv_ok(int t) { return t == GR_KV_F32 || t == GR_KV_F16 || t == GR_KV_Q8_0; }
+int kind_of(int wtype) { return wtype == GR_W_Q4_K ? kK32 : kK16; }
+
+// Carves a caller-provided workspace into 256-byte aligned regions; with base ==
+// nullptr it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <class T>
+  T* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+// Both actpack kinds of B rows x K columns.
+struct Pack2 {
+  PackOut k32, k16;
+  const PackOut& of(int wtype) const { return wtype == GR_W_Q4_K ? k32 : k16; }
+};
+Pack2 carve_pack2(Carver& c, int B, int K) {
+  Pack2 p;
+  p.k32.pack = c.take<u16>(actpack_frag_bytes(B, K, kK32));
+  p.k32.sums = c.take<float>(actpack_sum_bytes(B, K, kK32));
+  p.k32.kind = kK32;
+  p.k16.pack = c.take<u16>(actpack_frag_bytes(B, K, kK16));
+  p.k16.sums = c.take<float>(actpack_sum_bytes(B, K, kK16));
+  p.k16.kind = kK16;
+  return p;
+}
+
+// pack only the kinds some consumer needs
+PackOut need(const Pack2& p, bool need_k32) { return need_k32 ? p.k32 : PackOut{nullptr, nullptr, 0}; }
+PackOut need16(const Pack2& p, bool need_k16) { return need_k16 ? p.k16 : PackOut{nullptr, nullptr, 0}; }
+
+// GEMM over up to three matrices sharing K and the activation, grouped by type.
+hipError_t gemm_group(const void* const* w, const int* types, const int* rows, int nmat, int K, int B,
+                      const Pack2& xp, float* y, int ldy, hipStream_t st) {
+  int row_off = 0;
+  int i = 0;
+  hipError_t e = hipSuccess;
+  while (i < nmat) {
+    // maximal run of consecutive matrices of one type (outputs stay contiguous)
+    int j = i;
+    int run_rows[3];
+    const uint8_t* run_w[3];
+    int n = 0;
+    while (j < nmat && types[j] == types[i]) {
+      run_rows[n] = rows[j];
+      run_w[n] = (const uint8_t*)w[j];
+      ++n;
+      ++j;
+    }
+    const GemmPlan pl = plan_gemm(types[i], run_rows, n, K, B, 64);
+    const PackOut& pk = xp.of(types[i]);
+    e = launch_gemm(types[i], pl, run_w, run_rows, n, K, B, pk.pack, pk.sums, y + row_off, ldy, kStoreAtomic, st);
+    if (e != hipSuccess) return e;
+    for (int q = i; q < j; ++q) row_off += rows[q];
+    i = j;
+  }
+  return e;
+}
+
+struct LayerBufs {
+  Pack2 xp;   // residual stream, normalized (attention / FFN input)
+  Pack2 op;   // attention output (Wo input)
+  Pack2 ap;   // SwiGLU activation (down input)
+  float* qkv;
+  float* gu;
+  float *o_part, *m_part, *l_part;
+};
+
+LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan& ap) {
+  LayerBufs L;
+  const int qd = cfg->n_q_heads * cfg->head_dim, kvd = cfg->n_kv_heads * cfg->head_dim;
+  L.xp = carve_pack2(c, B, cfg->hidden);
+  L.op = carve_pack2(c, B, qd);
+  L.ap = carve_pack2(c, B, cfg->ffn);
+  L.qkv = c.take<float>((size_t)B * (qd + 2 * kvd) * 4);
+  L.gu = c.take<float>((size_t)B * 2 * cfg->ffn * 4);
+  const size_t units = (size_t)B * cfg->n_q_heads * ap.max_splits;
+  L.o_part = c.take<float>(units * cfg->head_dim * 4);
+  L.m_part = c.take<float>(units * 4);
+  L.l_part = c.take<float>(units * 4);
+  return L;
+}
+
+gr_status check_layer_cfg(const gr_layer_cfg* c) {
+  if (!c) return GR_ERR_NULL;
+  if (!kv_ok(c->kv_dtype) || (c->rope_style != GR_ROPE_NEOX && c->rope_style != GR_ROPE_NORM)) return GR_ERR_DTYPE;
+  if (c->page_size != GR_PAGE_SIZE) return GR_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return GR_ERR_SHAPE;
+  if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads) return GR_ERR_SHAPE;
+  if (c->n_q_heads / c->n_kv_heads > 8) return GR_ERR_SHAPE;
+  if (c->hidden <= 0 || c->hidden % 256 || c->ffn <= 0 || c->ffn % 256) return GR_ERR_SHAPE;
+  if ((c->n_q_heads * c->head_dim) % 256) return GR_ERR_SHAPE;
+  if (c->hidden > 65536 || c->ffn > 65536 || c->n_q_heads * c->head_dim > 65536) return GR_ERR_SHAPE;
+  if (!(c->rms_eps >= 0.0f) || !(c->rope_theta > 0.0)) return GR_ERR_SHAPE;
+  return GR_OK;
+}
+
+gr_status check_layer_w(const gr_layer_cfg* c, const gr_layer_weights* w) {
+  if (!w) return GR_ERR_NULL;
+  if (!w->attn_norm || !w->ffn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->w_gate || !w->w_up ||
+      !w->w_down)
+    return GR_ERR_NULL;
+  if (c->qk_norm && (!w->q_norm || !w->k_norm)) return GR_ERR_NULL;
+  const int ts[7] = {w->tq, w->tk, w->tv, w->to, w->tgate, w->tup, w->tdown};
+  for (int t : ts)
+    if (!wtype_ok(t)) return GR_ERR_DTYPE;
+  const void* ps[7] = {w->wq, w->wk, w->wv, w->wo, w->w_gate, w->w_up, w->w_down};
+  for (const void* p : ps)
+    if (!aligned(p, 16)) return GR_ERR_ALIGN;
+  if (!aligned(w->attn_norm, 4) || !aligned(w->ffn_norm, 4)) return GR_ERR_ALIGN;
+  return GR_OK;
+}
+
+AttnPlan layer_attn_plan(int B, const gr_layer_cfg* c, int max_ctx) {
+  return plan_attn(B, c->n_kv_heads, max_ctx + 1);
+}
+
+// The launch sequence of one decode layer (arguments already validated).
+gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pages, void* v_pages, float* x,
+                    const int32_t* bt, int max_blocks, const int32_t* ctx, int B, const AttnPlan& apl,
+                    const LayerBufs& L, hipStream_t st) {
+  const int H = c->hidden, D = c->head_dim, qd = c->n_q_heads * D, kvd = c->n_kv_heads * D, F = c->ffn;
+  hipError_t e;
+  // 1. attention RMSNorm -> actpack; zero the q/k/v accumulator
+  {
+    const bool k32 = w->tq == GR_W_Q4_K || w->tk == GR_W_Q4_K || w->tv == GR_W_Q4_K;
+    const bool k16 = w->tq == GR_W_Q6_K || w->tk == GR_W_Q6_K || w->tv == GR_W_Q6_K;
+    e = launch_pack_rows(x, H, B, H, w->attn_norm, c->rms_eps, need(L.xp, k32), need16(L.xp, k16), L.qkv,
+                         (size_t)B * (qd + 2 * kvd), st);
+    if (e != hipSuccess) return check_launch(e);
+  }
+  // 2. q, k, v = W xn
+  {
+    const void* ws[3] = {w->wq, w->wk, w->wv};
+    const int ts[3] = {w->tq, w->tk, w->tv};
+    const int rs[3] = {qd, kvd, kvd};
+    e = gemm_group(ws, ts, rs, 3, H, B, L.xp, L.qkv, qd + 2 * kvd, st);
+    if (e != hipSuccess) return check_launch(e);
+  }
+  // 3. QK-norm, RoPE, KV append and split attention; 4. merge + pack for Wo
+  AttnParams ap{};
+  ap.B = B;
+  ap.n_q_heads = c->n_q_heads;
+  ap.n_kv_heads = c->n_kv_heads;
+  ap.head_dim = D;
+  ap.max_blocks = max_blocks;
+  ap.pages_per_split = apl.pages_per_split;
+  ap.max_splits = apl.max_splits;
+  ap.scale = 1.0f / sqrtf((float)D);
+  ap.block_table = bt;
+  ap.ctx_lens = ctx;
+  ap.k_pages = k_pages;
+  ap.v_pages = v_pages;
+  ap.qkv = L.qkv;
+  ap.qkv_ld = qd + 2 * kvd;
+  ap.qkv_splits = 1;
+  ap.q_dim = qd;
+  ap.kv_dim = kvd;
+  ap.q_norm = c->qk_norm ? w->q_norm : nullptr;
+  ap.k_norm = c->qk_norm ? w->k_norm : nullptr;
+  ap.eps = c->rms_eps;
+  ap.rope_theta = c->rope_theta;
+  ap.rope_style = c->rope_style;
+  ap.o_part = L.o_part;
+  ap.m_part = L.m_part;
+  ap.l_part = L.l_part;
+  e = launch_attn_split(c->kv_dtype, true, ap, st);
+  if (e != hipSuccess) return check_launch(e);
+  {
+    const PackOut& op = L.op.of(w->to);
+    e = launch_attn_merge(ap, nullptr, op.pack, op.sums, op.kind, op.kind == kK32 ? qd / 32 : qd / 16, 1, st);
+    if (e != hipSuccess) return check_launch(e);
+  }
+  // 5. x += Wo o
+  {
+    const void* ws[1] = {w->wo};
+    const int ts[1] = {w->to};
+    const int rs[1] = {H};
+    e = gemm_group(ws, ts, rs, 1, qd, B, L.op, x, H, st);
+    if (e != hipSuccess) return check_launch(e);
+  }
+  // 6. FFN RMSNorm -> actpack; zero the gate/up accumulator
+  {
+    const bool k32 = w->tgate == GR_W_Q4_K || w->tup == GR_W_Q4_K;
+    const bool k16 = w->tgate == GR_W_Q6_K || w->tup == GR_W_Q6_K;
+    e = launch_pack_rows(x, H, B, H, w->ffn_norm, c->rms_eps, need(L.xp, k32), need16(L.xp, k16), L.gu,
+                         (size_t)B * 2 * F, st);
+    if (e != hipSuccess) return check_launch(e);
+  }
+  // 7. gate, up
+  {
+    const void* ws[2] = {w->w_gate, w->w_up};
+    const int ts[2] = {w->tgate, w->tup};
+    const int rs[2] = {F, F};
+    e = gemm_group(ws, ts, rs, 2, H, B, L.xp, L.gu, 2 * F, st);
+    if (e != hipSuccess) return check_launch(e);
+  }
+  // 8. a = silu(gate) * up -> actpack
+  e = launch_swiglu_pack(L.gu, B, F, L.ap.of(w->tdown), st);
+  if (e != hipSuccess) return check_launch(e);
+  // 9. x += W_down a
+  {
+    const void* ws[1] = {w->w_down};
+    const int ts[1] = {w->tdown};
+    const int rs[1] = {H};
+    e = gemm_group(ws, ts, rs, 1, F, B, L.ap, x, H, st);
+    if (e != hipSuccess) return check_launch(e);
+  }
+  return GR_OK;
+}
+
+gr_status run_head(const float* x, const float* norm, float eps, const void* w, int wtype, float* logits, int B,
+                   int H, int vocab, const Pack2& xp, hipStream_t st) {
+  const PackOut& pk = xp.of(wtype);
+  hipError_t e = launch_pack_rows(x, H, B, H, norm, eps, pk, PackOut{nullptr, nullptr, 0}, logits,
+                                  (size_t)B * vocab, st);
+  if (e != hipSuccess) return check_launch(e);
+  const void* ws[1] = {w};
+  const int ts[1] = {wtype};
+  const int rs[1] = {vocab};
+  e = gemm_group(ws, ts, rs, 1, H, B, xp, logits, vocab, st);
+  return check_launch(e);
+}
+
+}  // namespace
+}  // namespace gr
+
+using namespace gr;
+
+extern "C" {
+
+int gr_abi_version(void) { return GR_ABI_VERSION; }
+
+const char* gr_status_str(int s) {
+  switch (s) {
+    case GR_OK: return "ok";
+    case GR_ERR_NULL: return "required pointer is NULL";
+    case GR_ERR_SHAPE: return "size or shape out of the supported range";
+    case GR_ERR_DTYPE: return "unknown weight type, KV dtype or rope style";
+    case GR_ERR_ALIGN: return "pointer lacks the required alignment";
+    case GR_ERR_WORKSPACE: return "workspace missing or too small";
+    case GR_ERR_CAPACITY: return "max_ctx + 1 tokens exceed the block table's pages";
+    case GR_ERR_DEVICE: return "current device is not gfx950";
+    case GR_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int gr_last_hip_error(void) { return t_last_hip_error; }
+
+int64_t gr_kv_head_bytes(int kv_dtype, int head_dim) {
+  if (head_dim <= 0 || head_dim % 32) return -1;
+  if (kv_dtype == GR_KV_F32) return (int64_t)GR_PAGE_SIZE * head_dim * 4;
+  if (kv_dtype == GR_KV_F16) return (int64_t)GR_PAGE_SIZE * head_dim * 2;
+  if (kv_dtype == GR_KV_Q8_0) return (int64_t)GR_PAGE_SIZE * head_dim + GR_PAGE_SIZE * (head_dim / 32) * 2;
+  return -1;
+}
+
+// ------------------------------------------------------------------ dequant
+static gr_status dequant_common(int kind, const void* blocks, int64_t n, float* out, void* stream) {
+  if (n < 0) return GR_ERR_SHAPE;
+  if (n == 0) return GR_OK;
+  if (!blocks || !out) return GR_ERR_NULL;
+  if (!aligned(blocks, kind == 12 ? 16 : 2) || !aligned(out, 4)) return GR_ERR_ALIGN;
+  gr_status s = check_device();
+  if (s != GR_OK) return s;
+  return check_launch(launch_dequant(kind, blocks, n, out, (hipStream_t)stream));
+}
+gr_status gr_q4k_dequant(const void* b, int64_t n, float* out, void* s) { return dequant_common(12, b, n, out, s); }
+gr_status gr_q6k_dequant(const void* b, int64_t n, float* out, void* s) { return dequant_common(14, b, n, out, s); }
+gr_status gr_q8_0_dequant(const void* b, int64_t n, float* out, void* s) { return dequant_common(8, b, n, out, s); }
+
+// --------------------------------------------------------------------- GEMM
+size_t gr_gemm_workspace_size(int B, int N, int K) {
+  if (B <= 0 || K <= 0) return 0;
+  (void)N;
+  Carver c(nullptr);
+  carve_pack2(c, B, K);
+  return c.off + 256;
+}
+
+static gr_status gemm_api(int wtype, const void* w, const float* x, float* y, int B, int N, int K, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (B < 0 || N < 0 || K < 0) return GR_ERR_SHAPE;
+  if (B == 0 || N == 0) return GR_OK;
+  if (!w || !x || !y) return GR_ERR_NULL;
+  if (B > 64 || K == 0 || K % 256 || K > 65536) return GR_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return GR_ERR_ALIGN;
+  if (!ws || ws_bytes < gr_gemm_workspace_size(B, N, K) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
+  gr_status s = check_device();
+  if (s != GR_OK) return s;
+  Carver c(ws);
+  const Pack2 xp = carve_pack2(c, B, K);
+  hipStream_t st = (hipStream_t)stream;
+  const PackOut& pk = xp.of(wtype);
+  hipError_t e = launch_pack_rows(x, K, B, K, nullptr, 0.f, pk, PackOut{nullptr, nullptr, 0}, y, (size_t)B * N, st);
+  if (e != hipSuccess) return check_launch(e);
+  const void* ws1[1] = {w};
+  const int ts[1] = {wtype};
+  const int rs[1] = {N};
+  return check_launch(gemm_group(ws1, ts, rs, 1, K, B, xp, y, N, st));
+}
+
+gr_status gr_q4k_gemm(const void* w, const float* x, float* y, int B, int N, int K, void* ws, size_t wsb, void* s) {
+  return gemm_api(GR_W_Q4_K, w, x, y, B, N, K, ws, wsb, s);
+}
+gr_status gr_q6k_gemm(const void* w, const float* x, float* y, int B, int N, int K, void* ws, size_t wsb, void* s) {
+  return gemm_api(GR_W_Q6_K, w, x, y, B, N, K, ws, wsb, s);
+}
+
+// ---------------------------------------------------------------- attention
+static gr_status check_meta(const gr_attn_meta* m) {
+  if (!m) return GR_ERR_NULL;
+  if (!kv_ok(m->kv_dtype)) return GR_ERR_DTYPE;
+  if (m->page_size != GR_PAGE_SIZE) return GR_ERR_SHAPE;
+  if (m->head_dim != 64 && m->head_dim != 128) return GR_ERR_SHAPE;
+  if (m->n_q_heads <= 0 || m->n_kv_heads <= 0 || m->n_q_heads % m->n_kv_heads) return GR_ERR_SHAPE;
+  if (m->n_q_heads / m->n_kv_heads > 8) return GR_ERR_SHAPE;
+  if (m->num_pages <= 0 || m->max_blocks_per_row <= 0 || m->max_ctx <= 0) return GR_ERR_SHAPE;
+  if ((int64_t)m->max_ctx > (int64_t)GR_PAGE_SIZE * m->max_blocks_per_row) return GR_ERR_CAPACITY;
+  return GR_OK;
+}
+
+size_t gr_paged_decode_attn_workspace_size(const gr_attn_meta* m, int B) {
+  if (check_meta(m) != GR_OK || B <= 0) return 0;
+  const AttnPlan pl = plan_attn(B, m->n_kv_heads, m->max_ctx);
+  Carver c(nullptr);
+  const size_t units = (size_t)B * m->n_q_heads * pl.max_splits;
+  c.take<float>(units * m->head_dim * 4);
+  c.take<float>(units * 4);
+  c.take<float>(units * 4);
+  return c.off + 256;
+}
+
+gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                               const int32_t* ctx_lens, float* out, int B, const gr_attn_meta* m, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (B < 0) return GR_ERR_SHAPE;
+  gr_status s = check_meta(m);
+  if (s != GR_OK) return s;
+  if (B == 0) return GR_OK;
+  if (B > 4096) return GR_ERR_SHAPE;
+  if (!q || !k_pages || !v_pages || !block_table || !ctx_lens || !out) return GR_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 4) ||
+      !aligned(block_table, 4) || !aligned(ctx_lens, 4))
+    return GR_ERR_ALIGN;
+  if (!ws || ws_bytes < gr_paged_decode_attn_workspace_size(m, B) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
+  s = check_device();
+  if (s != GR_OK) return s;
+  const AttnPlan pl = plan_attn(B, m->n_kv_heads, m->max_ctx);
+  Carver c(ws);
+  const size_t units = (size_t)B * m->n_q_heads * pl.max_splits;
+  AttnParams ap{};
+  ap.o_part = c.take<float>(units * m->head_dim * 4);
+  ap.m_part = c.take<float>(units * 4);
+  ap.l_part = c.take<float>(units * 4);
+  ap.B = B;
+  ap.n_q_heads = m->n_q_heads;
+  ap.n_kv_heads = m->n_kv_heads;
+  ap.head_dim = m->head_dim;
+  ap.max_blocks = m->max_blocks_per_row;
+  ap.pages_per_split = pl.pages_per_split;
+  ap.max_splits = pl.max_splits;
+  ap.scale = m->scale;
+  ap.block_table = block_table;
+  ap.ctx_lens = ctx_lens;
+  ap.k_pages = k_pages;
+  ap.v_pages = v_pages;
+  ap.q = q;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_attn_split(m->kv_dtype, false, ap, st);
+  if (e != hipSuccess) return check_launch(e);
+  return check_launch(launch_attn_merge(ap, out, nullptr, nullptr, 0, 0, 0, st));
+}
+
+gr_status gr_paged_gather_kv(const void* pages, int is_v, const int32_t* block_table, const int32_t* ctx_lens, int B,
+                             const gr_attn_meta* m, float* out, void* stream) {
+  if (B < 0) return GR_ERR_SHAPE;
+  gr_status s = check_meta(m);
+  if (s != GR_OK) return s;
+  if (B == 0) return GR_OK;
+  if (!pages || !block_table || !ctx_lens || !out) return GR_ERR_NULL;
+  if (!aligned(pages, 16) || !aligned(out, 4)) return GR_ERR_ALIGN;
+  if (B > 65535 || m->n_kv_heads > 65535) return GR_ERR_SHAPE;
+  s = check_device();
+  if (s != GR_OK) return s;
+  return check_launch(launch_gather(m->kv_dtype, m->head_dim, pages, is_v ? 1 : 0, block_table, ctx_lens, B,
+                                    m->max_blocks_per_row, m->n_kv_heads, m->max_ctx, out, (hipStream_t)stream));
+}
+
+// --------------------------------------------------------------- decode layer
+size_t gr_decode_layer_workspace_size(const gr_layer_cfg* c, int B, int max_ctx) {
+  if (check_layer_cfg(c) != GR_OK || B <= 0 || max_ctx < 0) return 0;
+  Carver cv(nullptr);
+  carve_layer(cv, c, B, layer_attn_plan(B, c, max_ctx));
+  return cv.off + 256;
+}
+
+static gr_status check_layer_call(const gr_layer_cfg* c, const gr_layer_weights* w, const void* k_pages,
+                                  const void* v_pages, int num_pages, const float* x, const int32_t* bt,
+                                  int max_blocks, const int32_t* ctx, int max_ctx, int B) {
+  gr_status s = check_layer_cfg(c);
+  if (s != GR_OK) return s;
+  s = check_layer_w(c, w);
+  if (s != GR_OK) return s;
+  if (B < 0 || B > 64) return GR_ERR_SHAPE;
+  if (!k_pages || !v_pages || !x || !bt || !ctx) return GR_ERR_NULL;
+  if (num_pages <= 0 || max_blocks <= 0 || max_ctx < 0) return GR_ERR_SHAPE;
+  if ((int64_t)max_ctx + 1 > (int64_t)GR_PAGE_SIZE * max_blocks) return GR_ERR_CAPACITY;
+  if (!aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(x, 16) || !aligned(bt, 4) || !aligned(ctx, 4))
+    return GR_ERR_ALIGN;
+  return GR_OK;
+}
+
+gr_status gr_decode_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pages, void* v_pages,
+                          int num_pages, float* x, const int32_t* bt, int max_blocks, const int32_t* ctx, int max_ctx,
+                          int B, void* ws, size_t ws_bytes, void* stream) {
+  gr_status s = check_layer_call(c, w, k_pages, v_pages, num_pages, x, bt, max_blocks, ctx, max_ctx, B);
+  if (s != GR_OK) return s;
+  if (B == 0) return GR_OK;
+  if (!ws || ws_bytes < gr_decode_layer_workspace_size(c, B, max_ctx) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
+  s = check_device();
+  if (s != GR_OK) return s;
+  const AttnPlan apl = layer_attn_plan(B, c, max_ctx);
+  Carver cv(ws);
+  const LayerBufs L = carve_layer(cv, c, B, apl);
+  return run_layer(c, w, k_pages, v_pages, x, bt, max_blocks, ctx, B, apl, L, (hipStream_t)stream);
+}
+
+size_t gr_output_head_workspace_size(int B, int hidden, int vocab) {
+  if (B <= 0 || hidden <= 0) return 0;
+  (void)vocab;
+  Carver c(nullptr);
+  carve_pack2(c, B, hidden);
+  return c.off + 256;
+}
+
+gr_status gr_output_head(const float* x, const float* norm, float eps, const void* w, int wtype, float* logits, int B,
+                         int hidden, int vocab, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || hidden < 0 || vocab < 0) return GR_ERR_SHAPE;
+  if (!wtype_ok(wtype)) return GR_ERR_DTYPE;
+  if (B == 0 || vocab == 0) return GR_OK;
+  if (!x || !norm || !w || !logits) return GR_ERR_NULL;
+  if (B > 64 || hidden % 256 || hidden > 65536) return GR_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(logits, 4) || !aligned(norm, 4)) return GR_ERR_ALIGN;
+  if (!ws || ws_bytes < gr_output_head_workspace_size(B, hidden, vocab) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
+  gr_status s = check_device();
+  if (s != GR_OK) return s;
+  Carver c(ws);
+  const Pack2 xp = carve_pack2(c, B, hidden);
+  return run_head(x, norm, eps, w, wtype, logits, B, hidden, vocab, xp, (hipStream_t)stream);
+}
+
+size_t gr_decode_stack_workspace_size(const gr_layer_cfg* c, int B, int max_ctx, int vocab) {
+  (void)vocab;
+  return gr_decode_layer_workspace_size(c, B, max_ctx);
+}
+
+gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers,
+                          void* const* k_pages, void* const* v_pages, int num_pages, float* x, const int32_t* bt,
+                          int max_blocks, const int32_t* ctx, int max_ctx, int B, const float* head_norm,
+                          const void* head_w, int head_wtype, int vocab, float* logits, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (n_layers < 0) return GR_ERR_SHAPE;
+  if (n_layers > 0 && (!weights || !k_pages || !v_pages)) return GR_ERR_NULL;
+  for (int l = 0; l < n_layers; ++l) {
+    gr_status s = check_layer_call(c, &weights[l], k_pages[l], v_pages[l], num_pages, x, bt, max_blocks, ctx,
+                                   max_ctx, B);
+    if (s != GR_OK) return s;
+  }
+  if (head_w) {
+    if (!wtype_ok(head_wtype)) return GR_ERR_DTYPE;
+    if (!head_norm || !logits) return GR_ERR_NULL;
+    if (vocab <= 0) return GR_ERR_SHAPE;
+    if (!aligned(head_w, 16) || !aligned(head_norm, 4) || !aligned(logits, 4)) return GR_ERR_ALIGN;
+  }
+  if (n_layers == 0) {
+    gr_status s = check_layer_cfg(c);
+    if (s != GR_OK) return s;
+  }
+  if (B == 0) return GR_OK;
+  if (!ws || ws_bytes < gr_decode_stack_workspace_size(c, B, max_ctx, vocab) || !aligned(ws, 256))
+    return GR_ERR_WORKSPACE;
+  gr_status s = check_device();
+  if (s != GR_OK) return s;
+  const AttnPlan apl = layer_attn_plan(B, c, max_ctx);
+  Carver cv(ws);
+  const LayerBufs L = carve_layer(cv, c, B, apl);
+  hipStream_t st = (hipStream_t)stream;
+  for (int l = 0; l < n_layers; ++l) {
+    s = run_layer(c, &weights[l], k_pages[l], v_pages[l], x, bt, max_blocks, ctx, B, apl, L, st);
+    if (s != GR_OK) return s;
+  }
+  if (head_w) return run_head(x, head_norm, c->rms_eps, head_w, head_wtype, logits, B, c->hidden, vocab, L.xp, st);
+  return GR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,443 @@
+// attn.hip -- split-context paged GQA decode attention on gfx950.
+//
+// Each row keeps its own attention over its own pages (Leone, intro; tinyllm, Status:
+// a physical page pool addressed through a logical block table per sequence).
+// Instead of gathering pages into contiguous K/V (the reference path tinyllm
+// describes under Known limitations), every wave walks the block table directly.
+//
+// Work unit: one wave per (row b, KV head g, split s); split s covers a page-aligned
+// range of the row's context.  Per page (16 tokens):
+//   scores  S[m][t] = sum_d Q[m][d] K[t][d]  -- v_mfma_f32_16x16x32_f16, A = the R query
+//           heads of group g as f16 hi/lo rows (m = 2h + part), B = the page's K
+//   softmax online in the log2 domain (q is pre-scaled by scale*log2 e); running max
+//           and sum over the 16 tokens by lane shuffles inside each 16-lane group
+//   output  O[m][d] += P[m][t] V[t][d]        -- v_mfma_f32_16x16x16_f16, A = P as f16
+//           hi/lo rows (transposed through LDS), B = the page's V (dim-major pages)
+// q8_0 pages are expanded to exact f16 integers in registers; their per-token,
+// per-32-element scales multiply the K scores (K) or fold into P (V).  f32 pages are
+// split into f16 hi/lo operands.  Partials (unnormalized O, running max m, sum l)
+// are merged across splits by log-sum-exp in attn_merge_pack_kernel.
+//
+// The fused variant (used by the decode layer) also sums the QKV GEMM's split-K
+// partials, applies QK-RMSNorm and RoPE (angles in fp64), stores the new token's K/V
+// at slot ctx%16 of page block_table[b][ctx/16] in the pool's format, and
+// substitutes those stored values for the slot's contents when it reads that page.
+#include "gr_internal.h"
+#include "attn_internal.h"
+#include "kvpage.h"
+
+namespace gr {
+
+// ------------------------------------------------------------- setup helpers
+
+// pair index i (0..D/2) of lane: rope pairs (i, i+D/2) [neox] or (2i, 2i+1) [norm]
+GR_DEV void pair_dims(int i, int D, int style, int& da, int& db) {
+  if (style == 0) {
+    da = i;
+    db = i + D / 2;
+  } else {
+    da = 2 * i;
+    db = 2 * i + 1;
+  }
+}
+
+// Per-head vector in pair layout (lane i < D/2 holds dims da, db): optional RMSNorm
+// over the head, then RoPE at position pos with angles in fp64.
+GR_DEV void norm_rope(float& a, float& b, bool active, const float* gain, float eps, int D, int da, int db,
+                      double cs, double sn) {
+  if (gain) {
+    float ss = active ? a * a + b * b : 0.0f;
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+    if (active) {
+      a = a * r * gain[da];
+      b = b * r * gain[db];
+    }
+  }
+  if (active) {
+    const double ad = a, bd = b;
+    a = (float)(ad * cs - bd * sn);
+    b = (float)(ad * sn + bd * cs);
+  }
+}
+
+template <int KVDT>
+GR_DEV int kv_head_bytes_t(int D) {
+  if constexpr (KVDT == KV_F32_T) return kPage * D * 4;
+  if constexpr (KVDT == KV_F16_T) return kPage * D * 2;
+  return kPage * D + kPage * (D / 32) * 2;
+}
+
+// Store a token's vector (LDS f32 [D]) in pool format: into the LDS staging row
+// `stage` (format of patch_page) and, if `dst_head` is set, into the pool head block.
+template <int KVDT>
+GR_DEV void store_token(const float* vals, uint8_t* stage, uint8_t* dst_head, bool is_v, int D, int slot, int lane) {
+  const int epl = D / 64;  // elements per lane
+  if constexpr (KVDT == KV_Q8_T) {
+    // lane holds elements epl*lane + e; 32-element blocks span 32/epl lanes
+    float x[2] = {0.f, 0.f};
+    float amax = 0.f;
+    for (int e = 0; e < epl; ++e) {
+      x[e] = vals[epl * lane + e];
+      amax = fmaxf(amax, fabsf(x[e]));
+    }
+    const int span = 32 / epl;
+    for (int o = 1; o < span; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float dsc = amax / 127.0f;
+    for (int e = 0; e < epl; ++e) {
+      const int d = epl * lane + e;
+      float qf = dsc != 0.0f ? roundf(x[e] / dsc) : 0.0f;
+      qf = fminf(127.0f, fmaxf(-127.0f, qf));
+      const uint8_t c = (uint8_t)(int8_t)qf;
+      stage[d] = c;
+      if (dst_head) dst_head[is_v ? d * kPage + slot : slot * D + d] = c;
+    }
+    const int blk = (epl * lane) / 32;
+    if (((epl * lane) & 31) == 0) {
+      const u16 h = f2h(dsc);
+      ((u16*)(stage + D))[blk] = h;
+      if (dst_head) ((u16*)(dst_head + kPage * D))[slot * (D / 32) + blk] = h;
+    }
+  } else {
+    for (int e = 0; e < epl; ++e) {
+      const int d = epl * lane + e;
+      const int idx = is_v ? d * kPage + slot : slot * D + d;
+      if constexpr (KVDT == KV_F16_T) {
+        const u16 h = f2h(vals[d]);
+        ((u16*)stage)[d] = h;
+        if (dst_head) ((u16*)dst_head)[idx] = h;
+      } else {
+        const float f = vals[d];
+        ((float*)stage)[d] = f;
+        if (dst_head) ((float*)dst_head)[idx] = f;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------- the kernel
+
+template <int KVDT, int D, bool FUSED>
+__global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
+  constexpr int NS = D / 32;  // QK slices
+  constexpr int NT = D / 16;  // PV tiles
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int split = unit % p.max_splits;
+  const int bg = unit / p.max_splits;
+  const int g = bg % p.n_kv_heads;
+  const int b = bg / p.n_kv_heads;
+  const int R = p.n_q_heads / p.n_kv_heads;
+
+  const int ctx = p.ctx_lens[b];
+  const int n_tok = FUSED ? ctx + 1 : ctx;
+  const int n_pages = (n_tok + kPage - 1) / kPage;
+  const int pg0 = split * p.pages_per_split;
+  if (pg0 >= n_pages) return;
+  const int pg1 = min(n_pages, pg0 + p.pages_per_split);
+  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
+
+  __shared__ float s_vec[10][128];                  // q heads (and k, v) in linear layout
+  __shared__ __attribute__((aligned(16))) u16 s_q[NS][64][8];   // A fragments of Q
+  __shared__ __attribute__((aligned(16))) u16 s_p[KVDT == KV_Q8_T ? D / 32 : 1][16][16];  // P transpose
+  __shared__ __attribute__((aligned(16))) uint8_t s_knew[D * 4 + 64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vnew[D * 4 + 64];
+
+  const int n = lane & 15, kg = lane >> 4;
+  const int HB = kv_head_bytes_t<KVDT>(D);
+  const size_t page_bytes = (size_t)HB * p.n_kv_heads;
+  const int new_page = ctx / kPage, new_slot = ctx % kPage;
+  const bool owner = FUSED && new_page >= pg0 && new_page < pg1;
+
+  // ---- query (and, for the owner, the new token's k and v) ---------------------
+  {
+    const bool act = lane < D / 2;
+    int da = 0, db = 0;
+    pair_dims(act ? lane : 0, D, p.rope_style, da, db);
+    double cs = 1.0, sn = 0.0;
+    if (FUSED) {
+      const double inv = pow(p.rope_theta, -2.0 * (double)(act ? lane : 0) / (double)D);
+      sincos((double)ctx * inv, &sn, &cs);
+    }
+    const int nh = R + (owner ? 2 : 0);
+    for (int hh = 0; hh < nh; ++hh) {
+      // hh < R: query head g*R + hh; hh == R: k of head g; hh == R+1: v of head g
+      float a = 0.f, bb = 0.f;
+      if (act) {
+        if (FUSED) {
+          const int ld = p.qkv_ld;
+          const int off = hh < R ? (g * R + hh) * D : hh == R ? p.q_dim + g * D : p.q_dim + p.kv_dim + g * D;
+          for (int s = 0; s < p.qkv_splits; ++s) {
+            const float* src = p.qkv + ((size_t)s * p.B + b) * ld + off;
+            a += src[da];
+            bb += src[db];
+          }
+        } else {
+          const float* src = p.q + ((size_t)b * p.n_q_heads + g * R + hh) * D;
+          a = src[da];
+          bb = src[db];
+        }
+      }
+      if (FUSED && hh <= R) norm_rope(a, bb, act, hh < R ? p.q_norm : p.k_norm, p.eps, D, da, db, cs, sn);
+      if (act) {
+        s_vec[hh][da] = a;
+        s_vec[hh][db] = bb;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Q fragments: row m = 2h + part (f16 hi / lo of q * scale * log2 e); rows >= 2R zero.
+  {
+    const float qscale = p.scale * 1.4426950408889634f;
+    for (int idx = lane; idx < NS * 64 * 8; idx += 64) {
+      const int i = idx & 7, l = (idx >> 3) & 63, s = idx >> 9;
+      const int m = l & 15, k = l >> 4;
+      const int pos = KVDT == KV_Q8_T ? perm8(i) : i;
+      const int d = 32 * s + 8 * k + pos;
+      u16 v = 0;
+      if (m < 2 * R) {
+        const float x = s_vec[m >> 1][d] * qscale;
+        const u16 h = f2h(x);
+        v = (m & 1) ? f2h(x - h2f(h)) : h;
+      }
+      s_q[s][l][i] = v;
+    }
+    for (int idx = lane; idx < (int)sizeof(s_p) / 2; idx += 64) (&s_p[0][0][0])[idx] = 0;
+  }
+  if (owner) {
+    const size_t pg = (size_t)bt[new_page];
+    uint8_t* kdst = (uint8_t*)p.k_pages + pg * page_bytes + (size_t)g * HB;
+    uint8_t* vdst = (uint8_t*)p.v_pages + pg * page_bytes + (size_t)g * HB;
+    store_token<KVDT>(s_vec[R], s_knew, kdst, false, D, new_slot, lane);
+    store_token<KVDT>(s_vec[R + 1], s_vnew, vdst, true, D, new_slot, lane);
+  }
+  __syncthreads();
+  u32x4 qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)&s_q[s][lane][0];
+
+  // ---- page loop -------------------------------------------------------------------
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 O[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint8_t* kbase = (const uint8_t*)p.k_pages + (size_t)g * HB;
+  const uint8_t* vbase = (const uint8_t*)p.v_pages + (size_t)g * HB;
+  PageRegs<KVDT, D> cur, nxt;
+  {
+    const size_t pg = (size_t)bt[pg0];
+    load_page<KVDT, D>(cur, kbase + pg * page_bytes, vbase + pg * page_bytes, lane);
+  }
+  for (int j = pg0; j < pg1; ++j) {
+    if (j + 1 < pg1) {
+      const size_t pg = (size_t)bt[j + 1];
+      load_page<KVDT, D>(nxt, kbase + pg * page_bytes, vbase + pg * page_bytes, lane);
+    }
+    if (FUSED && owner && j == new_page) patch_page<KVDT, D>(cur, s_knew, s_vnew, new_slot, lane);
+    const int valid = min(kPage, n_tok - j * kPage);
+    if constexpr (KVDT != KV_Q8_T) {
+      // slots past the context may hold anything (NaN included): zero their V so
+      // that 0 * V stays 0 in the PV product
+      if (valid < kPage) mask_v_tail<KVDT, D>(cur, valid, lane);
+    }
+
+    // scores
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (KVDT == KV_F16_T) {
+        sc = mfma_f16_k32(qf[s], cur.k[s], sc);
+      } else if constexpr (KVDT == KV_F32_T) {
+        u32x2 h0, l0, h1, l1;
+        f32_to_f16hl(cur.k[s][0], h0, l0);
+        f32_to_f16hl(cur.k[s][1], h1, l1);
+        sc = mfma_f16_k32(qf[s], u32x4{h0.x, h0.y, h1.x, h1.y}, sc);
+        sc = mfma_f16_k32(qf[s], u32x4{l0.x, l0.y, l1.x, l1.y}, sc);
+      } else {
+        const u32x2 c0 = q8_to_f16x4(cur.k[s].x), c1 = q8_to_f16x4(cur.k[s].y);
+        const f32x4 part = mfma_f16_k32(qf[s], u32x4{c0.x, c0.y, c1.x, c1.y}, f32x4{0.f, 0.f, 0.f, 0.f});
+        const u32 w = cur.ksc[s >> 1];
+        const float ks = h2f((u16)((s & 1) ? (w >> 16) : (w & 0xFFFF)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = __builtin_fmaf(ks, part[i], sc[i]);
+      }
+    }
+    // lane (token n, kg): rows 4kg..4kg+3 = heads 2kg (hi, lo), 2kg+1 (hi, lo)
+    float sv[2], pv[2], alpha[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      sv[e] = n < valid ? sc[2 * e] + sc[2 * e + 1] : -INFINITY;
+      float mx = sv[e];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float mnew = fmaxf(m_run[e], mx);
+      alpha[e] = exp2f(m_run[e] - mnew);
+      pv[e] = exp2f(sv[e] - mnew);
+      float ps = pv[e];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
+      l_run[e] = l_run[e] * alpha[e] + ps;
+      m_run[e] = mnew;
+    }
+    // P (f16 hi/lo rows) to LDS, transposed to the PV A layout
+    const bool live = 2 * kg < R;  // this lane group holds real heads
+    if constexpr (KVDT == KV_Q8_T) {
+      const int col = 4 * (n >> 2) + perm4(n & 3);
+#pragma unroll
+      for (int blk = 0; blk < D / 32; ++blk) {
+        const u32 w = cur.vsc[blk >> 1];
+        const float vs = h2f((u16)((blk & 1) ? (w >> 16) : (w & 0xFFFF)));
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float x = n < valid ? pv[e] * vs : 0.0f;
+          const u16 h = f2h(x);
+          if (live) {
+            s_p[blk][4 * kg + 2 * e][col] = h;
+            s_p[blk][4 * kg + 2 * e + 1][col] = f2h(x - h2f(h));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const u16 h = f2h(pv[e]);
+        if (live) {
+          s_p[0][4 * kg + 2 * e][n] = h;
+          s_p[0][4 * kg + 2 * e + 1][n] = f2h(pv[e] - h2f(h));
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      O[t][0] *= alpha[0];
+      O[t][1] *= alpha[0];
+      O[t][2] *= alpha[1];
+      O[t][3] *= alpha[1];
+    }
+    if constexpr (KVDT == KV_Q8_T) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x2 pa = *(const u32x2*)&s_p[t >> 1][n][4 * kg];
+        O[t] = mfma_f16_k16(pa, q8_to_f16x4(cur.v[t]), O[t]);
+      }
+    } else {
+      const u32x2 pa = *(const u32x2*)&s_p[0][n][4 * kg];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (KVDT == KV_F16_T) {
+          O[t] = mfma_f16_k16(pa, cur.v[t], O[t]);
+        } else {
+          u32x2 hi, lo;
+          f32_to_f16hl(cur.v[t], hi, lo);
+          O[t] = mfma_f16_k16(pa, hi, O[t]);
+          O[t] = mfma_f16_k16(pa, lo, O[t]);
+        }
+      }
+    }
+    __syncthreads();
+    if (j + 1 < pg1) cur = nxt;
+  }
+
+  // ---- partial results -------------------------------------------------------------
+  if (2 * kg < R) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int h = g * R + 2 * kg + e;
+      if (2 * kg + e >= R) break;
+      const size_t base = ((size_t)b * p.n_q_heads + h) * p.max_splits + split;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) p.o_part[base * D + 16 * t + n] = O[t][2 * e] + O[t][2 * e + 1];
+      if (n == 0) {
+        p.m_part[base] = m_run[e];
+        p.l_part[base] = l_run[e];
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------- merge
+// Per (row b, query head h): M = max m_s, L = sum l_s 2^(m_s - M),
+// o = sum o_s 2^(m_s - M) / L.  Writes f32 out [B][Hq][D] and/or the activation pack
+// of the output projection (K = Hq*D, kind `kind`).
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p, float* out, uint16_t* pack, float* pack_sums,
+                                                        int kind, int nslices, int fused) {
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int h = bh % p.n_q_heads, b = bh / p.n_q_heads;
+  const int D = p.head_dim;
+  const int ctx = p.ctx_lens[b];
+  const int n_tok = fused ? ctx + 1 : ctx;
+  const int n_pages = (n_tok + kPage - 1) / kPage;
+  const int S = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
+  const size_t base = ((size_t)b * p.n_q_heads + h) * p.max_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, p.m_part[base + s]);
+  float L = 0.f;
+  for (int s = 0; s < S; ++s) L += p.l_part[base + s] * exp2f(p.m_part[base + s] - M);
+  const float invL = 1.0f / L;
+  for (int d = lane; d < D; d += 64) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) acc += p.o_part[(base + s) * D + d] * exp2f(p.m_part[base + s] - M);
+    const float v = acc * invL;
+    if (out) out[((size_t)b * p.n_q_heads + h) * D + d] = v;
+    if (pack) actpack_put_lane(pack, pack_sums, kind, nslices, b, h * D + d, v, lane);
+  }
+}
+
+// ------------------------------------------------------------------------ launch
+
+AttnPlan plan_attn(int B, int n_kv_heads, int max_ctx_tokens) {
+  // Enough (row, head, split) waves to fill the chip even when most rows are short:
+  // about 4096 waves at the longest context, at least 4 pages per split.
+  const int max_pages = (max_ctx_tokens + kPage - 1) / kPage;
+  const long long units = (long long)B * n_kv_heads * (max_pages > 0 ? max_pages : 1);
+  int pps = (int)((units + 4095) / 4096);
+  if (pps < 4) pps = 4;
+  AttnPlan pl;
+  pl.pages_per_split = pps;
+  pl.max_splits = max_pages > 0 ? (max_pages + pps - 1) / pps : 1;
+  return pl;
+}
+
+size_t attn_partial_floats(int B, int n_q_heads, int head_dim, const AttnPlan& pl) {
+  return (size_t)B * n_q_heads * pl.max_splits * (head_dim + 2);
+}
+
+hipError_t launch_attn_split(int kv_dtype, bool fused, const AttnParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)((size_t)p.B * p.n_kv_heads * p.max_splits));
+#define GR_A(KV, DD, FU) attn_split_kernel<KV, DD, FU><<<grid, 64, 0, st>>>(p)
+#define GR_AD(KV, FU)        \
+  if (p.head_dim == 128)     \
+    GR_A(KV, 128, FU);       \
+  else                       \
+    GR_A(KV, 64, FU);
+#define GR_AK(FU)                  \
+  if (kv_dtype == 0) {             \
+    GR_AD(KV_F32_T, FU)            \
+  } else if (kv_dtype == 1) {      \
+    GR_AD(KV_F16_T, FU)            \
+  } else {                         \
+    GR_AD(KV_Q8_T, FU)             \
+  }
+  if (fused) {
+    GR_AK(true)
+  } else {
+    GR_AK(false)
+  }
+#undef GR_AK
+#undef GR_AD
+#undef GR_A
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, float* pack_sums, int kind,
+                             int nslices, int fused, hipStream_t st) {
+  attn_merge_kernel<<<dim3((unsigned)(p.B * p.n_q_heads)), 64, 0, st>>>(p, out, pack, pack_sums, kind, nslices,
+                                                                         fused);
+  return hipGetLastError();
+}
+
+}  // namespace gr

@@ -1,0 +1,46 @@
+// attn_internal.h -- parameters of the split-context paged attention kernels.
+#pragma once
+
+#include "gr_common.h"
+
+namespace gr {
+
+constexpr int KV_F32_T = 0;
+constexpr int KV_F16_T = 1;
+constexpr int KV_Q8_T = 2;
+
+struct AttnParams {
+  int B, n_q_heads, n_kv_heads, head_dim;
+  int max_blocks, pages_per_split, max_splits;
+  float scale;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const void* k_pages;  // non-const in the fused variant (the new token is stored)
+  const void* v_pages;
+  // standalone: q f32 [B][Hq][D]
+  const float* q;
+  // fused: q/k/v f32 [B][qkv_ld] (q at 0, k at q_dim, v at q_dim + kv_dim)
+  const float* qkv;
+  int qkv_ld, qkv_splits, q_dim, kv_dim;
+  const float* q_norm;  // NULL: no QK-norm
+  const float* k_norm;
+  float eps;
+  double rope_theta;
+  int rope_style;
+  // partials [B][Hq][max_splits](*D)
+  float* o_part;
+  float* m_part;
+  float* l_part;
+};
+
+struct AttnPlan {
+  int pages_per_split, max_splits;
+};
+
+AttnPlan plan_attn(int B, int n_kv_heads, int max_ctx_tokens);
+size_t attn_partial_floats(int B, int n_q_heads, int head_dim, const AttnPlan& pl);
+hipError_t launch_attn_split(int kv_dtype, bool fused, const AttnParams& p, hipStream_t st);
+hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, float* pack_sums, int kind,
+                             int nslices, int fused, hipStream_t st);
+
+}  // namespace gr

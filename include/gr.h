@@ -1,0 +1,186 @@
+/*
+ * gr.h -- C ABI of the continuous-batched, quantized decode step on MI355X (gfx950).
+ *
+ * The operations follow the problem as the pages state it:
+ *  - Leone, intro: the server batches active decode rows into shared matrix
+ *    operations while each request keeps separate attention; "What ships": Q4_K and
+ *    Q6_K weights, f32 / f16 / q8 KV storage, graph-replayed decode.
+ *  - tinyllm, Status: a physical KV page pool, a logical block table per sequence,
+ *    variable-length batched decode; Roadmap item 6: paged KV blocks behind a typed
+ *    attention metadata boundary; Known limitations: 16-token pages.
+ *  - LeatEngine, Run: a q8_0 KV cache as llama.cpp keeps it (32-element blocks,
+ *    fp16 scale) in about half the memory of f16.
+ *
+ * Conventions for every call:
+ *  - Pointers are device memory owned by the caller (weights, pools, activations,
+ *    block tables, workspaces).  The library never allocates, frees or
+ *    synchronizes; calls enqueue work on `stream` (a hipStream_t, NULL = the null
+ *    stream) and return.  Results are valid once the stream reaches them.
+ *  - Every check the host can make runs before anything is enqueued; a call that
+ *    returns an error enqueued nothing.  Unknown enum values are rejected
+ *    (GR_ERR_DTYPE), never ignored.  Capacity errors are returned before the
+ *    capacity would be exceeded (GR_ERR_CAPACITY).
+ *  - Device-resident preconditions are documented, not checked: block-table
+ *    entries of the pages a row uses lie in [0, num_pages); ctx_lens[b] <= max_ctx.
+ *  - B == 0 returns GR_OK and enqueues nothing.
+ *  - Weight matrices are GGUF super-block rows: row n of an N x K matrix is K/256
+ *    consecutive blocks (Q4_K: 144 B, Q6_K: 210 B), rows back to back.
+ *    y[b][n] = sum_k W[n][k] * x[b][k].  K must be a multiple of 256.
+ *  - KV pools (one K pool and one V pool per layer): page p holds 16 tokens of all
+ *    KV heads; head g occupies bytes [g*HB, (g+1)*HB) of the page with
+ *    HB = gr_kv_head_bytes(kv_dtype, head_dim).  K heads are token-major [16][D],
+ *    V heads are dim-major [D][16].  f32 / f16 heads hold plain elements; q8_0 heads
+ *    hold the 16*D int8 codes in that order followed by fp16 scales [16][D/32]
+ *    (token t, block j covers elements 32j..32j+31 of that token).
+ *  - The block table is int32 [B][max_blocks_per_row]; entry j of row b is the
+ *    physical page holding that row's logical tokens 16j..16j+15.
+ */
+#ifndef GR_H_
+#define GR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GR_ABI_VERSION 1
+
+typedef enum {
+  GR_OK = 0,
+  GR_ERR_NULL = -1,      /* a required pointer is NULL */
+  GR_ERR_SHAPE = -2,     /* a size or shape is out of the supported range */
+  GR_ERR_DTYPE = -3,     /* unknown weight type, KV dtype or rope style */
+  GR_ERR_ALIGN = -4,     /* a pointer lacks the stated alignment */
+  GR_ERR_WORKSPACE = -5, /* workspace missing or smaller than the size query returns */
+  GR_ERR_CAPACITY = -6,  /* max_ctx + 1 tokens do not fit max_blocks_per_row pages */
+  GR_ERR_DEVICE = -7,    /* the current device is not gfx950 */
+  GR_ERR_LAUNCH = -8     /* a kernel launch failed; see gr_last_hip_error() */
+} gr_status;
+
+typedef enum { GR_KV_F32 = 0, GR_KV_F16 = 1, GR_KV_Q8_0 = 2 } gr_kv_dtype;
+/* values are the GGUF tensor type ids */
+typedef enum { GR_W_Q4_K = 12, GR_W_Q6_K = 14 } gr_wtype;
+/* NEOX rotates (v[i], v[i+D/2]); NORM rotates (v[2i], v[2i+1]) */
+typedef enum { GR_ROPE_NEOX = 0, GR_ROPE_NORM = 1 } gr_rope_style;
+
+#define GR_PAGE_SIZE 16
+
+int gr_abi_version(void);
+const char* gr_status_str(int status);
+/* hipError_t of the most recent GR_ERR_LAUNCH on the calling thread (0 if none). */
+int gr_last_hip_error(void);
+/* Bytes of one KV head's block inside a page, or -1 for an unknown dtype. */
+int64_t gr_kv_head_bytes(int kv_dtype, int head_dim);
+
+/* ---------------------------------------------------------------- dequant --
+ * Test exports (bit-exactness).  Leone, "What ships": Q4_K and Q6_K weights; the
+ * block layouts are the public GGUF formats.  out receives 256 (Q4_K, Q6_K) or 32
+ * (q8_0, 34-byte GGUF blocks) fp32 values per block.  Q4_K values are
+ * fp32(d*sc)*q - fp32(dmin*m) rounded once (one fused multiply-add); Q6_K and
+ * q8_0 values are exact in fp32.  blocks: 2-byte aligned; out: 4-byte aligned. */
+gr_status gr_q4k_dequant(const void* blocks, int64_t n_blocks, float* out, void* stream);
+gr_status gr_q6k_dequant(const void* blocks, int64_t n_blocks, float* out, void* stream);
+gr_status gr_q8_0_dequant(const void* blocks, int64_t n_blocks, float* out, void* stream);
+
+/* ------------------------------------------------------------------ GEMM --
+ * Fused-dequant skinny GEMM (Leone, intro: shared matrix operations over the
+ * active rows).  x: f32 [B][K], y: f32 [B][N], both row-major, 16-byte aligned;
+ * wblocks 16-byte aligned.  1 <= B <= 64, N >= 1, K % 256 == 0, K <= 65536.
+ * The workspace (16-byte aligned) holds the packed activations and split-K partial
+ * sums; size it with gr_gemm_workspace_size.  Weights are streamed once. */
+size_t gr_gemm_workspace_size(int B, int N, int K);
+gr_status gr_q4k_gemm(const void* wblocks, const float* x, float* y, int B, int N, int K, void* workspace,
+                      size_t ws_bytes, void* stream);
+gr_status gr_q6k_gemm(const void* wblocks, const float* x, float* y, int B, int N, int K, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------- attention --
+ * Typed attention metadata (tinyllm, Roadmap item 6). */
+typedef struct {
+  int n_q_heads, n_kv_heads, head_dim; /* head_dim in {64, 128}; n_q_heads % n_kv_heads == 0, ratio <= 8 */
+  int page_size;                       /* must be 16 */
+  int kv_dtype;                        /* gr_kv_dtype */
+  int num_pages, max_blocks_per_row, max_ctx;
+  float scale;                         /* softmax scale, normally 1/sqrt(head_dim) */
+} gr_attn_meta;
+
+/* Per-row GQA decode attention over paged KV (Leone, intro: each request keeps
+ * its own attention; tinyllm: pages addressed through a logical block table).
+ * q, out: f32 [B][n_q_heads][head_dim]; row b attends its first ctx_lens[b] tokens
+ * (1 <= ctx_lens[b] <= max_ctx, all already in the pools); query head h uses KV head
+ * h / (n_q_heads / n_kv_heads).  out[b][h] = sum_t softmax_t(scale * q.k_t) v_t.
+ * The context is cut into page-aligned splits processed in parallel and merged by
+ * log-sum-exp.  Pools and q 16-byte aligned. */
+size_t gr_paged_decode_attn_workspace_size(const gr_attn_meta* m, int B);
+gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                               const int32_t* ctx_lens, float* out, int B, const gr_attn_meta* m, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* Test export (bit-exactness of the page walk): decode the first ctx_lens[b] tokens
+ * of each row of one pool (is_v selects the V layout) into out f32
+ * [B][max_ctx][n_kv_heads][head_dim]; slots at or beyond ctx_lens[b] are untouched. */
+gr_status gr_paged_gather_kv(const void* pages, int is_v, const int32_t* block_table, const int32_t* ctx_lens, int B,
+                             const gr_attn_meta* m, float* out, void* stream);
+
+/* ----------------------------------------------------------- decode layer --
+ * One decode layer of a dense Qwen3 / Llama-3 stack (tinyllm, Status: RMSNorm,
+ * RoPE, GQA, SwiGLU MLP; Leone: Q4_K / Q6_K weights, f32 / f16 / q8 KV). */
+typedef struct {
+  int hidden, n_q_heads, n_kv_heads, head_dim, ffn;
+  float rms_eps;
+  double rope_theta;
+  int rope_style; /* gr_rope_style */
+  int qk_norm;    /* 1: per-head RMSNorm of q and k before RoPE (Qwen3) */
+  int kv_dtype;   /* gr_kv_dtype */
+  int page_size;  /* must be 16 */
+} gr_layer_cfg;
+
+typedef struct {
+  const float *attn_norm, *ffn_norm; /* f32 [hidden] */
+  const float *q_norm, *k_norm;      /* f32 [head_dim]; NULL unless qk_norm */
+  const void *wq, *wk, *wv;          /* [Hq*D x hidden], [Hkv*D x hidden], [Hkv*D x hidden] */
+  const void* wo;                    /* [hidden x Hq*D] */
+  const void *w_gate, *w_up;         /* [ffn x hidden] */
+  const void* w_down;                /* [hidden x ffn] */
+  int tq, tk, tv, to, tgate, tup, tdown; /* gr_wtype of each matrix */
+} gr_layer_weights;
+
+/* x: f32 [B][hidden], the residual stream, read and overwritten with the layer
+ * output.  ctx_lens[b] = tokens already cached for row b (0 <= ctx_lens[b] <=
+ * max_ctx); the step computes the new token's k and v, stores them at logical
+ * position ctx_lens[b] (page block_table[b][ctx_lens[b]/16], slot ctx_lens[b]%16;
+ * f32 / f16 round to nearest even; q8_0 per 32-element block: amax, d = amax/127,
+ * codes round(x/d) half away from zero, scale fp16(d)), and attends ctx_lens[b]+1
+ * tokens.  ctx_lens is not advanced (the caller does that).  Requires
+ * max_ctx + 1 <= 16 * max_blocks_per_row (else GR_ERR_CAPACITY). */
+size_t gr_decode_layer_workspace_size(const gr_layer_cfg* c, int B, int max_ctx);
+gr_status gr_decode_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pages, void* v_pages,
+                          int num_pages, float* x, const int32_t* block_table, int max_blocks_per_row,
+                          const int32_t* ctx_lens, int max_ctx, int B, void* workspace, size_t ws_bytes,
+                          void* stream);
+
+/* Final RMSNorm and output head (Leone: sampling follows the logits):
+ * logits f32 [B][vocab] = W (rms(x_b) * norm), W [vocab x hidden]. */
+size_t gr_output_head_workspace_size(int B, int hidden, int vocab);
+gr_status gr_output_head(const float* x, const float* norm, float eps, const void* w, int wtype, float* logits,
+                         int B, int hidden, int vocab, void* workspace, size_t ws_bytes, void* stream);
+
+/* Whole decode step: n_layers layers in order (layer l uses weights[l], k_pages[l],
+ * v_pages[l]; host arrays of device pointers), then, when head_w is not NULL, the
+ * final norm and output head into logits.  One workspace of
+ * gr_decode_stack_workspace_size bytes serves every layer.  Suitable for capture
+ * into one HIP graph (a fixed sequence of kernel launches, no host syncs). */
+size_t gr_decode_stack_workspace_size(const gr_layer_cfg* c, int B, int max_ctx, int vocab);
+gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers, void* const* k_pages,
+                          void* const* v_pages, int num_pages, float* x, const int32_t* block_table,
+                          int max_blocks_per_row, const int32_t* ctx_lens, int max_ctx, int B,
+                          const float* head_norm, const void* head_w, int head_wtype, int vocab, float* logits,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GR_H_ */

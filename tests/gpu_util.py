@@ -1,0 +1,29 @@
+"""Shared helpers of the GPU parity tests (device upload, error norms)."""
+import numpy as np
+import pytest
+
+
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def dev(a, torch):
+    """numpy -> device tensor with the same dtype and shape."""
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def rel_l2(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+
+
+def say(*a):
+    print(*a, flush=True)

@@ -1,0 +1,60 @@
+"""The C-ABI library loads and exports every function include/gr.h declares (no GPU)."""
+import ctypes
+import os
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gr.h")
+LIB = os.path.join(ROOT, "continuous_quantized_decode_amd", "libgr.so")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gr_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared()
+    for n in ("gr_q4k_gemm", "gr_q6k_gemm", "gr_paged_decode_attn", "gr_decode_layer", "gr_decode_stack",
+              "gr_q4k_dequant", "gr_q6k_dequant", "gr_q8_0_dequant", "gr_paged_gather_kv", "gr_output_head"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "build first: python -m continuous_quantized_decode_amd.build"
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_lists_match_header():
+    import continuous_quantized_decode_amd as gr
+    assert sorted(gr.EXPORTED) == declared()
+
+
+def test_host_side_checks_without_gpu():
+    """Calls that fail a host check return their status before touching the device."""
+    import continuous_quantized_decode_amd as gr
+    L = gr.lib()
+    assert L.gr_abi_version() == 1
+    assert L.gr_status_str(-6) == b"max_ctx + 1 tokens exceed the block table's pages"
+    assert L.gr_kv_head_bytes(2, 128) == 16 * 128 + 16 * 4 * 2
+    assert L.gr_kv_head_bytes(7, 128) == -1
+    # B == 0 is a no-op; NULL pointers, bad K, bad dtype, capacity are rejected
+    assert L.gr_q4k_gemm(None, None, None, 0, 16, 256, None, 0, None) == 0
+    assert L.gr_q4k_gemm(None, None, None, 1, 16, 256, None, 0, None) == -1
+    buf = ctypes.create_string_buffer(4096)
+    p = ctypes.addressof(buf) + (-ctypes.addressof(buf) % 256)
+    assert L.gr_q4k_gemm(p, p, p, 1, 16, 255, p, 1024, None) == -2
+    cfg = gr.layer_cfg(256, 4, 2, 64, 768, 1e-6, 1e4, 0, 0, 5)
+    w = gr.LayerWeights(*([p] * 11 + [12] * 7))
+    assert L.gr_decode_layer(ctypes.byref(cfg), ctypes.byref(w), p, p, 9, p, p, 9, p, 128, 1, p, 1 << 20, None) == -3
+    cfg = gr.layer_cfg(256, 4, 2, 64, 768, 1e-6, 1e4, 0, 0, 0)
+    assert L.gr_decode_layer(ctypes.byref(cfg), ctypes.byref(w), p, p, 9, p, p, 8, p, 128, 1, p, 1 << 20, None) == -6
+    w2 = gr.LayerWeights(*([p] * 11 + [12] * 6 + [13]))
+    assert L.gr_decode_layer(ctypes.byref(cfg), ctypes.byref(w2), p, p, 9, p, p, 9, p, 128, 1, p, 1 << 20, None) == -3
+    meta = gr.attn_meta(4, 2, 96, 1, 9, 9, 128)
+    assert L.gr_paged_decode_attn(p, p, p, p, p, p, 1, ctypes.byref(meta), p, 4096, None) == -2
+    meta = gr.attn_meta(4, 2, 64, 1, 9, 8, 129)
+    assert L.gr_paged_decode_attn(p, p, p, p, p, p, 1, ctypes.byref(meta), p, 4096, None) == -6

@@ -1,0 +1,195 @@
+"""GPU parity of the individual hot-path kernels against the fp64 oracle, through the C ABI.
+
+Bars: dequantization and the page gather are bit-exact; the GEMM and the standalone
+attention (fp32 accumulation of exact bf16/f16 hi-lo operands) stay within a
+relative L2 error of 1e-4 of the oracle, far inside the layer tolerances.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import dev, host, rel_l2, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+KERNEL_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return torch_cuda()
+
+
+@pytest.fixture(scope="module")
+def gr():
+    import continuous_quantized_decode_amd as gr
+    gr.lib()
+    return gr
+
+
+# ----------------------------------------------------------------------------- dequant
+
+@pytest.mark.parametrize("n_blocks", [1, 16, 37, 1000])
+def test_q4k_dequant_bit_exact(torch, gr, orc, n_blocks):
+    w = synth.q4k_weight(np.random.default_rng(100 + n_blocks), n_blocks, 256)
+    say("q4k dequant", n_blocks)
+    got = host(gr.gr_q4k_dequant(dev(w, torch)))
+    want = orc.dequant("q4k", w).astype(np.float32)  # exact fp64 value, rounded once
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("n_blocks", [1, 3, 17, 999])
+def test_q6k_dequant_bit_exact(torch, gr, orc, n_blocks):
+    # odd block counts put every other block at a 2-mod-4 byte offset
+    w = synth.q6k_weight(np.random.default_rng(200 + n_blocks), n_blocks, 256)
+    say("q6k dequant", n_blocks)
+    got = host(gr.gr_q6k_dequant(dev(w, torch)))
+    want = orc.dequant("q6k", w)
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_q8_0_dequant_bit_exact(torch, gr, orc):
+    rng = np.random.default_rng(300)
+    n = 777
+    blk = rng.integers(0, 256, size=(n, 34), dtype=np.uint8)
+    blk[:, 0:2] = rng.uniform(1e-3, 1.0, n).astype(np.float16).view(np.uint8).reshape(n, 2)
+    say("q8_0 dequant", n)
+    got = host(gr.gr_q8_0_dequant(dev(blk, torch)))
+    assert np.array_equal(got.astype(np.float64), orc.dequant("q8_0", blk))
+
+
+def test_handpacked_blocks_on_gpu(torch, gr, orc):
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "handpacked.json")))
+    for name, e in sorted(gold.items()):
+        raw = np.frombuffer(bytes.fromhex(e["hex"]), np.uint8).copy()
+        fn = {"Q4_K": (gr.gr_q4k_dequant, "q4k"), "Q6_K": (gr.gr_q6k_dequant, "q6k"),
+              "q8_0": (gr.gr_q8_0_dequant, "q8_0")}[e["format"]]
+        got = host(fn[0](dev(raw, torch))).astype(np.float64)
+        assert np.array_equal(got, orc.dequant(fn[1], raw)), name
+
+
+# ----------------------------------------------------------------------------- GEMM
+
+GEMM_CASES = [
+    (synth.W_Q4_K, 1, 16, 256),
+    (synth.W_Q4_K, 3, 40, 768),      # ragged row tile
+    (synth.W_Q4_K, 8, 256, 4096),
+    (synth.W_Q4_K, 8, 4096, 4096),   # split-K
+    (synth.W_Q4_K, 17, 200, 1024),   # three batch tiles, padded to four
+    (synth.W_Q4_K, 32, 512, 2048),
+    (synth.W_Q4_K, 64, 64, 512),
+    (synth.W_Q6_K, 1, 16, 256),
+    (synth.W_Q6_K, 5, 48, 768),      # odd blocks per row: 2-byte aligned blocks
+    (synth.W_Q6_K, 8, 1024, 3072),
+    (synth.W_Q6_K, 8, 4096, 14336),
+    (synth.W_Q6_K, 12, 100, 1280),
+    (synth.W_Q6_K, 32, 256, 1024),
+]
+
+
+@pytest.mark.parametrize("wtype,b,n,k", GEMM_CASES)
+def test_gemm_matches_oracle(torch, gr, orc, wtype, b, n, k):
+    rng = np.random.default_rng(1000 + b * 7 + n + k)
+    w = synth.weight(rng, wtype, n, k)
+    x = rng.standard_normal((b, k), dtype=np.float32)
+    say("gemm", wtype, b, n, k)
+    fn = gr.gr_q4k_gemm if wtype == synth.W_Q4_K else gr.gr_q6k_gemm
+    got = host(fn(dev(w, torch), dev(x, torch), n))
+    want = orc.gemm(wtype, w, x, n, k)
+    err = rel_l2(got, want)
+    say("  rel_l2", err)
+    assert err <= KERNEL_TOL
+
+
+def test_gemm_large_activation_range(torch, gr, orc):
+    """bf16 hi/lo keeps the full fp32 range: activations up to 1e6 and down to 1e-6."""
+    rng = np.random.default_rng(7)
+    n, k, b = 64, 1024, 4
+    w = synth.q4k_weight(rng, n, k)
+    x = (rng.standard_normal((b, k)) * 10.0 ** rng.uniform(-6, 6, (b, k))).astype(np.float32)
+    got = host(gr.gr_q4k_gemm(dev(w, torch), dev(x, torch), n))
+    assert rel_l2(got, orc.gemm(synth.W_Q4_K, w, x, n, k)) <= KERNEL_TOL
+
+
+def test_gemm_rows_independent(torch, gr):
+    """Batched rows equal the same rows computed alone (the pages' batched-service check)."""
+    rng = np.random.default_rng(8)
+    n, k = 512, 2048
+    w = dev(synth.q4k_weight(rng, n, k), torch)
+    x = rng.standard_normal((8, k), dtype=np.float32)
+    full = host(gr.gr_q4k_gemm(w, dev(x, torch), n))
+    for r in (0, 5):
+        one = host(gr.gr_q4k_gemm(w, dev(x[r:r + 1], torch), n))
+        assert rel_l2(one[0], full[r]) <= KERNEL_TOL
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _attn_case(kv_dtype, d, hq, hkv, ctx, seed, pool_kind="exact"):
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], kv_dtype=kv_dtype, head_dim=d, n_q_heads=hq, n_kv_heads=hkv,
+                             batch=len(ctx), pool_kind=pool_kind, seed=seed)
+    c = np.asarray(ctx, np.int32)
+    kv = synth.kv_state(wl, c, n_layers=1, extra_slot=False)
+    q = synth.attn_query(np.random.default_rng(seed), len(ctx), hq, d)
+    return wl, c, kv, q
+
+
+ATTN_CASES = [
+    (synth.KV_F16, 128, 8, 2, [1, 15, 16, 17, 300]),
+    (synth.KV_F16, 128, 32, 8, [1000, 64, 4097]),
+    (synth.KV_F16, 64, 4, 2, [128, 33]),
+    (synth.KV_F32, 64, 4, 2, [128, 1, 250]),
+    (synth.KV_F32, 128, 16, 8, [77, 512]),
+    (synth.KV_Q8_0, 128, 32, 8, [2000, 16, 5]),
+    (synth.KV_Q8_0, 64, 8, 1, [31, 700]),
+    (synth.KV_F16, 128, 24, 8, [40, 3]),   # GQA ratio 3
+]
+
+
+@pytest.mark.parametrize("kv_dtype,d,hq,hkv,ctx", ATTN_CASES)
+def test_paged_attention_matches_oracle(torch, gr, orc, kv_dtype, d, hq, hkv, ctx):
+    wl, c, kv, q = _attn_case(kv_dtype, d, hq, hkv, ctx, seed=len(ctx) + d + hq)
+    pm = kv.pages
+    meta = gr.attn_meta(hq, hkv, d, kv_dtype, pm.num_pages, pm.max_blocks, int(c.max()))
+    say("attn", kv_dtype, d, hq, hkv, ctx)
+    got = host(gr.gr_paged_decode_attn(dev(q, torch), dev(kv.k_pools[0], torch), dev(kv.v_pools[0], torch),
+                                       dev(pm.block_table, torch), dev(c, torch), meta))
+    want = orc.paged_attention(q, kv.k_pools[0], kv.v_pools[0], kv_dtype, pm.block_table, c, hkv)
+    assert np.isfinite(got).all()
+    err = rel_l2(got, want)
+    say("  rel_l2", err)
+    assert err <= KERNEL_TOL
+
+
+def test_paged_attention_page_permutation_is_bitwise_invariant(torch, gr):
+    wl, c, kv, q = _attn_case(synth.KV_F16, 128, 8, 2, [333, 40], seed=5)
+    pm = kv.pages
+    meta = gr.attn_meta(8, 2, 128, synth.KV_F16, pm.num_pages, pm.max_blocks, int(c.max()))
+    base = host(gr.gr_paged_decode_attn(dev(q, torch), dev(kv.k_pools[0], torch), dev(kv.v_pools[0], torch),
+                                        dev(pm.block_table, torch), dev(c, torch), meta))
+    perm = np.random.default_rng(6).permutation(pm.num_pages)
+    kp, vp = np.empty_like(kv.k_pools[0]), np.empty_like(kv.v_pools[0])
+    kp[perm], vp[perm] = kv.k_pools[0], kv.v_pools[0]
+    bt = np.where(pm.block_table >= 0, perm[np.maximum(pm.block_table, 0)], -1).astype(np.int32)
+    moved = host(gr.gr_paged_decode_attn(dev(q, torch), dev(kp, torch), dev(vp, torch), dev(bt, torch),
+                                         dev(c, torch), meta))
+    assert np.array_equal(base, moved)
+
+
+@pytest.mark.parametrize("kv_dtype,d", [(synth.KV_F32, 64), (synth.KV_F16, 128), (synth.KV_Q8_0, 128),
+                                        (synth.KV_Q8_0, 64)])
+def test_page_gather_bit_exact(torch, gr, orc, kv_dtype, d):
+    wl, c, kv, _ = _attn_case(kv_dtype, d, 4, 2, [1, 16, 17, 90], seed=11, pool_kind="fill90")
+    pm = kv.pages
+    meta = gr.attn_meta(4, 2, d, kv_dtype, pm.num_pages, pm.max_blocks, int(c.max()))
+    for is_v, pool in ((False, kv.k_pools[0]), (True, kv.v_pools[0])):
+        got = host(gr.gr_paged_gather_kv(dev(pool, torch), is_v, dev(pm.block_table, torch), dev(c, torch), meta))
+        want = orc.gather_kv(pool, kv_dtype, is_v, 2, d, pm.block_table, c)
+        off = 0
+        for b, n in enumerate(c):
+            assert np.array_equal(got[b, :n].astype(np.float64), want[off:off + n]), (is_v, b)
+            off += n

@@ -1,0 +1,158 @@
+"""GPU parity of whole decode layers and stacks against the fp64 oracle (C ABI).
+
+Bars (relative L2 over each layer's [B, hidden] output, the GPU running the stack
+end to end): 2e-3 for f32 / f16 KV, 5e-3 for q8_0 KV.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import dev, host, rel_l2, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def tol(kv_dtype):
+    return 5e-3 if kv_dtype == synth.KV_Q8_0 else 2e-3
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return torch_cuda()
+
+
+@pytest.fixture(scope="module")
+def gr():
+    import continuous_quantized_decode_amd as gr
+    gr.lib()
+    return gr
+
+
+def upload_layer(gr, torch, lw):
+    t = {k: dev(getattr(lw, k), torch) for k in ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo", "w_gate", "w_up",
+                                                  "w_down")}
+    if lw.q_norm is not None:
+        t["q_norm"] = dev(lw.q_norm, torch)
+        t["k_norm"] = dev(lw.k_norm, torch)
+    for k in ("tq", "tk", "tv", "to", "tgate", "tup", "tdown"):
+        t[k] = getattr(lw, k)
+    return t, gr.layer_weights(t)
+
+
+def cfg_of(gr, wl):
+    return gr.layer_cfg(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.ffn, wl.rms_eps, wl.rope_theta,
+                        wl.rope_style, wl.qk_norm, wl.kv_dtype)
+
+
+def tiny(**rep):
+    return dataclasses.replace(synth.WORKLOADS["tiny"], **rep)
+
+
+LAYER_CASES = [
+    dict(ctx=[128]),                                                    # the tiny workload as stated
+    dict(ctx=[0, 15, 16, 17, 128], batch=5),
+    dict(ctx=[5, 64, 200], batch=3, qk_norm=True),
+    dict(ctx=[31, 32, 47], batch=3, kv_dtype=synth.KV_F16, rope_style=synth.ROPE_NORM),
+    dict(ctx=[100, 1, 63], batch=3, kv_dtype=synth.KV_Q8_0, qk_norm=True),
+    dict(ctx=[10] * 9, batch=9, kv_dtype=synth.KV_F16),                # two batch tiles
+    dict(ctx=[300, 2, 77, 150, 19, 64, 33, 5, 1, 0, 250, 99], batch=12, kv_dtype=synth.KV_Q8_0, w_down=synth.W_Q6_K,
+         head_dim=128, n_q_heads=2, n_kv_heads=2),
+]
+
+
+def run_layer_case(torch, gr, orc, wl, ctx, layer=0):
+    lw = synth.layer_weights(wl, layer)
+    c = np.asarray(ctx, np.int32)
+    kv = synth.kv_state(wl, c, n_layers=1)
+    x = synth.input_x(wl, len(c))
+    pm = kv.pages
+    t, W = upload_layer(gr, torch, lw)
+    kp, vp = dev(kv.k_pools[0], torch), dev(kv.v_pools[0], torch)
+    xg = dev(x, torch)
+    gr.gr_decode_layer(cfg_of(gr, wl), W, kp, vp, pm.num_pages, xg, dev(pm.block_table, torch), dev(c, torch),
+                       int(c.max()))
+    got = host(xg)
+    okp, ovp = kv.k_pools[0].copy(), kv.v_pools[0].copy()
+    want = orc.decode_layer(wl, lw, okp, ovp, x, pm.block_table, c)
+    return got, want, (host(kp), host(vp)), (okp, ovp), kv
+
+
+@pytest.mark.parametrize("case", range(len(LAYER_CASES)))
+def test_tiny_layer_matches_oracle(torch, gr, orc, case):
+    spec = dict(LAYER_CASES[case])
+    ctx = spec.pop("ctx")
+    wl = tiny(**spec)
+    say("layer case", case, spec, ctx)
+    got, want, gpools, opools, kv = run_layer_case(torch, gr, orc, wl, ctx)
+    assert np.isfinite(got).all()
+    err = rel_l2(got, want)
+    say("  rel_l2", err)
+    assert err <= tol(wl.kv_dtype)
+    # the appended token: every row's new K and V decode close to the oracle's stored token
+    c = np.asarray(ctx, np.int32)
+    n_tok = c + 1
+    for i, is_v in enumerate((False, True)):
+        g = orc.gather_kv(gpools[i], wl.kv_dtype, is_v, wl.n_kv_heads, wl.head_dim, kv.pages.block_table, n_tok)
+        o = orc.gather_kv(opools[i], wl.kv_dtype, is_v, wl.n_kv_heads, wl.head_dim, kv.pages.block_table, n_tok)
+        assert np.isfinite(g).all()
+        assert rel_l2(g, o) <= tol(wl.kv_dtype)
+        # tokens before the new one are untouched
+        off = 0
+        for n in n_tok:
+            assert np.array_equal(g[off:off + n - 1], o[off:off + n - 1])
+            off += n
+
+
+def test_layer_batched_matches_rows_alone(torch, gr, orc):
+    wl = tiny(batch=4, kv_dtype=synth.KV_F16, qk_norm=True)
+    ctx = [7, 100, 16, 50]
+    lw = synth.layer_weights(wl, 0)
+    c = np.asarray(ctx, np.int32)
+    kv = synth.kv_state(wl, c, n_layers=1)
+    x = synth.input_x(wl, 4)
+    t, W = upload_layer(gr, torch, lw)
+    cfg = cfg_of(gr, wl)
+    bt = kv.pages.block_table
+
+    def run(rows):
+        kp, vp = dev(kv.k_pools[0], torch), dev(kv.v_pools[0], torch)
+        xg = dev(x[rows], torch)
+        gr.gr_decode_layer(cfg, W, kp, vp, kv.pages.num_pages, xg, dev(bt[rows], torch), dev(c[rows], torch),
+                           int(c.max()))
+        return host(xg)
+
+    full = run([0, 1, 2, 3])
+    for r in range(4):
+        assert rel_l2(run([r])[0], full[r]) <= 1e-5
+    # rows leaving and joining between steps: a subset in another order
+    sub = run([3, 1])
+    assert rel_l2(sub, full[[3, 1]]) <= 1e-5
+
+
+def test_qwen3_0p6b_stack_matches_oracle(torch, gr, orc):
+    """Qwen3-0.6B-shaped stack, 28 layers, B=8, f16 KV, QK-norm: every layer output."""
+    wl = synth.WORKLOADS["qwen3_0p6b"]
+    c = synth.ctx_lens(wl)
+    kv = synth.kv_state(wl, c)
+    x = synth.input_x(wl)
+    pm = kv.pages
+    cfg = cfg_of(gr, wl)
+    xg = dev(x, torch)
+    bt, cg = dev(pm.block_table, torch), dev(c, torch)
+    cur = x
+    worst = 0.0
+    ws = gr.workspace(gr.decode_layer_workspace_size(cfg, wl.batch, int(c.max())))
+    for layer in range(wl.n_layers):
+        lw = synth.layer_weights(wl, layer)
+        t, W = upload_layer(gr, torch, lw)
+        kp, vp = dev(kv.k_pools[layer], torch), dev(kv.v_pools[layer], torch)
+        gr.gr_decode_layer(cfg, W, kp, vp, pm.num_pages, xg, bt, cg, int(c.max()), ws=ws)
+        okp, ovp = kv.k_pools[layer].copy(), kv.v_pools[layer].copy()
+        cur = orc.decode_layer(wl, lw, okp, ovp, cur, pm.block_table, c)
+        err = rel_l2(host(xg), cur)
+        worst = max(worst, err)
+        say(f"  layer {layer}: rel_l2 {err:.3e}")
+        assert err <= tol(wl.kv_dtype), layer
+    say("worst", worst)
