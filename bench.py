@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Batched decode step throughput on one MI355X.
+
+One step = one continuous-batched decode step of the whole layer stack (every
+layer: RMSNorm, fused-dequant QKV GEMM, QK-norm/RoPE/KV append, split paged GQA
+attention, Wo, SwiGLU FFN; then the output head when the workload has one),
+replayed as one HIP graph on inputs resident in HBM.
+
+Prints one JSON line: tokens/s (B / step time), the step's algorithmic HBM
+bytes and GB/s, a roofline entry for the dominant kernel (timed live with HIP
+events recorded around its launches), and the fp64 CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "batched decode tokens/s per layer-stack + achieved HBM GB/s (% of peak), 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------ HIP events
+class Hip:
+    """hipEvent_t handles via libamdhip64 (events recorded inside the library's launches)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        assert self.L.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+
+# ------------------------------------------------------------------------ bytes
+def weight_bytes(wtype: int, n: int, k: int) -> int:
+    return n * (k // 256) * (144 if wtype == 12 else 210)
+
+
+def stage_bytes(wl, ctx, kvb_tok):
+    """Algorithmic HBM bytes per launch of each stage (one layer; head separately)."""
+    import numpy as np
+    B, H, F = wl.batch, wl.hidden, wl.ffn
+    qd, kvd = wl.q_dim, wl.kv_dim
+    t = wl.w_other
+    kv_read = int(np.sum(ctx.astype(np.int64) + 1)) * kvb_tok  # K + V of every attended token
+    pages = int(np.sum((ctx.astype(np.int64) + 16) // 16))
+    s = {
+        "qkv": weight_bytes(t, qd + 2 * kvd, H) + B * H * 4 + B * (qd + 2 * kvd) * 4,
+        "attn": kv_read + B * kvb_tok + B * (qd + 2 * kvd) * 4 + pages * 4,
+        "attn_merge": B * qd * 4,
+        "wo": weight_bytes(t, H, qd) + B * qd * 4 + 3 * B * H * 4,
+        "gate_up": 2 * weight_bytes(t, F, H) + B * H * 4 + B * F * 4,
+        "down": weight_bytes(wl.w_down, H, F) + B * F * 4 + 3 * B * H * 4,
+    }
+    head = 0
+    if wl.vocab:
+        head = weight_bytes(wl.w_head, wl.vocab, H) + B * H * 4 + B * wl.vocab * 4
+    pack = 2 * B * H * 4  # the step's first input pack
+    return s, head, pack
+
+
+def kv_bytes_per_token(wl) -> int:
+    per_elem = {0: 4.0, 1: 2.0, 2: 1.0625}[wl.kv_dtype]
+    return int(round(2 * wl.n_kv_heads * wl.head_dim * per_elem))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "continuous_quantized_decode_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, per_launch_bytes: float):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this decode path runs on a single MI355X and has no multi-GPU mode "
+              "(rows are independent; a multi-GPU run would shard them, as data-parallel replicas).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import continuous_quantized_decode_amd as gr
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    ctx = synth.ctx_lens(wl)
+    max_ctx = int(ctx.max())
+    log(f"[bench] workload {wl.name}: L={wl.n_layers} B={wl.batch} ctx mean {ctx.mean():.0f} max {max_ctx}")
+    kv = synth.kv_state(wl, ctx)
+    pm = kv.pages
+    k_dev = [up(p) for p in kv.k_pools]
+    v_dev = [up(p) for p in kv.v_pools]
+    del kv
+    host_layers = {}
+    keep = []
+    wts = []
+    for layer in range(wl.n_layers):
+        lw = synth.layer_weights(wl, layer)
+        if layer < 2:
+            host_layers[layer] = lw
+        t = {k: up(getattr(lw, k)) for k in ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo", "w_gate", "w_up",
+                                              "w_down")}
+        if lw.q_norm is not None:
+            t["q_norm"], t["k_norm"] = up(lw.q_norm), up(lw.k_norm)
+        t.update({k: getattr(lw, k) for k in ("tq", "tk", "tv", "to", "tgate", "tup", "tdown")})
+        keep.append(t)
+        wts.append(gr.layer_weights(t))
+    head_norm = head_w = logits = None
+    head_host = None
+    if wl.vocab:
+        hn, hw = synth.head_weights(wl)
+        head_host = (hn, hw)
+        head_norm, head_w = up(hn), up(hw)
+        logits = torch.empty((wl.batch, wl.vocab), dtype=torch.float32, device=dev)
+    x0_host = synth.input_x(wl)
+    x0 = up(x0_host)
+    x = torch.empty_like(x0)
+    bt, cg = up(pm.block_table), up(ctx)
+    cfg = gr.layer_cfg(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.ffn, wl.rms_eps, wl.rope_theta,
+                       wl.rope_style, wl.qk_norm, wl.kv_dtype)
+    sargs = gr.StackArgs(cfg, wts, k_dev, v_dev)
+    ws = gr.workspace(gr.decode_stack_workspace_size(cfg, wl.batch, max_ctx, wl.vocab), dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s")
+
+    def step():
+        x.copy_(x0)
+        gr.gr_decode_stack(sargs, pm.num_pages, x, bt, cg, max_ctx, head_norm, head_w, wl.w_head, wl.vocab, logits,
+                           ws=ws)
+
+    # warm eager once, then capture the step into one graph
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.time()
+    ev0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.time() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} graph replays: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+    assert torch.isfinite(x).all().item(), "non-finite decode output"
+
+    # ---- bytes
+    kvb = kv_bytes_per_token(wl)
+    sb, head_b, pack_b = stage_bytes(wl, ctx, kvb)
+    step_bytes = wl.n_layers * sum(sb.values()) + head_b + pack_b
+
+    # ---- per-stage live timing with HIP events around each stage's launches
+    hip = Hip()
+    n_ev = max(wl.n_layers, 1)
+    evb = [hip.event() for _ in range(n_ev)]
+    eve = [hip.event() for _ in range(n_ev)]
+    stages = {}
+    for si, name in enumerate(gr.STAGES):
+        if name == "head" and not wl.vocab:
+            continue
+        once = name in ("head", "pack")
+        durs = []
+        for _ in range(args.probe_reps):
+            x.copy_(x0)
+            gr.gr_decode_stack_probed(sargs, pm.num_pages, x, bt, cg, max_ctx, si, evb, eve, head_norm, head_w,
+                                      wl.w_head, wl.vocab, logits, ws=ws)
+            torch.cuda.synchronize()
+            if once:
+                durs.append(hip.elapsed_ms(evb[0], eve[0]))
+            else:
+                durs += [hip.elapsed_ms(evb[i], eve[i]) for i in range(wl.n_layers)]
+        avg_ms = float(np.mean(durs))
+        launches = 1 if once else wl.n_layers
+        per_launch = head_b if name == "head" else pack_b if name == "pack" else sb[name]
+        stages[name] = {"avg_us": round(avg_ms * 1e3, 2), "launches_per_step": launches,
+                        "us_per_step": round(avg_ms * 1e3 * launches, 1), "bytes_per_launch": int(per_launch),
+                        "gbs": round(per_launch / (avg_ms * 1e-3) / 1e9, 1)}
+    dom = max(stages, key=lambda k: stages[k]["us_per_step"])
+    d = stages[dom]
+    achieved = d["bytes_per_launch"] / (d["avg_us"] * 1e-6) / 1e9
+    kernel_names = {"attn": "attn_split_kernel", "attn_merge": "attn_merge_kernel", "pack": "pack_rows_kernel",
+                    "qkv": "gemm_kernel<12,...>", "wo": "gemm_kernel<12,...>", "gate_up": "gemm_kernel<12,2,...>",
+                    "down": f"gemm_kernel<{wl.w_down},...>", "head": f"gemm_kernel<{wl.w_head},...>"}
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": committed_traffic(dom, d["bytes_per_launch"]),
+                "kernel": kernel_names.get(dom, dom), "stage": dom,
+                "bytes_per_launch": d["bytes_per_launch"], "avg_launch_us": d["avg_us"]}
+    log("[bench] stages: " + json.dumps(stages))
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same step
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.lib()
+        k_host = [p.cpu().numpy() for p in k_dev[:2]]
+        v_host = [p.cpu().numpy() for p in v_dev[:2]]
+        layer_s = []
+        xc = x0_host
+        for layer in range(min(2, wl.n_layers)):
+            c0 = time.time()
+            xc = oracle.decode_layer(wl, host_layers[layer], k_host[layer], v_host[layer], xc, pm.block_table, ctx)
+            layer_s.append(time.time() - c0)
+        head_s = 0.0
+        sample = f"{len(layer_s)} of {wl.n_layers} layers at B={wl.batch} with the workload's contexts"
+        if wl.vocab:
+            rows = min(wl.vocab, 8192)
+            c0 = time.time()
+            oracle.output_head(xc, head_host[0], wl.rms_eps, head_host[1][:rows],
+                               wl.w_head, rows)
+            head_s = (time.time() - c0) * wl.vocab / rows
+            sample += f", plus {rows} of {wl.vocab} output-head rows"
+        est = float(np.mean(layer_s)) * wl.n_layers + head_s
+        sample += f"; scaled to the full step ({est:.1f} s)"
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        cpu = {"value": round(wl.batch / est, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": sample, "seconds_per_step": round(est, 3)}
+        log(f"[bench] oracle sample: layers {layer_s} head(scaled) {head_s:.2f} s -> {est:.2f} s/step")
+
+    tok_s = wl.batch / (ms * 1e-3)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 accumulate (bf16 hi/lo activations x exact quant integers; f16 KV operands)",
+        "data": "synthetic (seeded random GGUF blocks and KV pages)",
+        "config": {"workload": f"{wl.name}: {wl.n_layers} layers, hidden {wl.hidden}, {wl.n_q_heads}q/"
+                               f"{wl.n_kv_heads}kv heads x {wl.head_dim}, ffn {wl.ffn}, vocab {wl.vocab}, "
+                               f"B={wl.batch}, ctx {wl.ctx_kind} {wl.ctx_lo}-{wl.ctx_hi}, "
+                               f"kv {['f32', 'f16', 'q8_0'][wl.kv_dtype]}",
+                   "global_batch": wl.batch, "mean_ctx": round(float(ctx.mean()), 1), "parallelism": "none (1 GPU)"},
+        "step_bytes": int(step_bytes),
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -97,6 +97,8 @@ def _load() -> C.CDLL:
     L.gr_decode_stack.argtypes = [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _i, C.POINTER(_p), C.POINTER(_p), _i,
                                   _p, _p, _i, _p, _i, _i, _p, _p, _i, _i, _p, _p, _sz, _p]
     L.gr_decode_stack.restype = _i
+    L.gr_decode_stack_probed.argtypes = list(L.gr_decode_stack.argtypes) + [_i, C.POINTER(_p), C.POINTER(_p)]
+    L.gr_decode_stack_probed.restype = _i
     if L.gr_abi_version() != 1:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
@@ -111,7 +113,10 @@ EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_
             "gr_q6k_dequant", "gr_q8_0_dequant", "gr_gemm_workspace_size", "gr_q4k_gemm", "gr_q6k_gemm",
             "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_paged_gather_kv",
             "gr_decode_layer_workspace_size", "gr_decode_layer", "gr_output_head_workspace_size", "gr_output_head",
-            "gr_decode_stack_workspace_size", "gr_decode_stack")
+            "gr_decode_stack_workspace_size", "gr_decode_stack", "gr_decode_stack_probed")
+
+# gr_stage values
+STAGES = ("pack", "qkv", "attn", "attn_merge", "wo", "gate_up", "down", "head")
 
 
 # --------------------------------------------------------------------------- helpers
@@ -298,4 +303,22 @@ def gr_decode_stack(args: StackArgs, num_pages: int, x, block_table, ctx_lens, m
                                    _ptr(block_table), block_table.shape[1], _ptr(ctx_lens), max_ctx, b,
                                    _ptr(head_norm), _ptr(head_w), head_wtype, vocab, _ptr(logits), _ptr(ws),
                                    ws.numel(), _stream()))
+    return x
+
+
+def gr_decode_stack_probed(args: StackArgs, num_pages: int, x, block_table, ctx_lens, max_ctx: int, probe_stage: int,
+                           ev_begin: Sequence[int], ev_end: Sequence[int], head_norm=None, head_w=None,
+                           head_wtype: int = W_Q6_K, vocab: int = 0, logits=None, ws=None):
+    """gr_decode_stack plus hipEventRecord around the launches of one stage in each layer;
+    ev_begin / ev_end are raw hipEvent_t handles (ints)."""
+    b = x.shape[0]
+    if ws is None:
+        ws = workspace(decode_stack_workspace_size(args.cfg, b, max_ctx, vocab), x.device)
+    eb = (_p * len(ev_begin))(*ev_begin)
+    ee = (_p * len(ev_end))(*ev_end)
+    _check("gr_decode_stack_probed",
+           _load().gr_decode_stack_probed(C.byref(args.cfg), args.weights, args.n, args.k, args.v, num_pages, _ptr(x),
+                                          _ptr(block_table), block_table.shape[1], _ptr(ctx_lens), max_ctx, b,
+                                          _ptr(head_norm), _ptr(head_w), head_wtype, vocab, _ptr(logits), _ptr(ws),
+                                          ws.numel(), _stream(), probe_stage, eb, ee))
     return x

@@ -46,7 +46,6 @@ gr_status check_device() {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool wtype_ok(int t) { return t == GR_W_Q4_K || t == GR_W_Q6_K; }
 bool kv_ok(int t) { return t == GR_KV_F32 || t == GR_KV_F16 || t == GR_KV_Q8_0; }
-int kind_of(int wtype) { return wtype == GR_W_Q4_K ? kK32 : kK16; }
 
 // Carves a caller-provided workspace into 256-byte aligned regions; with base ==
 // nullptr it only measures.
@@ -70,53 +69,129 @@ struct Pack2 {
 };
 Pack2 carve_pack2(Carver& c, int B, int K) {
   Pack2 p;
-  p.k32.pack = c.take<u16>(actpack_frag_bytes(B, K, kK32));
-  p.k32.sums = c.take<float>(actpack_sum_bytes(B, K, kK32));
+  p.k32.pack = c.take<u16>(actpack_bytes(B, K));
   p.k32.kind = kK32;
-  p.k16.pack = c.take<u16>(actpack_frag_bytes(B, K, kK16));
-  p.k16.sums = c.take<float>(actpack_sum_bytes(B, K, kK16));
+  p.k16.pack = c.take<u16>(actpack_bytes(B, K));
   p.k16.kind = kK16;
   return p;
 }
+const PackOut kNoPack{nullptr, 0};
 
-// pack only the kinds some consumer needs
-PackOut need(const Pack2& p, bool need_k32) { return need_k32 ? p.k32 : PackOut{nullptr, nullptr, 0}; }
-PackOut need16(const Pack2& p, bool need_k16) { return need_k16 ? p.k16 : PackOut{nullptr, nullptr, 0}; }
+int nslices_of(int kind, int K) { return kind == kK32 ? K / 32 : K / 16; }
 
-// GEMM over up to three matrices sharing K and the activation, grouped by type.
-hipError_t gemm_group(const void* const* w, const int* types, const int* rows, int nmat, int K, int B,
-                      const Pack2& xp, float* y, int ldy, hipStream_t st) {
-  int row_off = 0;
+// The kinds an input must be packed in for matrices of the given types.
+struct Kinds {
+  bool k32 = false, k16 = false;
+  void add(int wtype) { (wtype == GR_W_Q4_K ? k32 : k16) = true; }
+};
+
+// GEMM epilogue parameters shared by one call of gemm_run.
+struct Epi {
+  int kind = kEpiStore;
+  float* y = nullptr;
+  int ldy = 0;
+  const float* ss = nullptr;  // RMSNorm sum of squares of the input rows (NULL: none)
+  float eps = 0.f;
+  const float* gain = nullptr;
+  PackOut out1 = kNoPack, out2 = kNoPack;
+  int out_k = 0;  // K of the packed outputs (columns of y)
+  float* ss_out = nullptr;
+  float* zero_ptr = nullptr;
+  int zero_n = 0;
+};
+
+// y (= the epilogue's destination) for up to three matrices sharing K and the input
+// pack, split into one launch per weight type (outputs stay column-contiguous).
+hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int nmat, int K, int B,
+                    const Pack2& xin, const Epi& ep, hipStream_t st) {
+  int col = 0;
   int i = 0;
-  hipError_t e = hipSuccess;
+  bool zeroed = false;
   while (i < nmat) {
-    // maximal run of consecutive matrices of one type (outputs stay contiguous)
-    int j = i;
-    int run_rows[3];
-    const uint8_t* run_w[3];
-    int n = 0;
+    GemmArgs a{};
+    int j = i, n = 0, tiles = 0;
     while (j < nmat && types[j] == types[i]) {
-      run_rows[n] = rows[j];
-      run_w[n] = (const uint8_t*)w[j];
+      a.w[n] = (const uint8_t*)w[j];
+      a.seg_rows[n] = rows[j];
+      a.seg_tile_off[n] = tiles;
+      a.seg_col_off[n] = col;
+      tiles += (rows[j] + 15) / 16;
+      col += rows[j];
       ++n;
       ++j;
     }
-    const GemmPlan pl = plan_gemm(types[i], run_rows, n, K, B, 64);
-    const PackOut& pk = xp.of(types[i]);
-    e = launch_gemm(types[i], pl, run_w, run_rows, n, K, B, pk.pack, pk.sums, y + row_off, ldy, kStoreAtomic, st);
+    a.seg_tile_off[n] = tiles;
+    a.nseg = n;
+    const int wt = types[i];
+    a.nsb = K / kQK;
+    a.row_bytes = (size_t)(K / kQK) * (wt == GR_W_Q4_K ? kQ4KBytes : kQ6KBytes);
+    const PackOut& pin = xin.of(wt);
+    a.xpack = pin.pack;
+    a.nslices = nslices_of(pin.kind, K);
+    a.ss = ep.ss;
+    a.inv_k = 1.0f / (float)K;
+    a.eps = ep.eps;
+    a.B = B;
+    a.epi = ep.kind;
+    a.y = ep.y;
+    a.ldy = ep.ldy;
+    a.gain = ep.gain;
+    a.pack_out = ep.out1.pack;
+    a.pack_kind = ep.out1.kind;
+    a.pack_nslices = nslices_of(ep.out1.kind, ep.out_k);
+    a.pack_out2 = ep.out2.pack;
+    a.pack_kind2 = ep.out2.kind;
+    a.pack_nslices2 = nslices_of(ep.out2.kind, ep.out_k);
+    a.ss_out = ep.ss_out;
+    if (!zeroed) {
+      a.zero_ptr = ep.zero_ptr;
+      a.zero_n = ep.zero_n;
+      zeroed = true;
+    }
+    const GemmPlan pl = plan_gemm(wt, tiles, K, B, false);
+    a.sb_per_wave = pl.sb_per_wave;
+    hipError_t e = launch_gemm(wt, pl, a, st);
     if (e != hipSuccess) return e;
-    for (int q = i; q < j; ++q) row_off += rows[q];
     i = j;
   }
-  return e;
+  return hipSuccess;
+}
+
+// The SwiGLU GEMM: gate and up (same type, F rows each) paired per 16-column tile.
+hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, int B, const Pack2& xin,
+                       const float* ss, float eps, PackOut out, float* zero_ptr, int zero_n, hipStream_t st) {
+  GemmArgs a{};
+  a.w[0] = (const uint8_t*)wg;
+  a.w[1] = (const uint8_t*)wu;
+  a.seg_rows[0] = a.seg_rows[1] = F;
+  a.nseg = 2;
+  const int tiles = (F + 15) / 16;
+  a.nsb = K / kQK;
+  a.row_bytes = (size_t)(K / kQK) * (wtype == GR_W_Q4_K ? kQ4KBytes : kQ6KBytes);
+  const PackOut& pin = xin.of(wtype);
+  a.xpack = pin.pack;
+  a.nslices = nslices_of(pin.kind, K);
+  a.ss = ss;
+  a.inv_k = 1.0f / (float)K;
+  a.eps = eps;
+  a.B = B;
+  a.epi = kEpiSwiGLU;
+  a.pack_out = out.pack;
+  a.pack_kind = out.kind;
+  a.pack_nslices = nslices_of(out.kind, F);
+  a.zero_ptr = zero_ptr;
+  a.zero_n = zero_n;
+  const GemmPlan pl = plan_gemm(wtype, tiles, K, B, true);
+  a.sb_per_wave = pl.sb_per_wave;
+  return launch_gemm(wtype, pl, a, st);
 }
 
 struct LayerBufs {
-  Pack2 xp;   // residual stream, normalized (attention / FFN input)
-  Pack2 op;   // attention output (Wo input)
-  Pack2 ap;   // SwiGLU activation (down input)
+  Pack2 xp;  // residual stream times the next RMSNorm gain (QKV / gate-up / head input)
+  Pack2 op;  // attention output (Wo input)
+  Pack2 ap;  // SwiGLU activation (down input)
   float* qkv;
-  float* gu;
+  float *ss_attn, *ss_ffn;
   float *o_part, *m_part, *l_part;
 };
 
@@ -127,7 +202,8 @@ LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan&
   L.op = carve_pack2(c, B, qd);
   L.ap = carve_pack2(c, B, cfg->ffn);
   L.qkv = c.take<float>((size_t)B * (qd + 2 * kvd) * 4);
-  L.gu = c.take<float>((size_t)B * 2 * cfg->ffn * 4);
+  L.ss_attn = c.take<float>((size_t)B * 4);
+  L.ss_ffn = c.take<float>((size_t)B * 4);
   const size_t units = (size_t)B * cfg->n_q_heads * ap.max_splits;
   L.o_part = c.take<float>(units * cfg->head_dim * 4);
   L.m_part = c.take<float>(units * 4);
@@ -158,6 +234,7 @@ gr_status check_layer_w(const gr_layer_cfg* c, const gr_layer_weights* w) {
   const int ts[7] = {w->tq, w->tk, w->tv, w->to, w->tgate, w->tup, w->tdown};
   for (int t : ts)
     if (!wtype_ok(t)) return GR_ERR_DTYPE;
+  if (w->tgate != w->tup) return GR_ERR_DTYPE;  // gate and up are streamed as pairs
   const void* ps[7] = {w->wq, w->wk, w->wv, w->wo, w->w_gate, w->w_up, w->w_down};
   for (const void* p : ps)
     if (!aligned(p, 16)) return GR_ERR_ALIGN;
@@ -169,29 +246,69 @@ AttnPlan layer_attn_plan(int B, const gr_layer_cfg* c, int max_ctx) {
   return plan_attn(B, c->n_kv_heads, max_ctx + 1);
 }
 
-// The launch sequence of one decode layer (arguments already validated).
+// Optional timing probe: events recorded on the launch stream just before and just
+// after the launches of one stage.
+struct Probe {
+  int stage = -1;
+  int layer = 0;
+  void* const* ev_begin = nullptr;
+  void* const* ev_end = nullptr;
+};
+
+struct ProbeScope {
+  const Probe* p;
+  bool on;
+  hipStream_t st;
+  ProbeScope(const Probe* pr, int stage, hipStream_t s) : p(pr), on(pr && pr->stage == stage), st(s) {
+    if (on) (void)hipEventRecord((hipEvent_t)p->ev_begin[p->layer], st);
+  }
+  ~ProbeScope() {
+    if (on) (void)hipEventRecord((hipEvent_t)p->ev_end[p->layer], st);
+  }
+};
+
+Kinds qkv_kinds(const gr_layer_weights* w) {
+  Kinds k;
+  k.add(w->tq);
+  k.add(w->tk);
+  k.add(w->tv);
+  return k;
+}
+
+// Pack of the layer input: x * attn_norm and its sum of squares.
+gr_status run_input_pack(const float* x, int B, int H, const float* gain, Kinds k, const Pack2& xp, float* ss,
+                         hipStream_t st, const Probe* probe) {
+  ProbeScope ps(probe, GR_STAGE_PACK, st);
+  return check_launch(launch_pack_rows(x, H, B, H, gain, k.k32 ? xp.k32 : kNoPack, k.k16 ? xp.k16 : kNoPack, ss, st));
+}
+
+// The launch sequence of one decode layer (arguments already validated).  On entry
+// L.xp holds x * attn_norm and L.ss_attn its per-row sum of squares.  On exit x is
+// the layer output and, when next_gain is set, L.xp / L.ss_attn hold x * next_gain
+// packed in the kinds `next`.
 gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pages, void* v_pages, float* x,
                     const int32_t* bt, int max_blocks, const int32_t* ctx, int B, const AttnPlan& apl,
-                    const LayerBufs& L, hipStream_t st) {
+                    const LayerBufs& L, const float* next_gain, Kinds next, hipStream_t st, const Probe* probe) {
   const int H = c->hidden, D = c->head_dim, qd = c->n_q_heads * D, kvd = c->n_kv_heads * D, F = c->ffn;
   hipError_t e;
-  // 1. attention RMSNorm -> actpack; zero the q/k/v accumulator
+  // 1. q, k, v = (W (x * g)) / rms(x); zero the FFN-norm accumulator for step 4
   {
-    const bool k32 = w->tq == GR_W_Q4_K || w->tk == GR_W_Q4_K || w->tv == GR_W_Q4_K;
-    const bool k16 = w->tq == GR_W_Q6_K || w->tk == GR_W_Q6_K || w->tv == GR_W_Q6_K;
-    e = launch_pack_rows(x, H, B, H, w->attn_norm, c->rms_eps, need(L.xp, k32), need16(L.xp, k16), L.qkv,
-                         (size_t)B * (qd + 2 * kvd), st);
-    if (e != hipSuccess) return check_launch(e);
-  }
-  // 2. q, k, v = W xn
-  {
+    ProbeScope ps(probe, GR_STAGE_QKV, st);
     const void* ws[3] = {w->wq, w->wk, w->wv};
     const int ts[3] = {w->tq, w->tk, w->tv};
     const int rs[3] = {qd, kvd, kvd};
-    e = gemm_group(ws, ts, rs, 3, H, B, L.xp, L.qkv, qd + 2 * kvd, st);
+    Epi ep;
+    ep.kind = kEpiStore;
+    ep.y = L.qkv;
+    ep.ldy = qd + 2 * kvd;
+    ep.ss = L.ss_attn;
+    ep.eps = c->rms_eps;
+    ep.zero_ptr = L.ss_ffn;
+    ep.zero_n = B;
+    e = gemm_run(ws, ts, rs, 3, H, B, L.xp, ep, st);
     if (e != hipSuccess) return check_launch(e);
   }
-  // 3. QK-norm, RoPE, KV append and split attention; 4. merge + pack for Wo
+  // 2. QK-norm, RoPE, KV append and split attention
   AttnParams ap{};
   ap.B = B;
   ap.n_q_heads = c->n_q_heads;
@@ -218,62 +335,80 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   ap.o_part = L.o_part;
   ap.m_part = L.m_part;
   ap.l_part = L.l_part;
-  e = launch_attn_split(c->kv_dtype, true, ap, st);
-  if (e != hipSuccess) return check_launch(e);
   {
+    ProbeScope ps(probe, GR_STAGE_ATTN, st);
+    e = launch_attn_split(c->kv_dtype, true, ap, st);
+  }
+  if (e != hipSuccess) return check_launch(e);
+  // 3. log-sum-exp merge -> Wo input pack
+  {
+    ProbeScope ps(probe, GR_STAGE_ATTN_MERGE, st);
     const PackOut& op = L.op.of(w->to);
-    e = launch_attn_merge(ap, nullptr, op.pack, op.sums, op.kind, op.kind == kK32 ? qd / 32 : qd / 16, 1, st);
+    e = launch_attn_merge(ap, nullptr, op.pack, op.kind, nslices_of(op.kind, qd), 1, st);
     if (e != hipSuccess) return check_launch(e);
   }
-  // 5. x += Wo o
+  // 4. x += Wo o; pack x * ffn_norm and its sum of squares for the gate/up GEMM
   {
+    ProbeScope ps(probe, GR_STAGE_WO, st);
     const void* ws[1] = {w->wo};
     const int ts[1] = {w->to};
     const int rs[1] = {H};
-    e = gemm_group(ws, ts, rs, 1, qd, B, L.op, x, H, st);
+    Epi ep;
+    ep.kind = kEpiResidual;
+    ep.y = x;
+    ep.ldy = H;
+    ep.gain = w->ffn_norm;
+    ep.out1 = L.xp.of(w->tgate);
+    ep.out_k = H;
+    ep.ss_out = L.ss_ffn;
+    e = gemm_run(ws, ts, rs, 1, qd, B, L.op, ep, st);
     if (e != hipSuccess) return check_launch(e);
   }
-  // 6. FFN RMSNorm -> actpack; zero the gate/up accumulator
+  // 5. a = silu(gate) * up (inputs divided by rms) -> down input pack; zero the
+  //    attention-norm accumulator for step 6
   {
-    const bool k32 = w->tgate == GR_W_Q4_K || w->tup == GR_W_Q4_K;
-    const bool k16 = w->tgate == GR_W_Q6_K || w->tup == GR_W_Q6_K;
-    e = launch_pack_rows(x, H, B, H, w->ffn_norm, c->rms_eps, need(L.xp, k32), need16(L.xp, k16), L.gu,
-                         (size_t)B * 2 * F, st);
+    ProbeScope ps(probe, GR_STAGE_GATE_UP, st);
+    e = gemm_swiglu(w->w_gate, w->w_up, w->tgate, F, H, B, L.xp, L.ss_ffn, c->rms_eps, L.ap.of(w->tdown),
+                    L.ss_attn, B, st);
     if (e != hipSuccess) return check_launch(e);
   }
-  // 7. gate, up
+  // 6. x += W_down a; pack x * next_gain for the next consumer
   {
-    const void* ws[2] = {w->w_gate, w->w_up};
-    const int ts[2] = {w->tgate, w->tup};
-    const int rs[2] = {F, F};
-    e = gemm_group(ws, ts, rs, 2, H, B, L.xp, L.gu, 2 * F, st);
-    if (e != hipSuccess) return check_launch(e);
-  }
-  // 8. a = silu(gate) * up -> actpack
-  e = launch_swiglu_pack(L.gu, B, F, L.ap.of(w->tdown), st);
-  if (e != hipSuccess) return check_launch(e);
-  // 9. x += W_down a
-  {
+    ProbeScope ps(probe, GR_STAGE_DOWN, st);
     const void* ws[1] = {w->w_down};
     const int ts[1] = {w->tdown};
     const int rs[1] = {H};
-    e = gemm_group(ws, ts, rs, 1, F, B, L.ap, x, H, st);
+    Epi ep;
+    ep.kind = kEpiResidual;
+    ep.y = x;
+    ep.ldy = H;
+    if (next_gain) {
+      ep.gain = next_gain;
+      ep.out1 = next.k32 ? L.xp.k32 : kNoPack;
+      ep.out2 = next.k16 ? L.xp.k16 : kNoPack;
+      ep.out_k = H;
+      ep.ss_out = L.ss_attn;
+    }
+    e = gemm_run(ws, ts, rs, 1, F, B, L.ap, ep, st);
     if (e != hipSuccess) return check_launch(e);
   }
   return GR_OK;
 }
 
-gr_status run_head(const float* x, const float* norm, float eps, const void* w, int wtype, float* logits, int B,
-                   int H, int vocab, const Pack2& xp, hipStream_t st) {
-  const PackOut& pk = xp.of(wtype);
-  hipError_t e = launch_pack_rows(x, H, B, H, norm, eps, pk, PackOut{nullptr, nullptr, 0}, logits,
-                                  (size_t)B * vocab, st);
-  if (e != hipSuccess) return check_launch(e);
+// Output head on a packed input (x * norm in xp, sum of squares in ss).
+gr_status run_head(const void* w, int wtype, float* logits, int B, int H, int vocab, float eps, const Pack2& xp,
+                   const float* ss, hipStream_t st, const Probe* probe) {
+  ProbeScope ps(probe, GR_STAGE_HEAD, st);
   const void* ws[1] = {w};
   const int ts[1] = {wtype};
   const int rs[1] = {vocab};
-  e = gemm_group(ws, ts, rs, 1, H, B, xp, logits, vocab, st);
-  return check_launch(e);
+  Epi ep;
+  ep.kind = kEpiStore;
+  ep.y = logits;
+  ep.ldy = vocab;
+  ep.ss = ss;
+  ep.eps = eps;
+  return check_launch(gemm_run(ws, ts, rs, 1, H, B, xp, ep, st));
 }
 
 }  // namespace
@@ -346,13 +481,16 @@ static gr_status gemm_api(int wtype, const void* w, const float* x, float* y, in
   Carver c(ws);
   const Pack2 xp = carve_pack2(c, B, K);
   hipStream_t st = (hipStream_t)stream;
-  const PackOut& pk = xp.of(wtype);
-  hipError_t e = launch_pack_rows(x, K, B, K, nullptr, 0.f, pk, PackOut{nullptr, nullptr, 0}, y, (size_t)B * N, st);
+  hipError_t e = launch_pack_rows(x, K, B, K, nullptr, xp.of(wtype), kNoPack, nullptr, st);
   if (e != hipSuccess) return check_launch(e);
   const void* ws1[1] = {w};
   const int ts[1] = {wtype};
   const int rs[1] = {N};
-  return check_launch(gemm_group(ws1, ts, rs, 1, K, B, xp, y, N, st));
+  Epi ep;
+  ep.kind = kEpiStore;
+  ep.y = y;
+  ep.ldy = N;
+  return check_launch(gemm_run(ws1, ts, rs, 1, K, B, xp, ep, st));
 }
 
 gr_status gr_q4k_gemm(const void* w, const float* x, float* y, int B, int N, int K, void* ws, size_t wsb, void* s) {
@@ -424,7 +562,7 @@ gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* 
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = launch_attn_split(m->kv_dtype, false, ap, st);
   if (e != hipSuccess) return check_launch(e);
-  return check_launch(launch_attn_merge(ap, out, nullptr, nullptr, 0, 0, 0, st));
+  return check_launch(launch_attn_merge(ap, out, nullptr, 0, 0, 0, st));
 }
 
 gr_status gr_paged_gather_kv(const void* pages, int is_v, const int32_t* block_table, const int32_t* ctx_lens, int B,
@@ -478,7 +616,10 @@ gr_status gr_decode_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void
   const AttnPlan apl = layer_attn_plan(B, c, max_ctx);
   Carver cv(ws);
   const LayerBufs L = carve_layer(cv, c, B, apl);
-  return run_layer(c, w, k_pages, v_pages, x, bt, max_blocks, ctx, B, apl, L, (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  s = run_input_pack(x, B, c->hidden, w->attn_norm, qkv_kinds(w), L.xp, L.ss_attn, st, nullptr);
+  if (s != GR_OK) return s;
+  return run_layer(c, w, k_pages, v_pages, x, bt, max_blocks, ctx, B, apl, L, nullptr, Kinds{}, st, nullptr);
 }
 
 size_t gr_output_head_workspace_size(int B, int hidden, int vocab) {
@@ -486,6 +627,7 @@ size_t gr_output_head_workspace_size(int B, int hidden, int vocab) {
   (void)vocab;
   Carver c(nullptr);
   carve_pack2(c, B, hidden);
+  c.take<float>((size_t)B * 4);
   return c.off + 256;
 }
 
@@ -502,7 +644,13 @@ gr_status gr_output_head(const float* x, const float* norm, float eps, const voi
   if (s != GR_OK) return s;
   Carver c(ws);
   const Pack2 xp = carve_pack2(c, B, hidden);
-  return run_head(x, norm, eps, w, wtype, logits, B, hidden, vocab, xp, (hipStream_t)stream);
+  float* ss = c.take<float>((size_t)B * 4);
+  hipStream_t st = (hipStream_t)stream;
+  Kinds k;
+  k.add(wtype);
+  s = run_input_pack(x, B, hidden, norm, k, xp, ss, st, nullptr);
+  if (s != GR_OK) return s;
+  return run_head(w, wtype, logits, B, hidden, vocab, eps, xp, ss, st, nullptr);
 }
 
 size_t gr_decode_stack_workspace_size(const gr_layer_cfg* c, int B, int max_ctx, int vocab) {
@@ -510,11 +658,11 @@ size_t gr_decode_stack_workspace_size(const gr_layer_cfg* c, int B, int max_ctx,
   return gr_decode_layer_workspace_size(c, B, max_ctx);
 }
 
-gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers,
-                          void* const* k_pages, void* const* v_pages, int num_pages, float* x, const int32_t* bt,
-                          int max_blocks, const int32_t* ctx, int max_ctx, int B, const float* head_norm,
-                          const void* head_w, int head_wtype, int vocab, float* logits, void* ws, size_t ws_bytes,
-                          void* stream) {
+static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers,
+                                   void* const* k_pages, void* const* v_pages, int num_pages, float* x,
+                                   const int32_t* bt, int max_blocks, const int32_t* ctx, int max_ctx, int B,
+                                   const float* head_norm, const void* head_w, int head_wtype, int vocab,
+                                   float* logits, void* ws, size_t ws_bytes, void* stream, Probe* probe) {
   if (n_layers < 0) return GR_ERR_SHAPE;
   if (n_layers > 0 && (!weights || !k_pages || !v_pages)) return GR_ERR_NULL;
   for (int l = 0; l < n_layers; ++l) {
@@ -532,6 +680,10 @@ gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
     gr_status s = check_layer_cfg(c);
     if (s != GR_OK) return s;
   }
+  if (probe && probe->stage >= 0) {
+    if (!probe->ev_begin || !probe->ev_end) return GR_ERR_NULL;
+    if (probe->stage > GR_STAGE_HEAD) return GR_ERR_SHAPE;
+  }
   if (B == 0) return GR_OK;
   if (!ws || ws_bytes < gr_decode_stack_workspace_size(c, B, max_ctx, vocab) || !aligned(ws, 256))
     return GR_ERR_WORKSPACE;
@@ -541,12 +693,56 @@ gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
   Carver cv(ws);
   const LayerBufs L = carve_layer(cv, c, B, apl);
   hipStream_t st = (hipStream_t)stream;
+  if (probe) probe->layer = 0;
+  if (n_layers > 0) {
+    s = run_input_pack(x, B, c->hidden, weights[0].attn_norm, qkv_kinds(&weights[0]), L.xp, L.ss_attn, st, probe);
+  } else if (head_w) {
+    Kinds k;
+    k.add(head_wtype);
+    s = run_input_pack(x, B, c->hidden, head_norm, k, L.xp, L.ss_attn, st, probe);
+  }
+  if (s != GR_OK) return s;
   for (int l = 0; l < n_layers; ++l) {
-    s = run_layer(c, &weights[l], k_pages[l], v_pages[l], x, bt, max_blocks, ctx, B, apl, L, st);
+    if (probe) probe->layer = l;
+    const float* next_gain = nullptr;
+    Kinds next;
+    if (l + 1 < n_layers) {
+      next_gain = weights[l + 1].attn_norm;
+      next = qkv_kinds(&weights[l + 1]);
+    } else if (head_w) {
+      next_gain = head_norm;
+      next.add(head_wtype);
+    }
+    s = run_layer(c, &weights[l], k_pages[l], v_pages[l], x, bt, max_blocks, ctx, B, apl, L, next_gain, next, st,
+                  probe);
     if (s != GR_OK) return s;
   }
-  if (head_w) return run_head(x, head_norm, c->rms_eps, head_w, head_wtype, logits, B, c->hidden, vocab, L.xp, st);
+  if (probe) probe->layer = 0;
+  if (head_w) return run_head(head_w, head_wtype, logits, B, c->hidden, vocab, c->rms_eps, L.xp, L.ss_attn, st, probe);
   return GR_OK;
+}
+
+gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers,
+                          void* const* k_pages, void* const* v_pages, int num_pages, float* x, const int32_t* bt,
+                          int max_blocks, const int32_t* ctx, int max_ctx, int B, const float* head_norm,
+                          const void* head_w, int head_wtype, int vocab, float* logits, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return decode_stack_impl(c, weights, n_layers, k_pages, v_pages, num_pages, x, bt, max_blocks, ctx, max_ctx, B,
+                           head_norm, head_w, head_wtype, vocab, logits, ws, ws_bytes, stream, nullptr);
+}
+
+gr_status gr_decode_stack_probed(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers,
+                                 void* const* k_pages, void* const* v_pages, int num_pages, float* x,
+                                 const int32_t* bt, int max_blocks, const int32_t* ctx, int max_ctx, int B,
+                                 const float* head_norm, const void* head_w, int head_wtype, int vocab,
+                                 float* logits, void* ws, size_t ws_bytes, void* stream, int probe_stage,
+                                 void* const* ev_begin, void* const* ev_end) {
+  Probe pr;
+  pr.stage = probe_stage;
+  pr.ev_begin = ev_begin;
+  pr.ev_end = ev_end;
+  return decode_stack_impl(c, weights, n_layers, k_pages, v_pages, num_pages, x, bt, max_blocks, ctx, max_ctx, B,
+                           head_norm, head_w, head_wtype, vocab, logits, ws, ws_bytes, stream, &pr);
 }
 
 }  // extern "C"

@@ -225,16 +225,8 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
 
   const uint8_t* kbase = (const uint8_t*)p.k_pages + (size_t)g * HB;
   const uint8_t* vbase = (const uint8_t*)p.v_pages + (size_t)g * HB;
-  PageRegs<KVDT, D> cur, nxt;
-  {
-    const size_t pg = (size_t)bt[pg0];
-    load_page<KVDT, D>(cur, kbase + pg * page_bytes, vbase + pg * page_bytes, lane);
-  }
-  for (int j = pg0; j < pg1; ++j) {
-    if (j + 1 < pg1) {
-      const size_t pg = (size_t)bt[j + 1];
-      load_page<KVDT, D>(nxt, kbase + pg * page_bytes, vbase + pg * page_bytes, lane);
-    }
+  // One page: scores, online softmax, P transpose, PV.
+  auto page = [&](PageRegs<KVDT, D>& cur, int j) {
     if (FUSED && owner && j == new_page) patch_page<KVDT, D>(cur, s_knew, s_vnew, new_slot, lane);
     const int valid = min(kPage, n_tok - j * kPage);
     if constexpr (KVDT != KV_Q8_T) {
@@ -338,8 +330,18 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
       }
     }
     __syncthreads();
-    if (j + 1 < pg1) cur = nxt;
-  }
+  };
+
+  // Two-buffer pipeline over the split's pages: page j+1 is in flight while page j is
+  // processed.
+  PageRegs<KVDT, D> r0, r1;
+  pipeline2(
+      pg0, pg1, r0, r1,
+      [&](PageRegs<KVDT, D>& r, int j) {
+        const size_t pg = (size_t)bt[j];
+        load_page<KVDT, D>(r, kbase + pg * page_bytes, vbase + pg * page_bytes, lane);
+      },
+      [&](PageRegs<KVDT, D>& cur, int j, bool) { page(cur, j); });
 
   // ---- partial results -------------------------------------------------------------
   if (2 * kg < R) {
@@ -359,31 +361,64 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
 }
 
 // ----------------------------------------------------------------------- merge
-// Per (row b, query head h): M = max m_s, L = sum l_s 2^(m_s - M),
-// o = sum o_s 2^(m_s - M) / L.  Writes f32 out [B][Hq][D] and/or the activation pack
-// of the output projection (K = Hq*D, kind `kind`).
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams p, float* out, uint16_t* pack, float* pack_sums,
-                                                        int kind, int nslices, int fused) {
-  const int lane = threadIdx.x;
+// Per (row b, query head h): M = max_s m_s, L = sum_s l_s 2^(m_s - M),
+// o = sum_s o_s 2^(m_s - M) / L (the partials are in the log2 domain).  Writes f32
+// out [B][Hq][D] and/or the actpack of the output projection (K = Hq*D, `kind`).
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxSplits = 1024;
+
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p, float* out, uint16_t* pack,
+                                                                   int kind, int nslices, int fused) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x;
   const int h = bh % p.n_q_heads, b = bh / p.n_q_heads;
   const int D = p.head_dim;
   const int ctx = p.ctx_lens[b];
   const int n_tok = fused ? ctx + 1 : ctx;
   const int n_pages = (n_tok + kPage - 1) / kPage;
-  const int S = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
+  const int S = min((n_pages + p.pages_per_split - 1) / p.pages_per_split, p.max_splits);
   const size_t base = ((size_t)b * p.n_q_heads + h) * p.max_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, p.m_part[base + s]);
+  __shared__ float s_w[kMergeMaxSplits];
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ float s_acc[kMergeThreads / 64][128];
+
+  float mx = -INFINITY;
+  for (int s = tid; s < S; s += kMergeThreads) mx = fmaxf(mx, p.m_part[base + s]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  float M = s_red[0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
+  __syncthreads();
+  float lsum = 0.f;
+  for (int s = tid; s < S; s += kMergeThreads) {
+    const float e = exp2f(p.m_part[base + s] - M);
+    s_w[s] = e;
+    lsum += p.l_part[base + s] * e;
+  }
+  lsum = wave_sum(lsum);
+  if (lane == 0) s_red[wave] = lsum;
+  __syncthreads();
   float L = 0.f;
-  for (int s = 0; s < S; ++s) L += p.l_part[base + s] * exp2f(p.m_part[base + s] - M);
+  for (int w = 0; w < kMergeThreads / 64; ++w) L += s_red[w];
   const float invL = 1.0f / L;
-  for (int d = lane; d < D; d += 64) {
+  // partial sums over splits s = wave, wave + 4, ... for dims lane, lane + 64
+  for (int d0 = 0; d0 < D; d0 += 64) {
+    const int d = d0 + lane;
     float acc = 0.f;
-    for (int s = 0; s < S; ++s) acc += p.o_part[(base + s) * D + d] * exp2f(p.m_part[base + s] - M);
-    const float v = acc * invL;
-    if (out) out[((size_t)b * p.n_q_heads + h) * D + d] = v;
-    if (pack) actpack_put_lane(pack, pack_sums, kind, nslices, b, h * D + d, v, lane);
+    for (int s = wave; s < S; s += kMergeThreads / 64) acc = __builtin_fmaf(p.o_part[(base + s) * D + d], s_w[s], acc);
+    s_acc[wave][d] = acc;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int d0 = 0; d0 < D; d0 += 64) {
+      const int d = d0 + lane;
+      float v = 0.f;
+      for (int w = 0; w < kMergeThreads / 64; ++w) v += s_acc[w][d];
+      v *= invL;
+      if (out) out[((size_t)b * p.n_q_heads + h) * D + d] = v;
+      if (pack) actpack_put(pack, kind, nslices, b, h * D + d, v);
+    }
   }
 }
 
@@ -396,6 +431,7 @@ AttnPlan plan_attn(int B, int n_kv_heads, int max_ctx_tokens) {
   const long long units = (long long)B * n_kv_heads * (max_pages > 0 ? max_pages : 1);
   int pps = (int)((units + 4095) / 4096);
   if (pps < 4) pps = 4;
+  while ((max_pages + pps - 1) / pps > 1024) ++pps;  // the merge handles up to 1024 splits
   AttnPlan pl;
   pl.pages_per_split = pps;
   pl.max_splits = max_pages > 0 ? (max_pages + pps - 1) / pps : 1;
@@ -433,10 +469,10 @@ hipError_t launch_attn_split(int kv_dtype, bool fused, const AttnParams& p, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, float* pack_sums, int kind,
-                             int nslices, int fused, hipStream_t st) {
-  attn_merge_kernel<<<dim3((unsigned)(p.B * p.n_q_heads)), 64, 0, st>>>(p, out, pack, pack_sums, kind, nslices,
-                                                                         fused);
+hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, int kind, int nslices, int fused,
+                             hipStream_t st) {
+  attn_merge_kernel<<<dim3((unsigned)(p.B * p.n_q_heads)), kMergeThreads, 0, st>>>(p, out, pack, kind, nslices,
+                                                                                    fused);
   return hipGetLastError();
 }
 

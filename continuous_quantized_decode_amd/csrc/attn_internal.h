@@ -40,7 +40,7 @@ struct AttnPlan {
 AttnPlan plan_attn(int B, int n_kv_heads, int max_ctx_tokens);
 size_t attn_partial_floats(int B, int n_q_heads, int head_dim, const AttnPlan& pl);
 hipError_t launch_attn_split(int kv_dtype, bool fused, const AttnParams& p, hipStream_t st);
-hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, float* pack_sums, int kind,
-                             int nslices, int fused, hipStream_t st);
+hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, int kind, int nslices, int fused,
+                             hipStream_t st);
 
 }  // namespace gr

@@ -4,264 +4,487 @@
 // the weights (Leone, intro: active decode rows share matrix operations).  Every
 // weight byte is read from HBM exactly once per call.
 //
-// Design (gfx950):
-//  * One wave owns NT tiles of 16 weight rows and a range of super-blocks (split-K).
+// Layout of the work (gfx950):
+//  * One workgroup per output tile of 16 weight rows (SwiGLU: 16 gate rows + the 16
+//    up rows of the same FFN columns) and all B rows; its waves split K into
+//    contiguous super-block ranges and reduce their partial sums through LDS, so the
+//    epilogue sees complete outputs (no atomics, no second pass).
 //  * Quants are expanded in registers into exact bf16 integers (128 + q via an OR
 //    with the exponent bits) and fed as the B operand of v_mfma_f32_16x16x32_bf16
 //    (Q4_K: one 32-weight sub-block per MFMA) or v_mfma_f32_16x16x16_bf16 (Q6_K: one
-//    16-weight sub-block per MFMA).  The A operand is the activation tile in bf16
-//    hi/lo form (actpack), so products and sums are exact up to fp32 accumulation.
-//  * Each MFMA result is scaled per (row, sub-block) in fp32:
-//      Q4_K: acc += d*sc*D - (128*d*sc + dmin*m) * S
-//      Q6_K: acc += d*sc*D - 160*d*sc * S
-//    where S is the sub-block sum of the activation part (precomputed in actpack).
-//  * Weight loads for super-block sb+1 are issued before the MFMAs of sb.
+//    16-weight sub-block).  The A operand is the activation tile in bf16 hi/lo rows
+//    (actpack), so the products are exact and sums are fp32.
+//  * A second MFMA of the same A against a ones vector gives, in the same output
+//    layout, the activation sums S of the sub-block, so each MFMA result is scaled in
+//    fp32 without any extra data:
+//      Q4_K: acc += d*sc * D - (128*d*sc + dmin*m) * S
+//      Q6_K: acc += d*sc * (D - 160 * S)
+//  * The weights and activation fragments of super-block sb+1 are loaded before the
+//    MFMAs of sb.
 #include "gr_internal.h"
 #include "quant.h"
 
 namespace gr {
 
-template <int NT, int BTN>
-__global__ __launch_bounds__(256) void q4k_gemm_kernel(GemmParams p) {
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= p.total_items) return;
-  const int split = item / p.total_groups;
-  const int gidx = item - split * p.total_groups;
-  int s = 0;
-  while (s + 1 < p.nseg && gidx >= p.seg[s + 1].group_off) ++s;
-  const GemmSeg sg = p.seg[s];
-  const int group = gidx - sg.group_off;
-  const int col = lane & 15, kg = lane >> 4;
+constexpr u32 kOnesBf16 = 0x3F803F80u;  // two bf16 1.0
 
-  const uint8_t* rowp[NT];
-  int nloc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    nloc[t] = (group * NT + t) * 16 + col;
-    rowp[t] = sg.w + (size_t)min(nloc[t], sg.rows - 1) * p.row_bytes;
-  }
-  const int sb0 = split * p.sb_per_split;
-  const int sb1 = min(p.nsb, sb0 + p.sb_per_split);
+// ---------------------------------------------------------------------------------
+// LDS staging of weights
+//
+// A wave streams the 16 rows of its tile one super-block at a time into a two-slot
+// LDS ring with direct global->LDS loads (lane i of a load lands at slot + size*i),
+// so every load instruction reads contiguous bytes; the MFMA operands are then read
+// from LDS.  Activation fragments (already contiguous per instruction) go to
+// registers.  An explicit vmcnt wait guards each slot before it is read.
 
-  f32x4 acc[NT][BTN];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int b = 0; b < BTN; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
-  const u32x4* xp = (const u32x4*)p.xpack;
-  const f32x4* xs = (const f32x4*)p.xsum;
+constexpr int kQ4Stage = 16 * kQ4KBytes;  // 2304 B: 16 rows x one super-block
+constexpr int kQ6Row = 212;                // 53 dwords per row slot
+constexpr int kQ6Stage = 16 * kQ6Row;      // 3392 B
+constexpr int kQ4LoadInstr = 3;            // 144 chunks of 16 B
+constexpr int kQ6LoadInstr = 14;           // 16 x 53 dword slots
 
-  Q4Regs cur[NT], nxt[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) q4_load(cur[t], rowp[t] + (size_t)sb0 * kQ4KBytes, kg);
-
-  for (int sb = sb0; sb < sb1; ++sb) {
-    if (sb + 1 < sb1) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) q4_load(nxt[t], rowp[t] + (size_t)(sb + 1) * kQ4KBytes, kg);
-    }
-    float sd[NT][8], mm[NT][8];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      q4_scales(cur[t].hdr, sd[t], mm[t]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mm[t][j] = __builtin_fmaf(128.0f, sd[t][j], mm[t][j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int slice = sb * 8 + j;
-      u32x4 a[BTN];
-      f32x4 ssum[BTN];
-#pragma unroll
-      for (int b = 0; b < BTN; ++b) {
-        a[b] = xp[((size_t)b * p.nslices + slice) * 64 + lane];
-        ssum[b] = xs[((size_t)b * p.nslices + slice) * 4 + kg];
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4 bq = q4_expand(cur[t].qs[j >> 1], (j & 1) != 0);
-#pragma unroll
-        for (int b = 0; b < BTN; ++b) {
-          const f32x4 dd = mfma_bf16_k32(a[b], bq, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[t][b][i] = __builtin_fmaf(sd[t][j], dd[i], __builtin_fmaf(-mm[t][j], ssum[b][i], acc[t][b][i]));
-        }
-      }
-    }
-    if (sb + 1 < sb1) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) cur[t] = nxt[t];
-    }
-  }
-  gemm_store<NT, BTN>(p, acc, sg, nloc, split, lane);
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+GR_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int NT, int BTN>
-__global__ __launch_bounds__(256) void q6k_gemm_kernel(GemmParams p) {
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= p.total_items) return;
-  const int split = item / p.total_groups;
-  const int gidx = item - split * p.total_groups;
-  int s = 0;
-  while (s + 1 < p.nseg && gidx >= p.seg[s + 1].group_off) ++s;
-  const GemmSeg sg = p.seg[s];
-  const int group = gidx - sg.group_off;
-  const int col = lane & 15, kg = lane >> 4;
+// Prefetch loads into registers whose completion the wave bodies guard with their own
+// vmcnt waits (the compiler's wait insertion is too conservative across the unrolled
+// two-buffer loop and would wait for the newer buffer too).  `base` is wave-uniform.
+GR_DEV u32x4 ldg_x4(const void* base, u32 voff) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(base));
+  return r;
+}
+GR_DEV u32 ldg_u16(const void* base, u32 voff) {
+  u32 r;
+  asm volatile("global_load_ushort %0, %1, %2" : "=v"(r) : "v"(voff), "s"(base));
+  return r;
+}
 
-  const uint8_t* rowp[NT];
-  int nloc[NT];
+// Hides a value from the optimiser so that address arithmetic derived from it is
+// recomputed where it is used rather than hoisted and kept live across the loop.
+GR_DEV int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// The 16 rows of a tile: `base` is its first row (wave-uniform, 16-byte aligned);
+// row r reads matrix row min(r, nvalid - 1) of the tile, so a ragged last tile
+// repeats its last row (results of such rows are never stored).
+struct TileRows {
+  const uint8_t* base;
+  int nvalid;
+  u32 row_bytes;
+  GR_DEV u32 off(int r) const { return (u32)min(r, nvalid - 1) * row_bytes; }
+};
+
+// Q4_K: 16 rows x 144 B = 144 chunks of 16 B; chunk c = 9r + piece -> LDS 16c.
+GR_DEV void q4_issue(const TileRows& tr, int sb, lds_u8* slot, int lane) {
+  const int l = opaque(lane);
+  const u32 sbo = (u32)sb * kQ4KBytes;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    nloc[t] = (group * NT + t) * 16 + col;
-    rowp[t] = sg.w + (size_t)min(nloc[t], sg.rows - 1) * p.row_bytes;
+  for (int i = 0; i < kQ4LoadInstr; ++i) {
+    const int c = l + 64 * i;
+    const int r = c / 9, pc = c - 9 * r;
+    const uint8_t* src = tr.base + (tr.off(r) + sbo + 16 * pc);
+    if (i < kQ4LoadInstr - 1 || lane < 144 - 64 * (kQ4LoadInstr - 1))
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(slot + 1024 * i), 16, 0, 0);
   }
-  const int sb0 = split * p.sb_per_split;
-  const int sb1 = min(p.nsb, sb0 + p.sb_per_split);
+}
 
-  f32x4 acc[NT][BTN];
+// Q6_K: rows are 2-byte aligned.  Row r's slot holds the dwords covering bytes
+// [A - sh, A - sh + 212) of its block (A its address, sh = A & 3): 53 dwords when
+// sh == 2 (the block's 210 bytes and the two before it), 52 when sh == 0 (the block's
+// first 208 bytes; d is read from global separately; slot 52 repeats dword 51), so no
+// read leaves the block's dwords.  Slot c = 53r + w -> LDS 4c.
+GR_DEV void q6_issue(const TileRows& tr, int sb, lds_u8* slot, int lane) {
+  const int l = opaque(lane);
+  const u32 sbo = (u32)sb * kQ6KBytes;
+  const u32 blo = (u32)(uintptr_t)tr.base;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int b = 0; b < BTN; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const u32x2* xp = (const u32x2*)p.xpack;
-  const f32x4* xs = (const f32x4*)p.xsum;
-
-  Q6Regs cur[NT], nxt[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) q6_load(cur[t], rowp[t] + (size_t)sb0 * kQ6KBytes, kg);
-
-  for (int sb = sb0; sb < sb1; ++sb) {
-    if (sb + 1 < sb1) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) q6_load(nxt[t], rowp[t] + (size_t)(sb + 1) * kQ6KBytes, kg);
-    }
-    float dsc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) dsc[t] = h2f(cur[t].d);
-#pragma unroll
-    for (int hu = 0; hu < 4; ++hu) {
-      const int h = hu >> 1, u = hu & 1;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int sub = 8 * h + 2 * r + u;  // 16-weight sub-block within the super-block
-        const int slice = sb * 16 + sub;
-        u32x2 a[BTN];
-        f32x4 ssum[BTN];
-#pragma unroll
-        for (int b = 0; b < BTN; ++b) {
-          a[b] = xp[((size_t)b * p.nslices + slice) * 64 + lane];
-          ssum[b] = xs[((size_t)b * p.nslices + slice) * 4 + kg];
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const u32x2 bq = q6_expand(cur[t].part[hu], r);
-          const int scv = (int)(int8_t)((cur[t].sc[sub >> 2] >> (8 * (sub & 3))) & 0xFF);
-          const float sd = dsc[t] * (float)scv;
-          const float c160 = 160.0f * sd;
-#pragma unroll
-          for (int b = 0; b < BTN; ++b) {
-            const f32x4 dd = mfma_bf16_k16(a[b], bq, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[t][b][i] = __builtin_fmaf(sd, dd[i], __builtin_fmaf(-c160, ssum[b][i], acc[t][b][i]));
-          }
-        }
-      }
-    }
-    if (sb + 1 < sb1) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) cur[t] = nxt[t];
-    }
+  for (int i = 0; i < kQ6LoadInstr; ++i) {
+    const int c = l + 64 * i;
+    const int r = c / 53, wd = c - 53 * r;
+    const u32 o = tr.off(r) + sbo;
+    const u32 sh = (blo + o) & 3u;
+    const int wde = (wd == 52 && sh == 0) ? 51 : wd;
+    const uint8_t* src = tr.base + ((o + 4u * (u32)wde) - sh);
+    if (i < kQ6LoadInstr - 1 || lane < 16 * 53 - 64 * (kQ6LoadInstr - 1))
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(slot + 256 * i), 4, 0, 0);
   }
-  gemm_store<NT, BTN>(p, acc, sg, nloc, split, lane);
+}
+
+// 4 bytes at byte offset `off` (even) of an LDS region whose dwords are aligned.
+GR_DEV u32 lds_u32_a2(const lds_u8* base, int off) {
+  const int a = off & ~3;
+  const u32 lo = *(const __attribute__((address_space(3))) u32*)(base + a);
+  const u32 hi = *(const __attribute__((address_space(3))) u32*)(base + a + 4);
+  return __builtin_amdgcn_alignbyte(hi, lo, (u32)(off & 3));
 }
 
 // ---------------------------------------------------------------------------------
-// launch
+// wave bodies: accumulate rows 8bt+2g and 8bt+2g+1 of output column n (lane (n, g))
+// of tile t over super-blocks [sb0, sb1).
 
-#define GR_GEMM_CASES(KER)                                                                         \
-  switch (nt * 100 + btn) {                                                                        \
-    case 101: KER<1, 1><<<grid, 256, 0, st>>>(p); break;                                           \
-    case 102: KER<1, 2><<<grid, 256, 0, st>>>(p); break;                                           \
-    case 104: KER<1, 4><<<grid, 256, 0, st>>>(p); break;                                           \
-    case 108: KER<1, 8><<<grid, 256, 0, st>>>(p); break;                                           \
-    case 201: KER<2, 1><<<grid, 256, 0, st>>>(p); break;                                           \
-    case 202: KER<2, 2><<<grid, 256, 0, st>>>(p); break;                                           \
-    case 204: KER<2, 4><<<grid, 256, 0, st>>>(p); break;                                           \
-    case 401: KER<4, 1><<<grid, 256, 0, st>>>(p); break;                                           \
-    case 402: KER<4, 2><<<grid, 256, 0, st>>>(p); break;                                           \
-    default: return hipErrorInvalidValue;                                                          \
+// One super-block of Q4_K for NT tiles, weights from LDS slots, activations `ca`.
+template <int NT, int BTN>
+GR_DEV void q4_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32x4* ca, int sb, int lane,
+                    float (&acc)[NT][BTN][2]) {
+  const u32x4* xp = (const u32x4*)a.xpack;
+  const u32x4 ones = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, kg = lane >> 4;
+  Q4Regs w[NT];
+  float sd[NT][8], mm[NT][8];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const lds_u8* rp = slot[t] + kQ4KBytes * n;
+    w[t].hdr = *(const __attribute__((address_space(3))) u32x4*)rp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[t].qs[c] = *(const __attribute__((address_space(3))) u32x2*)(rp + 16 + 32 * c + 8 * kg);
+    q4_scales(w[t].hdr, sd[t], mm[t]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mm[t][j] = __builtin_fmaf(128.0f, sd[t][j], mm[t][j]);
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u32x4 av[BTN];
+    float s0[BTN], s1[BTN];
+#pragma unroll
+    for (int b = 0; b < BTN; ++b) {
+      if constexpr (BTN == 1)
+        av[b] = ca[j];
+      else
+        av[b] = xp[(((size_t)b * a.nslices) + (size_t)sb * 8 + j) * 64 + lane];
+      const f32x4 sv = mfma_bf16_k32(av[b], ones, z4);
+      s0[b] = sv[0] + sv[1];
+      s1[b] = sv[2] + sv[3];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 bq = q4_expand(w[t].qs[j >> 1], (j & 1) != 0);
+#pragma unroll
+      for (int b = 0; b < BTN; ++b) {
+        const f32x4 dd = mfma_bf16_k32(av[b], bq, z4);
+        acc[t][b][0] = __builtin_fmaf(sd[t][j], dd[0] + dd[1], __builtin_fmaf(-mm[t][j], s0[b], acc[t][b][0]));
+        acc[t][b][1] = __builtin_fmaf(sd[t][j], dd[2] + dd[3], __builtin_fmaf(-mm[t][j], s1[b], acc[t][b][1]));
+      }
+    }
+  }
+}
 
-GemmPlan plan_gemm(int wtype, const int* seg_rows, int nseg, int K, int B, int max_splits) {
+template <int NT, int NA>
+struct Q4Buf {
+  int slot;     // LDS ring slot holding this buffer's weights
+  u32x4 a[NA];  // activation fragments
+};
+
+template <int NT, int BTN>
+GR_DEV void q4_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, int sb0, int sb1, int lane,
+                    float (&acc)[NT][BTN][2]) {
+  constexpr int NA = BTN == 1 ? 8 : 1;
+  constexpr int kBatch = NT * kQ4LoadInstr + (BTN == 1 ? 8 : 0);  // VMEM instructions per load()
+  Q4Buf<NT, NA> b0, b1;
+  b0.slot = 0;
+  b1.slot = 1;
+  auto load = [&](Q4Buf<NT, NA>& b, int sb) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) q4_issue(tr[t], sb, ring + (b.slot * NT + t) * kQ4Stage, lane);
+    if constexpr (BTN == 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b.a[j] = ldg_x4(a.xpack, ((u32)sb * 8 + j) * 1024u + 16u * lane);
+    }
+  };
+  auto step = [&](Q4Buf<NT, NA>& b, int sb, bool newer_in_flight) {
+    if (newer_in_flight)
+      wait_vmcnt<kBatch>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    lds_u8* slots[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) slots[t] = ring + (b.slot * NT + t) * kQ4Stage;
+    q4_step<NT, BTN>(a, slots, b.a, sb, lane, acc);
+  };
+  pipeline2(sb0, sb1, b0, b1, load, step);
+}
+
+template <int NT, int BTN>
+GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dreg)[NT], const u32x4* ca, int sb,
+                    int lane, float (&acc)[NT][BTN][2], const int (&sh)[NT]) {
+  const u32x4* xp = (const u32x4*)a.xpack;
+  const u32x2 ones = {kOnesBf16, kOnesBf16};
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, kg = lane >> 4;
+  Q6Regs w[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const lds_u8* rp = slot[t] + kQ6Row * n;
+    const int o = sh[t];
+#pragma unroll
+    for (int hu = 0; hu < 4; ++hu) {
+      const int h = hu >> 1, u = hu & 1;
+      w[t].part[hu].a = lds_u32_a2(rp, o + 64 * h + 16 * u + 4 * kg);
+      w[t].part[hu].b = lds_u32_a2(rp, o + 64 * h + 32 + 16 * u + 4 * kg);
+      w[t].part[hu].q = lds_u32_a2(rp, o + 128 + 32 * h + 16 * u + 4 * kg);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[t].sc[i] = lds_u32_a2(rp, o + 192 + 4 * i);
+    w[t].d = (u16)dreg[t];
+  }
+  float dsc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) dsc[t] = h2f(w[t].d);
+#pragma unroll
+  for (int hu = 0; hu < 4; ++hu) {
+    const int h = hu >> 1, u = hu & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sub = 8 * h + 2 * r + u;  // 16-weight sub-block within the super-block
+      u32x2 av[BTN];
+      float s0[BTN], s1[BTN];
+#pragma unroll
+      for (int b = 0; b < BTN; ++b) {
+        u32x4 pr;
+        if constexpr (BTN == 1)
+          pr = ca[sub >> 1];
+        else
+          pr = xp[(((size_t)b * (a.nslices >> 1)) + (size_t)sb * 8 + (sub >> 1)) * 64 + lane];
+        av[b] = (sub & 1) ? u32x2{pr.z, pr.w} : u32x2{pr.x, pr.y};
+        const f32x4 sv = mfma_bf16_k16(av[b], ones, z4);
+        s0[b] = 160.0f * (sv[0] + sv[1]);
+        s1[b] = 160.0f * (sv[2] + sv[3]);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x2 bq = q6_expand(w[t].part[hu], r);
+        const int scv = (int)(int8_t)((w[t].sc[sub >> 2] >> (8 * (sub & 3))) & 0xFF);
+        const float sd = dsc[t] * (float)scv;
+#pragma unroll
+        for (int b = 0; b < BTN; ++b) {
+          const f32x4 dd = mfma_bf16_k16(av[b], bq, z4);
+          acc[t][b][0] = __builtin_fmaf(sd, (dd[0] + dd[1]) - s0[b], acc[t][b][0]);
+          acc[t][b][1] = __builtin_fmaf(sd, (dd[2] + dd[3]) - s1[b], acc[t][b][1]);
+        }
+      }
+    }
+    // keep the scheduler from hoisting all sixteen sub-blocks' MFMAs at once
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int NT, int NA>
+struct Q6Buf {
+  int slot;
+  u32 d[NT];      // this lane's row's fp16 d (read from global: it is not always staged)
+  u32x4 a[NA];
+};
+
+template <int NT, int BTN>
+GR_DEV void q6_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, int sb0, int sb1, int lane,
+                    float (&acc)[NT][BTN][2]) {
+  constexpr int NA = BTN == 1 ? 8 : 1;
+  constexpr int kBatch = NT * (kQ6LoadInstr + 1) + (BTN == 1 ? 8 : 0);
+  const int n = lane & 15;
+  Q6Buf<NT, NA> b0, b1;
+  b0.slot = 0;
+  b1.slot = 1;
+  auto load = [&](Q6Buf<NT, NA>& b, int sb) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      q6_issue(tr[t], sb, ring + (b.slot * NT + t) * kQ6Stage, lane);
+      b.d[t] = ldg_u16(tr[t].base, tr[t].off(n) + (u32)sb * kQ6KBytes + 208u);
+    }
+    if constexpr (BTN == 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b.a[j] = ldg_x4(a.xpack, ((u32)sb * 8 + j) * 1024u + 16u * lane);
+    }
+  };
+  auto step = [&](Q6Buf<NT, NA>& b, int sb, bool newer_in_flight) {
+    if (newer_in_flight)
+      wait_vmcnt<kBatch>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    lds_u8* slots[NT];
+    int sh[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      slots[t] = ring + (b.slot * NT + t) * kQ6Stage;
+      sh[t] = (int)(((u32)(uintptr_t)tr[t].base + tr[t].off(n) + (u32)sb * kQ6KBytes) & 3u);
+    }
+    q6_step<NT, BTN>(a, slots, b.d, b.a, sb, lane, acc, sh);
+  };
+  pipeline2(sb0, sb1, b0, b1, load, step);
+}
+
+// ---------------------------------------------------------------------------------
+// the kernel: waves split K, LDS reduction, epilogue
+
+GR_DEV float row_scale(const GemmArgs& a, int b) {
+  return a.ss ? 1.0f / sqrtf(a.ss[b] * a.inv_k + a.eps) : 1.0f;
+}
+
+template <int WT, int NT, int BTN, int MAXT>
+__global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // staging rings, then the reduction
+  float* red = (float*)lds;  // [waves][NT][BTN][64 lanes][2]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nwaves = blockDim.x >> 6;
+  const int tile = blockIdx.x;
+  const int n = lane & 15;
+
+  if (a.zero_ptr && tile == 0)
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.f;
+
+  // rows of the tile(s)
+  int seg = 0, local = tile;
+  if (a.epi != kEpiSwiGLU) {
+    while (seg + 1 < a.nseg && tile >= a.seg_tile_off[seg + 1]) ++seg;
+    local = tile - a.seg_tile_off[seg];
+  }
+  TileRows tr[NT];
+  int rows_n = 0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int s = a.epi == kEpiSwiGLU ? t : seg;
+    rows_n = a.seg_rows[s];
+    tr[t] = TileRows{a.w[s] + (size_t)local * 16 * a.row_bytes, rows_n - local * 16, (u32)a.row_bytes};
+  }
+  float acc[NT][BTN][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int b = 0; b < BTN; ++b) acc[t][b][0] = acc[t][b][1] = 0.f;
+
+  const int sb0 = wave * a.sb_per_wave;
+  const int sb1 = min(a.nsb, sb0 + a.sb_per_wave);
+  constexpr int kStage = WT == 12 ? kQ4Stage : kQ6Stage;
+  lds_u8* ring = (lds_u8*)lds + __builtin_amdgcn_readfirstlane(wave) * (2 * NT * kStage);
+  if (sb0 < sb1) {
+    if constexpr (WT == 12)
+      q4_wave<NT, BTN>(a, tr, ring, sb0, sb1, lane, acc);
+    else
+      q6_wave<NT, BTN>(a, tr, ring, sb0, sb1, lane, acc);
+  }
+  __syncthreads();  // the reduction buffer reuses the staging area
+
+  // reduce over waves: red[((w*NT + t)*BTN + b)*128 + lane*2 + e]
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int b = 0; b < BTN; ++b) {
+      float* r = red + (((size_t)wave * NT + t) * BTN + b) * 128 + lane * 2;
+      r[0] = acc[t][b][0];
+      r[1] = acc[t][b][1];
+    }
+  __syncthreads();
+
+  // epilogue: element e = (t, bt, lane', k2); a SwiGLU pair handles both tiles at once
+  constexpr int kPer = NT * BTN * 128;
+  const int n_elem = a.epi == kEpiSwiGLU ? BTN * 128 : kPer;
+  for (int e = threadIdx.x; e < ((n_elem + 63) & ~63); e += blockDim.x) {
+    // every lane of the wave reaches the shuffles below
+    const bool in = e < n_elem;
+    const int t = a.epi == kEpiSwiGLU ? 0 : (in ? e / (BTN * 128) : 0);
+    const int rem = e % (BTN * 128);
+    const int bt = rem / 128, lp = (rem % 128) >> 1, k2 = rem & 1;
+    const int nn = lp & 15, g = lp >> 4;
+    const int brow = 8 * bt + 2 * g + k2;
+    float v = 0.f, v2 = 0.f;
+    if (in) {
+      for (int w = 0; w < nwaves; ++w) {
+        v += red[(((size_t)w * NT + t) * BTN + bt) * 128 + (rem % 128)];
+        if (a.epi == kEpiSwiGLU) v2 += red[(((size_t)w * NT + 1) * BTN + bt) * 128 + (rem % 128)];
+      }
+    }
+    const bool live = in && brow < a.B && local * 16 + nn < rows_n;
+    const float rs = live ? row_scale(a, brow) : 0.f;
+    const int col = (a.epi == kEpiSwiGLU ? 0 : a.seg_col_off[seg]) + local * 16 + nn;
+    if (a.epi == kEpiStore) {
+      if (live) a.y[(size_t)brow * a.ldy + col] = rs * v;
+    } else if (a.epi == kEpiSwiGLU) {
+      if (live) {
+        const float gv = rs * v, uv = rs * v2;
+        actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, brow, col, gv / (1.0f + expf(-gv)) * uv);
+      }
+    } else {
+      float xn = 0.f;
+      if (live) {
+        float* xp = a.y + (size_t)brow * a.ldy + col;
+        xn = *xp + rs * v;
+        *xp = xn;
+        const float pv = a.gain ? xn * a.gain[col] : xn;
+        if (a.pack_out) actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, brow, col, pv);
+        if (a.pack_out2) actpack_put(a.pack_out2, a.pack_kind2, a.pack_nslices2, brow, col, pv);
+      }
+      // sum of squares over the tile's 16 columns of each batch row: lanes with the
+      // same (g, k2) differ in nn, which is bits 1..4 of the thread index
+      float sq = xn * xn;
+#pragma unroll
+      for (int o = 2; o <= 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
+      if (in && nn == 0 && brow < a.B && a.ss_out) atomicAdd(a.ss_out + brow, sq);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// plan and launch
+
+GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, bool pair) {
   GemmPlan pl{};
-  int tiles = 0;
-  for (int i = 0; i < nseg; ++i) tiles += (seg_rows[i] + 15) / 16;
-  const int btn = B <= 8 ? 1 : B <= 16 ? 2 : B <= 32 ? 4 : 8;
-  int nt = 1;
-  if (tiles >= 4096)
-    nt = 4;
-  else if (tiles >= 1024)
-    nt = 2;
-  // registers: keep NT*BTN accumulators modest
-  while (nt > 1 && nt * btn > 8) nt >>= 1;
-  if (btn == 8) nt = 1;
-  int groups = 0;
-  for (int i = 0; i < nseg; ++i) groups += (seg_rows[i] + 16 * nt - 1) / (16 * nt);
+  pl.nt = pair ? 2 : 1;
+  pl.btn = actpack_tiles(B);
+  pl.tiles = total_tiles;
   const int nsb = K / kQK;
-  int splits = 1;
-  if (groups < 1536) splits = (2048 + groups - 1) / groups;
-  if (splits > max_splits) splits = max_splits;
-  int min_sb = wtype == 12 ? 2 : 1;
-  if (splits > nsb / min_sb) splits = nsb / min_sb;
-  if (splits < 1) splits = 1;
-  int per = (nsb + splits - 1) / splits;
-  splits = (nsb + per - 1) / per;
-  pl.nt = nt;
-  pl.btn = btn;
-  pl.groups = groups;
-  pl.splits = splits;
-  pl.sb_per_split = per;
+  // registers: one-tile, one-batch-tile kernels use up to 8 waves per workgroup, the
+  // others up to 4
+  pl.maxt = (pl.nt == 1 && pl.btn == 1) ? 512 : 256;
+  const int max_waves = pl.maxt / 64;
+  // about 4096 waves in flight, at least one super-block per wave
+  int want = (4096 + total_tiles - 1) / total_tiles;
+  if (want > max_waves) want = max_waves;
+  if (want > nsb) want = nsb;
+  // LDS: staging rings (waves * NT * 2 slots) and the reduction (waves * NT * BTN * 512 B)
+  // share one allocation of at most 64 KB
+  const int stage = wtype == 12 ? kQ4Stage : kQ6Stage;
+  auto lds_need = [&](int w) { return max(w * pl.nt * 2 * stage, w * pl.nt * pl.btn * 512); };
+  while (want > 1 && lds_need(want) > 65536) --want;
+  if (want < 1) want = 1;
+  pl.sb_per_wave = (nsb + want - 1) / want;
+  pl.waves = (nsb + pl.sb_per_wave - 1) / pl.sb_per_wave;
+  pl.lds = (size_t)lds_need(pl.waves);
   return pl;
 }
 
-hipError_t launch_gemm(int wtype, const GemmPlan& pl, const uint8_t* const* w, const int* seg_rows, int nseg, int K,
-                       int B, const void* xpack, const float* xsum, float* y, int ldy, int mode, hipStream_t st) {
-  GemmParams p{};
-  p.nseg = nseg;
-  int goff = 0, roff = 0;
-  for (int i = 0; i < nseg; ++i) {
-    p.seg[i].w = w[i];
-    p.seg[i].rows = seg_rows[i];
-    p.seg[i].row_off = roff;
-    p.seg[i].group_off = goff;
-    goff += (seg_rows[i] + 16 * pl.nt - 1) / (16 * pl.nt);
-    roff += seg_rows[i];
+#define GR_GEMM_SWITCH(WTv)                                                                          \
+  switch (pl.nt * 1000 + pl.btn * 10 + (pl.maxt == 512)) {                                          \
+    case 1011: gemm_kernel<WTv, 1, 1, 512><<<grid, block, lds, st>>>(a); break;                       \
+    case 1020: gemm_kernel<WTv, 1, 2, 256><<<grid, block, lds, st>>>(a); break;                       \
+    case 1040: gemm_kernel<WTv, 1, 4, 256><<<grid, block, lds, st>>>(a); break;                       \
+    case 1080: gemm_kernel<WTv, 1, 8, 256><<<grid, block, lds, st>>>(a); break;                       \
+    case 2010: gemm_kernel<WTv, 2, 1, 256><<<grid, block, lds, st>>>(a); break;                       \
+    case 2020: gemm_kernel<WTv, 2, 2, 256><<<grid, block, lds, st>>>(a); break;                       \
+    case 2040: gemm_kernel<WTv, 2, 4, 256><<<grid, block, lds, st>>>(a); break;                       \
+    case 2080: gemm_kernel<WTv, 2, 8, 256><<<grid, block, lds, st>>>(a); break;                       \
+    default: return hipErrorInvalidValue;                                                            \
   }
-  p.total_groups = goff;
-  p.nsb = K / kQK;
-  p.row_bytes = (size_t)(K / kQK) * (wtype == 12 ? kQ4KBytes : kQ6KBytes);
-  p.xpack = xpack;
-  p.xsum = xsum;
-  p.nslices = wtype == 12 ? K / 32 : K / 16;
-  p.B = B;
-  p.y = y;
-  p.ldy = ldy;
-  p.splits = pl.splits;
-  p.sb_per_split = pl.sb_per_split;
-  p.total_items = goff * pl.splits;
-  p.mode = mode;
-  const int nt = pl.nt, btn = pl.btn;
-  const dim3 grid((p.total_items + 3) / 4);
+
+hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st) {
+  if (pl.tiles <= 0) return hipSuccess;
+  const dim3 grid(pl.tiles), block(pl.waves * 64);
+  const size_t lds = pl.lds;
   if (wtype == 12) {
-    GR_GEMM_CASES(q4k_gemm_kernel)
+    GR_GEMM_SWITCH(12)
   } else {
-    GR_GEMM_CASES(q6k_gemm_kernel)
+    GR_GEMM_SWITCH(14)
   }
   return hipGetLastError();
 }

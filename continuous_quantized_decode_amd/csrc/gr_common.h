@@ -27,6 +27,14 @@ constexpr int kQ4KBytes = 144;
 constexpr int kQ6KBytes = 210;
 constexpr int kWave = 64;
 
+// Streamed loads (weights, KV pages).  Plain cached loads: a row's 128-byte lines are
+// read by several instructions of the same wave, which must hit in L2 (the
+// non-temporal policy refetches such lines from HBM).
+template <class T>
+GR_DEV T gr_ld(const T* p) {
+  return *p;
+}
+
 // ------------------------------------------------------------------ fp16 / bf16
 
 // Bit reinterpretation through a by-value argument: clang's __builtin_bit_cast applied
@@ -72,25 +80,63 @@ GR_DEV f32x4 mfma_f16_k16(u32x2 a, u32x2 b, f32x4 c) {
 // -------------------------------------------------------------- actpack layout
 //
 // The activation operand of a GEMM, x [B][K] f32, is stored once per step as bf16
-// pairs x = hi + lo so the MFMA sees it at ~fp32 accuracy.  Batch rows are grouped
-// in tiles of 8; a tile is the A operand of 16 MFMA rows: row m < 8 is the hi part of
-// batch row 8t+m, row m >= 8 the lo part of batch row 8t+m-8.
+// pairs x = hi + lo so that the MFMA sees it at ~fp32 accuracy.  Batch rows are
+// grouped in tiles of 8; a tile is the A operand of 16 MFMA rows: row m holds part
+// (m & 1) (0: hi, 1: lo) of batch row 8t + (m >> 1).  With the MFMA output layout
+// (lane (n, g) holds rows 4g..4g+3) each lane then owns hi and lo of batch rows
+// 8t + 2g and 8t + 2g + 1 and combines them without any lane exchange.
 //
 // Kind K32 (Q4_K consumers): slice s covers K [32s, 32s+32) (one Q4_K sub-block).
 //   Lane l = (m = l%16, g = l/16) of slice s holds 8 bf16 (16 B) at K positions
-//   32s + 8g + kPerm8[i], i = 0..7.
+//   32s + 8g + perm8(i), i = 0..7.
 // Kind K16 (Q6_K consumers): slice s covers K [16s, 16s+16) (one Q6_K sub-block).
-//   Lane l holds 4 bf16 (8 B) at K positions 16s + 4g + kPerm4[i].
+//   Lane l holds 4 bf16 (8 B) at K positions 16s + 4g + perm4(i); the fragments of
+//   slices 2p and 2p+1 sit side by side (16 B per lane, slice 2p first).
 // The permutations match the order in which the weight decoders emit quants (byte
 // pairs 0,2 then 1,3 of each dword).
-// Fragment of (tile t, slice s, lane l) sits at element ((t*nslices + s)*64 + l).
-// Sums: sums[(t*nslices + s)*16 + m] = sum over the slice of row m's values (hi or
-// lo part), used for the weight-offset terms.
+// K32: the 16 B of (tile t, slice s, lane l) are unit ((t*nslices + s)*64 + l);
+// K16: the 16 B of (tile t, slices 2p and 2p+1, lane l) are unit ((t*nslices/2 + p)*64 + l).
+// Producers write x * gain (the RMSNorm gain, or 1); the 1/rms factor of each row is
+// applied by the consuming GEMM to its outputs (the product is linear in x).
 
 enum ActKind { kK32 = 0, kK16 = 1 };
 
 GR_DEV int perm8(int i) { return (i & 4) | ((i & 1) << 1) | ((i >> 1) & 1); }  // 0,2,1,3,4,6,5,7
 GR_DEV int perm4(int i) { return ((i & 1) << 1) | ((i >> 1) & 1); }            // 0,2,1,3
+
+// ---------------------------------------------------------------- pipelining
+//
+// Software pipeline over items [i0, i1) with two register buffers used in turn:
+// the loads of item i+1 are issued into the idle buffer (and pinned there by a
+// scheduling barrier) before item i is processed from the other.  Unrolled by two so
+// that no buffer is ever copied (a loop-carried copy makes the compiler wait for the
+// fresh loads in the middle of the compute).
+// step(buffer, item, newer_in_flight) is told whether the next item's loads were
+// issued after this buffer's (so it can wait for its own loads only).
+template <class Buf, class Load, class Step>
+GR_DEV void pipeline2(int i0, int i1, Buf& b0, Buf& b1, Load&& load, Step&& step) {
+  int i = i0;
+  load(b0, i);
+  for (; i + 2 < i1; i += 2) {
+    load(b1, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    step(b0, i, true);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b0, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    step(b1, i + 1, true);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (i + 1 < i1) {
+    load(b1, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    step(b0, i, true);
+    __builtin_amdgcn_sched_barrier(0);
+    step(b1, i + 1, false);
+  } else {
+    step(b0, i, false);
+  }
+}
 
 // ---------------------------------------------------------------- reductions
 
@@ -103,16 +149,6 @@ GR_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
-}
-
-// Aligned 4-byte load of a possibly 2-byte-aligned address.
-GR_DEV u32 load_u32_a2(const uint8_t* p) {
-  uintptr_t a = (uintptr_t)p;
-  const u32* base = (const u32*)(a & ~(uintptr_t)3);
-  u32 lo = __builtin_nontemporal_load(base);
-  if ((a & 3) == 0) return lo;
-  u32 hi = __builtin_nontemporal_load(base + 1);
-  return __builtin_amdgcn_alignbyte(hi, lo, (u32)(a & 3));
 }
 
 }  // namespace gr

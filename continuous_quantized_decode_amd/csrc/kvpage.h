@@ -41,29 +41,29 @@ GR_DEV void load_page(PageRegs<KVDT, D>& r, const uint8_t* kh, const uint8_t* vh
   const int n = lane & 15, kg = lane >> 4;
   if constexpr (KVDT == KV_F16_T) {
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) r.k[s] = __builtin_nontemporal_load((const u32x4*)(kh + (n * D + 32 * s + 8 * kg) * 2));
+    for (int s = 0; s < D / 32; ++s) r.k[s] = gr_ld((const u32x4*)(kh + (n * D + 32 * s + 8 * kg) * 2));
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
-      r.v[t] = __builtin_nontemporal_load((const u32x2*)(vh + ((16 * t + n) * kPage + 4 * kg) * 2));
+      r.v[t] = gr_ld((const u32x2*)(vh + ((16 * t + n) * kPage + 4 * kg) * 2));
   } else if constexpr (KVDT == KV_F32_T) {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      r.k[s][0] = __builtin_nontemporal_load((const u32x4*)(kh + (n * D + 32 * s + 8 * kg) * 4));
-      r.k[s][1] = __builtin_nontemporal_load((const u32x4*)(kh + (n * D + 32 * s + 8 * kg + 4) * 4));
+      r.k[s][0] = gr_ld((const u32x4*)(kh + (n * D + 32 * s + 8 * kg) * 4));
+      r.k[s][1] = gr_ld((const u32x4*)(kh + (n * D + 32 * s + 8 * kg + 4) * 4));
     }
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
-      r.v[t] = __builtin_nontemporal_load((const u32x4*)(vh + ((16 * t + n) * kPage + 4 * kg) * 4));
+      r.v[t] = gr_ld((const u32x4*)(vh + ((16 * t + n) * kPage + 4 * kg) * 4));
   } else {
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) r.k[s] = __builtin_nontemporal_load((const u32x2*)(kh + n * D + 32 * s + 8 * kg));
+    for (int s = 0; s < D / 32; ++s) r.k[s] = gr_ld((const u32x2*)(kh + n * D + 32 * s + 8 * kg));
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) r.v[t] = __builtin_nontemporal_load((const u32*)(vh + (16 * t + n) * kPage + 4 * kg));
+    for (int t = 0; t < D / 16; ++t) r.v[t] = gr_ld((const u32*)(vh + (16 * t + n) * kPage + 4 * kg));
     // scales of token n: [16][D/32] fp16 after the 16*D codes
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
-      r.ksc[i] = __builtin_nontemporal_load((const u32*)(kh + kPage * D + (n * (D / 32) + 2 * i) * 2));
-      r.vsc[i] = __builtin_nontemporal_load((const u32*)(vh + kPage * D + (n * (D / 32) + 2 * i) * 2));
+      r.ksc[i] = gr_ld((const u32*)(kh + kPage * D + (n * (D / 32) + 2 * i) * 2));
+      r.vsc[i] = gr_ld((const u32*)(vh + kPage * D + (n * (D / 32) + 2 * i) * 2));
     }
   }
 }

@@ -55,9 +55,9 @@ struct Q4Regs {
 };
 
 GR_DEV void q4_load(Q4Regs& r, const uint8_t* blk, int kg) {
-  r.hdr = __builtin_nontemporal_load((const u32x4*)blk);
+  r.hdr = gr_ld((const u32x4*)blk);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) r.qs[c] = __builtin_nontemporal_load((const u32x2*)(blk + 16 + 32 * c + 8 * kg));
+  for (int c = 0; c < 4; ++c) r.qs[c] = gr_ld((const u32x2*)(blk + 16 + 32 * c + 8 * kg));
 }
 
 // ---------------------------------------------------------------------------------
@@ -74,17 +74,38 @@ struct Q6Regs {
   u16 d;
 };
 
+// 4 bytes at a 2-byte aligned address: one 8-byte load at the enclosing 4-byte
+// aligned address, then a byte funnel shift.  The load covers [p-2, p+6) or [p, p+8),
+// which must lie inside the buffer (callers keep at least 4 bytes after p + 4).
+typedef u32 u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+GR_DEV u32 ld4_a2(const uint8_t* p) {
+  const uintptr_t a = (uintptr_t)p;
+  const u32x2_a4 w = gr_ld((const u32x2_a4*)(a & ~(uintptr_t)3));
+  return __builtin_amdgcn_alignbyte(w.y, w.x, (u32)(a & 3));
+}
+
 GR_DEV void q6_load(Q6Regs& r, const uint8_t* blk, int kg) {
 #pragma unroll
   for (int hu = 0; hu < 4; ++hu) {
     const int h = hu >> 1, u = hu & 1;
-    r.part[hu].a = load_u32_a2(blk + 64 * h + 16 * u + 4 * kg);
-    r.part[hu].b = load_u32_a2(blk + 64 * h + 32 + 16 * u + 4 * kg);
-    r.part[hu].q = load_u32_a2(blk + 128 + 32 * h + 16 * u + 4 * kg);
+    r.part[hu].a = ld4_a2(blk + 64 * h + 16 * u + 4 * kg);
+    r.part[hu].b = ld4_a2(blk + 64 * h + 32 + 16 * u + 4 * kg);
+    r.part[hu].q = ld4_a2(blk + 128 + 32 * h + 16 * u + 4 * kg);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.sc[i] = load_u32_a2(blk + 192 + 4 * i);
-  r.d = __builtin_nontemporal_load((const u16*)(blk + 208));
+  // scales [192, 208): aligned dwords covering them, funnel-shifted when the block is
+  // 2 mod 4; the fifth dword is read only when needed (else the fourth again), so
+  // the reads stay inside the block, and there is no branch.
+  const uintptr_t a = (uintptr_t)(blk + 192);
+  const u32 sh = (u32)(a & 3);
+  const u32* base = (const u32*)(a & ~(uintptr_t)3);
+  const u32 w0 = gr_ld(base), w1 = gr_ld(base + 1);
+  const u32 w2 = gr_ld(base + 2), w3 = gr_ld(base + 3);
+  const u32 w4 = gr_ld(base + (sh ? 4 : 3));
+  r.sc[0] = __builtin_amdgcn_alignbyte(w1, w0, sh);
+  r.sc[1] = __builtin_amdgcn_alignbyte(w2, w1, sh);
+  r.sc[2] = __builtin_amdgcn_alignbyte(w3, w2, sh);
+  r.sc[3] = __builtin_amdgcn_alignbyte(w4, w3, sh);
+  r.d = gr_ld((const u16*)(blk + 208));
 }
 
 // 6-bit quants of sub-block (h, 2r+u) as four bytes, then as the bf16 B operand.

@@ -179,6 +179,29 @@ gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
                           const float* head_norm, const void* head_w, int head_wtype, int vocab, float* logits,
                           void* workspace, size_t ws_bytes, void* stream);
 
+/* Timing probe (profiling hook): the same launches as gr_decode_stack, plus
+ * hipEventRecord(ev_begin[l]) on `stream` just before and hipEventRecord(ev_end[l])
+ * just after the launches of stage `probe_stage` of layer l (ev_*[0] for the pack
+ * and head stages).  ev_begin / ev_end are host arrays of hipEvent_t with n_layers entries
+ * (1 for GR_STAGE_HEAD), created by the caller. */
+typedef enum {
+  GR_STAGE_PACK = 0,       /* RMSNorm input pack of the first layer (or of the head) */
+  GR_STAGE_QKV = 1,        /* q, k, v GEMM */
+  GR_STAGE_ATTN = 2,       /* QK-norm, RoPE, KV append, split attention */
+  GR_STAGE_ATTN_MERGE = 3, /* log-sum-exp merge + pack of the Wo input */
+  GR_STAGE_WO = 4,         /* output projection + residual + pack of the FFN input */
+  GR_STAGE_GATE_UP = 5,    /* gate and up GEMM + SwiGLU + pack of the down input */
+  GR_STAGE_DOWN = 6,       /* down projection + residual + pack of the next input */
+  GR_STAGE_HEAD = 7        /* output head GEMM */
+} gr_stage;
+
+gr_status gr_decode_stack_probed(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers,
+                                 void* const* k_pages, void* const* v_pages, int num_pages, float* x,
+                                 const int32_t* block_table, int max_blocks_per_row, const int32_t* ctx_lens,
+                                 int max_ctx, int B, const float* head_norm, const void* head_w, int head_wtype,
+                                 int vocab, float* logits, void* workspace, size_t ws_bytes, void* stream,
+                                 int probe_stage, void* const* ev_begin, void* const* ev_end);
+
 #ifdef __cplusplus
 }
 #endif
