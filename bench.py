@@ -120,7 +120,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--probe-reps", type=int, default=3)
+    ap.add_argument("--cpu-layers", type=int, default=64, help="layers the oracle runs (the rest are scaled)")
+    ap.add_argument("--probe-runs", type=int, default=2, help="probed stack runs per stage")
+    ap.add_argument("--probe-reps", type=int, default=8, help="back-to-back launches of the probed stage")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode path runs on a single MI355X and has no multi-GPU mode "
@@ -154,7 +156,7 @@ def main():
     wts = []
     for layer in range(wl.n_layers):
         lw = synth.layer_weights(wl, layer)
-        if layer < 2:
+        if layer < 4:
             host_layers[layer] = lw
         t = {k: up(getattr(lw, k)) for k in ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo", "w_gate", "w_up",
                                               "w_down")}
@@ -227,15 +229,15 @@ def main():
             continue
         once = name in ("head", "pack")
         durs = []
-        for _ in range(args.probe_reps):
+        for _ in range(args.probe_runs):
             x.copy_(x0)
-            gr.gr_decode_stack_probed(sargs, pm.num_pages, x, bt, cg, max_ctx, si, evb, eve, head_norm, head_w,
-                                      wl.w_head, wl.vocab, logits, ws=ws)
+            gr.gr_decode_stack_probed(sargs, pm.num_pages, x, bt, cg, max_ctx, si, args.probe_reps, evb, eve,
+                                      head_norm, head_w, wl.w_head, wl.vocab, logits, ws=ws)
             torch.cuda.synchronize()
             if once:
-                durs.append(hip.elapsed_ms(evb[0], eve[0]))
+                durs.append(hip.elapsed_ms(evb[0], eve[0]) / args.probe_reps)
             else:
-                durs += [hip.elapsed_ms(evb[i], eve[i]) for i in range(wl.n_layers)]
+                durs += [hip.elapsed_ms(evb[i], eve[i]) / args.probe_reps for i in range(wl.n_layers)]
         avg_ms = float(np.mean(durs))
         launches = 1 if once else wl.n_layers
         per_launch = head_b if name == "head" else pack_b if name == "pack" else sb[name]
@@ -255,34 +257,37 @@ def main():
                 "bytes_per_launch": d["bytes_per_launch"], "avg_launch_us": d["avg_us"]}
     log("[bench] stages: " + json.dumps(stages))
 
-    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same step
+    # ---- CPU baseline: the fp64 oracle on one whole step of the same workload (every
+    #      layer and the output head), when that is bounded; else on its first layers
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         oracle.lib()
-        k_host = [p.cpu().numpy() for p in k_dev[:2]]
-        v_host = [p.cpu().numpy() for p in v_dev[:2]]
+        n_cpu = min(wl.n_layers, args.cpu_layers)
         layer_s = []
         xc = x0_host
-        for layer in range(min(2, wl.n_layers)):
+        for layer in range(n_cpu):
+            lw = host_layers.get(layer) or synth.layer_weights(wl, layer)
+            k_host, v_host = k_dev[layer].cpu().numpy(), v_dev[layer].cpu().numpy()
             c0 = time.time()
-            xc = oracle.decode_layer(wl, host_layers[layer], k_host[layer], v_host[layer], xc, pm.block_table, ctx)
+            xc = oracle.decode_layer(wl, lw, k_host, v_host, xc, pm.block_table, ctx)
             layer_s.append(time.time() - c0)
+            del k_host, v_host, lw
         head_s = 0.0
-        sample = f"{len(layer_s)} of {wl.n_layers} layers at B={wl.batch} with the workload's contexts"
+        if n_cpu == wl.n_layers:
+            sample = f"one whole step: all {wl.n_layers} layers at B={wl.batch} with the workload's contexts"
+        else:
+            sample = f"{n_cpu} of {wl.n_layers} layers at B={wl.batch} with the workload's contexts, scaled"
         if wl.vocab:
-            rows = min(wl.vocab, 8192)
             c0 = time.time()
-            oracle.output_head(xc, head_host[0], wl.rms_eps, head_host[1][:rows],
-                               wl.w_head, rows)
-            head_s = (time.time() - c0) * wl.vocab / rows
-            sample += f", plus {rows} of {wl.vocab} output-head rows"
-        est = float(np.mean(layer_s)) * wl.n_layers + head_s
-        sample += f"; scaled to the full step ({est:.1f} s)"
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        cpu = {"value": round(wl.batch / est, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": sample, "seconds_per_step": round(est, 3)}
-        log(f"[bench] oracle sample: layers {layer_s} head(scaled) {head_s:.2f} s -> {est:.2f} s/step")
+            oracle.output_head(xc, head_host[0], wl.rms_eps, head_host[1], wl.w_head, wl.vocab)
+            head_s = time.time() - c0
+            sample += f", plus the full {wl.vocab}-row output head"
+        est = float(np.sum(layer_s)) * wl.n_layers / n_cpu + head_s
+        sample += f" ({est:.1f} s)"
+        cpu = {"value": round(wl.batch / est, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": sample, "seconds_per_step": round(est, 3)}
+        log(f"[bench] oracle: {n_cpu} layers {float(np.sum(layer_s)):.2f} s, head {head_s:.2f} s -> {est:.2f} s/step")
 
     tok_s = wl.batch / (ms * 1e-3)
     gbs = step_bytes / (ms * 1e-3) / 1e9

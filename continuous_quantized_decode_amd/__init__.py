@@ -97,7 +97,7 @@ def _load() -> C.CDLL:
     L.gr_decode_stack.argtypes = [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _i, C.POINTER(_p), C.POINTER(_p), _i,
                                   _p, _p, _i, _p, _i, _i, _p, _p, _i, _i, _p, _p, _sz, _p]
     L.gr_decode_stack.restype = _i
-    L.gr_decode_stack_probed.argtypes = list(L.gr_decode_stack.argtypes) + [_i, C.POINTER(_p), C.POINTER(_p)]
+    L.gr_decode_stack_probed.argtypes = list(L.gr_decode_stack.argtypes) + [_i, _i, C.POINTER(_p), C.POINTER(_p)]
     L.gr_decode_stack_probed.restype = _i
     if L.gr_abi_version() != 1:
         raise ImportError("libgr ABI version mismatch")
@@ -307,10 +307,10 @@ def gr_decode_stack(args: StackArgs, num_pages: int, x, block_table, ctx_lens, m
 
 
 def gr_decode_stack_probed(args: StackArgs, num_pages: int, x, block_table, ctx_lens, max_ctx: int, probe_stage: int,
-                           ev_begin: Sequence[int], ev_end: Sequence[int], head_norm=None, head_w=None,
-                           head_wtype: int = W_Q6_K, vocab: int = 0, logits=None, ws=None):
-    """gr_decode_stack plus hipEventRecord around the launches of one stage in each layer;
-    ev_begin / ev_end are raw hipEvent_t handles (ints)."""
+                           probe_reps: int, ev_begin: Sequence[int], ev_end: Sequence[int], head_norm=None,
+                           head_w=None, head_wtype: int = W_Q6_K, vocab: int = 0, logits=None, ws=None):
+    """gr_decode_stack with the launches of one stage repeated probe_reps times between
+    hipEventRecord calls in each layer; ev_begin / ev_end are raw hipEvent_t handles (ints)."""
     b = x.shape[0]
     if ws is None:
         ws = workspace(decode_stack_workspace_size(args.cfg, b, max_ctx, vocab), x.device)
@@ -320,5 +320,5 @@ def gr_decode_stack_probed(args: StackArgs, num_pages: int, x, block_table, ctx_
            _load().gr_decode_stack_probed(C.byref(args.cfg), args.weights, args.n, args.k, args.v, num_pages, _ptr(x),
                                           _ptr(block_table), block_table.shape[1], _ptr(ctx_lens), max_ctx, b,
                                           _ptr(head_norm), _ptr(head_w), head_wtype, vocab, _ptr(logits), _ptr(ws),
-                                          ws.numel(), _stream(), probe_stage, eb, ee))
+                                          ws.numel(), _stream(), probe_stage, probe_reps, eb, ee))
     return x

@@ -247,25 +247,27 @@ AttnPlan layer_attn_plan(int B, const gr_layer_cfg* c, int max_ctx) {
 }
 
 // Optional timing probe: events recorded on the launch stream just before and just
-// after the launches of one stage.
+// after the launches of one stage, which are repeated `reps` times in between so the
+// per-launch time is not dominated by the event markers.
 struct Probe {
   int stage = -1;
+  int reps = 1;
   int layer = 0;
   void* const* ev_begin = nullptr;
   void* const* ev_end = nullptr;
 };
 
-struct ProbeScope {
-  const Probe* p;
-  bool on;
-  hipStream_t st;
-  ProbeScope(const Probe* pr, int stage, hipStream_t s) : p(pr), on(pr && pr->stage == stage), st(s) {
-    if (on) (void)hipEventRecord((hipEvent_t)p->ev_begin[p->layer], st);
-  }
-  ~ProbeScope() {
-    if (on) (void)hipEventRecord((hipEvent_t)p->ev_end[p->layer], st);
-  }
-};
+// Runs body() once, or, for the probed stage, `reps` times between the events.
+template <class F>
+gr_status probed(const Probe* p, int stage, hipStream_t st, F&& body) {
+  const bool on = p && p->stage == stage;
+  if (on) (void)hipEventRecord((hipEvent_t)p->ev_begin[p->layer], st);
+  const int n = on ? p->reps : 1;
+  gr_status s = GR_OK;
+  for (int r = 0; r < n && s == GR_OK; ++r) s = body();
+  if (on) (void)hipEventRecord((hipEvent_t)p->ev_end[p->layer], st);
+  return s;
+}
 
 Kinds qkv_kinds(const gr_layer_weights* w) {
   Kinds k;
@@ -278,8 +280,9 @@ Kinds qkv_kinds(const gr_layer_weights* w) {
 // Pack of the layer input: x * attn_norm and its sum of squares.
 gr_status run_input_pack(const float* x, int B, int H, const float* gain, Kinds k, const Pack2& xp, float* ss,
                          hipStream_t st, const Probe* probe) {
-  ProbeScope ps(probe, GR_STAGE_PACK, st);
-  return check_launch(launch_pack_rows(x, H, B, H, gain, k.k32 ? xp.k32 : kNoPack, k.k16 ? xp.k16 : kNoPack, ss, st));
+  return probed(probe, GR_STAGE_PACK, st, [&] {
+    return check_launch(launch_pack_rows(x, H, B, H, gain, k.k32 ? xp.k32 : kNoPack, k.k16 ? xp.k16 : kNoPack, ss, st));
+  });
 }
 
 // The launch sequence of one decode layer (arguments already validated).  On entry
@@ -290,10 +293,9 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
                     const int32_t* bt, int max_blocks, const int32_t* ctx, int B, const AttnPlan& apl,
                     const LayerBufs& L, const float* next_gain, Kinds next, hipStream_t st, const Probe* probe) {
   const int H = c->hidden, D = c->head_dim, qd = c->n_q_heads * D, kvd = c->n_kv_heads * D, F = c->ffn;
-  hipError_t e;
+  gr_status s;
   // 1. q, k, v = (W (x * g)) / rms(x); zero the FFN-norm accumulator for step 4
-  {
-    ProbeScope ps(probe, GR_STAGE_QKV, st);
+  s = probed(probe, GR_STAGE_QKV, st, [&] {
     const void* ws[3] = {w->wq, w->wk, w->wv};
     const int ts[3] = {w->tq, w->tk, w->tv};
     const int rs[3] = {qd, kvd, kvd};
@@ -305,9 +307,9 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
     ep.eps = c->rms_eps;
     ep.zero_ptr = L.ss_ffn;
     ep.zero_n = B;
-    e = gemm_run(ws, ts, rs, 3, H, B, L.xp, ep, st);
-    if (e != hipSuccess) return check_launch(e);
-  }
+    return check_launch(gemm_run(ws, ts, rs, 3, H, B, L.xp, ep, st));
+  });
+  if (s != GR_OK) return s;
   // 2. QK-norm, RoPE, KV append and split attention
   AttnParams ap{};
   ap.B = B;
@@ -335,21 +337,16 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   ap.o_part = L.o_part;
   ap.m_part = L.m_part;
   ap.l_part = L.l_part;
-  {
-    ProbeScope ps(probe, GR_STAGE_ATTN, st);
-    e = launch_attn_split(c->kv_dtype, true, ap, st);
-  }
-  if (e != hipSuccess) return check_launch(e);
+  s = probed(probe, GR_STAGE_ATTN, st, [&] { return check_launch(launch_attn_split(c->kv_dtype, true, ap, st)); });
+  if (s != GR_OK) return s;
   // 3. log-sum-exp merge -> Wo input pack
-  {
-    ProbeScope ps(probe, GR_STAGE_ATTN_MERGE, st);
+  s = probed(probe, GR_STAGE_ATTN_MERGE, st, [&] {
     const PackOut& op = L.op.of(w->to);
-    e = launch_attn_merge(ap, nullptr, op.pack, op.kind, nslices_of(op.kind, qd), 1, st);
-    if (e != hipSuccess) return check_launch(e);
-  }
+    return check_launch(launch_attn_merge(ap, nullptr, op.pack, op.kind, nslices_of(op.kind, qd), 1, st));
+  });
+  if (s != GR_OK) return s;
   // 4. x += Wo o; pack x * ffn_norm and its sum of squares for the gate/up GEMM
-  {
-    ProbeScope ps(probe, GR_STAGE_WO, st);
+  s = probed(probe, GR_STAGE_WO, st, [&] {
     const void* ws[1] = {w->wo};
     const int ts[1] = {w->to};
     const int rs[1] = {H};
@@ -361,20 +358,18 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
     ep.out1 = L.xp.of(w->tgate);
     ep.out_k = H;
     ep.ss_out = L.ss_ffn;
-    e = gemm_run(ws, ts, rs, 1, qd, B, L.op, ep, st);
-    if (e != hipSuccess) return check_launch(e);
-  }
+    return check_launch(gemm_run(ws, ts, rs, 1, qd, B, L.op, ep, st));
+  });
+  if (s != GR_OK) return s;
   // 5. a = silu(gate) * up (inputs divided by rms) -> down input pack; zero the
   //    attention-norm accumulator for step 6
-  {
-    ProbeScope ps(probe, GR_STAGE_GATE_UP, st);
-    e = gemm_swiglu(w->w_gate, w->w_up, w->tgate, F, H, B, L.xp, L.ss_ffn, c->rms_eps, L.ap.of(w->tdown),
-                    L.ss_attn, B, st);
-    if (e != hipSuccess) return check_launch(e);
-  }
+  s = probed(probe, GR_STAGE_GATE_UP, st, [&] {
+    return check_launch(gemm_swiglu(w->w_gate, w->w_up, w->tgate, F, H, B, L.xp, L.ss_ffn, c->rms_eps,
+                                    L.ap.of(w->tdown), L.ss_attn, B, st));
+  });
+  if (s != GR_OK) return s;
   // 6. x += W_down a; pack x * next_gain for the next consumer
-  {
-    ProbeScope ps(probe, GR_STAGE_DOWN, st);
+  return probed(probe, GR_STAGE_DOWN, st, [&] {
     const void* ws[1] = {w->w_down};
     const int ts[1] = {w->tdown};
     const int rs[1] = {H};
@@ -389,26 +384,25 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
       ep.out_k = H;
       ep.ss_out = L.ss_attn;
     }
-    e = gemm_run(ws, ts, rs, 1, F, B, L.ap, ep, st);
-    if (e != hipSuccess) return check_launch(e);
-  }
-  return GR_OK;
+    return check_launch(gemm_run(ws, ts, rs, 1, F, B, L.ap, ep, st));
+  });
 }
 
 // Output head on a packed input (x * norm in xp, sum of squares in ss).
 gr_status run_head(const void* w, int wtype, float* logits, int B, int H, int vocab, float eps, const Pack2& xp,
                    const float* ss, hipStream_t st, const Probe* probe) {
-  ProbeScope ps(probe, GR_STAGE_HEAD, st);
-  const void* ws[1] = {w};
-  const int ts[1] = {wtype};
-  const int rs[1] = {vocab};
-  Epi ep;
-  ep.kind = kEpiStore;
-  ep.y = logits;
-  ep.ldy = vocab;
-  ep.ss = ss;
-  ep.eps = eps;
-  return check_launch(gemm_run(ws, ts, rs, 1, H, B, xp, ep, st));
+  return probed(probe, GR_STAGE_HEAD, st, [&] {
+    const void* ws[1] = {w};
+    const int ts[1] = {wtype};
+    const int rs[1] = {vocab};
+    Epi ep;
+    ep.kind = kEpiStore;
+    ep.y = logits;
+    ep.ldy = vocab;
+    ep.ss = ss;
+    ep.eps = eps;
+    return check_launch(gemm_run(ws, ts, rs, 1, H, B, xp, ep, st));
+  });
 }
 
 }  // namespace
@@ -736,9 +730,11 @@ gr_status gr_decode_stack_probed(const gr_layer_cfg* c, const gr_layer_weights* 
                                  const int32_t* bt, int max_blocks, const int32_t* ctx, int max_ctx, int B,
                                  const float* head_norm, const void* head_w, int head_wtype, int vocab,
                                  float* logits, void* ws, size_t ws_bytes, void* stream, int probe_stage,
-                                 void* const* ev_begin, void* const* ev_end) {
+                                 int probe_reps, void* const* ev_begin, void* const* ev_end) {
+  if (probe_reps < 1 || probe_reps > 1000) return GR_ERR_SHAPE;
   Probe pr;
   pr.stage = probe_stage;
+  pr.reps = probe_reps;
   pr.ev_begin = ev_begin;
   pr.ev_end = ev_end;
   return decode_stack_impl(c, weights, n_layers, k_pages, v_pages, num_pages, x, bt, max_blocks, ctx, max_ctx, B,

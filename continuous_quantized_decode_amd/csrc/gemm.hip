@@ -41,31 +41,20 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-constexpr int kQ4Stage = 16 * kQ4KBytes;  // 2304 B: 16 rows x one super-block
-constexpr int kQ6Row = 212;                // 53 dwords per row slot
-constexpr int kQ6Stage = 16 * kQ6Row;      // 3392 B
-constexpr int kQ4LoadInstr = 3;            // 144 chunks of 16 B
-constexpr int kQ6LoadInstr = 14;           // 16 x 53 dword slots
+constexpr int kQ4LoadInstr = 3;             // 144 chunks of 16 B, 64 per instruction
+constexpr int kQ6LoadInstr = 14;            // 16 x 53 dword slots, 64 per instruction
+constexpr int kQ6Row = 212;                 // 53 dwords per row slot
+// Every lane of every load instruction loads (lanes past the tile's data re-read a
+// valid chunk into the padding), so each stage is exactly kQ*LoadInstr VMEM
+// instructions on every path and the vmcnt waits below are exact.
+constexpr int kQ4Stage = kQ4LoadInstr * 64 * 16;  // 3072 B (2304 used)
+constexpr int kQ6Stage = kQ6LoadInstr * 64 * 4;   // 3584 B (3392 used)
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
 GR_DEV void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Prefetch loads into registers whose completion the wave bodies guard with their own
-// vmcnt waits (the compiler's wait insertion is too conservative across the unrolled
-// two-buffer loop and would wait for the newer buffer too).  `base` is wave-uniform.
-GR_DEV u32x4 ldg_x4(const void* base, u32 voff) {
-  u32x4 r;
-  asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(base));
-  return r;
-}
-GR_DEV u32 ldg_u16(const void* base, u32 voff) {
-  u32 r;
-  asm volatile("global_load_ushort %0, %1, %2" : "=v"(r) : "v"(voff), "s"(base));
-  return r;
 }
 
 // Hides a value from the optimiser so that address arithmetic derived from it is
@@ -91,11 +80,10 @@ GR_DEV void q4_issue(const TileRows& tr, int sb, lds_u8* slot, int lane) {
   const u32 sbo = (u32)sb * kQ4KBytes;
 #pragma unroll
   for (int i = 0; i < kQ4LoadInstr; ++i) {
-    const int c = l + 64 * i;
+    const int c = min(l + 64 * i, 143);
     const int r = c / 9, pc = c - 9 * r;
     const uint8_t* src = tr.base + (tr.off(r) + sbo + 16 * pc);
-    if (i < kQ4LoadInstr - 1 || lane < 144 - 64 * (kQ4LoadInstr - 1))
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(slot + 1024 * i), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(slot + 1024 * i), 16, 0, 0);
   }
 }
 
@@ -110,14 +98,13 @@ GR_DEV void q6_issue(const TileRows& tr, int sb, lds_u8* slot, int lane) {
   const u32 blo = (u32)(uintptr_t)tr.base;
 #pragma unroll
   for (int i = 0; i < kQ6LoadInstr; ++i) {
-    const int c = l + 64 * i;
+    const int c = min(l + 64 * i, 16 * 53 - 1);  // past the data: re-read the last slot
     const int r = c / 53, wd = c - 53 * r;
     const u32 o = tr.off(r) + sbo;
     const u32 sh = (blo + o) & 3u;
     const int wde = (wd == 52 && sh == 0) ? 51 : wd;
     const uint8_t* src = tr.base + ((o + 4u * (u32)wde) - sh);
-    if (i < kQ6LoadInstr - 1 || lane < 16 * 53 - 64 * (kQ6LoadInstr - 1))
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(slot + 256 * i), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(slot + 256 * i), 4, 0, 0);
   }
 }
 
@@ -199,7 +186,7 @@ GR_DEV void q4_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, i
     for (int t = 0; t < NT; ++t) q4_issue(tr[t], sb, ring + (b.slot * NT + t) * kQ4Stage, lane);
     if constexpr (BTN == 1) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b.a[j] = ldg_x4(a.xpack, ((u32)sb * 8 + j) * 1024u + 16u * lane);
+      for (int j = 0; j < 8; ++j) b.a[j] = ((const u32x4*)a.xpack)[((size_t)sb * 8 + j) * 64 + lane];
     }
   };
   auto step = [&](Q4Buf<NT, NA>& b, int sb, bool newer_in_flight) {
@@ -300,11 +287,11 @@ GR_DEV void q6_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, i
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       q6_issue(tr[t], sb, ring + (b.slot * NT + t) * kQ6Stage, lane);
-      b.d[t] = ldg_u16(tr[t].base, tr[t].off(n) + (u32)sb * kQ6KBytes + 208u);
+      b.d[t] = *(const u16*)(tr[t].base + (tr[t].off(n) + (u32)sb * kQ6KBytes + 208u));
     }
     if constexpr (BTN == 1) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b.a[j] = ldg_x4(a.xpack, ((u32)sb * 8 + j) * 1024u + 16u * lane);
+      for (int j = 0; j < 8; ++j) b.a[j] = ((const u32x4*)a.xpack)[((size_t)sb * 8 + j) * 64 + lane];
     }
   };
   auto step = [&](Q6Buf<NT, NA>& b, int sb, bool newer_in_flight) {

@@ -9,9 +9,10 @@
 
 namespace gr {
 
-constexpr int kPackThreads = 256;
+constexpr int kPackThreads = 1024;
 
-// grid: 8 * actpack_tiles(B) blocks, one per (padded) batch row.
+// grid: 8 * actpack_tiles(B) blocks, one per (padded) batch row; each thread takes
+// four consecutive columns per pass (K % 256 == 0, x rows 16-byte aligned).
 __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __restrict__ x, int ldx, int B, int K,
                                                                  const float* __restrict__ gain, PackOut o1,
                                                                  PackOut o2, float* ss_out) {
@@ -19,15 +20,21 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
   const int ns1 = o1.kind == kK32 ? K / 32 : K / 16, ns2 = o2.kind == kK32 ? K / 32 : K / 16;
   __shared__ float red[kPackThreads / 64];
   float ss = 0.f;
-  for (int k = tid; k < K; k += kPackThreads) {
-    float v = 0.f;
+  for (int k0 = 4 * tid; k0 < K; k0 += 4 * kPackThreads) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (b < B) {
-      const float xv = x[(size_t)b * ldx + k];
-      ss = __builtin_fmaf(xv, xv, ss);
-      v = gain ? xv * gain[k] : xv;
+      const f32x4 xv = *(const f32x4*)(x + (size_t)b * ldx + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ss = __builtin_fmaf(xv[i], xv[i], ss);
+        v[i] = gain ? xv[i] * gain[k0 + i] : xv[i];  // gains are only 4-byte aligned
+      }
     }
-    if (o1.pack) actpack_put(o1.pack, o1.kind, ns1, b, k, v);
-    if (o2.pack) actpack_put(o2.pack, o2.kind, ns2, b, k, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (o1.pack) actpack_put(o1.pack, o1.kind, ns1, b, k0 + i, v[i]);
+      if (o2.pack) actpack_put(o2.pack, o2.kind, ns2, b, k0 + i, v[i]);
+    }
   }
   if (ss_out && b < B) {
     ss = wave_sum(ss);

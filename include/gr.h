@@ -179,11 +179,15 @@ gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
                           const float* head_norm, const void* head_w, int head_wtype, int vocab, float* logits,
                           void* workspace, size_t ws_bytes, void* stream);
 
-/* Timing probe (profiling hook): the same launches as gr_decode_stack, plus
- * hipEventRecord(ev_begin[l]) on `stream` just before and hipEventRecord(ev_end[l])
- * just after the launches of stage `probe_stage` of layer l (ev_*[0] for the pack
- * and head stages).  ev_begin / ev_end are host arrays of hipEvent_t with n_layers entries
- * (1 for GR_STAGE_HEAD), created by the caller. */
+/* Timing probe (profiling hook): the same launches as gr_decode_stack, except that
+ * the launches of stage `probe_stage` are issued `probe_reps` times (1..1000) in a
+ * row, between hipEventRecord(ev_begin[l]) and hipEventRecord(ev_end[l]) on `stream`
+ * for layer l (ev_*[0] for the pack and head stages).  Repeating a stage recomputes
+ * the same outputs, except that the residual stages (Wo, down) add their product to x
+ * once per repetition, so x is meaningful only with probe_reps == 1.  ev_begin /
+ * ev_end are host arrays of hipEvent_t with n_layers entries (1 for GR_STAGE_HEAD and
+ * GR_STAGE_PACK), created by the caller.  Errors as gr_decode_stack; GR_ERR_SHAPE for
+ * a stage or repetition count out of range. */
 typedef enum {
   GR_STAGE_PACK = 0,       /* RMSNorm input pack of the first layer (or of the head) */
   GR_STAGE_QKV = 1,        /* q, k, v GEMM */
@@ -200,7 +204,8 @@ gr_status gr_decode_stack_probed(const gr_layer_cfg* c, const gr_layer_weights* 
                                  const int32_t* block_table, int max_blocks_per_row, const int32_t* ctx_lens,
                                  int max_ctx, int B, const float* head_norm, const void* head_w, int head_wtype,
                                  int vocab, float* logits, void* workspace, size_t ws_bytes, void* stream,
-                                 int probe_stage, void* const* ev_begin, void* const* ev_end);
+                                 int probe_stage, int probe_reps, void* const* ev_begin,
+                                 void* const* ev_end);
 
 #ifdef __cplusplus
 }

@@ -62,6 +62,8 @@ def _declare(L: C.CDLL) -> None:
     for n in ("orc_q4k_dequant", "orc_q6k_dequant", "orc_q8_0_dequant"):
         getattr(L, n).argtypes = [_p, _i64, _p]
         getattr(L, n).restype = None
+    L.orc_num_threads.argtypes = []
+    L.orc_num_threads.restype = _i
     L.orc_gemm.argtypes = [_i, _p, _p, _p, _i, _i, _i]
     L.orc_gemm.restype = _i
     L.orc_rmsnorm.argtypes = [_p, _p, _d, _i, _p]
@@ -91,6 +93,11 @@ def _declare(L: C.CDLL) -> None:
     L.orc_decode_layer.restype = _i
     L.orc_output_head.argtypes = [_p, _p, _d, _p, _i, _p, _i, _i, _i]
     L.orc_output_head.restype = _i
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops run on."""
+    return int(lib().orc_num_threads())
 
 
 def _ptr(a: Optional[np.ndarray]) -> Optional[int]:

@@ -25,6 +25,7 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (see build.py).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -534,3 +535,6 @@ int orc_output_head(const double* x, const float* norm, double eps, const uint8_
   free(xn);
   return rc;
 }
+
+/* Threads the parallel loops above use (bookkeeping for timing reports; no arithmetic). */
+int orc_num_threads(void) { return omp_get_max_threads(); }

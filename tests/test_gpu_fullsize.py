@@ -1,0 +1,196 @@
+"""GPU parity at the workloads' full sizes, through the C ABI.
+
+* llama3_8b: the whole step exactly as bench.py times it (32 layers and the
+  128256-row Q6_K head, B=8, f16 KV, one HIP graph), every logit against the
+  fp64 oracle run over the same 32 layers and head.
+* qwen3_8b: full layer shapes, B=32 (four batch tiles), q8_0 KV in a fragmented
+  pool filled to 90 %; the oracle follows the first layers of the stack, and the
+  batched rows equal the same rows decoded alone.
+* longctx: one Llama-3-8B layer at B=64 (eight batch tiles) with contexts up to
+  32768 tokens in q8_0.
+
+Bars as elsewhere: relative L2 2e-3 (f16 KV) and 5e-3 (q8_0 KV) against the oracle;
+1e-5 between GPU runs that differ only in launch form (graph replay, batch subset).
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import dev, host, rel_l2, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def tol(kv_dtype):
+    return 5e-3 if kv_dtype == synth.KV_Q8_0 else 2e-3
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return torch_cuda()
+
+
+@pytest.fixture(scope="module")
+def gr():
+    import continuous_quantized_decode_amd as gr
+    gr.lib()
+    return gr
+
+
+def cfg_of(gr, wl):
+    return gr.layer_cfg(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.ffn, wl.rms_eps, wl.rope_theta,
+                        wl.rope_style, wl.qk_norm, wl.kv_dtype)
+
+
+def upload(gr, torch, lw):
+    t = {k: dev(getattr(lw, k), torch) for k in ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo", "w_gate", "w_up",
+                                                  "w_down")}
+    if lw.q_norm is not None:
+        t["q_norm"], t["k_norm"] = dev(lw.q_norm, torch), dev(lw.k_norm, torch)
+    t.update({k: getattr(lw, k) for k in ("tq", "tk", "tv", "to", "tgate", "tup", "tdown")})
+    return t, gr.layer_weights(t)
+
+
+class Stack:
+    """A workload's first n layers resident on the GPU, with host copies for the oracle."""
+
+    def __init__(self, gr, torch, wl, n_layers, ctx=None):
+        self.wl = wl
+        self.ctx = synth.ctx_lens(wl) if ctx is None else np.asarray(ctx, np.int32)
+        self.kv = synth.kv_state(wl, self.ctx, n_layers=n_layers)
+        self.pm = self.kv.pages
+        self.host_layers = [synth.layer_weights(wl, i) for i in range(n_layers)]
+        keep, ws = zip(*[upload(gr, torch, lw) for lw in self.host_layers])
+        self.keep = keep
+        self.k = [dev(p, torch) for p in self.kv.k_pools]
+        self.v = [dev(p, torch) for p in self.kv.v_pools]
+        self.cfg = cfg_of(gr, wl)
+        self.args = gr.StackArgs(self.cfg, list(ws), self.k, self.v)
+        self.bt, self.cg = dev(self.pm.block_table, torch), dev(self.ctx, torch)
+        self.max_ctx = int(self.ctx.max())
+
+    def oracle(self, orc, x):
+        for i, lw in enumerate(self.host_layers):
+            x = orc.decode_layer(self.wl, lw, self.kv.k_pools[i].copy(), self.kv.v_pools[i].copy(), x,
+                                 self.pm.block_table, self.ctx)
+        return x
+
+
+def test_llama3_8b_step_matches_oracle(torch, gr, orc):
+    wl = synth.WORKLOADS["llama3_8b"]
+    say("llama3_8b full step: upload")
+    st = Stack(gr, torch, wl, wl.n_layers)
+    hn, hw = synth.head_weights(wl)
+    hn_d, hw_d = dev(hn, torch), dev(hw, torch)
+    x0_host = synth.input_x(wl)
+    x0 = dev(x0_host, torch)
+    x = torch.empty_like(x0)
+    logits = torch.empty((wl.batch, wl.vocab), dtype=torch.float32, device="cuda")
+    ws = gr.workspace(gr.decode_stack_workspace_size(st.cfg, wl.batch, st.max_ctx, wl.vocab))
+
+    def step():
+        x.copy_(x0)
+        gr.gr_decode_stack(st.args, st.pm.num_pages, x, st.bt, st.cg, st.max_ctx, hn_d, hw_d, wl.w_head, wl.vocab,
+                           logits, ws=ws)
+
+    say("  eager step")
+    step()
+    torch.cuda.synchronize()
+    eager_x, eager_logits = host(x), host(logits)
+    # the launch form bench.py times: one graph, replayed
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {r}")
+        assert rel_l2(host(logits), eager_logits) <= 1e-5
+        assert rel_l2(host(x), eager_x) <= 1e-5
+        logits.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+    say("  oracle: 32 layers + head")
+    want_x = st.oracle(orc, x0_host)
+    want_logits = orc.output_head(want_x, hn, wl.rms_eps, hw, wl.w_head, wl.vocab)
+    ex, el = rel_l2(eager_x, want_x), rel_l2(eager_logits, want_logits)
+    say(f"  rel_l2 x {ex:.3e} logits {el:.3e}")
+    assert np.isfinite(eager_logits).all()
+    assert ex <= tol(wl.kv_dtype)
+    assert el <= tol(wl.kv_dtype)
+    # the argmax of each row agrees wherever the oracle's top two logits are apart
+    top2 = np.sort(want_logits, axis=1)[:, -2:]
+    clear = (top2[:, 1] - top2[:, 0]) > 1e-2 * np.abs(top2[:, 1])
+    assert np.array_equal(eager_logits.argmax(1)[clear], want_logits.argmax(1)[clear])
+
+
+QWEN_LAYERS = 3
+
+
+def test_qwen3_8b_full_shape_layers_match_oracle(torch, gr, orc):
+    wl = synth.WORKLOADS["qwen3_8b"]
+    say(f"qwen3_8b: {QWEN_LAYERS} full-shape layers, B={wl.batch}, q8_0 KV")
+    st = Stack(gr, torch, wl, QWEN_LAYERS)
+    x0 = synth.input_x(wl)
+    xg = dev(x0, torch)
+    gr.gr_decode_stack(st.args, st.pm.num_pages, xg, st.bt, st.cg, st.max_ctx)
+    got = host(xg)
+    want = st.oracle(orc, x0)
+    err = rel_l2(got, want)
+    say(f"  rel_l2 {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= tol(wl.kv_dtype)
+    # rows of the full batch equal the same rows decoded alone, in another order
+    # (re-running rewrites each row's appended KV slot with the same values)
+    rows = [31, 0, 17]
+    xs = dev(x0[rows], torch)
+    gr.gr_decode_stack(st.args, st.pm.num_pages, xs, dev(st.pm.block_table[rows], torch), dev(st.ctx[rows], torch),
+                       st.max_ctx)
+    assert rel_l2(host(xs), got[rows]) <= 1e-5
+
+
+def test_longctx_layer_matches_oracle(torch, gr, orc):
+    wl = synth.WORKLOADS["longctx"]
+    say(f"longctx: 1 layer, B={wl.batch}, ctx up to {wl.ctx_hi}")
+    st = Stack(gr, torch, wl, 1)
+    x0 = synth.input_x(wl)
+    xg = dev(x0, torch)
+    gr.gr_decode_stack(st.args, st.pm.num_pages, xg, st.bt, st.cg, st.max_ctx)
+    got = host(xg)
+    want = st.oracle(orc, x0)
+    err = rel_l2(got, want)
+    say(f"  rel_l2 {err:.3e} (max ctx {st.max_ctx})")
+    assert np.isfinite(got).all()
+    assert err <= tol(wl.kv_dtype)
+
+
+def test_probed_stack_equals_stack(torch, gr):
+    """The timing probe with one repetition launches exactly the stack's work."""
+    wl = synth.WORKLOADS["qwen3_0p6b"]
+    st = Stack(gr, torch, wl, 2)
+    x0 = synth.input_x(wl)
+    xa = dev(x0, torch)
+    gr.gr_decode_stack(st.args, st.pm.num_pages, xa, st.bt, st.cg, st.max_ctx)
+    ref = host(xa)
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    evs = []
+    for _ in range(4):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    for stage in range(len(gr.STAGES) - 1):  # no head in this stack
+        # re-running rewrites the appended token's KV slot with the same values
+        xb = dev(x0, torch)
+        gr.gr_decode_stack_probed(st.args, st.pm.num_pages, xb, st.bt, st.cg, st.max_ctx, stage, 1, evs[:2],
+                                  evs[2:])
+        assert rel_l2(host(xb), ref) <= 1e-5, gr.STAGES[stage]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    for e in evs:
+        hip.hipEventDestroy(e)

@@ -88,6 +88,10 @@ GEMM_CASES = [
     (synth.W_Q6_K, 8, 4096, 14336),
     (synth.W_Q6_K, 12, 100, 1280),
     (synth.W_Q6_K, 32, 256, 1024),
+    (synth.W_Q6_K, 32, 256, 4096),   # several super-blocks per wave with four batch tiles
+    (synth.W_Q6_K, 16, 256, 12288),
+    (synth.W_Q6_K, 64, 128, 14336),
+    (synth.W_Q4_K, 64, 256, 14336),
 ]
 
 
