@@ -90,26 +90,94 @@ def kv_bytes_per_token(wl) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the HIP sources with comments and blank space removed, so counter data
+    stays valid across edits that change no code."""
+    import re
     h = hashlib.sha256()
     d = os.path.join(ROOT, "continuous_quantized_decode_amd", "csrc")
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(d, f), "rb").read())
+            src = open(os.path.join(d, f)).read()
+            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+            src = re.sub(r"//[^\n]*", " ", src)
+            h.update(f.encode() + b"\0" + " ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel: str, per_launch_bytes: float):
-    """HBM bytes per launch of `kernel` from the committed counter summary, if it was
-    taken on the current kernel sources; else None."""
+def committed_traffic(stage: str):
+    """Measured HBM bytes per launch of `stage`'s kernel from profiles/traffic.json, if
+    the counters were taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         d = json.load(open(p))
     except (OSError, ValueError):
         return None
-    e = d.get(kernel)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if d.get("source_hash") != kernel_source_hash():
         return None
-    return e.get("bytes_per_launch")
+    e = d.get("stages", {}).get(stage)
+    return None if not e else e.get("bytes_per_launch")
+
+
+COPY_KERNEL = "neg"  # the calibration kernel: torch.neg over a float32 buffer
+
+
+def pmc_rows(csv_path: str, counter: str):
+    """(kernel name, grid size, value in bytes) per dispatch from a rocprofv3
+    counter_collection.csv (FETCH_SIZE / WRITE_SIZE are reported in KiB)."""
+    import csv
+    out = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]) * 1024.0))
+    return out
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, launches: dict, out_path: str):
+    """Scale each stage kernel's FETCH_SIZE + WRITE_SIZE by what the same counters read
+    for a plain copy of copy_bytes (read copy_bytes, write copy_bytes) and write
+    profiles/traffic.json.  launches: stage -> (kernel name substring, grid size)."""
+    import numpy as np
+    res = {"source_hash": kernel_source_hash(), "copy_bytes": copy_bytes, "stages": {}}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = pmc_rows(path, counter)
+        copy = [v for k, g, v in rows if COPY_KERNEL in k]
+        if not copy:
+            raise SystemExit(f"no calibration copy dispatch in {path}")
+        scale = copy_bytes / float(np.median(copy))
+        res[counter.lower() + "_scale"] = round(scale, 4)
+        for stage, (name, grid) in launches.items():
+            vals = [v for k, g, v in rows if name in k and (grid is None or g == grid)]
+            if vals:
+                per.setdefault(stage, {})[counter] = (float(np.mean(vals)) * scale, len(vals))
+    for stage, c in per.items():
+        if "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+            res["stages"][stage] = {"kernel": launches[stage][0], "grid_size": launches[stage][1],
+                                    "dispatches": c["FETCH_SIZE"][1],
+                                    "fetch_bytes": round(c["FETCH_SIZE"][0]), "write_bytes": round(c["WRITE_SIZE"][0]),
+                                    "bytes_per_launch": round(c["FETCH_SIZE"][0] + c["WRITE_SIZE"][0])}
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
+def stage_launches(gr, wl) -> dict:
+    """stage -> (kernel name as the profilers print it, grid size in threads or None)."""
+    B, H, F = wl.batch, wl.hidden, wl.ffn
+    qkv_rows = wl.q_dim + 2 * wl.kv_dim
+    shapes = {"qkv": (wl.w_other, qkv_rows, H, False), "wo": (wl.w_other, H, wl.q_dim, False),
+              "gate_up": (wl.w_other, F, H, True), "down": (wl.w_down, H, F, False)}
+    if wl.vocab:
+        shapes["head"] = (wl.w_head, wl.vocab, H, False)
+    out = {s: (sh["kernel"], sh["grid_threads"])
+           for s, sh in ((s, gr.gr_gemm_launch_shape(*v[:3], B, v[3])) for s, v in shapes.items())}
+    kvdt = {0: 0, 1: 1, 2: 2}[wl.kv_dtype]
+    out["attn"] = (f"attn_split_kernel<{kvdt}, {wl.head_dim}, true>", None)
+    out["attn_merge"] = ("attn_merge_kernel", None)
+    out["pack"] = ("pack_rows_kernel", None)
+    return out
 
 
 # ------------------------------------------------------------------------ main
@@ -120,10 +188,24 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
+                    help="also run the counter-calibration copy (torch.neg over BYTES of float32)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs of this script "
+                         "with --copy-calib (no GPU work)")
     ap.add_argument("--cpu-layers", type=int, default=64, help="layers the oracle runs (the rest are scaled)")
-    ap.add_argument("--probe-runs", type=int, default=2, help="probed stack runs per stage")
-    ap.add_argument("--probe-reps", type=int, default=8, help="back-to-back launches of the probed stage")
+    ap.add_argument("--probe-runs", type=int, default=5, help="replays of the probed step per stage")
+    ap.add_argument("--probe-reps", type=int, default=1,
+                    help="launches of the probed stage per probe (above 1, a repeat may hit in cache)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        import continuous_quantized_decode_amd as gr
+        import synth
+        wl = synth.WORKLOADS[args.workload]
+        res = summarize_pmc(args.pmc_summary[0], args.pmc_summary[1], args.copy_calib or (1 << 30),
+                            stage_launches(gr, wl), os.path.join(ROOT, "profiles", "traffic.json"))
+        print(json.dumps(res))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode path runs on a single MI355X and has no multi-GPU mode "
               "(rows are independent; a multi-GPU run would shard them, as data-parallel replicas).", file=sys.stderr)
@@ -218,7 +300,11 @@ def main():
     sb, head_b, pack_b = stage_bytes(wl, ctx, kvb)
     step_bytes = wl.n_layers * sum(sb.values()) + head_b + pack_b
 
-    # ---- per-stage live timing with HIP events around each stage's launches
+    # ---- per-stage live timing: HIP events recorded on the launch stream around one
+    #      stage's launch in every layer of an eager step.  Each probed step is enqueued
+    #      right behind a replay of the timed graph, so the host stays ahead of the GPU
+    #      and no launch waits on the host; each launch runs once, in its place in the
+    #      step, so no cache holds its weights from a repeat.
     hip = Hip()
     n_ev = max(wl.n_layers, 1)
     evb = [hip.event() for _ in range(n_ev)]
@@ -230,6 +316,7 @@ def main():
         once = name in ("head", "pack")
         durs = []
         for _ in range(args.probe_runs):
+            graph.replay()
             x.copy_(x0)
             gr.gr_decode_stack_probed(sargs, pm.num_pages, x, bt, cg, max_ctx, si, args.probe_reps, evb, eve,
                                       head_norm, head_w, wl.w_head, wl.vocab, logits, ws=ws)
@@ -247,13 +334,11 @@ def main():
     dom = max(stages, key=lambda k: stages[k]["us_per_step"])
     d = stages[dom]
     achieved = d["bytes_per_launch"] / (d["avg_us"] * 1e-6) / 1e9
-    kernel_names = {"attn": "attn_split_kernel", "attn_merge": "attn_merge_kernel", "pack": "pack_rows_kernel",
-                    "qkv": "gemm_kernel<12,...>", "wo": "gemm_kernel<12,...>", "gate_up": "gemm_kernel<12,2,...>",
-                    "down": f"gemm_kernel<{wl.w_down},...>", "head": f"gemm_kernel<{wl.w_head},...>"}
+    launches = stage_launches(gr, wl)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": committed_traffic(dom, d["bytes_per_launch"]),
-                "kernel": kernel_names.get(dom, dom), "stage": dom,
+                "traffic": committed_traffic(dom),
+                "kernel": launches[dom][0], "grid_threads": launches[dom][1], "stage": dom,
                 "bytes_per_launch": d["bytes_per_launch"], "avg_launch_us": d["avg_us"]}
     log("[bench] stages: " + json.dumps(stages))
 
@@ -317,6 +402,16 @@ def main():
         "stages": stages,
     }
     print(json.dumps(out), flush=True)
+
+    if args.copy_calib:
+        # the counter calibration: a plain streaming kernel over a known byte count
+        n = args.copy_calib // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.copy_calib} bytes read and written by torch.neg, 3 times")
 
 
 if __name__ == "__main__":

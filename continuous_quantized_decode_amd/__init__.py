@@ -74,6 +74,8 @@ def _load() -> C.CDLL:
         getattr(L, n).restype = _i
     L.gr_gemm_workspace_size.argtypes = [_i, _i, _i]
     L.gr_gemm_workspace_size.restype = _sz
+    L.gr_gemm_launch_shape.argtypes = [_i, _i, _i, _i, _i] + [C.POINTER(_i)] * 5
+    L.gr_gemm_launch_shape.restype = _i
     for n in ("gr_q4k_gemm", "gr_q6k_gemm"):
         getattr(L, n).argtypes = [_p, _p, _p, _i, _i, _i, _p, _sz, _p]
         getattr(L, n).restype = _i
@@ -110,7 +112,8 @@ def lib() -> C.CDLL:
 
 
 EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_bytes", "gr_q4k_dequant",
-            "gr_q6k_dequant", "gr_q8_0_dequant", "gr_gemm_workspace_size", "gr_q4k_gemm", "gr_q6k_gemm",
+            "gr_q6k_dequant", "gr_q8_0_dequant", "gr_gemm_workspace_size", "gr_gemm_launch_shape", "gr_q4k_gemm",
+            "gr_q6k_gemm",
             "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_paged_gather_kv",
             "gr_decode_layer_workspace_size", "gr_decode_layer", "gr_output_head_workspace_size", "gr_output_head",
             "gr_decode_stack_workspace_size", "gr_decode_stack", "gr_decode_stack_probed")
@@ -197,6 +200,15 @@ def gr_q4k_gemm(wblocks, x, n: int, y=None, ws=None):
 
 def gr_q6k_gemm(wblocks, x, n: int, y=None, ws=None):
     return _gemm("gr_q6k_gemm", wblocks, x, n, y, ws)
+
+
+def gr_gemm_launch_shape(wtype: int, rows: int, k: int, b: int, pair: bool = False) -> dict:
+    """Kernel template parameters and grid of the GEMM launch for these sizes."""
+    v = [C.c_int() for _ in range(5)]
+    _check("gr_gemm_launch_shape", _load().gr_gemm_launch_shape(wtype, rows, k, b, int(pair), *[C.byref(i) for i in v]))
+    nt, btn, maxt, grid, block = (i.value for i in v)
+    return {"nt": nt, "btn": btn, "maxt": maxt, "grid_threads": grid, "block_threads": block,
+            "kernel": f"gemm_kernel<{wtype}, {nt}, {btn}, {maxt}>"}
 
 
 # --------------------------------------------------------------------------- attention

@@ -13,6 +13,9 @@
 
 namespace gr {
 
+thread_local ProbeEvents* probe_events = nullptr;
+
+
 hipError_t launch_dequant(int kind, const void* blocks, int64_t n, float* out, hipStream_t st);
 hipError_t launch_gather(int kv_dtype, int D, const void* pool, int is_v, const int32_t* bt, const int32_t* ctx,
                          int B, int max_blocks, int n_kv_heads, int max_ctx, float* out, hipStream_t st);
@@ -246,9 +249,8 @@ AttnPlan layer_attn_plan(int B, const gr_layer_cfg* c, int max_ctx) {
   return plan_attn(B, c->n_kv_heads, max_ctx + 1);
 }
 
-// Optional timing probe: events recorded on the launch stream just before and just
-// after the launches of one stage, which are repeated `reps` times in between so the
-// per-launch time is not dominated by the event markers.
+// Optional timing probe: the launches of one stage (repeated `reps` times) carry the
+// probe's start / stop events on their dispatches (see launch_kernel).
 struct Probe {
   int stage = -1;
   int reps = 1;
@@ -257,15 +259,19 @@ struct Probe {
   void* const* ev_end = nullptr;
 };
 
-// Runs body() once, or, for the probed stage, `reps` times between the events.
+// Runs body() once, or, for the probed stage, `reps` times with the layer's events
+// armed on this thread.
 template <class F>
 gr_status probed(const Probe* p, int stage, hipStream_t st, F&& body) {
-  const bool on = p && p->stage == stage;
-  if (on) (void)hipEventRecord((hipEvent_t)p->ev_begin[p->layer], st);
-  const int n = on ? p->reps : 1;
+  (void)st;
+  if (!p || p->stage != stage) return body();
+  ProbeEvents pe;
+  pe.start = (hipEvent_t)p->ev_begin[p->layer];
+  pe.stop = (hipEvent_t)p->ev_end[p->layer];
+  probe_events = &pe;
   gr_status s = GR_OK;
-  for (int r = 0; r < n && s == GR_OK; ++r) s = body();
-  if (on) (void)hipEventRecord((hipEvent_t)p->ev_end[p->layer], st);
+  for (int r = 0; r < p->reps && s == GR_OK; ++r) s = body();
+  probe_events = nullptr;
   return s;
 }
 
@@ -460,6 +466,20 @@ size_t gr_gemm_workspace_size(int B, int N, int K) {
   Carver c(nullptr);
   carve_pack2(c, B, K);
   return c.off + 256;
+}
+
+gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int pair, int* nt, int* btn, int* maxt,
+                               int* grid_threads, int* block_threads) {
+  if (!nt || !btn || !maxt || !grid_threads || !block_threads) return GR_ERR_NULL;
+  if (wtype != GR_W_Q4_K && wtype != GR_W_Q6_K) return GR_ERR_DTYPE;
+  if (rows <= 0 || K <= 0 || K % kQK || B <= 0 || B > 64) return GR_ERR_SHAPE;
+  const GemmPlan pl = plan_gemm(wtype, (rows + 15) / 16, K, B, pair != 0);
+  *nt = pl.nt;
+  *btn = pl.btn;
+  *maxt = pl.maxt;
+  *grid_threads = pl.tiles * pl.waves * 64;
+  *block_threads = pl.waves * 64;
+  return GR_OK;
 }
 
 static gr_status gemm_api(int wtype, const void* w, const float* x, float* y, int B, int N, int K, void* ws,

@@ -16,10 +16,10 @@
 // q8_0 pages are expanded to exact f16 integers in registers; their per-token,
 // per-32-element scales multiply the K scores (K) or fold into P (V).  f32 pages are
 // split into f16 hi/lo operands.  Partials (unnormalized O, running max m, sum l)
-// are merged across splits by log-sum-exp in attn_merge_pack_kernel.
+// are merged across splits by log-sum-exp in attn_merge_kernel.
 //
-// The fused variant (used by the decode layer) also sums the QKV GEMM's split-K
-// partials, applies QK-RMSNorm and RoPE (angles in fp64), stores the new token's K/V
+// The fused variant (used by the decode layer) also reads q, k, v from the QKV
+// GEMM's output, applies QK-RMSNorm and RoPE (angles in fp64), stores the new token's K/V
 // at slot ctx%16 of page block_table[b][ctx/16] in the pool's format, and
 // substitutes those stored values for the slot's contents when it reads that page.
 #include "gr_internal.h"
@@ -444,7 +444,7 @@ size_t attn_partial_floats(int B, int n_q_heads, int head_dim, const AttnPlan& p
 
 hipError_t launch_attn_split(int kv_dtype, bool fused, const AttnParams& p, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)p.B * p.n_kv_heads * p.max_splits));
-#define GR_A(KV, DD, FU) attn_split_kernel<KV, DD, FU><<<grid, 64, 0, st>>>(p)
+#define GR_A(KV, DD, FU) launch_kernel(attn_split_kernel<KV, DD, FU>, grid, dim3(64), 0, st, p)
 #define GR_AD(KV, FU)        \
   if (p.head_dim == 128)     \
     GR_A(KV, 128, FU);       \
@@ -471,8 +471,8 @@ hipError_t launch_attn_split(int kv_dtype, bool fused, const AttnParams& p, hipS
 
 hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, int kind, int nslices, int fused,
                              hipStream_t st) {
-  attn_merge_kernel<<<dim3((unsigned)(p.B * p.n_q_heads)), kMergeThreads, 0, st>>>(p, out, pack, kind, nslices,
-                                                                                    fused);
+  launch_kernel(attn_merge_kernel, dim3((unsigned)(p.B * p.n_q_heads)), dim3(kMergeThreads), 0, st, p, out, pack, kind,
+                nslices, fused);
   return hipGetLastError();
 }
 

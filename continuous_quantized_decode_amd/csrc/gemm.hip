@@ -453,14 +453,14 @@ GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, bool pair) {
 
 #define GR_GEMM_SWITCH(WTv)                                                                          \
   switch (pl.nt * 1000 + pl.btn * 10 + (pl.maxt == 512)) {                                          \
-    case 1011: gemm_kernel<WTv, 1, 1, 512><<<grid, block, lds, st>>>(a); break;                       \
-    case 1020: gemm_kernel<WTv, 1, 2, 256><<<grid, block, lds, st>>>(a); break;                       \
-    case 1040: gemm_kernel<WTv, 1, 4, 256><<<grid, block, lds, st>>>(a); break;                       \
-    case 1080: gemm_kernel<WTv, 1, 8, 256><<<grid, block, lds, st>>>(a); break;                       \
-    case 2010: gemm_kernel<WTv, 2, 1, 256><<<grid, block, lds, st>>>(a); break;                       \
-    case 2020: gemm_kernel<WTv, 2, 2, 256><<<grid, block, lds, st>>>(a); break;                       \
-    case 2040: gemm_kernel<WTv, 2, 4, 256><<<grid, block, lds, st>>>(a); break;                       \
-    case 2080: gemm_kernel<WTv, 2, 8, 256><<<grid, block, lds, st>>>(a); break;                       \
+    case 1011: launch_kernel(gemm_kernel<WTv, 1, 1, 512>, grid, block, lds, st, a); break;                \
+    case 1020: launch_kernel(gemm_kernel<WTv, 1, 2, 256>, grid, block, lds, st, a); break;                \
+    case 1040: launch_kernel(gemm_kernel<WTv, 1, 4, 256>, grid, block, lds, st, a); break;                \
+    case 1080: launch_kernel(gemm_kernel<WTv, 1, 8, 256>, grid, block, lds, st, a); break;                \
+    case 2010: launch_kernel(gemm_kernel<WTv, 2, 1, 256>, grid, block, lds, st, a); break;                \
+    case 2020: launch_kernel(gemm_kernel<WTv, 2, 2, 256>, grid, block, lds, st, a); break;                \
+    case 2040: launch_kernel(gemm_kernel<WTv, 2, 4, 256>, grid, block, lds, st, a); break;                \
+    case 2080: launch_kernel(gemm_kernel<WTv, 2, 8, 256>, grid, block, lds, st, a); break;                \
     default: return hipErrorInvalidValue;                                                            \
   }
 

@@ -1,10 +1,36 @@
 // gr_internal.h -- internal declarations shared by the translation units of libgr.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "gr_common.h"
 #include "../../include/gr.h"
 
 namespace gr {
+
+// ------------------------------------------------------------------ launches
+//
+// Every kernel of the library is launched through launch_kernel.  While a timing
+// probe is armed on this thread (probe_events non-null), the launch attaches the
+// probe's events to the dispatch itself (hipExtLaunchKernelGGL): the start event of
+// the first launch and the stop event of every launch, so the events span exactly
+// the kernels' execution, with no marker or dispatch latency in between.
+struct ProbeEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool first = true;
+};
+extern thread_local ProbeEvents* probe_events;
+
+template <class K, class... A>
+inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t st, A... args) {
+  if (ProbeEvents* pe = probe_events) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)shmem, st, pe->first ? pe->start : nullptr, pe->stop, 0,
+                          args...);
+    pe->first = false;
+  } else {
+    kernel<<<grid, block, shmem, st>>>(args...);
+  }
+}
 
 // ------------------------------------------------------------------------ GEMM
 //

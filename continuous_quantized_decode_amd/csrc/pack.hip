@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
 
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
                             float* ss_out, hipStream_t st) {
-  pack_rows_kernel<<<dim3(8 * actpack_tiles(B)), kPackThreads, 0, st>>>(x, ldx, B, K, gain, o1, o2, ss_out);
+  launch_kernel(pack_rows_kernel, dim3(8 * actpack_tiles(B)), dim3(kPackThreads), 0, st, x, ldx, B, K, gain, o1, o2,
+                ss_out);
   return hipGetLastError();
 }
 

@@ -96,6 +96,17 @@ gr_status gr_q4k_gemm(const void* wblocks, const float* x, float* y, int B, int 
 gr_status gr_q6k_gemm(const void* wblocks, const float* x, float* y, int B, int N, int K, void* workspace,
                       size_t ws_bytes, void* stream);
 
+/* Launch shape of one fused-dequant GEMM launch (a profiling aid: it names the
+ * dispatch a counter or trace row belongs to).  rows: output rows of the launch (for
+ * several matrices sharing one launch, the sum of each one's rows rounded up to 16;
+ * for a gate/up pair, pair = 1 and rows = F).  Returns the kernel's template
+ * parameters (16-row tiles per workgroup nt, 8-row batch tiles btn, launch bound
+ * maxt) and the grid and workgroup sizes in threads, as launched by every entry point
+ * above for these sizes.  GR_ERR_NULL for a null output pointer, GR_ERR_DTYPE for an
+ * unknown type, GR_ERR_SHAPE for rows, K or B out of range. */
+gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int pair, int* nt, int* btn, int* maxt,
+                               int* grid_threads, int* block_threads);
+
 /* ------------------------------------------------------------- attention --
  * Typed attention metadata (tinyllm, Roadmap item 6). */
 typedef struct {
@@ -181,13 +192,15 @@ gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
 
 /* Timing probe (profiling hook): the same launches as gr_decode_stack, except that
  * the launches of stage `probe_stage` are issued `probe_reps` times (1..1000) in a
- * row, between hipEventRecord(ev_begin[l]) and hipEventRecord(ev_end[l]) on `stream`
- * for layer l (ev_*[0] for the pack and head stages).  Repeating a stage recomputes
- * the same outputs, except that the residual stages (Wo, down) add their product to x
- * once per repetition, so x is meaningful only with probe_reps == 1.  ev_begin /
- * ev_end are host arrays of hipEvent_t with n_layers entries (1 for GR_STAGE_HEAD and
- * GR_STAGE_PACK), created by the caller.  Errors as gr_decode_stack; GR_ERR_SHAPE for
- * a stage or repetition count out of range. */
+ * row with events attached to their dispatches (hipExtLaunchKernel): ev_begin[l] is
+ * recorded when the stage's first kernel of layer l starts and ev_end[l] when its last
+ * one ends (ev_*[0] for the pack and head stages), so the interval is the kernels'
+ * execution alone.  Repeating a stage recomputes the same outputs, except that the
+ * residual stages (Wo, down) add their product to x once per repetition, so x is
+ * meaningful only with probe_reps == 1.  ev_begin / ev_end are host arrays of
+ * hipEvent_t with n_layers entries (1 for GR_STAGE_HEAD and GR_STAGE_PACK), created by
+ * the caller.  Not for use under stream capture.  Errors as gr_decode_stack;
+ * GR_ERR_SHAPE for a stage or repetition count out of range. */
 typedef enum {
   GR_STAGE_PACK = 0,       /* RMSNorm input pack of the first layer (or of the head) */
   GR_STAGE_QKV = 1,        /* q, k, v GEMM */
