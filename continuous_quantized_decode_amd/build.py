@@ -17,6 +17,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU ops stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the epilogue math reads them directly (no AGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-munsafe-fp-atomics",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unknown-pragmas",
     "-I", os.path.join(ROOT, "include"),

@@ -23,6 +23,7 @@
 //    MFMAs of sb.
 #include "gr_internal.h"
 #include "quant.h"
+#include "gemm_addr.h"
 
 namespace gr {
 
@@ -41,9 +42,8 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-constexpr int kQ4LoadInstr = 3;             // 144 chunks of 16 B, 64 per instruction
-constexpr int kQ6LoadInstr = 14;            // 16 x 53 dword slots, 64 per instruction
-constexpr int kQ6Row = 212;                 // 53 dwords per row slot
+constexpr int kQ4LoadInstr = addr::kQ4Instr;  // 16-byte loads per lane and stage
+constexpr int kQ6LoadInstr = addr::kQ6Instr;  // 4-byte loads per lane and stage
 // Every lane of every load instruction loads (lanes past the tile's data re-read a
 // valid chunk into the padding), so each stage is exactly kQ*LoadInstr VMEM
 // instructions on every path and the vmcnt waits below are exact.
@@ -57,13 +57,6 @@ GR_DEV void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Hides a value from the optimiser so that address arithmetic derived from it is
-// recomputed where it is used rather than hoisted and kept live across the loop.
-GR_DEV int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 // The 16 rows of a tile: `base` is its first row (wave-uniform, 16-byte aligned);
 // row r reads matrix row min(r, nvalid - 1) of the tile, so a ragged last tile
 // repeats its last row (results of such rows are never stored).
@@ -71,68 +64,100 @@ struct TileRows {
   const uint8_t* base;
   int nvalid;
   u32 row_bytes;
-  GR_DEV u32 off(int r) const { return (u32)min(r, nvalid - 1) * row_bytes; }
+  GR_DEV u32 off(int r) const { return addr::row_off(r, nvalid, row_bytes); }
+  GR_DEV const uint8_t* end() const { return base + (size_t)nvalid * row_bytes; }  // past its last row
 };
 
-// Q4_K: 16 rows x 144 B = 144 chunks of 16 B; chunk c = 9r + piece -> LDS 16c.
-GR_DEV void q4_issue(const TileRows& tr, int sb, lds_u8* slot, int lane) {
-  const int l = opaque(lane);
-  const u32 sbo = (u32)sb * kQ4KBytes;
+// Staging loads (unit mapping and address arithmetic: gemm_addr.h).  In LDS, row r's
+// Q4_K block sits at 144 r and its Q6_K dword window at 212 r.  The loads are buffer
+// loads into LDS: the wave-uniform part of the address (the tile's super-block) lives
+// in the buffer descriptor, rebuilt per stage with scalar instructions, and each lane
+// keeps its offsets within the tile, computed once.  The descriptor's size ends at the
+// tile's last row, so a stray offset would read zeros rather than fault.
+constexpr int kBufDword3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
+
+GR_DEV __amdgpu_buffer_rsrc_t stage_rsrc(const uint8_t* base, const TileRows& tr, const uint8_t* tile_end) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(u32)(tile_end - base), kBufDword3);
+}
+
+struct Q4Lane {
+  u32 p[kQ4LoadInstr];  // byte offset of this lane's chunk from the tile's block address
+};
+GR_DEV Q4Lane q4_lane(const TileRows& tr, int lane) {
+  Q4Lane l;
 #pragma unroll
   for (int i = 0; i < kQ4LoadInstr; ++i) {
-    const int c = min(l + 64 * i, 143);
-    const int r = c / 9, pc = c - 9 * r;
-    const uint8_t* src = tr.base + (tr.off(r) + sbo + 16 * pc);
-    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(slot + 1024 * i), 16, 0, 0);
+    const int c = addr::q4_unit(lane, i);
+    l.p[i] = tr.off(addr::q4_row(c)) + addr::q4_in_block(c);
   }
+  return l;
+}
+GR_DEV void q4_issue(const TileRows& tr, const Q4Lane& ln, int sb, lds_u8* slot) {
+  const uint8_t* blk = tr.base + (size_t)sb * kQ4KBytes;  // wave-uniform
+  const __amdgpu_buffer_rsrc_t rs = stage_rsrc(blk, tr, tr.end());
+#pragma unroll
+  for (int i = 0; i < kQ4LoadInstr; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(slot + 1024 * i), 16, ln.p[i], 0, 0, 0);
 }
 
-// Q6_K: rows are 2-byte aligned.  Row r's slot holds the dwords covering bytes
-// [A - sh, A - sh + 212) of its block (A its address, sh = A & 3): 53 dwords when
-// sh == 2 (the block's 210 bytes and the two before it), 52 when sh == 0 (the block's
-// first 208 bytes; d is read from global separately; slot 52 repeats dword 51), so no
-// read leaves the block's dwords.  Slot c = 53r + w -> LDS 4c.
-GR_DEV void q6_issue(const TileRows& tr, int sb, lds_u8* slot, int lane) {
-  const int l = opaque(lane);
-  const u32 sbo = (u32)sb * kQ6KBytes;
-  const u32 blo = (u32)(uintptr_t)tr.base;
+struct Q6Lane {
+  u32 pre[kQ6LoadInstr];  // addr::q6_pre of this lane's slot per instruction
+};
+GR_DEV Q6Lane q6_lane(const TileRows& tr, int lane) {
+  Q6Lane l;
 #pragma unroll
   for (int i = 0; i < kQ6LoadInstr; ++i) {
-    const int c = min(l + 64 * i, 16 * 53 - 1);  // past the data: re-read the last slot
-    const int r = c / 53, wd = c - 53 * r;
-    const u32 o = tr.off(r) + sbo;
-    const u32 sh = (blo + o) & 3u;
-    const int wde = (wd == 52 && sh == 0) ? 51 : wd;
-    const uint8_t* src = tr.base + ((o + 4u * (u32)wde) - sh);
-    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(slot + 256 * i), 4, 0, 0);
+    const int c = addr::q6_unit(lane, i);
+    l.pre[i] = addr::q6_pre(tr.off(addr::q6_row(c)), addr::q6_slot(c));
+  }
+  return l;
+}
+// ALIGNED: every row of the matrix is a multiple of 4 bytes, so all rows of a stage
+// share the tile's shift, which folds into the descriptor's base; otherwise each lane
+// finds its row's shift.
+template <bool ALIGNED>
+GR_DEV void q6_issue(const TileRows& tr, const Q6Lane& ln, int sb, lds_u8* slot) {
+  const uint8_t* blk = tr.base + (size_t)sb * kQ6KBytes;  // wave-uniform
+  if constexpr (ALIGNED) {
+    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(blk - addr::q6_sh((u32)(uintptr_t)blk), tr, tr.end());
+#pragma unroll
+    for (int i = 0; i < kQ6LoadInstr; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(slot + 256 * i), 4, ln.pre[i], 0, 0, 0);
+  } else {
+    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(blk - 2, tr, tr.end());
+#pragma unroll
+    for (int i = 0; i < kQ6LoadInstr; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lptr_t)(slot + 256 * i), 4, addr::q6_rel(ln.pre[i], addr::q6_sh((u32)(uintptr_t)blk + ln.pre[i])), 0, 0,
+          0);
   }
 }
 
-// 4 bytes at byte offset `off` (even) of an LDS region whose dwords are aligned.
-GR_DEV u32 lds_u32_a2(const lds_u8* base, int off) {
-  const int a = off & ~3;
-  const u32 lo = *(const __attribute__((address_space(3))) u32*)(base + a);
-  const u32 hi = *(const __attribute__((address_space(3))) u32*)(base + a + 4);
-  return __builtin_amdgcn_alignbyte(hi, lo, (u32)(off & 3));
+// 4 bytes at (lo dword, hi dword) shifted right by sh bytes.
+GR_DEV u32 lds_pair(const lds_u8* lo, const lds_u8* hi, u32 sh) {
+  return __builtin_amdgcn_alignbyte(*(const __attribute__((address_space(3))) u32*)hi,
+                                    *(const __attribute__((address_space(3))) u32*)lo, sh);
 }
 
 // ---------------------------------------------------------------------------------
 // wave bodies: accumulate rows 8bt+2g and 8bt+2g+1 of output column n (lane (n, g))
-// of tile t over super-blocks [sb0, sb1).
+// of tile t over super-blocks [sb0, sb1).  acc[t][b][e] holds MFMA row 4g + e, i.e.
+// batch row 8b + 2g + (e >> 1), bf16 hi (e even) or lo (e odd) part.
 
 // One super-block of Q4_K for NT tiles, weights from LDS slots, activations `ca`.
 template <int NT, int BTN>
 GR_DEV void q4_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32x4* ca, int sb, int lane,
-                    float (&acc)[NT][BTN][2]) {
+                    float (&acc)[NT][BTN][4]) {
   const u32x4* xp = (const u32x4*)a.xpack;
   const u32x4 ones = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   const int n = lane & 15, kg = lane >> 4;
+  const u32 M = vconst(0x43004300u);
   Q4Regs w[NT];
   float sd[NT][8], mm[NT][8];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const lds_u8* rp = slot[t] + kQ4KBytes * n;
+    const lds_u8* rp = slot[t] + kQ4KBytes * n;  // row n's block
     w[t].hdr = *(const __attribute__((address_space(3))) u32x4*)rp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) w[t].qs[c] = *(const __attribute__((address_space(3))) u32x2*)(rp + 16 + 32 * c + 8 * kg);
@@ -143,25 +168,24 @@ GR_DEV void q4_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32x4* c
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     u32x4 av[BTN];
-    float s0[BTN], s1[BTN];
+    f32x4 sv[BTN];
 #pragma unroll
     for (int b = 0; b < BTN; ++b) {
       if constexpr (BTN == 1)
         av[b] = ca[j];
       else
         av[b] = xp[(((size_t)b * a.nslices) + (size_t)sb * 8 + j) * 64 + lane];
-      const f32x4 sv = mfma_bf16_k32(av[b], ones, z4);
-      s0[b] = sv[0] + sv[1];
-      s1[b] = sv[2] + sv[3];
+      sv[b] = mfma_bf16_k32(av[b], ones, z4);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const u32x4 bq = q4_expand(w[t].qs[j >> 1], (j & 1) != 0);
+      const u32x4 bq = q4_expand(w[t].qs[j >> 1], (j & 1) != 0, M);
 #pragma unroll
       for (int b = 0; b < BTN; ++b) {
         const f32x4 dd = mfma_bf16_k32(av[b], bq, z4);
-        acc[t][b][0] = __builtin_fmaf(sd[t][j], dd[0] + dd[1], __builtin_fmaf(-mm[t][j], s0[b], acc[t][b][0]));
-        acc[t][b][1] = __builtin_fmaf(sd[t][j], dd[2] + dd[3], __builtin_fmaf(-mm[t][j], s1[b], acc[t][b][1]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[t][b][e] = __builtin_fmaf(sd[t][j], dd[e], __builtin_fmaf(-mm[t][j], sv[b][e], acc[t][b][e]));
       }
     }
   }
@@ -175,15 +199,18 @@ struct Q4Buf {
 
 template <int NT, int BTN>
 GR_DEV void q4_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, int sb0, int sb1, int lane,
-                    float (&acc)[NT][BTN][2]) {
+                    float (&acc)[NT][BTN][4]) {
   constexpr int NA = BTN == 1 ? 8 : 1;
   constexpr int kBatch = NT * kQ4LoadInstr + (BTN == 1 ? 8 : 0);  // VMEM instructions per load()
+  Q4Lane ln[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ln[t] = q4_lane(tr[t], lane);
   Q4Buf<NT, NA> b0, b1;
   b0.slot = 0;
   b1.slot = 1;
   auto load = [&](Q4Buf<NT, NA>& b, int sb) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) q4_issue(tr[t], sb, ring + (b.slot * NT + t) * kQ4Stage, lane);
+    for (int t = 0; t < NT; ++t) q4_issue(tr[t], ln[t], sb, ring + (b.slot * NT + t) * kQ4Stage);
     if constexpr (BTN == 1) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) b.a[j] = ((const u32x4*)a.xpack)[((size_t)sb * 8 + j) * 64 + lane];
@@ -203,27 +230,38 @@ GR_DEV void q4_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, i
   pipeline2(sb0, sb1, b0, b1, load, step);
 }
 
+constexpr u32 kNeg160Bf16 = 0xC320C320u;  // two bf16 -160.0
+
+// One super-block of Q6_K.  Per 16-weight sub-block: C = A x (-160) gives -160 * S
+// (S the activation sums), and the quant MFMA accumulates onto it, so the MFMA returns
+// D - 160 S = sum a * (q - 32) with no vector work; the scale is one FMA per row.
 template <int NT, int BTN>
-GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dreg)[NT], const u32x4* ca, int sb,
-                    int lane, float (&acc)[NT][BTN][2], const int (&sh)[NT]) {
+GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dreg)[NT], const u32 (&shreg)[NT],
+                    const u32x4* ca, int sb, int lane, float (&acc)[NT][BTN][4]) {
   const u32x4* xp = (const u32x4*)a.xpack;
-  const u32x2 ones = {kOnesBf16, kOnesBf16};
+  const u32x2 neg160 = {kNeg160Bf16, kNeg160Bf16};
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   const int n = lane & 15, kg = lane >> 4;
+  const u32 M = vconst(0x43004300u);
   Q6Regs w[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const lds_u8* rp = slot[t] + kQ6Row * n;
-    const int o = sh[t];
+    // row n's window at 212 n holds block byte b at b + sh (addr::q6_lds_byte): the field
+    // at block byte C (a multiple of 4) is the dword pair at 212 n + C shifted right by
+    // sh bytes
+    const u32 sh = shreg[t];  // bytes (alignbyte's shift operand counts bytes)
+    const lds_u8* rs = slot[t] + 212 * n;
+    const lds_u8* rp = rs + 4 * kg;
 #pragma unroll
     for (int hu = 0; hu < 4; ++hu) {
       const int h = hu >> 1, u = hu & 1;
-      w[t].part[hu].a = lds_u32_a2(rp, o + 64 * h + 16 * u + 4 * kg);
-      w[t].part[hu].b = lds_u32_a2(rp, o + 64 * h + 32 + 16 * u + 4 * kg);
-      w[t].part[hu].q = lds_u32_a2(rp, o + 128 + 32 * h + 16 * u + 4 * kg);
+      const int ca = 64 * h + 16 * u, cb = ca + 32, cq = 128 + 32 * h + 16 * u;
+      w[t].part[hu].a = lds_pair(rp + ca, rp + ca + 4, sh);
+      w[t].part[hu].b = lds_pair(rp + cb, rp + cb + 4, sh);
+      w[t].part[hu].q = lds_pair(rp + cq, rp + cq + 4, sh);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[t].sc[i] = lds_u32_a2(rp, o + 192 + 4 * i);
+    for (int i = 0; i < 4; ++i) w[t].sc[i] = lds_pair(rs + 192 + 4 * i, rs + 196 + 4 * i, sh);
     w[t].d = (u16)dreg[t];
   }
   float dsc[NT];
@@ -236,7 +274,7 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dr
     for (int r = 0; r < 4; ++r) {
       const int sub = 8 * h + 2 * r + u;  // 16-weight sub-block within the super-block
       u32x2 av[BTN];
-      float s0[BTN], s1[BTN];
+      f32x4 cs[BTN];
 #pragma unroll
       for (int b = 0; b < BTN; ++b) {
         u32x4 pr;
@@ -245,20 +283,18 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dr
         else
           pr = xp[(((size_t)b * (a.nslices >> 1)) + (size_t)sb * 8 + (sub >> 1)) * 64 + lane];
         av[b] = (sub & 1) ? u32x2{pr.z, pr.w} : u32x2{pr.x, pr.y};
-        const f32x4 sv = mfma_bf16_k16(av[b], ones, z4);
-        s0[b] = 160.0f * (sv[0] + sv[1]);
-        s1[b] = 160.0f * (sv[2] + sv[3]);
+        cs[b] = mfma_bf16_k16(av[b], neg160, z4);
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const u32x2 bq = q6_expand(w[t].part[hu], r);
+        const u32x2 bq = q6_expand(w[t].part[hu], r, M);
         const int scv = (int)(int8_t)((w[t].sc[sub >> 2] >> (8 * (sub & 3))) & 0xFF);
         const float sd = dsc[t] * (float)scv;
 #pragma unroll
         for (int b = 0; b < BTN; ++b) {
-          const f32x4 dd = mfma_bf16_k16(av[b], bq, z4);
-          acc[t][b][0] = __builtin_fmaf(sd, (dd[0] + dd[1]) - s0[b], acc[t][b][0]);
-          acc[t][b][1] = __builtin_fmaf(sd, (dd[2] + dd[3]) - s1[b], acc[t][b][1]);
+          const f32x4 dd = mfma_bf16_k16(av[b], bq, cs[b]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][b][e] = __builtin_fmaf(sd, dd[e], acc[t][b][e]);
         }
       }
     }
@@ -270,24 +306,31 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dr
 template <int NT, int NA>
 struct Q6Buf {
   int slot;
-  u32 d[NT];      // this lane's row's fp16 d (read from global: it is not always staged)
+  u32 d[NT];   // this lane's row's fp16 d (read from global: it is not always staged)
   u32x4 a[NA];
 };
 
-template <int NT, int BTN>
+template <int NT, int BTN, bool ALIGNED>
 GR_DEV void q6_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, int sb0, int sb1, int lane,
-                    float (&acc)[NT][BTN][2]) {
+                    float (&acc)[NT][BTN][4]) {
   constexpr int NA = BTN == 1 ? 8 : 1;
   constexpr int kBatch = NT * (kQ6LoadInstr + 1) + (BTN == 1 ? 8 : 0);
   const int n = lane & 15;
+  Q6Lane ln[NT];
+  u32 on[NT];  // byte offset of row n (block 0) from the tile base
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    ln[t] = q6_lane(tr[t], lane);
+    on[t] = tr[t].off(n);
+  }
   Q6Buf<NT, NA> b0, b1;
   b0.slot = 0;
   b1.slot = 1;
   auto load = [&](Q6Buf<NT, NA>& b, int sb) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      q6_issue(tr[t], sb, ring + (b.slot * NT + t) * kQ6Stage, lane);
-      b.d[t] = *(const u16*)(tr[t].base + (tr[t].off(n) + (u32)sb * kQ6KBytes + 208u));
+      q6_issue<ALIGNED>(tr[t], ln[t], sb, ring + (b.slot * NT + t) * kQ6Stage);
+      b.d[t] = *(const u16*)(tr[t].base + (size_t)sb * kQ6KBytes + on[t] + 208u);
     }
     if constexpr (BTN == 1) {
 #pragma unroll
@@ -301,13 +344,13 @@ GR_DEV void q6_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, i
       wait_vmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
     lds_u8* slots[NT];
-    int sh[NT];
+    u32 sh[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       slots[t] = ring + (b.slot * NT + t) * kQ6Stage;
-      sh[t] = (int)(((u32)(uintptr_t)tr[t].base + tr[t].off(n) + (u32)sb * kQ6KBytes) & 3u);
+      sh[t] = ((u32)(uintptr_t)(tr[t].base + (size_t)sb * kQ6KBytes) + on[t]) & 3u;
     }
-    q6_step<NT, BTN>(a, slots, b.d, b.a, sb, lane, acc, sh);
+    q6_step<NT, BTN>(a, slots, b.d, sh, b.a, sb, lane, acc);
   };
   pipeline2(sb0, sb1, b0, b1, load, step);
 }
@@ -319,7 +362,9 @@ GR_DEV float row_scale(const GemmArgs& a, int b) {
   return a.ss ? 1.0f / sqrtf(a.ss[b] * a.inv_k + a.eps) : 1.0f;
 }
 
-template <int WT, int NT, int BTN, int MAXT>
+// ALIGNED (Q6_K only): every weight row is a multiple of 4 bytes (an even number of
+// super-blocks per row).
+template <int WT, int NT, int BTN, int MAXT, bool ALIGNED>
 __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // staging rings, then the reduction
   float* red = (float*)lds;  // [waves][NT][BTN][64 lanes][2]
@@ -345,11 +390,13 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
     rows_n = a.seg_rows[s];
     tr[t] = TileRows{a.w[s] + (size_t)local * 16 * a.row_bytes, rows_n - local * 16, (u32)a.row_bytes};
   }
-  float acc[NT][BTN][2];
+  float acc[NT][BTN][4];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int b = 0; b < BTN; ++b) acc[t][b][0] = acc[t][b][1] = 0.f;
+    for (int b = 0; b < BTN; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][b][e] = 0.f;
 
   const int sb0 = wave * a.sb_per_wave;
   const int sb1 = min(a.nsb, sb0 + a.sb_per_wave);
@@ -359,7 +406,7 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
     if constexpr (WT == 12)
       q4_wave<NT, BTN>(a, tr, ring, sb0, sb1, lane, acc);
     else
-      q6_wave<NT, BTN>(a, tr, ring, sb0, sb1, lane, acc);
+      q6_wave<NT, BTN, ALIGNED>(a, tr, ring, sb0, sb1, lane, acc);
   }
   __syncthreads();  // the reduction buffer reuses the staging area
 
@@ -369,8 +416,8 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int b = 0; b < BTN; ++b) {
       float* r = red + (((size_t)wave * NT + t) * BTN + b) * 128 + lane * 2;
-      r[0] = acc[t][b][0];
-      r[1] = acc[t][b][1];
+      r[0] = acc[t][b][0] + acc[t][b][1];  // hi + lo parts of batch row 8b + 2g
+      r[1] = acc[t][b][2] + acc[t][b][3];  // and of row 8b + 2g + 1
     }
   __syncthreads();
 
@@ -451,16 +498,16 @@ GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, bool pair) {
   return pl;
 }
 
-#define GR_GEMM_SWITCH(WTv)                                                                          \
+#define GR_GEMM_SWITCH(WTv, ALv)                                                                        \
   switch (pl.nt * 1000 + pl.btn * 10 + (pl.maxt == 512)) {                                          \
-    case 1011: launch_kernel(gemm_kernel<WTv, 1, 1, 512>, grid, block, lds, st, a); break;                \
-    case 1020: launch_kernel(gemm_kernel<WTv, 1, 2, 256>, grid, block, lds, st, a); break;                \
-    case 1040: launch_kernel(gemm_kernel<WTv, 1, 4, 256>, grid, block, lds, st, a); break;                \
-    case 1080: launch_kernel(gemm_kernel<WTv, 1, 8, 256>, grid, block, lds, st, a); break;                \
-    case 2010: launch_kernel(gemm_kernel<WTv, 2, 1, 256>, grid, block, lds, st, a); break;                \
-    case 2020: launch_kernel(gemm_kernel<WTv, 2, 2, 256>, grid, block, lds, st, a); break;                \
-    case 2040: launch_kernel(gemm_kernel<WTv, 2, 4, 256>, grid, block, lds, st, a); break;                \
-    case 2080: launch_kernel(gemm_kernel<WTv, 2, 8, 256>, grid, block, lds, st, a); break;                \
+    case 1011: launch_kernel(gemm_kernel<WTv, 1, 1, 512, ALv>, grid, block, lds, st, a); break; \
+    case 1020: launch_kernel(gemm_kernel<WTv, 1, 2, 256, ALv>, grid, block, lds, st, a); break; \
+    case 1040: launch_kernel(gemm_kernel<WTv, 1, 4, 256, ALv>, grid, block, lds, st, a); break; \
+    case 1080: launch_kernel(gemm_kernel<WTv, 1, 8, 256, ALv>, grid, block, lds, st, a); break; \
+    case 2010: launch_kernel(gemm_kernel<WTv, 2, 1, 256, ALv>, grid, block, lds, st, a); break; \
+    case 2020: launch_kernel(gemm_kernel<WTv, 2, 2, 256, ALv>, grid, block, lds, st, a); break; \
+    case 2040: launch_kernel(gemm_kernel<WTv, 2, 4, 256, ALv>, grid, block, lds, st, a); break; \
+    case 2080: launch_kernel(gemm_kernel<WTv, 2, 8, 256, ALv>, grid, block, lds, st, a); break; \
     default: return hipErrorInvalidValue;                                                            \
   }
 
@@ -469,9 +516,13 @@ hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStre
   const dim3 grid(pl.tiles), block(pl.waves * 64);
   const size_t lds = pl.lds;
   if (wtype == 12) {
-    GR_GEMM_SWITCH(12)
+    GR_GEMM_SWITCH(12, true)
   } else {
-    GR_GEMM_SWITCH(14)
+    if (a.row_bytes % 4 == 0) {
+      GR_GEMM_SWITCH(14, true)
+    } else {
+      GR_GEMM_SWITCH(14, false)
+    }
   }
   return hipGetLastError();
 }

@@ -20,8 +20,15 @@ namespace gr {
 
 // Expand 8 bytes of Q4_K quants (two dwords) into the bf16 B operand of one
 // sub-block: `high` selects the high nibbles (odd sub-block of the chunk).
-GR_DEV u32x4 q4_expand(u32x2 q, bool high) {
-  const u32 M = 0x43004300u, NIB = 0x000F000Fu;
+// Keeps a constant in a VGPR, so that (x & mask) | c compiles to one three-input
+// v_and_or_b32 (gfx9 VOP3 takes no literal and one scalar operand).
+GR_DEV u32 vconst(u32 c) {
+  asm volatile("" : "+v"(c));
+  return c;
+}
+
+GR_DEV u32x4 q4_expand(u32x2 q, bool high, u32 M = 0x43004300u) {
+  const u32 NIB = 0x000F000Fu;
   u32 w0 = high ? (q.x >> 4) : q.x;
   u32 w1 = high ? (q.y >> 4) : q.y;
   u32x4 r;
@@ -109,7 +116,7 @@ GR_DEV void q6_load(Q6Regs& r, const uint8_t* blk, int kg) {
 }
 
 // 6-bit quants of sub-block (h, 2r+u) as four bytes, then as the bf16 B operand.
-GR_DEV u32x2 q6_expand(const Q6Part& pt, int r) {
+GR_DEV u32x2 q6_expand(const Q6Part& pt, int r, u32 M = 0x43004300u) {
   u32 v;
   if (r == 0)
     v = (pt.a & 0x0F0F0F0Fu) | ((pt.q << 4) & 0x30303030u);
@@ -119,7 +126,6 @@ GR_DEV u32x2 q6_expand(const Q6Part& pt, int r) {
     v = ((pt.a >> 4) & 0x0F0F0F0Fu) | (pt.q & 0x30303030u);
   else
     v = ((pt.b >> 4) & 0x0F0F0F0Fu) | ((pt.q >> 2) & 0x30303030u);
-  const u32 M = 0x43004300u;
   u32x2 o;
   o.x = (v & 0x00FF00FFu) | M;
   o.y = ((v >> 8) & 0x00FF00FFu) | M;

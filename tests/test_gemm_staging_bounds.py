@@ -1,0 +1,124 @@
+"""Host-side check of the GEMM kernel's weight-staging addresses (CPU only).
+
+The kernel computes every direct-to-LDS load address with the integer functions of
+continuous_quantized_decode_amd/csrc/gemm_addr.h.  This test compiles that header
+into a small C++ program that enumerates every tile shape, ragged last tile,
+super-block, lane and load instruction and checks that:
+  * every load lies inside the weight matrix (no read before its start or past its end);
+  * Q4_K loads are 16-byte chunks inside their row block;
+  * Q6_K loads are aligned dwords inside [block - sh, block + 210), except that a final
+    dword may end 2 bytes past the matrix (the tail of an aligned dword: no page crossed);
+  * no LDS write leaves the stage;
+  * every LDS byte the compute reads (row r's Q4_K block at 144 r; bytes 0..207 of its
+    Q6_K block at gemm_addr.h's q6_lds_byte) holds the right byte of the matrix after
+    the stage's loads.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "continuous_quantized_decode_amd", "csrc", "gemm_addr.h")
+
+PROGRAM = r"""
+#include <cstdio>
+#include <vector>
+#include "gemm_addr.h"
+using namespace gr::addr;
+
+static int fails = 0;
+#define CHECK(c, ...) do { if (!(c)) { if (fails++ < 20) { std::printf(__VA_ARGS__); std::printf("\n"); } } } while (0)
+
+int main() {
+  const int nsbs[] = {1, 2, 3, 4, 5, 7, 12, 16, 48, 56, 57};
+  const int rows[] = {1, 2, 15, 16, 17, 31, 33, 48};
+  for (int wt = 0; wt < 2; ++wt) {
+    const uint32_t bb = wt == 0 ? 144 : 210;
+    const int ni = wt == 0 ? kQ4Instr : kQ6Instr;
+    const int stage = wt == 0 ? kQ4Instr * 64 * 16 : kQ6Instr * 64 * 4;
+    for (int nsb : nsbs) for (int N : rows) {
+      const uint32_t row_bytes = bb * nsb;
+      const uint64_t total = (uint64_t)N * row_bytes;  // the matrix starts 16-byte aligned, at 0
+      for (int row0 = 0; row0 < N; row0 += 16) {
+        const int nvalid = N - row0 < 16 ? N - row0 : 16;
+        const uint64_t tile = (uint64_t)row0 * row_bytes;
+        for (int sb = 0; sb < nsb; ++sb) {
+          std::vector<int64_t> held(stage, -1);  // global byte address held by each LDS byte
+          for (int lane = 0; lane < 64; ++lane) {
+            for (int i = 0; i < ni; ++i) {
+              uint64_t a; uint32_t len, lds;
+              bool ok_end = false;  // a Q6_K dword may end up to 2 bytes past the matrix
+              if (wt == 0) {
+                const int c = q4_unit(lane, i);
+                const uint64_t blk = tile + row_off(q4_row(c), nvalid, row_bytes) + (uint64_t)sb * bb;
+                a = blk + q4_in_block(c); len = 16; lds = q4_lds(lane, i);
+                CHECK(a >= blk && a + len <= blk + bb, "q4 load leaves its row block");
+              } else {
+                // exactly the kernel's arithmetic: a per-lane constant and the tile's
+                // block address, with sh from the tile (rows of a multiple of 4 bytes)
+                // or from the slot's row (general)
+                const int c = q6_unit(lane, i);
+                const uint32_t pre = q6_pre(row_off(q6_row(c), nvalid, row_bytes), q6_slot(c));
+                const uint64_t tblk = tile + (uint64_t)sb * bb;
+                const uint64_t blk = tile + row_off(q6_row(c), nvalid, row_bytes) + (uint64_t)sb * bb;
+                const uint32_t sh = q6_sh((uint32_t)blk);
+                if (row_bytes % 4 == 0) {
+                  const uint32_t sh0 = q6_sh((uint32_t)tblk);
+                  CHECK(sh0 == sh, "tile sh differs from the row's");
+                  a = tblk - sh0 + pre;
+                } else {
+                  CHECK(q6_sh((uint32_t)tblk + pre) == sh, "row sh from the lane constant is wrong");
+                  a = tblk - 2 + q6_rel(pre, q6_sh((uint32_t)tblk + pre));
+                }
+                len = 4; lds = q6_lds(lane, i);
+                CHECK(a % 4 == 0 && a + sh >= blk && a < blk + 210, "q6 load leaves [blk - sh, blk + 210)");
+                // past the matrix end only as the tail of an aligned dword that starts inside
+                if (a + len > total) CHECK(a < total && a + len - total <= 2, "q6 load runs past the matrix end");
+                else CHECK(true, "");
+                ok_end = a + len > total;
+              }
+              CHECK(a < total && (a + len <= total || ok_end), "wt %d nsb %d N %d row0 %d sb %d lane %d i %d: [%llu,+%u) outside %llu",
+                    wt, nsb, N, row0, sb, lane, i, (unsigned long long)a, len, (unsigned long long)total);
+              CHECK(lds + len <= (uint32_t)stage, "LDS write past the stage");
+              for (uint32_t k = 0; k < len && lds + k < (uint32_t)stage; ++k)
+                held[lds + k] = a + k < total ? (int64_t)(a + k) : -2;  // bytes past the matrix read as garbage
+            }
+          }
+          // every byte the compute reads holds the right global byte
+          for (int r = 0; r < 16; ++r) {
+            const uint64_t blk = tile + row_off(r, nvalid, row_bytes) + (uint64_t)sb * bb;
+            if (wt == 0) {
+              for (int b = 0; b < 144; ++b)
+                CHECK(held[144 * r + b] == (int64_t)(blk + b), "q4 nsb %d N %d row0 %d sb %d row %d byte %d", nsb, N,
+                      row0, sb, r, b);
+            } else {
+              const uint32_t sh = q6_sh((uint32_t)blk);
+              for (uint32_t b = 0; b < 208; ++b)
+                CHECK(held[q6_lds_byte(r, b, sh)] == (int64_t)(blk + b), "q6 nsb %d N %d row0 %d sb %d row %d byte %u sh %u",
+                      nsb, N, row0, sb, r, b, sh);
+            }
+          }
+        }
+      }
+    }
+  }
+  std::printf("%s (%d failures)\n", fails ? "FAIL" : "ok", fails);
+  return fails ? 1 : 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_gemm_staging_loads_stay_in_bounds_and_land_where_read():
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "check.cpp")
+        exe = os.path.join(d, "check")
+        with open(src, "w") as f:
+            f.write(PROGRAM)
+        subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.dirname(HDR), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        print(out.stdout)
+        assert out.returncode == 0, out.stdout
