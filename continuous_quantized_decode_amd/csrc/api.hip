@@ -112,13 +112,15 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
   bool zeroed = false;
   while (i < nmat) {
     GemmArgs a{};
-    int j = i, n = 0, tiles = 0;
+    int j = i, n = 0, tiles = 0, all_tiles = 0;
+    for (int q = i; q < nmat && types[q] == types[i]; ++q) all_tiles += (rows[q] + 15) / 16;
+    const int group = gemm_group(all_tiles);
     while (j < nmat && types[j] == types[i]) {
       a.w[n] = (const uint8_t*)w[j];
       a.seg_rows[n] = rows[j];
       a.seg_tile_off[n] = tiles;
       a.seg_col_off[n] = col;
-      tiles += (rows[j] + 15) / 16;
+      tiles += ((rows[j] + 15) / 16 + group - 1) / group;  // workgroups of `group` tiles
       col += rows[j];
       ++n;
       ++j;
@@ -151,7 +153,7 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
       a.zero_n = ep.zero_n;
       zeroed = true;
     }
-    const GemmPlan pl = plan_gemm(wt, tiles, K, B, false);
+    const GemmPlan pl = plan_gemm(wt, tiles, K, B, group);
     a.sb_per_wave = pl.sb_per_wave;
     hipError_t e = launch_gemm(wt, pl, a, st);
     if (e != hipSuccess) return e;
@@ -184,7 +186,7 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   a.pack_nslices = nslices_of(out.kind, F);
   a.zero_ptr = zero_ptr;
   a.zero_n = zero_n;
-  const GemmPlan pl = plan_gemm(wtype, tiles, K, B, true);
+  const GemmPlan pl = plan_gemm(wtype, tiles, K, B, 2);
   a.sb_per_wave = pl.sb_per_wave;
   return launch_gemm(wtype, pl, a, st);
 }
@@ -473,7 +475,10 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int pair, int*
   if (!nt || !btn || !maxt || !grid_threads || !block_threads) return GR_ERR_NULL;
   if (wtype != GR_W_Q4_K && wtype != GR_W_Q6_K) return GR_ERR_DTYPE;
   if (rows <= 0 || K <= 0 || K % kQK || B <= 0 || B > 64) return GR_ERR_SHAPE;
-  const GemmPlan pl = plan_gemm(wtype, (rows + 15) / 16, K, B, pair != 0);
+  const int tiles = (rows + 15) / 16;
+  const int group = gemm_group(tiles);
+  const GemmPlan pl = pair ? plan_gemm(wtype, tiles, K, B, 2)
+                           : plan_gemm(wtype, (tiles + group - 1) / group, K, B, group);
   *nt = pl.nt;
   *btn = pl.btn;
   *maxt = pl.maxt;

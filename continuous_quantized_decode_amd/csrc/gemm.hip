@@ -43,12 +43,12 @@ typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr int kQ4LoadInstr = addr::kQ4Instr;  // 16-byte loads per lane and stage
-constexpr int kQ6LoadInstr = addr::kQ6Instr;  // 4-byte loads per lane and stage
+constexpr int kQ6LoadInstr = addr::kQ6Instr;  // 16-byte loads per lane and stage
 // Every lane of every load instruction loads (lanes past the tile's data re-read a
 // valid chunk into the padding), so each stage is exactly kQ*LoadInstr VMEM
 // instructions on every path and the vmcnt waits below are exact.
 constexpr int kQ4Stage = kQ4LoadInstr * 64 * 16;  // 3072 B (2304 used)
-constexpr int kQ6Stage = kQ6LoadInstr * 64 * 4;   // 3584 B (3392 used)
+constexpr int kQ6Stage = kQ6LoadInstr * 64 * 16;  // 4096 B (3584 used)
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -101,35 +101,35 @@ GR_DEV void q4_issue(const TileRows& tr, const Q4Lane& ln, int sb, lds_u8* slot)
 }
 
 struct Q6Lane {
-  u32 pre[kQ6LoadInstr];  // addr::q6_pre of this lane's slot per instruction
+  u32 pre[kQ6LoadInstr];  // addr::q6_pre of this lane's unit per instruction
 };
 GR_DEV Q6Lane q6_lane(const TileRows& tr, int lane) {
   Q6Lane l;
 #pragma unroll
   for (int i = 0; i < kQ6LoadInstr; ++i) {
     const int c = addr::q6_unit(lane, i);
-    l.pre[i] = addr::q6_pre(tr.off(addr::q6_row(c)), addr::q6_slot(c));
+    l.pre[i] = addr::q6_pre(tr.off(addr::q6_row(c)), c);
   }
   return l;
 }
-// ALIGNED: every row of the matrix is a multiple of 4 bytes, so all rows of a stage
-// share the tile's shift, which folds into the descriptor's base; otherwise each lane
-// finds its row's shift.
+// ALIGNED: every row of the matrix is a multiple of 16 bytes, so all rows of a stage
+// share the tile's s16, which folds into the descriptor's base; otherwise each lane
+// finds its row's.
 template <bool ALIGNED>
 GR_DEV void q6_issue(const TileRows& tr, const Q6Lane& ln, int sb, lds_u8* slot) {
   const uint8_t* blk = tr.base + (size_t)sb * kQ6KBytes;  // wave-uniform
   if constexpr (ALIGNED) {
-    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(blk - addr::q6_sh((u32)(uintptr_t)blk), tr, tr.end());
+    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(blk - addr::q6_s16((u32)(uintptr_t)blk), tr, tr.end());
 #pragma unroll
     for (int i = 0; i < kQ6LoadInstr; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(slot + 256 * i), 4, ln.pre[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(slot + 1024 * i), 16, ln.pre[i], 0, 0, 0);
   } else {
-    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(blk - 2, tr, tr.end());
+    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(blk - 16, tr, tr.end());
 #pragma unroll
     for (int i = 0; i < kQ6LoadInstr; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lptr_t)(slot + 256 * i), 4, addr::q6_rel(ln.pre[i], addr::q6_sh((u32)(uintptr_t)blk + ln.pre[i])), 0, 0,
-          0);
+          rs, (lptr_t)(slot + 1024 * i), 16, addr::q6_rel(ln.pre[i], addr::q6_s16((u32)(uintptr_t)blk + ln.pre[i])), 0,
+          0, 0);
   }
 }
 
@@ -137,6 +137,67 @@ GR_DEV void q6_issue(const TileRows& tr, const Q6Lane& ln, int sb, lds_u8* slot)
 GR_DEV u32 lds_pair(const lds_u8* lo, const lds_u8* hi, u32 sh) {
   return __builtin_amdgcn_alignbyte(*(const __attribute__((address_space(3))) u32*)hi,
                                     *(const __attribute__((address_space(3))) u32*)lo, sh);
+}
+
+// ---------------------------------------------------------------------------------
+// The per-wave stream over super-blocks [s0, s1): weights run D - 1 stages ahead in a
+// D-slot LDS ring, activation fragments one stage ahead in two register buffers (the
+// loop is unrolled by two so the buffers are named statically).  Before stage i's
+// math, the only memory instructions allowed outstanding are the ones issued after
+// stage i's activations (the weights of stage i + D - 1 and the activations of stage
+// i + 1, when issued), so every wait below is exact on each path.
+constexpr int kRing = 2;  // D (slots of the LDS ring; D - 1 stages of weights in flight)
+
+template <int KW, int KA, class Buf, class IssueW, class IssueA, class Step>
+GR_DEV void pipeline_ring(int s0, int s1, Buf& b0, Buf& b1, IssueW&& issue_w, IssueA&& issue_a, Step&& step) {
+  if (s1 - s0 >= kRing) {
+#pragma unroll
+    for (int d = 0; d < kRing - 1; ++d) issue_w(s0 + d);
+  } else {
+#pragma unroll
+    for (int d = 0; d < kRing - 1; ++d)
+      if (s0 + d < s1) issue_w(s0 + d);
+  }
+  issue_a(b0, s0);
+  int i = s0;
+  // steady state, no branches: both stages of a pair issue their successors' loads
+  for (; i + kRing < s1; i += 2) {
+    issue_w(i + kRing - 1);
+    issue_a(b1, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<KW + KA>();
+    __builtin_amdgcn_sched_barrier(0);
+    step(b0, i);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(i + kRing);
+    issue_a(b0, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<KW + KA>();
+    __builtin_amdgcn_sched_barrier(0);
+    step(b1, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the last (at most kRing) stages
+  auto one = [&](Buf& cur, Buf& nxt, int j) {
+    const bool w_next = j + kRing - 1 < s1;
+    const bool a_next = j + 1 < s1;
+    if (w_next) issue_w(j + kRing - 1);
+    if (a_next) issue_a(nxt, j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (w_next)
+      wait_vmcnt<KW + KA>();
+    else if (a_next)
+      wait_vmcnt<KA>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    step(cur, j);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (; i < s1; i += 2) {
+    one(b0, b1, i);
+    if (i + 1 < s1) one(b1, b0, i + 1);
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -191,43 +252,38 @@ GR_DEV void q4_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32x4* c
   }
 }
 
-template <int NT, int NA>
-struct Q4Buf {
-  int slot;     // LDS ring slot holding this buffer's weights
-  u32x4 a[NA];  // activation fragments
+template <int NA>
+struct ABuf {
+  u32x4 a[NA];  // activation fragments of one super-block
 };
 
 template <int NT, int BTN>
 GR_DEV void q4_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, int sb0, int sb1, int lane,
                     float (&acc)[NT][BTN][4]) {
   constexpr int NA = BTN == 1 ? 8 : 1;
-  constexpr int kBatch = NT * kQ4LoadInstr + (BTN == 1 ? 8 : 0);  // VMEM instructions per load()
+  constexpr int KW = NT * kQ4LoadInstr, KA = BTN == 1 ? 8 : 0;  // VMEM instructions per issue
   Q4Lane ln[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) ln[t] = q4_lane(tr[t], lane);
-  Q4Buf<NT, NA> b0, b1;
-  b0.slot = 0;
-  b1.slot = 1;
-  auto load = [&](Q4Buf<NT, NA>& b, int sb) {
+  auto slot_of = [&](int sb, int t) { return ring + (((sb - sb0) & (kRing - 1)) * NT + t) * kQ4Stage; };
+  ABuf<NA> b0, b1;
+  auto issue_w = [&](int sb) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) q4_issue(tr[t], ln[t], sb, ring + (b.slot * NT + t) * kQ4Stage);
+    for (int t = 0; t < NT; ++t) q4_issue(tr[t], ln[t], sb, slot_of(sb, t));
+  };
+  auto issue_a = [&](ABuf<NA>& b, int sb) {
     if constexpr (BTN == 1) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) b.a[j] = ((const u32x4*)a.xpack)[((size_t)sb * 8 + j) * 64 + lane];
     }
   };
-  auto step = [&](Q4Buf<NT, NA>& b, int sb, bool newer_in_flight) {
-    if (newer_in_flight)
-      wait_vmcnt<kBatch>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_sched_barrier(0);
+  auto step = [&](ABuf<NA>& b, int sb) {
     lds_u8* slots[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) slots[t] = ring + (b.slot * NT + t) * kQ4Stage;
+    for (int t = 0; t < NT; ++t) slots[t] = slot_of(sb, t);
     q4_step<NT, BTN>(a, slots, b.a, sb, lane, acc);
   };
-  pipeline2(sb0, sb1, b0, b1, load, step);
+  pipeline_ring<KW, KA>(sb0, sb1, b0, b1, issue_w, issue_a, step);
 }
 
 constexpr u32 kNeg160Bf16 = 0xC320C320u;  // two bf16 -160.0
@@ -236,8 +292,8 @@ constexpr u32 kNeg160Bf16 = 0xC320C320u;  // two bf16 -160.0
 // (S the activation sums), and the quant MFMA accumulates onto it, so the MFMA returns
 // D - 160 S = sum a * (q - 32) with no vector work; the scale is one FMA per row.
 template <int NT, int BTN>
-GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dreg)[NT], const u32 (&shreg)[NT],
-                    const u32x4* ca, int sb, int lane, float (&acc)[NT][BTN][4]) {
+GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&s16reg)[NT], const u32x4* ca, int sb,
+                    int lane, float (&acc)[NT][BTN][4]) {
   const u32x4* xp = (const u32x4*)a.xpack;
   const u32x2 neg160 = {kNeg160Bf16, kNeg160Bf16};
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -246,11 +302,12 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dr
   Q6Regs w[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    // row n's window at 212 n holds block byte b at b + sh (addr::q6_lds_byte): the field
-    // at block byte C (a multiple of 4) is the dword pair at 212 n + C shifted right by
-    // sh bytes
-    const u32 sh = shreg[t];  // bytes (alignbyte's shift operand counts bytes)
-    const lds_u8* rs = slot[t] + 212 * n;
+    // row n's window at 224 n holds block byte b at s16 + b (addr::q6_lds_byte): the
+    // field at block byte C (a multiple of 4) is the dword pair at 224 n + (s16 & 12) + C
+    // shifted right by s16 & 3 bytes
+    const u32 s16 = s16reg[t];
+    const u32 sh = s16 & 3u;  // bytes (alignbyte's shift operand counts bytes)
+    const lds_u8* rs = slot[t] + 224 * n + (s16 & 12u);
     const lds_u8* rp = rs + 4 * kg;
 #pragma unroll
     for (int hu = 0; hu < 4; ++hu) {
@@ -262,7 +319,7 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dr
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[t].sc[i] = lds_pair(rs + 192 + 4 * i, rs + 196 + 4 * i, sh);
-    w[t].d = (u16)dreg[t];
+    w[t].d = (u16)(lds_pair(rs + 208, rs + 212, sh) & 0xFFFFu);
   }
   float dsc[NT];
 #pragma unroll
@@ -303,18 +360,11 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&dr
   }
 }
 
-template <int NT, int NA>
-struct Q6Buf {
-  int slot;
-  u32 d[NT];   // this lane's row's fp16 d (read from global: it is not always staged)
-  u32x4 a[NA];
-};
-
 template <int NT, int BTN, bool ALIGNED>
 GR_DEV void q6_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, int sb0, int sb1, int lane,
                     float (&acc)[NT][BTN][4]) {
   constexpr int NA = BTN == 1 ? 8 : 1;
-  constexpr int kBatch = NT * (kQ6LoadInstr + 1) + (BTN == 1 ? 8 : 0);
+  constexpr int KW = NT * kQ6LoadInstr, KA = BTN == 1 ? 8 : 0;
   const int n = lane & 15;
   Q6Lane ln[NT];
   u32 on[NT];  // byte offset of row n (block 0) from the tile base
@@ -323,52 +373,41 @@ GR_DEV void q6_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, i
     ln[t] = q6_lane(tr[t], lane);
     on[t] = tr[t].off(n);
   }
-  Q6Buf<NT, NA> b0, b1;
-  b0.slot = 0;
-  b1.slot = 1;
-  auto load = [&](Q6Buf<NT, NA>& b, int sb) {
+  auto slot_of = [&](int sb, int t) { return ring + (((sb - sb0) & (kRing - 1)) * NT + t) * kQ6Stage; };
+  ABuf<NA> b0, b1;
+  auto issue_w = [&](int sb) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      q6_issue<ALIGNED>(tr[t], ln[t], sb, ring + (b.slot * NT + t) * kQ6Stage);
-      b.d[t] = *(const u16*)(tr[t].base + (size_t)sb * kQ6KBytes + on[t] + 208u);
-    }
+    for (int t = 0; t < NT; ++t) q6_issue<ALIGNED>(tr[t], ln[t], sb, slot_of(sb, t));
+  };
+  auto issue_a = [&](ABuf<NA>& b, int sb) {
     if constexpr (BTN == 1) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) b.a[j] = ((const u32x4*)a.xpack)[((size_t)sb * 8 + j) * 64 + lane];
     }
   };
-  auto step = [&](Q6Buf<NT, NA>& b, int sb, bool newer_in_flight) {
-    if (newer_in_flight)
-      wait_vmcnt<kBatch>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_sched_barrier(0);
+  auto step = [&](ABuf<NA>& b, int sb) {
     lds_u8* slots[NT];
-    u32 sh[NT];
+    u32 s16[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      slots[t] = ring + (b.slot * NT + t) * kQ6Stage;
-      sh[t] = ((u32)(uintptr_t)(tr[t].base + (size_t)sb * kQ6KBytes) + on[t]) & 3u;
+      slots[t] = slot_of(sb, t);
+      s16[t] = addr::q6_s16((u32)(uintptr_t)(tr[t].base + (size_t)sb * kQ6KBytes) + on[t]);
     }
-    q6_step<NT, BTN>(a, slots, b.d, sh, b.a, sb, lane, acc);
+    q6_step<NT, BTN>(a, slots, s16, b.a, sb, lane, acc);
   };
-  pipeline2(sb0, sb1, b0, b1, load, step);
+  pipeline_ring<KW, KA>(sb0, sb1, b0, b1, issue_w, issue_a, step);
 }
 
 // ---------------------------------------------------------------------------------
 // the kernel: waves split K, LDS reduction, epilogue
 
-GR_DEV float row_scale(const GemmArgs& a, int b) {
-  return a.ss ? 1.0f / sqrtf(a.ss[b] * a.inv_k + a.eps) : 1.0f;
-}
-
-// ALIGNED (Q6_K only): every weight row is a multiple of 4 bytes (an even number of
+// ALIGNED (Q6_K only): every weight row is a multiple of 16 bytes (a multiple of 8
 // super-blocks per row).
 template <int WT, int NT, int BTN, int MAXT, bool ALIGNED>
 __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // staging rings, then the reduction
   float* red = (float*)lds;  // [waves][NT][BTN][64 lanes][2]
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nwaves = blockDim.x >> 6;
   const int tile = blockIdx.x;
   const int n = lane & 15;
@@ -376,20 +415,58 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
   if (a.zero_ptr && tile == 0)
     for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.f;
 
-  // rows of the tile(s)
+  // rows of the tile(s).  SwiGLU: tile t of the pair is the same 16 columns of gate
+  // (t = 0) and up (t = 1).  Otherwise the workgroup's group of NT consecutive tiles of
+  // one matrix; a tile past the matrix's rows (odd tile count) re-reads the previous
+  // tile's rows and stores nothing.
   int seg = 0, local = tile;
   if (a.epi != kEpiSwiGLU) {
     while (seg + 1 < a.nseg && tile >= a.seg_tile_off[seg + 1]) ++seg;
     local = tile - a.seg_tile_off[seg];
   }
   TileRows tr[NT];
-  int rows_n = 0;
+  int rows_n = a.seg_rows[seg];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int s = a.epi == kEpiSwiGLU ? t : seg;
-    rows_n = a.seg_rows[s];
-    tr[t] = TileRows{a.w[s] + (size_t)local * 16 * a.row_bytes, rows_n - local * 16, (u32)a.row_bytes};
+    int lt = a.epi == kEpiSwiGLU ? local : local * NT + t;  // tile index within matrix s
+    if (lt * 16 >= a.seg_rows[s]) lt = (a.seg_rows[s] - 1) / 16;
+    tr[t] = TileRows{a.w[s] + (size_t)lt * 16 * a.row_bytes, a.seg_rows[s] - lt * 16, (u32)a.row_bytes};
   }
+  // Epilogue element e = (t, bt, lane', k2) (a SwiGLU pair handles both tiles at once).
+  // Its operands that do not depend on the GEMM (the row's sum of squares, the residual
+  // and the next norm gain) are loaded before the main loop, for the first kPre
+  // elements of each thread, so the epilogue waits on no memory.
+  constexpr int kPer = NT * BTN * 128;
+  const int n_elem = a.epi == kEpiSwiGLU ? BTN * 128 : kPer;
+  struct Elem {
+    bool in, live;
+    int t, rem, bt, nn, brow, col;
+  };
+  auto elem = [&](int e) {
+    Elem m;
+    m.in = e < n_elem;
+    m.t = a.epi == kEpiSwiGLU ? 0 : (m.in ? e / (BTN * 128) : 0);
+    m.rem = e % (BTN * 128);
+    m.bt = m.rem / 128;
+    const int lp = (m.rem % 128) >> 1, k2 = m.rem & 1;
+    m.nn = lp & 15;
+    m.brow = 8 * m.bt + 2 * (lp >> 4) + k2;
+    const int lt = a.epi == kEpiSwiGLU ? local : local * NT + m.t;  // output tile within the matrix
+    m.live = m.in && m.brow < a.B && lt * 16 + m.nn < rows_n;
+    m.col = (a.epi == kEpiSwiGLU ? 0 : a.seg_col_off[seg]) + lt * 16 + m.nn;
+    return m;
+  };
+  constexpr int kPre = BTN > 2 ? 0 : ((kPer + 63) / 64 < 4 ? (kPer + 63) / 64 : 4);
+  float pre_ss[kPre > 0 ? kPre : 1], pre_x[kPre > 0 ? kPre : 1], pre_g[kPre > 0 ? kPre : 1];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const Elem m = elem(threadIdx.x + k * blockDim.x);
+    pre_ss[k] = (m.live && a.ss) ? a.ss[m.brow] : 0.f;
+    pre_x[k] = (m.live && a.epi == kEpiResidual) ? a.y[(size_t)m.brow * a.ldy + m.col] : 0.f;
+    pre_g[k] = (m.live && a.epi == kEpiResidual && a.gain) ? a.gain[m.col] : 1.f;
+  }
+
   float acc[NT][BTN][4];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -401,7 +478,7 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
   const int sb0 = wave * a.sb_per_wave;
   const int sb1 = min(a.nsb, sb0 + a.sb_per_wave);
   constexpr int kStage = WT == 12 ? kQ4Stage : kQ6Stage;
-  lds_u8* ring = (lds_u8*)lds + __builtin_amdgcn_readfirstlane(wave) * (2 * NT * kStage);
+  lds_u8* ring = (lds_u8*)lds + wave * (kRing * NT * kStage);
   if (sb0 < sb1) {
     if constexpr (WT == 12)
       q4_wave<NT, BTN>(a, tr, ring, sb0, sb1, lane, acc);
@@ -421,50 +498,58 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
     }
   __syncthreads();
 
-  // epilogue: element e = (t, bt, lane', k2); a SwiGLU pair handles both tiles at once
-  constexpr int kPer = NT * BTN * 128;
-  const int n_elem = a.epi == kEpiSwiGLU ? BTN * 128 : kPer;
-  for (int e = threadIdx.x; e < ((n_elem + 63) & ~63); e += blockDim.x) {
+  // epilogue
+  const float inv_k = a.inv_k, eps = a.eps;
+  int k = 0;
+  for (int e = threadIdx.x; e < ((n_elem + 63) & ~63); e += blockDim.x, ++k) {
     // every lane of the wave reaches the shuffles below
-    const bool in = e < n_elem;
-    const int t = a.epi == kEpiSwiGLU ? 0 : (in ? e / (BTN * 128) : 0);
-    const int rem = e % (BTN * 128);
-    const int bt = rem / 128, lp = (rem % 128) >> 1, k2 = rem & 1;
-    const int nn = lp & 15, g = lp >> 4;
-    const int brow = 8 * bt + 2 * g + k2;
+    const Elem m = elem(e);
     float v = 0.f, v2 = 0.f;
-    if (in) {
+    if (m.in) {
       for (int w = 0; w < nwaves; ++w) {
-        v += red[(((size_t)w * NT + t) * BTN + bt) * 128 + (rem % 128)];
-        if (a.epi == kEpiSwiGLU) v2 += red[(((size_t)w * NT + 1) * BTN + bt) * 128 + (rem % 128)];
+        v += red[(((size_t)w * NT + m.t) * BTN + m.bt) * 128 + (m.rem % 128)];
+        if (a.epi == kEpiSwiGLU) v2 += red[(((size_t)w * NT + 1) * BTN + m.bt) * 128 + (m.rem % 128)];
       }
     }
-    const bool live = in && brow < a.B && local * 16 + nn < rows_n;
-    const float rs = live ? row_scale(a, brow) : 0.f;
-    const int col = (a.epi == kEpiSwiGLU ? 0 : a.seg_col_off[seg]) + local * 16 + nn;
+    float ssv = 0.f, xv = 0.f, gv_ = 1.f;
+    if (k < kPre) {
+#pragma unroll
+      for (int q = 0; q < kPre; ++q)
+        if (q == k) {
+          ssv = pre_ss[q];
+          xv = pre_x[q];
+          gv_ = pre_g[q];
+        }
+    } else if (m.live) {
+      ssv = a.ss ? a.ss[m.brow] : 0.f;
+      if (a.epi == kEpiResidual) {
+        xv = a.y[(size_t)m.brow * a.ldy + m.col];
+        gv_ = a.gain ? a.gain[m.col] : 1.f;
+      }
+    }
+    const float rs = m.live ? (a.ss ? 1.0f / sqrtf(ssv * inv_k + eps) : 1.0f) : 0.f;
     if (a.epi == kEpiStore) {
-      if (live) a.y[(size_t)brow * a.ldy + col] = rs * v;
+      if (m.live) a.y[(size_t)m.brow * a.ldy + m.col] = rs * v;
     } else if (a.epi == kEpiSwiGLU) {
-      if (live) {
+      if (m.live) {
         const float gv = rs * v, uv = rs * v2;
-        actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, brow, col, gv / (1.0f + expf(-gv)) * uv);
+        actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, m.brow, m.col, gv / (1.0f + expf(-gv)) * uv);
       }
     } else {
       float xn = 0.f;
-      if (live) {
-        float* xp = a.y + (size_t)brow * a.ldy + col;
-        xn = *xp + rs * v;
-        *xp = xn;
-        const float pv = a.gain ? xn * a.gain[col] : xn;
-        if (a.pack_out) actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, brow, col, pv);
-        if (a.pack_out2) actpack_put(a.pack_out2, a.pack_kind2, a.pack_nslices2, brow, col, pv);
+      if (m.live) {
+        xn = xv + rs * v;
+        a.y[(size_t)m.brow * a.ldy + m.col] = xn;
+        const float pv = xn * gv_;
+        if (a.pack_out) actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, m.brow, m.col, pv);
+        if (a.pack_out2) actpack_put(a.pack_out2, a.pack_kind2, a.pack_nslices2, m.brow, m.col, pv);
       }
       // sum of squares over the tile's 16 columns of each batch row: lanes with the
       // same (g, k2) differ in nn, which is bits 1..4 of the thread index
       float sq = xn * xn;
 #pragma unroll
       for (int o = 2; o <= 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
-      if (in && nn == 0 && brow < a.B && a.ss_out) atomicAdd(a.ss_out + brow, sq);
+      if (m.in && m.nn == 0 && m.brow < a.B && a.ss_out) atomicAdd(a.ss_out + m.brow, sq);
     }
   }
 }
@@ -472,25 +557,25 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------------
 // plan and launch
 
-GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, bool pair) {
+GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, int nt) {
   GemmPlan pl{};
-  pl.nt = pair ? 2 : 1;
+  pl.nt = nt;
   pl.btn = actpack_tiles(B);
   pl.tiles = total_tiles;
   const int nsb = K / kQK;
-  // registers: one-tile, one-batch-tile kernels use up to 8 waves per workgroup, the
-  // others up to 4
+  // registers: one-tile, one-batch-tile kernels fit 8 waves per workgroup (2 per SIMD),
+  // the others 4
   pl.maxt = (pl.nt == 1 && pl.btn == 1) ? 512 : 256;
   const int max_waves = pl.maxt / 64;
   // about 4096 waves in flight, at least one super-block per wave
   int want = (4096 + total_tiles - 1) / total_tiles;
   if (want > max_waves) want = max_waves;
   if (want > nsb) want = nsb;
-  // LDS: staging rings (waves * NT * 2 slots) and the reduction (waves * NT * BTN * 512 B)
-  // share one allocation of at most 64 KB
+  // LDS: staging rings (waves * NT * kRing slots) and the reduction (waves * NT * BTN *
+  // 512 B) share one allocation of at most kGemmLds
   const int stage = wtype == 12 ? kQ4Stage : kQ6Stage;
-  auto lds_need = [&](int w) { return max(w * pl.nt * 2 * stage, w * pl.nt * pl.btn * 512); };
-  while (want > 1 && lds_need(want) > 65536) --want;
+  auto lds_need = [&](int w) { return max(w * pl.nt * kRing * stage, w * pl.nt * pl.btn * 512); };
+  while (want > 1 && lds_need(want) > kGemmLds) --want;
   if (want < 1) want = 1;
   pl.sb_per_wave = (nsb + want - 1) / want;
   pl.waves = (nsb + pl.sb_per_wave - 1) / pl.sb_per_wave;
@@ -518,7 +603,7 @@ hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStre
   if (wtype == 12) {
     GR_GEMM_SWITCH(12, true)
   } else {
-    if (a.row_bytes % 4 == 0) {
+    if (a.row_bytes % 16 == 0) {
       GR_GEMM_SWITCH(14, true)
     } else {
       GR_GEMM_SWITCH(14, false)

@@ -13,13 +13,14 @@
 // Q4_K (144-byte blocks, 16-byte aligned): 9 chunks per row, 144 per stage; chunk c
 // is row c / 9, bytes 16 (c % 9) of its block; LDS byte 16 c.
 //
-// Q6_K (210-byte blocks, 2-byte aligned): let A be a row block's address and sh =
-// A % 4 (0 or 2).  The row's 53 dword slots are the window [A - sh, A - sh + 212):
-// block byte b sits at window byte b + sh.  The window never starts before the block's
-// row data (A - sh >= the matrix start: sh == 2 only when A is not 4-aligned); with
-// sh == 0 its last dword reaches 2 bytes past the block, which at the matrix's end is
-// the tail of an aligned dword (it cannot cross a page) and lies beyond the buffer
-// descriptor's size.  Slot c of a stage is row c / 53, window dword c % 53; LDS byte 4c.
+// Q6_K (210-byte blocks, 2-byte aligned): let A be a row block's address and s16 =
+// A % 16 (even).  The row's window is the 224 bytes [A - s16, A - s16 + 224), i.e. 14
+// whole 16-byte units: block byte b sits at window byte s16 + b, so the whole block
+// (quants, scales and d) is inside.  Every unit is 16-byte aligned and starts inside the
+// matrix (A - s16 >= the matrix start, which is 16-byte aligned), so a unit running past
+// the matrix's end stays within the aligned 16 bytes holding that end (no page is
+// crossed) and lies beyond the buffer descriptor's size.  Unit c of a stage is row
+// c / 14, window unit c % 14; LDS byte 16 c.
 #ifndef GR_GEMM_ADDR_H_
 #define GR_GEMM_ADDR_H_
 
@@ -35,9 +36,10 @@ namespace gr {
 namespace addr {
 
 constexpr int kQ4Instr = 3;   // 16-byte loads per lane and stage (144 chunks)
-constexpr int kQ6Instr = 14;  // 4-byte loads per lane and stage (848 dword slots)
+constexpr int kQ6Instr = 4;   // 16-byte loads per lane and stage (224 units)
 constexpr int kQ4Units = 144;
-constexpr int kQ6Units = 16 * 53;  // 53 window dwords per row
+constexpr int kQ6RowUnits = 14;  // 16-byte units per Q6_K row window
+constexpr int kQ6Units = 16 * kQ6RowUnits;
 
 // Byte offset from the tile's first row of tile row r: a ragged last tile (nvalid < 16
 // rows inside the matrix) repeats its last row.
@@ -52,28 +54,27 @@ GR_HD int q6_unit(int lane, int i) { const int c = lane + 64 * i; return c < kQ6
 GR_HD int q4_row(int c) { return c / 9; }
 GR_HD uint32_t q4_in_block(int c) { return 16u * (uint32_t)(c % 9); }  // byte offset in the row block
 
-GR_HD int q6_row(int c) { return c / 53; }
-GR_HD int q6_slot(int c) { return c % 53; }
+GR_HD int q6_row(int c) { return c / kQ6RowUnits; }
 
-// Q6_K: sh of a row block starting at an address with low 32 bits `addr_lo`.
-GR_HD uint32_t q6_sh(uint32_t addr_lo) { return addr_lo & 3u; }
+// Q6_K: s16 of a row block starting at an address with low 32 bits `addr_lo`.
+GR_HD uint32_t q6_s16(uint32_t addr_lo) { return addr_lo & 15u; }
 
-// Q6_K: per-lane constant of a slot: its window dword's offset from (the row's block
-// address - sh), measured from the tile's block address.
-GR_HD uint32_t q6_pre(uint32_t row_offset, int w) { return row_offset + 4u * (uint32_t)w; }
+// Q6_K: per-lane constant of a unit: its offset from (the row's block address - s16),
+// measured from the tile's block address.
+GR_HD uint32_t q6_pre(uint32_t row_offset, int c) { return row_offset + 16u * (uint32_t)(c % kQ6RowUnits); }
 
-// Q6_K, rows of a multiple of 4 bytes (every row block has the tile's sh): the load
-// address is (tile block address - sh) + pre.
-// Q6_K, general rows: the load address is (tile block address - 2) + q6_rel(pre, sh),
-// sh that of the slot's row.
-GR_HD uint32_t q6_rel(uint32_t pre, uint32_t sh) { return pre + 2u - sh; }
+// Q6_K, rows of a multiple of 16 bytes (every row block has the tile's s16): the load
+// address is (tile block address - s16) + pre.
+// Q6_K, general rows: the load address is (tile block address - 16) + q6_rel(pre, s16),
+// s16 that of the unit's row.
+GR_HD uint32_t q6_rel(uint32_t pre, uint32_t s16) { return pre + 16u - s16; }
 
-// Q6_K: LDS byte offset, within row r's slots, of block byte b.
-GR_HD uint32_t q6_lds_byte(int r, uint32_t b, uint32_t sh) { return 212u * (uint32_t)r + b + sh; }
+// Q6_K: LDS byte offset, within a stage, of block byte b of row r.
+GR_HD uint32_t q6_lds_byte(int r, uint32_t b, uint32_t s16) { return 224u * (uint32_t)r + s16 + b; }
 
 // LDS byte offset, within a stage, where lane `lane`'s load of instruction i lands.
 GR_HD uint32_t q4_lds(int lane, int i) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
-GR_HD uint32_t q6_lds(int lane, int i) { return 256u * (uint32_t)i + 4u * (uint32_t)lane; }
+GR_HD uint32_t q6_lds(int lane, int i) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
 
 }  // namespace addr
 }  // namespace gr

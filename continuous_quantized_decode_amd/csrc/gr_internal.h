@@ -48,7 +48,7 @@ enum GemmEpi {
 struct GemmArgs {
   const uint8_t* w[3];
   int seg_rows[3];
-  int seg_tile_off[4];  // first tile of each matrix; [nseg] = total tiles
+  int seg_tile_off[4];  // first workgroup of each matrix; [nseg] = total workgroups
   int seg_col_off[3];   // first output column of each matrix
   int nseg;
   int nsb;              // super-blocks per row (K/256)
@@ -77,7 +77,16 @@ struct GemmPlan {
   size_t lds;
 };
 
-GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, bool pair);
+// total_tiles: workgroups (tile groups of nt tiles, or gate/up pairs with nt = 2).
+GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, int nt);
+
+// Tiles per workgroup of a plain (non-SwiGLU) GEMM launch: consecutive 16-row tiles of
+// one matrix share each activation fragment when there are enough tiles to fill the
+// chip in pairs.
+inline int gemm_group(int tiles) { return tiles >= 1024 ? 2 : 1; }
+
+// LDS per GEMM workgroup (gfx950: 160 KB per workgroup).
+constexpr int kGemmLds = 160 * 1024;
 hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------------- actpack

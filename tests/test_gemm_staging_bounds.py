@@ -6,10 +6,11 @@ into a small C++ program that enumerates every tile shape, ragged last tile,
 super-block, lane and load instruction and checks that:
   * every load lies inside the weight matrix (no read before its start or past its end);
   * Q4_K loads are 16-byte chunks inside their row block;
-  * Q6_K loads are aligned dwords inside [block - sh, block + 210), except that a final
-    dword may end 2 bytes past the matrix (the tail of an aligned dword: no page crossed);
+  * Q6_K loads are 16-byte aligned units starting inside [block - s16, block + 210); a
+    unit may end past the matrix only inside the aligned 16 bytes that hold its end (no
+    page is crossed);
   * no LDS write leaves the stage;
-  * every LDS byte the compute reads (row r's Q4_K block at 144 r; bytes 0..207 of its
+  * every LDS byte the compute reads (row r's Q4_K block at 144 r; all 210 bytes of its
     Q6_K block at gemm_addr.h's q6_lds_byte) holds the right byte of the matrix after
     the stage's loads.
 """
@@ -38,7 +39,7 @@ int main() {
   for (int wt = 0; wt < 2; ++wt) {
     const uint32_t bb = wt == 0 ? 144 : 210;
     const int ni = wt == 0 ? kQ4Instr : kQ6Instr;
-    const int stage = wt == 0 ? kQ4Instr * 64 * 16 : kQ6Instr * 64 * 4;
+    const int stage = (wt == 0 ? kQ4Instr : kQ6Instr) * 64 * 16;
     for (int nsb : nsbs) for (int N : rows) {
       const uint32_t row_bytes = bb * nsb;
       const uint64_t total = (uint64_t)N * row_bytes;  // the matrix starts 16-byte aligned, at 0
@@ -50,7 +51,7 @@ int main() {
           for (int lane = 0; lane < 64; ++lane) {
             for (int i = 0; i < ni; ++i) {
               uint64_t a; uint32_t len, lds;
-              bool ok_end = false;  // a Q6_K dword may end up to 2 bytes past the matrix
+              bool ok_end = false;  // a Q6_K unit may end past the matrix inside its last aligned 16 bytes
               if (wt == 0) {
                 const int c = q4_unit(lane, i);
                 const uint64_t blk = tile + row_off(q4_row(c), nvalid, row_bytes) + (uint64_t)sb * bb;
@@ -58,27 +59,25 @@ int main() {
                 CHECK(a >= blk && a + len <= blk + bb, "q4 load leaves its row block");
               } else {
                 // exactly the kernel's arithmetic: a per-lane constant and the tile's
-                // block address, with sh from the tile (rows of a multiple of 4 bytes)
-                // or from the slot's row (general)
+                // block address, with s16 from the tile (rows of a multiple of 16 bytes)
+                // or from the unit's row (general)
                 const int c = q6_unit(lane, i);
-                const uint32_t pre = q6_pre(row_off(q6_row(c), nvalid, row_bytes), q6_slot(c));
+                const uint32_t pre = q6_pre(row_off(q6_row(c), nvalid, row_bytes), c);
                 const uint64_t tblk = tile + (uint64_t)sb * bb;
                 const uint64_t blk = tile + row_off(q6_row(c), nvalid, row_bytes) + (uint64_t)sb * bb;
-                const uint32_t sh = q6_sh((uint32_t)blk);
-                if (row_bytes % 4 == 0) {
-                  const uint32_t sh0 = q6_sh((uint32_t)tblk);
-                  CHECK(sh0 == sh, "tile sh differs from the row's");
-                  a = tblk - sh0 + pre;
+                const uint32_t s16 = q6_s16((uint32_t)blk);
+                if (row_bytes % 16 == 0) {
+                  const uint32_t t16 = q6_s16((uint32_t)tblk);
+                  CHECK(t16 == s16, "tile s16 differs from the row's");
+                  a = tblk - t16 + pre;
                 } else {
-                  CHECK(q6_sh((uint32_t)tblk + pre) == sh, "row sh from the lane constant is wrong");
-                  a = tblk - 2 + q6_rel(pre, q6_sh((uint32_t)tblk + pre));
+                  CHECK(q6_s16((uint32_t)tblk + pre) == s16, "row s16 from the lane constant is wrong");
+                  a = tblk - 16 + q6_rel(pre, q6_s16((uint32_t)tblk + pre));
                 }
-                len = 4; lds = q6_lds(lane, i);
-                CHECK(a % 4 == 0 && a + sh >= blk && a < blk + 210, "q6 load leaves [blk - sh, blk + 210)");
-                // past the matrix end only as the tail of an aligned dword that starts inside
-                if (a + len > total) CHECK(a < total && a + len - total <= 2, "q6 load runs past the matrix end");
-                else CHECK(true, "");
-                ok_end = a + len > total;
+                len = 16; lds = q6_lds(lane, i);
+                CHECK(a % 16 == 0 && a + s16 >= blk && a < blk + 210, "q6 unit does not start in [blk - s16, blk + 210)");
+                // past the matrix end only inside the aligned 16 bytes holding the end
+                ok_end = a % 16 == 0 && a < total;
               }
               CHECK(a < total && (a + len <= total || ok_end), "wt %d nsb %d N %d row0 %d sb %d lane %d i %d: [%llu,+%u) outside %llu",
                     wt, nsb, N, row0, sb, lane, i, (unsigned long long)a, len, (unsigned long long)total);
@@ -95,10 +94,10 @@ int main() {
                 CHECK(held[144 * r + b] == (int64_t)(blk + b), "q4 nsb %d N %d row0 %d sb %d row %d byte %d", nsb, N,
                       row0, sb, r, b);
             } else {
-              const uint32_t sh = q6_sh((uint32_t)blk);
-              for (uint32_t b = 0; b < 208; ++b)
-                CHECK(held[q6_lds_byte(r, b, sh)] == (int64_t)(blk + b), "q6 nsb %d N %d row0 %d sb %d row %d byte %u sh %u",
-                      nsb, N, row0, sb, r, b, sh);
+              const uint32_t s16 = q6_s16((uint32_t)blk);
+              for (uint32_t b = 0; b < 210; ++b)
+                CHECK(held[q6_lds_byte(r, b, s16)] == (int64_t)(blk + b), "q6 nsb %d N %d row0 %d sb %d row %d byte %u s16 %u",
+                      nsb, N, row0, sb, r, b, s16);
             }
           }
         }
