@@ -134,6 +134,7 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     a.xpack = pin.pack;
     a.nslices = nslices_of(pin.kind, K);
     a.ss = ep.ss;
+    a.ss_slots = ss_slots(B);
     a.inv_k = 1.0f / (float)K;
     a.eps = ep.eps;
     a.B = B;
@@ -177,6 +178,7 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   a.xpack = pin.pack;
   a.nslices = nslices_of(pin.kind, K);
   a.ss = ss;
+  a.ss_slots = ss_slots(B);
   a.inv_k = 1.0f / (float)K;
   a.eps = eps;
   a.B = B;
@@ -207,8 +209,8 @@ LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan&
   L.op = carve_pack2(c, B, qd);
   L.ap = carve_pack2(c, B, cfg->ffn);
   L.qkv = c.take<float>((size_t)B * (qd + 2 * kvd) * 4);
-  L.ss_attn = c.take<float>((size_t)B * 4);
-  L.ss_ffn = c.take<float>((size_t)B * 4);
+  L.ss_attn = c.take<float>((size_t)kSsCap * 4);  // [ss_slots(B)][B]
+  L.ss_ffn = c.take<float>((size_t)kSsCap * 4);
   const size_t units = (size_t)B * cfg->n_q_heads * ap.max_splits;
   L.o_part = c.take<float>(units * cfg->head_dim * 4);
   L.m_part = c.take<float>(units * 4);
@@ -314,7 +316,7 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
     ep.ss = L.ss_attn;
     ep.eps = c->rms_eps;
     ep.zero_ptr = L.ss_ffn;
-    ep.zero_n = B;
+    ep.zero_n = ss_slots(B) * B;
     return check_launch(gemm_run(ws, ts, rs, 3, H, B, L.xp, ep, st));
   });
   if (s != GR_OK) return s;
@@ -373,7 +375,7 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   //    attention-norm accumulator for step 6
   s = probed(probe, GR_STAGE_GATE_UP, st, [&] {
     return check_launch(gemm_swiglu(w->w_gate, w->w_up, w->tgate, F, H, B, L.xp, L.ss_ffn, c->rms_eps,
-                                    L.ap.of(w->tdown), L.ss_attn, B, st));
+                                    L.ap.of(w->tdown), L.ss_attn, ss_slots(B) * B, st));
   });
   if (s != GR_OK) return s;
   // 6. x += W_down a; pack x * next_gain for the next consumer

@@ -48,7 +48,7 @@ constexpr int kQ6LoadInstr = addr::kQ6Instr;  // 16-byte loads per lane and stag
 // valid chunk into the padding), so each stage is exactly kQ*LoadInstr VMEM
 // instructions on every path and the vmcnt waits below are exact.
 constexpr int kQ4Stage = kQ4LoadInstr * 64 * 16;  // 3072 B (2304 used)
-constexpr int kQ6Stage = kQ6LoadInstr * 64 * 16;  // 4096 B (3584 used)
+constexpr int kQ6Stage = kQ6LoadInstr * 64 * 16;  // 4096 B (3840 used)
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -68,8 +68,7 @@ struct TileRows {
   GR_DEV const uint8_t* end() const { return base + (size_t)nvalid * row_bytes; }  // past its last row
 };
 
-// Staging loads (unit mapping and address arithmetic: gemm_addr.h).  In LDS, row r's
-// Q4_K block sits at 144 r and its Q6_K dword window at 212 r.  The loads are buffer
+// Staging loads (unit mapping, address arithmetic and LDS row strides: gemm_addr.h).  The loads are buffer
 // loads into LDS: the wave-uniform part of the address (the tile's super-block) lives
 // in the buffer descriptor, rebuilt per stage with scalar instructions, and each lane
 // keeps its offsets within the tile, computed once.  The descriptor's size ends at the
@@ -218,7 +217,7 @@ GR_DEV void q4_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32x4* c
   float sd[NT][8], mm[NT][8];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const lds_u8* rp = slot[t] + kQ4KBytes * n;  // row n's block
+    const lds_u8* rp = slot[t] + addr::q4_lds_byte(n, 0);  // row n's block
     w[t].hdr = *(const __attribute__((address_space(3))) u32x4*)rp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) w[t].qs[c] = *(const __attribute__((address_space(3))) u32x2*)(rp + 16 + 32 * c + 8 * kg);
@@ -302,12 +301,12 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&s1
   Q6Regs w[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    // row n's window at 224 n holds block byte b at s16 + b (addr::q6_lds_byte): the
-    // field at block byte C (a multiple of 4) is the dword pair at 224 n + (s16 & 12) + C
-    // shifted right by s16 & 3 bytes
+    // row n's window holds block byte b at q6_lds_byte(n, b, s16): the field at block
+    // byte C (a multiple of 4) is the dword pair at q6_lds_byte(n, C, s16 & 12) shifted
+    // right by s16 & 3 bytes
     const u32 s16 = s16reg[t];
     const u32 sh = s16 & 3u;  // bytes (alignbyte's shift operand counts bytes)
-    const lds_u8* rs = slot[t] + 224 * n + (s16 & 12u);
+    const lds_u8* rs = slot[t] + addr::q6_lds_byte(n, 0, s16 & 12u);
     const lds_u8* rp = rs + 4 * kg;
 #pragma unroll
     for (int hu = 0; hu < 4; ++hu) {
@@ -433,10 +432,20 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
     if (lt * 16 >= a.seg_rows[s]) lt = (a.seg_rows[s] - 1) / 16;
     tr[t] = TileRows{a.w[s] + (size_t)lt * 16 * a.row_bytes, a.seg_rows[s] - lt * 16, (u32)a.row_bytes};
   }
+  // The input rows' RMSNorm partial sums (ss_slots * B <= kSsCap values) are loaded
+  // before the main loop and parked in LDS beside the reduction for the epilogue.
+  constexpr int kSsPer = kSsCap / 64;  // values per thread in the smallest workgroup
+  const int n_ss = a.ss ? a.ss_slots * a.B : 0;
+  float ssp[kSsPer];
+#pragma unroll
+  for (int j = 0; j < kSsPer; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    ssp[j] = i < n_ss ? a.ss[i] : 0.f;
+  }
   // Epilogue element e = (t, bt, lane', k2) (a SwiGLU pair handles both tiles at once).
-  // Its operands that do not depend on the GEMM (the row's sum of squares, the residual
-  // and the next norm gain) are loaded before the main loop, for the first kPre
-  // elements of each thread, so the epilogue waits on no memory.
+  // Its other operands that do not depend on the GEMM (the residual and the next norm
+  // gain) are loaded before the main loop, for the first kPre elements of each thread,
+  // so the epilogue waits on no memory.
   constexpr int kPer = NT * BTN * 128;
   const int n_elem = a.epi == kEpiSwiGLU ? BTN * 128 : kPer;
   struct Elem {
@@ -458,11 +467,10 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
     return m;
   };
   constexpr int kPre = BTN > 2 ? 0 : ((kPer + 63) / 64 < 4 ? (kPer + 63) / 64 : 4);
-  float pre_ss[kPre > 0 ? kPre : 1], pre_x[kPre > 0 ? kPre : 1], pre_g[kPre > 0 ? kPre : 1];
+  float pre_x[kPre > 0 ? kPre : 1], pre_g[kPre > 0 ? kPre : 1];
 #pragma unroll
   for (int k = 0; k < kPre; ++k) {
     const Elem m = elem(threadIdx.x + k * blockDim.x);
-    pre_ss[k] = (m.live && a.ss) ? a.ss[m.brow] : 0.f;
     pre_x[k] = (m.live && a.epi == kEpiResidual) ? a.y[(size_t)m.brow * a.ldy + m.col] : 0.f;
     pre_g[k] = (m.live && a.epi == kEpiResidual && a.gain) ? a.gain[m.col] : 1.f;
   }
@@ -496,6 +504,12 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
       r[0] = acc[t][b][0] + acc[t][b][1];  // hi + lo parts of batch row 8b + 2g
       r[1] = acc[t][b][2] + acc[t][b][3];  // and of row 8b + 2g + 1
     }
+  float* s_ss = red + (size_t)nwaves * NT * BTN * 128;  // [ss_slots][B]
+#pragma unroll
+  for (int j = 0; j < kSsPer; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    if (i < n_ss) s_ss[i] = ssp[j];
+  }
   __syncthreads();
 
   // epilogue
@@ -512,16 +526,16 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
       }
     }
     float ssv = 0.f, xv = 0.f, gv_ = 1.f;
+    if (m.live && a.ss)
+      for (int s = 0; s < a.ss_slots; ++s) ssv += s_ss[s * a.B + m.brow];
     if (k < kPre) {
 #pragma unroll
       for (int q = 0; q < kPre; ++q)
         if (q == k) {
-          ssv = pre_ss[q];
           xv = pre_x[q];
           gv_ = pre_g[q];
         }
     } else if (m.live) {
-      ssv = a.ss ? a.ss[m.brow] : 0.f;
       if (a.epi == kEpiResidual) {
         xv = a.y[(size_t)m.brow * a.ldy + m.col];
         gv_ = a.gain ? a.gain[m.col] : 1.f;
@@ -549,7 +563,8 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
       float sq = xn * xn;
 #pragma unroll
       for (int o = 2; o <= 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
-      if (m.in && m.nn == 0 && m.brow < a.B && a.ss_out) atomicAdd(a.ss_out + m.brow, sq);
+      if (m.in && m.nn == 0 && m.brow < a.B && a.ss_out)
+        atomicAdd(a.ss_out + (size_t)(tile % a.ss_slots) * a.B + m.brow, sq);
     }
   }
 }
@@ -572,9 +587,11 @@ GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, int nt) {
   if (want > max_waves) want = max_waves;
   if (want > nsb) want = nsb;
   // LDS: staging rings (waves * NT * kRing slots) and the reduction (waves * NT * BTN *
-  // 512 B) share one allocation of at most kGemmLds
+  // 512 B, then the RMSNorm partial sums) share one allocation of at most kGemmLds
   const int stage = wtype == 12 ? kQ4Stage : kQ6Stage;
-  auto lds_need = [&](int w) { return max(w * pl.nt * kRing * stage, w * pl.nt * pl.btn * 512); };
+  auto lds_need = [&](int w) {
+    return max(w * pl.nt * kRing * stage, w * pl.nt * pl.btn * 512 + kSsCap * (int)sizeof(float));
+  };
   while (want > 1 && lds_need(want) > kGemmLds) --want;
   if (want < 1) want = 1;
   pl.sb_per_wave = (nsb + want - 1) / want;

@@ -55,7 +55,9 @@ struct GemmArgs {
   size_t row_bytes;
   const void* xpack;    // actpack of the input, kind by weight type
   int nslices;
-  const float* ss;      // per-row sum of squares of the input (RMSNorm), or NULL: r = 1
+  const float* ss;      // per-row sum of squares of the input (RMSNorm) in ss_slots
+                        // partial slots [slot][B], or NULL: r = 1
+  int ss_slots;
   float inv_k, eps;
   int B;
   int sb_per_wave;
@@ -67,10 +69,19 @@ struct GemmArgs {
   int pack_kind, pack_nslices;
   u16* pack_out2;       // residual: a second actpack kind of the same values (NULL: none)
   int pack_kind2, pack_nslices2;
-  float* ss_out;        // residual: sum of squares accumulator of the packed rows
+  float* ss_out;        // residual: sum of squares accumulator of the packed rows, [ss_slots][B]
   float* zero_ptr;      // optional: workgroup 0 zeroes zero_n floats
   int zero_n;
 };
+
+// The RMSNorm statistic (per-row sum of squares) that a GEMM epilogue applies is kept
+// as ss_slots(B) partial sums [slot][B] (at most kSsCap floats).  A producer running in
+// many workgroups adds into slot (workgroup % slots), so that only a few atomics meet
+// on one address (hundreds of same-address float atomics from all XCDs serialize at
+// the memory side and hold the kernel's completion for microseconds); consumers add
+// the slots up.
+constexpr int kSsCap = 256;
+__host__ __device__ inline int ss_slots(int B) { return B <= 16 ? 16 : kSsCap / B; }
 
 struct GemmPlan {
   int nt, btn, waves, sb_per_wave, tiles, maxt;
@@ -123,6 +134,6 @@ struct PackOut {
 // x [B][K] -> actpack(s) of x * gain (gain NULL: 1); with ss_out, also the per-row sum
 // of squares of x (RMSNorm of the consumer).  Zeroes the padding rows of the packs.
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
-                            float* ss_out, hipStream_t st);
+                            float* ss_out, hipStream_t st);  // ss_out: [ss_slots(B)][B], slot 0 the sum
 
 }  // namespace gr

@@ -3,8 +3,9 @@
 // standalone call, and the standalone GEMM.
 //
 // RMSNorm (tinyllm, Status: the Qwen3 components) is x / sqrt(mean(x^2) + eps) * g;
-// the pack holds x * g and the per-row sum of squares, and the consuming GEMM applies
-// 1 / sqrt(sum/K + eps) to its outputs.
+// the pack holds x * g and the per-row sum of squares (slot 0 of the ss_slots partial
+// sums, the others zero), and the consuming GEMM applies 1 / sqrt(sum/K + eps) to its
+// outputs.
 #include "gr_internal.h"
 
 namespace gr {
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
       float tot = 0.f;
       for (int w = 0; w < kPackThreads / 64; ++w) tot += red[w];
       ss_out[b] = tot;
+      for (int s = 1; s < ss_slots(B); ++s) ss_out[(size_t)s * B + b] = 0.f;
     }
   }
 }

@@ -10,8 +10,8 @@ super-block, lane and load instruction and checks that:
     unit may end past the matrix only inside the aligned 16 bytes that hold its end (no
     page is crossed);
   * no LDS write leaves the stage;
-  * every LDS byte the compute reads (row r's Q4_K block at 144 r; all 210 bytes of its
-    Q6_K block at gemm_addr.h's q6_lds_byte) holds the right byte of the matrix after
+  * every LDS byte the compute reads (all bytes of row r's Q4_K / Q6_K block, at
+    gemm_addr.h's q4_lds_byte / q6_lds_byte) holds the right byte of the matrix after
     the stage's loads.
 """
 import os
@@ -91,7 +91,7 @@ int main() {
             const uint64_t blk = tile + row_off(r, nvalid, row_bytes) + (uint64_t)sb * bb;
             if (wt == 0) {
               for (int b = 0; b < 144; ++b)
-                CHECK(held[144 * r + b] == (int64_t)(blk + b), "q4 nsb %d N %d row0 %d sb %d row %d byte %d", nsb, N,
+                CHECK(held[q4_lds_byte(r, b)] == (int64_t)(blk + b), "q4 nsb %d N %d row0 %d sb %d row %d byte %d", nsb, N,
                       row0, sb, r, b);
             } else {
               const uint32_t s16 = q6_s16((uint32_t)blk);
