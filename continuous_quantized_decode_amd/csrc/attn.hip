@@ -364,7 +364,13 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
 // Per (row b, query head h): M = max_s m_s, L = sum_s l_s 2^(m_s - M),
 // o = sum_s o_s 2^(m_s - M) / L (the partials are in the log2 domain).  Writes f32
 // out [B][Hq][D] and/or the actpack of the output projection (K = Hq*D, `kind`).
+// Wave w takes splits w, w + 4, w + 8, ...: it issues the loads of up to kMergeChunk
+// of its splits (m, l and the o vectors) at once, so the common case costs one memory
+// round trip, and folds them into its running (M_w, L_w, o_w); the four waves' results
+// combine through LDS.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kMergeChunk = 16;  // splits per wave and round of loads
 constexpr int kMergeMaxSplits = 1024;
 
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p, float* out, uint16_t* pack,
@@ -372,53 +378,68 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x;
   const int h = bh % p.n_q_heads, b = bh / p.n_q_heads;
-  const int D = p.head_dim;
+  const int D = p.head_dim;  // 64 or 128: dims lane and lane + 64
   const int ctx = p.ctx_lens[b];
   const int n_tok = fused ? ctx + 1 : ctx;
   const int n_pages = (n_tok + kPage - 1) / kPage;
   const int S = min((n_pages + p.pages_per_split - 1) / p.pages_per_split, p.max_splits);
   const size_t base = ((size_t)b * p.n_q_heads + h) * p.max_splits;
-  __shared__ float s_w[kMergeMaxSplits];
-  __shared__ float s_red[kMergeThreads / 64];
-  __shared__ float s_acc[kMergeThreads / 64][128];
+  __shared__ float s_m[kMergeWaves], s_l[kMergeWaves];
+  __shared__ float s_o[kMergeWaves][128];
 
-  float mx = -INFINITY;
-  for (int s = tid; s < S; s += kMergeThreads) mx = fmaxf(mx, p.m_part[base + s]);
-  mx = wave_max(mx);
-  if (lane == 0) s_red[wave] = mx;
-  __syncthreads();
-  float M = s_red[0];
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
-  __syncthreads();
-  float lsum = 0.f;
-  for (int s = tid; s < S; s += kMergeThreads) {
-    const float e = exp2f(p.m_part[base + s] - M);
-    s_w[s] = e;
-    lsum += p.l_part[base + s] * e;
-  }
-  lsum = wave_sum(lsum);
-  if (lane == 0) s_red[wave] = lsum;
-  __syncthreads();
-  float L = 0.f;
-  for (int w = 0; w < kMergeThreads / 64; ++w) L += s_red[w];
-  const float invL = 1.0f / L;
-  // partial sums over splits s = wave, wave + 4, ... for dims lane, lane + 64
-  for (int d0 = 0; d0 < D; d0 += 64) {
-    const int d = d0 + lane;
-    float acc = 0.f;
-    for (int s = wave; s < S; s += kMergeThreads / 64) acc = __builtin_fmaf(p.o_part[(base + s) * D + d], s_w[s], acc);
-    s_acc[wave][d] = acc;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    for (int d0 = 0; d0 < D; d0 += 64) {
-      const int d = d0 + lane;
-      float v = 0.f;
-      for (int w = 0; w < kMergeThreads / 64; ++w) v += s_acc[w][d];
-      v *= invL;
-      if (out) out[((size_t)b * p.n_q_heads + h) * D + d] = v;
-      if (pack) actpack_put(pack, kind, nslices, b, h * D + d, v);
+  float Mw = -INFINITY, Lw = 0.f, ow[2] = {0.f, 0.f};
+  for (int c0 = 0; c0 < S; c0 += kMergeWaves * kMergeChunk) {
+    // lane j < kMergeChunk holds m and l of split c0 + wave + 4 j
+    const int sl = c0 + wave + kMergeWaves * lane;
+    float ml = -INFINITY, ll = 0.f;
+    if (lane < kMergeChunk && sl < S) {
+      ml = p.m_part[base + sl];
+      ll = p.l_part[base + sl];
     }
+    float ov[kMergeChunk][2];
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      const int sj = c0 + wave + kMergeWaves * j;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        ov[j][i] = (sj < S && 64 * i < D) ? p.o_part[(base + sj) * D + 64 * i + lane] : 0.f;
+    }
+    const float Mn = fmaxf(Mw, wave_max(ml));
+    if (Mn == -INFINITY) continue;  // no split of this wave yet (wave-uniform)
+    const float rs = exp2f(Mw - Mn);  // 0 while Mw is -inf
+    const float e = exp2f(ml - Mn);   // 0 for lanes without a split
+    Lw = __builtin_fmaf(Lw, rs, wave_sum(ll * e));
+    ow[0] *= rs;
+    ow[1] *= rs;
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      const float ej = __shfl(e, j, 64);
+      ow[0] = __builtin_fmaf(ov[j][0], ej, ow[0]);
+      ow[1] = __builtin_fmaf(ov[j][1], ej, ow[1]);
+    }
+    Mw = Mn;
+  }
+  if (lane == 0) {
+    s_m[wave] = Mw;
+    s_l[wave] = Lw;
+  }
+  s_o[wave][lane] = ow[0];
+  s_o[wave][64 + lane] = ow[1];
+  __syncthreads();
+  if (tid < D) {
+    float M = s_m[0];  // finite: wave 0 holds split 0
+#pragma unroll
+    for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, s_m[w]);
+    float L = 0.f, v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+      const float sc = s_m[w] == -INFINITY ? 0.f : exp2f(s_m[w] - M);
+      L = __builtin_fmaf(s_l[w], sc, L);
+      v = __builtin_fmaf(s_o[w][tid], sc, v);
+    }
+    v *= 1.0f / L;
+    if (out) out[((size_t)b * p.n_q_heads + h) * D + tid] = v;
+    if (pack) actpack_put(pack, kind, nslices, b, h * D + tid, v);
   }
 }
 
