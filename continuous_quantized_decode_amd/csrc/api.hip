@@ -114,7 +114,9 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     GemmArgs a{};
     int j = i, n = 0, tiles = 0, all_tiles = 0;
     for (int q = i; q < nmat && types[q] == types[i]; ++q) all_tiles += (rows[q] + 15) / 16;
-    const int group = gemm_group(all_tiles);
+    // many tiles and a plain store: the tile-loop kernel (one tile per group)
+    const bool tl = ep.kind == kEpiStore && use_tile_loop(all_tiles, K, B);
+    const int group = tl ? 1 : gemm_group(all_tiles);
     while (j < nmat && types[j] == types[i]) {
       a.w[n] = (const uint8_t*)w[j];
       a.seg_rows[n] = rows[j];
@@ -154,9 +156,15 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
       a.zero_n = ep.zero_n;
       zeroed = true;
     }
-    const GemmPlan pl = plan_gemm(wt, tiles, K, B, group);
-    a.sb_per_wave = pl.sb_per_wave;
-    hipError_t e = launch_gemm(wt, pl, a, st);
+    hipError_t e;
+    if (tl) {
+      a.tl_groups = tiles;
+      e = launch_gemm_tl(wt, 1, plan_gemm_tl(wt, 1, tiles, K), a, st);
+    } else {
+      const GemmPlan pl = plan_gemm(wt, tiles, K, B, group);
+      a.sb_per_wave = pl.sb_per_wave;
+      e = launch_gemm(wt, pl, a, st);
+    }
     if (e != hipSuccess) return e;
     i = j;
   }
@@ -188,6 +196,10 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   a.pack_nslices = nslices_of(out.kind, F);
   a.zero_ptr = zero_ptr;
   a.zero_n = zero_n;
+  if (use_tile_loop(tiles, K, B)) {
+    a.tl_groups = tiles;
+    return launch_gemm_tl(wtype, 2, plan_gemm_tl(wtype, 2, tiles, K), a, st);
+  }
   const GemmPlan pl = plan_gemm(wtype, tiles, K, B, 2);
   a.sb_per_wave = pl.sb_per_wave;
   return launch_gemm(wtype, pl, a, st);

@@ -432,16 +432,12 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
     if (lt * 16 >= a.seg_rows[s]) lt = (a.seg_rows[s] - 1) / 16;
     tr[t] = TileRows{a.w[s] + (size_t)lt * 16 * a.row_bytes, a.seg_rows[s] - lt * 16, (u32)a.row_bytes};
   }
-  // The input rows' RMSNorm partial sums (ss_slots * B <= kSsCap values) are loaded
-  // before the main loop and parked in LDS beside the reduction for the epilogue.
-  constexpr int kSsPer = kSsCap / 64;  // values per thread in the smallest workgroup
+  // The input rows' RMSNorm partial sums (ss_slots * B <= kSsCap values) are parked in
+  // LDS beside the reduction for the epilogue: one value per thread is loaded before the
+  // main loop (one register through it), any rest (workgroups of fewer threads than
+  // values) after it.
   const int n_ss = a.ss ? a.ss_slots * a.B : 0;
-  float ssp[kSsPer];
-#pragma unroll
-  for (int j = 0; j < kSsPer; ++j) {
-    const int i = threadIdx.x + j * blockDim.x;
-    ssp[j] = i < n_ss ? a.ss[i] : 0.f;
-  }
+  const float ssp = (int)threadIdx.x < n_ss ? a.ss[threadIdx.x] : 0.f;
   // Epilogue element e = (t, bt, lane', k2) (a SwiGLU pair handles both tiles at once).
   // Its other operands that do not depend on the GEMM (the residual and the next norm
   // gain) are loaded before the main loop, for the first kPre elements of each thread,
@@ -505,11 +501,8 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
       r[1] = acc[t][b][2] + acc[t][b][3];  // and of row 8b + 2g + 1
     }
   float* s_ss = red + (size_t)nwaves * NT * BTN * 128;  // [ss_slots][B]
-#pragma unroll
-  for (int j = 0; j < kSsPer; ++j) {
-    const int i = threadIdx.x + j * blockDim.x;
-    if (i < n_ss) s_ss[i] = ssp[j];
-  }
+  if ((int)threadIdx.x < n_ss) s_ss[threadIdx.x] = ssp;
+  for (int i = threadIdx.x + blockDim.x; i < n_ss; i += blockDim.x) s_ss[i] = a.ss[i];
   __syncthreads();
 
   // epilogue
@@ -570,7 +563,259 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
+// Tile-loop kernel for matrices with many tiles (one activation tile, K <= 2 super-
+// blocks per wave).  Each wave owns a fixed K slice of at most two super-blocks and
+// keeps that slice's activation fragments in registers for the whole launch; the
+// workgroup walks a contiguous run of tile groups, its waves streaming the weights of
+// their slice of each group through a kTlRing-slot LDS ring (prefetch crossing group
+// boundaries), and after each group the waves' partial sums meet in one of two LDS
+// reduction buffers for the group's epilogue.  Activations are read once per
+// workgroup instead of once per group, which leaves the texture path to the weights.
+//
+// Waits: every weight stage is NT * kQ*LoadInstr LDS-DMA loads; the activation loads
+// are issued before any of them.  Loads complete in order, so before stage q only the
+// stages issued after it may be outstanding.  Epilogue stores that are younger than a
+// waited-for load only make a wait longer (a pending older load keeps every younger
+// load pending), never shorter.
+
+// Workgroup barrier for LDS written with ds_write only: the weight loads in flight
+// (LDS-DMA into ring slots that no other wave reads) must not be drained at every
+// group, which a fence would do (LDS-DMA completion is counted by vmcnt).  The wave's
+// own LDS writes complete (lgkmcnt) before the barrier; the memory clobber keeps the
+// compiler from moving memory accesses across it.
+GR_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int WT, int NT, bool ALIGNED, int D>
+__global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
+  static_assert(D >= 2 && D <= 4, "ring depth");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int kStage = WT == 12 ? kQ4Stage : kQ6Stage;
+  constexpr int KW = NT * (WT == 12 ? kQ4LoadInstr : kQ6LoadInstr);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nwaves = blockDim.x >> 6;
+  const int n = lane & 15;
+  lds_u8* ring = (lds_u8*)lds + wave * (D * NT * kStage);
+  float* red = (float*)(lds + (size_t)nwaves * D * NT * kStage);  // [2][waves][NT][128]
+
+  if (a.zero_ptr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.f;
+
+  // this workgroup's tile groups and this wave's K slice
+  const int g0 = blockIdx.x * a.tl_groups_per_wg;
+  const int ng = min(a.tl_groups, g0 + a.tl_groups_per_wg) - g0;
+  const int sb0 = wave * a.sb_per_wave;
+  const int nst = max(0, min(a.nsb, sb0 + a.sb_per_wave) - sb0);  // 1 or 2 (0: idle wave)
+  const int nq = ng * nst;
+
+  // epilogue element of this thread (fixed): e < n_elem
+  const int n_elem = a.epi == kEpiSwiGLU ? 128 : NT * 128;
+  const int e = threadIdx.x;
+  const int e_t = a.epi == kEpiSwiGLU ? 0 : (e < n_elem ? e / 128 : 0);
+  const int e_rem = e & 127;
+  const int e_lp = e_rem >> 1;
+  const int e_nn = e_lp & 15;
+  const int e_brow = 2 * (e_lp >> 4) + (e_rem & 1);
+  // rows of group gi: as in gemm_kernel (SwiGLU pairs, or NT consecutive tiles of one
+  // matrix with a phantom tile re-reading the last one)
+  auto group_rows = [&](int gi, TileRows (&tr)[NT], int& seg, int& local) {
+    seg = 0;
+    local = gi;
+    if (a.epi != kEpiSwiGLU) {
+      while (seg + 1 < a.nseg && gi >= a.seg_tile_off[seg + 1]) ++seg;
+      local = gi - a.seg_tile_off[seg];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int sg = a.epi == kEpiSwiGLU ? t : seg;
+      int lt = a.epi == kEpiSwiGLU ? local : local * NT + t;
+      if (lt * 16 >= a.seg_rows[sg]) lt = (a.seg_rows[sg] - 1) / 16;
+      tr[t] = TileRows{a.w[sg] + (size_t)lt * 16 * a.row_bytes, a.seg_rows[sg] - lt * 16, (u32)a.row_bytes};
+    }
+  };
+  // per-lane load offsets of a full tile (a ragged tile recomputes its own)
+  const TileRows full{a.w[0], 16, (u32)a.row_bytes};
+  auto slot_of = [&](int q, int t) { return ring + ((q % D) * NT + t) * kStage; };
+  auto issue = [&](int q) {
+    const int gl = nst == 2 ? q >> 1 : q;
+    const int s = q - gl * nst;
+    TileRows tr[NT];
+    int seg, local;
+    group_rows(g0 + gl, tr, seg, local);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (WT == 12) {
+        const Q4Lane ln = q4_lane(tr[t].nvalid == 16 ? full : tr[t], lane);
+        q4_issue(tr[t], ln, sb0 + s, slot_of(q, t));
+      } else {
+        const Q6Lane ln = q6_lane(tr[t].nvalid == 16 ? full : tr[t], lane);
+        q6_issue<ALIGNED>(tr[t], ln, sb0 + s, slot_of(q, t));
+      }
+    }
+  };
+
+  float acc[NT][1][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[t][0][k] = 0.f;
+
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d)
+    if (d < nq) issue(d);
+  // activation fragments of the slice (8 per super-block), loaded once, after the first
+  // weight stages (the first step waits for both)
+  u32x4 act[2][8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      act[s][j] = s < nst ? ((const u32x4*)a.xpack)[((size_t)(sb0 + s) * 8 + j) * 64 + lane] : u32x4{0u, 0u, 0u, 0u};
+  float rs = 1.0f;  // 1 / rms of the input row (B <= 8: ss_slots(B) = 16, loaded at once)
+  if (a.ss && e < n_elem && e_brow < a.B) {
+    float sv[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) sv[s] = a.ss[s * a.B + e_brow];
+    float ssv = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) ssv += sv[s];
+    rs = 1.0f / sqrtf(ssv * a.inv_k + a.eps);
+  }
+
+  for (int gl = 0; gl < ng; ++gl) {
+    TileRows tr[NT];
+    int seg, local;
+    group_rows(g0 + gl, tr, seg, local);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < nst) {
+        const int q = gl * nst + s;
+        if (q + D - 1 < nq) issue(q + D - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int younger = min(D - 1, nq - 1 - q);
+        if (younger >= D - 1)
+          wait_vmcnt<(D - 1) * KW>();
+        else if (D > 2 && younger == 1)
+          wait_vmcnt<KW>();
+        else if (D > 3 && younger == 2)
+          wait_vmcnt<2 * KW>();
+        else
+          wait_vmcnt<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        lds_u8* slots[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) slots[t] = slot_of(q, t);
+        if constexpr (WT == 12) {
+          q4_step<NT, 1>(a, slots, act[s], sb0 + s, lane, acc);
+        } else {
+          u32 s16[NT];
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            s16[t] = addr::q6_s16((u32)(uintptr_t)(tr[t].base + (size_t)(sb0 + s) * kQ6KBytes) + tr[t].off(n));
+          q6_step<NT, 1>(a, slots, s16, act[s], sb0 + s, lane, acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the group's partial sums: red[gl & 1][wave][t][lane * 2 + k]
+    float* rb = red + (size_t)(gl & 1) * nwaves * NT * 128;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float* r = rb + ((size_t)wave * NT + t) * 128 + lane * 2;
+      r[0] = acc[t][0][0] + acc[t][0][1];
+      r[1] = acc[t][0][2] + acc[t][0][3];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[t][0][k] = 0.f;
+    }
+    lds_barrier();
+    if (e < n_elem) {
+      float v = 0.f, v2 = 0.f;
+      for (int w = 0; w < nwaves; ++w) {
+        v += rb[((size_t)w * NT + e_t) * 128 + e_rem];
+        if (a.epi == kEpiSwiGLU) v2 += rb[((size_t)w * NT + 1) * 128 + e_rem];
+      }
+      const int lt = a.epi == kEpiSwiGLU ? local : local * NT + e_t;
+      const bool live = e_brow < a.B && lt * 16 + e_nn < a.seg_rows[a.epi == kEpiSwiGLU ? 0 : seg];
+      if (live) {
+        if (a.epi == kEpiSwiGLU) {
+          const float gv = rs * v, uv = rs * v2;
+          actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, e_brow, lt * 16 + e_nn, gv / (1.0f + expf(-gv)) * uv);
+        } else {
+          a.y[(size_t)e_brow * a.ldy + a.seg_col_off[seg] + lt * 16 + e_nn] = rs * v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // plan and launch
+
+// Kernel variants by (NT, BTN): one-tile, one-batch-tile kernels take up to 16 waves
+// (their registers fit four waves per SIMD), the others up to 4.
+struct GemmVariant {
+  const void* fn = nullptr;
+  int maxt = 0;
+  int waves_per_cu = 0;  // resident waves per CU that the kernel's registers allow
+};
+
+template <int WT, bool AL>
+const void* variant_fn(int nt, int btn) {
+  switch (nt * 100 + btn) {
+    case 101: return (const void*)gemm_kernel<WT, 1, 1, 1024, AL>;
+    case 102: return (const void*)gemm_kernel<WT, 1, 2, 256, AL>;
+    case 104: return (const void*)gemm_kernel<WT, 1, 4, 256, AL>;
+    case 108: return (const void*)gemm_kernel<WT, 1, 8, 256, AL>;
+    case 201: return (const void*)gemm_kernel<WT, 2, 1, 256, AL>;
+    case 202: return (const void*)gemm_kernel<WT, 2, 2, 256, AL>;
+    case 204: return (const void*)gemm_kernel<WT, 2, 4, 256, AL>;
+    case 208: return (const void*)gemm_kernel<WT, 2, 8, 256, AL>;
+    default: return nullptr;
+  }
+}
+
+struct VariantTable {
+  GemmVariant v[3][2][4];  // (Q4_K, Q6_K aligned, Q6_K unaligned) x NT x log2 BTN
+  int cus = 256;
+  VariantTable() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                hipSuccess && n > 0)
+      cus = n;
+    for (int ty = 0; ty < 3; ++ty)
+      for (int nt = 1; nt <= 2; ++nt)
+        for (int lb = 0; lb < 4; ++lb) {
+          const int btn = 1 << lb;
+          GemmVariant& g = v[ty][nt - 1][lb];
+          g.fn = ty == 0 ? variant_fn<12, true>(nt, btn) : ty == 1 ? variant_fn<14, true>(nt, btn)
+                                                                  : variant_fn<14, false>(nt, btn);
+          g.maxt = nt == 1 && btn == 1 ? 1024 : 256;
+          // registers per lane -> waves per SIMD (512 VGPRs, granule 8); without a device
+          // to ask, assume the 128 that a 1024-thread workgroup requires
+          int regs = 128;
+          hipFuncAttributes at{};
+          if (hipFuncGetAttributes(&at, g.fn) == hipSuccess && at.numRegs > 0) regs = at.numRegs;
+          const int per_simd = 512 / ((regs + 7) & ~7);
+          g.waves_per_cu = 4 * (per_simd < 8 ? per_simd : 8);
+          (void)hipFuncSetAttribute(g.fn, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+        }
+    (void)hipGetLastError();  // a missing device leaves an error behind; it is not this call's
+  }
+};
+
+const VariantTable& variants() {
+  static const VariantTable t;  // built once, thread-safe
+  return t;
+}
+
+int log2_btn(int btn) { return btn == 1 ? 0 : btn == 2 ? 1 : btn == 4 ? 2 : 3; }
+
+const GemmVariant& gemm_variant(int wtype, bool aligned, int nt, int btn) {
+  const int ty = wtype == 12 ? 0 : aligned ? 1 : 2;
+  return variants().v[ty][nt - 1][log2_btn(btn)];
+}
+
+// Q6_K rows are a multiple of 16 bytes when K is a multiple of 8 super-blocks.
+bool q6_aligned(int K) { return (K / kQK) % 8 == 0; }
 
 GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, int nt) {
   GemmPlan pl{};
@@ -578,55 +823,105 @@ GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, int nt) {
   pl.btn = actpack_tiles(B);
   pl.tiles = total_tiles;
   const int nsb = K / kQK;
-  // registers: one-tile, one-batch-tile kernels fit 8 waves per workgroup (2 per SIMD),
-  // the others 4
-  pl.maxt = (pl.nt == 1 && pl.btn == 1) ? 512 : 256;
-  const int max_waves = pl.maxt / 64;
-  // about 4096 waves in flight, at least one super-block per wave
-  int want = (4096 + total_tiles - 1) / total_tiles;
-  if (want > max_waves) want = max_waves;
-  if (want > nsb) want = nsb;
+  const GemmVariant& v = gemm_variant(wtype, wtype == 12 || q6_aligned(K), nt, pl.btn);
+  pl.maxt = v.maxt;
+  const int max_waves = min(pl.maxt / 64, nsb);
   // LDS: staging rings (waves * NT * kRing slots) and the reduction (waves * NT * BTN *
   // 512 B, then the RMSNorm partial sums) share one allocation of at most kGemmLds
   const int stage = wtype == 12 ? kQ4Stage : kQ6Stage;
   auto lds_need = [&](int w) {
     return max(w * pl.nt * kRing * stage, w * pl.nt * pl.btn * 512 + kSsCap * (int)sizeof(float));
   };
-  while (want > 1 && lds_need(want) > kGemmLds) --want;
-  if (want < 1) want = 1;
-  pl.sb_per_wave = (nsb + want - 1) / want;
+  auto waves_for = [&](int w) {  // waves actually used when splitting nsb over w
+    const int spw = (nsb + w - 1) / w;
+    return (nsb + spw - 1) / spw;
+  };
+  // The most waves per workgroup that still lets every workgroup be resident at once
+  // (one round: no tail of workgroups that start late); when no choice does, about
+  // 4096 waves in flight.
+  int pick = 0;
+  for (int w = max_waves; w >= 1 && !pick; --w) {
+    const int wu = waves_for(w);
+    if (lds_need(wu) > kGemmLds) continue;
+    const int per_cu = min(v.waves_per_cu / wu, kGemmLds / lds_need(wu));
+    if ((long long)per_cu * variants().cus >= total_tiles) pick = wu;
+  }
+  if (!pick) {
+    int want = (4096 + total_tiles - 1) / total_tiles;
+    if (want > max_waves) want = max_waves;
+    while (want > 1 && lds_need(waves_for(want)) > kGemmLds) --want;
+    pick = want < 1 ? 1 : want;
+  }
+  pl.sb_per_wave = (nsb + pick - 1) / pick;
   pl.waves = (nsb + pl.sb_per_wave - 1) / pl.sb_per_wave;
   pl.lds = (size_t)lds_need(pl.waves);
   return pl;
 }
 
-#define GR_GEMM_SWITCH(WTv, ALv)                                                                        \
-  switch (pl.nt * 1000 + pl.btn * 10 + (pl.maxt == 512)) {                                          \
-    case 1011: launch_kernel(gemm_kernel<WTv, 1, 1, 512, ALv>, grid, block, lds, st, a); break; \
-    case 1020: launch_kernel(gemm_kernel<WTv, 1, 2, 256, ALv>, grid, block, lds, st, a); break; \
-    case 1040: launch_kernel(gemm_kernel<WTv, 1, 4, 256, ALv>, grid, block, lds, st, a); break; \
-    case 1080: launch_kernel(gemm_kernel<WTv, 1, 8, 256, ALv>, grid, block, lds, st, a); break; \
-    case 2010: launch_kernel(gemm_kernel<WTv, 2, 1, 256, ALv>, grid, block, lds, st, a); break; \
-    case 2020: launch_kernel(gemm_kernel<WTv, 2, 2, 256, ALv>, grid, block, lds, st, a); break; \
-    case 2040: launch_kernel(gemm_kernel<WTv, 2, 4, 256, ALv>, grid, block, lds, st, a); break; \
-    case 2080: launch_kernel(gemm_kernel<WTv, 2, 8, 256, ALv>, grid, block, lds, st, a); break; \
-    default: return hipErrorInvalidValue;                                                            \
-  }
-
 hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st) {
   if (pl.tiles <= 0) return hipSuccess;
+  const bool aligned = wtype == 12 || a.row_bytes % 16 == 0;
+  const GemmVariant& v = gemm_variant(wtype, aligned, pl.nt, pl.btn);
+  if (!v.fn || v.maxt != pl.maxt || pl.waves * 64 > pl.maxt) return hipErrorInvalidValue;
   const dim3 grid(pl.tiles), block(pl.waves * 64);
   const size_t lds = pl.lds;
-  if (wtype == 12) {
-    GR_GEMM_SWITCH(12, true)
-  } else {
-    if (a.row_bytes % 16 == 0) {
-      GR_GEMM_SWITCH(14, true)
-    } else {
-      GR_GEMM_SWITCH(14, false)
-    }
-  }
-  return hipGetLastError();
+  const void* fn = v.fn;
+  GemmArgs args = a;
+  void* kargs[] = {&args};
+  const hipError_t e = launch_fn(fn, grid, block, lds, st, kargs);
+  return e != hipSuccess ? e : hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// tile-loop plan and launch
+
+// ring depth by (type, NT): the deepest that fits kGemmLds with 8 waves
+constexpr int tl_ring(int wtype, int nt) { return wtype == 12 ? (nt == 1 ? 4 : 3) : (nt == 1 ? 4 : 2); }
+
+bool use_tile_loop(int groups, int K, int B) {
+  return B <= 8 && K % kQK == 0 && K / kQK <= 16 && groups >= 2 * variants().cus;
+}
+
+TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K) {
+  TlPlan pl{};
+  const int nsb = K / kQK;
+  pl.waves = (nsb + 1) / 2;
+  pl.ring = tl_ring(wtype, nt);
+  const int stage = wtype == 12 ? kQ4Stage : kQ6Stage;
+  pl.lds = (size_t)pl.waves * pl.ring * nt * stage + (size_t)2 * pl.waves * nt * 128 * sizeof(float);
+  const int per_cu = max(1, kGemmLds / (int)pl.lds);
+  int wgs = min(groups, variants().cus * per_cu);
+  pl.groups_per_wg = (groups + wgs - 1) / wgs;
+  pl.grid = (groups + pl.groups_per_wg - 1) / pl.groups_per_wg;
+  return pl;
+}
+
+template <int WT, bool AL>
+const void* tl_fn(int nt) {
+  if (nt == 1) return (const void*)gemm_tl_kernel<WT, 1, AL, tl_ring(WT, 1)>;
+  return (const void*)gemm_tl_kernel<WT, 2, AL, tl_ring(WT, 2)>;
+}
+
+hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st) {
+  if (pl.grid <= 0) return hipSuccess;
+  if ((nt != 1 && nt != 2) || pl.waves < 1 || pl.waves > 8 || pl.lds > (size_t)kGemmLds || a.B > 8 ||
+      (a.ss && a.ss_slots != 16))
+    return hipErrorInvalidValue;
+  const bool aligned = wtype == 12 || a.row_bytes % 16 == 0;
+  const void* fn = wtype == 12 ? tl_fn<12, true>(nt) : aligned ? tl_fn<14, true>(nt) : tl_fn<14, false>(nt);
+  static const bool lds_set = [] {
+    const void* all[] = {tl_fn<12, true>(1), tl_fn<12, true>(2), tl_fn<14, true>(1), tl_fn<14, true>(2),
+                         tl_fn<14, false>(1), tl_fn<14, false>(2)};
+    for (const void* f : all) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)lds_set;
+  a.sb_per_wave = 2;
+  a.tl_groups_per_wg = pl.groups_per_wg;
+  void* kargs[] = {&a};
+  const hipError_t e = launch_fn(fn, dim3(pl.grid), dim3(pl.waves * 64), pl.lds, st, kargs);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace gr

@@ -32,6 +32,17 @@ inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t shmem, hipStre
   }
 }
 
+// The same for a kernel chosen at run time (host pointer of a __global__ function and
+// its packed argument pointers).
+inline hipError_t launch_fn(const void* fn, dim3 grid, dim3 block, size_t shmem, hipStream_t st, void** args) {
+  if (ProbeEvents* pe = probe_events) {
+    const hipError_t e = hipExtLaunchKernel(fn, grid, block, args, shmem, st, pe->first ? pe->start : nullptr, pe->stop, 0);
+    pe->first = false;
+    return e;
+  }
+  return hipLaunchKernel(fn, grid, block, args, shmem, st);
+}
+
 // ------------------------------------------------------------------------ GEMM
 //
 // One workgroup per output tile: 16 weight rows (or, for the SwiGLU GEMM, 16 gate
@@ -61,6 +72,7 @@ struct GemmArgs {
   float inv_k, eps;
   int B;
   int sb_per_wave;
+  int tl_groups, tl_groups_per_wg;  // tile-loop kernel: tile groups in all, per workgroup
   int epi;
   float* y;             // store: output; residual: the residual stream x
   int ldy;
@@ -98,6 +110,17 @@ inline int gemm_group(int tiles) { return tiles >= 1024 ? 2 : 1; }
 
 // LDS per GEMM workgroup (gfx950: 160 KB per workgroup).
 constexpr int kGemmLds = 160 * 1024;
+
+// The tile-loop GEMM (workgroups walk runs of tile groups, activations held in
+// registers): used when the batch is one activation tile, K is at most 16 super-blocks
+// (two per wave) and there are at least two tile groups per CU.
+bool use_tile_loop(int groups, int K, int B);
+struct TlPlan {
+  int waves, grid, groups_per_wg, ring;
+  size_t lds;
+};
+TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K);
+hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st);
 hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------------- actpack

@@ -92,6 +92,11 @@ GEMM_CASES = [
     (synth.W_Q6_K, 16, 256, 12288),
     (synth.W_Q6_K, 64, 128, 14336),
     (synth.W_Q4_K, 64, 256, 14336),
+    # tile-loop kernel (at least two tile groups per CU, one batch tile, K <= 4096)
+    (synth.W_Q4_K, 8, 8200, 4096),   # 513 tiles, the last ragged; runs of three per workgroup
+    (synth.W_Q6_K, 5, 9000, 1280),   # 2-byte aligned rows, waves of two and one super-blocks
+    (synth.W_Q6_K, 8, 8192, 4096),
+    (synth.W_Q4_K, 1, 16384, 256),   # one super-block: a single wave per workgroup
 ]
 
 

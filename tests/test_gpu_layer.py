@@ -59,6 +59,9 @@ LAYER_CASES = [
     dict(ctx=[10] * 9, batch=9, kv_dtype=synth.KV_F16),                # two batch tiles
     dict(ctx=[300, 2, 77, 150, 19, 64, 33, 5, 1, 0, 250, 99], batch=12, kv_dtype=synth.KV_Q8_0, w_down=synth.W_Q6_K,
          head_dim=128, n_q_heads=2, n_kv_heads=2),
+    # FFN wide enough for the tile-loop gate/up GEMM (528 gate/up tile pairs)
+    dict(ctx=[40, 7, 300], batch=3, ffn=8448),
+    dict(ctx=[20, 90], batch=2, ffn=8448, w_other=synth.W_Q6_K, kv_dtype=synth.KV_F16),
 ]
 
 
