@@ -348,7 +348,6 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   ap.v_pages = v_pages;
   ap.qkv = L.qkv;
   ap.qkv_ld = qd + 2 * kvd;
-  ap.qkv_splits = 1;
   ap.q_dim = qd;
   ap.kv_dim = kvd;
   ap.q_norm = c->qk_norm ? w->q_norm : nullptr;

@@ -117,8 +117,9 @@ GR_DEV void store_token(const float* vals, uint8_t* stage, uint8_t* dst_head, bo
 
 // ------------------------------------------------------------------- the kernel
 
+// Three waves per SIMD (registers <= 168) for the 16-bit and 8-bit pools; f32 pages need more.
 template <int KVDT, int D, bool FUSED>
-__global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
+__global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kernel(AttnParams p) {
   constexpr int NS = D / 32;  // QK slices
   constexpr int NT = D / 16;  // PV tiles
   const int lane = threadIdx.x;
@@ -129,79 +130,119 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
   const int b = bg / p.n_kv_heads;
   const int R = p.n_q_heads / p.n_kv_heads;
 
+  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
+  const int pg0 = split * p.pages_per_split;
+  const int n = lane & 15, kg = lane >> 4;
+
+  // ---- loads issued before anything waits: the row's context length, the page ids
+  // of the split's first 64 pages (lane i: page pg0 + i; ids past the row's pages are
+  // never used), and the head vectors (q of the R heads; k and v of head g as well in
+  // the fused layer), pairs (da, db) per lane
+  constexpr int kMaxHeads = 10;  // R <= 8 query heads, then k and v
   const int ctx = p.ctx_lens[b];
+  int bt_chunk = pg0;
+  int bt_lane = pg0 + lane < p.max_blocks ? bt[pg0 + lane] : 0;
+  const bool act = lane < D / 2;
+  int da = 0, db = 0;
+  pair_dims(act ? lane : 0, D, p.rope_style, da, db);
+  const int nh = R + (FUSED ? 2 : 0);
+  float va[kMaxHeads], vb[kMaxHeads];
+#pragma unroll
+  for (int hh = 0; hh < kMaxHeads; ++hh) {
+    va[hh] = 0.f;
+    vb[hh] = 0.f;
+    if (hh < nh && act) {
+      const float* src;
+      if (FUSED) {
+        // hh < R: query head g*R + hh; hh == R: k of head g; hh == R+1: v of head g
+        const int off = hh < R ? (g * R + hh) * D : hh == R ? p.q_dim + g * D : p.q_dim + p.kv_dim + g * D;
+        src = p.qkv + (size_t)b * p.qkv_ld + off;
+      } else {
+        src = p.q + ((size_t)b * p.n_q_heads + g * R + hh) * D;
+      }
+      va[hh] = src[da];
+      vb[hh] = src[db];
+    }
+  }
+
   const int n_tok = FUSED ? ctx + 1 : ctx;
   const int n_pages = (n_tok + kPage - 1) / kPage;
-  const int pg0 = split * p.pages_per_split;
   if (pg0 >= n_pages) return;
   const int pg1 = min(n_pages, pg0 + p.pages_per_split);
-  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
 
-  __shared__ float s_vec[10][128];                  // q heads (and k, v) in linear layout
-  __shared__ __attribute__((aligned(16))) u16 s_q[NS][64][8];   // A fragments of Q
+  __shared__ __attribute__((aligned(16))) float s_vec[kMaxHeads][128];  // head vectors, linear layout
   __shared__ __attribute__((aligned(16))) u16 s_p[KVDT == KV_Q8_T ? D / 32 : 1][16][16];  // P transpose
   __shared__ __attribute__((aligned(16))) uint8_t s_knew[D * 4 + 64];
   __shared__ __attribute__((aligned(16))) uint8_t s_vnew[D * 4 + 64];
 
-  const int n = lane & 15, kg = lane >> 4;
   const int HB = kv_head_bytes_t<KVDT>(D);
   const size_t page_bytes = (size_t)HB * p.n_kv_heads;
   const int new_page = ctx / kPage, new_slot = ctx % kPage;
   const bool owner = FUSED && new_page >= pg0 && new_page < pg1;
+  const uint8_t* kbase = (const uint8_t*)p.k_pages + (size_t)g * HB;
+  const uint8_t* vbase = (const uint8_t*)p.v_pages + (size_t)g * HB;
 
-  // ---- query (and, for the owner, the new token's k and v) ---------------------
+  // page j's id: from the lanes' chunk (wave-uniform read), reloaded every 64 pages
+  auto page_id = [&](int j) -> size_t {
+    if (j - bt_chunk >= 64) {
+      bt_chunk = pg0 + ((j - pg0) & ~63);
+      bt_lane = bt_chunk + lane < p.max_blocks ? bt[bt_chunk + lane] : 0;
+    }
+    return (size_t)(u32)__builtin_amdgcn_readlane(bt_lane, j - bt_chunk);
+  };
+  auto load = [&](PageRegs<KVDT, D>& r, int j) {
+    const size_t pg = page_id(j);
+    load_page<KVDT, D>(r, kbase + pg * page_bytes, vbase + pg * page_bytes, lane);
+  };
+  // the first page is in flight during the setup below
+  PageRegs<KVDT, D> r0, r1;
+  load(r0, pg0);
+
+  // ---- QK-norm and RoPE (angles in fp64) of the head vectors, to LDS ----------------
   {
-    const bool act = lane < D / 2;
-    int da = 0, db = 0;
-    pair_dims(act ? lane : 0, D, p.rope_style, da, db);
     double cs = 1.0, sn = 0.0;
     if (FUSED) {
       const double inv = pow(p.rope_theta, -2.0 * (double)(act ? lane : 0) / (double)D);
       sincos((double)ctx * inv, &sn, &cs);
     }
-    const int nh = R + (owner ? 2 : 0);
-    for (int hh = 0; hh < nh; ++hh) {
-      // hh < R: query head g*R + hh; hh == R: k of head g; hh == R+1: v of head g
-      float a = 0.f, bb = 0.f;
-      if (act) {
-        if (FUSED) {
-          const int ld = p.qkv_ld;
-          const int off = hh < R ? (g * R + hh) * D : hh == R ? p.q_dim + g * D : p.q_dim + p.kv_dim + g * D;
-          for (int s = 0; s < p.qkv_splits; ++s) {
-            const float* src = p.qkv + ((size_t)s * p.B + b) * ld + off;
-            a += src[da];
-            bb += src[db];
-          }
-        } else {
-          const float* src = p.q + ((size_t)b * p.n_q_heads + g * R + hh) * D;
-          a = src[da];
-          bb = src[db];
+#pragma unroll
+    for (int hh = 0; hh < kMaxHeads; ++hh) {
+      if (hh < nh) {
+        float a = va[hh], bb = vb[hh];
+        if (FUSED && hh <= R) norm_rope(a, bb, act, hh < R ? p.q_norm : p.k_norm, p.eps, D, da, db, cs, sn);
+        if (act) {
+          s_vec[hh][da] = a;
+          s_vec[hh][db] = bb;
         }
-      }
-      if (FUSED && hh <= R) norm_rope(a, bb, act, hh < R ? p.q_norm : p.k_norm, p.eps, D, da, db, cs, sn);
-      if (act) {
-        s_vec[hh][da] = a;
-        s_vec[hh][db] = bb;
       }
     }
   }
   __syncthreads();
 
-  // Q fragments: row m = 2h + part (f16 hi / lo of q * scale * log2 e); rows >= 2R zero.
+  // Q fragments in registers: lane (m = 2h + part, k) of slice s holds dims
+  // 32s + 8k + pos(i), i < 8, of head h as f16 hi (part 0) or lo (part 1) of
+  // q * scale * log2 e; rows m >= 2R are zero.  pos is the identity, or perm8 for the
+  // q8_0 K layout.
+  u32x4 qf[NS];
   {
     const float qscale = p.scale * 1.4426950408889634f;
-    for (int idx = lane; idx < NS * 64 * 8; idx += 64) {
-      const int i = idx & 7, l = (idx >> 3) & 63, s = idx >> 9;
-      const int m = l & 15, k = l >> 4;
-      const int pos = KVDT == KV_Q8_T ? perm8(i) : i;
-      const int d = 32 * s + 8 * k + pos;
-      u16 v = 0;
-      if (m < 2 * R) {
-        const float x = s_vec[m >> 1][d] * qscale;
+    const int m = lane & 15, k = lane >> 4;
+    const bool live_m = m < 2 * R;
+    const int hq = live_m ? m >> 1 : 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const f32x4 x0 = *(const f32x4*)&s_vec[hq][32 * s + 8 * k];
+      const f32x4 x1 = *(const f32x4*)&s_vec[hq][32 * s + 8 * k + 4];
+      const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      u16 hv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = xv[KVDT == KV_Q8_T ? perm8(i) : i] * qscale;
         const u16 h = f2h(x);
-        v = (m & 1) ? f2h(x - h2f(h)) : h;
+        hv[i] = !live_m ? (u16)0 : (m & 1) ? f2h(x - h2f(h)) : h;
       }
-      s_q[s][l][i] = v;
+      qf[s] = u32x4{(u32)hv[0] | ((u32)hv[1] << 16), (u32)hv[2] | ((u32)hv[3] << 16),
+                    (u32)hv[4] | ((u32)hv[5] << 16), (u32)hv[6] | ((u32)hv[7] << 16)};
     }
     for (int idx = lane; idx < (int)sizeof(s_p) / 2; idx += 64) (&s_p[0][0][0])[idx] = 0;
   }
@@ -213,9 +254,6 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
     store_token<KVDT>(s_vec[R + 1], s_vnew, vdst, true, D, new_slot, lane);
   }
   __syncthreads();
-  u32x4 qf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)&s_q[s][lane][0];
 
   // ---- page loop -------------------------------------------------------------------
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
@@ -223,8 +261,6 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* kbase = (const uint8_t*)p.k_pages + (size_t)g * HB;
-  const uint8_t* vbase = (const uint8_t*)p.v_pages + (size_t)g * HB;
   // One page: scores, online softmax, P transpose, PV.
   auto page = [&](PageRegs<KVDT, D>& cur, int j) {
     if (FUSED && owner && j == new_page) patch_page<KVDT, D>(cur, s_knew, s_vnew, new_slot, lane);
@@ -332,16 +368,9 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
     __syncthreads();
   };
 
-  // Two-buffer pipeline over the split's pages: page j+1 is in flight while page j is
-  // processed.
-  PageRegs<KVDT, D> r0, r1;
-  pipeline2(
-      pg0, pg1, r0, r1,
-      [&](PageRegs<KVDT, D>& r, int j) {
-        const size_t pg = (size_t)bt[j];
-        load_page<KVDT, D>(r, kbase + pg * page_bytes, vbase + pg * page_bytes, lane);
-      },
-      [&](PageRegs<KVDT, D>& cur, int j, bool) { page(cur, j); });
+  // Two-buffer pipeline over the split's pages (the first already in flight): page
+  // j+1 is in flight while page j is processed.
+  pipeline2_loaded(pg0, pg1, r0, r1, load, [&](PageRegs<KVDT, D>& cur, int j, bool) { page(cur, j); });
 
   // ---- partial results -------------------------------------------------------------
   if (2 * kg < R) {

@@ -21,7 +21,7 @@ struct AttnParams {
   const float* q;
   // fused: q/k/v f32 [B][qkv_ld] (q at 0, k at q_dim, v at q_dim + kv_dim)
   const float* qkv;
-  int qkv_ld, qkv_splits, q_dim, kv_dim;
+  int qkv_ld, q_dim, kv_dim;
   const float* q_norm;  // NULL: no QK-norm
   const float* k_norm;
   float eps;

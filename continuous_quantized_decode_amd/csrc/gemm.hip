@@ -297,7 +297,7 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&s1
   const u32x2 neg160 = {kNeg160Bf16, kNeg160Bf16};
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   const int n = lane & 15, kg = lane >> 4;
-  const u32 M = vconst(0x43004300u);
+  const u32 E = vconst(0x43434343u);
   Q6Regs w[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -343,9 +343,8 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&s1
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const u32x2 bq = q6_expand(w[t].part[hu], r, M);
-        const int scv = (int)(int8_t)((w[t].sc[sub >> 2] >> (8 * (sub & 3))) & 0xFF);
-        const float sd = dsc[t] * (float)scv;
+        const u32x2 bq = q6_expand(w[t].part[hu], r, E);
+        const float sd = dsc[t] * (float)(int)(int8_t)((w[t].sc[sub >> 2] >> (8 * (sub & 3))) & 0xFF);
 #pragma unroll
         for (int b = 0; b < BTN; ++b) {
           const f32x4 dd = mfma_bf16_k16(av[b], bq, cs[b]);
@@ -616,24 +615,34 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
   const int e_nn = e_lp & 15;
   const int e_brow = 2 * (e_lp >> 4) + (e_rem & 1);
   // rows of group gi: as in gemm_kernel (SwiGLU pairs, or NT consecutive tiles of one
-  // matrix with a phantom tile re-reading the last one)
+  // matrix with a phantom tile re-reading the last one).  The segment table (at most
+  // three matrices) is read into scalar registers once, so that finding a group's rows
+  // costs no memory access inside the loops.
+  const int nseg = a.nseg;
+  const int off1 = a.seg_tile_off[1], off2 = a.seg_tile_off[2];
+  const int rows0 = a.seg_rows[0], rows1 = a.seg_rows[1], rows2 = a.seg_rows[2];
+  const uint8_t* const w0 = a.w[0];
+  const uint8_t* const w1 = a.w[1];
+  const uint8_t* const w2 = a.w[2];
+  const int col1 = a.seg_col_off[1], col2 = a.seg_col_off[2];
+  auto seg_of = [&](int gi) { return (nseg > 1 && gi >= off1 ? 1 : 0) + (nseg > 2 && gi >= off2 ? 1 : 0); };
+  auto rows_of = [&](int sg) { return sg == 0 ? rows0 : sg == 1 ? rows1 : rows2; };
+  auto w_of = [&](int sg) { return sg == 0 ? w0 : sg == 1 ? w1 : w2; };
+  auto col_of = [&](int sg) { return sg == 0 ? 0 : sg == 1 ? col1 : col2; };
   auto group_rows = [&](int gi, TileRows (&tr)[NT], int& seg, int& local) {
-    seg = 0;
-    local = gi;
-    if (a.epi != kEpiSwiGLU) {
-      while (seg + 1 < a.nseg && gi >= a.seg_tile_off[seg + 1]) ++seg;
-      local = gi - a.seg_tile_off[seg];
-    }
+    seg = a.epi == kEpiSwiGLU ? 0 : seg_of(gi);
+    local = gi - (seg == 0 ? 0 : seg == 1 ? off1 : off2);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int sg = a.epi == kEpiSwiGLU ? t : seg;
+      const int rows = rows_of(sg);
       int lt = a.epi == kEpiSwiGLU ? local : local * NT + t;
-      if (lt * 16 >= a.seg_rows[sg]) lt = (a.seg_rows[sg] - 1) / 16;
-      tr[t] = TileRows{a.w[sg] + (size_t)lt * 16 * a.row_bytes, a.seg_rows[sg] - lt * 16, (u32)a.row_bytes};
+      if (lt * 16 >= rows) lt = (rows - 1) / 16;
+      tr[t] = TileRows{w_of(sg) + (size_t)lt * 16 * a.row_bytes, rows - lt * 16, (u32)a.row_bytes};
     }
   };
   // per-lane load offsets of a full tile (a ragged tile recomputes its own)
-  const TileRows full{a.w[0], 16, (u32)a.row_bytes};
+  const TileRows full{w0, 16, (u32)a.row_bytes};
   auto slot_of = [&](int q, int t) { return ring + ((q % D) * NT + t) * kStage; };
   auto issue = [&](int q) {
     const int gl = nst == 2 ? q >> 1 : q;
@@ -734,13 +743,13 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
         if (a.epi == kEpiSwiGLU) v2 += rb[((size_t)w * NT + 1) * 128 + e_rem];
       }
       const int lt = a.epi == kEpiSwiGLU ? local : local * NT + e_t;
-      const bool live = e_brow < a.B && lt * 16 + e_nn < a.seg_rows[a.epi == kEpiSwiGLU ? 0 : seg];
+      const bool live = e_brow < a.B && lt * 16 + e_nn < rows_of(seg);
       if (live) {
         if (a.epi == kEpiSwiGLU) {
           const float gv = rs * v, uv = rs * v2;
           actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, e_brow, lt * 16 + e_nn, gv / (1.0f + expf(-gv)) * uv);
         } else {
-          a.y[(size_t)e_brow * a.ldy + a.seg_col_off[seg] + lt * 16 + e_nn] = rs * v;
+          a.y[(size_t)e_brow * a.ldy + col_of(seg) + lt * 16 + e_nn] = rs * v;
         }
       }
     }

@@ -113,10 +113,10 @@ GR_DEV int perm4(int i) { return ((i & 1) << 1) | ((i >> 1) & 1); }            /
 // fresh loads in the middle of the compute).
 // step(buffer, item, newer_in_flight) is told whether the next item's loads were
 // issued after this buffer's (so it can wait for its own loads only).
+// The first load (i0 into b0) is issued by the caller, before its own setup work.
 template <class Buf, class Load, class Step>
-GR_DEV void pipeline2(int i0, int i1, Buf& b0, Buf& b1, Load&& load, Step&& step) {
+GR_DEV void pipeline2_loaded(int i0, int i1, Buf& b0, Buf& b1, Load&& load, Step&& step) {
   int i = i0;
-  load(b0, i);
   for (; i + 2 < i1; i += 2) {
     load(b1, i + 1);
     __builtin_amdgcn_sched_barrier(0);

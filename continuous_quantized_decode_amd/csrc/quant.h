@@ -115,8 +115,19 @@ GR_DEV void q6_load(Q6Regs& r, const uint8_t* blk, int kg) {
   r.d = gr_ld((const u16*)(blk + 208));
 }
 
+// Four bytes b0..b3 of v (each < 128) as the bf16 pairs (128 + b0, 128 + b2) and
+// (128 + b1, 128 + b3): one byte permute each, the exponent byte 0x43 taken from E
+// (0x43434343; v_perm_b32 selectors 0-3 pick bytes of its second operand, 4-7 of
+// its first).
+GR_DEV u32x2 bytes_to_bf16(u32 v, u32 E) {
+  u32x2 o;
+  o.x = __builtin_amdgcn_perm(E, v, 0x04020400u);
+  o.y = __builtin_amdgcn_perm(E, v, 0x04030401u);
+  return o;
+}
+
 // 6-bit quants of sub-block (h, 2r+u) as four bytes, then as the bf16 B operand.
-GR_DEV u32x2 q6_expand(const Q6Part& pt, int r, u32 M = 0x43004300u) {
+GR_DEV u32x2 q6_expand(const Q6Part& pt, int r, u32 E = 0x43434343u) {
   u32 v;
   if (r == 0)
     v = (pt.a & 0x0F0F0F0Fu) | ((pt.q << 4) & 0x30303030u);
@@ -126,10 +137,7 @@ GR_DEV u32x2 q6_expand(const Q6Part& pt, int r, u32 M = 0x43004300u) {
     v = ((pt.a >> 4) & 0x0F0F0F0Fu) | (pt.q & 0x30303030u);
   else
     v = ((pt.b >> 4) & 0x0F0F0F0Fu) | ((pt.q >> 2) & 0x30303030u);
-  u32x2 o;
-  o.x = (v & 0x00FF00FFu) | M;
-  o.y = ((v >> 8) & 0x00FF00FFu) | M;
-  return o;
+  return bytes_to_bf16(v, E);
 }
 
 }  // namespace gr
