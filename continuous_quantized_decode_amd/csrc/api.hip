@@ -212,6 +212,7 @@ struct LayerBufs {
   float* qkv;
   float *ss_attn, *ss_ffn;
   float *o_part, *m_part, *l_part;
+  double* rope;  // [B][head_dim / 2][2]: RoPE of the step's positions
 };
 
 LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan& ap) {
@@ -227,6 +228,7 @@ LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan&
   L.o_part = c.take<float>(units * cfg->head_dim * 4);
   L.m_part = c.take<float>(units * 4);
   L.l_part = c.take<float>(units * 4);
+  L.rope = c.take<double>((size_t)B * cfg->head_dim * sizeof(double));
   return L;
 }
 
@@ -299,12 +301,23 @@ Kinds qkv_kinds(const gr_layer_weights* w) {
   return k;
 }
 
-// Pack of the layer input: x * attn_norm and its sum of squares.
+// Pack of the layer input: x * attn_norm and its sum of squares (and, for a decode
+// step, the RoPE table of its positions).
 gr_status run_input_pack(const float* x, int B, int H, const float* gain, Kinds k, const Pack2& xp, float* ss,
-                         hipStream_t st, const Probe* probe) {
+                         hipStream_t st, const Probe* probe, RopeTable rope = RopeTable{}) {
   return probed(probe, GR_STAGE_PACK, st, [&] {
-    return check_launch(launch_pack_rows(x, H, B, H, gain, k.k32 ? xp.k32 : kNoPack, k.k16 ? xp.k16 : kNoPack, ss, st));
+    return check_launch(
+        launch_pack_rows(x, H, B, H, gain, k.k32 ? xp.k32 : kNoPack, k.k16 ? xp.k16 : kNoPack, ss, st, rope));
   });
+}
+
+RopeTable rope_table(const gr_layer_cfg* c, const int32_t* ctx, const LayerBufs& L) {
+  RopeTable r;
+  r.ctx = ctx;
+  r.theta = c->rope_theta;
+  r.half_d = c->head_dim / 2;
+  r.out = L.rope;
+  return r;
 }
 
 // The launch sequence of one decode layer (arguments already validated).  On entry
@@ -353,8 +366,8 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   ap.q_norm = c->qk_norm ? w->q_norm : nullptr;
   ap.k_norm = c->qk_norm ? w->k_norm : nullptr;
   ap.eps = c->rms_eps;
-  ap.rope_theta = c->rope_theta;
   ap.rope_style = c->rope_style;
+  ap.rope = L.rope;
   ap.o_part = L.o_part;
   ap.m_part = L.m_part;
   ap.l_part = L.l_part;
@@ -649,7 +662,7 @@ gr_status gr_decode_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void
   Carver cv(ws);
   const LayerBufs L = carve_layer(cv, c, B, apl);
   hipStream_t st = (hipStream_t)stream;
-  s = run_input_pack(x, B, c->hidden, w->attn_norm, qkv_kinds(w), L.xp, L.ss_attn, st, nullptr);
+  s = run_input_pack(x, B, c->hidden, w->attn_norm, qkv_kinds(w), L.xp, L.ss_attn, st, nullptr, rope_table(c, ctx, L));
   if (s != GR_OK) return s;
   return run_layer(c, w, k_pages, v_pages, x, bt, max_blocks, ctx, B, apl, L, nullptr, Kinds{}, st, nullptr);
 }
@@ -727,7 +740,8 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
   hipStream_t st = (hipStream_t)stream;
   if (probe) probe->layer = 0;
   if (n_layers > 0) {
-    s = run_input_pack(x, B, c->hidden, weights[0].attn_norm, qkv_kinds(&weights[0]), L.xp, L.ss_attn, st, probe);
+    s = run_input_pack(x, B, c->hidden, weights[0].attn_norm, qkv_kinds(&weights[0]), L.xp, L.ss_attn, st, probe,
+                       rope_table(c, ctx, L));
   } else if (head_w) {
     Kinds k;
     k.add(head_wtype);

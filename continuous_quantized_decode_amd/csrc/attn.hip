@@ -19,7 +19,7 @@
 // are merged across splits by log-sum-exp in attn_merge_kernel.
 //
 // The fused variant (used by the decode layer) also reads q, k, v from the QKV
-// GEMM's output, applies QK-RMSNorm and RoPE (angles in fp64), stores the new token's K/V
+// GEMM's output, applies QK-RMSNorm and RoPE (fp64 angles, one table per step), stores the new token's K/V
 // at slot ctx%16 of page block_table[b][ctx/16] in the pool's format, and
 // substitutes those stored values for the slot's contents when it reads that page.
 #include "gr_internal.h"
@@ -136,8 +136,9 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
 
   // ---- loads issued before anything waits: the row's context length, the page ids
   // of the split's first 64 pages (lane i: page pg0 + i; ids past the row's pages are
-  // never used), and the head vectors (q of the R heads; k and v of head g as well in
-  // the fused layer), pairs (da, db) per lane
+  // never used), the head vectors (q of the R heads; k and v of head g as well in the
+  // fused layer), pairs (da, db) per lane, and the RoPE cosine and sine of the lane's
+  // pair at the row's new position (computed in fp64 once per step)
   constexpr int kMaxHeads = 10;  // R <= 8 query heads, then k and v
   const int ctx = p.ctx_lens[b];
   int bt_chunk = pg0;
@@ -146,6 +147,11 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
   int da = 0, db = 0;
   pair_dims(act ? lane : 0, D, p.rope_style, da, db);
   const int nh = R + (FUSED ? 2 : 0);
+  double cs = 1.0, sn = 0.0;
+  if (FUSED && act) {
+    cs = p.rope[((size_t)b * (D / 2) + lane) * 2];
+    sn = p.rope[((size_t)b * (D / 2) + lane) * 2 + 1];
+  }
   float va[kMaxHeads], vb[kMaxHeads];
 #pragma unroll
   for (int hh = 0; hh < kMaxHeads; ++hh) {
@@ -194,17 +200,12 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
     const size_t pg = page_id(j);
     load_page<KVDT, D>(r, kbase + pg * page_bytes, vbase + pg * page_bytes, lane);
   };
-  // the first page is in flight during the setup below
+  // the first two pages are in flight during the setup below
   PageRegs<KVDT, D> r0, r1;
   load(r0, pg0);
 
-  // ---- QK-norm and RoPE (angles in fp64) of the head vectors, to LDS ----------------
+  // ---- QK-norm and RoPE (rotation in fp64) of the head vectors, to LDS -------------
   {
-    double cs = 1.0, sn = 0.0;
-    if (FUSED) {
-      const double inv = pow(p.rope_theta, -2.0 * (double)(act ? lane : 0) / (double)D);
-      sincos((double)ctx * inv, &sn, &cs);
-    }
 #pragma unroll
     for (int hh = 0; hh < kMaxHeads; ++hh) {
       if (hh < nh) {
@@ -368,8 +369,7 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
     __syncthreads();
   };
 
-  // Two-buffer pipeline over the split's pages (the first already in flight): page
-  // j+1 is in flight while page j is processed.
+  // Two-buffer pipeline over the split's pages (the first two already in flight).
   pipeline2_loaded(pg0, pg1, r0, r1, load, [&](PageRegs<KVDT, D>& cur, int j, bool) { page(cur, j); });
 
   // ---- partial results -------------------------------------------------------------

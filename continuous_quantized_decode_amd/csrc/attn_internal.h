@@ -25,8 +25,8 @@ struct AttnParams {
   const float* q_norm;  // NULL: no QK-norm
   const float* k_norm;
   float eps;
-  double rope_theta;
   int rope_style;
+  const double* rope;  // fused: cos, sin of each row's new position per pair [B][D/2][2]
   // partials [B][Hq][max_splits](*D)
   float* o_part;
   float* m_part;

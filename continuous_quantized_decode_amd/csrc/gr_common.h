@@ -106,14 +106,13 @@ GR_DEV int perm4(int i) { return ((i & 1) << 1) | ((i >> 1) & 1); }            /
 
 // ---------------------------------------------------------------- pipelining
 //
-// Software pipeline over items [i0, i1) with two register buffers used in turn:
-// the loads of item i+1 are issued into the idle buffer (and pinned there by a
-// scheduling barrier) before item i is processed from the other.  Unrolled by two so
-// that no buffer is ever copied (a loop-carried copy makes the compiler wait for the
-// fresh loads in the middle of the compute).
-// step(buffer, item, newer_in_flight) is told whether the next item's loads were
-// issued after this buffer's (so it can wait for its own loads only).
-// The first load (i0 into b0) is issued by the caller, before its own setup work.
+// Software pipeline over items [i0, i1) with two register buffers used in turn: b0
+// holds item i0, issued by the caller before its own setup work; the loads of item
+// i+1 are issued into the idle buffer (and pinned there by a scheduling barrier)
+// before item i is processed from the other.  Unrolled by two so that no buffer is
+// ever copied (a loop-carried copy makes the compiler wait for the fresh loads in the
+// middle of the compute).  step(buffer, item, newer_in_flight) is told whether the next
+// item's loads were issued after this buffer's.
 template <class Buf, class Load, class Step>
 GR_DEV void pipeline2_loaded(int i0, int i1, Buf& b0, Buf& b1, Load&& load, Step&& step) {
   int i = i0;

@@ -156,7 +156,17 @@ struct PackOut {
 
 // x [B][K] -> actpack(s) of x * gain (gain NULL: 1); with ss_out, also the per-row sum
 // of squares of x (RMSNorm of the consumer).  Zeroes the padding rows of the packs.
+// RoPE of the step's new tokens (position ctx[b]): for pair i < half_d the angle
+// ctx[b] * theta^(-2i / (2 half_d)), its cosine and sine in fp64 at out[(b * half_d +
+// i) * 2 + {0, 1}], computed once per step for every layer's attention.
+struct RopeTable {
+  const int32_t* ctx = nullptr;
+  double theta = 0.0;
+  int half_d = 0;
+  double* out = nullptr;  // NULL: none
+};
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
-                            float* ss_out, hipStream_t st);  // ss_out: [ss_slots(B)][B], slot 0 the sum
+                            float* ss_out, hipStream_t st,  // ss_out: [ss_slots(B)][B], slot 0 the sum
+                            RopeTable rope = RopeTable{});
 
 }  // namespace gr

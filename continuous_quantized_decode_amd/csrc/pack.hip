@@ -16,8 +16,15 @@ constexpr int kPackThreads = 1024;
 // four consecutive columns per pass (K % 256 == 0, x rows 16-byte aligned).
 __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __restrict__ x, int ldx, int B, int K,
                                                                  const float* __restrict__ gain, PackOut o1,
-                                                                 PackOut o2, float* ss_out) {
+                                                                 PackOut o2, float* ss_out, RopeTable rope) {
   const int b = blockIdx.x, tid = threadIdx.x;
+  if (rope.out && b < B && tid < rope.half_d) {
+    const double inv = pow(rope.theta, -2.0 * (double)tid / (double)(2 * rope.half_d));
+    double sn, cs;
+    sincos((double)rope.ctx[b] * inv, &sn, &cs);
+    rope.out[((size_t)b * rope.half_d + tid) * 2] = cs;
+    rope.out[((size_t)b * rope.half_d + tid) * 2 + 1] = sn;
+  }
   const int ns1 = o1.kind == kK32 ? K / 32 : K / 16, ns2 = o2.kind == kK32 ? K / 32 : K / 16;
   __shared__ float red[kPackThreads / 64];
   float ss = 0.f;
@@ -51,9 +58,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
 }
 
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
-                            float* ss_out, hipStream_t st) {
+                            float* ss_out, hipStream_t st, RopeTable rope) {
+  if (rope.out && (rope.half_d <= 0 || rope.half_d > kPackThreads || !rope.ctx)) return hipErrorInvalidValue;
   launch_kernel(pack_rows_kernel, dim3(8 * actpack_tiles(B)), dim3(kPackThreads), 0, st, x, ldx, B, K, gain, o1, o2,
-                ss_out);
+                ss_out, rope);
   return hipGetLastError();
 }
 
