@@ -577,6 +577,71 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
 // waited-for load only make a wait longer (a pending older load keeps every younger
 // load pending), never shorter.
 
+constexpr u32 kNeg128Bf16 = 0xC300C300u;  // two bf16 -128.0
+
+// bf16 of a small non-negative integer value v (exact), in both halves of a dword.
+GR_DEV u32 bf16_dup(float v) {
+  const u32 b = f2u(v);
+  return (b >> 16) | (b & 0xFFFF0000u);
+}
+
+// One Q4_K super-block in the tile-loop kernel.  The wave's activation slice is fixed,
+// so the sums S_j of its 32-weight sub-blocks come precomputed (aS: the K = 16 MFMA
+// A operand holding S_2g and S_2g+1 of row l % 16 as bf16 hi/lo pairs).  Each
+// sub-block's quant MFMA starts from C_j = A_j x (-128) = -128 S_j, so it returns
+// sum a q with no vector work (as the Q6_K path), and the mins term is one MFMA per
+// tile (B: the mins m_j as exact bf16, repeated for the hi and lo parts of S_j):
+//   acc += sum_j d sc_j (D_j - 128 S_j) - dmin sum_j m_j S_j
+template <int NT>
+GR_DEV void q4_step_tl(lds_u8* const (&slot)[NT], const u32x4 (&ca)[8], u32x2 aS, int lane,
+                       float (&acc)[NT][1][4]) {
+  const u32x4 neg128 = {kNeg128Bf16, kNeg128Bf16, kNeg128Bf16, kNeg128Bf16};
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, kg = lane >> 4;
+  const u32 M = vconst(0x43004300u);
+  Q4Regs w[NT];
+  float sd[NT][8], dmin[NT];
+  u32x2 bm[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const lds_u8* rp = slot[t] + addr::q4_lds_byte(n, 0);  // row n's block
+    w[t].hdr = *(const __attribute__((address_space(3))) u32x4*)rp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[t].qs[c] = *(const __attribute__((address_space(3))) u32x2*)(rp + 16 + 32 * c + 8 * kg);
+    const u32 h0 = w[t].hdr.x, s0 = w[t].hdr.y, s1 = w[t].hdr.z, s2 = w[t].hdr.w;
+    const float d = h2f((u16)(h0 & 0xFFFF));
+    dmin[t] = h2f((u16)(h0 >> 16));
+    const u32 sc_lo = s0 & 0x3F3F3F3Fu, sc_hi = (s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sd[t][j] = d * (float)((sc_lo >> (8 * j)) & 0xFF);
+      sd[t][j + 4] = d * (float)((sc_hi >> (8 * j)) & 0xFF);
+    }
+    // mins m_2kg and m_2kg+1: bytes 2(kg & 1) and 2(kg & 1) + 1 of the low (j < 4) or
+    // high (j >= 4) mins word
+    const u32 m_lo = s1 & 0x3F3F3F3Fu, m_hi = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
+    const u32 mw = (kg < 2 ? m_lo : m_hi) >> (16 * (kg & 1));
+    bm[t] = u32x2{bf16_dup((float)(mw & 0xFF)), bf16_dup((float)((mw >> 8) & 0xFF))};
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f32x4 cj = mfma_bf16_k32(ca[j], neg128, z4);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 bq = q4_expand(w[t].qs[j >> 1], (j & 1) != 0, M);
+      const f32x4 dd = mfma_bf16_k32(ca[j], bq, cj);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][0][e] = __builtin_fmaf(sd[t][j], dd[e], acc[t][0][e]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const f32x4 corr = mfma_bf16_k16(aS, bm[t], z4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[t][0][e] = __builtin_fmaf(-dmin[t], corr[e], acc[t][0][e]);
+  }
+}
+
 // Workgroup barrier for LDS written with ds_write only: the weight loads in flight
 // (LDS-DMA into ring slots that no other wave reads) must not be drained at every
 // group, which a fence would do (LDS-DMA completion is counted by vmcnt).  The wave's
@@ -668,22 +733,60 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc[t][0][k] = 0.f;
 
+  // Issue order: the RMSNorm partial sums, the slice's activation fragments (8 per
+  // super-block, loaded once; a one-super-block slice loads its block twice), then the
+  // first D - 1 weight stages (unconditionally: a workgroup with fewer stages repeats
+  // its last one into slots it never reads).  So the first step waits for stage 0 and
+  // what is older than it, not for the whole prologue.
+  float sv[16];  // B <= 8: ss_slots(B) = 16; every lane loads (a valid row), uniformly
+  if (a.ss) {
+    const int row = min(e_brow, a.B - 1);
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d)
-    if (d < nq) issue(d);
-  // activation fragments of the slice (8 per super-block), loaded once, after the first
-  // weight stages (the first step waits for both)
+    for (int s = 0; s < 16; ++s) sv[s] = a.ss[s * a.B + row];
+  }
   u32x4 act[2][8];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < 2; ++s) {
+    const int sb = min(sb0 + s, a.nsb - 1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      act[s][j] = s < nst ? ((const u32x4*)a.xpack)[((size_t)(sb0 + s) * 8 + j) * 64 + lane] : u32x4{0u, 0u, 0u, 0u};
-  float rs = 1.0f;  // 1 / rms of the input row (B <= 8: ss_slots(B) = 16, loaded at once)
+    for (int j = 0; j < 8; ++j) act[s][j] = ((const u32x4*)a.xpack)[((size_t)sb * 8 + j) * 64 + lane];
+  }
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) issue(d < nq ? d : nq - 1);
+  // everything but the prologue's stages has landed (so the loop starts with no
+  // register load pending, and the compiler adds no wait of its own before it)
+  wait_vmcnt<(D - 1) * KW>();
+  // Q4_K: the slice's sub-block sums S_j as the mins MFMA's A operand (row l % 16,
+  // j = 2kg and 2kg + 1, bf16 hi/lo), transposed through this wave's part of the
+  // reduction buffers before any group uses them
+  u32x2 aS[2] = {u32x2{0u, 0u}, u32x2{0u, 0u}};
+  if constexpr (WT == 12) {
+    const u32x4 ones = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float* scr = red + ((size_t)s * nwaves + wave) * NT * 128;  // 128 floats: [j][row]
+      f32x4 sj[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sj[j] = mfma_bf16_k32(act[s][j], ones, z4);
+      if (m == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) scr[j * 16 + 4 * g + q] = sj[j][q];
+      }
+      u16 h0, l0, h1, l1;
+      split_bf16(scr[(2 * g) * 16 + m], h0, l0);
+      split_bf16(scr[(2 * g + 1) * 16 + m], h1, l1);
+      aS[s] = u32x2{(u32)h0 | ((u32)l0 << 16), (u32)h1 | ((u32)l1 << 16)};
+    }
+  }
+  float rs = 1.0f;  // 1 / rms of the input row
   if (a.ss && e < n_elem && e_brow < a.B) {
-    float sv[16];
+    // (the empty asm keeps the sum from being hoisted above the prologue's loads)
 #pragma unroll
-    for (int s = 0; s < 16; ++s) sv[s] = a.ss[s * a.B + e_brow];
+    for (int s = 0; s < 16; ++s) asm volatile("" : "+v"(sv[s]));
     float ssv = 0.f;
 #pragma unroll
     for (int s = 0; s < 16; ++s) ssv += sv[s];
@@ -714,7 +817,7 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) slots[t] = slot_of(q, t);
         if constexpr (WT == 12) {
-          q4_step<NT, 1>(a, slots, act[s], sb0 + s, lane, acc);
+          q4_step_tl<NT>(slots, act[s], aS[s], lane, acc);
         } else {
           u32 s16[NT];
 #pragma unroll
