@@ -167,10 +167,10 @@ def stage_launches(gr, wl) -> dict:
     """stage -> (kernel name as the profilers print it, grid size in threads or None)."""
     B, H, F = wl.batch, wl.hidden, wl.ffn
     qkv_rows = wl.q_dim + 2 * wl.kv_dim
-    shapes = {"qkv": (wl.w_other, qkv_rows, H, False), "wo": (wl.w_other, H, wl.q_dim, False),
-              "gate_up": (wl.w_other, F, H, True), "down": (wl.w_down, H, F, False)}
+    shapes = {"qkv": (wl.w_other, qkv_rows, H, gr.GEMM_EPI_STORE), "wo": (wl.w_other, H, wl.q_dim, gr.GEMM_EPI_RESIDUAL),
+              "gate_up": (wl.w_other, F, H, gr.GEMM_EPI_SWIGLU), "down": (wl.w_down, H, F, gr.GEMM_EPI_RESIDUAL)}
     if wl.vocab:
-        shapes["head"] = (wl.w_head, wl.vocab, H, False)
+        shapes["head"] = (wl.w_head, wl.vocab, H, gr.GEMM_EPI_STORE)
     out = {s: (sh["kernel"], sh["grid_threads"])
            for s, sh in ((s, gr.gr_gemm_launch_shape(*v[:3], B, v[3])) for s, v in shapes.items())}
     kvdt = {0: 0, 1: 1, 2: 2}[wl.kv_dtype]

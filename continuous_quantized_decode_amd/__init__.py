@@ -74,7 +74,7 @@ def _load() -> C.CDLL:
         getattr(L, n).restype = _i
     L.gr_gemm_workspace_size.argtypes = [_i, _i, _i]
     L.gr_gemm_workspace_size.restype = _sz
-    L.gr_gemm_launch_shape.argtypes = [_i, _i, _i, _i, _i] + [C.POINTER(_i)] * 5
+    L.gr_gemm_launch_shape.argtypes = [_i, _i, _i, _i, _i] + [C.POINTER(_i)] * 6
     L.gr_gemm_launch_shape.restype = _i
     for n in ("gr_q4k_gemm", "gr_q6k_gemm"):
         getattr(L, n).argtypes = [_p, _p, _p, _i, _i, _i, _p, _sz, _p]
@@ -101,7 +101,7 @@ def _load() -> C.CDLL:
     L.gr_decode_stack.restype = _i
     L.gr_decode_stack_probed.argtypes = list(L.gr_decode_stack.argtypes) + [_i, _i, C.POINTER(_p), C.POINTER(_p)]
     L.gr_decode_stack_probed.restype = _i
-    if L.gr_abi_version() != 1:
+    if L.gr_abi_version() != 2:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
     return L
@@ -202,13 +202,18 @@ def gr_q6k_gemm(wblocks, x, n: int, y=None, ws=None):
     return _gemm("gr_q6k_gemm", wblocks, x, n, y, ws)
 
 
-def gr_gemm_launch_shape(wtype: int, rows: int, k: int, b: int, pair: bool = False) -> dict:
-    """Kernel template parameters and grid of the GEMM launch for these sizes."""
-    v = [C.c_int() for _ in range(5)]
-    _check("gr_gemm_launch_shape", _load().gr_gemm_launch_shape(wtype, rows, k, b, int(pair), *[C.byref(i) for i in v]))
-    nt, btn, maxt, grid, block = (i.value for i in v)
-    return {"nt": nt, "btn": btn, "maxt": maxt, "grid_threads": grid, "block_threads": block,
-            "kernel": f"gemm_kernel<{wtype}, {nt}, {btn}, {maxt}>"}
+GEMM_EPI_STORE, GEMM_EPI_RESIDUAL, GEMM_EPI_SWIGLU = 0, 1, 2
+
+
+def gr_gemm_launch_shape(wtype: int, rows: int, k: int, b: int, epi: int = GEMM_EPI_STORE) -> dict:
+    """Which GEMM kernel runs for these sizes, its template parameters and grid.  `kernel`
+    is the prefix of the kernel's name as profilers print it."""
+    v = [C.c_int() for _ in range(6)]
+    _check("gr_gemm_launch_shape", _load().gr_gemm_launch_shape(wtype, rows, k, b, int(epi), *[C.byref(i) for i in v]))
+    tl, nt, btn, maxt, grid, block = (i.value for i in v)
+    name = f"gemm_tl_kernel<{wtype}, {nt}," if tl else f"gemm_kernel<{wtype}, {nt}, {btn}, {maxt},"
+    return {"tile_loop": bool(tl), "nt": nt, "btn": btn, "maxt": maxt, "grid_threads": grid, "block_threads": block,
+            "kernel": name}
 
 
 # --------------------------------------------------------------------------- attention

@@ -496,12 +496,25 @@ size_t gr_gemm_workspace_size(int B, int N, int K) {
   return c.off + 256;
 }
 
-gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int pair, int* nt, int* btn, int* maxt,
-                               int* grid_threads, int* block_threads) {
-  if (!nt || !btn || !maxt || !grid_threads || !block_threads) return GR_ERR_NULL;
+gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* tile_loop, int* nt, int* btn,
+                               int* maxt, int* grid_threads, int* block_threads) {
+  if (!tile_loop || !nt || !btn || !maxt || !grid_threads || !block_threads) return GR_ERR_NULL;
   if (wtype != GR_W_Q4_K && wtype != GR_W_Q6_K) return GR_ERR_DTYPE;
-  if (rows <= 0 || K <= 0 || K % kQK || B <= 0 || B > 64) return GR_ERR_SHAPE;
+  if (rows <= 0 || K <= 0 || K % kQK || B <= 0 || B > 64 || epi < 0 || epi > 2) return GR_ERR_SHAPE;
   const int tiles = (rows + 15) / 16;
+  const bool pair = epi == 2;
+  // the choices gemm_run and gemm_swiglu make
+  if ((pair || epi == 0) && use_tile_loop(tiles, K, B)) {
+    const TlPlan tp = plan_gemm_tl(wtype, pair ? 2 : 1, tiles, K);
+    *tile_loop = 1;
+    *nt = pair ? 2 : 1;
+    *btn = 1;
+    *maxt = 512;
+    *grid_threads = tp.grid * tp.waves * 64;
+    *block_threads = tp.waves * 64;
+    return GR_OK;
+  }
+  *tile_loop = 0;
   const int group = gemm_group(tiles);
   const GemmPlan pl = pair ? plan_gemm(wtype, tiles, K, B, 2)
                            : plan_gemm(wtype, (tiles + group - 1) / group, K, B, group);

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GR_ABI_VERSION 1
+#define GR_ABI_VERSION 2
 
 typedef enum {
   GR_OK = 0,
@@ -99,13 +99,16 @@ gr_status gr_q6k_gemm(const void* wblocks, const float* x, float* y, int B, int 
 /* Launch shape of one fused-dequant GEMM launch (a profiling aid: it names the
  * dispatch a counter or trace row belongs to).  rows: output rows of the launch (for
  * several matrices sharing one launch, the sum of each one's rows rounded up to 16;
- * for a gate/up pair, pair = 1 and rows = F).  Returns the kernel's template
- * parameters (16-row tiles per workgroup nt, 8-row batch tiles btn, launch bound
- * maxt) and the grid and workgroup sizes in threads, as launched by every entry point
- * above for these sizes.  GR_ERR_NULL for a null output pointer, GR_ERR_DTYPE for an
- * unknown type, GR_ERR_SHAPE for rows, K or B out of range. */
-gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int pair, int* nt, int* btn, int* maxt,
-                               int* grid_threads, int* block_threads);
+ * for a gate/up pair, rows = F).  epi: 0 plain store, 1 residual update, 2 gate/up
+ * pair with SwiGLU.  Returns which kernel runs (tile_loop 0: the split-K kernel
+ * gemm_kernel<type, nt, btn, maxt, aligned>; 1: the tile-loop kernel
+ * gemm_tl_kernel<type, nt, aligned, ring> with btn = 1 and maxt = 512), its template
+ * parameters (16-row tiles per workgroup or group nt, 8-row batch tiles btn, launch
+ * bound maxt) and the grid and workgroup sizes in threads, as launched by every entry
+ * point above for these sizes.  GR_ERR_NULL for a null output pointer, GR_ERR_DTYPE for
+ * an unknown type, GR_ERR_SHAPE for rows, K, B or epi out of range. */
+gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* tile_loop, int* nt, int* btn,
+                               int* maxt, int* grid_threads, int* block_threads);
 
 /* ------------------------------------------------------------- attention --
  * Typed attention metadata (tinyllm, Roadmap item 6). */

@@ -37,7 +37,7 @@ def test_host_side_checks_without_gpu():
     """Calls that fail a host check return their status before touching the device."""
     import continuous_quantized_decode_amd as gr
     L = gr.lib()
-    assert L.gr_abi_version() == 1
+    assert L.gr_abi_version() == 2
     assert L.gr_status_str(-6) == b"max_ctx + 1 tokens exceed the block table's pages"
     assert L.gr_kv_head_bytes(2, 128) == 16 * 128 + 16 * 4 * 2
     assert L.gr_kv_head_bytes(7, 128) == -1
@@ -58,3 +58,25 @@ def test_host_side_checks_without_gpu():
     assert L.gr_paged_decode_attn(p, p, p, p, p, p, 1, ctypes.byref(meta), p, 4096, None) == -2
     meta = gr.attn_meta(4, 2, 64, 1, 9, 8, 129)
     assert L.gr_paged_decode_attn(p, p, p, p, p, p, 1, ctypes.byref(meta), p, 4096, None) == -6
+
+
+def test_gemm_launch_shape_names_the_kernel():
+    """The launch-shape query picks the kernel the entry points launch (host-only call)."""
+    import continuous_quantized_decode_amd as gr
+    q4, q6 = 12, 14
+    # Llama-3-8B shapes at B = 8: the output head and the gate/up pairs run the tile loop
+    head = gr.gr_gemm_launch_shape(q6, 128256, 4096, 8, gr.GEMM_EPI_STORE)
+    assert head["tile_loop"] and head["nt"] == 1 and head["kernel"] == "gemm_tl_kernel<14, 1,"
+    gu = gr.gr_gemm_launch_shape(q4, 14336, 4096, 8, gr.GEMM_EPI_SWIGLU)
+    assert gu["tile_loop"] and gu["nt"] == 2 and gu["block_threads"] == 8 * 64
+    # residual updates and small matrices keep the split-K kernel
+    down = gr.gr_gemm_launch_shape(q6, 4096, 14336, 8, gr.GEMM_EPI_RESIDUAL)
+    assert not down["tile_loop"] and down["kernel"].startswith("gemm_kernel<14, 1, 1,")
+    assert not gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_RESIDUAL)["tile_loop"]
+    assert gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_STORE)["tile_loop"]
+    # more than one batch tile, or K above 16 super-blocks: split-K
+    assert not gr.gr_gemm_launch_shape(q6, 128256, 4096, 9, gr.GEMM_EPI_STORE)["tile_loop"]
+    assert not gr.gr_gemm_launch_shape(q6, 128256, 4352, 8, gr.GEMM_EPI_STORE)["tile_loop"]
+    L = gr.lib()
+    out = [ctypes.c_int() for _ in range(6)]
+    assert L.gr_gemm_launch_shape(q4, 64, 256, 1, 3, *[ctypes.byref(o) for o in out]) == -2
