@@ -117,7 +117,8 @@ GR_DEV void store_token(const float* vals, uint8_t* stage, uint8_t* dst_head, bo
 
 // ------------------------------------------------------------------- the kernel
 
-// Three waves per SIMD (registers <= 168) for the 16-bit and 8-bit pools; f32 pages need more.
+// Three waves per SIMD (registers <= 168) with a chunk of pages in flight: two f16 pages
+// or four q8_0 pages; f32 pages (two in flight) need more registers.
 template <int KVDT, int D, bool FUSED>
 __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kernel(AttnParams p) {
   constexpr int NS = D / 32;  // QK slices
@@ -200,9 +201,17 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
     const size_t pg = page_id(j);
     load_page<KVDT, D>(r, kbase + pg * page_bytes, vbase + pg * page_bytes, lane);
   };
-  // the first two pages are in flight during the setup below
-  PageRegs<KVDT, D> r0, r1;
-  load(r0, pg0);
+  // Pages go in chunks of NP, all of a chunk's loads in flight at once (as many as the
+  // registers of three waves per SIMD allow); the first chunk is in flight during the
+  // setup below.
+  constexpr int NP = KVDT == KV_Q8_T ? 4 : 2;
+  PageRegs<KVDT, D> r[NP];
+  auto issue_chunk = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      if (c0 + i < pg1) load(r[i], c0 + i);
+  };
+  issue_chunk(pg0);
 
   // ---- QK-norm and RoPE (rotation in fp64) of the head vectors, to LDS -------------
   {
@@ -369,8 +378,13 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
     __syncthreads();
   };
 
-  // Two-buffer pipeline over the split's pages (the first two already in flight).
-  pipeline2_loaded(pg0, pg1, r0, r1, load, [&](PageRegs<KVDT, D>& cur, int j, bool) { page(cur, j); });
+  // The split's pages, chunk by chunk (the first chunk already in flight).
+  for (int c0 = pg0; c0 < pg1; c0 += NP) {
+    if (c0 != pg0) issue_chunk(c0);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      if (c0 + i < pg1) page(r[i], c0 + i);
+  }
 
   // ---- partial results -------------------------------------------------------------
   if (2 * kg < R) {
