@@ -93,6 +93,12 @@ def _declare(L: C.CDLL) -> None:
     L.orc_decode_layer.restype = _i
     L.orc_output_head.argtypes = [_p, _p, _d, _p, _i, _p, _i, _i, _i]
     L.orc_output_head.restype = _i
+    L.orc_exp_neg.argtypes = [_d]
+    L.orc_exp_neg.restype = _d
+    L.orc_sample_weight.argtypes = [_d]
+    L.orc_sample_weight.restype = C.c_uint32
+    L.orc_sample.argtypes = [_p, _i, _i, _p, _p, _p, _p, _p, _p, _p]
+    L.orc_sample.restype = _i
 
 
 def num_threads() -> int:
@@ -282,6 +288,35 @@ def output_head(x: np.ndarray, norm: np.ndarray, eps: float, w: np.ndarray, wtyp
     if rc:
         raise ValueError("oracle output_head rejected its arguments")
     return out
+
+
+def exp_neg(d: float) -> float:
+    """e^d for -22 <= d <= 0 as the sampler evaluates it (fp64)."""
+    return float(lib().orc_exp_neg(float(d)))
+
+
+def sample_weight(d: float) -> int:
+    """Fixed-point weight floor(2^31 e^d) of a scaled logit difference d (0 below -22 or for NaN)."""
+    return int(lib().orc_sample_weight(float(d)))
+
+
+def sample(logits: np.ndarray, temperature, top_p, top_k, u, diag: bool = False):
+    """One token per row of float32 logits [B, vocab]; per-row temperature, top_p, top_k, uniform u.
+
+    With diag=True also returns (Wk, Wp): the kept weight after the top-k and the top-p cuts."""
+    lg = _c(np.atleast_2d(logits), np.float32)
+    bsz, vocab = lg.shape
+    t = _c(np.broadcast_to(np.asarray(temperature, dtype=np.float64), (bsz,)), np.float64)
+    p = _c(np.broadcast_to(np.asarray(top_p, dtype=np.float64), (bsz,)), np.float64)
+    k = _c(np.broadcast_to(np.asarray(top_k, dtype=np.int32), (bsz,)), np.int32)
+    uu = _c(np.broadcast_to(np.asarray(u, dtype=np.float64), (bsz,)), np.float64)
+    tok = np.empty(bsz, dtype=np.int32)
+    wk = np.empty(bsz, dtype=np.uint64)
+    wp = np.empty(bsz, dtype=np.uint64)
+    rc = lib().orc_sample(_ptr(lg), bsz, vocab, _ptr(t), _ptr(p), _ptr(k), _ptr(uu), _ptr(tok), _ptr(wk), _ptr(wp))
+    if rc:
+        raise ValueError("oracle sample rejected its arguments")
+    return (tok, wk, wp) if diag else tok
 
 
 def decode_stack(workload, layers: Sequence, k_pools: Sequence[np.ndarray], v_pools: Sequence[np.ndarray],

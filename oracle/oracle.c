@@ -16,6 +16,9 @@
  *     logical pages (Known limitations), 16-token pages.
  *   - LeatEngine, Run: the q8_0 cache as llama.cpp keeps it (32-element blocks with
  *     an fp16 scale).
+ *   - Leone, "What ships": greedy and stochastic sampling (temperature, top-k, top-p)
+ *     after the output head, with fixed-point weights so every decision is an
+ *     integer one (the readings sit with orc_sample below).
  * The byte layouts of Q4_K, Q6_K and q8_0 are not printed on the pages; they are
  * the public GGUF block formats.  Everything runs in fp64 on exactly decoded
  * inputs, with contiguous (gathered) K/V and one softmax over the whole context.
@@ -538,3 +541,120 @@ int orc_output_head(const double* x, const float* norm, double eps, const uint8_
 
 /* Threads the parallel loops above use (bookkeeping for timing reports; no arithmetic). */
 int orc_num_threads(void) { return omp_get_max_threads(); }
+
+/* ---------------------------------------------------------------------------------------------
+ * Sampling after the output head (Leone, "What ships": greedy and stochastic sampling with an
+ * FP64 CPU oracle).  The pages name the feature and nothing of its arithmetic; the readings
+ * taken here make every decision an integer one:
+ *   - order: logits sorted by value, largest first, equal values by index ascending; NaN sorts
+ *     last and -0 equals +0;
+ *   - greedy (temperature <= 0 or NaN, 1/temperature not finite, top_k == 1, or a largest logit
+ *     that is not finite): the first element of the order;
+ *   - weight of element i: W_i = floor(2^31 e^d) with d = (l_i - l_max) * (1/T) in fp64, and
+ *     W_i = 0 when d < -22 or d is NaN (e^-22 < 2^-31, so the floor is 0 there anyway);
+ *   - top_k = k in [2, vocab): the first k elements of the order are kept, Wk their weight sum;
+ *     otherwise Wk is the sum over the whole row;
+ *   - top_p = p < 1: P = ceil(p Wk) clamped to [1, Wk]; the kept prefix ends at the first element
+ *     whose running weight reaches P, Wp that running weight; otherwise Wp = Wk;
+ *   - draw: U = floor(u Wp) clamped to [0, Wp - 1] for the caller's uniform u in [0, 1); the token
+ *     is the first element of the order whose running weight exceeds U.
+ * ------------------------------------------------------------------------------------------- */
+
+/* e^d for -22 <= d <= 0 in fp64.  Cody and Waite's reduction d = k ln2 + r, k = rint(d / ln2),
+ * with ln2 split into a high part whose low bits are zero (so k ln2_hi is exact) and a low part
+ * (the fdlibm split); e^r from the Taylor series of the exponential to degree 13 in Horner form,
+ * one fused multiply-add per step; then e^d = 2^k e^r. */
+double orc_exp_neg(double d) {
+  static const double ln2_hi = 0x1.62e42fee00000p-1, ln2_lo = 0x1.a39ef35793c76p-33;
+  static const double inv_ln2 = 0x1.71547652b82fep+0;
+  double c[14], f = 1.0;
+  c[0] = 1.0;
+  for (int n = 1; n <= 13; ++n) {
+    f *= n; /* n! is exact in fp64 up to 22! */
+    c[n] = 1.0 / f;
+  }
+  const double k = rint(d * inv_ln2);
+  double r = fma(-k, ln2_hi, d);
+  r = fma(-k, ln2_lo, r);
+  double p = c[13];
+  for (int n = 12; n >= 0; --n) p = fma(p, r, c[n]);
+  return ldexp(p, (int)k);
+}
+
+/* Fixed-point weight of an element whose scaled logit difference is d. */
+uint32_t orc_sample_weight(double d) {
+  if (!(d >= -22.0)) return 0;
+  return (uint32_t)floor(ldexp(orc_exp_neg(d), 31));
+}
+
+typedef struct {
+  double l;
+  int i, nan;
+} OrcRank;
+
+static int orc_rank_cmp(const void* a, const void* b) {
+  const OrcRank* x = (const OrcRank*)a;
+  const OrcRank* y = (const OrcRank*)b;
+  if (x->nan != y->nan) return x->nan ? 1 : -1;
+  if (!x->nan && x->l != y->l) return x->l > y->l ? -1 : 1;
+  return (x->i > y->i) - (x->i < y->i);
+}
+
+/* One token per row.  temperature, top_p, u: B doubles; top_k: B ints.  wk_out and wp_out (may
+ * be NULL) receive Wk and Wp (0 for a greedy row). */
+int orc_sample(const float* logits, int B, int vocab, const double* temperature, const double* top_p,
+               const int* top_k, const double* u, int32_t* tokens, uint64_t* wk_out, uint64_t* wp_out) {
+  if (B < 0 || vocab < 1) return -1;
+  OrcRank* e = (OrcRank*)malloc(sizeof(OrcRank) * (size_t)vocab);
+  uint32_t* w = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)vocab);
+  for (int b = 0; b < B; ++b) {
+    const float* row = logits + (size_t)b * vocab;
+    for (int i = 0; i < vocab; ++i) {
+      e[i].l = (double)row[i];
+      e[i].i = i;
+      e[i].nan = isnan(row[i]) ? 1 : 0;
+    }
+    qsort(e, (size_t)vocab, sizeof(OrcRank), orc_rank_cmp);
+    const double T = temperature[b], inv_t = 1.0 / T, lmax = e[0].l;
+    if (wk_out) wk_out[b] = 0;
+    if (wp_out) wp_out[b] = 0;
+    if (!(T > 0.0) || !isfinite(inv_t) || top_k[b] == 1 || e[0].nan || !isfinite(lmax)) {
+      tokens[b] = e[0].i;
+      continue;
+    }
+    for (int j = 0; j < vocab; ++j) w[j] = orc_sample_weight((e[j].l - lmax) * inv_t);
+    const int kk = (top_k[b] <= 0 || top_k[b] >= vocab) ? vocab : top_k[b];
+    uint64_t wk = 0;
+    for (int j = 0; j < kk; ++j) wk += w[j];
+    uint64_t wp = wk;
+    if (top_p[b] < 1.0) {
+      const double pd = ceil(top_p[b] * (double)wk);
+      const uint64_t P = !(pd > 1.0) ? 1 : (pd >= (double)wk ? wk : (uint64_t)pd);
+      uint64_t cum = 0;
+      for (int j = 0; j < vocab; ++j) {
+        cum += w[j];
+        if (cum >= P) {
+          wp = cum;
+          break;
+        }
+      }
+    }
+    const double x = floor(u[b] * (double)wp);
+    const uint64_t U = x >= (double)wp ? wp - 1 : (x > 0.0 ? (uint64_t)x : 0);
+    uint64_t cum = 0;
+    int tok = e[0].i;
+    for (int j = 0; j < vocab; ++j) {
+      cum += w[j];
+      if (cum > U) {
+        tok = e[j].i;
+        break;
+      }
+    }
+    tokens[b] = tok;
+    if (wk_out) wk_out[b] = wk;
+    if (wp_out) wp_out[b] = wp;
+  }
+  free(e);
+  free(w);
+  return 0;
+}
