@@ -101,7 +101,11 @@ def _load() -> C.CDLL:
     L.gr_decode_stack.restype = _i
     L.gr_decode_stack_probed.argtypes = list(L.gr_decode_stack.argtypes) + [_i, _i, C.POINTER(_p), C.POINTER(_p)]
     L.gr_decode_stack_probed.restype = _i
-    if L.gr_abi_version() != 2:
+    L.gr_sample_workspace_size.argtypes = [_i, _i]
+    L.gr_sample_workspace_size.restype = _sz
+    L.gr_sample.argtypes = [_p, _i, _i, _p, _p, _p, _p, _sz, _p]
+    L.gr_sample.restype = _i
+    if L.gr_abi_version() != 3:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
     return L
@@ -116,7 +120,8 @@ EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_
             "gr_q6k_gemm",
             "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_paged_gather_kv",
             "gr_decode_layer_workspace_size", "gr_decode_layer", "gr_output_head_workspace_size", "gr_output_head",
-            "gr_decode_stack_workspace_size", "gr_decode_stack", "gr_decode_stack_probed")
+            "gr_decode_stack_workspace_size", "gr_decode_stack", "gr_decode_stack_probed", "gr_sample_workspace_size",
+            "gr_sample")
 
 # gr_stage values
 STAGES = ("pack", "qkv", "attn", "attn_merge", "wo", "gate_up", "down", "head")
@@ -292,6 +297,45 @@ def gr_output_head(x, norm, eps: float, w, wtype: int, vocab: int, logits=None, 
     _check("gr_output_head", _load().gr_output_head(_ptr(x), _ptr(norm), float(eps), _ptr(w), wtype, _ptr(logits), b,
                                                     h, vocab, _ptr(ws), ws.numel(), _stream()))
     return logits
+
+
+# --------------------------------------------------------------------------- sampling
+
+SAMPLE_PARAMS_DTYPE = [("temperature", "<f8"), ("top_p", "<f8"), ("u", "<f8"), ("top_k", "<i4"), ("reserved", "<i4")]
+
+
+def sample_params(temperature, top_p, top_k, u, b: Optional[int] = None, device=None):
+    """Device array of gr_sample_params (32 bytes per row) from per-row values or scalars."""
+    import numpy as np
+    torch = _torch()
+    cols = [np.atleast_1d(np.asarray(v)) for v in (temperature, top_p, top_k, u)]
+    n = b if b is not None else max(len(c) for c in cols)
+    a = np.zeros(n, dtype=SAMPLE_PARAMS_DTYPE)
+    a["temperature"] = np.broadcast_to(cols[0], (n,))
+    a["top_p"] = np.broadcast_to(cols[1], (n,))
+    a["top_k"] = np.broadcast_to(cols[2], (n,))
+    a["u"] = np.broadcast_to(cols[3], (n,))
+    raw = torch.from_numpy(a.view(np.uint8).copy())
+    return raw.to(device or "cuda")
+
+
+def sample_workspace_size(b: int, vocab: int) -> int:
+    return int(_load().gr_sample_workspace_size(b, vocab))
+
+
+def gr_sample(logits, params, tokens=None, kept=None, ws=None):
+    """tokens int32 [B] from f32 logits [B, vocab]; kept (optional int64 [B, 2]) receives (Wk, Wp)."""
+    torch = _torch()
+    b, vocab = logits.shape
+    if params.numel() != 32 * b:
+        raise ValueError("params must hold one 32-byte gr_sample_params per row")
+    if tokens is None:
+        tokens = torch.empty(b, dtype=torch.int32, device=logits.device)
+    if ws is None:
+        ws = workspace(sample_workspace_size(b, vocab), logits.device)
+    _check("gr_sample", _load().gr_sample(_ptr(logits), b, vocab, _ptr(params), _ptr(tokens), _ptr(kept), _ptr(ws),
+                                          ws.numel(), _stream()))
+    return tokens
 
 
 def decode_stack_workspace_size(cfg: LayerCfg, b: int, max_ctx: int, vocab: int) -> int:

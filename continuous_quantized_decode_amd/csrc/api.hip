@@ -17,6 +17,10 @@ thread_local ProbeEvents* probe_events = nullptr;
 
 
 hipError_t launch_dequant(int kind, const void* blocks, int64_t n, float* out, hipStream_t st);
+size_t sample_workspace_bytes(int B, int vocab);
+int sample_max_vocab();
+hipError_t launch_sample(const float* logits, int B, int vocab, const gr_sample_params* params, int32_t* tokens,
+                         uint64_t* kept, void* ws, hipStream_t st);
 hipError_t launch_gather(int kv_dtype, int D, const void* pool, int is_v, const int32_t* bt, const int32_t* ctx,
                          int B, int max_blocks, int n_kv_heads, int max_ctx, float* out, hipStream_t st);
 
@@ -709,6 +713,24 @@ gr_status gr_output_head(const float* x, const float* norm, float eps, const voi
   s = run_input_pack(x, B, hidden, norm, k, xp, ss, st, nullptr);
   if (s != GR_OK) return s;
   return run_head(w, wtype, logits, B, hidden, vocab, eps, xp, ss, st, nullptr);
+}
+
+size_t gr_sample_workspace_size(int B, int vocab) {
+  if (B <= 0 || vocab <= 0 || vocab > sample_max_vocab() || B > 65535) return 0;
+  return sample_workspace_bytes(B, vocab) + 256;
+}
+
+gr_status gr_sample(const float* logits, int B, int vocab, const gr_sample_params* params, int32_t* tokens,
+                    uint64_t* kept_weight, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || vocab < 1 || vocab > sample_max_vocab() || B > 65535) return GR_ERR_SHAPE;
+  if (B == 0) return GR_OK;
+  if (!logits || !params || !tokens) return GR_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(params, 8) || !aligned(tokens, 4) || !aligned(kept_weight, 8))
+    return GR_ERR_ALIGN;
+  if (!ws || ws_bytes < gr_sample_workspace_size(B, vocab) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
+  gr_status s = check_device();
+  if (s != GR_OK) return s;
+  return check_launch(launch_sample(logits, B, vocab, params, tokens, kept_weight, ws, (hipStream_t)stream));
 }
 
 size_t gr_decode_stack_workspace_size(const gr_layer_cfg* c, int B, int max_ctx, int vocab) {

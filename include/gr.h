@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GR_ABI_VERSION 2
+#define GR_ABI_VERSION 3
 
 typedef enum {
   GR_OK = 0,
@@ -180,6 +180,40 @@ gr_status gr_decode_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void
 size_t gr_output_head_workspace_size(int B, int hidden, int vocab);
 gr_status gr_output_head(const float* x, const float* norm, float eps, const void* w, int wtype, float* logits,
                          int B, int hidden, int vocab, void* workspace, size_t ws_bytes, void* stream);
+
+/* Token sampling after the output head (Leone, "What ships": greedy and stochastic
+ * sampling).  The pages fix no formula; this call defines one in which every decision is
+ * an integer one, so a result is reproducible bit for bit:
+ *  - order: a row's logits by value, largest first, equal values by index ascending;
+ *    NaN sorts last and -0 equals +0;
+ *  - greedy rows (temperature <= 0 or NaN, 1/temperature not finite, top_k == 1, or a
+ *    largest logit that is not finite) take the first element of the order;
+ *  - otherwise element i weighs W_i = floor(2^31 e^d), d = (l_i - l_max) * (1/temperature)
+ *    in fp64 (W_i = 0 for d < -22 or NaN), e^d evaluated by Cody-Waite reduction and a
+ *    degree-13 Taylor polynomial with fused multiply-adds;
+ *  - top_k = k with 1 < k < vocab: Wk = running weight of the k-th element of the order,
+ *    else the row's total weight;
+ *  - top_p = p < 1: P = ceil(p * Wk) (fp64 product) clamped to [1, Wk]; Wp = running
+ *    weight of the first element whose running weight reaches P, else Wp = Wk;
+ *  - draw: U = floor(u * Wp) clamped to [0, Wp - 1]; the token is the first element of
+ *    the order whose running weight exceeds U.
+ * params: device array [B] of gr_sample_params (8-byte aligned).  u is the caller's
+ * uniform random number for the row (a seeded generator of the caller's choice).
+ * logits: f32 [B][vocab], 1 <= vocab <= 262144.  tokens: int32 [B].  kept_weight: NULL
+ * or uint64 [B][2] receiving (Wk, Wp), (0, 0) for greedy rows.  The workspace holds
+ * per-row weights and histograms; the call issues three kernels and no host
+ * synchronization (capturable in a HIP graph).  B > 65535 is GR_ERR_SHAPE. */
+typedef struct {
+  double temperature;
+  double top_p;
+  double u;
+  int32_t top_k;
+  int32_t reserved;
+} gr_sample_params;
+
+size_t gr_sample_workspace_size(int B, int vocab);
+gr_status gr_sample(const float* logits, int B, int vocab, const gr_sample_params* params, int32_t* tokens,
+                    uint64_t* kept_weight, void* workspace, size_t ws_bytes, void* stream);
 
 /* Whole decode step: n_layers layers in order (layer l uses weights[l], k_pages[l],
  * v_pages[l]; host arrays of device pointers), then, when head_w is not NULL, the

@@ -426,3 +426,21 @@ def kv_state(w: Workload, ctx: np.ndarray, n_layers: Optional[int] = None, extra
 def attn_query(rng: np.random.Generator, b: int, hq: int, d: int) -> np.ndarray:
     """Standalone attention query ~ N(0,1) (scores of std ~1 at D=128 after 1/sqrt(D))."""
     return rng.standard_normal((b, hq, d), dtype=np.float32)
+
+
+def sample_logits(rng: np.random.Generator, b: int, vocab: int, sigma: float = 2.5, spikes: int = 8,
+                  spike_lo: float = 4.0, spike_hi: float = 12.0) -> np.ndarray:
+    """Logits for the sampler: N(0, sigma) over the vocabulary plus `spikes` tokens per row
+    lifted by U(spike_lo, spike_hi) (a few likely tokens above a broad tail, the shape of a
+    language model's next-token logits).  float32 [b, vocab]."""
+    x = rng.normal(0.0, sigma, (b, vocab)).astype(np.float32)
+    for r in range(b):
+        if spikes:
+            idx = rng.choice(vocab, min(spikes, vocab), replace=False)
+            x[r, idx] += rng.uniform(spike_lo, spike_hi, len(idx)).astype(np.float32)
+    return x
+
+
+def sample_uniforms(rng: np.random.Generator, b: int) -> np.ndarray:
+    """The per-row uniform draws in [0, 1) the sampler consumes (float64)."""
+    return rng.random(b)

@@ -37,7 +37,7 @@ def test_host_side_checks_without_gpu():
     """Calls that fail a host check return their status before touching the device."""
     import continuous_quantized_decode_amd as gr
     L = gr.lib()
-    assert L.gr_abi_version() == 2
+    assert L.gr_abi_version() == 3
     assert L.gr_status_str(-6) == b"max_ctx + 1 tokens exceed the block table's pages"
     assert L.gr_kv_head_bytes(2, 128) == 16 * 128 + 16 * 4 * 2
     assert L.gr_kv_head_bytes(7, 128) == -1
@@ -80,3 +80,22 @@ def test_gemm_launch_shape_names_the_kernel():
     L = gr.lib()
     out = [ctypes.c_int() for _ in range(6)]
     assert L.gr_gemm_launch_shape(q4, 64, 256, 1, 3, *[ctypes.byref(o) for o in out]) == -2
+
+
+def test_sample_host_checks_without_gpu():
+    import continuous_quantized_decode_amd as gr
+    L = gr.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.addressof(buf) + (-ctypes.addressof(buf) % 256)
+    big = 1 << 30
+    assert L.gr_sample(None, 0, 10, None, None, None, None, 0, None) == 0
+    assert L.gr_sample(p, 1, 0, p, p, None, p, big, None) == -2
+    assert L.gr_sample(p, 1, (1 << 18) + 1, p, p, None, p, big, None) == -2
+    assert L.gr_sample(p, 65536, 10, p, p, None, p, big, None) == -2
+    assert L.gr_sample(None, 1, 10, p, p, None, p, big, None) == -1
+    assert L.gr_sample(p, 1, 10, p + 4, p, None, p, big, None) == -4
+    assert L.gr_sample(p, 1, 10, p, p, p + 4, p, big, None) == -4
+    assert L.gr_sample(p, 1, 10, p, p, None, p, 64, None) == -5
+    assert L.gr_sample(p, 1, 10, p, p, None, p + 8, big, None) == -5
+    assert L.gr_sample_workspace_size(8, 128256) > 8 * 4096 * 12 > 0
+    assert L.gr_sample_workspace_size(8, (1 << 18) + 1) == 0
