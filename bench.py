@@ -163,6 +163,64 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, launches: dic
     return res
 
 
+SAMPLING_CASES = {  # name: (temperature, top_p, top_k)
+    "greedy": (0.0, 1.0, 0),
+    "t0.6_p0.9": (0.6, 0.9, 0),
+    "t0.7_k50_p0.9": (0.7, 0.9, 50),
+    "t1.0": (1.0, 1.0, 0),
+}
+
+
+def measure_sampling(gr, torch, wl, reps: int = 200) -> dict:
+    """gr_sample on language-model-shaped synthetic logits of the workload's batch and
+    vocabulary: per-call time (events on the launch stream, eager launches and one-graph
+    replays) for a few parameter sets, and the logits read as the algorithmic bytes."""
+    import numpy as np
+    import synth
+    rng = np.random.default_rng(4242)
+    b, v = wl.batch, wl.vocab
+    lg = torch.from_numpy(synth.sample_logits(rng, b, v)).cuda()
+    ws = gr.workspace(gr.sample_workspace_size(b, v))
+    tok = torch.empty(b, dtype=torch.int32, device="cuda")
+    algo_bytes = b * v * 4
+    out = {"logits": f"synth.sample_logits: N(0, 2.5) plus 8 tokens per row lifted by U(4, 12); B={b}, vocab={v}",
+           "bytes_per_call": algo_bytes, "cases": {}}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, (t, p, k) in SAMPLING_CASES.items():
+        prm = gr.sample_params(t, p, k, synth.sample_uniforms(rng, b), b=b)
+        for _ in range(5):
+            gr.gr_sample(lg, prm, tokens=tok, ws=ws)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            gr.gr_sample(lg, prm, tokens=tok, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) / reps * 1e3
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            gr.gr_sample(lg, prm, tokens=tok, ws=ws)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            gr.gr_sample(lg, prm, tokens=tok, ws=ws)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) / reps * 1e3
+        best = min(eager_us, graph_us)
+        out["cases"][name] = {"eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
+                              "rows_per_s": round(b / (best * 1e-6), 1),
+                              "gbs": round(algo_bytes / (best * 1e-6) / 1e9, 1)}
+    return out
+
+
 def stage_launches(gr, wl) -> dict:
     """stage -> (kernel name as the profilers print it, grid size in threads or None)."""
     B, H, F = wl.batch, wl.hidden, wl.ffn
@@ -188,6 +246,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sampling", action="store_true", help="skip the sampler measurement")
+    ap.add_argument("--sampling-only", action="store_true",
+                    help="measure only the sampler (prints its JSON object; for profiling runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
                     help="also run the counter-calibration copy (torch.neg over BYTES of float32)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -221,6 +282,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
+    if args.sampling_only:
+        print(json.dumps(measure_sampling(gr, torch, wl)), flush=True)
+        return
 
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -342,6 +406,11 @@ def main():
                 "bytes_per_launch": d["bytes_per_launch"], "avg_launch_us": d["avg_us"]}
     log("[bench] stages: " + json.dumps(stages))
 
+    sampling = None
+    if wl.vocab and not args.no_sampling:
+        sampling = measure_sampling(gr, torch, wl)
+        log("[bench] sampling: " + json.dumps(sampling["cases"]))
+
     # ---- CPU baseline: the fp64 oracle on one whole step of the same workload (every
     #      layer and the output head), when that is bounded; else on its first layers
     cpu = None
@@ -400,6 +469,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
+        "sampling": sampling,
     }
     print(json.dumps(out), flush=True)
 

@@ -48,6 +48,7 @@ constexpr int kHistChunk = 4096;  // elements per workgroup of the histogram ker
 constexpr int kHistThreads = 512;
 constexpr int kWideThreads = 256;
 constexpr int kSeg = 256;         // elements per segment: one wave of the histogram kernel, 4 per lane
+constexpr int kSegTop = 4;        // largest composites each segment records
 constexpr int kBins1 = 4096;      // level 1: top 12 bits of the order key
 constexpr int kSelThreads = 512;
 constexpr int kCap = 8192;        // elements a select can hold in LDS
@@ -60,7 +61,7 @@ struct SampleWs {
   uint64_t* cmax;  // [B][nch]  packed (key, 2^32-1 - index) chunk maxima
   uint32_t* hcnt;  // [B][kBins1]
   uint64_t* hsum;  // [B][kBins1]
-  uint64_t* segtop;  // [B][nseg] largest composite of each 256-element segment
+  uint64_t* segtop;  // [B][nseg][kSegTop] largest composites of each 256-element segment, descending
   uint32_t* segsec;  // [B][nseg] largest key of the segment's other elements (0 if none)
 };
 
@@ -240,34 +241,49 @@ __global__ __launch_bounds__(kHistThreads) void sample_hist_kernel(const float* 
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
     const int i0 = c * kHistChunk + j * 4 * kHistThreads + 4 * t;
-    uint64_t best = 0ull;  // the lane's largest composite
-    uint32_t second = 0u;  // the largest key among the lane's other elements
+    uint64_t cq[4];  // the lane's composites, 0 for positions past the row
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      cq[q] = 0ull;
       if (i0 + q < vocab) {
         const float l = elem(v[j], q);
         const uint32_t key = order_key(l);
         const uint32_t w = weight_of(l, h);
         atomicAdd((unsigned long long*)&s_bin[key >> 20], (1ull << 44) | (unsigned long long)w);
-        const uint64_t cq = composite(key, (uint32_t)(i0 + q));
-        if (cq > best) {
-          const uint32_t prev = (uint32_t)(best >> kIdxBits);
-          second = prev > second ? prev : second;
-          best = cq;
-        } else {
-          second = key > second ? key : second;
-        }
+        cq[q] = composite(key, (uint32_t)(i0 + q));
       }
     }
-    // wave wv covers the 256 consecutive elements of one segment: its top composite, and the
-    // largest key of the rest (the winner's lane offers its own second, the others their best)
-    const uint64_t top = wave_max_dpp(best);
-    const uint32_t offer = best == top ? second : (uint32_t)(best >> kIdxBits);
-    const uint32_t sec = (uint32_t)wave_max_dpp((uint64_t)offer);
-    const int seg = (c * kHistChunk + j * 4 * kHistThreads) / kSeg + wv;
-    if (lane == 0 && seg < nseg) {
-      ws.segtop[(size_t)b * nseg + seg] = top;
-      ws.segsec[(size_t)b * nseg + seg] = sec;
+    // wave wv covers the 256 consecutive elements of one segment: its kSegTop largest
+    // composites (each round the lane holding the winner moves to its next), then the largest
+    // key of the rest
+    auto cx = [](uint64_t& a, uint64_t& b2) {
+      const uint64_t hi = a > b2 ? a : b2, lo = a > b2 ? b2 : a;
+      a = hi;
+      b2 = lo;
+    };
+    cx(cq[0], cq[1]);
+    cx(cq[2], cq[3]);
+    cx(cq[0], cq[2]);
+    cx(cq[1], cq[3]);
+    cx(cq[1], cq[2]);
+    int head = 0;
+    uint64_t tops[kSegTop];
+#pragma unroll
+    for (int r = 0; r <= kSegTop; ++r) {
+      const uint64_t cur = head == 0 ? cq[0] : head == 1 ? cq[1] : head == 2 ? cq[2] : head == 3 ? cq[3] : 0ull;
+      const uint64_t m = wave_max_dpp(cur);
+      if (r < kSegTop) {
+        tops[r] = m;
+        if (m != 0ull && cur == m) ++head;
+      } else {
+        const int seg = (c * kHistChunk + j * 4 * kHistThreads) / kSeg + wv;
+        if (lane == 0 && seg < nseg) {
+          ulonglong2* dst = (ulonglong2*)(ws.segtop + ((size_t)b * nseg + seg) * kSegTop);
+          dst[0] = make_ulonglong2(tops[0], tops[1]);
+          dst[1] = make_ulonglong2(tops[2], tops[3]);
+          ws.segsec[(size_t)b * nseg + seg] = (uint32_t)(m >> kIdxBits);
+        }
+      }
     }
   }
   __syncthreads();
@@ -383,7 +399,7 @@ __device__ inline void list_weights(SelShared& s, const RowHead& h) {
 // Per-thread copy of the segment summaries (segments t and t + kSelThreads).
 static_assert(kMaxSegs <= 2 * kSelThreads, "two segment summaries per select thread");
 struct SegSummary {
-  uint64_t top[2];
+  uint64_t top[2][kSegTop];
   uint32_t sec[2];
 };
 
@@ -398,24 +414,31 @@ __device__ void gather_top(SelShared& s, const float* row, int vocab, const SegS
     s.n_segs = 0u;
   }
   __syncthreads();
-  uint32_t direct = 0u;  // bit k: segment t + k * kSelThreads contributes its top element alone
+  // a segment whose key below its recorded top ones misses the bin gives those of its top
+  // ones that reach it; the others that reach it are read
+  int nd[2] = {0, 0};
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int seg = t + k * kSelThreads;
-    if (seg < nseg && (int)(sum.top[k] >> (kIdxBits + 20)) >= b_low) {
-      if ((int)(sum.sec[k] >> 20) < b_low)
-        direct |= 1u << k;
-      else
+    if (seg < nseg && (int)(sum.top[k][0] >> (kIdxBits + 20)) >= b_low) {
+      if ((int)(sum.sec[k] >> 20) < b_low) {
+        const int valid = min(kSegTop, vocab - seg * kSeg);
+#pragma unroll
+        for (int r = 0; r < kSegTop; ++r) nd[k] += (r < valid && (int)(sum.top[k][r] >> (kIdxBits + 20)) >= b_low) ? 1 : 0;
+      } else {
         s.segs[atomicAdd(&s.n_segs, 1u)] = (uint16_t)seg;
+      }
     }
   }
-  uint32_t slot = wave_reserve(s, (uint32_t)__popc(direct));
+  uint32_t slot = wave_reserve(s, (uint32_t)(nd[0] + nd[1]));
 #pragma unroll
   for (int k = 0; k < 2; ++k)
-    if ((direct >> k) & 1u) {
-      if (slot < (uint32_t)kCap) s.lc[slot] = sum.top[k];
-      ++slot;
-    }
+#pragma unroll
+    for (int r = 0; r < kSegTop; ++r)
+      if (r < nd[k]) {
+        if (slot < (uint32_t)kCap) s.lc[slot] = sum.top[k][r];
+        ++slot;
+      }
   __syncthreads();
   const int nq = (int)s.n_segs;
   constexpr int kWaves = kSelThreads / 64, kInFlight = 8;
@@ -759,8 +782,14 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const float*
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int seg = t + k * kSelThreads;
-    sum.top[k] = seg < nseg ? ws.segtop[(size_t)b * nseg + seg] : 0ull;
-    sum.sec[k] = seg < nseg ? ws.segsec[(size_t)b * nseg + seg] : 0u;
+    const bool in = seg < nseg;
+    const ulonglong2* src = (const ulonglong2*)(ws.segtop + ((size_t)b * nseg + (in ? seg : 0)) * kSegTop);
+    const ulonglong2 p0 = src[0], p1 = src[1];
+    sum.top[k][0] = in ? p0.x : 0ull;
+    sum.top[k][1] = in ? p0.y : 0ull;
+    sum.top[k][2] = in ? p1.x : 0ull;
+    sum.top[k][3] = in ? p1.y : 0ull;
+    sum.sec[k] = in ? ws.segsec[(size_t)b * nseg + seg] : 0u;
   }
   const gr_sample_params pr = params[b];
   const RowHead h = row_head(row, ws.cmax + (size_t)b * nch, nch, pr);
@@ -848,7 +877,7 @@ SampleWs carve_sample(void* base, int B, int vocab, size_t* bytes) {
   w.cmax = (uint64_t*)take((size_t)B * nch * 8);
   w.hcnt = (uint32_t*)take((size_t)B * kBins1 * 4);
   w.hsum = (uint64_t*)take((size_t)B * kBins1 * 8);
-  w.segtop = (uint64_t*)take((size_t)B * nseg * 8);
+  w.segtop = (uint64_t*)take((size_t)B * nseg * kSegTop * 8);
   w.segsec = (uint32_t*)take((size_t)B * nseg * 4);
   if (bytes) *bytes = off;
   return w;

@@ -160,3 +160,23 @@ def test_repeat_calls_reuse_the_workspace(torch, gr, orc):
         params = gr.sample_params(T, P, K, U, b=b)
         tok = host(gr.gr_sample(dev(lg, torch), params, ws=ws))
         np.testing.assert_array_equal(tok, orc.sample(lg, T, P, K, U))
+
+
+@pytest.mark.parametrize("vocab", [128256, 4099])
+def test_segments_with_few_and_many_candidates(torch, gr, orc, vocab):
+    """Each 256-element segment holds 0 to 7 elements above a gap (the gathered prefix then
+    mixes segments served from their top records with segments that must be read)."""
+    rng = np.random.default_rng(55)
+    b = 6
+    lg = rng.normal(-4.0, 0.5, (b, vocab)).astype(np.float32)
+    for r in range(b):
+        for s0 in range(0, vocab, 256):
+            m = (s0 // 256 + r) % 8
+            idx = s0 + rng.choice(min(256, vocab - s0), min(m, vocab - s0), replace=False)
+            lg[r, idx] = rng.uniform(2.0, 3.0, len(idx)).astype(np.float32)
+    n_hi = int((lg[0] > 0).sum())
+    T = np.array([0.5, 0.8, 1.0, 0.7, 1.2, 0.9])
+    P = np.array([1.0, 0.9, 1.0, 0.5, 1.0, 0.99])
+    K = np.array([n_hi, 0, n_hi // 2, 0, 0, 100], np.int32)
+    U = synth.sample_uniforms(rng, b)
+    _check(gr, torch, orc, lg, T, P, K, U, label=f"segment records v={vocab}")
