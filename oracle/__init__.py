@@ -332,3 +332,43 @@ def decode_stack(workload, layers: Sequence, k_pools: Sequence[np.ndarray], v_po
         norm, w = head
         logits = output_head(cur, norm, workload.rms_eps, w, workload.w_head, workload.vocab)
     return outs, logits
+
+
+def verify_stack(workload, layers: Sequence, k_pools: Sequence[np.ndarray], v_pools: Sequence[np.ndarray],
+                 x: np.ndarray, block_table: np.ndarray, ctx: np.ndarray, t: int, head=None):
+    """T tokens per sequence in one step (speculative verification; Leone, "What ships").
+
+    x holds B*T rows, token j of sequence b in row b*T + j at position ctx[b] + j.  Layer by
+    layer, the tokens go through decode_layer in token order, so token j's attention sees the
+    K/V that tokens 0..j-1 of the same step appended: the step equals T decode steps.  Pools
+    are modified in place.  Returns (per-layer outputs [B*T, H], logits or None)."""
+    ctx = np.asarray(ctx, dtype=np.int32)
+    bsz = len(ctx)
+    h = workload.hidden
+    cur = np.asarray(x, dtype=np.float64).reshape(bsz, t, h)
+    outs = []
+    for lw, kp, vp in zip(layers, k_pools, v_pools):
+        nxt = np.empty_like(cur)
+        for j in range(t):
+            nxt[:, j] = decode_layer(workload, lw, kp, vp, cur[:, j], block_table, ctx + j)
+        cur = nxt
+        outs.append(cur.reshape(bsz * t, h).copy())
+    logits = None
+    if head is not None:
+        norm, w = head
+        logits = output_head(cur.reshape(bsz * t, h), norm, workload.rms_eps, w, workload.w_head, workload.vocab)
+    return outs, logits
+
+
+def spec_accept(sampled: np.ndarray, draft: np.ndarray) -> np.ndarray:
+    """Accepted proposals per sequence: the leading positions j < T-1 where the target's token
+    after position j equals the step's input token j+1 (the proposal there)."""
+    sampled = np.atleast_2d(sampled)
+    draft = np.atleast_2d(draft)
+    out = np.zeros(sampled.shape[0], dtype=np.int32)
+    for b in range(sampled.shape[0]):
+        n = 0
+        while n < sampled.shape[1] - 1 and sampled[b, n] == draft[b, n + 1]:
+            n += 1
+        out[b] = n
+    return out

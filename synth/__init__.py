@@ -282,16 +282,17 @@ class PageMap:
 
 
 def page_map(rng: np.random.Generator, ctx: np.ndarray, pool_kind: str, max_ctx: Optional[int] = None,
-             extra_slot: bool = True) -> PageMap:
-    """Allocate pages for every row: ceil((ctx+1)/16) pages when the step appends a token
-    (extra_slot) else ceil(ctx/16).  "exact" pools hold exactly the needed pages in a random
-    order; "fill90" pools have ceil(needed/0.9) pages with the used ones a random subset in
-    random order (a fragmented pool)."""
-    tok = ctx.astype(np.int64) + (1 if extra_slot else 0)
+             extra_slot=True) -> PageMap:
+    """Allocate pages for every row: ceil((ctx+n)/16) pages when the step appends n tokens
+    (extra_slot: True for one, an int for several, False for none).  "exact" pools hold
+    exactly the needed pages in a random order; "fill90" pools have ceil(needed/0.9) pages
+    with the used ones a random subset in random order (a fragmented pool)."""
+    n_extra = int(extra_slot)
+    tok = ctx.astype(np.int64) + n_extra
     per_row = (tok + PAGE - 1) // PAGE
     needed = int(per_row.sum())
     mc = int(max_ctx if max_ctx is not None else int(ctx.max(initial=0)))
-    max_blocks = max(1, (mc + (1 if extra_slot else 0) + PAGE - 1) // PAGE, int(per_row.max(initial=1)))
+    max_blocks = max(1, (mc + n_extra + PAGE - 1) // PAGE, int(per_row.max(initial=1)))
     if pool_kind == "exact":
         num_pages = max(needed, 1)
         phys = rng.permutation(num_pages)[:needed]
@@ -390,14 +391,15 @@ class KVState:
     v_pools: List[np.ndarray]
 
 
-def kv_state(w: Workload, ctx: np.ndarray, n_layers: Optional[int] = None, extra_slot: bool = True,
+def kv_state(w: Workload, ctx: np.ndarray, n_layers: Optional[int] = None, extra_slot=True,
              max_ctx: Optional[int] = None, poison: bool = True, seed_key: int = 0) -> KVState:
     """Paged K/V pools for every layer plus the shared block table.
 
     Layout per pool page: for each KV head, K is token-major [16][D] and V is
     dim-major [D][16]; q8_0 heads store the int8 codes in that order followed by
     fp16 scales [16 tokens][D/32].  Unused pages and unused slots (including the
-    slot the step appends into) decode to NaN when `poison` is set.
+    slots the step appends into: one with extra_slot=True, n with an int) decode to NaN
+    when `poison` is set.
     """
     L = n_layers if n_layers is not None else w.n_layers
     rng = rng_for(w, 5, seed_key)
@@ -411,14 +413,15 @@ def kv_state(w: Workload, ctx: np.ndarray, n_layers: Optional[int] = None, extra
             pool = _fill_pool(rng_for(w, 6, seed_key, layer, int(is_v)), w.kv_dtype, pm.num_pages, hkv, d)
             if poison:
                 _poison_pages(pool, w.kv_dtype, hkv, d, np.nonzero(~used)[0])
+                n_extra = int(extra_slot)
                 for b, c in enumerate(ctx):
                     c = int(c)
-                    last = c // PAGE if extra_slot else (c - 1) // PAGE
-                    if last < 0:
-                        continue
-                    first_unused = c % PAGE if extra_slot else (c - 1) % PAGE + 1
-                    _poison_slots(pool, w.kv_dtype, is_v, hkv, d, int(pm.block_table[b, last]),
-                                  list(range(first_unused, PAGE)))
+                    # positions c .. end of the row's last page are not cached yet
+                    n_pg = (c + n_extra + PAGE - 1) // PAGE
+                    for pg in range(c // PAGE, n_pg):
+                        first = max(c - pg * PAGE, 0)
+                        _poison_slots(pool, w.kv_dtype, is_v, hkv, d, int(pm.block_table[b, pg]),
+                                      list(range(first, PAGE)))
             lst.append(pool)
     return KVState(w.kv_dtype, hkv, d, pm, kp, vp)
 
