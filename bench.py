@@ -221,6 +221,61 @@ def measure_sampling(gr, torch, wl, reps: int = 200) -> dict:
     return out
 
 
+def measure_verify(gr, torch, wl, ctx, sargs_layers, cfg, head, ts, steps: int, warmup: int, decode_ms: float) -> dict:
+    """The speculative verification step (T tokens per sequence through the whole stack and
+    the head, one graph) on the decode step's weights, with pools that have room for T new
+    tokens per sequence; per-step time and verified positions per second."""
+    import numpy as np
+    import synth
+    head_norm, head_w = head
+    out = {}
+    max_ctx = int(ctx.max())
+    for t in ts:
+        kv = synth.kv_state(wl, ctx, extra_slot=t, seed_key=t)
+        pm = kv.pages
+        kd = [torch.from_numpy(p).cuda() for p in kv.k_pools]
+        vd = [torch.from_numpy(p).cuda() for p in kv.v_pools]
+        del kv
+        args = gr.StackArgs(cfg, sargs_layers, kd, vd)
+        rows = wl.batch * t
+        x0 = torch.from_numpy(synth.activations(np.random.default_rng(77 + t), rows, wl.hidden)).cuda()
+        x = torch.empty_like(x0)
+        logits = torch.empty((rows, wl.vocab), dtype=torch.float32, device="cuda") if wl.vocab else None
+        bt, cg = torch.from_numpy(pm.block_table).cuda(), torch.from_numpy(ctx).cuda()
+        ws = gr.workspace(gr.verify_stack_workspace_size(cfg, wl.batch, t, max_ctx, wl.vocab))
+
+        def step():
+            x.copy_(x0)
+            gr.gr_verify_stack(args, pm.num_pages, x, bt, cg, max_ctx, t, head_norm=head_norm, head_w=head_w,
+                               head_wtype=wl.w_head, vocab=wl.vocab, logits=logits, ws=ws)
+
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            step()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        assert torch.isfinite(x).all().item(), "non-finite verification output"
+        out[str(t)] = {"rows": rows, "ms_per_step": round(ms, 4), "positions_per_s": round(rows / (ms * 1e-3), 1),
+                       "step_time_vs_decode": round(ms / decode_ms, 3)}
+        del g, kd, vd, args, ws, logits
+        torch.cuda.synchronize()
+    return out
+
+
 def stage_launches(gr, wl) -> dict:
     """stage -> (kernel name as the profilers print it, grid size in threads or None)."""
     B, H, F = wl.batch, wl.hidden, wl.ffn
@@ -247,6 +302,9 @@ def main():
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sampling", action="store_true", help="skip the sampler measurement")
+    ap.add_argument("--no-verify", action="store_true", help="skip the speculative verification step measurement")
+    ap.add_argument("--verify-t", type=int, nargs="+", default=[2, 4], metavar="T",
+                    help="tokens per sequence of the measured verification steps")
     ap.add_argument("--sampling-only", action="store_true",
                     help="measure only the sampler (prints its JSON object; for profiling runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
@@ -406,6 +464,12 @@ def main():
                 "bytes_per_launch": d["bytes_per_launch"], "avg_launch_us": d["avg_us"]}
     log("[bench] stages: " + json.dumps(stages))
 
+    verify = None
+    if not args.no_verify and wl.n_layers and wl.batch * max(args.verify_t) <= 64:
+        verify = measure_verify(gr, torch, wl, ctx, wts, cfg, (head_norm, head_w), args.verify_t, args.steps,
+                                args.warmup, ms)
+        log("[bench] verify: " + json.dumps(verify))
+
     sampling = None
     if wl.vocab and not args.no_sampling:
         sampling = measure_sampling(gr, torch, wl)
@@ -470,6 +534,7 @@ def main():
         "cpu_baseline": cpu,
         "stages": stages,
         "sampling": sampling,
+        "verify": verify,
     }
     print(json.dumps(out), flush=True)
 

@@ -101,11 +101,18 @@ def _load() -> C.CDLL:
     L.gr_decode_stack.restype = _i
     L.gr_decode_stack_probed.argtypes = list(L.gr_decode_stack.argtypes) + [_i, _i, C.POINTER(_p), C.POINTER(_p)]
     L.gr_decode_stack_probed.restype = _i
+    L.gr_verify_stack_workspace_size.argtypes = [C.POINTER(LayerCfg), _i, _i, _i, _i]
+    L.gr_verify_stack_workspace_size.restype = _sz
+    L.gr_verify_stack.argtypes = [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _i, C.POINTER(_p), C.POINTER(_p), _i,
+                                  _p, _p, _i, _p, _i, _i, _i, _p, _p, _i, _i, _p, _p, _sz, _p]
+    L.gr_verify_stack.restype = _i
+    L.gr_spec_accept.argtypes = [_p, _p, _i, _i, _p, _p]
+    L.gr_spec_accept.restype = _i
     L.gr_sample_workspace_size.argtypes = [_i, _i]
     L.gr_sample_workspace_size.restype = _sz
     L.gr_sample.argtypes = [_p, _i, _i, _p, _p, _p, _p, _sz, _p]
     L.gr_sample.restype = _i
-    if L.gr_abi_version() != 3:
+    if L.gr_abi_version() != 4:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
     return L
@@ -121,7 +128,7 @@ EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_
             "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_paged_gather_kv",
             "gr_decode_layer_workspace_size", "gr_decode_layer", "gr_output_head_workspace_size", "gr_output_head",
             "gr_decode_stack_workspace_size", "gr_decode_stack", "gr_decode_stack_probed", "gr_sample_workspace_size",
-            "gr_sample")
+            "gr_sample", "gr_verify_stack_workspace_size", "gr_verify_stack", "gr_spec_accept")
 
 # gr_stage values
 STAGES = ("pack", "qkv", "attn", "attn_merge", "wo", "gate_up", "down", "head")
@@ -365,6 +372,37 @@ def gr_decode_stack(args: StackArgs, num_pages: int, x, block_table, ctx_lens, m
                                    _ptr(head_norm), _ptr(head_w), head_wtype, vocab, _ptr(logits), _ptr(ws),
                                    ws.numel(), _stream()))
     return x
+
+
+def verify_stack_workspace_size(cfg: LayerCfg, b: int, t: int, max_ctx: int, vocab: int) -> int:
+    return int(_load().gr_verify_stack_workspace_size(C.byref(cfg), b, t, max_ctx, vocab))
+
+
+def gr_verify_stack(args: StackArgs, num_pages: int, x, block_table, ctx_lens, max_ctx: int, t: int, head_norm=None,
+                    head_w=None, head_wtype: int = W_Q6_K, vocab: int = 0, logits=None, ws=None):
+    """T tokens per sequence in one step: x [B*T, hidden] (token j of sequence b in row b*T + j)."""
+    rows = x.shape[0]
+    if rows % t:
+        raise ValueError("x must hold B*T rows")
+    b = rows // t
+    if ws is None:
+        ws = workspace(verify_stack_workspace_size(args.cfg, b, t, max_ctx, vocab), x.device)
+    _check("gr_verify_stack",
+           _load().gr_verify_stack(C.byref(args.cfg), args.weights, args.n, args.k, args.v, num_pages, _ptr(x),
+                                   _ptr(block_table), block_table.shape[1], _ptr(ctx_lens), max_ctx, b, t,
+                                   _ptr(head_norm), _ptr(head_w), head_wtype, vocab, _ptr(logits), _ptr(ws),
+                                   ws.numel(), _stream()))
+    return x
+
+
+def gr_spec_accept(sampled, draft, n_accepted=None):
+    """n_accepted int32 [B] from the target's tokens sampled [B, T] and the step's inputs draft [B, T]."""
+    torch = _torch()
+    b, t = sampled.shape
+    if n_accepted is None:
+        n_accepted = torch.empty(b, dtype=torch.int32, device=sampled.device)
+    _check("gr_spec_accept", _load().gr_spec_accept(_ptr(sampled), _ptr(draft), b, t, _ptr(n_accepted), _stream()))
+    return n_accepted
 
 
 def gr_decode_stack_probed(args: StackArgs, num_pages: int, x, block_table, ctx_lens, max_ctx: int, probe_stage: int,

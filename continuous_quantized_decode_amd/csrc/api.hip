@@ -18,6 +18,8 @@ thread_local ProbeEvents* probe_events = nullptr;
 
 hipError_t launch_dequant(int kind, const void* blocks, int64_t n, float* out, hipStream_t st);
 size_t sample_workspace_bytes(int B, int vocab);
+hipError_t launch_spec_accept(const int32_t* sampled, const int32_t* draft, int B, int T, int32_t* n_accepted,
+                              hipStream_t st);
 int sample_max_vocab();
 hipError_t launch_sample(const float* logits, int B, int vocab, const gr_sample_params* params, int32_t* tokens,
                          uint64_t* kept, void* ws, hipStream_t st);
@@ -217,6 +219,7 @@ struct LayerBufs {
   float *ss_attn, *ss_ffn;
   float *o_part, *m_part, *l_part;
   double* rope;  // [B][head_dim / 2][2]: RoPE of the step's positions
+  float* qbuf;   // [B][Hq][D]: roped queries when a step carries several tokens per sequence
 };
 
 LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan& ap) {
@@ -233,6 +236,7 @@ LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan&
   L.m_part = c.take<float>(units * 4);
   L.l_part = c.take<float>(units * 4);
   L.rope = c.take<double>((size_t)B * cfg->head_dim * sizeof(double));
+  L.qbuf = c.take<float>((size_t)B * qd * 4);
   return L;
 }
 
@@ -267,8 +271,9 @@ gr_status check_layer_w(const gr_layer_cfg* c, const gr_layer_weights* w) {
   return GR_OK;
 }
 
-AttnPlan layer_attn_plan(int B, const gr_layer_cfg* c, int max_ctx) {
-  return plan_attn(B, c->n_kv_heads, max_ctx + 1);
+// rows = B * T attention rows; a sequence holds at most max_ctx + T tokens after the step
+AttnPlan layer_attn_plan(int rows, const gr_layer_cfg* c, int max_ctx, int T = 1) {
+  return plan_attn(rows, c->n_kv_heads, max_ctx + T);
 }
 
 // Optional timing probe: the launches of one stage (repeated `reps` times) carry the
@@ -315,22 +320,25 @@ gr_status run_input_pack(const float* x, int B, int H, const float* gain, Kinds 
   });
 }
 
-RopeTable rope_table(const gr_layer_cfg* c, const int32_t* ctx, const LayerBufs& L) {
+RopeTable rope_table(const gr_layer_cfg* c, const int32_t* ctx, const LayerBufs& L, int T = 1) {
   RopeTable r;
   r.ctx = ctx;
   r.theta = c->rope_theta;
   r.half_d = c->head_dim / 2;
+  r.tokens_per_seq = T;
   r.out = L.rope;
   return r;
 }
 
-// The launch sequence of one decode layer (arguments already validated).  On entry
-// L.xp holds x * attn_norm and L.ss_attn its per-row sum of squares.  On exit x is
-// the layer output and, when next_gain is set, L.xp / L.ss_attn hold x * next_gain
-// packed in the kinds `next`.
+// The launch sequence of one decode layer (arguments already validated).  B rows: row
+// b is token b % T of sequence b / T (T = 1 for a decode step).  On entry L.xp holds
+// x * attn_norm and L.ss_attn its per-row sum of squares.  On exit x is the layer output
+// and, when next_gain is set, L.xp / L.ss_attn hold x * next_gain packed in the kinds
+// `next`.
 gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pages, void* v_pages, float* x,
                     const int32_t* bt, int max_blocks, const int32_t* ctx, int B, const AttnPlan& apl,
-                    const LayerBufs& L, const float* next_gain, Kinds next, hipStream_t st, const Probe* probe) {
+                    const LayerBufs& L, const float* next_gain, Kinds next, hipStream_t st, const Probe* probe,
+                    int T = 1) {
   const int H = c->hidden, D = c->head_dim, qd = c->n_q_heads * D, kvd = c->n_kv_heads * D, F = c->ffn;
   gr_status s;
   // 1. q, k, v = (W (x * g)) / rms(x); zero the FFN-norm accumulator for step 4
@@ -352,6 +360,8 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   // 2. QK-norm, RoPE, KV append and split attention
   AttnParams ap{};
   ap.B = B;
+  ap.tokens_per_seq = T;
+  ap.self_in_pool = T > 1 ? 1 : 0;
   ap.n_q_heads = c->n_q_heads;
   ap.n_kv_heads = c->n_kv_heads;
   ap.head_dim = D;
@@ -375,12 +385,21 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   ap.o_part = L.o_part;
   ap.m_part = L.m_part;
   ap.l_part = L.l_part;
-  s = probed(probe, GR_STAGE_ATTN, st, [&] { return check_launch(launch_attn_split(c->kv_dtype, true, ap, st)); });
+  if (T == 1) {
+    s = probed(probe, GR_STAGE_ATTN, st, [&] { return check_launch(launch_attn_split(c->kv_dtype, true, ap, st)); });
+  } else {
+    // several tokens per sequence: every row's K/V is stored before any row attends
+    ap.q = L.qbuf;
+    s = probed(probe, GR_STAGE_ATTN, st, [&] {
+      const hipError_t e = launch_attn_append(c->kv_dtype, ap, L.qbuf, st);
+      return check_launch(e != hipSuccess ? e : launch_attn_split(c->kv_dtype, false, ap, st));
+    });
+  }
   if (s != GR_OK) return s;
   // 3. log-sum-exp merge -> Wo input pack
   s = probed(probe, GR_STAGE_ATTN_MERGE, st, [&] {
     const PackOut& op = L.op.of(w->to);
-    return check_launch(launch_attn_merge(ap, nullptr, op.pack, op.kind, nslices_of(op.kind, qd), 1, st));
+    return check_launch(launch_attn_merge(ap, nullptr, op.pack, op.kind, nslices_of(op.kind, qd), T == 1 ? 1 : 0, st));
   });
   if (s != GR_OK) return s;
   // 4. x += Wo o; pack x * ffn_norm and its sum of squares for the gate/up GEMM
@@ -605,6 +624,8 @@ gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* 
   Carver c(ws);
   const size_t units = (size_t)B * m->n_q_heads * pl.max_splits;
   AttnParams ap{};
+  ap.tokens_per_seq = 1;
+  ap.self_in_pool = 0;
   ap.o_part = c.take<float>(units * m->head_dim * 4);
   ap.m_part = c.take<float>(units * 4);
   ap.l_part = c.take<float>(units * 4);
@@ -643,24 +664,29 @@ gr_status gr_paged_gather_kv(const void* pages, int is_v, const int32_t* block_t
 }
 
 // --------------------------------------------------------------- decode layer
-size_t gr_decode_layer_workspace_size(const gr_layer_cfg* c, int B, int max_ctx) {
-  if (check_layer_cfg(c) != GR_OK || B <= 0 || max_ctx < 0) return 0;
+static size_t layer_ws_bytes(const gr_layer_cfg* c, int B, int T, int max_ctx) {
+  if (check_layer_cfg(c) != GR_OK || B <= 0 || T <= 0 || max_ctx < 0) return 0;
   Carver cv(nullptr);
-  carve_layer(cv, c, B, layer_attn_plan(B, c, max_ctx));
+  carve_layer(cv, c, B * T, layer_attn_plan(B * T, c, max_ctx, T));
   return cv.off + 256;
 }
 
+size_t gr_decode_layer_workspace_size(const gr_layer_cfg* c, int B, int max_ctx) {
+  return layer_ws_bytes(c, B, 1, max_ctx);
+}
+
+// B sequences of T tokens each (B * T rows through the GEMMs).
 static gr_status check_layer_call(const gr_layer_cfg* c, const gr_layer_weights* w, const void* k_pages,
                                   const void* v_pages, int num_pages, const float* x, const int32_t* bt,
-                                  int max_blocks, const int32_t* ctx, int max_ctx, int B) {
+                                  int max_blocks, const int32_t* ctx, int max_ctx, int B, int T = 1) {
   gr_status s = check_layer_cfg(c);
   if (s != GR_OK) return s;
   s = check_layer_w(c, w);
   if (s != GR_OK) return s;
-  if (B < 0 || B > 64) return GR_ERR_SHAPE;
+  if (B < 0 || T < 1 || (int64_t)B * T > 64) return GR_ERR_SHAPE;
   if (!k_pages || !v_pages || !x || !bt || !ctx) return GR_ERR_NULL;
   if (num_pages <= 0 || max_blocks <= 0 || max_ctx < 0) return GR_ERR_SHAPE;
-  if ((int64_t)max_ctx + 1 > (int64_t)GR_PAGE_SIZE * max_blocks) return GR_ERR_CAPACITY;
+  if ((int64_t)max_ctx + T > (int64_t)GR_PAGE_SIZE * max_blocks) return GR_ERR_CAPACITY;
   if (!aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(x, 16) || !aligned(bt, 4) || !aligned(ctx, 4))
     return GR_ERR_ALIGN;
   return GR_OK;
@@ -742,12 +768,13 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
                                    void* const* k_pages, void* const* v_pages, int num_pages, float* x,
                                    const int32_t* bt, int max_blocks, const int32_t* ctx, int max_ctx, int B,
                                    const float* head_norm, const void* head_w, int head_wtype, int vocab,
-                                   float* logits, void* ws, size_t ws_bytes, void* stream, Probe* probe) {
+                                   float* logits, void* ws, size_t ws_bytes, void* stream, Probe* probe,
+                                   int T = 1) {
   if (n_layers < 0) return GR_ERR_SHAPE;
   if (n_layers > 0 && (!weights || !k_pages || !v_pages)) return GR_ERR_NULL;
   for (int l = 0; l < n_layers; ++l) {
     gr_status s = check_layer_call(c, &weights[l], k_pages[l], v_pages[l], num_pages, x, bt, max_blocks, ctx,
-                                   max_ctx, B);
+                                   max_ctx, B, T);
     if (s != GR_OK) return s;
   }
   if (head_w) {
@@ -759,28 +786,29 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
   if (n_layers == 0) {
     gr_status s = check_layer_cfg(c);
     if (s != GR_OK) return s;
+    if (B < 0 || T < 1 || (int64_t)B * T > 64) return GR_ERR_SHAPE;
   }
   if (probe && probe->stage >= 0) {
     if (!probe->ev_begin || !probe->ev_end) return GR_ERR_NULL;
     if (probe->stage > GR_STAGE_HEAD) return GR_ERR_SHAPE;
   }
   if (B == 0) return GR_OK;
-  if (!ws || ws_bytes < gr_decode_stack_workspace_size(c, B, max_ctx, vocab) || !aligned(ws, 256))
-    return GR_ERR_WORKSPACE;
+  if (!ws || ws_bytes < layer_ws_bytes(c, B, T, max_ctx) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
   gr_status s = check_device();
   if (s != GR_OK) return s;
-  const AttnPlan apl = layer_attn_plan(B, c, max_ctx);
+  const int rows = B * T;
+  const AttnPlan apl = layer_attn_plan(rows, c, max_ctx, T);
   Carver cv(ws);
-  const LayerBufs L = carve_layer(cv, c, B, apl);
+  const LayerBufs L = carve_layer(cv, c, rows, apl);
   hipStream_t st = (hipStream_t)stream;
   if (probe) probe->layer = 0;
   if (n_layers > 0) {
-    s = run_input_pack(x, B, c->hidden, weights[0].attn_norm, qkv_kinds(&weights[0]), L.xp, L.ss_attn, st, probe,
-                       rope_table(c, ctx, L));
+    s = run_input_pack(x, rows, c->hidden, weights[0].attn_norm, qkv_kinds(&weights[0]), L.xp, L.ss_attn, st, probe,
+                       rope_table(c, ctx, L, T));
   } else if (head_w) {
     Kinds k;
     k.add(head_wtype);
-    s = run_input_pack(x, B, c->hidden, head_norm, k, L.xp, L.ss_attn, st, probe);
+    s = run_input_pack(x, rows, c->hidden, head_norm, k, L.xp, L.ss_attn, st, probe);
   }
   if (s != GR_OK) return s;
   for (int l = 0; l < n_layers; ++l) {
@@ -794,12 +822,13 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
       next_gain = head_norm;
       next.add(head_wtype);
     }
-    s = run_layer(c, &weights[l], k_pages[l], v_pages[l], x, bt, max_blocks, ctx, B, apl, L, next_gain, next, st,
-                  probe);
+    s = run_layer(c, &weights[l], k_pages[l], v_pages[l], x, bt, max_blocks, ctx, rows, apl, L, next_gain, next, st,
+                  probe, T);
     if (s != GR_OK) return s;
   }
   if (probe) probe->layer = 0;
-  if (head_w) return run_head(head_w, head_wtype, logits, B, c->hidden, vocab, c->rms_eps, L.xp, L.ss_attn, st, probe);
+  if (head_w)
+    return run_head(head_w, head_wtype, logits, rows, c->hidden, vocab, c->rms_eps, L.xp, L.ss_attn, st, probe);
   return GR_OK;
 }
 
@@ -826,6 +855,33 @@ gr_status gr_decode_stack_probed(const gr_layer_cfg* c, const gr_layer_weights* 
   pr.ev_end = ev_end;
   return decode_stack_impl(c, weights, n_layers, k_pages, v_pages, num_pages, x, bt, max_blocks, ctx, max_ctx, B,
                            head_norm, head_w, head_wtype, vocab, logits, ws, ws_bytes, stream, &pr);
+}
+
+size_t gr_verify_stack_workspace_size(const gr_layer_cfg* c, int B, int T, int max_ctx, int vocab) {
+  (void)vocab;
+  if (B <= 0 || T <= 0 || (int64_t)B * T > 64) return 0;
+  return layer_ws_bytes(c, B, T, max_ctx);
+}
+
+gr_status gr_verify_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers,
+                          void* const* k_pages, void* const* v_pages, int num_pages, float* x, const int32_t* bt,
+                          int max_blocks, const int32_t* ctx, int max_ctx, int B, int T, const float* head_norm,
+                          const void* head_w, int head_wtype, int vocab, float* logits, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (T < 1) return GR_ERR_SHAPE;
+  return decode_stack_impl(c, weights, n_layers, k_pages, v_pages, num_pages, x, bt, max_blocks, ctx, max_ctx, B,
+                           head_norm, head_w, head_wtype, vocab, logits, ws, ws_bytes, stream, nullptr, T);
+}
+
+gr_status gr_spec_accept(const int32_t* sampled, const int32_t* draft, int B, int T, int32_t* n_accepted,
+                         void* stream) {
+  if (B < 0 || T < 1 || T > 1024) return GR_ERR_SHAPE;
+  if (B == 0) return GR_OK;
+  if (!sampled || !draft || !n_accepted) return GR_ERR_NULL;
+  if (!aligned(sampled, 4) || !aligned(draft, 4) || !aligned(n_accepted, 4)) return GR_ERR_ALIGN;
+  gr_status s = check_device();
+  if (s != GR_OK) return s;
+  return check_launch(launch_spec_accept(sampled, draft, B, T, n_accepted, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -131,7 +131,9 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
   const int b = bg / p.n_kv_heads;
   const int R = p.n_q_heads / p.n_kv_heads;
 
-  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
+  const int T = p.tokens_per_seq > 0 ? p.tokens_per_seq : 1;
+  const int seq = b / T;
+  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
   const int pg0 = split * p.pages_per_split;
   const int n = lane & 15, kg = lane >> 4;
 
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
   // fused layer), pairs (da, db) per lane, and the RoPE cosine and sine of the lane's
   // pair at the row's new position (computed in fp64 once per step)
   constexpr int kMaxHeads = 10;  // R <= 8 query heads, then k and v
-  const int ctx = p.ctx_lens[b];
+  const int ctx = p.ctx_lens[seq] + (b - seq * T);  // the row's position
   int bt_chunk = pg0;
   int bt_lane = pg0 + lane < p.max_blocks ? bt[pg0 + lane] : 0;
   const bool act = lane < D / 2;
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
     }
   }
 
-  const int n_tok = FUSED ? ctx + 1 : ctx;
+  const int n_tok = FUSED ? ctx + 1 : ctx + p.self_in_pool;
   const int n_pages = (n_tok + kPage - 1) / kPage;
   if (pg0 >= n_pages) return;
   const int pg1 = min(n_pages, pg0 + p.pages_per_split);
@@ -422,8 +424,10 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p,
   const int bh = blockIdx.x;
   const int h = bh % p.n_q_heads, b = bh / p.n_q_heads;
   const int D = p.head_dim;  // 64 or 128: dims lane and lane + 64
-  const int ctx = p.ctx_lens[b];
-  const int n_tok = fused ? ctx + 1 : ctx;
+  const int T = p.tokens_per_seq > 0 ? p.tokens_per_seq : 1;
+  const int seq = b / T;
+  const int ctx = p.ctx_lens[seq] + (b - seq * T);
+  const int n_tok = fused ? ctx + 1 : ctx + p.self_in_pool;
   const int n_pages = (n_tok + kPage - 1) / kPage;
   const int S = min((n_pages + p.pages_per_split - 1) / p.pages_per_split, p.max_splits);
   const size_t base = ((size_t)b * p.n_q_heads + h) * p.max_splits;
@@ -487,6 +491,72 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p,
 }
 
 // ------------------------------------------------------------------------ launch
+
+// ------------------------------------------------------------ several tokens per row
+//
+// When a step carries several tokens of a sequence (tokens_per_seq > 1), a row's
+// attention must see the tokens before it in the same step, so every row's K/V is
+// stored first: one wave per (row, KV head) applies QK-norm and RoPE (the fused
+// variant's set-up), stores K and V at the row's position and writes the roped query
+// heads; the standalone attention kernel then runs with self_in_pool set.
+template <int KVDT, int D>
+__global__ __launch_bounds__(64) void attn_append_kernel(AttnParams p, float* q_out) {
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x % p.n_kv_heads, b = blockIdx.x / p.n_kv_heads;
+  const int R = p.n_q_heads / p.n_kv_heads;
+  const int T = p.tokens_per_seq > 0 ? p.tokens_per_seq : 1;
+  const int seq = b / T;
+  const int pos = p.ctx_lens[seq] + (b - seq * T);
+  const bool act = lane < D / 2;
+  int da = 0, db = 0;
+  pair_dims(act ? lane : 0, D, p.rope_style, da, db);
+  double cs = 1.0, sn = 0.0;
+  if (act) {
+    cs = p.rope[((size_t)b * (D / 2) + lane) * 2];
+    sn = p.rope[((size_t)b * (D / 2) + lane) * 2 + 1];
+  }
+  __shared__ __attribute__((aligned(16))) float s_kv[2][128];
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[D * 4 + 64];
+  const float* row = p.qkv + (size_t)b * p.qkv_ld;
+  // query heads g*R .. g*R+R-1, then k, then v of head g
+  for (int hh = 0; hh < R + 2; ++hh) {
+    const int off = hh < R ? (g * R + hh) * D : hh == R ? p.q_dim + g * D : p.q_dim + p.kv_dim + g * D;
+    float a = act ? row[off + da] : 0.f, bb = act ? row[off + db] : 0.f;
+    if (hh <= R) norm_rope(a, bb, act, hh < R ? p.q_norm : p.k_norm, p.eps, D, da, db, cs, sn);
+    if (hh < R) {
+      if (act) {
+        float* dst = q_out + ((size_t)b * p.n_q_heads + g * R + hh) * D;
+        dst[da] = a;
+        dst[db] = bb;
+      }
+    } else if (act) {
+      s_kv[hh - R][da] = a;
+      s_kv[hh - R][db] = bb;
+    }
+  }
+  __syncthreads();
+  const int HB = kv_head_bytes_t<KVDT>(D);
+  const size_t page_bytes = (size_t)HB * p.n_kv_heads;
+  const size_t pg = (size_t)p.block_table[(size_t)seq * p.max_blocks + pos / kPage];
+  uint8_t* kdst = (uint8_t*)p.k_pages + pg * page_bytes + (size_t)g * HB;
+  uint8_t* vdst = (uint8_t*)p.v_pages + pg * page_bytes + (size_t)g * HB;
+  store_token<KVDT>(s_kv[0], s_stage, kdst, false, D, pos % kPage, lane);
+  store_token<KVDT>(s_kv[1], s_stage, vdst, true, D, pos % kPage, lane);
+}
+
+hipError_t launch_attn_append(int kv_dtype, const AttnParams& p, float* q_out, hipStream_t st) {
+  const dim3 grid((unsigned)((size_t)p.B * p.n_kv_heads));
+#define GR_AP(KV, DD) launch_kernel(attn_append_kernel<KV, DD>, grid, dim3(64), 0, st, p, q_out)
+  if (kv_dtype == 0) {
+    if (p.head_dim == 128) GR_AP(KV_F32_T, 128); else GR_AP(KV_F32_T, 64);
+  } else if (kv_dtype == 1) {
+    if (p.head_dim == 128) GR_AP(KV_F16_T, 128); else GR_AP(KV_F16_T, 64);
+  } else {
+    if (p.head_dim == 128) GR_AP(KV_Q8_T, 128); else GR_AP(KV_Q8_T, 64);
+  }
+#undef GR_AP
+  return hipGetLastError();
+}
 
 AttnPlan plan_attn(int B, int n_kv_heads, int max_ctx_tokens) {
   // Enough (row, head, split) waves to fill the chip even when most rows are short:

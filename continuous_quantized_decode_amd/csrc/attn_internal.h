@@ -10,7 +10,11 @@ constexpr int KV_F16_T = 1;
 constexpr int KV_Q8_T = 2;
 
 struct AttnParams {
+  // B attention rows; row b is token b % tokens_per_seq of sequence b / tokens_per_seq, at
+  // position ctx_lens[seq] + b % tokens_per_seq (its sequence's block table row is seq)
   int B, n_q_heads, n_kv_heads, head_dim;
+  int tokens_per_seq;  // 1 for a decode step
+  int self_in_pool;    // standalone: 1 if the row's own token is already stored (n_tok = pos + 1)
   int max_blocks, pages_per_split, max_splits;
   float scale;
   const int32_t* block_table;
@@ -42,5 +46,8 @@ size_t attn_partial_floats(int B, int n_q_heads, int head_dim, const AttnPlan& p
 hipError_t launch_attn_split(int kv_dtype, bool fused, const AttnParams& p, hipStream_t st);
 hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, int kind, int nslices, int fused,
                              hipStream_t st);
+// QK-norm and RoPE of every row's q and k, the row's K/V stored at its position (several
+// tokens of a sequence in one step), q written to q_out [B][Hq][D] for the standalone kernel.
+hipError_t launch_attn_append(int kv_dtype, const AttnParams& p, float* q_out, hipStream_t st);
 
 }  // namespace gr

@@ -862,8 +862,9 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------------
 // plan and launch
 
-// Kernel variants by (NT, BTN): one-tile, one-batch-tile kernels take up to 16 waves
-// (their registers fit four waves per SIMD), the others up to 4.
+// Kernel variants by (NT, BTN): those whose registers fit four waves per SIMD (one tile
+// with up to four batch tiles, two tiles with up to two) take up to 16 waves, the
+// others up to 4.
 struct GemmVariant {
   const void* fn = nullptr;
   int maxt = 0;
@@ -874,11 +875,11 @@ template <int WT, bool AL>
 const void* variant_fn(int nt, int btn) {
   switch (nt * 100 + btn) {
     case 101: return (const void*)gemm_kernel<WT, 1, 1, 1024, AL>;
-    case 102: return (const void*)gemm_kernel<WT, 1, 2, 256, AL>;
-    case 104: return (const void*)gemm_kernel<WT, 1, 4, 256, AL>;
+    case 102: return (const void*)gemm_kernel<WT, 1, 2, 1024, AL>;
+    case 104: return (const void*)gemm_kernel<WT, 1, 4, 1024, AL>;
     case 108: return (const void*)gemm_kernel<WT, 1, 8, 256, AL>;
     case 201: return (const void*)gemm_kernel<WT, 2, 1, 256, AL>;
-    case 202: return (const void*)gemm_kernel<WT, 2, 2, 256, AL>;
+    case 202: return (const void*)gemm_kernel<WT, 2, 2, 1024, AL>;
     case 204: return (const void*)gemm_kernel<WT, 2, 4, 256, AL>;
     case 208: return (const void*)gemm_kernel<WT, 2, 8, 256, AL>;
     default: return nullptr;
@@ -900,7 +901,7 @@ struct VariantTable {
           GemmVariant& g = v[ty][nt - 1][lb];
           g.fn = ty == 0 ? variant_fn<12, true>(nt, btn) : ty == 1 ? variant_fn<14, true>(nt, btn)
                                                                   : variant_fn<14, false>(nt, btn);
-          g.maxt = nt == 1 && btn == 1 ? 1024 : 256;
+          g.maxt = (nt == 1 && btn <= 4) || (nt == 2 && btn <= 2 && btn != 1) ? 1024 : 256;
           // registers per lane -> waves per SIMD (512 VGPRs, granule 8); without a device
           // to ask, assume the 128 that a 1024-thread workgroup requires
           int regs = 128;

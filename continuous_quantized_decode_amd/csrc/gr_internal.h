@@ -160,9 +160,10 @@ struct PackOut {
 // ctx[b] * theta^(-2i / (2 half_d)), its cosine and sine in fp64 at out[(b * half_d +
 // i) * 2 + {0, 1}], computed once per step for every layer's attention.
 struct RopeTable {
-  const int32_t* ctx = nullptr;
+  const int32_t* ctx = nullptr;  // per sequence; row b sits at ctx[b / T] + b % T
   double theta = 0.0;
   int half_d = 0;
+  int tokens_per_seq = 1;  // T
   double* out = nullptr;  // NULL: none
 };
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,

@@ -21,7 +21,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
   if (rope.out && b < B && tid < rope.half_d) {
     const double inv = pow(rope.theta, -2.0 * (double)tid / (double)(2 * rope.half_d));
     double sn, cs;
-    sincos((double)rope.ctx[b] * inv, &sn, &cs);
+    const int T = rope.tokens_per_seq > 0 ? rope.tokens_per_seq : 1;
+    const int pos = rope.ctx[b / T] + b % T;  // row b: token b % T of sequence b / T
+    sincos((double)pos * inv, &sn, &cs);
     rope.out[((size_t)b * rope.half_d + tid) * 2] = cs;
     rope.out[((size_t)b * rope.half_d + tid) * 2 + 1] = sn;
   }

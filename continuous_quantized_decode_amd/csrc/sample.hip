@@ -912,3 +912,29 @@ hipError_t launch_sample(const float* logits, int B, int vocab, const gr_sample_
 }
 
 }  // namespace gr
+
+// ------------------------------------------------------------ speculative acceptance
+namespace gr {
+namespace {
+
+// Row b accepts its proposals while the target's token after each position equals the
+// proposal that follows it.
+__global__ void spec_accept_kernel(const int32_t* __restrict__ sampled, const int32_t* __restrict__ draft, int B,
+                                   int T, int32_t* __restrict__ n_accepted) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int n = 0;
+  while (n < T - 1 && sampled[(size_t)b * T + n] == draft[(size_t)b * T + n + 1]) ++n;
+  n_accepted[b] = n;
+}
+
+}  // namespace
+
+hipError_t launch_spec_accept(const int32_t* sampled, const int32_t* draft, int B, int T, int32_t* n_accepted,
+                              hipStream_t st) {
+  launch_kernel(spec_accept_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st, sampled, draft, B, T,
+                n_accepted);
+  return hipGetLastError();
+}
+
+}  // namespace gr

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GR_ABI_VERSION 3
+#define GR_ABI_VERSION 4
 
 typedef enum {
   GR_OK = 0,
@@ -226,6 +226,29 @@ gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
                           int max_blocks_per_row, const int32_t* ctx_lens, int max_ctx, int B,
                           const float* head_norm, const void* head_w, int head_wtype, int vocab, float* logits,
                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Exact speculative verification (Leone, "What ships": exact speculative verification).
+ * gr_verify_stack is the decode stack for T tokens per row in one step: x [B*T][hidden]
+ * (row b*T + j is token j of sequence b, at position ctx_lens[b] + j) holds the inputs
+ * (the sequence's last accepted token, then T-1 proposed tokens); every token's K/V is
+ * appended at its position and every token attends to the sequence's cached tokens and
+ * to the step's tokens at or before it, exactly as T decode steps would.  Returns the
+ * outputs in x and, with a head, logits [B*T][vocab].  B*T <= 64;
+ * max_ctx + T <= 16 * max_blocks_per_row (else GR_ERR_CAPACITY).  T = 1 is gr_decode_stack.
+ * gr_spec_accept: sampled [B][T] holds the target's token after each position (for
+ * example gr_sample over the verify logits, one uniform per position), draft [B][T] the
+ * step's input tokens; n_accepted[b] = the number of leading j < T-1 with
+ * sampled[b][j] == draft[b][j+1].  The sequence then emits sampled[b][0..n_accepted[b]].
+ * With deterministic proposals every emitted token follows the target's own
+ * distribution, so the acceptance is exact. */
+size_t gr_verify_stack_workspace_size(const gr_layer_cfg* c, int B, int T, int max_ctx, int vocab);
+gr_status gr_verify_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers, void* const* k_pages,
+                          void* const* v_pages, int num_pages, float* x, const int32_t* block_table,
+                          int max_blocks_per_row, const int32_t* ctx_lens, int max_ctx, int B, int T,
+                          const float* head_norm, const void* head_w, int head_wtype, int vocab, float* logits,
+                          void* workspace, size_t ws_bytes, void* stream);
+gr_status gr_spec_accept(const int32_t* sampled, const int32_t* draft, int B, int T, int32_t* n_accepted,
+                         void* stream);
 
 /* Timing probe (profiling hook): the same launches as gr_decode_stack, except that
  * the launches of stage `probe_stage` are issued `probe_reps` times (1..1000) in a
