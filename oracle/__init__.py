@@ -372,3 +372,31 @@ def spec_accept(sampled: np.ndarray, draft: np.ndarray) -> np.ndarray:
             n += 1
         out[b] = n
     return out
+
+
+def mixed_stack(workload, layers: Sequence, k_pools: Sequence[np.ndarray], v_pools: Sequence[np.ndarray],
+                x: np.ndarray, block_table: np.ndarray, row_seq: np.ndarray, row_pos: np.ndarray, head=None):
+    """A step of rows placed by (sequence, position) (Leone, "What ships": chunked prefill and
+    continuous decode batching): decode rows, verification runs and prompt chunks together.
+
+    Layer by layer, the rows go through decode_layer one at a time in increasing position, each
+    with its own sequence's block table row, so a sequence's earlier tokens are appended before
+    its later ones attend.  Pools are modified in place.  Returns (per-layer outputs [rows, H],
+    logits or None)."""
+    row_seq = np.asarray(row_seq, dtype=np.int64)
+    row_pos = np.asarray(row_pos, dtype=np.int32)
+    order = np.argsort(row_pos, kind="stable")
+    cur = np.asarray(x, dtype=np.float64).copy()
+    outs = []
+    for lw, kp, vp in zip(layers, k_pools, v_pools):
+        nxt = np.empty_like(cur)
+        for r in order:
+            s = int(row_seq[r])
+            nxt[r] = decode_layer(workload, lw, kp, vp, cur[r:r + 1], block_table[s:s + 1], row_pos[r:r + 1])[0]
+        cur = nxt
+        outs.append(cur.copy())
+    logits = None
+    if head is not None:
+        norm, w = head
+        logits = output_head(cur, norm, workload.rms_eps, w, workload.w_head, workload.vocab)
+    return outs, logits
