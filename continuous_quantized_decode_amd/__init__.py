@@ -106,13 +106,18 @@ def _load() -> C.CDLL:
     L.gr_verify_stack.argtypes = [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _i, C.POINTER(_p), C.POINTER(_p), _i,
                                   _p, _p, _i, _p, _i, _i, _i, _p, _p, _i, _i, _p, _p, _sz, _p]
     L.gr_verify_stack.restype = _i
+    L.gr_mixed_stack_workspace_size.argtypes = [C.POINTER(LayerCfg), _i, _i, _i]
+    L.gr_mixed_stack_workspace_size.restype = _sz
+    L.gr_mixed_stack.argtypes = [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _i, C.POINTER(_p), C.POINTER(_p), _i,
+                                 _p, _p, _i, _p, _p, _i, _i, _p, _p, _i, _i, _p, _p, _sz, _p]
+    L.gr_mixed_stack.restype = _i
     L.gr_spec_accept.argtypes = [_p, _p, _i, _i, _p, _p]
     L.gr_spec_accept.restype = _i
     L.gr_sample_workspace_size.argtypes = [_i, _i]
     L.gr_sample_workspace_size.restype = _sz
     L.gr_sample.argtypes = [_p, _i, _i, _p, _p, _p, _p, _sz, _p]
     L.gr_sample.restype = _i
-    if L.gr_abi_version() != 4:
+    if L.gr_abi_version() != 5:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
     return L
@@ -128,7 +133,8 @@ EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_
             "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_paged_gather_kv",
             "gr_decode_layer_workspace_size", "gr_decode_layer", "gr_output_head_workspace_size", "gr_output_head",
             "gr_decode_stack_workspace_size", "gr_decode_stack", "gr_decode_stack_probed", "gr_sample_workspace_size",
-            "gr_sample", "gr_verify_stack_workspace_size", "gr_verify_stack", "gr_spec_accept")
+            "gr_sample", "gr_verify_stack_workspace_size", "gr_verify_stack", "gr_spec_accept",
+            "gr_mixed_stack_workspace_size", "gr_mixed_stack")
 
 # gr_stage values
 STAGES = ("pack", "qkv", "attn", "attn_merge", "wo", "gate_up", "down", "head")
@@ -392,6 +398,24 @@ def gr_verify_stack(args: StackArgs, num_pages: int, x, block_table, ctx_lens, m
                                    _ptr(block_table), block_table.shape[1], _ptr(ctx_lens), max_ctx, b, t,
                                    _ptr(head_norm), _ptr(head_w), head_wtype, vocab, _ptr(logits), _ptr(ws),
                                    ws.numel(), _stream()))
+    return x
+
+
+def mixed_stack_workspace_size(cfg: LayerCfg, rows: int, max_pos: int, vocab: int) -> int:
+    return int(_load().gr_mixed_stack_workspace_size(C.byref(cfg), rows, max_pos, vocab))
+
+
+def gr_mixed_stack(args: StackArgs, num_pages: int, x, block_table, row_seq, row_pos, max_pos: int, head_norm=None,
+                   head_w=None, head_wtype: int = W_Q6_K, vocab: int = 0, logits=None, ws=None):
+    """Rows placed by (row_seq, row_pos): decode rows, verification runs and prompt chunks in one step."""
+    rows = x.shape[0]
+    if ws is None:
+        ws = workspace(mixed_stack_workspace_size(args.cfg, rows, max_pos, vocab), x.device)
+    _check("gr_mixed_stack",
+           _load().gr_mixed_stack(C.byref(args.cfg), args.weights, args.n, args.k, args.v, num_pages, _ptr(x),
+                                  _ptr(block_table), block_table.shape[1], _ptr(row_seq), _ptr(row_pos), rows, max_pos,
+                                  _ptr(head_norm), _ptr(head_w), head_wtype, vocab, _ptr(logits), _ptr(ws),
+                                  ws.numel(), _stream()))
     return x
 
 

@@ -320,15 +320,27 @@ gr_status run_input_pack(const float* x, int B, int H, const float* gain, Kinds 
   });
 }
 
-RopeTable rope_table(const gr_layer_cfg* c, const int32_t* ctx, const LayerBufs& L, int T = 1) {
+RopeTable rope_table(const gr_layer_cfg* c, const int32_t* ctx, const LayerBufs& L, int T = 1,
+                     const int32_t* row_pos = nullptr) {
   RopeTable r;
   r.ctx = ctx;
   r.theta = c->rope_theta;
   r.half_d = c->head_dim / 2;
   r.tokens_per_seq = T;
+  r.row_pos = row_pos;
   r.out = L.rope;
   return r;
 }
+
+// Where a step's rows sit: row b is token b % T of sequence b / T at position
+// ctx_lens[seq] + b % T (T = 1: a decode step), or, when pos is set, the token at
+// position pos[b] of sequence seq[b].
+struct RowMap {
+  int T = 1;
+  const int32_t* seq = nullptr;
+  const int32_t* pos = nullptr;
+  bool fused() const { return T == 1 && !pos; }  // one token per sequence: append inside attention
+};
 
 // The launch sequence of one decode layer (arguments already validated).  B rows: row
 // b is token b % T of sequence b / T (T = 1 for a decode step).  On entry L.xp holds
@@ -338,7 +350,8 @@ RopeTable rope_table(const gr_layer_cfg* c, const int32_t* ctx, const LayerBufs&
 gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pages, void* v_pages, float* x,
                     const int32_t* bt, int max_blocks, const int32_t* ctx, int B, const AttnPlan& apl,
                     const LayerBufs& L, const float* next_gain, Kinds next, hipStream_t st, const Probe* probe,
-                    int T = 1) {
+                    RowMap rm = RowMap{}) {
+  const int T = rm.T;
   const int H = c->hidden, D = c->head_dim, qd = c->n_q_heads * D, kvd = c->n_kv_heads * D, F = c->ffn;
   gr_status s;
   // 1. q, k, v = (W (x * g)) / rms(x); zero the FFN-norm accumulator for step 4
@@ -361,7 +374,9 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   AttnParams ap{};
   ap.B = B;
   ap.tokens_per_seq = T;
-  ap.self_in_pool = T > 1 ? 1 : 0;
+  ap.self_in_pool = rm.fused() ? 0 : 1;
+  ap.row_seq = rm.seq;
+  ap.row_pos = rm.pos;
   ap.n_q_heads = c->n_q_heads;
   ap.n_kv_heads = c->n_kv_heads;
   ap.head_dim = D;
@@ -385,10 +400,10 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   ap.o_part = L.o_part;
   ap.m_part = L.m_part;
   ap.l_part = L.l_part;
-  if (T == 1) {
+  if (rm.fused()) {
     s = probed(probe, GR_STAGE_ATTN, st, [&] { return check_launch(launch_attn_split(c->kv_dtype, true, ap, st)); });
   } else {
-    // several tokens per sequence: every row's K/V is stored before any row attends
+    // several tokens of a sequence: every row's K/V is stored before any row attends
     ap.q = L.qbuf;
     s = probed(probe, GR_STAGE_ATTN, st, [&] {
       const hipError_t e = launch_attn_append(c->kv_dtype, ap, L.qbuf, st);
@@ -399,7 +414,8 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   // 3. log-sum-exp merge -> Wo input pack
   s = probed(probe, GR_STAGE_ATTN_MERGE, st, [&] {
     const PackOut& op = L.op.of(w->to);
-    return check_launch(launch_attn_merge(ap, nullptr, op.pack, op.kind, nslices_of(op.kind, qd), T == 1 ? 1 : 0, st));
+    return check_launch(
+        launch_attn_merge(ap, nullptr, op.pack, op.kind, nslices_of(op.kind, qd), rm.fused() ? 1 : 0, st));
   });
   if (s != GR_OK) return s;
   // 4. x += Wo o; pack x * ffn_norm and its sum of squares for the gate/up GEMM
@@ -678,16 +694,19 @@ size_t gr_decode_layer_workspace_size(const gr_layer_cfg* c, int B, int max_ctx)
 // B sequences of T tokens each (B * T rows through the GEMMs).
 static gr_status check_layer_call(const gr_layer_cfg* c, const gr_layer_weights* w, const void* k_pages,
                                   const void* v_pages, int num_pages, const float* x, const int32_t* bt,
-                                  int max_blocks, const int32_t* ctx, int max_ctx, int B, int T = 1) {
+                                  int max_blocks, const int32_t* ctx, int max_ctx, int B, int T = 1,
+                                  const int32_t* row_seq = nullptr, const int32_t* row_pos = nullptr) {
   gr_status s = check_layer_cfg(c);
   if (s != GR_OK) return s;
   s = check_layer_w(c, w);
   if (s != GR_OK) return s;
   if (B < 0 || T < 1 || (int64_t)B * T > 64) return GR_ERR_SHAPE;
-  if (!k_pages || !v_pages || !x || !bt || !ctx) return GR_ERR_NULL;
+  if (!k_pages || !v_pages || !x || !bt) return GR_ERR_NULL;
+  if (row_pos ? !row_seq : !ctx) return GR_ERR_NULL;
   if (num_pages <= 0 || max_blocks <= 0 || max_ctx < 0) return GR_ERR_SHAPE;
   if ((int64_t)max_ctx + T > (int64_t)GR_PAGE_SIZE * max_blocks) return GR_ERR_CAPACITY;
-  if (!aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(x, 16) || !aligned(bt, 4) || !aligned(ctx, 4))
+  if (!aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(x, 16) || !aligned(bt, 4) || !aligned(ctx, 4) ||
+      !aligned(row_seq, 4) || !aligned(row_pos, 4))
     return GR_ERR_ALIGN;
   return GR_OK;
 }
@@ -769,12 +788,13 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
                                    const int32_t* bt, int max_blocks, const int32_t* ctx, int max_ctx, int B,
                                    const float* head_norm, const void* head_w, int head_wtype, int vocab,
                                    float* logits, void* ws, size_t ws_bytes, void* stream, Probe* probe,
-                                   int T = 1) {
+                                   RowMap rm = RowMap{}) {
+  const int T = rm.T;
   if (n_layers < 0) return GR_ERR_SHAPE;
   if (n_layers > 0 && (!weights || !k_pages || !v_pages)) return GR_ERR_NULL;
   for (int l = 0; l < n_layers; ++l) {
     gr_status s = check_layer_call(c, &weights[l], k_pages[l], v_pages[l], num_pages, x, bt, max_blocks, ctx,
-                                   max_ctx, B, T);
+                                   max_ctx, B, T, rm.seq, rm.pos);
     if (s != GR_OK) return s;
   }
   if (head_w) {
@@ -804,7 +824,7 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
   if (probe) probe->layer = 0;
   if (n_layers > 0) {
     s = run_input_pack(x, rows, c->hidden, weights[0].attn_norm, qkv_kinds(&weights[0]), L.xp, L.ss_attn, st, probe,
-                       rope_table(c, ctx, L, T));
+                       rope_table(c, ctx, L, T, rm.pos));
   } else if (head_w) {
     Kinds k;
     k.add(head_wtype);
@@ -823,7 +843,7 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
       next.add(head_wtype);
     }
     s = run_layer(c, &weights[l], k_pages[l], v_pages[l], x, bt, max_blocks, ctx, rows, apl, L, next_gain, next, st,
-                  probe, T);
+                  probe, rm);
     if (s != GR_OK) return s;
   }
   if (probe) probe->layer = 0;
@@ -869,8 +889,29 @@ gr_status gr_verify_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
                           const void* head_w, int head_wtype, int vocab, float* logits, void* ws, size_t ws_bytes,
                           void* stream) {
   if (T < 1) return GR_ERR_SHAPE;
+  RowMap rm;
+  rm.T = T;
   return decode_stack_impl(c, weights, n_layers, k_pages, v_pages, num_pages, x, bt, max_blocks, ctx, max_ctx, B,
-                           head_norm, head_w, head_wtype, vocab, logits, ws, ws_bytes, stream, nullptr, T);
+                           head_norm, head_w, head_wtype, vocab, logits, ws, ws_bytes, stream, nullptr, rm);
+}
+
+size_t gr_mixed_stack_workspace_size(const gr_layer_cfg* c, int rows, int max_pos, int vocab) {
+  (void)vocab;
+  if (rows <= 0 || rows > 64 || max_pos < 0) return 0;
+  return layer_ws_bytes(c, rows, 1, max_pos);
+}
+
+gr_status gr_mixed_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers, void* const* k_pages,
+                         void* const* v_pages, int num_pages, float* x, const int32_t* bt, int max_blocks,
+                         const int32_t* row_seq, const int32_t* row_pos, int rows, int max_pos,
+                         const float* head_norm, const void* head_w, int head_wtype, int vocab, float* logits, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (n_layers > 0 && (!row_seq || !row_pos) && rows > 0) return GR_ERR_NULL;
+  RowMap rm;
+  rm.seq = row_seq;
+  rm.pos = row_pos;
+  return decode_stack_impl(c, weights, n_layers, k_pages, v_pages, num_pages, x, bt, max_blocks, nullptr, max_pos,
+                           rows, head_norm, head_w, head_wtype, vocab, logits, ws, ws_bytes, stream, nullptr, rm);
 }
 
 gr_status gr_spec_accept(const int32_t* sampled, const int32_t* draft, int B, int T, int32_t* n_accepted,

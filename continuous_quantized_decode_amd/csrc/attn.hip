@@ -131,8 +131,8 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
   const int b = bg / p.n_kv_heads;
   const int R = p.n_q_heads / p.n_kv_heads;
 
-  const int T = p.tokens_per_seq > 0 ? p.tokens_per_seq : 1;
-  const int seq = b / T;
+  int seq, ctx;  // the row's sequence and position
+  attn_row_place(p, b, seq, ctx);
   const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
   const int pg0 = split * p.pages_per_split;
   const int n = lane & 15, kg = lane >> 4;
@@ -143,7 +143,6 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
   // fused layer), pairs (da, db) per lane, and the RoPE cosine and sine of the lane's
   // pair at the row's new position (computed in fp64 once per step)
   constexpr int kMaxHeads = 10;  // R <= 8 query heads, then k and v
-  const int ctx = p.ctx_lens[seq] + (b - seq * T);  // the row's position
   int bt_chunk = pg0;
   int bt_lane = pg0 + lane < p.max_blocks ? bt[pg0 + lane] : 0;
   const bool act = lane < D / 2;
@@ -424,9 +423,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p,
   const int bh = blockIdx.x;
   const int h = bh % p.n_q_heads, b = bh / p.n_q_heads;
   const int D = p.head_dim;  // 64 or 128: dims lane and lane + 64
-  const int T = p.tokens_per_seq > 0 ? p.tokens_per_seq : 1;
-  const int seq = b / T;
-  const int ctx = p.ctx_lens[seq] + (b - seq * T);
+  int seq, ctx;
+  attn_row_place(p, b, seq, ctx);
   const int n_tok = fused ? ctx + 1 : ctx + p.self_in_pool;
   const int n_pages = (n_tok + kPage - 1) / kPage;
   const int S = min((n_pages + p.pages_per_split - 1) / p.pages_per_split, p.max_splits);
@@ -494,7 +492,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p,
 
 // ------------------------------------------------------------ several tokens per row
 //
-// When a step carries several tokens of a sequence (tokens_per_seq > 1), a row's
+// When a step carries several tokens of a sequence (tokens_per_seq > 1, or rows placed
+// by row_seq / row_pos), a row's
 // attention must see the tokens before it in the same step, so every row's K/V is
 // stored first: one wave per (row, KV head) applies QK-norm and RoPE (the fused
 // variant's set-up), stores K and V at the row's position and writes the roped query
@@ -504,9 +503,8 @@ __global__ __launch_bounds__(64) void attn_append_kernel(AttnParams p, float* q_
   const int lane = threadIdx.x;
   const int g = blockIdx.x % p.n_kv_heads, b = blockIdx.x / p.n_kv_heads;
   const int R = p.n_q_heads / p.n_kv_heads;
-  const int T = p.tokens_per_seq > 0 ? p.tokens_per_seq : 1;
-  const int seq = b / T;
-  const int pos = p.ctx_lens[seq] + (b - seq * T);
+  int seq, pos;
+  attn_row_place(p, b, seq, pos);
   const bool act = lane < D / 2;
   int da = 0, db = 0;
   pair_dims(act ? lane : 0, D, p.rope_style, da, db);

@@ -15,6 +15,9 @@ struct AttnParams {
   int B, n_q_heads, n_kv_heads, head_dim;
   int tokens_per_seq;  // 1 for a decode step
   int self_in_pool;    // standalone: 1 if the row's own token is already stored (n_tok = pos + 1)
+  // when set, row b is the token at position row_pos[b] of sequence row_seq[b] instead
+  const int32_t* row_seq;
+  const int32_t* row_pos;
   int max_blocks, pages_per_split, max_splits;
   float scale;
   const int32_t* block_table;
@@ -36,6 +39,18 @@ struct AttnParams {
   float* m_part;
   float* l_part;
 };
+
+// Sequence and position of attention row b.
+GR_DEV void attn_row_place(const AttnParams& p, int b, int& seq, int& pos) {
+  if (p.row_pos) {
+    seq = p.row_seq[b];
+    pos = p.row_pos[b];
+  } else {
+    const int T = p.tokens_per_seq > 0 ? p.tokens_per_seq : 1;
+    seq = b / T;
+    pos = p.ctx_lens[seq] + (b - seq * T);
+  }
+}
 
 struct AttnPlan {
   int pages_per_split, max_splits;

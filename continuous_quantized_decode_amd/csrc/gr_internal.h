@@ -164,6 +164,7 @@ struct RopeTable {
   double theta = 0.0;
   int half_d = 0;
   int tokens_per_seq = 1;  // T
+  const int32_t* row_pos = nullptr;  // when set, row b sits at row_pos[b]
   double* out = nullptr;  // NULL: none
 };
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,

@@ -22,7 +22,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
     const double inv = pow(rope.theta, -2.0 * (double)tid / (double)(2 * rope.half_d));
     double sn, cs;
     const int T = rope.tokens_per_seq > 0 ? rope.tokens_per_seq : 1;
-    const int pos = rope.ctx[b / T] + b % T;  // row b: token b % T of sequence b / T
+    // row b: the token at row_pos[b], or token b % T of sequence b / T
+    const int pos = rope.row_pos ? rope.row_pos[b] : rope.ctx[b / T] + b % T;
     sincos((double)pos * inv, &sn, &cs);
     rope.out[((size_t)b * rope.half_d + tid) * 2] = cs;
     rope.out[((size_t)b * rope.half_d + tid) * 2 + 1] = sn;
@@ -61,7 +62,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
 
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
                             float* ss_out, hipStream_t st, RopeTable rope) {
-  if (rope.out && (rope.half_d <= 0 || rope.half_d > kPackThreads || !rope.ctx)) return hipErrorInvalidValue;
+  if (rope.out && (rope.half_d <= 0 || rope.half_d > kPackThreads || (!rope.ctx && !rope.row_pos)))
+    return hipErrorInvalidValue;
   launch_kernel(pack_rows_kernel, dim3(8 * actpack_tiles(B)), dim3(kPackThreads), 0, st, x, ldx, B, K, gain, o1, o2,
                 ss_out, rope);
   return hipGetLastError();

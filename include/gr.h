@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GR_ABI_VERSION 4
+#define GR_ABI_VERSION 5
 
 typedef enum {
   GR_OK = 0,
@@ -249,6 +249,24 @@ gr_status gr_verify_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
                           void* workspace, size_t ws_bytes, void* stream);
 gr_status gr_spec_accept(const int32_t* sampled, const int32_t* draft, int B, int T, int32_t* n_accepted,
                          void* stream);
+
+/* Mixed step (continuous batching with chunked prefill; Leone, What ships: chunked
+ * prefill, continuous decode batching; Leone, intro: decode rows and prompt chunks in one
+ * schedule).  Row r of x [rows][hidden] is the token at position row_pos[r] of sequence
+ * row_seq[r] (device int32 arrays; block_table row row_seq[r]).  Every row's K/V is stored
+ * at its position, then every row attends to positions 0..row_pos[r] of its sequence.  A
+ * step can hold decode rows (one token at the cached length), verification runs and
+ * prompt chunks (consecutive positions), in any row order.  Device-resident
+ * preconditions (documented, not checked): the positions of a sequence's rows in one step
+ * are distinct and, together with the tokens cached before the step, cover 0..max of them;
+ * row_pos[r] <= max_pos.  1 <= rows <= 64; max_pos + 1 <= 16 * max_blocks_per_row (else
+ * GR_ERR_CAPACITY).  logits [rows][vocab] with a head. */
+size_t gr_mixed_stack_workspace_size(const gr_layer_cfg* c, int rows, int max_pos, int vocab);
+gr_status gr_mixed_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers, void* const* k_pages,
+                         void* const* v_pages, int num_pages, float* x, const int32_t* block_table,
+                         int max_blocks_per_row, const int32_t* row_seq, const int32_t* row_pos, int rows, int max_pos,
+                         const float* head_norm, const void* head_w, int head_wtype, int vocab, float* logits,
+                         void* workspace, size_t ws_bytes, void* stream);
 
 /* Timing probe (profiling hook): the same launches as gr_decode_stack, except that
  * the launches of stage `probe_stage` are issued `probe_reps` times (1..1000) in a
