@@ -276,6 +276,61 @@ def measure_verify(gr, torch, wl, ctx, sargs_layers, cfg, head, ts, steps: int, 
     return out
 
 
+def measure_mixed(gr, torch, wl, ctx, sargs_layers, cfg, head, chunk: int, steps: int, warmup: int,
+                  decode_ms: float) -> dict:
+    """A mixed step on the decode step's weights: the workload's B decode rows plus a prompt
+    chunk of `chunk` tokens of a new sequence (from an empty cache), one graph with the head."""
+    import numpy as np
+    import synth
+    head_norm, head_w = head
+    b = wl.batch
+    ctx2 = np.concatenate([ctx, [0]]).astype(np.int32)
+    kv = synth.kv_state(wl, ctx2, extra_slot=chunk, seed_key=100 + chunk)
+    pm = kv.pages
+    kd = [torch.from_numpy(p).cuda() for p in kv.k_pools]
+    vd = [torch.from_numpy(p).cuda() for p in kv.v_pools]
+    del kv
+    args = gr.StackArgs(cfg, sargs_layers, kd, vd)
+    rows = b + chunk
+    seq = np.concatenate([np.arange(b), np.full(chunk, b)]).astype(np.int32)
+    pos = np.concatenate([ctx, np.arange(chunk)]).astype(np.int32)
+    max_pos = int(pos.max())
+    x0 = torch.from_numpy(synth.activations(np.random.default_rng(55), rows, wl.hidden)).cuda()
+    x = torch.empty_like(x0)
+    logits = torch.empty((rows, wl.vocab), dtype=torch.float32, device="cuda") if wl.vocab else None
+    bt = torch.from_numpy(pm.block_table).cuda()
+    sq, ps = torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda()
+    ws = gr.workspace(gr.mixed_stack_workspace_size(cfg, rows, max_pos, wl.vocab))
+
+    def step():
+        x.copy_(x0)
+        gr.gr_mixed_stack(args, pm.num_pages, x, bt, sq, ps, max_pos, head_norm=head_norm, head_w=head_w,
+                          head_wtype=wl.w_head, vocab=wl.vocab, logits=logits, ws=ws)
+
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert torch.isfinite(x).all().item(), "non-finite mixed-step output"
+    return {"decode_rows": b, "prefill_rows": chunk, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(rows / (ms * 1e-3), 1), "step_time_vs_decode": round(ms / decode_ms, 3)}
+
+
 def stage_launches(gr, wl) -> dict:
     """stage -> (kernel name as the profilers print it, grid size in threads or None)."""
     B, H, F = wl.batch, wl.hidden, wl.ffn
@@ -305,6 +360,8 @@ def main():
     ap.add_argument("--no-verify", action="store_true", help="skip the speculative verification step measurement")
     ap.add_argument("--verify-t", type=int, nargs="+", default=[2, 4], metavar="T",
                     help="tokens per sequence of the measured verification steps")
+    ap.add_argument("--mixed-chunk", type=int, default=56,
+                    help="prompt tokens next to the decode rows in the measured mixed step (0: skip)")
     ap.add_argument("--sampling-only", action="store_true",
                     help="measure only the sampler (prints its JSON object; for profiling runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
@@ -470,6 +527,12 @@ def main():
                                 args.warmup, ms)
         log("[bench] verify: " + json.dumps(verify))
 
+    mixed = None
+    if args.mixed_chunk > 0 and wl.n_layers and wl.batch + args.mixed_chunk <= 64:
+        mixed = measure_mixed(gr, torch, wl, ctx, wts, cfg, (head_norm, head_w), args.mixed_chunk, args.steps,
+                              args.warmup, ms)
+        log("[bench] mixed: " + json.dumps(mixed))
+
     sampling = None
     if wl.vocab and not args.no_sampling:
         sampling = measure_sampling(gr, torch, wl)
@@ -535,6 +598,7 @@ def main():
         "stages": stages,
         "sampling": sampling,
         "verify": verify,
+        "mixed": mixed,
     }
     print(json.dumps(out), flush=True)
 
