@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-Q4_K, Q6_K = 12, 14
+Q8_0, Q4_K, Q5_K, Q6_K = 8, 12, 13, 14
 KV_F32, KV_F16, KV_Q8_0 = 0, 1, 2
 
 
@@ -59,7 +59,7 @@ def _declare(L: C.CDLL) -> None:
     L.orc_f16_to_f64.restype = _d
     L.orc_f64_to_f16.argtypes = [_d]
     L.orc_f64_to_f16.restype = C.c_uint16
-    for n in ("orc_q4k_dequant", "orc_q6k_dequant", "orc_q8_0_dequant"):
+    for n in ("orc_q4k_dequant", "orc_q6k_dequant", "orc_q8_0_dequant", "orc_q5k_dequant"):
         getattr(L, n).argtypes = [_p, _i64, _p]
         getattr(L, n).restype = None
     L.orc_num_threads.argtypes = []
@@ -131,9 +131,9 @@ def silu(z: float) -> float:
 # ------------------------------------------------------------------------------------ decoders
 
 def dequant(kind: str, blocks: np.ndarray) -> np.ndarray:
-    """kind in {"q4k", "q6k", "q8_0"}; blocks: raw bytes (any shape) -> flat float64 values."""
+    """kind in {"q4k", "q5k", "q6k", "q8_0"}; blocks: raw bytes (any shape) -> flat float64 values."""
     b = _c(blocks, np.uint8).reshape(-1)
-    size, per = {"q4k": (144, 256), "q6k": (210, 256), "q8_0": (34, 32)}[kind]
+    size, per = {"q4k": (144, 256), "q5k": (176, 256), "q6k": (210, 256), "q8_0": (34, 32)}[kind]
     assert b.size % size == 0
     n = b.size // size
     out = np.empty(n * per, dtype=np.float64)

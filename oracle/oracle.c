@@ -16,6 +16,7 @@
  *     logical pages (Known limitations), 16-token pages.
  *   - LeatEngine, Run: the q8_0 cache as llama.cpp keeps it (32-element blocks with
  *     an fp16 scale).
+ *   - Q5_K and Q8_0 weight rows (the survey's next decoders; public GGUF layouts).
  *   - Leone, "What ships": greedy and stochastic sampling (temperature, top-k, top-p)
  *     after the output head, with fixed-point weights so every decision is an
  *     integer one (the readings sit with orc_sample below).
@@ -33,7 +34,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#define ORC_Q8_0 8
 #define ORC_Q4_K 12
+#define ORC_Q5_K 13
 #define ORC_Q6_K 14
 #define ORC_KV_F32 0
 #define ORC_KV_F16 1
@@ -110,6 +113,36 @@ void orc_q4k_block(const uint8_t* blk, double* w) {
   }
 }
 
+/* Q5_K super-block (GGUF): 256 weights in 176 bytes.
+ *   [0,2) d (fp16), [2,4) dmin (fp16), [4,16) the Q4_K packing of eight 6-bit scales
+ *   and mins, [16,48) 32 bytes of high bits, [48,176) 128 bytes of low 4 bits.
+ *   Sub-block j (32 weights) has w = d*sc[j]*q - dmin*m[j], q in [0,32).  Byte 32c+l
+ *   of the low bits holds weight 64c+l (low nibble) and 64c+32+l (high nibble); their
+ *   fifth bits are bits 2c and 2c+1 of high-bit byte l. */
+void orc_q5k_block(const uint8_t* blk, double* w) {
+  double d = orc_f16_to_f64(rd16(blk)), dmin = orc_f16_to_f64(rd16(blk + 2));
+  const uint8_t* s = blk + 4;
+  const uint8_t* qh = blk + 16;
+  const uint8_t* qs = blk + 48;
+  int sc[8], mn[8];
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = s[j] & 63;
+    mn[j] = s[j + 4] & 63;
+  }
+  for (int j = 4; j < 8; ++j) {
+    sc[j] = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+    mn[j] = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+  }
+  for (int c = 0; c < 4; ++c) {
+    for (int l = 0; l < 32; ++l) {
+      int lo = (qs[32 * c + l] & 15) | (((qh[l] >> (2 * c)) & 1) << 4);
+      int hi = (qs[32 * c + l] >> 4) | (((qh[l] >> (2 * c + 1)) & 1) << 4);
+      w[64 * c + l] = d * sc[2 * c] * lo - dmin * mn[2 * c];
+      w[64 * c + 32 + l] = d * sc[2 * c + 1] * hi - dmin * mn[2 * c + 1];
+    }
+  }
+}
+
 /* Q6_K super-block (GGUF): 256 weights in 210 bytes.
  *   [0,128) low 4 bits, [128,192) high 2 bits, [192,208) sixteen int8 scales,
  *   [208,210) d (fp16).  Weight i = d * scale[i/16] * (q_i - 32), q_i in [0,64).
@@ -152,18 +185,28 @@ void orc_q6k_dequant(const uint8_t* blocks, int64_t n_blocks, double* out) {
 void orc_q8_0_dequant(const uint8_t* blocks, int64_t n_blocks, double* out) {
   for (int64_t i = 0; i < n_blocks; ++i) orc_q8_0_block(blocks + 34 * i, out + 32 * i);
 }
+void orc_q5k_dequant(const uint8_t* blocks, int64_t n_blocks, double* out) {
+  for (int64_t i = 0; i < n_blocks; ++i) orc_q5k_block(blocks + 176 * i, out + 256 * i);
+}
 
+/* Bytes per 256 weights of a matrix row (Q8_0 rows are K/32 consecutive q8_0 blocks). */
 static int wtype_block_bytes(int wtype) {
-  return wtype == ORC_Q4_K ? 144 : wtype == ORC_Q6_K ? 210 : 0;
+  return wtype == ORC_Q4_K ? 144 : wtype == ORC_Q6_K ? 210 : wtype == ORC_Q5_K ? 176 : wtype == ORC_Q8_0 ? 272 : 0;
 }
 
 static void decode_row(int wtype, const uint8_t* row, int K, double* w) {
   int nb = K / ORC_QK, bb = wtype_block_bytes(wtype);
   for (int j = 0; j < nb; ++j) {
+    const uint8_t* blk = row + (size_t)bb * j;
+    double* out = w + ORC_QK * j;
     if (wtype == ORC_Q4_K)
-      orc_q4k_block(row + (size_t)bb * j, w + ORC_QK * j);
+      orc_q4k_block(blk, out);
+    else if (wtype == ORC_Q5_K)
+      orc_q5k_block(blk, out);
+    else if (wtype == ORC_Q8_0)
+      for (int b = 0; b < ORC_QK / ORC_Q8B; ++b) orc_q8_0_block(blk + 34 * b, out + ORC_Q8B * b);
     else
-      orc_q6k_block(row + (size_t)bb * j, w + ORC_QK * j);
+      orc_q6k_block(blk, out);
   }
 }
 

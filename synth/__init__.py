@@ -22,7 +22,9 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 # GGUF tensor type ids (public GGUF enumeration) used as weight-type tags.
+W_Q8_0 = 8
 W_Q4_K = 12
+W_Q5_K = 13
 W_Q6_K = 14
 
 KV_F32 = 0
@@ -34,7 +36,9 @@ ROPE_NORM = 1
 
 PAGE = 16
 Q4K_BYTES = 144
+Q5K_BYTES = 176
 Q6K_BYTES = 210
+Q8_0_BYTES = 34
 QK = 256  # weights per K-quant super-block
 Q8_BLOCK = 32  # q8_0 block length along head_dim
 
@@ -185,11 +189,37 @@ def q6k_weight(rng: np.random.Generator, n_rows: int, k: int) -> np.ndarray:
     return out.reshape(n_rows, nb * Q6K_BYTES)
 
 
+def q5k_weight(rng: np.random.Generator, n_rows: int, k: int) -> np.ndarray:
+    """Random Q5_K matrix: n_rows rows of k/256 super-blocks (176 B each): uniform random
+    quant, high-bit and packed scale/min bytes; d and dmin fp16 draws of U(1e-3, 1e-2)."""
+    assert k % QK == 0
+    nb = k // QK
+    out = random_bytes(_seq(rng), n_rows * nb * Q5K_BYTES).reshape(n_rows, nb, Q5K_BYTES)
+    dd = _f16_uniform_bits(rng, n_rows * nb * 2, 1e-3, 1e-2).reshape(n_rows, nb, 2)
+    out[:, :, 0:4] = dd.view(np.uint8).reshape(n_rows, nb, 4)
+    return out.reshape(n_rows, nb * Q5K_BYTES)
+
+
+def q8_0_weight(rng: np.random.Generator, n_rows: int, k: int) -> np.ndarray:
+    """Random Q8_0 matrix: n_rows rows of k/32 blocks (34 B each): uniform random int8
+    codes (all 256 values) and fp16 scales d of U(1e-4, 1e-3)."""
+    assert k % QK == 0
+    nb = k // Q8_BLOCK
+    out = random_bytes(_seq(rng), n_rows * nb * Q8_0_BYTES).reshape(n_rows, nb, Q8_0_BYTES)
+    d = _f16_uniform_bits(rng, n_rows * nb, 1e-4, 1e-3).reshape(n_rows, nb, 1)
+    out[:, :, 0:2] = d.view(np.uint8).reshape(n_rows, nb, 2)
+    return out.reshape(n_rows, nb * Q8_0_BYTES)
+
+
 def weight(rng: np.random.Generator, wtype: int, n_rows: int, k: int) -> np.ndarray:
     if wtype == W_Q4_K:
         return q4k_weight(rng, n_rows, k)
     if wtype == W_Q6_K:
         return q6k_weight(rng, n_rows, k)
+    if wtype == W_Q5_K:
+        return q5k_weight(rng, n_rows, k)
+    if wtype == W_Q8_0:
+        return q8_0_weight(rng, n_rows, k)
     raise ValueError(f"unknown weight type {wtype}")
 
 

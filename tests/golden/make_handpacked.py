@@ -1,5 +1,5 @@
-"""Write handpacked.json: hand-chosen field values of Q4_K / Q6_K / q8_0 blocks and
-their packed bytes.
+"""Write handpacked.json: hand-chosen field values of Q4_K / Q5_K / Q6_K / q8_0 blocks
+and their packed bytes.
 
 The byte layouts are the public GGUF block formats (the pages only name the
 formats: Leone, "What ships": Q4_K and Q6_K weights; LeatEngine, Run: the q8_0
@@ -12,7 +12,7 @@ import os
 import sys
 
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
-from refimpl import pack_q4k_block, pack_q6k_block, pack_q8_0_block  # noqa: E402
+from refimpl import pack_q4k_block, pack_q5k_block, pack_q6k_block, pack_q8_0_block  # noqa: E402
 
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "handpacked.json")
 
@@ -58,6 +58,23 @@ def main():
     # q8_0: d=0.5 and codes -127..127 over 8 blocks (last padded with 0).
     codes = list(range(-127, 128)) + [0]
     hexes = [pack_q8_0_block(0.5, codes[32 * b:32 * b + 32]).hex() for b in range(8)]
+    # Q5_K blocks: the Q4_K fields with five-bit quants (the fifth bits in their own bytes).
+    sc = [j + 1 for j in range(8)]
+    mn = [2 * j for j in range(8)]
+    q = [i % 32 for i in range(256)]
+    entries["q5k_a"] = dict(format="Q5_K", d=1.0, dmin=0.5, sc=sc, m=mn, q="i%32",
+                            expect="w_i = (j+1)*(i%32) - j, j = i//32",
+                            hex=pack_q5k_block(1.0, 0.5, sc, mn, q).hex())
+    q = [31 - (i % 32) for i in range(256)]
+    entries["q5k_b"] = dict(format="Q5_K", d=0.25, dmin=0.125, sc=[63] * 8, m=[63] * 8, q="31-(i%32)",
+                            expect="w_i = 0.25*63*(31-(i%32)) - 0.125*63",
+                            hex=pack_q5k_block(0.25, 0.125, [63] * 8, [63] * 8, q).hex())
+    sc = [32 + j for j in range(8)]
+    mn = [63 - j for j in range(8)]
+    q = [(i * 7) % 32 for i in range(256)]
+    entries["q5k_c"] = dict(format="Q5_K", d=2.0, dmin=1.0, sc=sc, m=mn, q="(7i)%32",
+                            expect="w_i = 2*(32+j)*((7i)%32) - (63-j), j = i//32",
+                            hex=pack_q5k_block(2.0, 1.0, sc, mn, q).hex())
     entries["q8_0_a"] = dict(format="q8_0", d=0.5, q="-127..127 then 0", expect="x = 0.5*q", hex="".join(hexes))
     with open(OUT, "w") as f:
         json.dump(entries, f, indent=1, sort_keys=True)

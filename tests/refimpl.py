@@ -67,6 +67,19 @@ def pack_q6k_block(d: float, scales, q) -> bytes:
     return bytes(ql) + bytes(qh) + bytes((s & 255) for s in scales) + f16_bits(d).to_bytes(2, "little")
 
 
+def pack_q5k_block(d: float, dmin: float, sc, mn, q) -> bytes:
+    """q: 256 ints in [0,32) in logical weight order (the Q4_K nibble order, fifth bits apart)."""
+    qs = [0] * 128
+    qh = [0] * 32
+    for c in range(4):
+        for l in range(32):
+            a, b = q[64 * c + l], q[64 * c + 32 + l]
+            qs[32 * c + l] = (a & 15) | ((b & 15) << 4)
+            qh[l] |= ((a >> 4) & 1) << (2 * c) | ((b >> 4) & 1) << (2 * c + 1)
+    return (f16_bits(d).to_bytes(2, "little") + f16_bits(dmin).to_bytes(2, "little") + pack_q4k_scales(sc, mn)
+            + bytes(qh) + bytes(qs))
+
+
 def pack_q8_0_block(d: float, q) -> bytes:
     return f16_bits(d).to_bytes(2, "little") + bytes((v & 255) for v in q)
 
@@ -98,6 +111,25 @@ def decode_q4k(blocks: np.ndarray) -> np.ndarray:
     return w.reshape(-1, 256)
 
 
+def decode_q5k(blocks: np.ndarray) -> np.ndarray:
+    """[n, 176] uint8 -> [n, 256] float64 (exact)."""
+    b = blocks.reshape(-1, 176)
+    d = _f16(b[:, 0].astype(np.uint16) | (b[:, 1].astype(np.uint16) << 8))
+    dmin = _f16(b[:, 2].astype(np.uint16) | (b[:, 3].astype(np.uint16) << 8))
+    sc, mn = np.empty((b.shape[0], 8), np.int64), np.empty((b.shape[0], 8), np.int64)
+    for r in range(b.shape[0]):
+        sc[r], mn[r] = unpack_q4k_scales(bytes(b[r, 4:16]))
+    qh = b[:, 16:48].astype(np.int64)  # [n, l]
+    qs = b[:, 48:176].astype(np.int64).reshape(-1, 4, 32)
+    q = np.empty((b.shape[0], 4, 2, 32), np.int64)
+    for c in range(4):
+        q[:, c, 0] = (qs[:, c] & 15) + 16 * ((qh >> (2 * c)) & 1)
+        q[:, c, 1] = (qs[:, c] >> 4) + 16 * ((qh >> (2 * c + 1)) & 1)
+    q = q.reshape(-1, 8, 32)
+    w = d[:, None, None] * sc[:, :, None] * q - dmin[:, None, None] * mn[:, :, None]
+    return w.reshape(-1, 256)
+
+
 def decode_q6k(blocks: np.ndarray) -> np.ndarray:
     b = blocks.reshape(-1, 210)
     ql = b[:, 0:128].astype(np.int64).reshape(-1, 2, 2, 32)  # [n, half, lo/hi 32, l]
@@ -124,6 +156,10 @@ def decode_matrix(wtype: int, w: np.ndarray, n: int, k: int) -> np.ndarray:
         return decode_q4k(w.reshape(n * (k // 256), 144)).reshape(n, k)
     if wtype == 14:
         return decode_q6k(w.reshape(n * (k // 256), 210)).reshape(n, k)
+    if wtype == 13:
+        return decode_q5k(w.reshape(n * (k // 256), 176)).reshape(n, k)
+    if wtype == 8:
+        return decode_q8_0(w.reshape(n * (k // 32), 34)).reshape(n, k)
     raise ValueError(wtype)
 
 

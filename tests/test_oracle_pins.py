@@ -92,6 +92,48 @@ def test_q4k_random_blocks_exact(orc):
     np.testing.assert_array_equal(orc.dequant("q4k", w), refimpl.decode_q4k(w).reshape(-1))
 
 
+# ----------------------------------------------------------------------------- Q5_K
+
+def _q5k_expect(name):
+    i = np.arange(256)
+    j = i // 32
+    if name == "q5k_a":
+        return (j + 1) * (i % 32) - j
+    if name == "q5k_b":
+        return 0.25 * 63 * (31 - (i % 32)) - 0.125 * 63
+    if name == "q5k_c":
+        return 2.0 * (32 + j) * ((7 * i) % 32) - (63 - j)
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["q5k_a", "q5k_b", "q5k_c"])
+def test_q5k_handpacked(orc, gold, name):
+    e = gold[name]
+    q = {"q5k_a": [i % 32 for i in range(256)], "q5k_b": [31 - (i % 32) for i in range(256)],
+         "q5k_c": [(7 * i) % 32 for i in range(256)]}[name]
+    assert refimpl.pack_q5k_block(e["d"], e["dmin"], e["sc"], e["m"], q).hex() == e["hex"]
+    got = orc.dequant("q5k", np.frombuffer(bytes.fromhex(e["hex"]), np.uint8))
+    np.testing.assert_array_equal(got, _q5k_expect(name))
+
+
+def test_q5k_random_blocks_exact(orc):
+    w = synth.q5k_weight(np.random.default_rng(13), 64, 1024)
+    np.testing.assert_array_equal(orc.dequant("q5k", w), refimpl.decode_q5k(w).reshape(-1))
+
+
+def test_q5k_fifth_bits_one_at_a_time(orc):
+    """Each high-bit byte bit, alone, adds 16 * d * sc to exactly one weight."""
+    base = refimpl.pack_q5k_block(1.0, 0.0, [1] * 8, [0] * 8, [0] * 256)
+    for l in (0, 7, 31):
+        for bit in range(8):
+            blk = bytearray(base)
+            blk[16 + l] = 1 << bit
+            got = orc.dequant("q5k", np.frombuffer(bytes(blk), np.uint8))
+            want = np.zeros(256)
+            want[64 * (bit // 2) + 32 * (bit % 2) + l] = 16.0
+            np.testing.assert_array_equal(got, want)
+
+
 # ----------------------------------------------------------------------------- Q6_K
 
 def _q6k_expect(name):
@@ -147,7 +189,7 @@ def test_q8_0_quantizer_properties(orc):
 
 # ----------------------------------------------------------------------------- GEMM
 
-@pytest.mark.parametrize("wtype", [synth.W_Q4_K, synth.W_Q6_K])
+@pytest.mark.parametrize("wtype", [synth.W_Q4_K, synth.W_Q6_K, synth.W_Q5_K, synth.W_Q8_0])
 def test_gemm_matches_decoded_matmul(orc, wtype):
     rng = np.random.default_rng(6)
     n, k, b = 40, 768, 3
