@@ -57,8 +57,11 @@ class Hip:
 
 
 # ------------------------------------------------------------------------ bytes
+ROW_BYTES_PER_256 = {8: 272, 12: 144, 13: 176, 14: 210}  # GGUF Q8_0, Q4_K, Q5_K, Q6_K
+
+
 def weight_bytes(wtype: int, n: int, k: int) -> int:
-    return n * (k // 256) * (144 if wtype == 12 else 210)
+    return n * (k // 256) * ROW_BYTES_PER_256[wtype]
 
 
 def stage_bytes(wl, ctx, kvb_tok):
@@ -221,6 +224,41 @@ def measure_sampling(gr, torch, wl, reps: int = 200) -> dict:
     return out
 
 
+WEIGHT_FORMATS = {"q4_k": (12, "gr_q4k_gemm"), "q5_k": (13, "gr_q5k_gemm"), "q6_k": (14, "gr_q6k_gemm"),
+                  "q8_0": (8, "gr_q8_0_gemm")}
+
+
+def measure_weight_formats(gr, torch, wl, reps: int = 50) -> dict:
+    """One fused-dequant GEMM per weight format on the workload's stacked gate/up shape
+    (2 ffn x hidden) at its batch: per-call time of the C-ABI call (activation pack and
+    GEMM; events on the launch stream) and the weight bytes streamed per second."""
+    import numpy as np
+    import synth
+    n, k, b = 2 * wl.ffn, wl.hidden, wl.batch
+    out = {"shape": f"{n} x {k} (stacked gate/up), B={b}", "formats": {}}
+    x = torch.randn(b, k, device="cuda")
+    y = torch.empty(b, n, device="cuda")
+    ws = gr.workspace(gr.lib().gr_gemm_workspace_size(b, n, k))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, (wt, fn_name) in WEIGHT_FORMATS.items():
+        w = torch.from_numpy(synth.weight(np.random.default_rng(31 + wt), wt, n, k)).cuda()
+        fn = getattr(gr, fn_name)
+        for _ in range(3):
+            fn(w, x, n, y, ws)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn(w, x, n, y, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        wb = weight_bytes(wt, n, k)
+        out["formats"][name] = {"us_per_call": round(us, 2), "weight_bytes": wb,
+                                "weight_gbs": round(wb / (us * 1e-6) / 1e9, 1)}
+        del w
+    return out
+
+
 def measure_verify(gr, torch, wl, ctx, sargs_layers, cfg, head, ts, steps: int, warmup: int, decode_ms: float) -> dict:
     """The speculative verification step (T tokens per sequence through the whole stack and
     the head, one graph) on the decode step's weights, with pools that have room for T new
@@ -362,6 +400,9 @@ def main():
                     help="tokens per sequence of the measured verification steps")
     ap.add_argument("--mixed-chunk", type=int, default=56,
                     help="prompt tokens next to the decode rows in the measured mixed step (0: skip)")
+    ap.add_argument("--no-formats", action="store_true", help="skip the per-weight-format GEMM measurement")
+    ap.add_argument("--formats-only", action="store_true",
+                    help="only the per-weight-format GEMM measurement (one JSON line)")
     ap.add_argument("--sampling-only", action="store_true",
                     help="measure only the sampler (prints its JSON object; for profiling runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
@@ -399,6 +440,9 @@ def main():
     t0 = time.time()
     if args.sampling_only:
         print(json.dumps(measure_sampling(gr, torch, wl)), flush=True)
+        return
+    if args.formats_only:
+        print(json.dumps(measure_weight_formats(gr, torch, wl)), flush=True)
         return
 
     def up(a):
@@ -538,6 +582,11 @@ def main():
         sampling = measure_sampling(gr, torch, wl)
         log("[bench] sampling: " + json.dumps(sampling["cases"]))
 
+    formats = None
+    if not args.no_formats:
+        formats = measure_weight_formats(gr, torch, wl)
+        log("[bench] weight formats: " + json.dumps(formats["formats"]))
+
     # ---- CPU baseline: the fp64 oracle on one whole step of the same workload (every
     #      layer and the output head), when that is bounded; else on its first layers
     cpu = None
@@ -599,6 +648,7 @@ def main():
         "sampling": sampling,
         "verify": verify,
         "mixed": mixed,
+        "weight_formats": formats,
     }
     print(json.dumps(out), flush=True)
 

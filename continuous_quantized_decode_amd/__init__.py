@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgr.so")
 
 GR_OK = 0
-W_Q4_K, W_Q6_K = 12, 14
+W_Q8_0, W_Q4_K, W_Q5_K, W_Q6_K = 8, 12, 13, 14
 KV_F32, KV_F16, KV_Q8_0 = 0, 1, 2
 ROPE_NEOX, ROPE_NORM = 0, 1
 PAGE_SIZE = 16
@@ -76,7 +76,7 @@ def _load() -> C.CDLL:
     L.gr_gemm_workspace_size.restype = _sz
     L.gr_gemm_launch_shape.argtypes = [_i, _i, _i, _i, _i] + [C.POINTER(_i)] * 6
     L.gr_gemm_launch_shape.restype = _i
-    for n in ("gr_q4k_gemm", "gr_q6k_gemm"):
+    for n in ("gr_q4k_gemm", "gr_q6k_gemm", "gr_q5k_gemm", "gr_q8_0_gemm"):
         getattr(L, n).argtypes = [_p, _p, _p, _i, _i, _i, _p, _sz, _p]
         getattr(L, n).restype = _i
     L.gr_paged_decode_attn_workspace_size.argtypes = [C.POINTER(AttnMeta), _i]
@@ -117,7 +117,7 @@ def _load() -> C.CDLL:
     L.gr_sample_workspace_size.restype = _sz
     L.gr_sample.argtypes = [_p, _i, _i, _p, _p, _p, _p, _sz, _p]
     L.gr_sample.restype = _i
-    if L.gr_abi_version() != 5:
+    if L.gr_abi_version() != 6:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
     return L
@@ -129,7 +129,7 @@ def lib() -> C.CDLL:
 
 EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_bytes", "gr_q4k_dequant",
             "gr_q6k_dequant", "gr_q8_0_dequant", "gr_gemm_workspace_size", "gr_gemm_launch_shape", "gr_q4k_gemm",
-            "gr_q6k_gemm",
+            "gr_q6k_gemm", "gr_q5k_gemm", "gr_q8_0_gemm",
             "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_paged_gather_kv",
             "gr_decode_layer_workspace_size", "gr_decode_layer", "gr_output_head_workspace_size", "gr_output_head",
             "gr_decode_stack_workspace_size", "gr_decode_stack", "gr_decode_stack_probed", "gr_sample_workspace_size",
@@ -218,6 +218,14 @@ def gr_q4k_gemm(wblocks, x, n: int, y=None, ws=None):
 
 def gr_q6k_gemm(wblocks, x, n: int, y=None, ws=None):
     return _gemm("gr_q6k_gemm", wblocks, x, n, y, ws)
+
+
+def gr_q5k_gemm(wblocks, x, n: int, y=None, ws=None):
+    return _gemm("gr_q5k_gemm", wblocks, x, n, y, ws)
+
+
+def gr_q8_0_gemm(wblocks, x, n: int, y=None, ws=None):
+    return _gemm("gr_q8_0_gemm", wblocks, x, n, y, ws)
 
 
 GEMM_EPI_STORE, GEMM_EPI_RESIDUAL, GEMM_EPI_SWIGLU = 0, 1, 2

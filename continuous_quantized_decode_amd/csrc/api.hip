@@ -53,7 +53,7 @@ gr_status check_device() {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-bool wtype_ok(int t) { return t == GR_W_Q4_K || t == GR_W_Q6_K; }
+bool wtype_ok(int t) { return t == GR_W_Q4_K || t == GR_W_Q6_K || t == GR_W_Q5_K || t == GR_W_Q8_0; }
 bool kv_ok(int t) { return t == GR_KV_F32 || t == GR_KV_F16 || t == GR_KV_Q8_0; }
 
 // Carves a caller-provided workspace into 256-byte aligned regions; with base ==
@@ -74,7 +74,7 @@ struct Carver {
 // Both actpack kinds of B rows x K columns.
 struct Pack2 {
   PackOut k32, k16;
-  const PackOut& of(int wtype) const { return wtype == GR_W_Q4_K ? k32 : k16; }
+  const PackOut& of(int wtype) const { return wtype == GR_W_Q6_K ? k16 : k32; }  // Q6_K: K=16 MFMA slices
 };
 Pack2 carve_pack2(Carver& c, int B, int K) {
   Pack2 p;
@@ -91,7 +91,7 @@ int nslices_of(int kind, int K) { return kind == kK32 ? K / 32 : K / 16; }
 // The kinds an input must be packed in for matrices of the given types.
 struct Kinds {
   bool k32 = false, k16 = false;
-  void add(int wtype) { (wtype == GR_W_Q4_K ? k32 : k16) = true; }
+  void add(int wtype) { (wtype == GR_W_Q6_K ? k16 : k32) = true; }
 };
 
 // GEMM epilogue parameters shared by one call of gemm_run.
@@ -121,7 +121,7 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     int j = i, n = 0, tiles = 0, all_tiles = 0;
     for (int q = i; q < nmat && types[q] == types[i]; ++q) all_tiles += (rows[q] + 15) / 16;
     // many tiles and a plain store: the tile-loop kernel (one tile per group)
-    const bool tl = ep.kind == kEpiStore && use_tile_loop(all_tiles, K, B);
+    const bool tl = ep.kind == kEpiStore && use_tile_loop(types[i], all_tiles, K, B);
     const int group = tl ? 1 : gemm_group(all_tiles);
     while (j < nmat && types[j] == types[i]) {
       a.w[n] = (const uint8_t*)w[j];
@@ -137,7 +137,7 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     a.nseg = n;
     const int wt = types[i];
     a.nsb = K / kQK;
-    a.row_bytes = (size_t)(K / kQK) * (wt == GR_W_Q4_K ? kQ4KBytes : kQ6KBytes);
+    a.row_bytes = (size_t)(K / kQK) * sb_bytes(wt);
     const PackOut& pin = xin.of(wt);
     a.xpack = pin.pack;
     a.nslices = nslices_of(pin.kind, K);
@@ -187,7 +187,7 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   a.nseg = 2;
   const int tiles = (F + 15) / 16;
   a.nsb = K / kQK;
-  a.row_bytes = (size_t)(K / kQK) * (wtype == GR_W_Q4_K ? kQ4KBytes : kQ6KBytes);
+  a.row_bytes = (size_t)(K / kQK) * sb_bytes(wtype);
   const PackOut& pin = xin.of(wtype);
   a.xpack = pin.pack;
   a.nslices = nslices_of(pin.kind, K);
@@ -202,7 +202,7 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   a.pack_nslices = nslices_of(out.kind, F);
   a.zero_ptr = zero_ptr;
   a.zero_n = zero_n;
-  if (use_tile_loop(tiles, K, B)) {
+  if (use_tile_loop(wtype, tiles, K, B)) {
     a.tl_groups = tiles;
     return launch_gemm_tl(wtype, 2, plan_gemm_tl(wtype, 2, tiles, K), a, st);
   }
@@ -538,12 +538,12 @@ size_t gr_gemm_workspace_size(int B, int N, int K) {
 gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* tile_loop, int* nt, int* btn,
                                int* maxt, int* grid_threads, int* block_threads) {
   if (!tile_loop || !nt || !btn || !maxt || !grid_threads || !block_threads) return GR_ERR_NULL;
-  if (wtype != GR_W_Q4_K && wtype != GR_W_Q6_K) return GR_ERR_DTYPE;
+  if (!wtype_ok(wtype)) return GR_ERR_DTYPE;
   if (rows <= 0 || K <= 0 || K % kQK || B <= 0 || B > 64 || epi < 0 || epi > 2) return GR_ERR_SHAPE;
   const int tiles = (rows + 15) / 16;
   const bool pair = epi == 2;
   // the choices gemm_run and gemm_swiglu make
-  if ((pair || epi == 0) && use_tile_loop(tiles, K, B)) {
+  if ((pair || epi == 0) && use_tile_loop(wtype, tiles, K, B)) {
     const TlPlan tp = plan_gemm_tl(wtype, pair ? 2 : 1, tiles, K);
     *tile_loop = 1;
     *nt = pair ? 2 : 1;
@@ -595,6 +595,12 @@ gr_status gr_q4k_gemm(const void* w, const float* x, float* y, int B, int N, int
 }
 gr_status gr_q6k_gemm(const void* w, const float* x, float* y, int B, int N, int K, void* ws, size_t wsb, void* s) {
   return gemm_api(GR_W_Q6_K, w, x, y, B, N, K, ws, wsb, s);
+}
+gr_status gr_q5k_gemm(const void* w, const float* x, float* y, int B, int N, int K, void* ws, size_t wsb, void* s) {
+  return gemm_api(GR_W_Q5_K, w, x, y, B, N, K, ws, wsb, s);
+}
+gr_status gr_q8_0_gemm(const void* w, const float* x, float* y, int B, int N, int K, void* ws, size_t wsb, void* s) {
+  return gemm_api(GR_W_Q8_0, w, x, y, B, N, K, ws, wsb, s);
 }
 
 // ---------------------------------------------------------------- attention

@@ -49,6 +49,12 @@ constexpr int kQ6LoadInstr = addr::kQ6Instr;  // 16-byte loads per lane and stag
 // instructions on every path and the vmcnt waits below are exact.
 constexpr int kQ4Stage = kQ4LoadInstr * 64 * 16;  // 3072 B (2304 used)
 constexpr int kQ6Stage = kQ6LoadInstr * 64 * 16;  // 4096 B (3840 used)
+constexpr int kQ5Stage = addr::kQ5Instr * 64 * 16;  // 3072 B (2816 used)
+constexpr int kQ8Stage = addr::kQ8Instr * 64 * 16;  // 5120 B (4352 used)
+
+constexpr int stage_bytes(int wtype) {
+  return wtype == 12 ? kQ4Stage : wtype == 13 ? kQ5Stage : wtype == 8 ? kQ8Stage : kQ6Stage;
+}
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -97,6 +103,28 @@ GR_DEV void q4_issue(const TileRows& tr, const Q4Lane& ln, int sb, lds_u8* slot)
 #pragma unroll
   for (int i = 0; i < kQ4LoadInstr; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(slot + 1024 * i), 16, ln.p[i], 0, 0, 0);
+}
+
+// Q5_K and Q8_0: the aligned-format staging (gemm_addr.h), NI loads of RU units per row.
+template <int NI, int RU>
+struct AlLane {
+  u32 p[NI];  // byte offset of this lane's chunk from the tile's block address
+};
+template <int NI, int RU>
+GR_DEV AlLane<NI, RU> al_lane(const TileRows& tr, int lane) {
+  AlLane<NI, RU> l;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = addr::al_unit(lane, i, RU);
+    l.p[i] = tr.off(addr::al_row(c, RU)) + addr::al_in_block(c, RU);
+  }
+  return l;
+}
+// One load instruction of the aligned-format staging: 16 bytes per lane into slot + 1024 i.
+GR_DEV void al_issue1(const TileRows& tr, u32 p, int sb, int row_bytes, lds_u8* slot) {
+  const uint8_t* blk = tr.base + (size_t)sb * row_bytes;  // wave-uniform
+  const __amdgpu_buffer_rsrc_t rs = stage_rsrc(blk, tr, tr.end());
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)slot, 16, p, 0, 0, 0);
 }
 
 struct Q6Lane {
@@ -281,6 +309,151 @@ GR_DEV void q4_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, i
 #pragma unroll
     for (int t = 0; t < NT; ++t) slots[t] = slot_of(sb, t);
     q4_step<NT, BTN>(a, slots, b.a, sb, lane, acc);
+  };
+  pipeline_ring<KW, KA>(sb0, sb1, b0, b1, issue_w, issue_a, step);
+}
+
+// One super-block of Q5_K: Q4_K's header and nibbles with a fifth bit per weight (bit
+// 2c + high of high-bit byte l); 128 + q (q < 32) is still an exact bf16, so the sums
+// and scales are Q4_K's.
+template <int NT, int BTN>
+GR_DEV void q5_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32x4* ca, int sb, int lane,
+                    float (&acc)[NT][BTN][4]) {
+  const u32x4* xp = (const u32x4*)a.xpack;
+  const u32x4 ones = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, kg = lane >> 4;
+  const u32 M = vconst(0x43004300u);
+  u32x4 hdr[NT];
+  u32x2 qs[NT][4], qh[NT];
+  float sd[NT][8], mm[NT][8];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const lds_u8* rp = slot[t] + addr::al_lds_byte(n, 0, addr::kQ5RowUnits);  // row n's block
+    hdr[t] = *(const __attribute__((address_space(3))) u32x4*)rp;
+    qh[t] = *(const __attribute__((address_space(3))) u32x2*)(rp + 16 + 8 * kg);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qs[t][c] = *(const __attribute__((address_space(3))) u32x2*)(rp + 48 + 32 * c + 8 * kg);
+    q4_scales(hdr[t], sd[t], mm[t]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mm[t][j] = __builtin_fmaf(128.0f, sd[t][j], mm[t][j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u32x4 av[BTN];
+    f32x4 sv[BTN];
+#pragma unroll
+    for (int b = 0; b < BTN; ++b) {
+      if constexpr (BTN == 1)
+        av[b] = ca[j];
+      else
+        av[b] = xp[(((size_t)b * a.nslices) + (size_t)sb * 8 + j) * 64 + lane];
+      sv[b] = mfma_bf16_k32(av[b], ones, z4);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 bq = q5_expand(qs[t][j >> 1], qh[t], j, M);
+#pragma unroll
+      for (int b = 0; b < BTN; ++b) {
+        const f32x4 dd = mfma_bf16_k32(av[b], bq, z4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[t][b][e] = __builtin_fmaf(sd[t][j], dd[e], __builtin_fmaf(-mm[t][j], sv[b][e], acc[t][b][e]));
+      }
+    }
+  }
+}
+
+// Four bytes of row n's stage from byte offset `off` (any 2-byte-aligned offset) as one
+// dword, and the next four.
+GR_DEV u32x2 lds_8bytes(const lds_u8* row, u32 off) {
+  const u32 al = off & ~3u, sh = off & 3u;
+  const u32 d0 = *(const __attribute__((address_space(3))) u32*)(row + al);
+  const u32 d1 = *(const __attribute__((address_space(3))) u32*)(row + al + 4);
+  const u32 d2 = *(const __attribute__((address_space(3))) u32*)(row + al + 8);
+  return u32x2{__builtin_amdgcn_alignbyte(d1, d0, sh), __builtin_amdgcn_alignbyte(d2, d1, sh)};
+}
+
+constexpr u32 kNeg2304Bf16 = 0xC510C510u;  // two bf16 -2304.0
+
+// One super-block of Q8_0 (eight 34-byte blocks: fp16 d, 32 int8 codes).  A code q is
+// u - 128 with u = q ^ 0x80 = 16 h + l; the MFMA chain C = A x (-2304), then B = 128 + l,
+// then B = 2048 + 16 h (both exact bf16) returns sum a * (16 h + l - 128) = sum a * q.
+template <int NT, int BTN>
+GR_DEV void q8_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32x4* ca, int sb, int lane,
+                    float (&acc)[NT][BTN][4]) {
+  const u32x4* xp = (const u32x4*)a.xpack;
+  const u32x4 neg = {kNeg2304Bf16, kNeg2304Bf16, kNeg2304Bf16, kNeg2304Bf16};
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, kg = lane >> 4;
+  const u32 NIB = 0x000F000Fu;
+  const u32 ML = vconst(0x43004300u), MH = vconst(0x45004500u);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u32x4 av[BTN];
+    f32x4 c0[BTN];
+#pragma unroll
+    for (int b = 0; b < BTN; ++b) {
+      if constexpr (BTN == 1)
+        av[b] = ca[j];
+      else
+        av[b] = xp[(((size_t)b * a.nslices) + (size_t)sb * 8 + j) * 64 + lane];
+      c0[b] = mfma_bf16_k32(av[b], neg, z4);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const lds_u8* rp = slot[t] + addr::al_lds_byte(n, 0, addr::kQ8RowUnits);  // row n's 272 bytes
+      const float d = h2f(*(const __attribute__((address_space(3))) u16*)(rp + 34 * j));
+      const u32x2 q = lds_8bytes(rp, 34 * j + 2 + 8 * kg);
+      const u32 u0 = q.x ^ 0x80808080u, u1 = q.y ^ 0x80808080u;
+      const u32x4 bl = {(u0 & NIB) | ML, ((u0 >> 8) & NIB) | ML, (u1 & NIB) | ML, ((u1 >> 8) & NIB) | ML};
+      const u32x4 bh = {((u0 >> 4) & NIB) | MH, ((u0 >> 12) & NIB) | MH, ((u1 >> 4) & NIB) | MH,
+                        ((u1 >> 12) & NIB) | MH};
+#pragma unroll
+      for (int b = 0; b < BTN; ++b) {
+        const f32x4 dd = mfma_bf16_k32(av[b], bh, mfma_bf16_k32(av[b], bl, c0[b]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][b][e] = __builtin_fmaf(d, dd[e], acc[t][b][e]);
+      }
+    }
+  }
+}
+
+// The per-wave stream of the aligned formats (WT 13: Q5_K, 8: Q8_0).
+template <int WT, int NT, int BTN>
+GR_DEV void al_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, int sb0, int sb1, int lane,
+                    float (&acc)[NT][BTN][4]) {
+  constexpr int NI = WT == 13 ? addr::kQ5Instr : addr::kQ8Instr;
+  constexpr int RU = WT == 13 ? addr::kQ5RowUnits : addr::kQ8RowUnits;
+  constexpr int kStg = stage_bytes(WT);
+  constexpr int NA = BTN == 1 ? 8 : 1;
+  constexpr int KW = NT * NI, KA = BTN == 1 ? 8 : 0;  // VMEM instructions per issue
+  AlLane<NI, RU> ln[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ln[t] = al_lane<NI, RU>(tr[t], lane);
+  auto slot_of = [&](int sb, int t) { return ring + (((sb - sb0) & (kRing - 1)) * NT + t) * kStg; };
+  ABuf<NA> b0, b1;
+  auto issue_w = [&](int sb) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) al_issue1(tr[t], ln[t].p[i], sb, 16 * RU, slot_of(sb, t) + 1024 * i);
+    }
+  };
+  auto issue_a = [&](ABuf<NA>& b, int sb) {
+    if constexpr (BTN == 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b.a[j] = ((const u32x4*)a.xpack)[((size_t)sb * 8 + j) * 64 + lane];
+    }
+  };
+  auto step = [&](ABuf<NA>& b, int sb) {
+    lds_u8* slots[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) slots[t] = slot_of(sb, t);
+    if constexpr (WT == 13)
+      q5_step<NT, BTN>(a, slots, b.a, sb, lane, acc);
+    else
+      q8_step<NT, BTN>(a, slots, b.a, sb, lane, acc);
   };
   pipeline_ring<KW, KA>(sb0, sb1, b0, b1, issue_w, issue_a, step);
 }
@@ -480,11 +653,13 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
 
   const int sb0 = wave * a.sb_per_wave;
   const int sb1 = min(a.nsb, sb0 + a.sb_per_wave);
-  constexpr int kStage = WT == 12 ? kQ4Stage : kQ6Stage;
+  constexpr int kStage = stage_bytes(WT);
   lds_u8* ring = (lds_u8*)lds + wave * (kRing * NT * kStage);
   if (sb0 < sb1) {
     if constexpr (WT == 12)
       q4_wave<NT, BTN>(a, tr, ring, sb0, sb1, lane, acc);
+    else if constexpr (WT == 13 || WT == 8)
+      al_wave<WT, NT, BTN>(a, tr, ring, sb0, sb1, lane, acc);
     else
       q6_wave<NT, BTN, ALIGNED>(a, tr, ring, sb0, sb1, lane, acc);
   }
@@ -871,37 +1046,46 @@ struct GemmVariant {
   int waves_per_cu = 0;  // resident waves per CU that the kernel's registers allow
 };
 
+// Workgroup size of a variant: 1024 threads where the kernel fits 128 VGPRs without
+// spilling (Q5_K's NT 2 x BTN 2 does not), else 256.
+constexpr int variant_maxt(int wt, int nt, int btn) {
+  return (nt == 1 && btn <= 4) || (nt == 2 && btn == 2 && wt != 13) ? 1024 : 256;
+}
+
 template <int WT, bool AL>
 const void* variant_fn(int nt, int btn) {
   switch (nt * 100 + btn) {
-    case 101: return (const void*)gemm_kernel<WT, 1, 1, 1024, AL>;
-    case 102: return (const void*)gemm_kernel<WT, 1, 2, 1024, AL>;
-    case 104: return (const void*)gemm_kernel<WT, 1, 4, 1024, AL>;
-    case 108: return (const void*)gemm_kernel<WT, 1, 8, 256, AL>;
-    case 201: return (const void*)gemm_kernel<WT, 2, 1, 256, AL>;
-    case 202: return (const void*)gemm_kernel<WT, 2, 2, 1024, AL>;
-    case 204: return (const void*)gemm_kernel<WT, 2, 4, 256, AL>;
-    case 208: return (const void*)gemm_kernel<WT, 2, 8, 256, AL>;
+    case 101: return (const void*)gemm_kernel<WT, 1, 1, variant_maxt(WT, 1, 1), AL>;
+    case 102: return (const void*)gemm_kernel<WT, 1, 2, variant_maxt(WT, 1, 2), AL>;
+    case 104: return (const void*)gemm_kernel<WT, 1, 4, variant_maxt(WT, 1, 4), AL>;
+    case 108: return (const void*)gemm_kernel<WT, 1, 8, variant_maxt(WT, 1, 8), AL>;
+    case 201: return (const void*)gemm_kernel<WT, 2, 1, variant_maxt(WT, 2, 1), AL>;
+    case 202: return (const void*)gemm_kernel<WT, 2, 2, variant_maxt(WT, 2, 2), AL>;
+    case 204: return (const void*)gemm_kernel<WT, 2, 4, variant_maxt(WT, 2, 4), AL>;
+    case 208: return (const void*)gemm_kernel<WT, 2, 8, variant_maxt(WT, 2, 8), AL>;
     default: return nullptr;
   }
 }
 
 struct VariantTable {
-  GemmVariant v[3][2][4];  // (Q4_K, Q6_K aligned, Q6_K unaligned) x NT x log2 BTN
+  GemmVariant v[5][2][4];  // (Q4_K, Q6_K aligned, Q6_K unaligned, Q5_K, Q8_0) x NT x log2 BTN
   int cus = 256;
   VariantTable() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
                                                 hipSuccess && n > 0)
       cus = n;
-    for (int ty = 0; ty < 3; ++ty)
+    for (int ty = 0; ty < 5; ++ty)
       for (int nt = 1; nt <= 2; ++nt)
         for (int lb = 0; lb < 4; ++lb) {
           const int btn = 1 << lb;
           GemmVariant& g = v[ty][nt - 1][lb];
-          g.fn = ty == 0 ? variant_fn<12, true>(nt, btn) : ty == 1 ? variant_fn<14, true>(nt, btn)
-                                                                  : variant_fn<14, false>(nt, btn);
-          g.maxt = (nt == 1 && btn <= 4) || (nt == 2 && btn <= 2 && btn != 1) ? 1024 : 256;
+          g.fn = ty == 0   ? variant_fn<12, true>(nt, btn)
+                 : ty == 1 ? variant_fn<14, true>(nt, btn)
+                 : ty == 2 ? variant_fn<14, false>(nt, btn)
+                 : ty == 3 ? variant_fn<13, true>(nt, btn)
+                           : variant_fn<8, true>(nt, btn);
+          g.maxt = variant_maxt(ty == 0 ? 12 : ty == 3 ? 13 : ty == 4 ? 8 : 14, nt, btn);
           // registers per lane -> waves per SIMD (512 VGPRs, granule 8); without a device
           // to ask, assume the 128 that a 1024-thread workgroup requires
           int regs = 128;
@@ -923,7 +1107,7 @@ const VariantTable& variants() {
 int log2_btn(int btn) { return btn == 1 ? 0 : btn == 2 ? 1 : btn == 4 ? 2 : 3; }
 
 const GemmVariant& gemm_variant(int wtype, bool aligned, int nt, int btn) {
-  const int ty = wtype == 12 ? 0 : aligned ? 1 : 2;
+  const int ty = wtype == 12 ? 0 : wtype == 13 ? 3 : wtype == 8 ? 4 : aligned ? 1 : 2;
   return variants().v[ty][nt - 1][log2_btn(btn)];
 }
 
@@ -936,12 +1120,12 @@ GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, int nt) {
   pl.btn = actpack_tiles(B);
   pl.tiles = total_tiles;
   const int nsb = K / kQK;
-  const GemmVariant& v = gemm_variant(wtype, wtype == 12 || q6_aligned(K), nt, pl.btn);
+  const GemmVariant& v = gemm_variant(wtype, wtype != 14 || q6_aligned(K), nt, pl.btn);
   pl.maxt = v.maxt;
   const int max_waves = min(pl.maxt / 64, nsb);
   // LDS: staging rings (waves * NT * kRing slots) and the reduction (waves * NT * BTN *
   // 512 B, then the RMSNorm partial sums) share one allocation of at most kGemmLds
-  const int stage = wtype == 12 ? kQ4Stage : kQ6Stage;
+  const int stage = stage_bytes(wtype);
   auto lds_need = [&](int w) {
     return max(w * pl.nt * kRing * stage, w * pl.nt * pl.btn * 512 + kSsCap * (int)sizeof(float));
   };
@@ -973,7 +1157,7 @@ GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, int nt) {
 
 hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st) {
   if (pl.tiles <= 0) return hipSuccess;
-  const bool aligned = wtype == 12 || a.row_bytes % 16 == 0;
+  const bool aligned = wtype != 14 || a.row_bytes % 16 == 0;
   const GemmVariant& v = gemm_variant(wtype, aligned, pl.nt, pl.btn);
   if (!v.fn || v.maxt != pl.maxt || pl.waves * 64 > pl.maxt) return hipErrorInvalidValue;
   const dim3 grid(pl.tiles), block(pl.waves * 64);
@@ -991,8 +1175,8 @@ hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStre
 // ring depth by (type, NT): the deepest that fits kGemmLds with 8 waves
 constexpr int tl_ring(int wtype, int nt) { return wtype == 12 ? (nt == 1 ? 4 : 3) : (nt == 1 ? 4 : 2); }
 
-bool use_tile_loop(int groups, int K, int B) {
-  return B <= 8 && K % kQK == 0 && K / kQK <= 16 && groups >= 2 * variants().cus;
+bool use_tile_loop(int wtype, int groups, int K, int B) {
+  return (wtype == 12 || wtype == 14) && B <= 8 && K % kQK == 0 && K / kQK <= 16 && groups >= 2 * variants().cus;
 }
 
 TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K) {

@@ -47,6 +47,20 @@ constexpr int kQ4Units = 16 * kQ4RowUnits;
 constexpr int kQ6RowUnits = 15;  // 14 window units + 1 padding per Q6_K row
 constexpr int kQ6Units = 16 * kQ6RowUnits;
 
+// Formats whose 256 weights take a multiple of 16 bytes in a row (Q4_K 144 B above; Q5_K
+// 176 B; Q8_0, eight 34-byte blocks, 272 B) stage the same way: RU 16-byte units per row
+// block, unit c is row c / RU, chunk c % RU, LDS byte 16 c (row r at 16 RU r).
+constexpr int kQ5Instr = 3;       // 176 units per stage
+constexpr int kQ5RowUnits = 11;
+constexpr int kQ8Instr = 5;       // 272 units per stage
+constexpr int kQ8RowUnits = 17;
+
+GR_HD int al_unit(int lane, int i, int ru) { const int c = lane + 64 * i; return c < 16 * ru ? c : 16 * ru - 1; }
+GR_HD int al_row(int c, int ru) { return c / ru; }
+GR_HD uint32_t al_in_block(int c, int ru) { return 16u * (uint32_t)(c % ru); }
+GR_HD uint32_t al_lds_byte(int r, uint32_t b, int ru) { return 16u * (uint32_t)ru * (uint32_t)r + b; }
+GR_HD uint32_t al_lds(int lane, int i) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
+
 // Byte offset from the tile's first row of tile row r: a ragged last tile (nvalid < 16
 // rows inside the matrix) repeats its last row.
 GR_HD uint32_t row_off(int r, int nvalid, uint32_t row_bytes) {

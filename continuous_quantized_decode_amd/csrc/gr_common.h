@@ -24,7 +24,15 @@ namespace gr {
 constexpr int kPage = 16;
 constexpr int kQK = 256;  // weights per K-quant super-block
 constexpr int kQ4KBytes = 144;
+constexpr int kQ5KBytes = 176;
 constexpr int kQ6KBytes = 210;
+constexpr int kQ8SbBytes = 272;  // eight 34-byte q8_0 blocks: 256 weights of a Q8_0 row
+
+// Bytes of 256 consecutive weights of a matrix row (GGUF type ids: Q8_0 8, Q4_K 12, Q5_K
+// 13, Q6_K 14).
+constexpr int sb_bytes(int wtype) {
+  return wtype == 12 ? kQ4KBytes : wtype == 13 ? kQ5KBytes : wtype == 8 ? kQ8SbBytes : kQ6KBytes;
+}
 constexpr int kWave = 64;
 
 // Streamed loads (weights, KV pages).  Plain cached loads: a row's 128-byte lines are

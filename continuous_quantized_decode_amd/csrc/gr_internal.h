@@ -114,7 +114,7 @@ constexpr int kGemmLds = 160 * 1024;
 // The tile-loop GEMM (workgroups walk runs of tile groups, activations held in
 // registers): used when the batch is one activation tile, K is at most 16 super-blocks
 // (two per wave) and there are at least two tile groups per CU.
-bool use_tile_loop(int groups, int K, int B);
+bool use_tile_loop(int wtype, int groups, int K, int B);
 struct TlPlan {
   int waves, grid, groups_per_wg, ring;
   size_t lds;

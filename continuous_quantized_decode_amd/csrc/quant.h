@@ -39,6 +39,21 @@ GR_DEV u32x4 q4_expand(u32x2 q, bool high, u32 M = 0x43004300u) {
   return r;
 }
 
+// Q5_K: the Q4_K expansion with each weight's fifth bit (bit j of its high-bit byte for
+// sub-block j) at value 16; 128 + q (q < 32) is an exact bf16.
+GR_DEV u32x4 q5_expand(u32x2 q, u32x2 h, int j, u32 M = 0x43004300u) {
+  const u32 NIB = 0x000F000Fu, B1 = 0x00010001u;
+  const bool high = (j & 1) != 0;
+  const u32 w0 = high ? (q.x >> 4) : q.x, w1 = high ? (q.y >> 4) : q.y;
+  const u32 h0 = h.x >> j, h1 = h.y >> j;
+  u32x4 r;
+  r.x = (w0 & NIB) | ((h0 & B1) << 4) | M;
+  r.y = ((w0 >> 8) & NIB) | (((h0 >> 8) & B1) << 4) | M;
+  r.z = (w1 & NIB) | ((h1 & B1) << 4) | M;
+  r.w = ((w1 >> 8) & NIB) | (((h1 >> 8) & B1) << 4) | M;
+  return r;
+}
+
 // Scales of one Q4_K super-block header: sd[j] = d*sc[j] and dm[j] = dmin*m[j], both
 // exact in fp32 (11-bit fp16 mantissa times a 6-bit integer).
 GR_DEV void q4_scales(u32x4 hdr, float* sd, float* dm) {

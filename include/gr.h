@@ -23,8 +23,9 @@
  *  - Device-resident preconditions are documented, not checked: block-table
  *    entries of the pages a row uses lie in [0, num_pages); ctx_lens[b] <= max_ctx.
  *  - B == 0 returns GR_OK and enqueues nothing.
- *  - Weight matrices are GGUF super-block rows: row n of an N x K matrix is K/256
- *    consecutive blocks (Q4_K: 144 B, Q6_K: 210 B), rows back to back.
+ *  - Weight matrices are GGUF rows: row n of an N x K matrix is K/256 consecutive
+ *    super-blocks (Q4_K: 144 B, Q5_K: 176 B, Q6_K: 210 B), or K/32 consecutive q8_0
+ *    blocks (34 B: fp16 d, 32 int8), rows back to back.
  *    y[b][n] = sum_k W[n][k] * x[b][k].  K must be a multiple of 256.
  *  - KV pools (one K pool and one V pool per layer): page p holds 16 tokens of all
  *    KV heads; head g occupies bytes [g*HB, (g+1)*HB) of the page with
@@ -45,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GR_ABI_VERSION 5
+#define GR_ABI_VERSION 6
 
 typedef enum {
   GR_OK = 0,
@@ -61,7 +62,10 @@ typedef enum {
 
 typedef enum { GR_KV_F32 = 0, GR_KV_F16 = 1, GR_KV_Q8_0 = 2 } gr_kv_dtype;
 /* values are the GGUF tensor type ids */
-typedef enum { GR_W_Q4_K = 12, GR_W_Q6_K = 14 } gr_wtype;
+/* GGUF type ids.  Q4_K / Q6_K are the decode step's formats (Leone, What ships); Q5_K
+ * and Q8_0 weight rows are accepted by every GEMM (the tile-loop kernel stays Q4_K /
+ * Q6_K). */
+typedef enum { GR_W_Q8_0 = 8, GR_W_Q4_K = 12, GR_W_Q5_K = 13, GR_W_Q6_K = 14 } gr_wtype;
 /* NEOX rotates (v[i], v[i+D/2]); NORM rotates (v[2i], v[2i+1]) */
 typedef enum { GR_ROPE_NEOX = 0, GR_ROPE_NORM = 1 } gr_rope_style;
 
@@ -95,6 +99,10 @@ gr_status gr_q4k_gemm(const void* wblocks, const float* x, float* y, int B, int 
                       size_t ws_bytes, void* stream);
 gr_status gr_q6k_gemm(const void* wblocks, const float* x, float* y, int B, int N, int K, void* workspace,
                       size_t ws_bytes, void* stream);
+gr_status gr_q5k_gemm(const void* wblocks, const float* x, float* y, int B, int N, int K, void* workspace,
+                      size_t ws_bytes, void* stream);
+gr_status gr_q8_0_gemm(const void* wblocks, const float* x, float* y, int B, int N, int K, void* workspace,
+                       size_t ws_bytes, void* stream);
 
 /* Launch shape of one fused-dequant GEMM launch (a profiling aid: it names the
  * dispatch a counter or trace row belongs to).  rows: output rows of the launch (for

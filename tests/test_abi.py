@@ -37,7 +37,7 @@ def test_host_side_checks_without_gpu():
     """Calls that fail a host check return their status before touching the device."""
     import continuous_quantized_decode_amd as gr
     L = gr.lib()
-    assert L.gr_abi_version() == 5
+    assert L.gr_abi_version() == 6
     assert L.gr_status_str(-6) == b"max_ctx + 1 tokens exceed the block table's pages"
     assert L.gr_kv_head_bytes(2, 128) == 16 * 128 + 16 * 4 * 2
     assert L.gr_kv_head_bytes(7, 128) == -1
@@ -52,7 +52,7 @@ def test_host_side_checks_without_gpu():
     assert L.gr_decode_layer(ctypes.byref(cfg), ctypes.byref(w), p, p, 9, p, p, 9, p, 128, 1, p, 1 << 20, None) == -3
     cfg = gr.layer_cfg(256, 4, 2, 64, 768, 1e-6, 1e4, 0, 0, 0)
     assert L.gr_decode_layer(ctypes.byref(cfg), ctypes.byref(w), p, p, 9, p, p, 8, p, 128, 1, p, 1 << 20, None) == -6
-    w2 = gr.LayerWeights(*([p] * 11 + [12] * 6 + [13]))
+    w2 = gr.LayerWeights(*([p] * 11 + [12] * 6 + [11]))  # Q3_K: not a supported row format
     assert L.gr_decode_layer(ctypes.byref(cfg), ctypes.byref(w2), p, p, 9, p, p, 9, p, 128, 1, p, 1 << 20, None) == -3
     meta = gr.attn_meta(4, 2, 96, 1, 9, 9, 128)
     assert L.gr_paged_decode_attn(p, p, p, p, p, p, 1, ctypes.byref(meta), p, 4096, None) == -2

@@ -5,14 +5,16 @@ continuous_quantized_decode_amd/csrc/gemm_addr.h.  This test compiles that heade
 into a small C++ program that enumerates every tile shape, ragged last tile,
 super-block, lane and load instruction and checks that:
   * every load lies inside the weight matrix (no read before its start or past its end);
-  * Q4_K loads are 16-byte chunks inside their row block;
+  * Q4_K, Q5_K and Q8_0 loads are 16-byte chunks inside their row block (Q5_K: 176 B,
+    Q8_0: eight 34-byte blocks, 272 B, per 256 weights);
   * Q6_K loads are 16-byte aligned units starting inside [block - s16, block + 210); a
     unit may end past the matrix only inside the aligned 16 bytes that hold its end (no
     page is crossed);
   * no LDS write leaves the stage;
   * every LDS byte the compute reads (all bytes of row r's Q4_K / Q6_K block, at
     gemm_addr.h's q4_lds_byte / q6_lds_byte) holds the right byte of the matrix after
-    the stage's loads.
+    the stage's loads, and Q8_0's three-dword reads around 2-byte aligned offsets stay
+    inside the stage.
 """
 import os
 import shutil
@@ -36,10 +38,12 @@ static int fails = 0;
 int main() {
   const int nsbs[] = {1, 2, 3, 4, 5, 7, 12, 16, 48, 56, 57};
   const int rows[] = {1, 2, 15, 16, 17, 31, 33, 48};
-  for (int wt = 0; wt < 2; ++wt) {
-    const uint32_t bb = wt == 0 ? 144 : 210;
-    const int ni = wt == 0 ? kQ4Instr : kQ6Instr;
-    const int stage = (wt == 0 ? kQ4Instr : kQ6Instr) * 64 * 16;
+  // 0: Q4_K, 1: Q6_K, 2: Q5_K, 3: Q8_0
+  for (int wt = 0; wt < 4; ++wt) {
+    const uint32_t bb = wt == 0 ? 144 : wt == 1 ? 210 : wt == 2 ? 176 : 272;
+    const int ni = wt == 0 ? kQ4Instr : wt == 1 ? kQ6Instr : wt == 2 ? kQ5Instr : kQ8Instr;
+    const int ru = wt == 2 ? kQ5RowUnits : kQ8RowUnits;
+    const int stage = ni * 64 * 16;
     for (int nsb : nsbs) for (int N : rows) {
       const uint32_t row_bytes = bb * nsb;
       const uint64_t total = (uint64_t)N * row_bytes;  // the matrix starts 16-byte aligned, at 0
@@ -57,6 +61,11 @@ int main() {
                 const uint64_t blk = tile + row_off(q4_row(c), nvalid, row_bytes) + (uint64_t)sb * bb;
                 a = blk + q4_in_block(c); len = 16; lds = q4_lds(lane, i);
                 CHECK(a >= blk && a + len <= blk + bb, "q4 load leaves its row block");
+              } else if (wt >= 2) {
+                const int c = al_unit(lane, i, ru);
+                const uint64_t blk = tile + row_off(al_row(c, ru), nvalid, row_bytes) + (uint64_t)sb * bb;
+                a = blk + al_in_block(c, ru); len = 16; lds = al_lds(lane, i);
+                CHECK(a >= blk && a + len <= blk + bb, "aligned-format load leaves its row block");
               } else {
                 // exactly the kernel's arithmetic: a per-lane constant and the tile's
                 // block address, with s16 from the tile (rows of a multiple of 16 bytes)
@@ -89,7 +98,17 @@ int main() {
           // every byte the compute reads holds the right global byte
           for (int r = 0; r < 16; ++r) {
             const uint64_t blk = tile + row_off(r, nvalid, row_bytes) + (uint64_t)sb * bb;
-            if (wt == 0) {
+            if (wt >= 2) {
+              for (uint32_t b = 0; b < bb; ++b)
+                CHECK(held[al_lds_byte(r, b, ru)] == (int64_t)(blk + b), "wt %d nsb %d N %d row0 %d sb %d row %d byte %u",
+                      wt, nsb, N, row0, sb, r, b);
+              if (wt == 3)  // d at 34 j, codes at 34 j + 2 + 8 kg: dwords [off & ~3, +12)
+                for (int j = 0; j < 8; ++j)
+                  for (int kg = 0; kg < 4; ++kg) {
+                    const uint32_t off = 34 * j + 2 + 8 * kg;
+                    CHECK(off % 2 == 0 && al_lds_byte(r, (off & ~3u) + 12, ru) <= (uint32_t)stage, "q8 read past the stage");
+                  }
+            } else if (wt == 0) {
               for (int b = 0; b < 144; ++b)
                 CHECK(held[q4_lds_byte(r, b)] == (int64_t)(blk + b), "q4 nsb %d N %d row0 %d sb %d row %d byte %d", nsb, N,
                       row0, sb, r, b);

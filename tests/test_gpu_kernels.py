@@ -66,6 +66,15 @@ def test_handpacked_blocks_on_gpu(torch, gr, orc):
     gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "handpacked.json")))
     for name, e in sorted(gold.items()):
         raw = np.frombuffer(bytes.fromhex(e["hex"]), np.uint8).copy()
+        if e["format"] == "Q5_K":
+            # no dequant export for Q5_K: the block as a one-row matrix times one-hot
+            # activations (64 per call) gives its 256 weights, to fp32 rounding
+            want = orc.dequant("q5k", raw)
+            eye = np.eye(256, dtype=np.float32)
+            got = np.concatenate([host(gr.gr_q5k_gemm(dev(raw, torch), dev(eye[i:i + 64], torch), 1))[:, 0]
+                                  for i in range(0, 256, 64)])
+            assert np.abs(got - want).max() <= 1e-6 * np.abs(want).max(), name
+            continue
         fn = {"Q4_K": (gr.gr_q4k_dequant, "q4k"), "Q6_K": (gr.gr_q6k_dequant, "q6k"),
               "q8_0": (gr.gr_q8_0_dequant, "q8_0")}[e["format"]]
         got = host(fn[0](dev(raw, torch))).astype(np.float64)
@@ -97,7 +106,27 @@ GEMM_CASES = [
     (synth.W_Q6_K, 5, 9000, 1280),   # 2-byte aligned rows, waves of two and one super-blocks
     (synth.W_Q6_K, 8, 8192, 4096),
     (synth.W_Q4_K, 1, 16384, 256),   # one super-block: a single wave per workgroup
+    # Q5_K and Q8_0 rows (split-K kernel only): every batch-tile count, ragged rows
+    (synth.W_Q5_K, 1, 16, 256),
+    (synth.W_Q5_K, 2, 40, 768),
+    (synth.W_Q5_K, 4, 1000, 4096),
+    (synth.W_Q5_K, 7, 4096, 4096),
+    (synth.W_Q5_K, 13, 300, 1280),
+    (synth.W_Q5_K, 32, 256, 2048),
+    (synth.W_Q5_K, 64, 96, 14336),
+    (synth.W_Q5_K, 8, 9000, 1024),   # many tiles: no tile-loop kernel for this type
+    (synth.W_Q8_0, 1, 16, 256),
+    (synth.W_Q8_0, 3, 40, 768),
+    (synth.W_Q8_0, 4, 1000, 4096),
+    (synth.W_Q8_0, 8, 4096, 4096),
+    (synth.W_Q8_0, 9, 300, 1280),
+    (synth.W_Q8_0, 24, 256, 2048),
+    (synth.W_Q8_0, 64, 96, 14336),
+    (synth.W_Q8_0, 8, 9000, 1024),
 ]
+
+GEMM_FN = {synth.W_Q4_K: "gr_q4k_gemm", synth.W_Q6_K: "gr_q6k_gemm", synth.W_Q5_K: "gr_q5k_gemm",
+           synth.W_Q8_0: "gr_q8_0_gemm"}
 
 
 @pytest.mark.parametrize("wtype,b,n,k", GEMM_CASES)
@@ -106,7 +135,7 @@ def test_gemm_matches_oracle(torch, gr, orc, wtype, b, n, k):
     w = synth.weight(rng, wtype, n, k)
     x = rng.standard_normal((b, k), dtype=np.float32)
     say("gemm", wtype, b, n, k)
-    fn = gr.gr_q4k_gemm if wtype == synth.W_Q4_K else gr.gr_q6k_gemm
+    fn = getattr(gr, GEMM_FN[wtype])
     got = host(fn(dev(w, torch), dev(x, torch), n))
     want = orc.gemm(wtype, w, x, n, k)
     err = rel_l2(got, want)
@@ -122,6 +151,34 @@ def test_gemm_large_activation_range(torch, gr, orc):
     x = (rng.standard_normal((b, k)) * 10.0 ** rng.uniform(-6, 6, (b, k))).astype(np.float32)
     got = host(gr.gr_q4k_gemm(dev(w, torch), dev(x, torch), n))
     assert rel_l2(got, orc.gemm(synth.W_Q4_K, w, x, n, k)) <= KERNEL_TOL
+
+
+@pytest.mark.parametrize("wtype", [synth.W_Q5_K, synth.W_Q8_0])
+def test_gemm_large_activation_range_q5_q8(torch, gr, orc, wtype):
+    """The Q5_K / Q8_0 decoders under activations from 1e-6 to 1e6 (Q8_0's -2304 start and
+    the two code MFMAs cancel exactly only if every product is exact)."""
+    rng = np.random.default_rng(17 + wtype)
+    n, k, b = 80, 2048, 3
+    w = synth.weight(rng, wtype, n, k)
+    x = (rng.standard_normal((b, k)) * 10.0 ** rng.uniform(-6, 6, (b, k))).astype(np.float32)
+    got = host(getattr(gr, GEMM_FN[wtype])(dev(w, torch), dev(x, torch), n))
+    assert rel_l2(got, orc.gemm(wtype, w, x, n, k)) <= KERNEL_TOL
+
+
+@pytest.mark.parametrize("wtype", [synth.W_Q4_K, synth.W_Q5_K, synth.W_Q6_K, synth.W_Q8_0])
+def test_output_head_each_weight_type(torch, gr, orc, wtype):
+    """The output head (final RMSNorm fused into the GEMM) over a vocabulary of 5000 rows
+    in each weight format, at B = 5."""
+    rng = np.random.default_rng(23 + wtype)
+    h, vocab, b = 1024, 5000, 5
+    x = synth.activations(rng, b, h)
+    norm = (1.0 + 0.1 * rng.standard_normal(h)).astype(np.float32)
+    w = synth.weight(rng, wtype, vocab, h)
+    say("head", wtype, b, vocab, h)
+    got = host(gr.gr_output_head(dev(x, torch), dev(norm, torch), 1e-6, dev(w, torch), wtype, vocab))
+    err = rel_l2(got, orc.output_head(x, norm, 1e-6, w, wtype, vocab))
+    say("  rel_l2", err)
+    assert err <= KERNEL_TOL
 
 
 def test_gemm_rows_independent(torch, gr):

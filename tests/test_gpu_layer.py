@@ -62,6 +62,11 @@ LAYER_CASES = [
     # FFN wide enough for the tile-loop gate/up GEMM (528 gate/up tile pairs)
     dict(ctx=[40, 7, 300], batch=3, ffn=8448),
     dict(ctx=[20, 90], batch=2, ffn=8448, w_other=synth.W_Q6_K, kv_dtype=synth.KV_F16),
+    # Q5_K / Q8_0 weight rows in the fused GEMMs (QKV, O, gate/up + SwiGLU, down)
+    dict(ctx=[40, 7, 300], batch=3, w_other=synth.W_Q5_K, w_down=synth.W_Q8_0, kv_dtype=synth.KV_F16),
+    dict(ctx=[12, 0, 33, 64, 5, 17, 90, 2, 45, 9, 1, 60, 31, 16, 15, 200, 3, 8, 77, 50], batch=20,
+         w_other=synth.W_Q8_0, w_down=synth.W_Q5_K, qk_norm=True, kv_dtype=synth.KV_Q8_0),
+    dict(ctx=[40, 7], batch=2, ffn=8448, w_other=synth.W_Q8_0, w_down=synth.W_Q8_0),
 ]
 
 
