@@ -237,9 +237,12 @@ def gr_gemm_launch_shape(wtype: int, rows: int, k: int, b: int, epi: int = GEMM_
     v = [C.c_int() for _ in range(6)]
     _check("gr_gemm_launch_shape", _load().gr_gemm_launch_shape(wtype, rows, k, b, int(epi), *[C.byref(i) for i in v]))
     tl, nt, btn, maxt, grid, block = (i.value for i in v)
-    name = f"gemm_tl_kernel<{wtype}, {nt}," if tl else f"gemm_kernel<{wtype}, {nt}, {btn}, {maxt},"
-    return {"tile_loop": bool(tl), "nt": nt, "btn": btn, "maxt": maxt, "grid_threads": grid, "block_threads": block,
-            "kernel": name}
+    if tl == 2:
+        name = f"gemm_mm_kernel<{wtype},"
+    else:
+        name = f"gemm_tl_kernel<{wtype}, {nt}," if tl else f"gemm_kernel<{wtype}, {nt}, {btn}, {maxt},"
+    return {"tile_loop": tl == 1, "many_rows": tl == 2, "nt": nt, "btn": btn, "maxt": maxt, "grid_threads": grid,
+            "block_threads": block, "kernel": name}
 
 
 # --------------------------------------------------------------------------- attention

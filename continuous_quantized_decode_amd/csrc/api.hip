@@ -120,9 +120,11 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     GemmArgs a{};
     int j = i, n = 0, tiles = 0, all_tiles = 0;
     for (int q = i; q < nmat && types[q] == types[i]; ++q) all_tiles += (rows[q] + 15) / 16;
-    // many tiles and a plain store: the tile-loop kernel (one tile per group)
-    const bool tl = ep.kind == kEpiStore && use_tile_loop(types[i], all_tiles, K, B);
-    const int group = tl ? 1 : gemm_group(all_tiles);
+    // many rows: the 2-D tiled kernel; many tiles and a plain store: the tile-loop
+    // kernel (one tile per group)
+    const bool mm = use_mm(B);
+    const bool tl = !mm && ep.kind == kEpiStore && use_tile_loop(types[i], all_tiles, K, B);
+    const int group = mm ? mm_group_tiles(false) : tl ? 1 : gemm_group(all_tiles);
     while (j < nmat && types[j] == types[i]) {
       a.w[n] = (const uint8_t*)w[j];
       a.seg_rows[n] = rows[j];
@@ -163,7 +165,9 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
       zeroed = true;
     }
     hipError_t e;
-    if (tl) {
+    if (mm) {
+      e = launch_gemm_mm(wt, tiles, a, st);
+    } else if (tl) {
       a.tl_groups = tiles;
       e = launch_gemm_tl(wt, 1, plan_gemm_tl(wt, 1, tiles, K), a, st);
     } else {
@@ -202,6 +206,7 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   a.pack_nslices = nslices_of(out.kind, F);
   a.zero_ptr = zero_ptr;
   a.zero_n = zero_n;
+  if (use_mm(B)) return launch_gemm_mm(wtype, (tiles + mm_group_tiles(true) - 1) / mm_group_tiles(true), a, st);
   if (use_tile_loop(wtype, tiles, K, B)) {
     a.tl_groups = tiles;
     return launch_gemm_tl(wtype, 2, plan_gemm_tl(wtype, 2, tiles, K), a, st);
@@ -229,8 +234,8 @@ LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan&
   L.op = carve_pack2(c, B, qd);
   L.ap = carve_pack2(c, B, cfg->ffn);
   L.qkv = c.take<float>((size_t)B * (qd + 2 * kvd) * 4);
-  L.ss_attn = c.take<float>((size_t)kSsCap * 4);  // [ss_slots(B)][B]
-  L.ss_ffn = c.take<float>((size_t)kSsCap * 4);
+  L.ss_attn = c.take<float>(ss_floats(B) * 4);  // [ss_slots(B)][B]
+  L.ss_ffn = c.take<float>(ss_floats(B) * 4);
   const size_t units = (size_t)B * cfg->n_q_heads * ap.max_splits;
   L.o_part = c.take<float>(units * cfg->head_dim * 4);
   L.m_part = c.take<float>(units * 4);
@@ -539,9 +544,21 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
                                int* maxt, int* grid_threads, int* block_threads) {
   if (!tile_loop || !nt || !btn || !maxt || !grid_threads || !block_threads) return GR_ERR_NULL;
   if (!wtype_ok(wtype)) return GR_ERR_DTYPE;
-  if (rows <= 0 || K <= 0 || K % kQK || B <= 0 || B > 64 || epi < 0 || epi > 2) return GR_ERR_SHAPE;
+  if (rows <= 0 || K <= 0 || K % kQK || B <= 0 || B > kMaxRows || epi < 0 || epi > 2) return GR_ERR_SHAPE;
+  if (use_mm(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
   const int tiles = (rows + 15) / 16;
   const bool pair = epi == 2;
+  if (use_mm(B)) {  // the many-row kernel: 512 threads, activation tile groups x weight tile groups
+    const int gt = mm_group_tiles(pair);
+    const int mb = wtype == GR_W_Q4_K ? 4 : 2;
+    *tile_loop = 2;
+    *nt = 2;
+    *btn = mb;
+    *maxt = 512;
+    *block_threads = 512;
+    *grid_threads = (actpack_tiles(B) / mb) * ((tiles + gt - 1) / gt) * 512;
+    return GR_OK;
+  }
   // the choices gemm_run and gemm_swiglu make
   if ((pair || epi == 0) && use_tile_loop(wtype, tiles, K, B)) {
     const TlPlan tp = plan_gemm_tl(wtype, pair ? 2 : 1, tiles, K);
@@ -570,7 +587,8 @@ static gr_status gemm_api(int wtype, const void* w, const float* x, float* y, in
   if (B < 0 || N < 0 || K < 0) return GR_ERR_SHAPE;
   if (B == 0 || N == 0) return GR_OK;
   if (!w || !x || !y) return GR_ERR_NULL;
-  if (B > 64 || K == 0 || K % 256 || K > 65536) return GR_ERR_SHAPE;
+  if (B > kMaxRows || K == 0 || K % 256 || K > 65536) return GR_ERR_SHAPE;
+  if (use_mm(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
   if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return GR_ERR_ALIGN;
   if (!ws || ws_bytes < gr_gemm_workspace_size(B, N, K) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
   gr_status s = check_device();
@@ -706,7 +724,12 @@ static gr_status check_layer_call(const gr_layer_cfg* c, const gr_layer_weights*
   if (s != GR_OK) return s;
   s = check_layer_w(c, w);
   if (s != GR_OK) return s;
-  if (B < 0 || T < 1 || (int64_t)B * T > 64) return GR_ERR_SHAPE;
+  if (B < 0 || T < 1 || (int64_t)B * T > kMaxRows) return GR_ERR_SHAPE;
+  if (use_mm(B * T)) {
+    const int ts[7] = {w->tq, w->tk, w->tv, w->to, w->tgate, w->tup, w->tdown};
+    for (int t : ts)
+      if (!mm_supported(t)) return GR_ERR_DTYPE;
+  }
   if (!k_pages || !v_pages || !x || !bt) return GR_ERR_NULL;
   if (row_pos ? !row_seq : !ctx) return GR_ERR_NULL;
   if (num_pages <= 0 || max_blocks <= 0 || max_ctx < 0) return GR_ERR_SHAPE;
@@ -740,7 +763,7 @@ size_t gr_output_head_workspace_size(int B, int hidden, int vocab) {
   (void)vocab;
   Carver c(nullptr);
   carve_pack2(c, B, hidden);
-  c.take<float>((size_t)B * 4);
+  c.take<float>(ss_floats(B) * 4);
   return c.off + 256;
 }
 
@@ -750,14 +773,15 @@ gr_status gr_output_head(const float* x, const float* norm, float eps, const voi
   if (!wtype_ok(wtype)) return GR_ERR_DTYPE;
   if (B == 0 || vocab == 0) return GR_OK;
   if (!x || !norm || !w || !logits) return GR_ERR_NULL;
-  if (B > 64 || hidden % 256 || hidden > 65536) return GR_ERR_SHAPE;
+  if (B > kMaxRows || hidden % 256 || hidden > 65536) return GR_ERR_SHAPE;
+  if (use_mm(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(logits, 4) || !aligned(norm, 4)) return GR_ERR_ALIGN;
   if (!ws || ws_bytes < gr_output_head_workspace_size(B, hidden, vocab) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
   gr_status s = check_device();
   if (s != GR_OK) return s;
   Carver c(ws);
   const Pack2 xp = carve_pack2(c, B, hidden);
-  float* ss = c.take<float>((size_t)B * 4);
+  float* ss = c.take<float>(ss_floats(B) * 4);
   hipStream_t st = (hipStream_t)stream;
   Kinds k;
   k.add(wtype);
@@ -805,6 +829,7 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
   }
   if (head_w) {
     if (!wtype_ok(head_wtype)) return GR_ERR_DTYPE;
+    if (use_mm(B * T) && !mm_supported(head_wtype)) return GR_ERR_DTYPE;
     if (!head_norm || !logits) return GR_ERR_NULL;
     if (vocab <= 0) return GR_ERR_SHAPE;
     if (!aligned(head_w, 16) || !aligned(head_norm, 4) || !aligned(logits, 4)) return GR_ERR_ALIGN;
@@ -812,7 +837,7 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
   if (n_layers == 0) {
     gr_status s = check_layer_cfg(c);
     if (s != GR_OK) return s;
-    if (B < 0 || T < 1 || (int64_t)B * T > 64) return GR_ERR_SHAPE;
+    if (B < 0 || T < 1 || (int64_t)B * T > kMaxRows) return GR_ERR_SHAPE;
   }
   if (probe && probe->stage >= 0) {
     if (!probe->ev_begin || !probe->ev_end) return GR_ERR_NULL;
@@ -885,7 +910,7 @@ gr_status gr_decode_stack_probed(const gr_layer_cfg* c, const gr_layer_weights* 
 
 size_t gr_verify_stack_workspace_size(const gr_layer_cfg* c, int B, int T, int max_ctx, int vocab) {
   (void)vocab;
-  if (B <= 0 || T <= 0 || (int64_t)B * T > 64) return 0;
+  if (B <= 0 || T <= 0 || (int64_t)B * T > kMaxRows) return 0;
   return layer_ws_bytes(c, B, T, max_ctx);
 }
 
@@ -903,7 +928,7 @@ gr_status gr_verify_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
 
 size_t gr_mixed_stack_workspace_size(const gr_layer_cfg* c, int rows, int max_pos, int vocab) {
   (void)vocab;
-  if (rows <= 0 || rows > 64 || max_pos < 0) return 0;
+  if (rows <= 0 || rows > kMaxRows || max_pos < 0) return 0;
   return layer_ws_bytes(c, rows, 1, max_pos);
 }
 

@@ -460,6 +460,27 @@ GR_DEV void al_wave(const GemmArgs& a, const TileRows (&tr)[NT], lds_u8* ring, i
 
 constexpr u32 kNeg160Bf16 = 0xC320C320u;  // two bf16 -160.0
 
+// Row n's Q6_K super-block from a staged window (lane group kg's quant dwords, the
+// scales and d).  The window holds block byte b at q6_lds_byte(n, b, s16): the field at
+// block byte C (a multiple of 4) is the dword pair at q6_lds_byte(n, C, s16 & 12)
+// shifted right by s16 & 3 bytes.
+GR_DEV void q6_load_lds(const lds_u8* slot, u32 s16, int n, int kg, Q6Regs& w) {
+  const u32 sh = s16 & 3u;  // bytes (alignbyte's shift operand counts bytes)
+  const lds_u8* rs = slot + addr::q6_lds_byte(n, 0, s16 & 12u);
+  const lds_u8* rp = rs + 4 * kg;
+#pragma unroll
+  for (int hu = 0; hu < 4; ++hu) {
+    const int h = hu >> 1, u = hu & 1;
+    const int ca = 64 * h + 16 * u, cb = ca + 32, cq = 128 + 32 * h + 16 * u;
+    w.part[hu].a = lds_pair(rp + ca, rp + ca + 4, sh);
+    w.part[hu].b = lds_pair(rp + cb, rp + cb + 4, sh);
+    w.part[hu].q = lds_pair(rp + cq, rp + cq + 4, sh);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w.sc[i] = lds_pair(rs + 192 + 4 * i, rs + 196 + 4 * i, sh);
+  w.d = (u16)(lds_pair(rs + 208, rs + 212, sh) & 0xFFFFu);
+}
+
 // One super-block of Q6_K.  Per 16-weight sub-block: C = A x (-160) gives -160 * S
 // (S the activation sums), and the quant MFMA accumulates onto it, so the MFMA returns
 // D - 160 S = sum a * (q - 32) with no vector work; the scale is one FMA per row.
@@ -473,26 +494,7 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&s1
   const u32 E = vconst(0x43434343u);
   Q6Regs w[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    // row n's window holds block byte b at q6_lds_byte(n, b, s16): the field at block
-    // byte C (a multiple of 4) is the dword pair at q6_lds_byte(n, C, s16 & 12) shifted
-    // right by s16 & 3 bytes
-    const u32 s16 = s16reg[t];
-    const u32 sh = s16 & 3u;  // bytes (alignbyte's shift operand counts bytes)
-    const lds_u8* rs = slot[t] + addr::q6_lds_byte(n, 0, s16 & 12u);
-    const lds_u8* rp = rs + 4 * kg;
-#pragma unroll
-    for (int hu = 0; hu < 4; ++hu) {
-      const int h = hu >> 1, u = hu & 1;
-      const int ca = 64 * h + 16 * u, cb = ca + 32, cq = 128 + 32 * h + 16 * u;
-      w[t].part[hu].a = lds_pair(rp + ca, rp + ca + 4, sh);
-      w[t].part[hu].b = lds_pair(rp + cb, rp + cb + 4, sh);
-      w[t].part[hu].q = lds_pair(rp + cq, rp + cq + 4, sh);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[t].sc[i] = lds_pair(rs + 192 + 4 * i, rs + 196 + 4 * i, sh);
-    w[t].d = (u16)(lds_pair(rs + 208, rs + 212, sh) & 0xFFFFu);
-  }
+  for (int t = 0; t < NT; ++t) q6_load_lds(slot[t], s16reg[t], n, kg, w[t]);
   float dsc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) dsc[t] = h2f(w[t].d);
@@ -760,6 +762,29 @@ GR_DEV u32 bf16_dup(float v) {
   return (b >> 16) | (b & 0xFFFF0000u);
 }
 
+// Row n's Q4_K super-block from its staged bytes (rp): the quants of lane group kg, the
+// scales sd[j] = d sc_j, dmin, and the mins m_2kg, m_2kg+1 as the B operand of a K = 16
+// MFMA (each repeated for a bf16 hi / lo pair of the A operand).
+GR_DEV void q4_load_tl(const lds_u8* rp, int kg, Q4Regs& w, float (&sd)[8], float& dmin, u32x2& bm) {
+  w.hdr = *(const __attribute__((address_space(3))) u32x4*)rp;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) w.qs[c] = *(const __attribute__((address_space(3))) u32x2*)(rp + 16 + 32 * c + 8 * kg);
+  const u32 h0 = w.hdr.x, s0 = w.hdr.y, s1 = w.hdr.z, s2 = w.hdr.w;
+  const float d = h2f((u16)(h0 & 0xFFFF));
+  dmin = h2f((u16)(h0 >> 16));
+  const u32 sc_lo = s0 & 0x3F3F3F3Fu, sc_hi = (s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sd[j] = d * (float)((sc_lo >> (8 * j)) & 0xFF);
+    sd[j + 4] = d * (float)((sc_hi >> (8 * j)) & 0xFF);
+  }
+  // mins m_2kg and m_2kg+1: bytes 2(kg & 1) and 2(kg & 1) + 1 of the low (j < 4) or
+  // high (j >= 4) mins word
+  const u32 m_lo = s1 & 0x3F3F3F3Fu, m_hi = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
+  const u32 mw = (kg < 2 ? m_lo : m_hi) >> (16 * (kg & 1));
+  bm = u32x2{bf16_dup((float)(mw & 0xFF)), bf16_dup((float)((mw >> 8) & 0xFF))};
+}
+
 // One Q4_K super-block in the tile-loop kernel.  The wave's activation slice is fixed,
 // so the sums S_j of its 32-weight sub-blocks come precomputed (aS: the K = 16 MFMA
 // A operand holding S_2g and S_2g+1 of row l % 16 as bf16 hi/lo pairs).  Each
@@ -778,26 +803,7 @@ GR_DEV void q4_step_tl(lds_u8* const (&slot)[NT], const u32x4 (&ca)[8], u32x2 aS
   float sd[NT][8], dmin[NT];
   u32x2 bm[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const lds_u8* rp = slot[t] + addr::q4_lds_byte(n, 0);  // row n's block
-    w[t].hdr = *(const __attribute__((address_space(3))) u32x4*)rp;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) w[t].qs[c] = *(const __attribute__((address_space(3))) u32x2*)(rp + 16 + 32 * c + 8 * kg);
-    const u32 h0 = w[t].hdr.x, s0 = w[t].hdr.y, s1 = w[t].hdr.z, s2 = w[t].hdr.w;
-    const float d = h2f((u16)(h0 & 0xFFFF));
-    dmin[t] = h2f((u16)(h0 >> 16));
-    const u32 sc_lo = s0 & 0x3F3F3F3Fu, sc_hi = (s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sd[t][j] = d * (float)((sc_lo >> (8 * j)) & 0xFF);
-      sd[t][j + 4] = d * (float)((sc_hi >> (8 * j)) & 0xFF);
-    }
-    // mins m_2kg and m_2kg+1: bytes 2(kg & 1) and 2(kg & 1) + 1 of the low (j < 4) or
-    // high (j >= 4) mins word
-    const u32 m_lo = s1 & 0x3F3F3F3Fu, m_hi = ((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u);
-    const u32 mw = (kg < 2 ? m_lo : m_hi) >> (16 * (kg & 1));
-    bm[t] = u32x2{bf16_dup((float)(mw & 0xFF)), bf16_dup((float)((mw >> 8) & 0xFF))};
-  }
+  for (int t = 0; t < NT; ++t) q4_load_tl(slot[t] + addr::q4_lds_byte(n, 0), kg, w[t], sd[t], dmin[t], bm[t]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const f32x4 cj = mfma_bf16_k32(ca[j], neg128, z4);
@@ -1035,6 +1041,293 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
+// Many-row kernel (more than 64 rows: prompt chunks, long verification runs).  The
+// skinny kernels above read every activation fragment once per weight tile, which is
+// cheap for a few rows and dominates for hundreds.  Here a workgroup owns a 2-D output
+// tile: MB activation tiles (8 rows each) x 16 weight tiles (16 rows each), with 8
+// waves; wave w owns weight tiles 2w and 2w + 1 (SwiGLU: gate and up tile w) for all MB
+// activation tiles, so each activation fragment read from LDS feeds two MFMAs and each
+// expanded weight fragment feeds MB.  Per super-block the MB tiles' activation
+// fragments are staged in LDS once for all waves (one workgroup barrier per
+// super-block), and each wave streams its own two weight tiles through a private
+// two-slot ring.  The whole K accumulates in registers (no split-K, no reduction).
+//
+// Q4_K arithmetic is the tile-loop kernel's: C_j = A_j x (-128) starts each sub-block's
+// quant MFMA, so it returns sum a q; the mins term is one K = 16 MFMA per tile pair and
+// super-block, its A operand the sub-block sums of each MFMA row, which an MFMA of a
+// ones matrix against the activation fragment (passed as the B operand: the two
+// operand layouts hold the same registers) returns already indexed by row.
+// Q6_K arithmetic is q6_step's.
+
+constexpr int kMmWaves = 8, kMmNT = 2;
+constexpr int mm_mb(int wtype) { return wtype == 12 ? 4 : 2; }  // activation tiles per workgroup
+constexpr int mm_wstage(int wtype) { return wtype == 12 ? kQ4Stage : kQ6Stage; }
+// LDS: two activation stages (MB tiles x 8 fragments of 1 KB) and every wave's
+// two-slot ring of its two weight tiles (Q4_K: 64 + 96 KB; Q6_K: 32 + 128 KB)
+constexpr size_t mm_lds(int wtype) {
+  return (size_t)2 * mm_mb(wtype) * 8 * 1024 + (size_t)kMmWaves * 2 * kMmNT * mm_wstage(wtype);
+}
+static_assert(mm_lds(12) <= (size_t)kGemmLds && mm_lds(14) <= (size_t)kGemmLds, "many-row LDS");
+
+template <int BT>
+GR_DEV void q4_step_mm(const lds_u8* as, lds_u8* const (&slot)[kMmNT], int lane, float (&acc)[kMmNT][BT][4]) {
+  constexpr int NT = kMmNT;
+  const u32x4 neg128 = {kNeg128Bf16, kNeg128Bf16, kNeg128Bf16, kNeg128Bf16};
+  const u32x4 ones = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, kg = lane >> 4;
+  const u32 M = vconst(0x43004300u);
+  Q4Regs w[NT];
+  float sd[NT][8], dmin[NT];
+  u32x2 bm[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) q4_load_tl(slot[t] + addr::q4_lds_byte(n, 0), kg, w[t], sd[t], dmin[t], bm[t]);
+  float se[BT], so[BT];  // S_2kg and S_2kg+1 of MFMA row l % 16
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u32x4 av[BT];
+    f32x4 cj[BT];
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      av[b] = *(const __attribute__((address_space(3))) u32x4*)(as + (b * 8 + j) * 1024 + lane * 16);
+      cj[b] = mfma_bf16_k32(av[b], neg128, z4);
+      const f32x4 st = mfma_bf16_k32(ones, av[b], z4);  // every element: S_j of row l % 16
+      if (j == 2 * kg) se[b] = st[0];
+      if (j == 2 * kg + 1) so[b] = st[0];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 bq = q4_expand(w[t].qs[j >> 1], (j & 1) != 0, M);
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        const f32x4 dd = mfma_bf16_k32(av[b], bq, cj[b]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][b][e] = __builtin_fmaf(sd[t][j], dd[e], acc[t][b][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+    u16 h0, l0, h1, l1;
+    split_bf16(se[b], h0, l0);
+    split_bf16(so[b], h1, l1);
+    const u32x2 aS = {(u32)h0 | ((u32)l0 << 16), (u32)h1 | ((u32)l1 << 16)};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 corr = mfma_bf16_k16(aS, bm[t], z4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][b][e] = __builtin_fmaf(-dmin[t], corr[e], acc[t][b][e]);
+    }
+  }
+}
+
+template <int BT>
+GR_DEV void q6_step_mm(const lds_u8* as, lds_u8* const (&slot)[kMmNT], const u32 (&s16)[kMmNT], int lane,
+                       float (&acc)[kMmNT][BT][4]) {
+  constexpr int NT = kMmNT;
+  const u32x2 neg160 = {kNeg160Bf16, kNeg160Bf16};
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, kg = lane >> 4;
+  const u32 E = vconst(0x43434343u);
+  Q6Regs w[NT];
+  float dsc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    q6_load_lds(slot[t], s16[t], n, kg, w[t]);
+    dsc[t] = h2f(w[t].d);
+  }
+#pragma unroll
+  for (int hu = 0; hu < 4; ++hu) {
+    const int h = hu >> 1, u = hu & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sub = 8 * h + 2 * r + u;  // 16-weight sub-block within the super-block
+      u32x2 av[BT];
+      f32x4 cs[BT];
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        const u32x4 pr = *(const __attribute__((address_space(3))) u32x4*)(as + (b * 8 + (sub >> 1)) * 1024 + lane * 16);
+        av[b] = (sub & 1) ? u32x2{pr.z, pr.w} : u32x2{pr.x, pr.y};
+        cs[b] = mfma_bf16_k16(av[b], neg160, z4);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x2 bq = q6_expand(w[t].part[hu], r, E);
+        const float sd = dsc[t] * (float)(int)(int8_t)((w[t].sc[sub >> 2] >> (8 * (sub & 3))) & 0xFF);
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          const f32x4 dd = mfma_bf16_k16(av[b], bq, cs[b]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][b][e] = __builtin_fmaf(sd, dd[e], acc[t][b][e]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Grid: mtiles * ngroups workgroups (mtiles = activation tiles / MB; ngroups: groups of
+// 16 weight tiles per matrix segment, or of 8 gate/up tile pairs), 512 threads.
+// a.seg_tile_off counts groups.  a.tl_groups carries mtiles.
+template <int WT, bool ALIGNED>
+__global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
+  constexpr int MB = mm_mb(WT), BT = MB, NT = kMmNT;
+  constexpr int kW = mm_wstage(WT);
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  lds_u8* abuf = (lds_u8*)lds;                                                   // [2][MB * 8][1 KB]
+  lds_u8* ring = (lds_u8*)lds + 2 * MB * 8 * 1024 + wave * (2 * NT * kW);         // [2][NT][kW]
+
+  if (a.zero_ptr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.f;
+
+  // workgroup -> (activation tile group, weight tile group); on a grid that is a
+  // multiple of 8, consecutive groups of weight tiles go to one XCD (workgroups are
+  // dealt to the 8 XCDs round-robin), so the activation tiles sharing a weight tile
+  // meet in that XCD's L2
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int lg = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int mtiles = a.tl_groups;
+  const int mt = lg % mtiles, ng = lg / mtiles;
+  int seg = 0;
+  if (a.epi != kEpiSwiGLU)
+    while (seg + 1 < a.nseg && ng >= a.seg_tile_off[seg + 1]) ++seg;
+  const int local = ng - (a.epi == kEpiSwiGLU ? 0 : a.seg_tile_off[seg]);
+  // this wave's tiles: SwiGLU tile t = 0 gate, 1 up, both at column tile local * 8 + wave
+  int lt[NT];
+  TileRows tr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int sg = a.epi == kEpiSwiGLU ? t : seg;
+    lt[t] = a.epi == kEpiSwiGLU ? local * kMmWaves + wave : local * (kMmWaves * NT) + wave * NT + t;
+    int ltc = lt[t];
+    if (ltc * 16 >= a.seg_rows[sg]) ltc = (a.seg_rows[sg] - 1) / 16;  // past the matrix: re-read, store nothing
+    tr[t] = TileRows{a.w[sg] + (size_t)ltc * 16 * a.row_bytes, a.seg_rows[sg] - ltc * 16, (u32)a.row_bytes};
+  }
+
+  // activation staging: fragment f = b * 8 + j (1 KB) of stage sb is tile (mt * MB + b),
+  // slice 8 sb + j; wave w loads fragments w, w + 8, ...
+  const int tile_kb = a.nsb * 8;  // KB per activation tile (K / 32 fragments of 1 KB)
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)a.xpack + (size_t)mt * MB * tile_kb * 1024), 0, MB * tile_kb * 1024, kBufDword3);
+  Q4Lane l4[NT];
+  Q6Lane l6[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if constexpr (WT == 12)
+      l4[t] = q4_lane(tr[t], lane);
+    else
+      l6[t] = q6_lane(tr[t], lane);
+  }
+  auto issue = [&](int sb) {
+    lds_u8* as = abuf + (sb & 1) * (MB * 8 * 1024);
+#pragma unroll
+    for (int f = wave; f < MB * 8; f += kMmWaves) {
+      const int b = f >> 3, j = f & 7;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lptr_t)(as + f * 1024), 16,
+                                               (u32)((b * tile_kb + sb * 8 + j) * 1024 + lane * 16), 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      lds_u8* slot = ring + ((sb & 1) * NT + t) * kW;
+      if constexpr (WT == 12)
+        q4_issue(tr[t], l4[t], sb, slot);
+      else
+        q6_issue<ALIGNED>(tr[t], l6[t], sb, slot);
+    }
+  };
+
+  float acc[NT][BT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][b][e] = 0.f;
+
+  issue(0);
+  for (int sb = 0; sb < a.nsb; ++sb) {
+    // only stage sb's loads are outstanding: once every wave has seen its own land, the
+    // stage is complete, and every wave is done with stage sb - 1, whose slots the next
+    // issue reuses
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (sb + 1 < a.nsb) issue(sb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_u8* slots[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) slots[t] = ring + ((sb & 1) * NT + t) * kW;
+    const lds_u8* as = abuf + (sb & 1) * (MB * 8 * 1024);
+    if constexpr (WT == 12) {
+      q4_step_mm<BT>(as, slots, lane, acc);
+    } else {
+      u32 s16[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        s16[t] = addr::q6_s16((u32)(uintptr_t)(tr[t].base + (size_t)sb * kQ6KBytes) + tr[t].off(n));
+      q6_step_mm<BT>(as, slots, s16, lane, acc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // epilogue: lane (n, g) holds rows 8 b' + 2 g and 8 b' + 2 g + 1 (b' the activation
+  // tile) of column n of each of its tiles
+  const int rows0 = a.seg_rows[a.epi == kEpiSwiGLU ? 0 : seg];
+  const int col0 = a.epi == kEpiSwiGLU ? 0 : a.seg_col_off[seg];
+#pragma unroll
+  for (int b = 0; b < BT; ++b) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * (mt * MB + b) + 2 * g + h;
+      const bool row_ok = row < a.B;
+      float rs = 1.0f;
+      if (a.ss && row_ok) {
+        float ssv = 0.f;
+        for (int s = 0; s < a.ss_slots; ++s) ssv += a.ss[s * a.B + row];
+        rs = 1.0f / sqrtf(ssv * a.inv_k + a.eps);
+      }
+      if (a.epi == kEpiSwiGLU) {
+        const int col = lt[0] * 16 + n;
+        if (row_ok && col < rows0) {
+          const float gv = rs * (acc[0][b][2 * h] + acc[0][b][2 * h + 1]);
+          const float uv = rs * (acc[1][b][2 * h] + acc[1][b][2 * h + 1]);
+          actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, row, col, gv / (1.0f + expf(-gv)) * uv);
+        }
+      } else if (a.epi == kEpiStore) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int c = lt[t] * 16 + n;
+          if (row_ok && c < rows0) a.y[(size_t)row * a.ldy + col0 + c] = rs * (acc[t][b][2 * h] + acc[t][b][2 * h + 1]);
+        }
+      } else {
+        float sq = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int c = lt[t] * 16 + n;
+          if (row_ok && c < rows0) {
+            float* yp = a.y + (size_t)row * a.ldy + col0 + c;
+            const float xn = *yp + rs * (acc[t][b][2 * h] + acc[t][b][2 * h + 1]);
+            *yp = xn;
+            const float pv = xn * (a.gain ? a.gain[col0 + c] : 1.f);
+            if (a.pack_out) actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, row, col0 + c, pv);
+            if (a.pack_out2) actpack_put(a.pack_out2, a.pack_kind2, a.pack_nslices2, row, col0 + c, pv);
+            sq = __builtin_fmaf(xn, xn, sq);
+          }
+        }
+        // the row's sum over the wave's 32 columns: lanes with the same g differ in n
+#pragma unroll
+        for (int o = 1; o <= 8; o <<= 1) sq += __shfl_xor(sq, o, 64);
+        if (n == 0 && row_ok && a.ss_out)
+          atomicAdd(a.ss_out + (size_t)(bid % a.ss_slots) * a.B + row, sq);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // plan and launch
 
 // Kernel variants by (NT, BTN): those whose registers fit four waves per SIMD (one tile
@@ -1218,6 +1511,32 @@ hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipSt
   a.tl_groups_per_wg = pl.groups_per_wg;
   void* kargs[] = {&a};
   const hipError_t e = launch_fn(fn, dim3(pl.grid), dim3(pl.waves * 64), pl.lds, st, kargs);
+  return e != hipSuccess ? e : hipGetLastError();
+}
+
+bool use_mm(int B) { return B > kSkinnyRows; }
+bool mm_supported(int wtype) { return wtype == 12 || wtype == 14; }
+int mm_group_tiles(bool swiglu) { return swiglu ? kMmWaves : kMmWaves * kMmNT; }
+
+hipError_t launch_gemm_mm(int wtype, int groups, GemmArgs a, hipStream_t st) {
+  if (groups <= 0) return hipSuccess;
+  if (!mm_supported(wtype) || a.B <= 0 || a.ss_slots < 1) return hipErrorInvalidValue;
+  const int mtiles = actpack_tiles(a.B) / mm_mb(wtype);
+  if (mtiles * mm_mb(wtype) != actpack_tiles(a.B)) return hipErrorInvalidValue;
+  const bool aligned = wtype == 12 || a.row_bytes % 16 == 0;
+  const void* fn = wtype == 12 ? (const void*)gemm_mm_kernel<12, true>
+                               : aligned ? (const void*)gemm_mm_kernel<14, true> : (const void*)gemm_mm_kernel<14, false>;
+  static const bool lds_set = [] {
+    const void* all[] = {(const void*)gemm_mm_kernel<12, true>, (const void*)gemm_mm_kernel<14, true>,
+                         (const void*)gemm_mm_kernel<14, false>};
+    for (const void* f : all) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)lds_set;
+  a.tl_groups = mtiles;
+  void* kargs[] = {&a};
+  const hipError_t e = launch_fn(fn, dim3(mtiles * groups), dim3(kMmWaves * 64), mm_lds(wtype), st, kargs);
   return e != hipSuccess ? e : hipGetLastError();
 }
 

@@ -93,7 +93,9 @@ struct GemmArgs {
 // the memory side and hold the kernel's completion for microseconds); consumers add
 // the slots up.
 constexpr int kSsCap = 256;
-__host__ __device__ inline int ss_slots(int B) { return B <= 16 ? 16 : kSsCap / B; }
+__host__ __device__ inline int ss_slots(int B) { return B <= 16 ? 16 : B <= kSsCap ? kSsCap / B : 1; }
+// floats of one RMSNorm partial-sum buffer
+inline size_t ss_floats(int B) { return (size_t)ss_slots(B) * B > (size_t)kSsCap ? (size_t)ss_slots(B) * B : kSsCap; }
 
 struct GemmPlan {
   int nt, btn, waves, sb_per_wave, tiles, maxt;
@@ -123,9 +125,22 @@ TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K);
 hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st);
 hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);
 
+// Rows above kSkinnyRows take the many-row kernel (Q4_K and Q6_K weights; kMaxRows at
+// most): a 2-D output tile per workgroup, ngroups groups of mm_group_tiles weight tiles
+// (per matrix segment; SwiGLU: gate/up tile pairs), a.seg_tile_off counted in groups.
+constexpr int kSkinnyRows = 64;
+constexpr int kMaxRows = 512;
+bool use_mm(int B);
+bool mm_supported(int wtype);
+int mm_group_tiles(bool swiglu);
+hipError_t launch_gemm_mm(int wtype, int groups, GemmArgs a, hipStream_t st);
+
 // ---------------------------------------------------------------------- actpack
 
-__host__ __device__ inline int actpack_tiles(int B) { return B <= 8 ? 1 : B <= 16 ? 2 : B <= 32 ? 4 : 8; }
+// (above 64 rows, a multiple of 4 tiles: the many-row GEMM's activation tile groups)
+__host__ __device__ inline int actpack_tiles(int B) {
+  return B <= 8 ? 1 : B <= 16 ? 2 : B <= 32 ? 4 : B <= 64 ? 8 : ((B + 31) / 32) * 4;
+}
 
 // Bytes of an actpack for B rows of K values (16 MFMA rows of bf16 per batch tile).
 inline size_t actpack_bytes(int B, int K) { return (size_t)actpack_tiles(B) * K * 16 * 2; }

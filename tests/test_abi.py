@@ -80,6 +80,19 @@ def test_gemm_launch_shape_names_the_kernel():
     L = gr.lib()
     out = [ctypes.c_int() for _ in range(6)]
     assert L.gr_gemm_launch_shape(q4, 64, 256, 1, 3, *[ctypes.byref(o) for o in out]) == -2
+    # more than 64 rows: the many-row kernel (512 threads; groups of 16 weight tiles, or of
+    # 8 gate/up pairs, times groups of 4 (Q4_K) or 2 (Q6_K) activation tiles of 8 rows)
+    mm = gr.gr_gemm_launch_shape(q4, 14336, 4096, 264, gr.GEMM_EPI_SWIGLU)
+    assert mm["many_rows"] and not mm["tile_loop"] and mm["kernel"] == "gemm_mm_kernel<12,"
+    assert mm["block_threads"] == 512 and mm["grid_threads"] == (36 // 4) * (896 // 8) * 512
+    mm6 = gr.gr_gemm_launch_shape(q6, 4096, 14336, 65, gr.GEMM_EPI_RESIDUAL)
+    assert mm6["many_rows"] and mm6["btn"] == 2 and mm6["grid_threads"] == (12 // 2) * (256 // 16) * 512
+    assert not gr.gr_gemm_launch_shape(q4, 4096, 4096, 64)["many_rows"]
+    assert L.gr_gemm_launch_shape(13, 64, 256, 65, 0, *[ctypes.byref(o) for o in out]) == -3  # Q5_K: at most 64 rows
+    assert L.gr_gemm_launch_shape(q4, 64, 256, 513, 0, *[ctypes.byref(o) for o in out]) == -2
+    p = ctypes.c_void_p(256)
+    assert L.gr_q8_0_gemm(p, p, p, 65, 16, 256, p, 1 << 20, None) == -3
+    assert L.gr_q4k_gemm(p, p, p, 513, 16, 256, p, 1 << 20, None) == -2
 
 
 def test_sample_host_checks_without_gpu():
