@@ -259,6 +259,42 @@ def measure_weight_formats(gr, torch, wl, reps: int = 50) -> dict:
     return out
 
 
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def measure_many_rows(gr, torch, wl, rows=(128, 256, 512), reps: int = 20) -> dict:
+    """The many-row GEMM (prompt chunks) on the workload's stacked gate/up (Q4_K) and down
+    (its down type) shapes: per-call time of the C-ABI call (activation pack and GEMM;
+    events on the launch stream) and the useful rate 2 B N K / t against the dense bf16
+    MFMA peak.  (The kernel issues twice the useful MFMA work: each activation row is two
+    bf16 rows, hi and lo.)"""
+    import numpy as np
+    import synth
+    out = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, wt, n, k in (("gate_up", wl.w_other, 2 * wl.ffn, wl.hidden), ("down", wl.w_down, wl.hidden, wl.ffn)):
+        w = torch.from_numpy(synth.weight(np.random.default_rng(77 + wt), wt, n, k)).cuda()
+        fn = getattr(gr, WEIGHT_FORMATS[{8: "q8_0", 12: "q4_k", 13: "q5_k", 14: "q6_k"}[wt]][1])
+        for b in rows:
+            x = torch.randn(b, k, device="cuda")
+            y = torch.empty(b, n, device="cuda")
+            ws = gr.workspace(gr.lib().gr_gemm_workspace_size(b, n, k))
+            for _ in range(3):
+                fn(w, x, n, y, ws)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn(w, x, n, y, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            tf = 2.0 * b * n * k / (us * 1e-6) / 1e12
+            out[f"{name} {n}x{k} B={b}"] = {"us_per_call": round(us, 1), "useful_tflops": round(tf, 1),
+                                            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del w
+    return out
+
+
 def measure_verify(gr, torch, wl, ctx, sargs_layers, cfg, head, ts, steps: int, warmup: int, decode_ms: float) -> dict:
     """The speculative verification step (T tokens per sequence through the whole stack and
     the head, one graph) on the decode step's weights, with pools that have room for T new
@@ -335,7 +371,9 @@ def measure_mixed(gr, torch, wl, ctx, sargs_layers, cfg, head, chunk: int, steps
     max_pos = int(pos.max())
     x0 = torch.from_numpy(synth.activations(np.random.default_rng(55), rows, wl.hidden)).cuda()
     x = torch.empty_like(x0)
-    logits = torch.empty((rows, wl.vocab), dtype=torch.float32, device="cuda") if wl.vocab else None
+    # logits for the rows that sample: the decode rows and the chunk's last token
+    head_rows = torch.tensor(list(range(b)) + [rows - 1], dtype=torch.int32, device="cuda")
+    logits = torch.empty((b + 1, wl.vocab), dtype=torch.float32, device="cuda") if wl.vocab else None
     bt = torch.from_numpy(pm.block_table).cuda()
     sq, ps = torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda()
     ws = gr.workspace(gr.mixed_stack_workspace_size(cfg, rows, max_pos, wl.vocab))
@@ -343,7 +381,8 @@ def measure_mixed(gr, torch, wl, ctx, sargs_layers, cfg, head, chunk: int, steps
     def step():
         x.copy_(x0)
         gr.gr_mixed_stack(args, pm.num_pages, x, bt, sq, ps, max_pos, head_norm=head_norm, head_w=head_w,
-                          head_wtype=wl.w_head, vocab=wl.vocab, logits=logits, ws=ws)
+                          head_wtype=wl.w_head, vocab=wl.vocab, logits=logits, ws=ws,
+                          head_rows=head_rows if wl.vocab else None)
 
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
@@ -365,7 +404,7 @@ def measure_mixed(gr, torch, wl, ctx, sargs_layers, cfg, head, chunk: int, steps
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     assert torch.isfinite(x).all().item(), "non-finite mixed-step output"
-    return {"decode_rows": b, "prefill_rows": chunk, "ms_per_step": round(ms, 4),
+    return {"decode_rows": b, "prefill_rows": chunk, "logit_rows": b + 1, "ms_per_step": round(ms, 4),
             "tokens_per_s": round(rows / (ms * 1e-3), 1), "step_time_vs_decode": round(ms / decode_ms, 3)}
 
 
@@ -398,9 +437,12 @@ def main():
     ap.add_argument("--no-verify", action="store_true", help="skip the speculative verification step measurement")
     ap.add_argument("--verify-t", type=int, nargs="+", default=[2, 4], metavar="T",
                     help="tokens per sequence of the measured verification steps")
-    ap.add_argument("--mixed-chunk", type=int, default=56,
-                    help="prompt tokens next to the decode rows in the measured mixed step (0: skip)")
+    ap.add_argument("--mixed-chunk", type=int, nargs="+", default=[56, 256], metavar="TOKENS",
+                    help="prompt chunk sizes next to the decode rows in the measured mixed steps (0: skip)")
     ap.add_argument("--no-formats", action="store_true", help="skip the per-weight-format GEMM measurement")
+    ap.add_argument("--many-rows-only", action="store_true",
+                    help="only the many-row GEMM measurement (one JSON line)")
+    ap.add_argument("--no-many-rows", action="store_true", help="skip the many-row GEMM measurement")
     ap.add_argument("--formats-only", action="store_true",
                     help="only the per-weight-format GEMM measurement (one JSON line)")
     ap.add_argument("--sampling-only", action="store_true",
@@ -443,6 +485,9 @@ def main():
         return
     if args.formats_only:
         print(json.dumps(measure_weight_formats(gr, torch, wl)), flush=True)
+        return
+    if args.many_rows_only:
+        print(json.dumps(measure_many_rows(gr, torch, wl)), flush=True)
         return
 
     def up(a):
@@ -572,15 +617,22 @@ def main():
         log("[bench] verify: " + json.dumps(verify))
 
     mixed = None
-    if args.mixed_chunk > 0 and wl.n_layers and wl.batch + args.mixed_chunk <= 64:
-        mixed = measure_mixed(gr, torch, wl, ctx, wts, cfg, (head_norm, head_w), args.mixed_chunk, args.steps,
-                              args.warmup, ms)
-        log("[bench] mixed: " + json.dumps(mixed))
+    for chunk in args.mixed_chunk:
+        if chunk > 0 and wl.n_layers and wl.batch + chunk <= 512:
+            mixed = mixed or {}
+            mixed[str(chunk)] = measure_mixed(gr, torch, wl, ctx, wts, cfg, (head_norm, head_w), chunk, args.steps,
+                                              args.warmup, ms)
+            log(f"[bench] mixed, {chunk}-token chunk: " + json.dumps(mixed[str(chunk)]))
 
     sampling = None
     if wl.vocab and not args.no_sampling:
         sampling = measure_sampling(gr, torch, wl)
         log("[bench] sampling: " + json.dumps(sampling["cases"]))
+
+    many_rows = None
+    if not args.no_many_rows:
+        many_rows = measure_many_rows(gr, torch, wl)
+        log("[bench] many-row GEMM: " + json.dumps(many_rows))
 
     formats = None
     if not args.no_formats:
@@ -649,6 +701,7 @@ def main():
         "verify": verify,
         "mixed": mixed,
         "weight_formats": formats,
+        "many_row_gemm": many_rows,
     }
     print(json.dumps(out), flush=True)
 

@@ -109,7 +109,7 @@ def _load() -> C.CDLL:
     L.gr_mixed_stack_workspace_size.argtypes = [C.POINTER(LayerCfg), _i, _i, _i]
     L.gr_mixed_stack_workspace_size.restype = _sz
     L.gr_mixed_stack.argtypes = [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _i, C.POINTER(_p), C.POINTER(_p), _i,
-                                 _p, _p, _i, _p, _p, _i, _i, _p, _p, _i, _i, _p, _p, _sz, _p]
+                                 _p, _p, _i, _p, _p, _i, _i, _p, _p, _i, _i, _p, _i, _p, _p, _sz, _p]
     L.gr_mixed_stack.restype = _i
     L.gr_spec_accept.argtypes = [_p, _p, _i, _i, _p, _p]
     L.gr_spec_accept.restype = _i
@@ -117,7 +117,7 @@ def _load() -> C.CDLL:
     L.gr_sample_workspace_size.restype = _sz
     L.gr_sample.argtypes = [_p, _i, _i, _p, _p, _p, _p, _sz, _p]
     L.gr_sample.restype = _i
-    if L.gr_abi_version() != 6:
+    if L.gr_abi_version() != 7:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
     return L
@@ -417,16 +417,18 @@ def mixed_stack_workspace_size(cfg: LayerCfg, rows: int, max_pos: int, vocab: in
 
 
 def gr_mixed_stack(args: StackArgs, num_pages: int, x, block_table, row_seq, row_pos, max_pos: int, head_norm=None,
-                   head_w=None, head_wtype: int = W_Q6_K, vocab: int = 0, logits=None, ws=None):
-    """Rows placed by (row_seq, row_pos): decode rows, verification runs and prompt chunks in one step."""
+                   head_w=None, head_wtype: int = W_Q6_K, vocab: int = 0, logits=None, ws=None, head_rows=None):
+    """Rows placed by (row_seq, row_pos): decode rows, verification runs and prompt chunks in one step.
+    With head_rows (device int32), logits are computed for those rows only."""
     rows = x.shape[0]
     if ws is None:
         ws = workspace(mixed_stack_workspace_size(args.cfg, rows, max_pos, vocab), x.device)
+    n_head = head_rows.numel() if head_rows is not None else 0
     _check("gr_mixed_stack",
            _load().gr_mixed_stack(C.byref(args.cfg), args.weights, args.n, args.k, args.v, num_pages, _ptr(x),
                                   _ptr(block_table), block_table.shape[1], _ptr(row_seq), _ptr(row_pos), rows, max_pos,
-                                  _ptr(head_norm), _ptr(head_w), head_wtype, vocab, _ptr(logits), _ptr(ws),
-                                  ws.numel(), _stream()))
+                                  _ptr(head_norm), _ptr(head_w), head_wtype, vocab, _ptr(head_rows), n_head,
+                                  _ptr(logits), _ptr(ws), ws.numel(), _stream()))
     return x
 
 

@@ -318,10 +318,10 @@ Kinds qkv_kinds(const gr_layer_weights* w) {
 // Pack of the layer input: x * attn_norm and its sum of squares (and, for a decode
 // step, the RoPE table of its positions).
 gr_status run_input_pack(const float* x, int B, int H, const float* gain, Kinds k, const Pack2& xp, float* ss,
-                         hipStream_t st, const Probe* probe, RopeTable rope = RopeTable{}) {
+                         hipStream_t st, const Probe* probe, RopeTable rope = RopeTable{}, RowSel sel = RowSel{}) {
   return probed(probe, GR_STAGE_PACK, st, [&] {
     return check_launch(
-        launch_pack_rows(x, H, B, H, gain, k.k32 ? xp.k32 : kNoPack, k.k16 ? xp.k16 : kNoPack, ss, st, rope));
+        launch_pack_rows(x, H, B, H, gain, k.k32 ? xp.k32 : kNoPack, k.k16 ? xp.k16 : kNoPack, ss, st, rope, sel));
   });
 }
 
@@ -344,6 +344,8 @@ struct RowMap {
   int T = 1;
   const int32_t* seq = nullptr;
   const int32_t* pos = nullptr;
+  const int32_t* head_rows = nullptr;  // when set, the head runs on these n_head rows only
+  int n_head = 0;
   bool fused() const { return T == 1 && !pos; }  // one token per sequence: append inside attention
 };
 
@@ -827,9 +829,12 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
                                    max_ctx, B, T, rm.seq, rm.pos);
     if (s != GR_OK) return s;
   }
+  if (rm.head_rows && (rm.n_head < 1 || (int64_t)rm.n_head > (int64_t)B * T)) return GR_ERR_SHAPE;
+  if (rm.head_rows && !aligned(rm.head_rows, 4)) return GR_ERR_ALIGN;
+  const int head_b = rm.head_rows ? rm.n_head : B * T;
   if (head_w) {
     if (!wtype_ok(head_wtype)) return GR_ERR_DTYPE;
-    if (use_mm(B * T) && !mm_supported(head_wtype)) return GR_ERR_DTYPE;
+    if (use_mm(head_b) && !mm_supported(head_wtype)) return GR_ERR_DTYPE;
     if (!head_norm || !logits) return GR_ERR_NULL;
     if (vocab <= 0) return GR_ERR_SHAPE;
     if (!aligned(head_w, 16) || !aligned(head_norm, 4) || !aligned(logits, 4)) return GR_ERR_ALIGN;
@@ -859,7 +864,10 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
   } else if (head_w) {
     Kinds k;
     k.add(head_wtype);
-    s = run_input_pack(x, rows, c->hidden, head_norm, k, L.xp, L.ss_attn, st, probe);
+    RowSel sel;
+    sel.idx = rm.head_rows;
+    sel.src_rows = rows;
+    s = run_input_pack(x, head_b, c->hidden, head_norm, k, L.xp, L.ss_attn, st, probe, RopeTable{}, sel);
   }
   if (s != GR_OK) return s;
   for (int l = 0; l < n_layers; ++l) {
@@ -869,7 +877,7 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
     if (l + 1 < n_layers) {
       next_gain = weights[l + 1].attn_norm;
       next = qkv_kinds(&weights[l + 1]);
-    } else if (head_w) {
+    } else if (head_w && !rm.head_rows) {
       next_gain = head_norm;
       next.add(head_wtype);
     }
@@ -878,8 +886,18 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
     if (s != GR_OK) return s;
   }
   if (probe) probe->layer = 0;
+  if (head_w && rm.head_rows && n_layers > 0) {
+    // the selected rows' final states, gathered into the pack with the head's norm
+    Kinds k;
+    k.add(head_wtype);
+    RowSel sel;
+    sel.idx = rm.head_rows;
+    sel.src_rows = rows;
+    s = run_input_pack(x, head_b, c->hidden, head_norm, k, L.xp, L.ss_attn, st, probe, RopeTable{}, sel);
+    if (s != GR_OK) return s;
+  }
   if (head_w)
-    return run_head(head_w, head_wtype, logits, rows, c->hidden, vocab, c->rms_eps, L.xp, L.ss_attn, st, probe);
+    return run_head(head_w, head_wtype, logits, head_b, c->hidden, vocab, c->rms_eps, L.xp, L.ss_attn, st, probe);
   return GR_OK;
 }
 
@@ -935,12 +953,15 @@ size_t gr_mixed_stack_workspace_size(const gr_layer_cfg* c, int rows, int max_po
 gr_status gr_mixed_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers, void* const* k_pages,
                          void* const* v_pages, int num_pages, float* x, const int32_t* bt, int max_blocks,
                          const int32_t* row_seq, const int32_t* row_pos, int rows, int max_pos,
-                         const float* head_norm, const void* head_w, int head_wtype, int vocab, float* logits, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         const float* head_norm, const void* head_w, int head_wtype, int vocab,
+                         const int32_t* head_rows, int n_head_rows, float* logits, void* ws, size_t ws_bytes,
+                         void* stream) {
   if (n_layers > 0 && (!row_seq || !row_pos) && rows > 0) return GR_ERR_NULL;
   RowMap rm;
   rm.seq = row_seq;
   rm.pos = row_pos;
+  rm.head_rows = head_w ? head_rows : nullptr;
+  rm.n_head = n_head_rows;
   return decode_stack_impl(c, weights, n_layers, k_pages, v_pages, num_pages, x, bt, max_blocks, nullptr, max_pos,
                            rows, head_norm, head_w, head_wtype, vocab, logits, ws, ws_bytes, stream, nullptr, rm);
 }

@@ -182,8 +182,14 @@ struct RopeTable {
   const int32_t* row_pos = nullptr;  // when set, row b sits at row_pos[b]
   double* out = nullptr;  // NULL: none
 };
+// Optional row selection of a pack: packed row b is x row idx[b] (clamped to
+// [0, src_rows)).
+struct RowSel {
+  const int32_t* idx = nullptr;
+  int src_rows = 0;
+};
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
                             float* ss_out, hipStream_t st,  // ss_out: [ss_slots(B)][B], slot 0 the sum
-                            RopeTable rope = RopeTable{});
+                            RopeTable rope = RopeTable{}, RowSel sel = RowSel{});
 
 }  // namespace gr

@@ -16,8 +16,10 @@ constexpr int kPackThreads = 1024;
 // four consecutive columns per pass (K % 256 == 0, x rows 16-byte aligned).
 __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __restrict__ x, int ldx, int B, int K,
                                                                  const float* __restrict__ gain, PackOut o1,
-                                                                 PackOut o2, float* ss_out, RopeTable rope) {
+                                                                 PackOut o2, float* ss_out, RopeTable rope,
+                                                                 RowSel sel) {
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int src = (sel.idx && b < B) ? min(max(sel.idx[b], 0), sel.src_rows - 1) : b;
   if (rope.out && b < B && tid < rope.half_d) {
     const double inv = pow(rope.theta, -2.0 * (double)tid / (double)(2 * rope.half_d));
     double sn, cs;
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
   for (int k0 = 4 * tid; k0 < K; k0 += 4 * kPackThreads) {
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (b < B) {
-      const f32x4 xv = *(const f32x4*)(x + (size_t)b * ldx + k0);
+      const f32x4 xv = *(const f32x4*)(x + (size_t)src * ldx + k0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         ss = __builtin_fmaf(xv[i], xv[i], ss);
@@ -61,11 +63,12 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
 }
 
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
-                            float* ss_out, hipStream_t st, RopeTable rope) {
+                            float* ss_out, hipStream_t st, RopeTable rope, RowSel sel) {
   if (rope.out && (rope.half_d <= 0 || rope.half_d > kPackThreads || (!rope.ctx && !rope.row_pos)))
     return hipErrorInvalidValue;
+  if (sel.idx && sel.src_rows <= 0) return hipErrorInvalidValue;
   launch_kernel(pack_rows_kernel, dim3(8 * actpack_tiles(B)), dim3(kPackThreads), 0, st, x, ldx, B, K, gain, o1, o2,
-                ss_out, rope);
+                ss_out, rope, sel);
   return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GR_ABI_VERSION 6
+#define GR_ABI_VERSION 7
 
 typedef enum {
   GR_OK = 0,
@@ -91,9 +91,12 @@ gr_status gr_q8_0_dequant(const void* blocks, int64_t n_blocks, float* out, void
 /* ------------------------------------------------------------------ GEMM --
  * Fused-dequant skinny GEMM (Leone, intro: shared matrix operations over the
  * active rows).  x: f32 [B][K], y: f32 [B][N], both row-major, 16-byte aligned;
- * wblocks 16-byte aligned.  1 <= B <= 64, N >= 1, K % 256 == 0, K <= 65536.
- * The workspace (16-byte aligned) holds the packed activations and split-K partial
- * sums; size it with gr_gemm_workspace_size.  Weights are streamed once. */
+ * wblocks 16-byte aligned.  1 <= B <= 512, N >= 1, K % 256 == 0, K <= 65536.  Above
+ * 64 rows (prompt chunks; Leone, What ships: chunked prefill) a 2-D tiled kernel runs,
+ * for Q4_K and Q6_K only: Q5_K and Q8_0 above 64 rows return GR_ERR_DTYPE.
+ * The workspace (16-byte aligned) holds the packed activations; size it with
+ * gr_gemm_workspace_size.  Up to 64 rows the weights are streamed once; above, once
+ * per group of 32 (Q4_K) or 16 (Q6_K) rows, from L2 after the first. */
 size_t gr_gemm_workspace_size(int B, int N, int K);
 gr_status gr_q4k_gemm(const void* wblocks, const float* x, float* y, int B, int N, int K, void* workspace,
                       size_t ws_bytes, void* stream);
@@ -110,7 +113,9 @@ gr_status gr_q8_0_gemm(const void* wblocks, const float* x, float* y, int B, int
  * for a gate/up pair, rows = F).  epi: 0 plain store, 1 residual update, 2 gate/up
  * pair with SwiGLU.  Returns which kernel runs (tile_loop 0: the split-K kernel
  * gemm_kernel<type, nt, btn, maxt, aligned>; 1: the tile-loop kernel
- * gemm_tl_kernel<type, nt, aligned, ring> with btn = 1 and maxt = 512), its template
+ * gemm_tl_kernel<type, nt, aligned, ring> with btn = 1 and maxt = 512; 2: the many-row
+ * kernel gemm_mm_kernel<type, aligned>, 512 threads, nt = 2 tiles per wave and btn = 4
+ * (Q4_K) or 2 (Q6_K) activation tiles per workgroup), its template
  * parameters (16-row tiles per workgroup or group nt, 8-row batch tiles btn, launch
  * bound maxt) and the grid and workgroup sizes in threads, as launched by every entry
  * point above for these sizes.  GR_ERR_NULL for a null output pointer, GR_ERR_DTYPE for
@@ -241,7 +246,8 @@ gr_status gr_decode_stack(const gr_layer_cfg* c, const gr_layer_weights* weights
  * (the sequence's last accepted token, then T-1 proposed tokens); every token's K/V is
  * appended at its position and every token attends to the sequence's cached tokens and
  * to the step's tokens at or before it, exactly as T decode steps would.  Returns the
- * outputs in x and, with a head, logits [B*T][vocab].  B*T <= 64;
+ * outputs in x and, with a head, logits [B*T][vocab].  B*T <= 512 (above 64, Q4_K / Q6_K
+ * weights only, else GR_ERR_DTYPE);
  * max_ctx + T <= 16 * max_blocks_per_row (else GR_ERR_CAPACITY).  T = 1 is gr_decode_stack.
  * gr_spec_accept: sampled [B][T] holds the target's token after each position (for
  * example gr_sample over the verify logits, one uniform per position), draft [B][T] the
@@ -267,14 +273,19 @@ gr_status gr_spec_accept(const int32_t* sampled, const int32_t* draft, int B, in
  * prompt chunks (consecutive positions), in any row order.  Device-resident
  * preconditions (documented, not checked): the positions of a sequence's rows in one step
  * are distinct and, together with the tokens cached before the step, cover 0..max of them;
- * row_pos[r] <= max_pos.  1 <= rows <= 64; max_pos + 1 <= 16 * max_blocks_per_row (else
- * GR_ERR_CAPACITY).  logits [rows][vocab] with a head. */
+ * row_pos[r] <= max_pos.  1 <= rows <= 512 (above 64, Q4_K / Q6_K weights only, else
+ * GR_ERR_DTYPE); max_pos + 1 <= 16 * max_blocks_per_row (else
+ * GR_ERR_CAPACITY).  With a head: logits [rows][vocab], or, when head_rows (device int32
+ * [n_head_rows], 1 <= n_head_rows <= rows) is set, logits [n_head_rows][vocab] of rows
+ * head_rows[i] only (a prompt chunk needs the logits of its last token alone; indices
+ * are clamped to [0, rows)). */
 size_t gr_mixed_stack_workspace_size(const gr_layer_cfg* c, int rows, int max_pos, int vocab);
 gr_status gr_mixed_stack(const gr_layer_cfg* c, const gr_layer_weights* weights, int n_layers, void* const* k_pages,
                          void* const* v_pages, int num_pages, float* x, const int32_t* block_table,
                          int max_blocks_per_row, const int32_t* row_seq, const int32_t* row_pos, int rows, int max_pos,
-                         const float* head_norm, const void* head_w, int head_wtype, int vocab, float* logits,
-                         void* workspace, size_t ws_bytes, void* stream);
+                         const float* head_norm, const void* head_w, int head_wtype, int vocab,
+                         const int32_t* head_rows, int n_head_rows, float* logits, void* workspace, size_t ws_bytes,
+                         void* stream);
 
 /* Timing probe (profiling hook): the same launches as gr_decode_stack, except that
  * the launches of stage `probe_stage` are issued `probe_reps` times (1..1000) in a

@@ -37,7 +37,7 @@ def test_host_side_checks_without_gpu():
     """Calls that fail a host check return their status before touching the device."""
     import continuous_quantized_decode_amd as gr
     L = gr.lib()
-    assert L.gr_abi_version() == 6
+    assert L.gr_abi_version() == 7
     assert L.gr_status_str(-6) == b"max_ctx + 1 tokens exceed the block table's pages"
     assert L.gr_kv_head_bytes(2, 128) == 16 * 128 + 16 * 4 * 2
     assert L.gr_kv_head_bytes(7, 128) == -1

@@ -161,3 +161,17 @@ def test_two_chunks_fill_the_512_budget_with_head(torch, gr, orc):
     seq, pos = _mixed_rows(rng, ctx, [256, 248] + [1] * 8)
     x = synth.activations(rng, len(seq), wl.hidden)
     s.step(x, seq, pos, "tiny 512 rows")
+
+
+def test_head_on_selected_rows(torch, gr, orc):
+    """The head on the rows that need logits only (each chunk's last token and the decode
+    rows): equal to those rows of the all-rows logits.  A repeated index is allowed."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], n_layers=2, kv_dtype=synth.KV_F16, vocab=1000)
+    ctx = np.array([0, 100, 5, 60, 300, 17, 250, 33, 90, 2], np.int32)
+    s = Session(torch, gr, orc, wl, ctx, 200, True)
+    rng = np.random.default_rng(12)
+    seq, pos = _mixed_rows(rng, ctx, [200, 100] + [1] * 8)
+    need = [int(np.nonzero((seq == 0) & (pos == 199))[0][0]), int(np.nonzero((seq == 1) & (pos == 199))[0][0])]
+    need += [int(i) for i in np.nonzero(seq >= 2)[0]] + [need[0]]
+    x = synth.activations(rng, len(seq), wl.hidden)
+    s.step(x, seq, pos, "tiny 308 rows, head on 11", head_rows=need)

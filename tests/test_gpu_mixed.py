@@ -70,18 +70,20 @@ class Session:
         self.head = synth.head_weights(wl) if with_head else None
         self.hd = (dev(self.head[0], torch), dev(self.head[1], torch)) if with_head else (None, None)
 
-    def step(self, x, seq, pos, label):
+    def step(self, x, seq, pos, label, head_rows=None):
         torch, gr, wl = self.torch, self.gr, self.wl
         seq = np.asarray(seq, np.int32)
         pos = np.asarray(pos, np.int32)
         xg = dev(x, torch)
         logits = None
         if self.head is not None:
-            logits = torch.empty((len(seq), wl.vocab), dtype=torch.float32, device="cuda")
+            n_logit = len(seq) if head_rows is None else len(head_rows)
+            logits = torch.empty((n_logit, wl.vocab), dtype=torch.float32, device="cuda")
         say("mixed", label, "rows", len(seq))
+        hr = None if head_rows is None else dev(np.asarray(head_rows, np.int32), torch)
         gr.gr_mixed_stack(self.args, self.pm.num_pages, xg, self.bt, dev(seq, torch), dev(pos, torch), int(pos.max()),
                           head_norm=self.hd[0], head_w=self.hd[1], head_wtype=wl.w_head,
-                          vocab=wl.vocab if self.head is not None else 0, logits=logits)
+                          vocab=wl.vocab if self.head is not None else 0, logits=logits, head_rows=hr)
         torch.cuda.synchronize()
         outs, want_logits = self.orc.mixed_stack(wl, self.layers, self.ok, self.ov, x, self.pm.block_table, seq, pos,
                                                  head=self.head)
@@ -89,6 +91,8 @@ class Session:
         say(f"  rel_l2 x {err:.3e}")
         assert err <= tol(wl.kv_dtype), label
         if logits is not None:
+            if head_rows is not None:
+                want_logits = want_logits[np.asarray(head_rows)]
             lerr = rel_l2(host(logits), want_logits)
             say(f"  rel_l2 logits {lerr:.3e}")
             assert lerr <= tol(wl.kv_dtype), label
