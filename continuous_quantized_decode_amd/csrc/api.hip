@@ -107,6 +107,8 @@ struct Epi {
   float* ss_out = nullptr;
   float* zero_ptr = nullptr;
   int zero_n = 0;
+  float* part = nullptr;  // many-row K-split partial sums (NULL: no split)
+  size_t part_cap = 0;
 };
 
 // y (= the epilogue's destination) for up to three matrices sharing K and the input
@@ -118,11 +120,12 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
   bool zeroed = false;
   while (i < nmat) {
     GemmArgs a{};
+    const int col_begin = col;
     int j = i, n = 0, tiles = 0, all_tiles = 0;
     for (int q = i; q < nmat && types[q] == types[i]; ++q) all_tiles += (rows[q] + 15) / 16;
     // many rows: the 2-D tiled kernel; many tiles and a plain store: the tile-loop
     // kernel (one tile per group)
-    const bool mm = use_mm(B);
+    const bool mm = use_mm(types[i], B);
     const bool tl = !mm && ep.kind == kEpiStore && use_tile_loop(types[i], all_tiles, K, B);
     const int group = mm ? mm_group_tiles(false) : tl ? 1 : gemm_group(all_tiles);
     while (j < nmat && types[j] == types[i]) {
@@ -166,6 +169,10 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     }
     hipError_t e;
     if (mm) {
+      a.part = ep.part;
+      a.part_cap = ep.part_cap;
+      a.ldp = col - col_begin;
+      a.pcol0 = col_begin;
       e = launch_gemm_mm(wt, tiles, a, st);
     } else if (tl) {
       a.tl_groups = tiles;
@@ -206,7 +213,7 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   a.pack_nslices = nslices_of(out.kind, F);
   a.zero_ptr = zero_ptr;
   a.zero_n = zero_n;
-  if (use_mm(B)) return launch_gemm_mm(wtype, (tiles + mm_group_tiles(true) - 1) / mm_group_tiles(true), a, st);
+  if (use_mm(wtype, B)) return launch_gemm_mm(wtype, (tiles + mm_group_tiles(true) - 1) / mm_group_tiles(true), a, st);
   if (use_tile_loop(wtype, tiles, K, B)) {
     a.tl_groups = tiles;
     return launch_gemm_tl(wtype, 2, plan_gemm_tl(wtype, 2, tiles, K), a, st);
@@ -225,7 +232,16 @@ struct LayerBufs {
   float *o_part, *m_part, *l_part;
   double* rope;  // [B][head_dim / 2][2]: RoPE of the step's positions
   float* qbuf;   // [B][Hq][D]: roped queries when a step carries several tokens per sequence
+  float* part;   // many-row K-split partial sums (more than 64 rows), part_cap floats
+  size_t part_cap;
 };
+
+// floats of the many-row K-split partial sums for `rows` rows and outputs of `cols`
+// columns (no split above kMmSplitMaxCols columns or at 64 rows and below)
+size_t mm_part_floats(int rows, int cols) {
+  if (rows <= kMmMinRows) return 0;
+  return (size_t)kMmMaxSplit * rows * (cols < kMmSplitMaxCols ? cols : kMmSplitMaxCols);
+}
 
 LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan& ap) {
   LayerBufs L;
@@ -242,6 +258,8 @@ LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan&
   L.l_part = c.take<float>(units * 4);
   L.rope = c.take<double>((size_t)B * cfg->head_dim * sizeof(double));
   L.qbuf = c.take<float>((size_t)B * qd * 4);
+  L.part_cap = mm_part_floats(B, qd + 2 * kvd > cfg->hidden ? qd + 2 * kvd : cfg->hidden);
+  L.part = L.part_cap ? c.take<float>(L.part_cap * 4) : nullptr;
   return L;
 }
 
@@ -374,6 +392,8 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
     ep.eps = c->rms_eps;
     ep.zero_ptr = L.ss_ffn;
     ep.zero_n = ss_slots(B) * B;
+    ep.part = L.part;
+    ep.part_cap = L.part_cap;
     return check_launch(gemm_run(ws, ts, rs, 3, H, B, L.xp, ep, st));
   });
   if (s != GR_OK) return s;
@@ -438,6 +458,8 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
     ep.out1 = L.xp.of(w->tgate);
     ep.out_k = H;
     ep.ss_out = L.ss_ffn;
+    ep.part = L.part;
+    ep.part_cap = L.part_cap;
     return check_launch(gemm_run(ws, ts, rs, 1, qd, B, L.op, ep, st));
   });
   if (s != GR_OK) return s;
@@ -464,6 +486,8 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
       ep.out_k = H;
       ep.ss_out = L.ss_attn;
     }
+    ep.part = L.part;
+    ep.part_cap = L.part_cap;
     return check_launch(gemm_run(ws, ts, rs, 1, F, B, L.ap, ep, st));
   });
 }
@@ -535,10 +559,10 @@ gr_status gr_q8_0_dequant(const void* b, int64_t n, float* out, void* s) { retur
 
 // --------------------------------------------------------------------- GEMM
 size_t gr_gemm_workspace_size(int B, int N, int K) {
-  if (B <= 0 || K <= 0) return 0;
-  (void)N;
+  if (B <= 0 || K <= 0 || N < 0) return 0;
   Carver c(nullptr);
   carve_pack2(c, B, K);
+  c.take<float>(mm_part_floats(B, N) * 4);
   return c.off + 256;
 }
 
@@ -547,10 +571,10 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
   if (!tile_loop || !nt || !btn || !maxt || !grid_threads || !block_threads) return GR_ERR_NULL;
   if (!wtype_ok(wtype)) return GR_ERR_DTYPE;
   if (rows <= 0 || K <= 0 || K % kQK || B <= 0 || B > kMaxRows || epi < 0 || epi > 2) return GR_ERR_SHAPE;
-  if (use_mm(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
+  if (mm_required(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
   const int tiles = (rows + 15) / 16;
   const bool pair = epi == 2;
-  if (use_mm(B)) {  // the many-row kernel: 512 threads, activation tile groups x weight tile groups
+  if (use_mm(wtype, B)) {  // the many-row kernel: 512 threads, activation tile groups x weight tile groups
     const int gt = mm_group_tiles(pair);
     const int mb = wtype == GR_W_Q4_K ? 4 : 2;
     *tile_loop = 2;
@@ -558,7 +582,9 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
     *btn = mb;
     *maxt = 512;
     *block_threads = 512;
-    *grid_threads = (actpack_tiles(B) / mb) * ((tiles + gt - 1) / gt) * 512;
+    const int groups = (tiles + gt - 1) / gt;
+    const int split = mm_split(wtype, B, rows, K / kQK, groups, epi, mm_part_floats(B, rows));
+    *grid_threads = (actpack_tiles(B) / mb) * groups * split * 512;  // a split adds a finishing pass
     return GR_OK;
   }
   // the choices gemm_run and gemm_swiglu make
@@ -590,13 +616,15 @@ static gr_status gemm_api(int wtype, const void* w, const float* x, float* y, in
   if (B == 0 || N == 0) return GR_OK;
   if (!w || !x || !y) return GR_ERR_NULL;
   if (B > kMaxRows || K == 0 || K % 256 || K > 65536) return GR_ERR_SHAPE;
-  if (use_mm(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
+  if (mm_required(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
   if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return GR_ERR_ALIGN;
   if (!ws || ws_bytes < gr_gemm_workspace_size(B, N, K) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
   gr_status s = check_device();
   if (s != GR_OK) return s;
   Carver c(ws);
   const Pack2 xp = carve_pack2(c, B, K);
+  const size_t part_cap = mm_part_floats(B, N);
+  float* part = part_cap ? c.take<float>(part_cap * 4) : nullptr;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = launch_pack_rows(x, K, B, K, nullptr, xp.of(wtype), kNoPack, nullptr, st);
   if (e != hipSuccess) return check_launch(e);
@@ -607,6 +635,8 @@ static gr_status gemm_api(int wtype, const void* w, const float* x, float* y, in
   ep.kind = kEpiStore;
   ep.y = y;
   ep.ldy = N;
+  ep.part = part;
+  ep.part_cap = part_cap;
   return check_launch(gemm_run(ws1, ts, rs, 1, K, B, xp, ep, st));
 }
 
@@ -727,7 +757,7 @@ static gr_status check_layer_call(const gr_layer_cfg* c, const gr_layer_weights*
   s = check_layer_w(c, w);
   if (s != GR_OK) return s;
   if (B < 0 || T < 1 || (int64_t)B * T > kMaxRows) return GR_ERR_SHAPE;
-  if (use_mm(B * T)) {
+  if (mm_required(B * T)) {
     const int ts[7] = {w->tq, w->tk, w->tv, w->to, w->tgate, w->tup, w->tdown};
     for (int t : ts)
       if (!mm_supported(t)) return GR_ERR_DTYPE;
@@ -776,7 +806,7 @@ gr_status gr_output_head(const float* x, const float* norm, float eps, const voi
   if (B == 0 || vocab == 0) return GR_OK;
   if (!x || !norm || !w || !logits) return GR_ERR_NULL;
   if (B > kMaxRows || hidden % 256 || hidden > 65536) return GR_ERR_SHAPE;
-  if (use_mm(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
+  if (mm_required(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(logits, 4) || !aligned(norm, 4)) return GR_ERR_ALIGN;
   if (!ws || ws_bytes < gr_output_head_workspace_size(B, hidden, vocab) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
   gr_status s = check_device();
@@ -834,7 +864,7 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
   const int head_b = rm.head_rows ? rm.n_head : B * T;
   if (head_w) {
     if (!wtype_ok(head_wtype)) return GR_ERR_DTYPE;
-    if (use_mm(head_b) && !mm_supported(head_wtype)) return GR_ERR_DTYPE;
+    if (mm_required(head_b) && !mm_supported(head_wtype)) return GR_ERR_DTYPE;
     if (!head_norm || !logits) return GR_ERR_NULL;
     if (vocab <= 0) return GR_ERR_SHAPE;
     if (!aligned(head_w, 16) || !aligned(head_norm, 4) || !aligned(logits, 4)) return GR_ERR_ALIGN;

@@ -1188,8 +1188,11 @@ __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
   // meet in that XCD's L2
   const int G = gridDim.x, bid = blockIdx.x;
   const int lg = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  const int mtiles = a.tl_groups;
-  const int mt = lg % mtiles, ng = lg / mtiles;
+  const int mtiles = a.tl_groups, per_split = mtiles * a.tl_groups_per_wg;  // tl_groups_per_wg: weight groups
+  const int ks = lg / per_split, rem = lg - ks * per_split;
+  const int mt = rem % mtiles, ng = rem / mtiles;
+  const int nsplit = a.part ? G / per_split : 1;
+  const int sb_lo = ks * a.nsb / nsplit, sb_hi = (ks + 1) * a.nsb / nsplit;  // this workgroup's K range
   int seg = 0;
   if (a.epi != kEpiSwiGLU)
     while (seg + 1 < a.nseg && ng >= a.seg_tile_off[seg + 1]) ++seg;
@@ -1246,8 +1249,8 @@ __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[t][b][e] = 0.f;
 
-  issue(0);
-  for (int sb = 0; sb < a.nsb; ++sb) {
+  issue(sb_lo);
+  for (int sb = sb_lo; sb < sb_hi; ++sb) {
     // only stage sb's loads are outstanding: once every wave has seen its own land, the
     // stage is complete, and every wave is done with stage sb - 1, whose slots the next
     // issue reuses
@@ -1255,7 +1258,7 @@ __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (sb + 1 < a.nsb) issue(sb + 1);
+    if (sb + 1 < sb_hi) issue(sb + 1);
     __builtin_amdgcn_sched_barrier(0);
     lds_u8* slots[NT];
 #pragma unroll
@@ -1277,6 +1280,21 @@ __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
   // tile) of column n of each of its tiles
   const int rows0 = a.seg_rows[a.epi == kEpiSwiGLU ? 0 : seg];
   const int col0 = a.epi == kEpiSwiGLU ? 0 : a.seg_col_off[seg];
+  if (a.part) {  // split K: raw partial sums, finished by gemm_mm_finish_kernel
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * (mt * MB + b) + 2 * g + h;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int c = lt[t] * 16 + n;
+          if (row < a.B && c < rows0)
+            a.part[((size_t)ks * a.B + row) * a.ldp + (col0 - a.pcol0) + c] = acc[t][b][2 * h] + acc[t][b][2 * h + 1];
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < BT; ++b) {
 #pragma unroll
@@ -1325,6 +1343,43 @@ __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+// Second pass of a K-split many-row launch: the sum of the partial sums, then the store
+// or residual epilogue.  Grid (ceil(ldp / 256), B), 256 threads: thread = one column.
+__global__ __launch_bounds__(256) void gemm_mm_finish_kernel(GemmArgs a, int nsplit) {
+  __shared__ float red[4];
+  const int row = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+  const bool live = c < a.ldp;
+  float v = 0.f;
+  if (live)
+    for (int s = 0; s < nsplit; ++s) v += a.part[((size_t)s * a.B + row) * a.ldp + c];
+  float rs = 1.0f;
+  if (a.ss) {
+    float ssv = 0.f;
+    for (int s = 0; s < a.ss_slots; ++s) ssv += a.ss[s * a.B + row];
+    rs = 1.0f / sqrtf(ssv * a.inv_k + a.eps);
+  }
+  const int col = a.pcol0 + c;
+  if (a.epi == kEpiStore) {
+    if (live) a.y[(size_t)row * a.ldy + col] = rs * v;
+    return;
+  }
+  float sq = 0.f;
+  if (live) {
+    float* yp = a.y + (size_t)row * a.ldy + col;
+    const float xn = *yp + rs * v;
+    *yp = xn;
+    const float pv = xn * (a.gain ? a.gain[col] : 1.f);
+    if (a.pack_out) actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, row, col, pv);
+    if (a.pack_out2) actpack_put(a.pack_out2, a.pack_kind2, a.pack_nslices2, row, col, pv);
+    sq = xn * xn;
+  }
+  sq = wave_sum(sq);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
+  __syncthreads();
+  if (threadIdx.x == 0 && a.ss_out)
+    atomicAdd(a.ss_out + (size_t)(blockIdx.x % a.ss_slots) * a.B + row, red[0] + red[1] + red[2] + red[3]);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1514,9 +1569,32 @@ hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipSt
   return e != hipSuccess ? e : hipGetLastError();
 }
 
-bool use_mm(int B) { return B > kSkinnyRows; }
+bool mm_required(int B) { return B > kSkinnyRows; }
+bool use_mm(int wtype, int B) { return mm_supported(wtype) && B > kMmMinRows; }
 bool mm_supported(int wtype) { return wtype == 12 || wtype == 14; }
 int mm_group_tiles(bool swiglu) { return swiglu ? kMmWaves : kMmWaves * kMmNT; }
+
+// Few workgroups (narrow matrices: QKV, Wo, down at a few hundred rows): split K so the
+// grid fills the CUs more than once; a second pass sums the ranges.
+// One workgroup per CU at a time (its LDS), so a launch takes ceil(workgroups / CUs)
+// rounds; n ranges make rounds of 1/n the work.  The split that minimizes rounds / n
+// wins, a split paying 5 % for its finishing pass.
+int mm_split(int wtype, int B, int cols, int nsb, int groups, int epi, size_t part_cap) {
+  const int wgs = (actpack_tiles(B) / mm_mb(wtype)) * groups;
+  if (epi == kEpiSwiGLU || cols > kMmSplitMaxCols) return 1;
+  const int cus = variants().cus;
+  int best = 1;
+  double best_t = (double)((wgs + cus - 1) / cus);
+  for (int n = 2; n <= kMmMaxSplit && n <= nsb / 2; ++n) {
+    if ((size_t)n * B * cols > part_cap) break;
+    const double t = (double)((wgs * n + cus - 1) / cus) / n + 0.05;
+    if (t < best_t) {
+      best_t = t;
+      best = n;
+    }
+  }
+  return best;
+}
 
 hipError_t launch_gemm_mm(int wtype, int groups, GemmArgs a, hipStream_t st) {
   if (groups <= 0) return hipSuccess;
@@ -1535,9 +1613,15 @@ hipError_t launch_gemm_mm(int wtype, int groups, GemmArgs a, hipStream_t st) {
   }();
   (void)lds_set;
   a.tl_groups = mtiles;
+  a.tl_groups_per_wg = groups;
+  const int nsplit = a.part ? mm_split(wtype, a.B, a.ldp, a.nsb, groups, a.epi, a.part_cap) : 1;
+  if (nsplit <= 1) a.part = nullptr;
   void* kargs[] = {&a};
-  const hipError_t e = launch_fn(fn, dim3(mtiles * groups), dim3(kMmWaves * 64), mm_lds(wtype), st, kargs);
-  return e != hipSuccess ? e : hipGetLastError();
+  hipError_t e = launch_fn(fn, dim3(mtiles * groups * nsplit), dim3(kMmWaves * 64), mm_lds(wtype), st, kargs);
+  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess || nsplit <= 1) return e;
+  launch_kernel(gemm_mm_finish_kernel, dim3((a.ldp + 255) / 256, a.B), dim3(256), 0, st, a, nsplit);
+  return hipGetLastError();
 }
 
 }  // namespace gr

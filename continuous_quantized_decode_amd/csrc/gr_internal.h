@@ -84,6 +84,12 @@ struct GemmArgs {
   float* ss_out;        // residual: sum of squares accumulator of the packed rows, [ss_slots][B]
   float* zero_ptr;      // optional: workgroup 0 zeroes zero_n floats
   int zero_n;
+  // many-row kernel split over K (store and residual epilogues): the K ranges' partial
+  // sums part[split][B][ldp] (launch-local columns, the launch's first output column
+  // pcol0), summed and finished by a second kernel; part NULL: no split
+  float* part;
+  size_t part_cap;      // floats available at part
+  int ldp, pcol0;
 };
 
 // The RMSNorm statistic (per-row sum of squares) that a GEMM epilogue applies is kept
@@ -130,10 +136,17 @@ hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStre
 // (per matrix segment; SwiGLU: gate/up tile pairs), a.seg_tile_off counted in groups.
 constexpr int kSkinnyRows = 64;
 constexpr int kMaxRows = 512;
-bool use_mm(int B);
+constexpr int kMmMinRows = 32;  // above this many rows Q4_K / Q6_K take the many-row kernel (measured: 32 rows skinny, 64 rows many-row)
+constexpr int kMmMaxSplit = 4;        // K ranges of a many-row launch with few workgroups
+constexpr int kMmSplitMaxCols = 8192;  // only launches this narrow are split
+bool mm_required(int B);              // rows only the many-row kernel takes
+bool use_mm(int wtype, int B);       // the kernel a GEMM of this type and rows takes
 bool mm_supported(int wtype);
 int mm_group_tiles(bool swiglu);
 hipError_t launch_gemm_mm(int wtype, int groups, GemmArgs a, hipStream_t st);
+// K ranges of a many-row launch of `groups` weight tile groups and `cols` output columns
+// (1: no split), given part_cap floats of partial-sum space
+int mm_split(int wtype, int B, int cols, int nsb, int groups, int epi, size_t part_cap);
 
 // ---------------------------------------------------------------------- actpack
 

@@ -85,9 +85,20 @@ def test_gemm_launch_shape_names_the_kernel():
     mm = gr.gr_gemm_launch_shape(q4, 14336, 4096, 264, gr.GEMM_EPI_SWIGLU)
     assert mm["many_rows"] and not mm["tile_loop"] and mm["kernel"] == "gemm_mm_kernel<12,"
     assert mm["block_threads"] == 512 and mm["grid_threads"] == (36 // 4) * (896 // 8) * 512
+    # 96 workgroups for a narrow matrix: K split in 2 ranges (one round of half the work
+    # on 192 CUs; then a finishing pass)
     mm6 = gr.gr_gemm_launch_shape(q6, 4096, 14336, 65, gr.GEMM_EPI_RESIDUAL)
-    assert mm6["many_rows"] and mm6["btn"] == 2 and mm6["grid_threads"] == (12 // 2) * (256 // 16) * 512
-    assert not gr.gr_gemm_launch_shape(q4, 4096, 4096, 64)["many_rows"]
+    assert mm6["many_rows"] and mm6["btn"] == 2 and mm6["grid_threads"] == (12 // 2) * (256 // 16) * 2 * 512
+    # 288 workgroups: two rounds unsplit, five rounds of a quarter split in 4
+    assert gr.gr_gemm_launch_shape(q6, 4096, 14336, 264, 1)["grid_threads"] == 18 * 16 * 4 * 512
+    # one full round, or more than 8192 columns: no split
+    assert gr.gr_gemm_launch_shape(q4, 4096, 4096, 512)["grid_threads"] == (64 // 4) * 16 * 512
+    assert gr.gr_gemm_launch_shape(q4, 9000, 1024, 300)["grid_threads"] == (40 // 4) * 36 * 512
+    # Q4_K / Q6_K from 33 rows up take the many-row kernel (measured faster at 64 rows,
+    # slower at 32); Q5_K / Q8_0 keep the split-K kernel up to 64 rows
+    assert gr.gr_gemm_launch_shape(q4, 4096, 4096, 33)["many_rows"]
+    assert not gr.gr_gemm_launch_shape(q4, 4096, 4096, 32)["many_rows"]
+    assert not gr.gr_gemm_launch_shape(13, 4096, 4096, 64)["many_rows"]
     assert L.gr_gemm_launch_shape(13, 64, 256, 65, 0, *[ctypes.byref(o) for o in out]) == -3  # Q5_K: at most 64 rows
     assert L.gr_gemm_launch_shape(q4, 64, 256, 513, 0, *[ctypes.byref(o) for o in out]) == -2
     p = ctypes.c_void_p(256)

@@ -42,7 +42,8 @@ GEMM_CASES = [
     (synth.W_Q4_K, 100, 4096, 4096),
     (synth.W_Q4_K, 257, 300, 2048),    # ragged activation tile group
     (synth.W_Q4_K, 512, 1000, 4096),   # the largest step
-    (synth.W_Q4_K, 96, 16, 256),       # one weight tile, one super-block
+    (synth.W_Q4_K, 96, 16, 256),       # one weight tile, one super-block (no K split)
+    (synth.W_Q4_K, 300, 9000, 1024),   # wider than the K-split limit
     (synth.W_Q6_K, 72, 64, 2048),      # 16-byte aligned rows
     (synth.W_Q6_K, 129, 500, 3072),    # 2-byte aligned rows (12 super-blocks)
     (synth.W_Q6_K, 300, 700, 768),     # odd super-blocks per row
