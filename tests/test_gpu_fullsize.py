@@ -129,6 +129,75 @@ def test_llama3_8b_step_matches_oracle(torch, gr, orc):
     assert np.array_equal(eager_logits.argmax(1)[clear], want_logits.argmax(1)[clear])
 
 
+def test_llama3_8b_mixed_step_chunk256_matches_oracle(torch, gr, orc):
+    """bench.py's mixed step at full size: the Llama-3-8B layer shapes, its 8 decode rows and
+    a 256-token prompt chunk of a new sequence from an empty cache (264 rows through the
+    many-row GEMMs, QKV / Wo / down split over K), built from the same recipe, with logits
+    for the decode rows and the chunk's last token.  The first layer (every row against
+    the oracle; the launch configuration is the same in every layer) and the head on the
+    nine rows, eager and as one graph replayed."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["llama3_8b"], n_layers=1)
+    chunk = 256
+    ctx = synth.ctx_lens(wl)
+    b = len(ctx)
+    ctx2 = np.concatenate([ctx, [0]]).astype(np.int32)
+    kv = synth.kv_state(wl, ctx2, n_layers=1, extra_slot=chunk, seed_key=100 + chunk)
+    lw = synth.layer_weights(wl, 0)
+    keep, w = upload(gr, torch, lw)
+    kd, vd = dev(kv.k_pools[0], torch), dev(kv.v_pools[0], torch)
+    args = gr.StackArgs(cfg_of(gr, wl), [w], [kd], [vd])
+    rows = b + chunk
+    seq = np.concatenate([np.arange(b), np.full(chunk, b)]).astype(np.int32)
+    pos = np.concatenate([ctx, np.arange(chunk)]).astype(np.int32)
+    x_host = synth.activations(np.random.default_rng(55), rows, wl.hidden)
+    hn, hw = synth.head_weights(wl)
+    need = np.array(list(range(b)) + [rows - 1], np.int32)
+    x = dev(x_host, torch)
+    logits = torch.empty((len(need), wl.vocab), dtype=torch.float32, device="cuda")
+    hn_d, hw_d, hr = dev(hn, torch), dev(hw, torch), dev(need, torch)
+    bt, sq, ps = dev(kv.pages.block_table, torch), dev(seq, torch), dev(pos, torch)
+    say("llama3_8b mixed step: 8 decode rows + 256-token chunk, first layer and head")
+    gr.gr_mixed_stack(args, kv.pages.num_pages, x, bt, sq, ps, int(pos.max()), head_norm=hn_d, head_w=hw_d,
+                      head_wtype=wl.w_head, vocab=wl.vocab, logits=logits, head_rows=hr)
+    torch.cuda.synchronize()
+    got_x, got_logits = host(x), host(logits)
+    say("  oracle: 264 rows, one layer")
+    outs, _ = orc.mixed_stack(wl, [lw], [kv.k_pools[0].copy()], [kv.v_pools[0].copy()], x_host,
+                              kv.pages.block_table, seq, pos)
+    want_logits = orc.output_head(outs[-1][need], hn, wl.rms_eps, hw, wl.w_head, wl.vocab)
+    ex, el = rel_l2(got_x, outs[-1]), rel_l2(got_logits, want_logits)
+    say(f"  rel_l2 x {ex:.3e} logits {el:.3e}")
+    assert ex <= tol(wl.kv_dtype) and el <= tol(wl.kv_dtype)
+    # the graph bench.py replays gives the same result (pools restored first: the step
+    # stores every row's K/V)
+    kd.copy_(dev(kv.k_pools[0], torch))
+    vd.copy_(dev(kv.v_pools[0], torch))
+    x0 = dev(x_host, torch)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    ws = gr.workspace(gr.mixed_stack_workspace_size(args.cfg, rows, int(pos.max()), wl.vocab))
+
+    def step():
+        x.copy_(x0)
+        gr.gr_mixed_stack(args, kv.pages.num_pages, x, bt, sq, ps, int(pos.max()), head_norm=hn_d, head_w=hw_d,
+                          head_wtype=wl.w_head, vocab=wl.vocab, logits=logits, head_rows=hr, ws=ws)
+
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        assert rel_l2(host(x), got_x) <= 1e-5 and rel_l2(host(logits), got_logits) <= 1e-5, r
+        logits.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+
 QWEN_LAYERS = 3
 
 
