@@ -558,11 +558,12 @@ hipError_t launch_attn_append(int kv_dtype, const AttnParams& p, float* q_out, h
 
 AttnPlan plan_attn(int B, int n_kv_heads, int max_ctx_tokens) {
   // Enough (row, head, split) waves to fill the chip even when most rows are short:
-  // about 4096 waves at the longest context, at least 4 pages per split.
+  // about kAttnWaves waves at the longest context, at least kAttnMinPages pages per split.
+  constexpr int kAttnWaves = 4096, kAttnMinPages = 4;  // measured: 2 or 8 pages per split are slower
   const int max_pages = (max_ctx_tokens + kPage - 1) / kPage;
   const long long units = (long long)B * n_kv_heads * (max_pages > 0 ? max_pages : 1);
-  int pps = (int)((units + 4095) / 4096);
-  if (pps < 4) pps = 4;
+  int pps = (int)((units + kAttnWaves - 1) / kAttnWaves);
+  if (pps < kAttnMinPages) pps = kAttnMinPages;
   while ((max_pages + pps - 1) / pps > 1024) ++pps;  // the merge handles up to 1024 splits
   AttnPlan pl;
   pl.pages_per_split = pps;
