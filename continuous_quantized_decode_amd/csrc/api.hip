@@ -402,6 +402,9 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   ap.B = B;
   ap.tokens_per_seq = T;
   ap.self_in_pool = rm.fused() ? 0 : 1;
+  // standalone: consecutive rows of one sequence (verification runs, prompt chunks) share
+  // each page read, 8 / (Hq / Hkv) rows to a wave
+  ap.rows_per_unit = rm.fused() ? 1 : 8 / (c->n_q_heads / c->n_kv_heads);
   ap.row_seq = rm.seq;
   ap.row_pos = rm.pos;
   ap.n_q_heads = c->n_q_heads;
@@ -698,6 +701,7 @@ gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* 
   AttnParams ap{};
   ap.tokens_per_seq = 1;
   ap.self_in_pool = 0;
+  ap.rows_per_unit = 1;
   ap.o_part = c.take<float>(units * m->head_dim * 4);
   ap.m_part = c.take<float>(units * 4);
   ap.l_part = c.take<float>(units * 4);

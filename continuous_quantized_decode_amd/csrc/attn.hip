@@ -128,27 +128,70 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
   const int split = unit % p.max_splits;
   const int bg = unit / p.max_splits;
   const int g = bg % p.n_kv_heads;
-  const int b = bg / p.n_kv_heads;
   const int R = p.n_q_heads / p.n_kv_heads;
-
-  int seq, ctx;  // the row's sequence and position
-  attn_row_place(p, b, seq, ctx);
-  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
   const int pg0 = split * p.pages_per_split;
   const int n = lane & 15, kg = lane >> 4;
+
+  // Row groups: rows are taken P at a time (P = 1 in the fused layer).  When a group's
+  // rows belong to one sequence, the unit of its first row takes them through the pages
+  // together, their R P query heads side by side in the MFMA rows (R P <= 8), so each
+  // page is read once for all of them, each row masked to its own token count, and the
+  // other rows' units have nothing to do; otherwise every row's unit takes its own row.
+  const int P = FUSED ? 1 : (p.rows_per_unit > 0 ? p.rows_per_unit : 1);
+  const int brow = bg / p.n_kv_heads;
+  const int b0 = brow - brow % P;
+  const int nr = min(P, p.B - b0);
+  bool together = true;
+  if constexpr (!FUSED) {
+    int seq0, pos0;
+    attn_row_place(p, b0, seq0, pos0);
+    for (int r = 1; r < nr; ++r) {
+      int sr, pr;
+      attn_row_place(p, b0 + r, sr, pr);
+      together = together && sr == seq0;
+    }
+  }
+
+  __shared__ __attribute__((aligned(16))) float s_vec[10][128];  // head vectors, linear layout
+  __shared__ __attribute__((aligned(16))) u16 s_p[KVDT == KV_Q8_T ? D / 32 : 1][16][16];  // P transpose
+  __shared__ __attribute__((aligned(16))) uint8_t s_knew[D * 4 + 64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vnew[D * 4 + 64];
+
+  // rows b .. b + nrows - 1 of one sequence
+  auto run = [&](const int b, const int nrows) {
+  int seq, ctx;  // the first row's sequence and position
+  attn_row_place(p, b, seq, ctx);
+  const int nq = R * nrows;  // query head vectors (MFMA row pairs) in use
+  // token counts of the rows of this lane's two MFMA row pairs (head vectors 2 kg, 2 kg + 1)
+  int ntok_e[2] = {0, 0};
+  int n_tok = 0;  // the most tokens any row attends to
+  if constexpr (FUSED) {
+    n_tok = ctx + 1;
+    ntok_e[0] = ntok_e[1] = n_tok;
+  } else {
+    for (int r = 0; r < nrows; ++r) {
+      int sr, pr;
+      attn_row_place(p, b + r, sr, pr);
+      const int t = pr + p.self_in_pool;
+      n_tok = max(n_tok, t);
+      if ((2 * kg) / R == r) ntok_e[0] = t;
+      if ((2 * kg + 1) / R == r) ntok_e[1] = t;
+    }
+  }
+  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
 
   // ---- loads issued before anything waits: the row's context length, the page ids
   // of the split's first 64 pages (lane i: page pg0 + i; ids past the row's pages are
   // never used), the head vectors (q of the R heads; k and v of head g as well in the
   // fused layer), pairs (da, db) per lane, and the RoPE cosine and sine of the lane's
   // pair at the row's new position (computed in fp64 once per step)
-  constexpr int kMaxHeads = 10;  // R <= 8 query heads, then k and v
+  constexpr int kMaxHeads = 10;  // R P <= 8 query heads, then k and v
   int bt_chunk = pg0;
   int bt_lane = pg0 + lane < p.max_blocks ? bt[pg0 + lane] : 0;
   const bool act = lane < D / 2;
   int da = 0, db = 0;
   pair_dims(act ? lane : 0, D, p.rope_style, da, db);
-  const int nh = R + (FUSED ? 2 : 0);
+  const int nh = nq + (FUSED ? 2 : 0);
   double cs = 1.0, sn = 0.0;
   if (FUSED && act) {
     cs = p.rope[((size_t)b * (D / 2) + lane) * 2];
@@ -166,22 +209,16 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
         const int off = hh < R ? (g * R + hh) * D : hh == R ? p.q_dim + g * D : p.q_dim + p.kv_dim + g * D;
         src = p.qkv + (size_t)b * p.qkv_ld + off;
       } else {
-        src = p.q + ((size_t)b * p.n_q_heads + g * R + hh) * D;
+        src = p.q + ((size_t)(b + hh / R) * p.n_q_heads + g * R + hh % R) * D;
       }
       va[hh] = src[da];
       vb[hh] = src[db];
     }
   }
 
-  const int n_tok = FUSED ? ctx + 1 : ctx + p.self_in_pool;
   const int n_pages = (n_tok + kPage - 1) / kPage;
   if (pg0 >= n_pages) return;
   const int pg1 = min(n_pages, pg0 + p.pages_per_split);
-
-  __shared__ __attribute__((aligned(16))) float s_vec[kMaxHeads][128];  // head vectors, linear layout
-  __shared__ __attribute__((aligned(16))) u16 s_p[KVDT == KV_Q8_T ? D / 32 : 1][16][16];  // P transpose
-  __shared__ __attribute__((aligned(16))) uint8_t s_knew[D * 4 + 64];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vnew[D * 4 + 64];
 
   const int HB = kv_head_bytes_t<KVDT>(D);
   const size_t page_bytes = (size_t)HB * p.n_kv_heads;
@@ -205,7 +242,7 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
   // Pages go in chunks of NP, all of a chunk's loads in flight at once (as many as the
   // registers of three waves per SIMD allow); the first chunk is in flight during the
   // setup below.
-  constexpr int NP = KVDT == KV_Q8_T ? 4 : 2;
+  constexpr int NP = KVDT == KV_Q8_T ? (FUSED ? 4 : 2) : 2;  // the standalone kernel's extra row state
   PageRegs<KVDT, D> r[NP];
   auto issue_chunk = [&](int c0) {
 #pragma unroll
@@ -238,7 +275,7 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
   {
     const float qscale = p.scale * 1.4426950408889634f;
     const int m = lane & 15, k = lane >> 4;
-    const bool live_m = m < 2 * R;
+    const bool live_m = m < 2 * nq;
     const int hq = live_m ? m >> 1 : 0;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -275,7 +312,9 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
   // One page: scores, online softmax, P transpose, PV.
   auto page = [&](PageRegs<KVDT, D>& cur, int j) {
     if (FUSED && owner && j == new_page) patch_page<KVDT, D>(cur, s_knew, s_vnew, new_slot, lane);
-    const int valid = min(kPage, n_tok - j * kPage);
+    const int valid = min(kPage, n_tok - j * kPage);  // of the row with the most tokens
+    const int valid_e[2] = {FUSED ? valid : min(kPage, ntok_e[0] - j * kPage),
+                            FUSED ? valid : min(kPage, ntok_e[1] - j * kPage)};
     if constexpr (KVDT != KV_Q8_T) {
       // slots past the context may hold anything (NaN included): zero their V so
       // that 0 * V stays 0 in the PV product
@@ -307,13 +346,16 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
     float sv[2], pv[2], alpha[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      sv[e] = n < valid ? sc[2 * e] + sc[2 * e + 1] : -INFINITY;
+      sv[e] = n < valid_e[e] ? sc[2 * e] + sc[2 * e + 1] : -INFINITY;
       float mx = sv[e];
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
       const float mnew = fmaxf(m_run[e], mx);
-      alpha[e] = exp2f(m_run[e] - mnew);
-      pv[e] = exp2f(sv[e] - mnew);
+      // a row with no token yet (its tokens start on a later page) keeps m = -inf and
+      // l = 0: scale against 0 instead of -inf so nothing becomes NaN
+      const float mref = (!FUSED && mnew == -INFINITY) ? 0.f : mnew;
+      alpha[e] = exp2f(m_run[e] - mref);
+      pv[e] = exp2f(sv[e] - mref);
       float ps = pv[e];
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
@@ -321,7 +363,7 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
       m_run[e] = mnew;
     }
     // P (f16 hi/lo rows) to LDS, transposed to the PV A layout
-    const bool live = 2 * kg < R;  // this lane group holds real heads
+    const bool live = 2 * kg < nq;  // this lane group holds real heads
     if constexpr (KVDT == KV_Q8_T) {
       const int col = 4 * (n >> 2) + perm4(n & 3);
 #pragma unroll
@@ -330,7 +372,7 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
         const float vs = h2f((u16)((blk & 1) ? (w >> 16) : (w & 0xFFFF)));
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const float x = n < valid ? pv[e] * vs : 0.0f;
+          const float x = n < valid_e[e] ? pv[e] * vs : 0.0f;
           const u16 h = f2h(x);
           if (live) {
             s_p[blk][4 * kg + 2 * e][col] = h;
@@ -387,13 +429,15 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
       if (c0 + i < pg1) page(r[i], c0 + i);
   }
 
-  // ---- partial results -------------------------------------------------------------
-  if (2 * kg < R) {
+  // ---- partial results: for each row with tokens in this split ----------------------
+  if (2 * kg < nq) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int h = g * R + 2 * kg + e;
-      if (2 * kg + e >= R) break;
-      const size_t base = ((size_t)b * p.n_q_heads + h) * p.max_splits + split;
+      const int hq = 2 * kg + e;
+      if (hq >= nq) break;
+      if (!FUSED && pg0 * kPage >= ntok_e[e]) continue;  // the row ends before this split
+      const int h = g * R + hq % R;
+      const size_t base = ((size_t)(b + hq / R) * p.n_q_heads + h) * p.max_splits + split;
 #pragma unroll
       for (int t = 0; t < NT; ++t) p.o_part[base * D + 16 * t + n] = O[t][2 * e] + O[t][2 * e + 1];
       if (n == 0) {
@@ -401,6 +445,13 @@ __global__ __launch_bounds__(64, KVDT == KV_F32_T ? 2 : 3) void attn_split_kerne
         p.l_part[base] = l_run[e];
       }
     }
+  }
+  };  // run
+
+  if (FUSED || !together) {
+    run(brow, 1);
+  } else if (brow == b0) {
+    run(b0, nr);
   }
 }
 
@@ -563,6 +614,11 @@ AttnPlan plan_attn(int B, int n_kv_heads, int max_ctx_tokens) {
   const int max_pages = (max_ctx_tokens + kPage - 1) / kPage;
   const long long units = (long long)B * n_kv_heads * (max_pages > 0 ? max_pages : 1);
   int pps = (int)((units + kAttnWaves - 1) / kAttnWaves);
+  // many short rows (a prompt chunk) next to a few long ones (decode rows): the count
+  // above assumes every row is as long as the longest and would leave the long rows a
+  // handful of splits, each walking its pages alone; keep at least 16 splits for them
+  const int long_rows_pps = (max_pages + 15) / 16;
+  if (pps > long_rows_pps) pps = long_rows_pps;
   if (pps < kAttnMinPages) pps = kAttnMinPages;
   while ((max_pages + pps - 1) / pps > 1024) ++pps;  // the merge handles up to 1024 splits
   AttnPlan pl;
@@ -576,6 +632,8 @@ size_t attn_partial_floats(int B, int n_q_heads, int head_dim, const AttnPlan& p
 }
 
 hipError_t launch_attn_split(int kv_dtype, bool fused, const AttnParams& p, hipStream_t st) {
+  const int P = fused ? 1 : (p.rows_per_unit > 0 ? p.rows_per_unit : 1);
+  if (P * (p.n_q_heads / p.n_kv_heads) > 8) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((size_t)p.B * p.n_kv_heads * p.max_splits));
 #define GR_A(KV, DD, FU) launch_kernel(attn_split_kernel<KV, DD, FU>, grid, dim3(64), 0, st, p)
 #define GR_AD(KV, FU)        \

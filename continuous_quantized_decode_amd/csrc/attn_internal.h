@@ -15,6 +15,8 @@ struct AttnParams {
   int B, n_q_heads, n_kv_heads, head_dim;
   int tokens_per_seq;  // 1 for a decode step
   int self_in_pool;    // standalone: 1 if the row's own token is already stored (n_tok = pos + 1)
+  int rows_per_unit;   // standalone: consecutive rows per wave when they share a sequence
+                       // (rows_per_unit * n_q_heads / n_kv_heads <= 8); 0 or 1: one row
   // when set, row b is the token at position row_pos[b] of sequence row_seq[b] instead
   const int32_t* row_seq;
   const int32_t* row_pos;

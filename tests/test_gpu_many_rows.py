@@ -176,3 +176,33 @@ def test_head_on_selected_rows(torch, gr, orc):
     need += [int(i) for i in np.nonzero(seq >= 2)[0]] + [need[0]]
     x = synth.activations(rng, len(seq), wl.hidden)
     s.step(x, seq, pos, "tiny 308 rows, head on 11", head_rows=need)
+
+
+@pytest.mark.parametrize("kv_dtype", [synth.KV_F32, synth.KV_F16, synth.KV_Q8_0])
+def test_contiguous_chunk_rows_share_page_reads(torch, gr, orc, kv_dtype):
+    """Rows in sequence order (a chunk's rows next to each other, as a scheduler lays them
+    out): the standalone attention takes 8 / (Hq / Hkv) consecutive rows of one sequence to
+    a wave.  Chunks of odd lengths, resumed mid-page and from an empty cache, so groups
+    straddle sequence boundaries and rows end on different pages of a split."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], n_layers=2, kv_dtype=kv_dtype, qk_norm=True)
+    ctx = np.array([0, 37, 300, 5, 64, 1], np.int32)
+    s = Session(torch, gr, orc, wl, ctx, 70, False)
+    spec = [70, 33, 1, 7, 50, 3]
+    seq = np.concatenate([np.full(n, i) for i, n in enumerate(spec)]).astype(np.int32)
+    pos = np.concatenate([ctx[i] + np.arange(n) for i, n in enumerate(spec)]).astype(np.int32)
+    x = synth.activations(np.random.default_rng(13 + kv_dtype), len(seq), wl.hidden)
+    s.step(x, seq, pos, f"contiguous rows kv={kv_dtype}")
+
+
+def test_contiguous_chunk_rows_llama_heads(torch, gr, orc):
+    """The same with Llama-3-style grouped heads (Hq / Hkv = 4: two rows to a wave) and
+    head_dim 128, f16 KV, with the head on the chunks' last tokens."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], n_layers=1, kv_dtype=synth.KV_F16, head_dim=128,
+                             n_q_heads=8, n_kv_heads=2, vocab=500)
+    ctx = np.array([0, 200, 17], np.int32)
+    s = Session(torch, gr, orc, wl, ctx, 90, True)
+    spec = [90, 41, 1]
+    seq = np.concatenate([np.full(n, i) for i, n in enumerate(spec)]).astype(np.int32)
+    pos = np.concatenate([ctx[i] + np.arange(n) for i, n in enumerate(spec)]).astype(np.int32)
+    x = synth.activations(np.random.default_rng(17), len(seq), wl.hidden)
+    s.step(x, seq, pos, "contiguous rows, 4 q heads per kv head", head_rows=[89, 130, 131])
