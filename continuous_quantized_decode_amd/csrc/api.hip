@@ -125,7 +125,9 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     for (int q = i; q < nmat && types[q] == types[i]; ++q) all_tiles += (rows[q] + 15) / 16;
     // many rows: the 2-D tiled kernel; many tiles and a plain store: the tile-loop
     // kernel (one tile per group)
-    const bool mm = use_mm(types[i], B);
+    int type_cols = 0;
+    for (int q = i; q < nmat && types[q] == types[i]; ++q) type_cols += rows[q];
+    const bool mm = ep.kind == kEpiStore ? use_mm_store(types[i], B, type_cols) : use_mm(types[i], B);
     const bool tl = !mm && ep.kind == kEpiStore && use_tile_loop(types[i], all_tiles, K, B);
     const int group = mm ? mm_group_tiles(false) : tl ? 1 : gemm_group(all_tiles);
     while (j < nmat && types[j] == types[i]) {
@@ -577,7 +579,7 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
   if (mm_required(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
   const int tiles = (rows + 15) / 16;
   const bool pair = epi == 2;
-  if (use_mm(wtype, B)) {  // the many-row kernel: 512 threads, activation tile groups x weight tile groups
+  if (epi == 0 ? use_mm_store(wtype, B, rows) : use_mm(wtype, B)) {  // the many-row kernel: 512 threads, activation tile groups x weight tile groups
     const int gt = mm_group_tiles(pair);
     const int mb = wtype == GR_W_Q4_K ? 4 : 2;
     *tile_loop = 2;

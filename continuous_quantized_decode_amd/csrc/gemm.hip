@@ -1571,6 +1571,13 @@ hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipSt
 
 bool mm_required(int B) { return B > kSkinnyRows; }
 bool use_mm(int wtype, int B) { return mm_supported(wtype) && B > kMmMinRows; }
+// Wide plain-store GEMMs (the output head) from 9 rows: the many-row kernel streams each
+// weight tile once per 16 (Q6_K) or 32 (Q4_K) rows instead of re-reading every row's
+// activations per tile
+bool use_mm_store(int wtype, int B, int cols) {
+  return use_mm(wtype, B) ||
+         (mm_supported(wtype) && cols > kMmSplitMaxCols && B > 8 && actpack_tiles(B) % mm_mb(wtype) == 0);
+}
 bool mm_supported(int wtype) { return wtype == 12 || wtype == 14; }
 int mm_group_tiles(bool swiglu) { return swiglu ? kMmWaves : kMmWaves * kMmNT; }
 

@@ -141,6 +141,7 @@ constexpr int kMmMaxSplit = 4;        // K ranges of a many-row launch with few 
 constexpr int kMmSplitMaxCols = 8192;  // only launches this narrow are split
 bool mm_required(int B);              // rows only the many-row kernel takes
 bool use_mm(int wtype, int B);       // the kernel a GEMM of this type and rows takes
+bool use_mm_store(int wtype, int B, int cols);  // the same for a plain store of `cols` outputs
 bool mm_supported(int wtype);
 int mm_group_tiles(bool swiglu);
 hipError_t launch_gemm_mm(int wtype, int groups, GemmArgs a, hipStream_t st);
