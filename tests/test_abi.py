@@ -123,3 +123,25 @@ def test_sample_host_checks_without_gpu():
     assert L.gr_sample(p, 1, 10, p, p, None, p + 8, big, None) == -5
     assert L.gr_sample_workspace_size(8, 128256) > 8 * 4096 * 12 > 0
     assert L.gr_sample_workspace_size(8, (1 << 18) + 1) == 0
+
+
+def test_mixed_stack_head_rows_host_checks():
+    """gr_mixed_stack's named logit rows are checked on the host: 1 <= n_head_rows <= rows,
+    the index array 4-byte aligned (the indices themselves are clamped on the device)."""
+    import continuous_quantized_decode_amd as gr
+    L = gr.lib()
+    buf = ctypes.create_string_buffer(8192)
+    p = ctypes.addressof(buf) + (-ctypes.addressof(buf) % 256)
+    cfg = gr.layer_cfg(256, 4, 2, 64, 768, 1e-6, 1e4, 0, 0, 0)
+    w = gr.LayerWeights(*([p] * 11 + [12] * 7))
+    kp = (ctypes.c_void_p * 1)(p)
+    vp = (ctypes.c_void_p * 1)(p)
+
+    def call(head_rows, n_head, rows=4):
+        return L.gr_mixed_stack(ctypes.byref(cfg), ctypes.byref(w), 1, kp, vp, 9, p, p, 8, p, p, rows, 100, p, p, 14,
+                                1000, head_rows, n_head, p, p, 1 << 24, None)
+
+    assert call(p, 5) == -2      # more named rows than the step has
+    assert call(p, 0) == -2
+    assert call(p + 2, 2) == -4  # misaligned index array
+    assert call(p, 2, rows=513) == -2  # above the 512-row step budget
