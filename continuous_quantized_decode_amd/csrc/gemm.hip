@@ -1523,8 +1523,12 @@ hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStre
 // ring depth by (type, NT): the deepest that fits kGemmLds with 8 waves
 constexpr int tl_ring(int wtype, int nt) { return wtype == 12 ? (nt == 1 ? 4 : 3) : (nt == 1 ? 4 : 2); }
 
+// The epilogue gives each of a group's 128 outputs (a tile, or a gate/up pair, of 8 rows)
+// a thread of its own, so the workgroup needs at least two waves: K of at least three
+// super-blocks (one wave per two).
 bool use_tile_loop(int wtype, int groups, int K, int B) {
-  return (wtype == 12 || wtype == 14) && B <= 8 && K % kQK == 0 && K / kQK <= 16 && groups >= 2 * variants().cus;
+  return (wtype == 12 || wtype == 14) && B <= 8 && K % kQK == 0 && K / kQK >= 3 && K / kQK <= 16 &&
+         groups >= 2 * variants().cus;
 }
 
 TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K) {
@@ -1549,8 +1553,8 @@ const void* tl_fn(int nt) {
 
 hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st) {
   if (pl.grid <= 0) return hipSuccess;
-  if ((nt != 1 && nt != 2) || pl.waves < 1 || pl.waves > 8 || pl.lds > (size_t)kGemmLds || a.B > 8 ||
-      (a.ss && a.ss_slots != 16))
+  if ((nt != 1 && nt != 2) || pl.waves < 2 || pl.waves > 8 || pl.lds > (size_t)kGemmLds || a.B > 8 ||
+      (a.ss && a.ss_slots != 16) || (a.epi != kEpiSwiGLU && nt * 128 > pl.waves * 64))
     return hipErrorInvalidValue;
   const bool aligned = wtype == 12 || a.row_bytes % 16 == 0;
   const void* fn = wtype == 12 ? tl_fn<12, true>(nt) : aligned ? tl_fn<14, true>(nt) : tl_fn<14, false>(nt);

@@ -74,6 +74,9 @@ def test_gemm_launch_shape_names_the_kernel():
     assert not down["tile_loop"] and down["kernel"].startswith("gemm_kernel<14, 1, 1,")
     assert not gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_RESIDUAL)["tile_loop"]
     assert gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_STORE)["tile_loop"]
+    # the tile loop's epilogue needs two waves (K of three super-blocks or more)
+    assert not gr.gr_gemm_launch_shape(q4, 16384, 512, 8, gr.GEMM_EPI_STORE)["tile_loop"]
+    assert gr.gr_gemm_launch_shape(q4, 16384, 768, 8, gr.GEMM_EPI_STORE)["tile_loop"]
     # more than one batch tile, or K above 16 super-blocks: split-K
     assert not gr.gr_gemm_launch_shape(q6, 128256, 4096, 9, gr.GEMM_EPI_STORE)["tile_loop"]
     assert not gr.gr_gemm_launch_shape(q6, 128256, 4352, 8, gr.GEMM_EPI_STORE)["tile_loop"]

@@ -105,7 +105,10 @@ GEMM_CASES = [
     (synth.W_Q4_K, 8, 8200, 4096),   # 513 tiles, the last ragged; runs of three per workgroup
     (synth.W_Q6_K, 5, 9000, 1280),   # 2-byte aligned rows, waves of two and one super-blocks
     (synth.W_Q6_K, 8, 8192, 4096),
-    (synth.W_Q4_K, 1, 16384, 256),   # one super-block: a single wave per workgroup
+    (synth.W_Q4_K, 1, 16384, 256),   # one super-block: too few waves for the tile loop
+    (synth.W_Q4_K, 8, 16384, 256),   # the same at 8 rows (every row's outputs written)
+    (synth.W_Q6_K, 6, 9000, 512),
+    (synth.W_Q4_K, 8, 9000, 768),    # three super-blocks: the smallest tile-loop K
     # Q5_K and Q8_0 rows (split-K kernel only): every batch-tile count, ragged rows
     (synth.W_Q5_K, 1, 16, 256),
     (synth.W_Q5_K, 2, 40, 768),
