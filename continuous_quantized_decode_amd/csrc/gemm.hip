@@ -1166,9 +1166,9 @@ GR_DEV void q6_step_mm(const lds_u8* as, lds_u8* const (&slot)[kMmNT], const u32
   }
 }
 
-// Grid: mtiles * ngroups workgroups (mtiles = activation tiles / MB; ngroups: groups of
-// 16 weight tiles per matrix segment, or of 8 gate/up tile pairs), 512 threads.
-// a.seg_tile_off counts groups.  a.tl_groups carries mtiles.
+// Grid: mtiles * groups workgroups per K range (a.mm_mtiles = activation tiles / MB;
+// a.mm_groups: groups of 16 weight tiles per matrix segment, or of 8 gate/up tile
+// pairs), 512 threads.  a.seg_tile_off counts groups.
 template <int WT, bool ALIGNED>
 __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
   constexpr int MB = mm_mb(WT), BT = MB, NT = kMmNT;
@@ -1188,7 +1188,7 @@ __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
   // meet in that XCD's L2
   const int G = gridDim.x, bid = blockIdx.x;
   const int lg = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  const int mtiles = a.tl_groups, per_split = mtiles * a.tl_groups_per_wg;  // tl_groups_per_wg: weight groups
+  const int mtiles = a.mm_mtiles, per_split = mtiles * a.mm_groups;
   const int ks = lg / per_split, rem = lg - ks * per_split;
   const int mt = rem % mtiles, ng = rem / mtiles;
   const int nsplit = a.part ? G / per_split : 1;
@@ -1623,8 +1623,8 @@ hipError_t launch_gemm_mm(int wtype, int groups, GemmArgs a, hipStream_t st) {
     return true;
   }();
   (void)lds_set;
-  a.tl_groups = mtiles;
-  a.tl_groups_per_wg = groups;
+  a.mm_mtiles = mtiles;
+  a.mm_groups = groups;
   const int nsplit = a.part ? mm_split(wtype, a.B, a.ldp, a.nsb, groups, a.epi, a.part_cap) : 1;
   if (nsplit <= 1) a.part = nullptr;
   void* kargs[] = {&a};

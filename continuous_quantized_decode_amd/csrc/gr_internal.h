@@ -73,6 +73,7 @@ struct GemmArgs {
   int B;
   int sb_per_wave;
   int tl_groups, tl_groups_per_wg;  // tile-loop kernel: tile groups in all, per workgroup
+  int mm_mtiles, mm_groups;         // many-row kernel: activation tile groups, weight tile groups
   int epi;
   float* y;             // store: output; residual: the residual stream x
   int ldy;
