@@ -127,8 +127,8 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     // kernel (one tile per group)
     int type_cols = 0;
     for (int q = i; q < nmat && types[q] == types[i]; ++q) type_cols += rows[q];
-    const bool mm = ep.kind == kEpiStore ? use_mm_store(types[i], B, type_cols) : use_mm(types[i], B);
-    const bool tl = !mm && ep.kind == kEpiStore && use_tile_loop(types[i], all_tiles, K, B);
+    const bool tl = ep.kind == kEpiStore && !use_mm(types[i], B) && use_tile_loop(types[i], all_tiles, K, B);
+    const bool mm = !tl && (ep.kind == kEpiStore ? use_mm_store(types[i], B, type_cols) : use_mm(types[i], B));
     const int group = mm ? mm_group_tiles(false) : tl ? 1 : gemm_group(all_tiles);
     while (j < nmat && types[j] == types[i]) {
       a.w[n] = (const uint8_t*)w[j];
@@ -178,7 +178,7 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
       e = launch_gemm_mm(wt, tiles, a, st);
     } else if (tl) {
       a.tl_groups = tiles;
-      e = launch_gemm_tl(wt, 1, plan_gemm_tl(wt, 1, tiles, K), a, st);
+      e = launch_gemm_tl(wt, 1, plan_gemm_tl(wt, 1, tiles, K, B), a, st);
     } else {
       const GemmPlan pl = plan_gemm(wt, tiles, K, B, group);
       a.sb_per_wave = pl.sb_per_wave;
@@ -218,7 +218,7 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   if (use_mm(wtype, B)) return launch_gemm_mm(wtype, (tiles + mm_group_tiles(true) - 1) / mm_group_tiles(true), a, st);
   if (use_tile_loop(wtype, tiles, K, B)) {
     a.tl_groups = tiles;
-    return launch_gemm_tl(wtype, 2, plan_gemm_tl(wtype, 2, tiles, K), a, st);
+    return launch_gemm_tl(wtype, 2, plan_gemm_tl(wtype, 2, tiles, K, B), a, st);
   }
   const GemmPlan pl = plan_gemm(wtype, tiles, K, B, 2);
   a.sb_per_wave = pl.sb_per_wave;
@@ -579,6 +579,17 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
   if (mm_required(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
   const int tiles = (rows + 15) / 16;
   const bool pair = epi == 2;
+  // the choices gemm_run and gemm_swiglu make
+  if ((pair || epi == 0) && !use_mm(wtype, B) && use_tile_loop(wtype, tiles, K, B)) {
+    const TlPlan tp = plan_gemm_tl(wtype, pair ? 2 : 1, tiles, K, B);
+    *tile_loop = 1;
+    *nt = pair ? 2 : 1;
+    *btn = tl_btn(B);
+    *maxt = 512;
+    *grid_threads = tp.grid * tp.waves * 64;
+    *block_threads = tp.waves * 64;
+    return GR_OK;
+  }
   if (epi == 0 ? use_mm_store(wtype, B, rows) : use_mm(wtype, B)) {  // the many-row kernel: 512 threads, activation tile groups x weight tile groups
     const int gt = mm_group_tiles(pair);
     const int mb = wtype == GR_W_Q4_K ? 4 : 2;
@@ -590,17 +601,6 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
     const int groups = (tiles + gt - 1) / gt;
     const int split = mm_split(wtype, B, rows, K / kQK, groups, epi, mm_part_floats(B, rows));
     *grid_threads = (actpack_tiles(B) / mb) * groups * split * 512;  // a split adds a finishing pass
-    return GR_OK;
-  }
-  // the choices gemm_run and gemm_swiglu make
-  if ((pair || epi == 0) && use_tile_loop(wtype, tiles, K, B)) {
-    const TlPlan tp = plan_gemm_tl(wtype, pair ? 2 : 1, tiles, K);
-    *tile_loop = 1;
-    *nt = pair ? 2 : 1;
-    *btn = 1;
-    *maxt = 512;
-    *grid_threads = tp.grid * tp.waves * 64;
-    *block_threads = tp.waves * 64;
     return GR_OK;
   }
   *tile_loop = 0;

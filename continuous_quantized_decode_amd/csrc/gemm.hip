@@ -484,7 +484,9 @@ GR_DEV void q6_load_lds(const lds_u8* slot, u32 s16, int n, int kg, Q6Regs& w) {
 // One super-block of Q6_K.  Per 16-weight sub-block: C = A x (-160) gives -160 * S
 // (S the activation sums), and the quant MFMA accumulates onto it, so the MFMA returns
 // D - 160 S = sum a * (q - 32) with no vector work; the scale is one FMA per row.
-template <int NT, int BTN>
+// REG: the activation fragments come from registers, ca[b * 8 + pair] (the tile-loop
+// kernel; the split-K kernel's single batch tile); otherwise from the pack in memory.
+template <int NT, int BTN, bool REG = (BTN == 1)>
 GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&s16reg)[NT], const u32x4* ca, int sb,
                     int lane, float (&acc)[NT][BTN][4]) {
   const u32x4* xp = (const u32x4*)a.xpack;
@@ -509,8 +511,8 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&s1
 #pragma unroll
       for (int b = 0; b < BTN; ++b) {
         u32x4 pr;
-        if constexpr (BTN == 1)
-          pr = ca[sub >> 1];
+        if constexpr (REG)
+          pr = ca[b * 8 + (sub >> 1)];
         else
           pr = xp[(((size_t)b * (a.nslices >> 1)) + (size_t)sb * 8 + (sub >> 1)) * 64 + lane];
         av[b] = (sub & 1) ? u32x2{pr.z, pr.w} : u32x2{pr.x, pr.y};
@@ -792,9 +794,9 @@ GR_DEV void q4_load_tl(const lds_u8* rp, int kg, Q4Regs& w, float (&sd)[8], floa
 // sum a q with no vector work (as the Q6_K path), and the mins term is one MFMA per
 // tile (B: the mins m_j as exact bf16, repeated for the hi and lo parts of S_j):
 //   acc += sum_j d sc_j (D_j - 128 S_j) - dmin sum_j m_j S_j
-template <int NT>
-GR_DEV void q4_step_tl(lds_u8* const (&slot)[NT], const u32x4 (&ca)[8], u32x2 aS, int lane,
-                       float (&acc)[NT][1][4]) {
+template <int NT, int BTN>
+GR_DEV void q4_step_tl(lds_u8* const (&slot)[NT], const u32x4 (&ca)[BTN][8], const u32x2 (&aS)[BTN], int lane,
+                       float (&acc)[NT][BTN][4]) {
   const u32x4 neg128 = {kNeg128Bf16, kNeg128Bf16, kNeg128Bf16, kNeg128Bf16};
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   const int n = lane & 15, kg = lane >> 4;
@@ -806,21 +808,28 @@ GR_DEV void q4_step_tl(lds_u8* const (&slot)[NT], const u32x4 (&ca)[8], u32x2 aS
   for (int t = 0; t < NT; ++t) q4_load_tl(slot[t] + addr::q4_lds_byte(n, 0), kg, w[t], sd[t], dmin[t], bm[t]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const f32x4 cj = mfma_bf16_k32(ca[j], neg128, z4);
+    f32x4 cj[BTN];
+#pragma unroll
+    for (int b = 0; b < BTN; ++b) cj[b] = mfma_bf16_k32(ca[b][j], neg128, z4);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const u32x4 bq = q4_expand(w[t].qs[j >> 1], (j & 1) != 0, M);
-      const f32x4 dd = mfma_bf16_k32(ca[j], bq, cj);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][0][e] = __builtin_fmaf(sd[t][j], dd[e], acc[t][0][e]);
+      for (int b = 0; b < BTN; ++b) {
+        const f32x4 dd = mfma_bf16_k32(ca[b][j], bq, cj[b]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][b][e] = __builtin_fmaf(sd[t][j], dd[e], acc[t][b][e]);
+      }
     }
   }
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const f32x4 corr = mfma_bf16_k16(aS, bm[t], z4);
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[t][0][e] = __builtin_fmaf(-dmin[t], corr[e], acc[t][0][e]);
-  }
+    for (int b = 0; b < BTN; ++b) {
+      const f32x4 corr = mfma_bf16_k16(aS[b], bm[t], z4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][b][e] = __builtin_fmaf(-dmin[t], corr[e], acc[t][b][e]);
+    }
 }
 
 // Workgroup barrier for LDS written with ds_write only: the weight loads in flight
@@ -830,7 +839,7 @@ GR_DEV void q4_step_tl(lds_u8* const (&slot)[NT], const u32x4 (&ca)[8], u32x2 aS
 // compiler from moving memory accesses across it.
 GR_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int WT, int NT, bool ALIGNED, int D>
+template <int WT, int NT, bool ALIGNED, int D, int BTN>
 __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
   static_assert(D >= 2 && D <= 4, "ring depth");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -840,7 +849,7 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
   const int nwaves = blockDim.x >> 6;
   const int n = lane & 15;
   lds_u8* ring = (lds_u8*)lds + wave * (D * NT * kStage);
-  float* red = (float*)(lds + (size_t)nwaves * D * NT * kStage);  // [2][waves][NT][128]
+  float* red = (float*)(lds + (size_t)nwaves * D * NT * kStage);  // [2][waves][NT][BTN][128]
 
   if (a.zero_ptr && blockIdx.x == 0)
     for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.f;
@@ -852,14 +861,15 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
   const int nst = max(0, min(a.nsb, sb0 + a.sb_per_wave) - sb0);  // 1 or 2 (0: idle wave)
   const int nq = ng * nst;
 
-  // epilogue element of this thread (fixed): e < n_elem
-  const int n_elem = a.epi == kEpiSwiGLU ? 128 : NT * 128;
+  // epilogue element of this thread (fixed): e < n_elem, e = (t, batch tile, 128 outputs)
+  const int n_elem = (a.epi == kEpiSwiGLU ? 128 : NT * 128) * BTN;
   const int e = threadIdx.x;
-  const int e_t = a.epi == kEpiSwiGLU ? 0 : (e < n_elem ? e / 128 : 0);
+  const int e_t = a.epi == kEpiSwiGLU ? 0 : (e < n_elem ? e / (128 * BTN) : 0);
+  const int e_b = (e >> 7) % BTN;
   const int e_rem = e & 127;
   const int e_lp = e_rem >> 1;
   const int e_nn = e_lp & 15;
-  const int e_brow = 2 * (e_lp >> 4) + (e_rem & 1);
+  const int e_brow = 8 * e_b + 2 * (e_lp >> 4) + (e_rem & 1);
   // rows of group gi: as in gemm_kernel (SwiGLU pairs, or NT consecutive tiles of one
   // matrix with a phantom tile re-reading the last one).  The segment table (at most
   // three matrices) is read into scalar registers once, so that finding a group's rows
@@ -908,29 +918,36 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
     }
   };
 
-  float acc[NT][1][4];
+  float acc[NT][BTN][4];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc[t][0][k] = 0.f;
+    for (int b = 0; b < BTN; ++b)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[t][b][k] = 0.f;
 
   // Issue order: the RMSNorm partial sums, the slice's activation fragments (8 per
   // super-block, loaded once; a one-super-block slice loads its block twice), then the
   // first D - 1 weight stages (unconditionally: a workgroup with fewer stages repeats
   // its last one into slots it never reads).  So the first step waits for stage 0 and
   // what is older than it, not for the whole prologue.
-  float sv[16];  // B <= 8: ss_slots(B) = 16; every lane loads (a valid row), uniformly
+  float sv[16];  // B <= 16: ss_slots(B) = 16; every lane loads (a valid row), uniformly
   if (a.ss) {
     const int row = min(e_brow, a.B - 1);
 #pragma unroll
     for (int s = 0; s < 16; ++s) sv[s] = a.ss[s * a.B + row];
   }
-  u32x4 act[2][8];
+  // activation tile b starts K / 32 fragments of 1 KB after tile b - 1 (both pack kinds)
+  const size_t tile_frags = (size_t)a.nsb * 8;
+  u32x4 act[2][BTN][8];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int sb = min(sb0 + s, a.nsb - 1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) act[s][j] = ((const u32x4*)a.xpack)[((size_t)sb * 8 + j) * 64 + lane];
+    for (int b = 0; b < BTN; ++b)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        act[s][b][j] = ((const u32x4*)a.xpack)[((size_t)b * tile_frags + (size_t)sb * 8 + j) * 64 + lane];
   }
 #pragma unroll
   for (int d = 0; d < D - 1; ++d) issue(d < nq ? d : nq - 1);
@@ -940,27 +957,33 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
   // Q4_K: the slice's sub-block sums S_j as the mins MFMA's A operand (row l % 16,
   // j = 2kg and 2kg + 1, bf16 hi/lo), transposed through this wave's part of the
   // reduction buffers before any group uses them
-  u32x2 aS[2] = {u32x2{0u, 0u}, u32x2{0u, 0u}};
+  u32x2 aS[2][BTN];
   if constexpr (WT == 12) {
     const u32x4 ones = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     const int m = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float* scr = red + ((size_t)s * nwaves + wave) * NT * 128;  // 128 floats: [j][row]
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int b = 0; b < BTN; ++b) {
+      // 128 floats of the wave's part of buffer s per batch tile, each written once and
+      // read once: a location reused for the next tile would let the compiler keep, for
+      // the lanes that do not write it, the value they loaded for the previous tile
+      float* scr = red + (((size_t)s * nwaves + wave) * NT * BTN + b) * 128;  // [j][row]
       f32x4 sj[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sj[j] = mfma_bf16_k32(act[s][j], ones, z4);
+      for (int j = 0; j < 8; ++j) sj[j] = mfma_bf16_k32(act[s][b][j], ones, z4);
       if (m == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) scr[j * 16 + 4 * g + q] = sj[j][q];
       }
+      asm volatile("" ::: "memory");  // the reads below see the other lanes' writes
       u16 h0, l0, h1, l1;
       split_bf16(scr[(2 * g) * 16 + m], h0, l0);
       split_bf16(scr[(2 * g + 1) * 16 + m], h1, l1);
-      aS[s] = u32x2{(u32)h0 | ((u32)l0 << 16), (u32)h1 | ((u32)l1 << 16)};
+      aS[s][b] = u32x2{(u32)h0 | ((u32)l0 << 16), (u32)h1 | ((u32)l1 << 16)};
     }
   }
   float rs = 1.0f;  // 1 / rms of the input row
@@ -998,33 +1021,35 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) slots[t] = slot_of(q, t);
         if constexpr (WT == 12) {
-          q4_step_tl<NT>(slots, act[s], aS[s], lane, acc);
+          q4_step_tl<NT, BTN>(slots, act[s], aS[s], lane, acc);
         } else {
           u32 s16[NT];
 #pragma unroll
           for (int t = 0; t < NT; ++t)
             s16[t] = addr::q6_s16((u32)(uintptr_t)(tr[t].base + (size_t)(sb0 + s) * kQ6KBytes) + tr[t].off(n));
-          q6_step<NT, 1>(a, slots, s16, act[s], sb0 + s, lane, acc);
+          q6_step<NT, BTN, true>(a, slots, s16, &act[s][0][0], sb0 + s, lane, acc);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the group's partial sums: red[gl & 1][wave][t][lane * 2 + k]
-    float* rb = red + (size_t)(gl & 1) * nwaves * NT * 128;
+    // the group's partial sums: red[gl & 1][wave][t][b][lane * 2 + k]
+    float* rb = red + (size_t)(gl & 1) * nwaves * NT * BTN * 128;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float* r = rb + ((size_t)wave * NT + t) * 128 + lane * 2;
-      r[0] = acc[t][0][0] + acc[t][0][1];
-      r[1] = acc[t][0][2] + acc[t][0][3];
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[t][0][k] = 0.f;
-    }
+      for (int b = 0; b < BTN; ++b) {
+        float* r = rb + (((size_t)wave * NT + t) * BTN + b) * 128 + lane * 2;
+        r[0] = acc[t][b][0] + acc[t][b][1];
+        r[1] = acc[t][b][2] + acc[t][b][3];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[t][b][k] = 0.f;
+      }
     lds_barrier();
     if (e < n_elem) {
       float v = 0.f, v2 = 0.f;
       for (int w = 0; w < nwaves; ++w) {
-        v += rb[((size_t)w * NT + e_t) * 128 + e_rem];
-        if (a.epi == kEpiSwiGLU) v2 += rb[((size_t)w * NT + 1) * 128 + e_rem];
+        v += rb[(((size_t)w * NT + e_t) * BTN + e_b) * 128 + e_rem];
+        if (a.epi == kEpiSwiGLU) v2 += rb[(((size_t)w * NT + 1) * BTN + e_b) * 128 + e_rem];
       }
       const int lt = a.epi == kEpiSwiGLU ? local : local * NT + e_t;
       const bool live = e_brow < a.B && lt * 16 + e_nn < rows_of(seg);
@@ -1521,23 +1546,29 @@ hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStre
 // tile-loop plan and launch
 
 // ring depth by (type, NT): the deepest that fits kGemmLds with 8 waves
-constexpr int tl_ring(int wtype, int nt) { return wtype == 12 ? (nt == 1 ? 4 : 3) : (nt == 1 ? 4 : 2); }
+// ring depth by (type, NT, batch tiles): the deepest that fits kGemmLds with 8 waves
+constexpr int tl_ring(int wtype, int nt, int btn) {
+  return wtype == 12 ? (nt == 1 ? 4 : btn == 1 ? 3 : 2) : (nt == 1 ? 4 : 2);
+}
 
-// The epilogue gives each of a group's 128 outputs (a tile, or a gate/up pair, of 8 rows)
-// a thread of its own, so the workgroup needs at least two waves: K of at least three
-// super-blocks (one wave per two).
+// One or two activation tiles (at most 16 rows).  The epilogue gives each of a group's
+// 128 outputs per batch tile (a tile, or a gate/up pair, of 8 rows) a thread of its own,
+// so the workgroup needs two waves per batch tile: K of at least three super-blocks (one
+// wave per two) for 8 rows, seven for 16.
 bool use_tile_loop(int wtype, int groups, int K, int B) {
-  return (wtype == 12 || wtype == 14) && B <= 8 && K % kQK == 0 && K / kQK >= 3 && K / kQK <= 16 &&
+  const int nsb = K / kQK;
+  return (wtype == 12 || wtype == 14) && B <= 16 && K % kQK == 0 && nsb >= (B <= 8 ? 3 : 7) && nsb <= 16 &&
          groups >= 2 * variants().cus;
 }
 
-TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K) {
+TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K, int B) {
   TlPlan pl{};
   const int nsb = K / kQK;
+  const int btn = tl_btn(B);
   pl.waves = (nsb + 1) / 2;
-  pl.ring = tl_ring(wtype, nt);
+  pl.ring = tl_ring(wtype, nt, btn);
   const int stage = wtype == 12 ? kQ4Stage : kQ6Stage;
-  pl.lds = (size_t)pl.waves * pl.ring * nt * stage + (size_t)2 * pl.waves * nt * 128 * sizeof(float);
+  pl.lds = (size_t)pl.waves * pl.ring * nt * stage + (size_t)2 * pl.waves * nt * btn * 128 * sizeof(float);
   const int per_cu = max(1, kGemmLds / (int)pl.lds);
   int wgs = min(groups, variants().cus * per_cu);
   pl.groups_per_wg = (groups + wgs - 1) / wgs;
@@ -1546,22 +1577,30 @@ TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K) {
 }
 
 template <int WT, bool AL>
-const void* tl_fn(int nt) {
-  if (nt == 1) return (const void*)gemm_tl_kernel<WT, 1, AL, tl_ring(WT, 1)>;
-  return (const void*)gemm_tl_kernel<WT, 2, AL, tl_ring(WT, 2)>;
+const void* tl_fn(int nt, int btn) {
+  if (btn == 1) {
+    if (nt == 1) return (const void*)gemm_tl_kernel<WT, 1, AL, tl_ring(WT, 1, 1), 1>;
+    return (const void*)gemm_tl_kernel<WT, 2, AL, tl_ring(WT, 2, 1), 1>;
+  }
+  if (nt == 1) return (const void*)gemm_tl_kernel<WT, 1, AL, tl_ring(WT, 1, 2), 2>;
+  return (const void*)gemm_tl_kernel<WT, 2, AL, tl_ring(WT, 2, 2), 2>;
 }
 
 hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st) {
   if (pl.grid <= 0) return hipSuccess;
-  if ((nt != 1 && nt != 2) || pl.waves < 2 || pl.waves > 8 || pl.lds > (size_t)kGemmLds || a.B > 8 ||
-      (a.ss && a.ss_slots != 16) || (a.epi != kEpiSwiGLU && nt * 128 > pl.waves * 64))
+  const int btn = tl_btn(a.B);
+  if ((nt != 1 && nt != 2) || pl.waves < 2 || pl.waves > 8 || pl.lds > (size_t)kGemmLds || a.B > 16 ||
+      (a.ss && a.ss_slots != 16) || (a.epi == kEpiSwiGLU ? 1 : nt) * 128 * btn > pl.waves * 64)
     return hipErrorInvalidValue;
   const bool aligned = wtype == 12 || a.row_bytes % 16 == 0;
-  const void* fn = wtype == 12 ? tl_fn<12, true>(nt) : aligned ? tl_fn<14, true>(nt) : tl_fn<14, false>(nt);
+  const void* fn =
+      wtype == 12 ? tl_fn<12, true>(nt, btn) : aligned ? tl_fn<14, true>(nt, btn) : tl_fn<14, false>(nt, btn);
   static const bool lds_set = [] {
-    const void* all[] = {tl_fn<12, true>(1), tl_fn<12, true>(2), tl_fn<14, true>(1), tl_fn<14, true>(2),
-                         tl_fn<14, false>(1), tl_fn<14, false>(2)};
-    for (const void* f : all) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    for (int b = 1; b <= 2; ++b)
+      for (int t = 1; t <= 2; ++t) {
+        const void* all[] = {tl_fn<12, true>(t, b), tl_fn<14, true>(t, b), tl_fn<14, false>(t, b)};
+        for (const void* f : all) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+      }
     (void)hipGetLastError();
     return true;
   }();

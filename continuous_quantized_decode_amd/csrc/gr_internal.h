@@ -128,7 +128,8 @@ struct TlPlan {
   int waves, grid, groups_per_wg, ring;
   size_t lds;
 };
-TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K);
+TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K, int B);
+inline int tl_btn(int B) { return B <= 8 ? 1 : 2; }  // activation tiles of the tile loop
 hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st);
 hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);
 

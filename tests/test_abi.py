@@ -78,7 +78,13 @@ def test_gemm_launch_shape_names_the_kernel():
     assert not gr.gr_gemm_launch_shape(q4, 16384, 512, 8, gr.GEMM_EPI_STORE)["tile_loop"]
     assert gr.gr_gemm_launch_shape(q4, 16384, 768, 8, gr.GEMM_EPI_STORE)["tile_loop"]
     # more than one batch tile, or K above 16 super-blocks: split-K
-    assert not gr.gr_gemm_launch_shape(q6, 128256, 4096, 9, gr.GEMM_EPI_STORE)["tile_loop"]
+    # up to 16 rows (two activation tiles) with K of seven super-blocks or more: the tile
+    # loop with two batch tiles
+    two = gr.gr_gemm_launch_shape(q6, 128256, 4096, 9, gr.GEMM_EPI_STORE)
+    assert two["tile_loop"] and two["btn"] == 2 and two["kernel"] == "gemm_tl_kernel<14, 1,"
+    assert gr.gr_gemm_launch_shape(q4, 14336, 4096, 16, gr.GEMM_EPI_SWIGLU)["tile_loop"]
+    assert not gr.gr_gemm_launch_shape(q4, 16384, 1536, 16, gr.GEMM_EPI_STORE)["tile_loop"]
+    assert not gr.gr_gemm_launch_shape(q6, 128256, 4096, 17, gr.GEMM_EPI_STORE)["tile_loop"]
     assert not gr.gr_gemm_launch_shape(q6, 128256, 4352, 8, gr.GEMM_EPI_STORE)["tile_loop"]
     L = gr.lib()
     out = [ctypes.c_int() for _ in range(6)]

@@ -109,6 +109,9 @@ GEMM_CASES = [
     (synth.W_Q4_K, 8, 16384, 256),   # the same at 8 rows (every row's outputs written)
     (synth.W_Q6_K, 6, 9000, 512),
     (synth.W_Q4_K, 8, 9000, 768),    # three super-blocks: the smallest tile-loop K
+    (synth.W_Q4_K, 12, 9000, 2048),  # tile loop with two batch tiles (ragged rows and tiles)
+    (synth.W_Q6_K, 16, 8200, 4096),
+    (synth.W_Q6_K, 10, 9000, 1792),  # 2-byte aligned rows, seven super-blocks
     # Q5_K and Q8_0 rows (split-K kernel only): every batch-tile count, ragged rows
     (synth.W_Q5_K, 1, 16, 256),
     (synth.W_Q5_K, 2, 40, 768),

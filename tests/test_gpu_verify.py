@@ -153,6 +153,14 @@ def test_verify_llama3_layers_and_head(torch, gr, orc):
     _run(torch, gr, orc, wl, ctx, 5, 2, with_head=True, seed=2)
 
 
+def test_verify_llama3_t2_one_layer_and_head(torch, gr, orc):
+    """bench.py's verification shape (Llama-3-8B, B = 8, T = 2: 16 rows), one layer and the
+    head: gate/up and the head take the tile loop with two batch tiles."""
+    wl = dataclasses.replace(synth.WORKLOADS["llama3_8b"], n_layers=1)
+    assert gr.gr_gemm_launch_shape(wl.w_head, wl.vocab, wl.hidden, 16)["btn"] == 2
+    _run(torch, gr, orc, wl, synth.ctx_lens(wl), 2, 1, with_head=True, seed=6)
+
+
 def test_spec_accept_matches_oracle(torch, gr, orc):
     rng = np.random.default_rng(3)
     b, t = 37, 6
