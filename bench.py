@@ -74,8 +74,8 @@ def stage_bytes(wl, ctx, kvb_tok):
     pages = int(np.sum((ctx.astype(np.int64) + 16) // 16))
     s = {
         "qkv": weight_bytes(t, qd + 2 * kvd, H) + B * H * 4 + B * (qd + 2 * kvd) * 4,
-        "attn": kv_read + B * kvb_tok + B * (qd + 2 * kvd) * 4 + pages * 4,
-        "attn_merge": B * qd * 4,
+        # K + V read, the new token's K + V written, q/k/v read, the Wo input written
+        "attn": kv_read + B * kvb_tok + B * (qd + 2 * kvd) * 4 + pages * 4 + B * qd * 4,
         "wo": weight_bytes(t, H, qd) + B * qd * 4 + 3 * B * H * 4,
         "gate_up": 2 * weight_bytes(t, F, H) + B * H * 4 + B * F * 4,
         "down": weight_bytes(wl.w_down, H, F) + B * F * 4 + 3 * B * H * 4,
@@ -419,8 +419,7 @@ def stage_launches(gr, wl) -> dict:
     out = {s: (sh["kernel"], sh["grid_threads"])
            for s, sh in ((s, gr.gr_gemm_launch_shape(*v[:3], B, v[3])) for s, v in shapes.items())}
     kvdt = {0: 0, 1: 1, 2: 2}[wl.kv_dtype]
-    out["attn"] = (f"attn_split_kernel<{kvdt}, {wl.head_dim}, true>", None)
-    out["attn_merge"] = ("attn_merge_kernel", None)
+    out["attn"] = (f"attn_decode_kernel<{kvdt}, {wl.head_dim}, true>", None)
     out["pack"] = ("pack_rows_kernel", None)
     return out
 
@@ -580,6 +579,8 @@ def main():
     stages = {}
     for si, name in enumerate(gr.STAGES):
         if name == "head" and not wl.vocab:
+            continue
+        if name == "attn_merge":  # the decode step merges inside the attention kernel
             continue
         once = name in ("head", "pack")
         durs = []

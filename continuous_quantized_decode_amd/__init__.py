@@ -83,6 +83,9 @@ def _load() -> C.CDLL:
     L.gr_paged_decode_attn_workspace_size.restype = _sz
     L.gr_paged_decode_attn.argtypes = [_p, _p, _p, _p, _p, _p, _i, C.POINTER(AttnMeta), _p, _sz, _p]
     L.gr_paged_decode_attn.restype = _i
+    L.gr_attn_launch_shape.argtypes = [_i, _i, _i, _i, C.POINTER(_i), C.POINTER(_i), C.POINTER(_i),
+                                       C.POINTER(C.c_longlong)]
+    L.gr_attn_launch_shape.restype = _i
     L.gr_paged_gather_kv.argtypes = [_p, _i, _p, _p, _i, C.POINTER(AttnMeta), _p, _p]
     L.gr_paged_gather_kv.restype = _i
     L.gr_decode_layer_workspace_size.argtypes = [C.POINTER(LayerCfg), _i, _i]
@@ -117,7 +120,7 @@ def _load() -> C.CDLL:
     L.gr_sample_workspace_size.restype = _sz
     L.gr_sample.argtypes = [_p, _i, _i, _p, _p, _p, _p, _sz, _p]
     L.gr_sample.restype = _i
-    if L.gr_abi_version() != 7:
+    if L.gr_abi_version() != 8:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
     return L
@@ -130,7 +133,7 @@ def lib() -> C.CDLL:
 EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_bytes", "gr_q4k_dequant",
             "gr_q6k_dequant", "gr_q8_0_dequant", "gr_gemm_workspace_size", "gr_gemm_launch_shape", "gr_q4k_gemm",
             "gr_q6k_gemm", "gr_q5k_gemm", "gr_q8_0_gemm",
-            "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_paged_gather_kv",
+            "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_attn_launch_shape", "gr_paged_gather_kv",
             "gr_decode_layer_workspace_size", "gr_decode_layer", "gr_output_head_workspace_size", "gr_output_head",
             "gr_decode_stack_workspace_size", "gr_decode_stack", "gr_decode_stack_probed", "gr_sample_workspace_size",
             "gr_sample", "gr_verify_stack_workspace_size", "gr_verify_stack", "gr_spec_accept",
@@ -246,6 +249,17 @@ def gr_gemm_launch_shape(wtype: int, rows: int, k: int, b: int, epi: int = GEMM_
 
 
 # --------------------------------------------------------------------------- attention
+
+def gr_attn_launch_shape(kv_dtype: int, b: int, n_kv_heads: int, max_tokens: int) -> dict:
+    """Launch shape of the decode attention (waves per workgroup, pages per wave, the most
+    workgroups of one (row, KV head), grid threads) for rows of up to max_tokens tokens."""
+    v = [C.c_int() for _ in range(3)]
+    g = C.c_longlong()
+    _check("gr_attn_launch_shape", _load().gr_attn_launch_shape(kv_dtype, b, n_kv_heads, max_tokens,
+                                                                *[C.byref(i) for i in v], C.byref(g)))
+    return {"waves_per_wg": v[0].value, "pages_per_wave": v[1].value, "wg_per_row": v[2].value,
+            "grid_threads": g.value, "kernel": f"attn_decode_kernel<{kv_dtype},"}
+
 
 def attn_meta(n_q_heads, n_kv_heads, head_dim, kv_dtype, num_pages, max_blocks, max_ctx, scale=None) -> AttnMeta:
     return AttnMeta(n_q_heads, n_kv_heads, head_dim, PAGE_SIZE, kv_dtype, num_pages, max_blocks, max_ctx,

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libgr.so")
-SOURCES = ["api.hip", "gemm.hip", "attn.hip", "pack.hip", "dequant.hip", "sample.hip"]
+SOURCES = ["api.hip", "gemm.hip", "attn.hip", "attn_decode.hip", "pack.hip", "dequant.hip", "sample.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

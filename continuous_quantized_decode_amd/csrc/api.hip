@@ -236,6 +236,10 @@ struct LayerBufs {
   float* qbuf;   // [B][Hq][D]: roped queries when a step carries several tokens per sequence
   float* part;   // many-row K-split partial sums (more than 64 rows), part_cap floats
   size_t part_cap;
+  float* wg_part;     // decode attention: workgroup partial states
+  uint32_t* wg_cnt;   // decode attention: arrival counters [B][Hkv], zeroed by the input pack
+  int n_cnt;
+  uint32_t* sched;    // decode attention: the step's work list, built by the input pack
 };
 
 // floats of the many-row K-split partial sums for `rows` rows and outputs of `cols`
@@ -262,6 +266,10 @@ LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan&
   L.qbuf = c.take<float>((size_t)B * qd * 4);
   L.part_cap = mm_part_floats(B, qd + 2 * kvd > cfg->hidden ? qd + 2 * kvd : cfg->hidden);
   L.part = L.part_cap ? c.take<float>(L.part_cap * 4) : nullptr;
+  L.n_cnt = B * cfg->n_kv_heads;
+  L.wg_cnt = c.take<uint32_t>((size_t)L.n_cnt * 4);
+  L.wg_part = c.take<float>(attn_dec_part_floats(B, cfg->n_q_heads, cfg->head_dim, ap.dec_wg_max > 1 ? ap.dec_wg_max : 1) * 4);
+  L.sched = c.take<uint32_t>(attn_sched_words(B, ap.dec_wg_max > 1 ? ap.dec_wg_max : 1) * 4);
   return L;
 }
 
@@ -298,7 +306,11 @@ gr_status check_layer_w(const gr_layer_cfg* c, const gr_layer_weights* w) {
 
 // rows = B * T attention rows; a sequence holds at most max_ctx + T tokens after the step
 AttnPlan layer_attn_plan(int rows, const gr_layer_cfg* c, int max_ctx, int T = 1) {
-  return plan_attn(rows, c->n_kv_heads, max_ctx + T);
+  AttnPlan pl = plan_attn(rows, c->n_kv_heads, max_ctx + T);
+  const AttnDecPlan dp = plan_attn_dec(c->kv_dtype, max_ctx + T);
+  pl.dec_wg_max = dp.wg_max;
+  pl.dec_wg_pages = dp.wg_pages;
+  return pl;
 }
 
 // Optional timing probe: the launches of one stage (repeated `reps` times) carry the
@@ -338,11 +350,29 @@ Kinds qkv_kinds(const gr_layer_weights* w) {
 // Pack of the layer input: x * attn_norm and its sum of squares (and, for a decode
 // step, the RoPE table of its positions).
 gr_status run_input_pack(const float* x, int B, int H, const float* gain, Kinds k, const Pack2& xp, float* ss,
-                         hipStream_t st, const Probe* probe, RopeTable rope = RopeTable{}, RowSel sel = RowSel{}) {
+                         hipStream_t st, const Probe* probe, RopeTable rope = RopeTable{}, RowSel sel = RowSel{},
+                         AttnSched sched = AttnSched{}) {
   return probed(probe, GR_STAGE_PACK, st, [&] {
-    return check_launch(
-        launch_pack_rows(x, H, B, H, gain, k.k32 ? xp.k32 : kNoPack, k.k16 ? xp.k16 : kNoPack, ss, st, rope, sel));
+    return check_launch(launch_pack_rows(x, H, B, H, gain, k.k32 ? xp.k32 : kNoPack, k.k16 ? xp.k16 : kNoPack, ss,
+                                         st, rope, sel, sched));
   });
+}
+
+// The decode attention's work list and arrival counters, built and cleared by a decode
+// step's first kernel (one token per row).
+AttnSched attn_sched(const LayerBufs& L, const int32_t* ctx, int B, const AttnPlan& apl) {
+  AttnSched z;
+  z.ctx = ctx;
+  z.B = B;
+  z.self = 1;
+  z.n_kv_heads = L.n_cnt / (B > 0 ? B : 1);
+  z.slots = attn_dec_slots();
+  z.group_pages = apl.dec_wg_pages;
+  z.max_groups = kAttnDecMaxGroups;
+  z.list = L.sched;
+  z.cnt = L.wg_cnt;
+  z.n_cnt = L.n_cnt;
+  return z;
 }
 
 RopeTable rope_table(const gr_layer_cfg* c, const int32_t* ctx, const LayerBufs& L, int T = 1,
@@ -433,7 +463,19 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   ap.m_part = L.m_part;
   ap.l_part = L.l_part;
   if (rm.fused()) {
-    s = probed(probe, GR_STAGE_ATTN, st, [&] { return check_launch(launch_attn_split(c->kv_dtype, true, ap, st)); });
+    // one token per sequence: the decode kernel stores the new K/V, attends, merges its
+    // workgroups' partial states and writes the Wo input pack (no merge launch)
+    const PackOut& op = L.op.of(w->to);
+    ap.wg_part = L.wg_part;
+    ap.wg_cnt = L.wg_cnt;
+    ap.wg_max = apl.dec_wg_max;
+    ap.wg_pages = apl.dec_wg_pages;
+    ap.sched = L.sched;
+    ap.pack = op.pack;
+    ap.pack_kind = op.kind;
+    ap.pack_nslices = nslices_of(op.kind, qd);
+    s = probed(probe, GR_STAGE_ATTN, st, [&] { return check_launch(launch_attn_decode(c->kv_dtype, true, ap, st)); });
+    if (s != GR_OK) return s;
   } else {
     // several tokens of a sequence: every row's K/V is stored before any row attends
     ap.q = L.qbuf;
@@ -441,15 +483,14 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
       const hipError_t e = launch_attn_append(c->kv_dtype, ap, L.qbuf, st);
       return check_launch(e != hipSuccess ? e : launch_attn_split(c->kv_dtype, false, ap, st));
     });
+    if (s != GR_OK) return s;
+    // 3. log-sum-exp merge -> Wo input pack
+    s = probed(probe, GR_STAGE_ATTN_MERGE, st, [&] {
+      const PackOut& op = L.op.of(w->to);
+      return check_launch(launch_attn_merge(ap, nullptr, op.pack, op.kind, nslices_of(op.kind, qd), 0, st));
+    });
+    if (s != GR_OK) return s;
   }
-  if (s != GR_OK) return s;
-  // 3. log-sum-exp merge -> Wo input pack
-  s = probed(probe, GR_STAGE_ATTN_MERGE, st, [&] {
-    const PackOut& op = L.op.of(w->to);
-    return check_launch(
-        launch_attn_merge(ap, nullptr, op.pack, op.kind, nslices_of(op.kind, qd), rm.fused() ? 1 : 0, st));
-  });
-  if (s != GR_OK) return s;
   // 4. x += Wo o; pack x * ffn_norm and its sum of squares for the gate/up GEMM
   s = probed(probe, GR_STAGE_WO, st, [&] {
     const void* ws[1] = {w->wo};
@@ -668,17 +709,28 @@ static gr_status check_meta(const gr_attn_meta* m) {
   if (m->n_q_heads / m->n_kv_heads > 8) return GR_ERR_SHAPE;
   if (m->num_pages <= 0 || m->max_blocks_per_row <= 0 || m->max_ctx <= 0) return GR_ERR_SHAPE;
   if ((int64_t)m->max_ctx > (int64_t)GR_PAGE_SIZE * m->max_blocks_per_row) return GR_ERR_CAPACITY;
+  if (plan_attn_dec(m->kv_dtype, m->max_ctx).wg_max == 0) return GR_ERR_CAPACITY;
   return GR_OK;
+}
+
+// Standalone decode attention workspace: arrival counters [B][Hkv], then the workgroup
+// partial states.
+static void carve_attn_ws(Carver& c, const gr_attn_meta* m, int B, AttnParams& ap, uint32_t** list) {
+  const AttnDecPlan dp = plan_attn_dec(m->kv_dtype, m->max_ctx);
+  ap.wg_max = dp.wg_max;
+  ap.wg_pages = dp.wg_pages;
+  ap.wg_cnt = c.take<uint32_t>((size_t)B * m->n_kv_heads * 4);
+  ap.wg_part = c.take<float>(attn_dec_part_floats(B, m->n_q_heads, m->head_dim, ap.wg_max) * 4);
+  *list = c.take<uint32_t>(attn_sched_words(B, ap.wg_max) * 4);
+  ap.sched = *list;
 }
 
 size_t gr_paged_decode_attn_workspace_size(const gr_attn_meta* m, int B) {
   if (check_meta(m) != GR_OK || B <= 0) return 0;
-  const AttnPlan pl = plan_attn(B, m->n_kv_heads, m->max_ctx);
   Carver c(nullptr);
-  const size_t units = (size_t)B * m->n_q_heads * pl.max_splits;
-  c.take<float>(units * m->head_dim * 4);
-  c.take<float>(units * 4);
-  c.take<float>(units * 4);
+  AttnParams ap{};
+  uint32_t* list;
+  carve_attn_ws(c, m, B, ap, &list);
   return c.off + 256;
 }
 
@@ -697,33 +749,52 @@ gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* 
   if (!ws || ws_bytes < gr_paged_decode_attn_workspace_size(m, B) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
   s = check_device();
   if (s != GR_OK) return s;
-  const AttnPlan pl = plan_attn(B, m->n_kv_heads, m->max_ctx);
   Carver c(ws);
-  const size_t units = (size_t)B * m->n_q_heads * pl.max_splits;
   AttnParams ap{};
+  uint32_t* list;
+  carve_attn_ws(c, m, B, ap, &list);
   ap.tokens_per_seq = 1;
-  ap.self_in_pool = 0;
-  ap.rows_per_unit = 1;
-  ap.o_part = c.take<float>(units * m->head_dim * 4);
-  ap.m_part = c.take<float>(units * 4);
-  ap.l_part = c.take<float>(units * 4);
   ap.B = B;
   ap.n_q_heads = m->n_q_heads;
   ap.n_kv_heads = m->n_kv_heads;
   ap.head_dim = m->head_dim;
   ap.max_blocks = m->max_blocks_per_row;
-  ap.pages_per_split = pl.pages_per_split;
-  ap.max_splits = pl.max_splits;
   ap.scale = m->scale;
   ap.block_table = block_table;
   ap.ctx_lens = ctx_lens;
   ap.k_pages = k_pages;
   ap.v_pages = v_pages;
   ap.q = q;
+  ap.out = out;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_attn_split(m->kv_dtype, false, ap, st);
+  AttnSched sc;
+  sc.ctx = ctx_lens;
+  sc.B = B;
+  sc.self = 0;
+  sc.n_kv_heads = m->n_kv_heads;
+  sc.slots = attn_dec_slots();
+  sc.group_pages = ap.wg_pages;
+  sc.max_groups = kAttnDecMaxGroups;
+  sc.list = list;
+  sc.cnt = ap.wg_cnt;
+  sc.n_cnt = B * m->n_kv_heads;
+  hipError_t e = launch_attn_sched(sc, st);
   if (e != hipSuccess) return check_launch(e);
-  return check_launch(launch_attn_merge(ap, out, nullptr, 0, 0, 0, st));
+  return check_launch(launch_attn_decode(m->kv_dtype, false, ap, st));
+}
+
+gr_status gr_attn_launch_shape(int kv_dtype, int B, int n_kv_heads, int max_tokens, int* waves_per_wg,
+                               int* pages_per_wave, int* wg_per_row, long long* grid_threads) {
+  if (!waves_per_wg || !pages_per_wave || !wg_per_row || !grid_threads) return GR_ERR_NULL;
+  if (!kv_ok(kv_dtype)) return GR_ERR_DTYPE;
+  if (B <= 0 || n_kv_heads <= 0 || max_tokens <= 0) return GR_ERR_SHAPE;
+  const AttnDecPlan dp = plan_attn_dec(kv_dtype, max_tokens);
+  if (dp.wg_max == 0) return GR_ERR_CAPACITY;
+  *waves_per_wg = kAttnDecWaves;
+  *pages_per_wave = dp.wg_pages / kAttnDecWaves;
+  *wg_per_row = dp.wg_max;
+  *grid_threads = (long long)B * n_kv_heads * dp.wg_max * kAttnDecWaves * 64;
+  return GR_OK;
 }
 
 gr_status gr_paged_gather_kv(const void* pages, int is_v, const int32_t* block_table, const int32_t* ctx_lens, int B,
@@ -772,6 +843,9 @@ static gr_status check_layer_call(const gr_layer_cfg* c, const gr_layer_weights*
   if (row_pos ? !row_seq : !ctx) return GR_ERR_NULL;
   if (num_pages <= 0 || max_blocks <= 0 || max_ctx < 0) return GR_ERR_SHAPE;
   if ((int64_t)max_ctx + T > (int64_t)GR_PAGE_SIZE * max_blocks) return GR_ERR_CAPACITY;
+  // one token per sequence: the decode attention kernel's longest context
+  if (T == 1 && !row_pos && plan_attn_dec(c->kv_dtype, max_ctx + 1).wg_max == 0)
+    return GR_ERR_CAPACITY;
   if (!aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(x, 16) || !aligned(bt, 4) || !aligned(ctx, 4) ||
       !aligned(row_seq, 4) || !aligned(row_pos, 4))
     return GR_ERR_ALIGN;
@@ -791,7 +865,8 @@ gr_status gr_decode_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void
   Carver cv(ws);
   const LayerBufs L = carve_layer(cv, c, B, apl);
   hipStream_t st = (hipStream_t)stream;
-  s = run_input_pack(x, B, c->hidden, w->attn_norm, qkv_kinds(w), L.xp, L.ss_attn, st, nullptr, rope_table(c, ctx, L));
+  s = run_input_pack(x, B, c->hidden, w->attn_norm, qkv_kinds(w), L.xp, L.ss_attn, st, nullptr, rope_table(c, ctx, L),
+                     RowSel{}, attn_sched(L, ctx, B, apl));
   if (s != GR_OK) return s;
   return run_layer(c, w, k_pages, v_pages, x, bt, max_blocks, ctx, B, apl, L, nullptr, Kinds{}, st, nullptr);
 }
@@ -896,7 +971,8 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
   if (probe) probe->layer = 0;
   if (n_layers > 0) {
     s = run_input_pack(x, rows, c->hidden, weights[0].attn_norm, qkv_kinds(&weights[0]), L.xp, L.ss_attn, st, probe,
-                       rope_table(c, ctx, L, T, rm.pos));
+                       rope_table(c, ctx, L, T, rm.pos), RowSel{},
+                       rm.fused() ? attn_sched(L, ctx, rows, apl) : AttnSched{});
   } else if (head_w) {
     Kinds k;
     k.add(head_wtype);

@@ -40,6 +40,17 @@ struct AttnParams {
   float* o_part;
   float* m_part;
   float* l_part;
+  // decode kernel (one token per row; the log-sum-exp merge is done by the workgroup
+  // that finishes a (row, KV head) last): workgroup partials [B * Hkv][wg_max][R (D + 2)]
+  // (o[R][D], then m[R], l[R]), arrival counters [B * Hkv] (zero between launches), and
+  // the output: f32 out [B][Hq][D] and / or the Wo input actpack (pack, kind, nslices)
+  float* wg_part;
+  uint32_t* wg_cnt;
+  int wg_max, wg_pages;
+  const uint32_t* sched;  // the work list (AttnSched): workgroup i * Hkv + g takes entry i
+  float* out;
+  uint16_t* pack;
+  int pack_kind, pack_nslices;
 };
 
 // Sequence and position of attention row b.
@@ -56,6 +67,8 @@ GR_DEV void attn_row_place(const AttnParams& p, int b, int& seq, int& pos) {
 
 struct AttnPlan {
   int pages_per_split, max_splits;
+  int dec_wg_max = 0, dec_wg_pages = 0;  // decode kernel (one token per row): workgroups per
+                                         // (row, KV head), pages per workgroup
 };
 
 AttnPlan plan_attn(int B, int n_kv_heads, int max_ctx_tokens);
@@ -63,6 +76,30 @@ size_t attn_partial_floats(int B, int n_q_heads, int head_dim, const AttnPlan& p
 hipError_t launch_attn_split(int kv_dtype, bool fused, const AttnParams& p, hipStream_t st);
 hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, int kind, int nslices, int fused,
                              hipStream_t st);
+// Decode attention with the merge folded in (one token per row): workgroups of
+// kAttnDecWaves waves take kAttnDecWaves * attn_dec_pages consecutive pages of one (row,
+// KV head); each wave loads its pages all at once.
+constexpr int kAttnDecWaves = 4;
+constexpr int kAttnDecMaxWg = 256;  // workgroups per (row, KV head) one merge takes
+constexpr int kAttnDecMaxGroups = 8;  // groups of pages per workgroup
+constexpr int kAttnDecWgPerCu = 2;    // resident workgroups per CU (two waves per SIMD)
+// pages per wave: every page in flight at once within two waves' registers per SIMD
+__host__ __device__ constexpr int attn_dec_pages(int kv_dtype) {
+  return kv_dtype == KV_F32_T ? 2 : kv_dtype == KV_F16_T ? 4 : 8;
+}
+struct AttnDecPlan {
+  int wg_pages;  // pages per workgroup
+  int wg_max;    // the most workgroups of one (row, KV head); 0: max_tokens too long
+};
+AttnDecPlan plan_attn_dec(int kv_dtype, int max_tokens);
+int attn_dec_slots();  // resident decode-attention workgroups of the device
+size_t attn_dec_part_floats(int B, int n_q_heads, int head_dim, int wg_max);
+// fused: the decode layer's variant (QK-norm, RoPE and the KV append of the new token
+// from p.qkv, n_tok = ctx + 1); otherwise q from p.q and ctx tokens already in the pool.
+hipError_t launch_attn_decode(int kv_dtype, bool fused, const AttnParams& p, hipStream_t st);
+// The work list and cleared counters of a standalone call (one workgroup).
+hipError_t launch_attn_sched(const struct AttnSched& s, hipStream_t st);
+
 // QK-norm and RoPE of every row's q and k, the row's K/V stored at its position (several
 // tokens of a sequence in one step), q written to q_out [B][Hq][D] for the standalone kernel.
 hipError_t launch_attn_append(int kv_dtype, const AttnParams& p, float* q_out, hipStream_t st);

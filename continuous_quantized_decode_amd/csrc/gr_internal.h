@@ -204,8 +204,86 @@ struct RowSel {
   const int32_t* idx = nullptr;
   int src_rows = 0;
 };
+// The decode attention's work list of a step (one token per row), built once per step
+// by its first kernel (one block) and read by every layer's attention.  Pages per
+// workgroup P: a multiple of group_pages, at most max_groups groups, chosen so that the
+// step's workgroups (each row's ceil(pages / P) ranges times the KV heads) about fill
+// `slots` resident workgroups.  The list: [0] its entries, [1] P, then per row b (in
+// order) and range j < ceil(ceil((ctx[b] + self) / 16) / P) the entry
+// {(b << 16) | j, ctx[b]}; and the attention's arrival counters cleared.
+struct AttnSched {
+  const int32_t* ctx = nullptr;
+  int B = 0, self = 1;
+  int n_kv_heads = 1, slots = 512, group_pages = 16, max_groups = 8;
+  uint32_t* list = nullptr;  // entry i at list[2 + 2 i], list[3 + 2 i]
+  uint32_t* cnt = nullptr;   // arrival counters to clear
+  int n_cnt = 0;
+};
+// Words of a list for B rows of up to wg_max ranges each.
+inline size_t attn_sched_words(int B, int wg_max) { return 2 + 2 * (size_t)B * wg_max; }
+// The list and the counters by one workgroup of blockDim.x threads (a multiple of 64).
+GR_DEV uint32_t block_sum_u32(uint32_t v, uint32_t* lds_scratch) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) lds_scratch[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < (int)blockDim.x / 64; ++w) t += lds_scratch[w];
+  __syncthreads();
+  return t;
+}
+GR_DEV void build_attn_sched(const AttnSched& s, uint32_t* lds_scratch /* blockDim.x / 64 + 1 words */) {
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < s.n_cnt; i += nthr) s.cnt[i] = 0u;
+  // pages per workgroup from the step's total
+  uint32_t mine = 0;
+  for (int b = tid; b < s.B; b += nthr) mine += (uint32_t)((s.ctx[b] + s.self + 15) / 16);
+  const uint64_t total = (uint64_t)block_sum_u32(mine, lds_scratch) * (uint64_t)s.n_kv_heads;
+  const uint64_t gp = (uint64_t)s.group_pages;
+  uint64_t want = (total + (uint64_t)s.slots - 1) / (uint64_t)s.slots;
+  want = (want + gp - 1) / gp * gp;
+  const uint32_t wpp = (uint32_t)(want < gp ? gp : want > gp * (uint64_t)s.max_groups ? gp * s.max_groups : want);
+  uint32_t running = 0;
+  for (int b0 = 0; b0 < s.B; b0 += nthr) {
+    const int b = b0 + tid;
+    const int c = b < s.B ? s.ctx[b] : 0;
+    const uint32_t pages = b < s.B ? (uint32_t)((c + s.self + 15) / 16) : 0u;
+    const uint32_t n = (pages + wpp - 1) / wpp;
+    // inclusive scan of n over the workgroup: within waves, then the wave totals
+    uint32_t v = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = __shfl_up(v, o, 64);
+      if (lane >= o) v += u;
+    }
+    if (lane == 63) lds_scratch[wave] = v;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t acc = 0;
+      for (int w = 0; w < nthr / 64; ++w) {
+        const uint32_t t = lds_scratch[w];
+        lds_scratch[w] = acc;
+        acc += t;
+      }
+      lds_scratch[nthr / 64] = acc;
+    }
+    __syncthreads();
+    const uint32_t first = running + lds_scratch[wave] + v - n;
+    for (uint32_t r = 0; r < n; ++r) {
+      s.list[2 + 2 * (first + r)] = ((uint32_t)b << 16) | r;
+      s.list[3 + 2 * (first + r)] = (uint32_t)c;
+    }
+    running += lds_scratch[nthr / 64];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    s.list[0] = running;
+    s.list[1] = wpp;
+  }
+}
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
                             float* ss_out, hipStream_t st,  // ss_out: [ss_slots(B)][B], slot 0 the sum
-                            RopeTable rope = RopeTable{}, RowSel sel = RowSel{});
+                            RopeTable rope = RopeTable{}, RowSel sel = RowSel{}, AttnSched sched = AttnSched{});
 
 }  // namespace gr

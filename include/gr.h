@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GR_ABI_VERSION 7
+#define GR_ABI_VERSION 8
 
 typedef enum {
   GR_OK = 0,
@@ -138,12 +138,23 @@ typedef struct {
  * q, out: f32 [B][n_q_heads][head_dim]; row b attends its first ctx_lens[b] tokens
  * (1 <= ctx_lens[b] <= max_ctx, all already in the pools); query head h uses KV head
  * h / (n_q_heads / n_kv_heads).  out[b][h] = sum_t softmax_t(scale * q.k_t) v_t.
- * The context is cut into page-aligned splits processed in parallel and merged by
- * log-sum-exp.  Pools and q 16-byte aligned. */
+ * The context is cut into page-aligned ranges processed by separate workgroups whose
+ * softmax states the last one to finish merges by log-sum-exp.  Pools and q 16-byte
+ * aligned.  GR_ERR_CAPACITY when max_ctx needs more ranges than one merge takes
+ * (see gr_attn_launch_shape).  The workspace holds per-row arrival counters that
+ * the call clears first: calls that share a workspace must not overlap. */
 size_t gr_paged_decode_attn_workspace_size(const gr_attn_meta* m, int B);
 gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                                const int32_t* ctx_lens, float* out, int B, const gr_attn_meta* m, void* workspace,
                                size_t ws_bytes, void* stream);
+
+/* Launch shape of the decode attention for rows of up to max_tokens attended tokens
+ * (profiling aid and test of the page walk): waves per workgroup, pages per wave, the
+ * most workgroups one (row, KV head) takes, and the grid in threads for B rows and
+ * n_kv_heads heads.  GR_ERR_CAPACITY when max_tokens needs more workgroups than the
+ * merging workgroup takes (the decode layer then rejects max_ctx + 1 as well). */
+gr_status gr_attn_launch_shape(int kv_dtype, int B, int n_kv_heads, int max_tokens, int* waves_per_wg,
+                               int* pages_per_wave, int* wg_per_row, long long* grid_threads);
 
 /* Test export (bit-exactness of the page walk): decode the first ctx_lens[b] tokens
  * of each row of one pool (is_v selects the V layout) into out f32

@@ -27,3 +27,13 @@ def rel_l2(got, want) -> float:
 
 def say(*a):
     print(*a, flush=True)
+
+
+def row_rel_l2(got, want) -> float:
+    """Largest relative L2 error of any row (first axis; the other axes flattened), so
+    that one wrong row or tile cannot hide inside a tensor-wide norm."""
+    got = np.asarray(got, dtype=np.float64).reshape(len(got), -1)
+    want = np.asarray(want, dtype=np.float64).reshape(len(want), -1)
+    num = np.linalg.norm(got - want, axis=1)
+    den = np.maximum(np.linalg.norm(want, axis=1), 1e-300)
+    return float(np.max(num / den))

@@ -37,7 +37,7 @@ def test_host_side_checks_without_gpu():
     """Calls that fail a host check return their status before touching the device."""
     import continuous_quantized_decode_amd as gr
     L = gr.lib()
-    assert L.gr_abi_version() == 7
+    assert L.gr_abi_version() == 8
     assert L.gr_status_str(-6) == b"max_ctx + 1 tokens exceed the block table's pages"
     assert L.gr_kv_head_bytes(2, 128) == 16 * 128 + 16 * 4 * 2
     assert L.gr_kv_head_bytes(7, 128) == -1
@@ -154,3 +154,32 @@ def test_mixed_stack_head_rows_host_checks():
     assert call(p, 0) == -2
     assert call(p + 2, 2) == -4  # misaligned index array
     assert call(p, 2, rows=513) == -2  # above the 512-row step budget
+
+
+def test_attn_launch_shape():
+    """The decode attention's plan (host-only call): four waves per workgroup, each with
+    all of its pages in flight (f32 2, f16 4, q8_0 8 pages); the long-context workload's
+    rows take more than 64 workgroups, whose states the last one merges; a context past
+    256 workgroups is refused before anything runs, by the decode layer too."""
+    import continuous_quantized_decode_amd as gr
+    sh = gr.gr_attn_launch_shape(2, 64, 8, 32768 + 1)  # q8_0: 32 pages per workgroup
+    assert sh["waves_per_wg"] == 4 and sh["pages_per_wave"] == 8
+    assert sh["wg_per_row"] == -(-2049 // 32) > 64
+    assert sh["grid_threads"] == 64 * 8 * sh["wg_per_row"] * 256
+    llama = gr.gr_attn_launch_shape(1, 8, 8, 3574)  # f16: 16 pages per workgroup
+    assert llama["pages_per_wave"] == 4 and llama["wg_per_row"] == 14
+    assert gr.gr_attn_launch_shape(1, 8, 8, 16)["wg_per_row"] == 1
+    assert gr.gr_attn_launch_shape(0, 1, 1, 16 * 8 + 1)["wg_per_row"] == 2  # f32: 8 pages per workgroup
+    assert gr.gr_attn_launch_shape(1, 1, 1, 256 * 16 * 16)["wg_per_row"] == 256
+    L = gr.lib()
+    v = [ctypes.c_int() for _ in range(3)]
+    g = ctypes.c_longlong()
+    too_long = 256 * 16 * 16 + 1  # f16: 256 workgroups of 16 pages
+    assert L.gr_attn_launch_shape(1, 1, 1, too_long, *[ctypes.byref(i) for i in v], ctypes.byref(g)) == -6
+    # the same limit for a decode layer: max_ctx + 1 tokens
+    cfg = gr.layer_cfg(256, 4, 2, 64, 768, 1e-6, 1e4, 0, 0, 1)
+    buf = ctypes.create_string_buffer(4096)
+    p = ctypes.addressof(buf) + (-ctypes.addressof(buf) % 256)
+    w = gr.LayerWeights(*([p] * 11 + [12] * 7))
+    assert L.gr_decode_layer(ctypes.byref(cfg), ctypes.byref(w), p, p, 9, p, p, 5000, p, too_long - 1, 1, p,
+                             1 << 20, None) == -6

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import dev, host, rel_l2, say, torch_cuda
+from gpu_util import dev, host, rel_l2, row_rel_l2, say, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -119,10 +119,18 @@ def test_llama3_8b_step_matches_oracle(torch, gr, orc):
     want_x = st.oracle(orc, x0_host)
     want_logits = orc.output_head(want_x, hn, wl.rms_eps, hw, wl.w_head, wl.vocab)
     ex, el = rel_l2(eager_x, want_x), rel_l2(eager_logits, want_logits)
-    say(f"  rel_l2 x {ex:.3e} logits {el:.3e}")
+    rx, rl = row_rel_l2(eager_x, want_x), row_rel_l2(eager_logits, want_logits)
+    say(f"  rel_l2 x {ex:.3e} logits {el:.3e}; worst row x {rx:.3e} logits {rl:.3e}")
     assert np.isfinite(eager_logits).all()
-    assert ex <= tol(wl.kv_dtype)
-    assert el <= tol(wl.kv_dtype)
+    assert ex <= tol(wl.kv_dtype) and rx <= tol(wl.kv_dtype)
+    assert el <= tol(wl.kv_dtype) and rl <= tol(wl.kv_dtype)
+    # every 16-row tile of the head's outputs on its own (one wrong tile of 16 logit
+    # columns would otherwise vanish in a 128256-column row)
+    tiles = (eager_logits - want_logits).reshape(wl.batch, -1, 16)
+    tile_err = np.linalg.norm(tiles, axis=2) / np.maximum(np.linalg.norm(want_logits.reshape(wl.batch, -1, 16),
+                                                                         axis=2), 1e-30)
+    say(f"  worst 16-column logit tile {tile_err.max():.3e}")
+    assert tile_err.max() <= 5e-2
     # the argmax of each row agrees wherever the oracle's top two logits are apart
     top2 = np.sort(want_logits, axis=1)[:, -2:]
     clear = (top2[:, 1] - top2[:, 0]) > 1e-2 * np.abs(top2[:, 1])
@@ -198,29 +206,44 @@ def test_llama3_8b_mixed_step_chunk256_matches_oracle(torch, gr, orc):
         torch.cuda.synchronize()
 
 
-QWEN_LAYERS = 3
-
-
-def test_qwen3_8b_full_shape_layers_match_oracle(torch, gr, orc):
+@pytest.mark.timeout(900)
+def test_qwen3_8b_stack_every_layer_matches_oracle(torch, gr, orc):
+    """The whole 36-layer Qwen3-8B-shaped stack at B = 32 with q8_0 KV in a fragmented
+    pool: the GPU runs the layers one call each and every layer's output is checked
+    against the oracle's chain (whole tensor and every row); the stack in one call then
+    equals the layer-by-layer result, and rows decoded alone equal the batch's."""
     wl = synth.WORKLOADS["qwen3_8b"]
-    say(f"qwen3_8b: {QWEN_LAYERS} full-shape layers, B={wl.batch}, q8_0 KV")
-    st = Stack(gr, torch, wl, QWEN_LAYERS)
+    say(f"qwen3_8b: {wl.n_layers} layers, B={wl.batch}, q8_0 KV")
+    st = Stack(gr, torch, wl, wl.n_layers)
     x0 = synth.input_x(wl)
+    ws = gr.workspace(gr.decode_layer_workspace_size(st.cfg, wl.batch, st.max_ctx))
     xg = dev(x0, torch)
-    gr.gr_decode_stack(st.args, st.pm.num_pages, xg, st.bt, st.cg, st.max_ctx)
-    got = host(xg)
-    want = st.oracle(orc, x0)
-    err = rel_l2(got, want)
-    say(f"  rel_l2 {err:.3e}")
-    assert np.isfinite(got).all()
-    assert err <= tol(wl.kv_dtype)
+    cur = x0
+    worst = 0.0
+    for layer in range(wl.n_layers):
+        gr.gr_decode_layer(st.cfg, st.args.weights[layer], st.k[layer], st.v[layer], st.pm.num_pages, xg, st.bt,
+                           st.cg, st.max_ctx, ws=ws)
+        cur = orc.decode_layer(wl, st.host_layers[layer], st.kv.k_pools[layer].copy(), st.kv.v_pools[layer].copy(),
+                               cur, st.pm.block_table, st.ctx)
+        got = host(xg)
+        err, rerr = rel_l2(got, cur), row_rel_l2(got, cur)
+        worst = max(worst, rerr)
+        say(f"  layer {layer}: rel_l2 {err:.3e}, worst row {rerr:.3e}")
+        assert np.isfinite(got).all()
+        assert err <= tol(wl.kv_dtype) and rerr <= tol(wl.kv_dtype), layer
+    by_layer = host(xg)
+    say(f"  worst row over the stack {worst:.3e}")
+    # the stack in one call (re-running rewrites each row's appended KV slot with the
+    # same values)
+    xs = dev(x0, torch)
+    gr.gr_decode_stack(st.args, st.pm.num_pages, xs, st.bt, st.cg, st.max_ctx)
+    assert rel_l2(host(xs), by_layer) <= 1e-5
     # rows of the full batch equal the same rows decoded alone, in another order
-    # (re-running rewrites each row's appended KV slot with the same values)
     rows = [31, 0, 17]
-    xs = dev(x0[rows], torch)
-    gr.gr_decode_stack(st.args, st.pm.num_pages, xs, dev(st.pm.block_table[rows], torch), dev(st.ctx[rows], torch),
+    xr = dev(x0[rows], torch)
+    gr.gr_decode_stack(st.args, st.pm.num_pages, xr, dev(st.pm.block_table[rows], torch), dev(st.ctx[rows], torch),
                        st.max_ctx)
-    assert rel_l2(host(xs), got[rows]) <= 1e-5
+    assert rel_l2(host(xr), by_layer[rows]) <= 1e-5
 
 
 def test_longctx_layer_matches_oracle(torch, gr, orc):
@@ -236,6 +259,26 @@ def test_longctx_layer_matches_oracle(torch, gr, orc):
     say(f"  rel_l2 {err:.3e} (max ctx {st.max_ctx})")
     assert np.isfinite(got).all()
     assert err <= tol(wl.kv_dtype)
+
+
+def test_longctx_layer_qk_norm_matches_oracle(torch, gr, orc):
+    """The long-context layer shape (B = 64, contexts to 32768, q8_0 KV in a 90 %-full
+    pool) with QK-RMSNorm on: scores are of order one, so the cached pages, not the new
+    token, carry the softmax and the decode kernel's page walk and many-workgroup merge
+    are what the oracle checks."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["longctx"], qk_norm=True)
+    say(f"longctx + QK-norm: 1 layer, B={wl.batch}, ctx up to {wl.ctx_hi}")
+    st = Stack(gr, torch, wl, 1)
+    x0 = synth.input_x(wl)
+    xg = dev(x0, torch)
+    gr.gr_decode_stack(st.args, st.pm.num_pages, xg, st.bt, st.cg, st.max_ctx)
+    got = host(xg)
+    want = st.oracle(orc, x0)
+    err, rerr = rel_l2(got, want), row_rel_l2(got, want)
+    say(f"  rel_l2 {err:.3e}, worst row {rerr:.3e} (max ctx {st.max_ctx})")
+    assert np.isfinite(got).all()
+    assert err <= tol(wl.kv_dtype) and rerr <= tol(wl.kv_dtype)
 
 
 def test_probed_stack_equals_stack(torch, gr):

@@ -218,6 +218,42 @@ def test_gemm_rejects_bad_k(orc):
         orc.gemm(synth.W_Q4_K, np.zeros(144, np.uint8), np.zeros((1, 255)), 1, 255)
 
 
+# ----------------------------------------------------------------------------- output head
+
+@pytest.mark.parametrize("wtype,k", [(synth.W_Q6_K, 768), (synth.W_Q6_K, 512), (synth.W_Q4_K, 1024)])
+def test_output_head_matches_brute_force(orc, wtype, k):
+    """logits = W (rms(x) * g): numpy RMSNorm with the given eps and gain, then the decoded
+    matrix (the final norm and output head of the Llama-3 shape; a 3-super-block Q6_K row is
+    2-byte aligned)."""
+    rng = np.random.default_rng(31)
+    vocab, b = 50, 3
+    w = synth.weight(rng, wtype, vocab, k)
+    x = rng.standard_normal((b, k)) * np.array([[1.0], [1e-3], [40.0]])
+    g = rng.uniform(0.5, 1.5, k).astype(np.float32)
+    W = refimpl.decode_matrix(wtype, w, vocab, k)
+    for eps in (1e-5, 0.7):  # a large eps makes a dropped or misplaced eps visible
+        got = orc.output_head(x, g, eps, w, wtype, vocab)
+        want = np.stack([refimpl.rms(x[i], g, eps) for i in range(b)]) @ W.T
+        np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-11 * np.abs(want).max())
+
+
+def test_output_head_closed_forms(orc):
+    """Constant rows: rms(c 1) = c / sqrt(c^2 + eps), so the logits are that factor times
+    W g; a doubled gain doubles them; a row of zeros gives zeros for any eps > 0."""
+    rng = np.random.default_rng(32)
+    vocab, k = 24, 512
+    w = synth.weight(rng, synth.W_Q6_K, vocab, k)
+    W = refimpl.decode_matrix(synth.W_Q6_K, w, vocab, k)
+    g = rng.uniform(0.5, 1.5, k).astype(np.float32)
+    c, eps = 2.5, 0.3
+    x = np.stack([np.full(k, c), np.zeros(k)])
+    got = orc.output_head(x, g, eps, w, synth.W_Q6_K, vocab)
+    np.testing.assert_allclose(got[0], c / math.sqrt(c * c + eps) * (W @ g.astype(np.float64)), rtol=1e-12)
+    assert not got[1].any()
+    got2 = orc.output_head(x[:1], (2 * g).astype(np.float32), eps, w, synth.W_Q6_K, vocab)
+    np.testing.assert_allclose(got2[0], 2 * got[0], rtol=1e-14)
+
+
 # ----------------------------------------------------------------------------- RMSNorm, RoPE, SiLU
 
 def test_rmsnorm_closed_form_and_scale_invariance(orc):
