@@ -83,6 +83,8 @@ def _load() -> C.CDLL:
     L.gr_paged_decode_attn_workspace_size.restype = _sz
     L.gr_paged_decode_attn.argtypes = [_p, _p, _p, _p, _p, _p, _i, C.POINTER(AttnMeta), _p, _sz, _p]
     L.gr_paged_decode_attn.restype = _i
+    L.gr_paged_decode_attn_noalloc.argtypes = [_p, _p, _p, _p, _p, _p, _i, C.POINTER(AttnMeta), _p]
+    L.gr_paged_decode_attn_noalloc.restype = _i
     L.gr_attn_launch_shape.argtypes = [_i, _i, _i, _i, C.POINTER(_i), C.POINTER(_i), C.POINTER(_i),
                                        C.POINTER(C.c_longlong)]
     L.gr_attn_launch_shape.restype = _i
@@ -120,7 +122,7 @@ def _load() -> C.CDLL:
     L.gr_sample_workspace_size.restype = _sz
     L.gr_sample.argtypes = [_p, _i, _i, _p, _p, _p, _p, _sz, _p]
     L.gr_sample.restype = _i
-    if L.gr_abi_version() != 8:
+    if L.gr_abi_version() != 9:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
     return L
@@ -133,7 +135,7 @@ def lib() -> C.CDLL:
 EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_bytes", "gr_q4k_dequant",
             "gr_q6k_dequant", "gr_q8_0_dequant", "gr_gemm_workspace_size", "gr_gemm_launch_shape", "gr_q4k_gemm",
             "gr_q6k_gemm", "gr_q5k_gemm", "gr_q8_0_gemm",
-            "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_attn_launch_shape", "gr_paged_gather_kv",
+            "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_paged_decode_attn_noalloc", "gr_attn_launch_shape", "gr_paged_gather_kv",
             "gr_decode_layer_workspace_size", "gr_decode_layer", "gr_output_head_workspace_size", "gr_output_head",
             "gr_decode_stack_workspace_size", "gr_decode_stack", "gr_decode_stack_probed", "gr_sample_workspace_size",
             "gr_sample", "gr_verify_stack_workspace_size", "gr_verify_stack", "gr_spec_accept",
@@ -277,6 +279,17 @@ def gr_paged_decode_attn(q, k_pages, v_pages, block_table, ctx_lens, meta: AttnM
     _check("gr_paged_decode_attn",
            _load().gr_paged_decode_attn(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
                                         _ptr(out), b, C.byref(meta), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def gr_paged_decode_attn_noalloc(q, k_pages, v_pages, block_table, ctx_lens, meta: AttnMeta, out=None):
+    """gr_paged_decode_attn with the library's own per-device scratch (no workspace argument)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q)
+    _check("gr_paged_decode_attn_noalloc",
+           _load().gr_paged_decode_attn_noalloc(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                                _ptr(ctx_lens), _ptr(out), q.shape[0], C.byref(meta), _stream()))
     return out
 
 

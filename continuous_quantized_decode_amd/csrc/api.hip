@@ -7,6 +7,7 @@
 // batched decode) is just a different B, block table and ctx_lens on the next call.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "gr_internal.h"
 #include "attn_internal.h"
@@ -734,9 +735,14 @@ size_t gr_paged_decode_attn_workspace_size(const gr_attn_meta* m, int B) {
   return c.off + 256;
 }
 
-gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
-                               const int32_t* ctx_lens, float* out, int B, const gr_attn_meta* m, void* ws,
-                               size_t ws_bytes, void* stream) {
+// The decode attention call with its workspace at ws (device memory, 256-byte aligned,
+// at least gr_paged_decode_attn_workspace_size bytes, checked by the caller).
+static gr_status paged_decode_attn_ws(const float* q, const void* k_pages, const void* v_pages,
+                                      const int32_t* block_table, const int32_t* ctx_lens, float* out, int B,
+                                      const gr_attn_meta* m, void* ws, void* stream);
+
+static gr_status check_attn_call(const float* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                 const int32_t* ctx_lens, float* out, int B, const gr_attn_meta* m) {
   if (B < 0) return GR_ERR_SHAPE;
   gr_status s = check_meta(m);
   if (s != GR_OK) return s;
@@ -746,9 +752,23 @@ gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* 
   if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 4) ||
       !aligned(block_table, 4) || !aligned(ctx_lens, 4))
     return GR_ERR_ALIGN;
+  return GR_OK;
+}
+
+gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                               const int32_t* ctx_lens, float* out, int B, const gr_attn_meta* m, void* ws,
+                               size_t ws_bytes, void* stream) {
+  gr_status s = check_attn_call(q, k_pages, v_pages, block_table, ctx_lens, out, B, m);
+  if (s != GR_OK || B == 0) return s;
   if (!ws || ws_bytes < gr_paged_decode_attn_workspace_size(m, B) || !aligned(ws, 256)) return GR_ERR_WORKSPACE;
   s = check_device();
   if (s != GR_OK) return s;
+  return paged_decode_attn_ws(q, k_pages, v_pages, block_table, ctx_lens, out, B, m, ws, stream);
+}
+
+static gr_status paged_decode_attn_ws(const float* q, const void* k_pages, const void* v_pages,
+                                      const int32_t* block_table, const int32_t* ctx_lens, float* out, int B,
+                                      const gr_attn_meta* m, void* ws, void* stream) {
   Carver c(ws);
   AttnParams ap{};
   uint32_t* list;
@@ -781,6 +801,45 @@ gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* 
   hipError_t e = launch_attn_sched(sc, st);
   if (e != hipSuccess) return check_launch(e);
   return check_launch(launch_attn_decode(m->kv_dtype, false, ap, st));
+}
+
+// ------------------------------------------- decode attention without allocation
+// The allocation-free variant keeps its workspace (arrival counters, workgroup partial
+// states, work list) in this file-scope array: one copy per device, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the host it is
+// a stand-in, not a device address): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[GR_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static gr_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GR_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return check_launch(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GR_OK;
+}
+
+gr_status gr_paged_decode_attn_noalloc(const float* q, const void* k_pages, const void* v_pages,
+                                       const int32_t* block_table, const int32_t* ctx_lens, float* out, int B,
+                                       const gr_attn_meta* m, void* stream) {
+  gr_status s = check_attn_call(q, k_pages, v_pages, block_table, ctx_lens, out, B, m);
+  if (s != GR_OK || B == 0) return s;
+  if (gr_paged_decode_attn_workspace_size(m, B) > (size_t)GR_NOALLOC_SCRATCH_BYTES) return GR_ERR_WORKSPACE;
+  s = check_device();
+  if (s != GR_OK) return s;
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != GR_OK) return s;
+  return paged_decode_attn_ws(q, k_pages, v_pages, block_table, ctx_lens, out, B, m, ws, stream);
 }
 
 gr_status gr_attn_launch_shape(int kv_dtype, int B, int n_kv_heads, int max_tokens, int* waves_per_wg,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GR_ABI_VERSION 8
+#define GR_ABI_VERSION 9
 
 typedef enum {
   GR_OK = 0,
@@ -147,6 +147,22 @@ size_t gr_paged_decode_attn_workspace_size(const gr_attn_meta* m, int B);
 gr_status gr_paged_decode_attn(const float* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                                const int32_t* ctx_lens, float* out, int B, const gr_attn_meta* m, void* workspace,
                                size_t ws_bytes, void* stream);
+
+/* gr_paged_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments, kernels and results, without the workspace arguments.  Its
+ * workspace lives in a static array of GR_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each device it runs on until the process ends; the call allocates nothing
+ * (the array's device address is looked up once per device, on the first call with
+ * that device current).  GR_ERR_WORKSPACE when the call needs more than the array
+ * (gr_paged_decode_attn_workspace_size(m, B) > GR_NOALLOC_SCRATCH_BYTES); the other
+ * errors as gr_paged_decode_attn.  Every call on a device shares that device's array,
+ * which keeps the last call's contents (the call clears its arrival counters itself):
+ * calls that overlap on one device race, whatever their streams. */
+#define GR_NOALLOC_SCRATCH_BYTES (16u << 20)
+gr_status gr_paged_decode_attn_noalloc(const float* q, const void* k_pages, const void* v_pages,
+                                       const int32_t* block_table, const int32_t* ctx_lens, float* out, int B,
+                                       const gr_attn_meta* m, void* stream);
 
 /* Launch shape of the decode attention for rows of up to max_tokens attended tokens
  * (profiling aid and test of the page walk): waves per workgroup, pages per wave, the

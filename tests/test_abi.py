@@ -37,7 +37,7 @@ def test_host_side_checks_without_gpu():
     """Calls that fail a host check return their status before touching the device."""
     import continuous_quantized_decode_amd as gr
     L = gr.lib()
-    assert L.gr_abi_version() == 8
+    assert L.gr_abi_version() == 9
     assert L.gr_status_str(-6) == b"max_ctx + 1 tokens exceed the block table's pages"
     assert L.gr_kv_head_bytes(2, 128) == 16 * 128 + 16 * 4 * 2
     assert L.gr_kv_head_bytes(7, 128) == -1
@@ -58,6 +58,14 @@ def test_host_side_checks_without_gpu():
     assert L.gr_paged_decode_attn(p, p, p, p, p, p, 1, ctypes.byref(meta), p, 4096, None) == -2
     meta = gr.attn_meta(4, 2, 64, 1, 9, 8, 129)
     assert L.gr_paged_decode_attn(p, p, p, p, p, p, 1, ctypes.byref(meta), p, 4096, None) == -6
+    # the allocation-free variant: the same checks, and a call needing more than its
+    # fixed scratch is refused before the device is touched
+    assert L.gr_paged_decode_attn_noalloc(p, p, p, p, p, p, 1, ctypes.byref(meta), None) == -6
+    assert L.gr_paged_decode_attn_noalloc(None, p, p, p, p, p, 0, ctypes.byref(meta), None) == -6
+    meta = gr.attn_meta(64, 8, 128, 1, 1 << 20, 2048, 32768)
+    assert L.gr_paged_decode_attn_workspace_size(ctypes.byref(meta), 512) > 16 << 20
+    assert L.gr_paged_decode_attn_noalloc(p, p, p, p, p, p, 512, ctypes.byref(meta), None) == -5
+    assert L.gr_paged_decode_attn_noalloc(None, p, p, p, p, p, 512, ctypes.byref(meta), None) == -1
 
 
 def test_gemm_launch_shape_names_the_kernel():
