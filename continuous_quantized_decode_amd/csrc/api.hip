@@ -100,13 +100,13 @@ struct Epi {
   int kind = kEpiStore;
   float* y = nullptr;
   int ldy = 0;
-  const float* ss = nullptr;  // RMSNorm sum of squares of the input rows (NULL: none)
+  const double* ss = nullptr;  // RMSNorm sum of squares of the input rows (NULL: none)
   float eps = 0.f;
   const float* gain = nullptr;
   PackOut out1 = kNoPack, out2 = kNoPack;
   int out_k = 0;  // K of the packed outputs (columns of y)
-  float* ss_out = nullptr;
-  float* zero_ptr = nullptr;
+  double* ss_out = nullptr;
+  double* zero_ptr = nullptr;
   int zero_n = 0;
   float* part = nullptr;  // many-row K-split partial sums (NULL: no split)
   size_t part_cap = 0;
@@ -193,7 +193,7 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
 
 // The SwiGLU GEMM: gate and up (same type, F rows each) paired per 16-column tile.
 hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, int B, const Pack2& xin,
-                       const float* ss, float eps, PackOut out, float* zero_ptr, int zero_n, hipStream_t st) {
+                       const double* ss, float eps, PackOut out, double* zero_ptr, int zero_n, hipStream_t st) {
   GemmArgs a{};
   a.w[0] = (const uint8_t*)wg;
   a.w[1] = (const uint8_t*)wu;
@@ -231,7 +231,7 @@ struct LayerBufs {
   Pack2 op;  // attention output (Wo input)
   Pack2 ap;  // SwiGLU activation (down input)
   float* qkv;
-  float *ss_attn, *ss_ffn;
+  double *ss_attn, *ss_ffn;
   float *o_part, *m_part, *l_part;
   double* rope;  // [B][head_dim / 2][2]: RoPE of the step's positions
   float* qbuf;   // [B][Hq][D]: roped queries when a step carries several tokens per sequence
@@ -257,8 +257,8 @@ LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan&
   L.op = carve_pack2(c, B, qd);
   L.ap = carve_pack2(c, B, cfg->ffn);
   L.qkv = c.take<float>((size_t)B * (qd + 2 * kvd) * 4);
-  L.ss_attn = c.take<float>(ss_floats(B) * 4);  // [ss_slots(B)][B]
-  L.ss_ffn = c.take<float>(ss_floats(B) * 4);
+  L.ss_attn = c.take<double>(ss_count(B) * 8);  // [ss_slots(B)][B]
+  L.ss_ffn = c.take<double>(ss_count(B) * 8);
   const size_t units = (size_t)B * cfg->n_q_heads * ap.max_splits;
   L.o_part = c.take<float>(units * cfg->head_dim * 4);
   L.m_part = c.take<float>(units * 4);
@@ -350,7 +350,7 @@ Kinds qkv_kinds(const gr_layer_weights* w) {
 
 // Pack of the layer input: x * attn_norm and its sum of squares (and, for a decode
 // step, the RoPE table of its positions).
-gr_status run_input_pack(const float* x, int B, int H, const float* gain, Kinds k, const Pack2& xp, float* ss,
+gr_status run_input_pack(const float* x, int B, int H, const float* gain, Kinds k, const Pack2& xp, double* ss,
                          hipStream_t st, const Probe* probe, RopeTable rope = RopeTable{}, RowSel sel = RowSel{},
                          AttnSched sched = AttnSched{}) {
   return probed(probe, GR_STAGE_PACK, st, [&] {
@@ -541,7 +541,7 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
 
 // Output head on a packed input (x * norm in xp, sum of squares in ss).
 gr_status run_head(const void* w, int wtype, float* logits, int B, int H, int vocab, float eps, const Pack2& xp,
-                   const float* ss, hipStream_t st, const Probe* probe) {
+                   const double* ss, hipStream_t st, const Probe* probe) {
   return probed(probe, GR_STAGE_HEAD, st, [&] {
     const void* ws[1] = {w};
     const int ts[1] = {wtype};
@@ -935,7 +935,7 @@ size_t gr_output_head_workspace_size(int B, int hidden, int vocab) {
   (void)vocab;
   Carver c(nullptr);
   carve_pack2(c, B, hidden);
-  c.take<float>(ss_floats(B) * 4);
+  c.take<double>(ss_count(B) * 8);
   return c.off + 256;
 }
 
@@ -953,7 +953,7 @@ gr_status gr_output_head(const float* x, const float* norm, float eps, const voi
   if (s != GR_OK) return s;
   Carver c(ws);
   const Pack2 xp = carve_pack2(c, B, hidden);
-  float* ss = c.take<float>(ss_floats(B) * 4);
+  double* ss = c.take<double>(ss_count(B) * 8);
   hipStream_t st = (hipStream_t)stream;
   Kinds k;
   k.add(wtype);

@@ -588,7 +588,7 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
   const int n = lane & 15;
 
   if (a.zero_ptr && tile == 0)
-    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.f;
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.0;
 
   // rows of the tile(s).  SwiGLU: tile t of the pair is the same 16 columns of gate
   // (t = 0) and up (t = 1).  Otherwise the workgroup's group of NT consecutive tiles of
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
   // main loop (one register through it), any rest (workgroups of fewer threads than
   // values) after it.
   const int n_ss = a.ss ? a.ss_slots * a.B : 0;
-  const float ssp = (int)threadIdx.x < n_ss ? a.ss[threadIdx.x] : 0.f;
+  const double ssp = (int)threadIdx.x < n_ss ? a.ss[threadIdx.x] : 0.0;
   // Epilogue element e = (t, bt, lane', k2) (a SwiGLU pair handles both tiles at once).
   // Its other operands that do not depend on the GEMM (the residual and the next norm
   // gain) are loaded before the main loop, for the first kPre elements of each thread,
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
       r[0] = acc[t][b][0] + acc[t][b][1];  // hi + lo parts of batch row 8b + 2g
       r[1] = acc[t][b][2] + acc[t][b][3];  // and of row 8b + 2g + 1
     }
-  float* s_ss = red + (size_t)nwaves * NT * BTN * 128;  // [ss_slots][B]
+  double* s_ss = (double*)(red + (size_t)nwaves * NT * BTN * 128);  // [ss_slots][B]
   if ((int)threadIdx.x < n_ss) s_ss[threadIdx.x] = ssp;
   for (int i = threadIdx.x + blockDim.x; i < n_ss; i += blockDim.x) s_ss[i] = a.ss[i];
   __syncthreads();
@@ -696,7 +696,8 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
         if (a.epi == kEpiSwiGLU) v2 += red[(((size_t)w * NT + 1) * BTN + m.bt) * 128 + (m.rem % 128)];
       }
     }
-    float ssv = 0.f, xv = 0.f, gv_ = 1.f;
+    double ssv = 0.0;
+    float xv = 0.f, gv_ = 1.f;
     if (m.live && a.ss)
       for (int s = 0; s < a.ss_slots; ++s) ssv += s_ss[s * a.B + m.brow];
     if (k < kPre) {
@@ -712,7 +713,7 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
         gv_ = a.gain ? a.gain[m.col] : 1.f;
       }
     }
-    const float rs = m.live ? (a.ss ? 1.0f / sqrtf(ssv * inv_k + eps) : 1.0f) : 0.f;
+    const float rs = m.live ? (a.ss ? 1.0f / sqrtf((float)ssv * inv_k + eps) : 1.0f) : 0.f;
     if (a.epi == kEpiStore) {
       if (m.live) a.y[(size_t)m.brow * a.ldy + m.col] = rs * v;
     } else if (a.epi == kEpiSwiGLU) {
@@ -735,7 +736,7 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int o = 2; o <= 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
       if (m.in && m.nn == 0 && m.brow < a.B && a.ss_out)
-        atomicAdd(a.ss_out + (size_t)(tile % a.ss_slots) * a.B + m.brow, sq);
+        atomicAdd(a.ss_out + (size_t)(tile % a.ss_slots) * a.B + m.brow, (double)sq);
     }
   }
 }
@@ -852,7 +853,7 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
   float* red = (float*)(lds + (size_t)nwaves * D * NT * kStage);  // [2][waves][NT][BTN][128]
 
   if (a.zero_ptr && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.f;
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.0;
 
   // this workgroup's tile groups and this wave's K slice
   const int g0 = blockIdx.x * a.tl_groups_per_wg;
@@ -931,7 +932,7 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
   // first D - 1 weight stages (unconditionally: a workgroup with fewer stages repeats
   // its last one into slots it never reads).  So the first step waits for stage 0 and
   // what is older than it, not for the whole prologue.
-  float sv[16];  // B <= 16: ss_slots(B) = 16; every lane loads (a valid row), uniformly
+  double sv[16];  // B <= 16: ss_slots(B) = 16; every lane loads (a valid row), uniformly
   if (a.ss) {
     const int row = min(e_brow, a.B - 1);
 #pragma unroll
@@ -991,10 +992,10 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
     // (the empty asm keeps the sum from being hoisted above the prologue's loads)
 #pragma unroll
     for (int s = 0; s < 16; ++s) asm volatile("" : "+v"(sv[s]));
-    float ssv = 0.f;
+    double ssv = 0.0;
 #pragma unroll
     for (int s = 0; s < 16; ++s) ssv += sv[s];
-    rs = 1.0f / sqrtf(ssv * a.inv_k + a.eps);
+    rs = 1.0f / sqrtf((float)ssv * a.inv_k + a.eps);
   }
 
   for (int gl = 0; gl < ng; ++gl) {
@@ -1205,7 +1206,7 @@ __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
   lds_u8* ring = (lds_u8*)lds + 2 * MB * 8 * 1024 + wave * (2 * NT * kW);         // [2][NT][kW]
 
   if (a.zero_ptr && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.f;
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.0;
 
   // workgroup -> (activation tile group, weight tile group); on a grid that is a
   // multiple of 8, consecutive groups of weight tiles go to one XCD (workgroups are
@@ -1328,9 +1329,9 @@ __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
       const bool row_ok = row < a.B;
       float rs = 1.0f;
       if (a.ss && row_ok) {
-        float ssv = 0.f;
+        double ssv = 0.0;
         for (int s = 0; s < a.ss_slots; ++s) ssv += a.ss[s * a.B + row];
-        rs = 1.0f / sqrtf(ssv * a.inv_k + a.eps);
+        rs = 1.0f / sqrtf((float)ssv * a.inv_k + a.eps);
       }
       if (a.epi == kEpiSwiGLU) {
         const int col = lt[0] * 16 + n;
@@ -1364,7 +1365,7 @@ __global__ __launch_bounds__(512) void gemm_mm_kernel(GemmArgs a) {
 #pragma unroll
         for (int o = 1; o <= 8; o <<= 1) sq += __shfl_xor(sq, o, 64);
         if (n == 0 && row_ok && a.ss_out)
-          atomicAdd(a.ss_out + (size_t)(bid % a.ss_slots) * a.B + row, sq);
+          atomicAdd(a.ss_out + (size_t)(bid % a.ss_slots) * a.B + row, (double)sq);
       }
     }
   }
@@ -1381,9 +1382,9 @@ __global__ __launch_bounds__(256) void gemm_mm_finish_kernel(GemmArgs a, int nsp
     for (int s = 0; s < nsplit; ++s) v += a.part[((size_t)s * a.B + row) * a.ldp + c];
   float rs = 1.0f;
   if (a.ss) {
-    float ssv = 0.f;
+    double ssv = 0.0;
     for (int s = 0; s < a.ss_slots; ++s) ssv += a.ss[s * a.B + row];
-    rs = 1.0f / sqrtf(ssv * a.inv_k + a.eps);
+    rs = 1.0f / sqrtf((float)ssv * a.inv_k + a.eps);
   }
   const int col = a.pcol0 + c;
   if (a.epi == kEpiStore) {
@@ -1404,7 +1405,7 @@ __global__ __launch_bounds__(256) void gemm_mm_finish_kernel(GemmArgs a, int nsp
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
   __syncthreads();
   if (threadIdx.x == 0 && a.ss_out)
-    atomicAdd(a.ss_out + (size_t)(blockIdx.x % a.ss_slots) * a.B + row, red[0] + red[1] + red[2] + red[3]);
+    atomicAdd(a.ss_out + (size_t)(blockIdx.x % a.ss_slots) * a.B + row, (double)(red[0] + red[1] + red[2] + red[3]));
 }
 
 // ---------------------------------------------------------------------------------
@@ -1500,7 +1501,7 @@ GemmPlan plan_gemm(int wtype, int total_tiles, int K, int B, int nt) {
   // 512 B, then the RMSNorm partial sums) share one allocation of at most kGemmLds
   const int stage = stage_bytes(wtype);
   auto lds_need = [&](int w) {
-    return max(w * pl.nt * kRing * stage, w * pl.nt * pl.btn * 512 + kSsCap * (int)sizeof(float));
+    return max(w * pl.nt * kRing * stage, w * pl.nt * pl.btn * 512 + kSsCap * (int)sizeof(double));
   };
   auto waves_for = [&](int w) {  // waves actually used when splitting nsb over w
     const int spw = (nsb + w - 1) / w;

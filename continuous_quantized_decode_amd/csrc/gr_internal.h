@@ -66,7 +66,7 @@ struct GemmArgs {
   size_t row_bytes;
   const void* xpack;    // actpack of the input, kind by weight type
   int nslices;
-  const float* ss;      // per-row sum of squares of the input (RMSNorm) in ss_slots
+  const double* ss;     // per-row sum of squares of the input (RMSNorm) in ss_slots
                         // partial slots [slot][B], or NULL: r = 1
   int ss_slots;
   float inv_k, eps;
@@ -82,8 +82,8 @@ struct GemmArgs {
   int pack_kind, pack_nslices;
   u16* pack_out2;       // residual: a second actpack kind of the same values (NULL: none)
   int pack_kind2, pack_nslices2;
-  float* ss_out;        // residual: sum of squares accumulator of the packed rows, [ss_slots][B]
-  float* zero_ptr;      // optional: workgroup 0 zeroes zero_n floats
+  double* ss_out;       // residual: sum of squares accumulator of the packed rows, [ss_slots][B]
+  double* zero_ptr;     // optional: workgroup 0 zeroes zero_n values (a sum-of-squares buffer)
   int zero_n;
   // many-row kernel split over K (store and residual epilogues): the K ranges' partial
   // sums part[split][B][ldp] (launch-local columns, the launch's first output column
@@ -94,15 +94,17 @@ struct GemmArgs {
 };
 
 // The RMSNorm statistic (per-row sum of squares) that a GEMM epilogue applies is kept
-// as ss_slots(B) partial sums [slot][B] (at most kSsCap floats).  A producer running in
+// as ss_slots(B) partial sums [slot][B] (at most kSsCap values).  A producer running in
 // many workgroups adds into slot (workgroup % slots), so that only a few atomics meet
-// on one address (hundreds of same-address float atomics from all XCDs serialize at
-// the memory side and hold the kernel's completion for microseconds); consumers add
-// the slots up.
+// on one address (hundreds of same-address atomics from all XCDs serialize at the
+// memory side and hold the kernel's completion for microseconds); consumers add the
+// slots up in slot order.  The sums are fp64: each addend is a float (a tile's 16
+// squares summed in fp32), so the adds into a slot are exact, and the result does not
+// depend on the atomics' order, unless one row's addends span more than 2^29.
 constexpr int kSsCap = 256;
 __host__ __device__ inline int ss_slots(int B) { return B <= 16 ? 16 : B <= kSsCap ? kSsCap / B : 1; }
-// floats of one RMSNorm partial-sum buffer
-inline size_t ss_floats(int B) { return (size_t)ss_slots(B) * B > (size_t)kSsCap ? (size_t)ss_slots(B) * B : kSsCap; }
+// values (doubles) of one RMSNorm partial-sum buffer
+inline size_t ss_count(int B) { return (size_t)ss_slots(B) * B > (size_t)kSsCap ? (size_t)ss_slots(B) * B : kSsCap; }
 
 struct GemmPlan {
   int nt, btn, waves, sb_per_wave, tiles, maxt;
@@ -283,7 +285,7 @@ GR_DEV void build_attn_sched(const AttnSched& s, uint32_t* lds_scratch /* blockD
   }
 }
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
-                            float* ss_out, hipStream_t st,  // ss_out: [ss_slots(B)][B], slot 0 the sum
+                            double* ss_out, hipStream_t st,  // ss_out: [ss_slots(B)][B], slot 0 the sum
                             RopeTable rope = RopeTable{}, RowSel sel = RowSel{}, AttnSched sched = AttnSched{});
 
 }  // namespace gr

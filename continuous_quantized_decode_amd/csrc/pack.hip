@@ -16,7 +16,7 @@ constexpr int kPackThreads = 1024;
 // four consecutive columns per pass (K % 256 == 0, x rows 16-byte aligned).
 __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __restrict__ x, int ldx, int B, int K,
                                                                  const float* __restrict__ gain, PackOut o1,
-                                                                 PackOut o2, float* ss_out, RopeTable rope,
+                                                                 PackOut o2, double* ss_out, RopeTable rope,
                                                                  RowSel sel, AttnSched sched) {
   const int b = blockIdx.x, tid = threadIdx.x;
   __shared__ uint32_t sched_scan[kPackThreads / 64 + 1];
@@ -58,14 +58,14 @@ __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __
     if (tid == 0) {
       float tot = 0.f;
       for (int w = 0; w < kPackThreads / 64; ++w) tot += red[w];
-      ss_out[b] = tot;
-      for (int s = 1; s < ss_slots(B); ++s) ss_out[(size_t)s * B + b] = 0.f;
+      ss_out[b] = (double)tot;
+      for (int s = 1; s < ss_slots(B); ++s) ss_out[(size_t)s * B + b] = 0.0;
     }
   }
 }
 
 hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* gain, PackOut o1, PackOut o2,
-                            float* ss_out, hipStream_t st, RopeTable rope, RowSel sel, AttnSched sched) {
+                            double* ss_out, hipStream_t st, RopeTable rope, RowSel sel, AttnSched sched) {
   if (rope.out && (rope.half_d <= 0 || rope.half_d > kPackThreads || (!rope.ctx && !rope.row_pos)))
     return hipErrorInvalidValue;
   if (sel.idx && sel.src_rows <= 0) return hipErrorInvalidValue;

@@ -69,12 +69,14 @@ LAYER_CASES = [
     dict(ctx=[40, 7], batch=2, ffn=8448, w_other=synth.W_Q8_0, w_down=synth.W_Q8_0),
     # Q6_K gate/up with SwiGLU on many tile pairs: 8 rows and a ragged 12, hidden 768 (three
     # super-blocks: 2-byte aligned Q6_K rows) and 1024 (16-byte aligned)
+    # (gu: the gate/up launch the case must take, (tile loop?, batch tiles); 12 rows need
+    # K of seven super-blocks for the tile loop, so hidden 768 takes split-K there)
     dict(ctx=[40, 7, 300, 0, 16, 90, 1, 33], batch=8, hidden=768, ffn=8192, w_other=synth.W_Q6_K,
-         kv_dtype=synth.KV_F16),
+         kv_dtype=synth.KV_F16, gu=(True, 1)),
     dict(ctx=[3, 70, 11, 0, 200, 15, 16, 17, 64, 5, 90, 31], batch=12, hidden=768, ffn=8448, w_other=synth.W_Q6_K,
-         kv_dtype=synth.KV_Q8_0, qk_norm=True),
+         kv_dtype=synth.KV_Q8_0, qk_norm=True, gu=(False, 2)),
     dict(ctx=[9, 130, 47, 2, 61, 18, 77, 5, 100, 1], batch=10, hidden=2048, ffn=8192, w_other=synth.W_Q6_K,
-         kv_dtype=synth.KV_F16),
+         kv_dtype=synth.KV_F16, gu=(True, 2)),
 ]
 
 
@@ -99,8 +101,14 @@ def run_layer_case(torch, gr, orc, wl, ctx, layer=0):
 def test_tiny_layer_matches_oracle(torch, gr, orc, case):
     spec = dict(LAYER_CASES[case])
     ctx = spec.pop("ctx")
+    gu = spec.pop("gu", None)
     wl = tiny(**spec)
     say("layer case", case, spec, ctx)
+    if gu is not None:
+        # the gate/up kernel this case exists to cover (so the choice cannot drift unseen)
+        sh = gr.gr_gemm_launch_shape(synth.layer_weights(wl, 0).tgate, wl.ffn, wl.hidden, len(ctx), gr.GEMM_EPI_SWIGLU)
+        say("  gate/up launch", sh)
+        assert (sh["tile_loop"], sh["btn"]) == gu
     got, want, gpools, opools, kv = run_layer_case(torch, gr, orc, wl, ctx)
     assert np.isfinite(got).all()
     err, rerr = rel_l2(got, want), row_rel_l2(got, want)

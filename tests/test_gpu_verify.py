@@ -141,6 +141,34 @@ def test_verify_one_token_equals_decode(torch, gr, orc):
     np.testing.assert_array_equal(outs[0], outs[1])
 
 
+def test_decode_stack_repeats_bitwise(torch, gr):
+    """The same step twice gives the same bits: every cross-workgroup sum (the RMSNorm
+    statistics, the attention partial states) is added in a fixed order or exactly."""
+    wl = dataclasses.replace(synth.WORKLOADS["llama3_8b"], n_layers=2)
+    ctx = synth.ctx_lens(wl)
+    kv = synth.kv_state(wl, ctx, n_layers=2)
+    pm = kv.pages
+    layers = [synth.layer_weights(wl, layer) for layer in range(2)]
+    keep, ws = [], []
+    for lw in layers:
+        tt, w = _upload(gr, torch, lw)
+        keep.append(tt)
+        ws.append(w)
+    x = synth.input_x(wl, len(ctx))
+    outs = []
+    for rep in range(3):
+        kd = [dev(p, torch) for p in kv.k_pools]
+        vd = [dev(p, torch) for p in kv.v_pools]
+        xg = dev(x, torch)
+        gr.gr_decode_stack(gr.StackArgs(_cfg(gr, wl), ws, kd, vd), pm.num_pages, xg, dev(pm.block_table, torch),
+                           dev(ctx, torch), int(ctx.max()))
+        torch.cuda.synchronize()
+        outs.append((host(xg), host(kd[1]), host(vd[1])))
+    for rep in (1, 2):
+        for a, b in zip(outs[0], outs[rep]):
+            np.testing.assert_array_equal(a, b)
+
+
 def test_verify_qwen3_0p6b_shapes(torch, gr, orc):
     wl = dataclasses.replace(synth.WORKLOADS["qwen3_0p6b"], n_layers=3)
     _run(torch, gr, orc, wl, [64, 1000, 255, 17], 4, 3, with_head=False, seed=1)
