@@ -228,14 +228,26 @@ WEIGHT_FORMATS = {"q4_k": (12, "gr_q4k_gemm"), "q5_k": (13, "gr_q5k_gemm"), "q6_
                   "q8_0": (8, "gr_q8_0_gemm")}
 
 
-def measure_weight_formats(gr, torch, wl, reps: int = 50) -> dict:
+COLD_BYTES = 768 << 20  # copies rotated per measured matrix: more than the 256 MB Infinity Cache
+
+
+def cold_copies(torch, w):
+    """Enough device copies of w that calls rotating over them stream from HBM."""
+    n = max(2, -(-COLD_BYTES // (w.numel() * w.element_size())))
+    return [w] + [w.clone() for _ in range(n - 1)]
+
+
+def measure_weight_formats(gr, torch, wl, reps: int = 48) -> dict:
     """One fused-dequant GEMM per weight format on the workload's stacked gate/up shape
     (2 ffn x hidden) at its batch: per-call time of the C-ABI call (activation pack and
-    GEMM; events on the launch stream) and the weight bytes streamed per second."""
+    GEMM; events on the launch stream) and the weight bytes streamed per second.  Calls
+    rotate over copies of the matrix totalling more than the 256 MB Infinity Cache, so
+    each call reads its weights from HBM (cache-cold)."""
     import numpy as np
     import synth
     n, k, b = 2 * wl.ffn, wl.hidden, wl.batch
-    out = {"shape": f"{n} x {k} (stacked gate/up), B={b}", "formats": {}}
+    out = {"shape": f"{n} x {k} (stacked gate/up), B={b}", "cache": "cold (rotating copies, > 256 MB)",
+           "formats": {}}
     x = torch.randn(b, k, device="cuda")
     y = torch.empty(b, n, device="cuda")
     ws = gr.workspace(gr.lib().gr_gemm_workspace_size(b, n, k))
@@ -243,19 +255,20 @@ def measure_weight_formats(gr, torch, wl, reps: int = 50) -> dict:
     for name, (wt, fn_name) in WEIGHT_FORMATS.items():
         w = torch.from_numpy(synth.weight(np.random.default_rng(31 + wt), wt, n, k)).cuda()
         fn = getattr(gr, fn_name)
-        for _ in range(3):
-            fn(w, x, n, y, ws)
+        ws_ = cold_copies(torch, w)
+        for i in range(len(ws_)):
+            fn(ws_[i], x, n, y, ws)
         torch.cuda.synchronize()
         e0.record()
-        for _ in range(reps):
-            fn(w, x, n, y, ws)
+        for i in range(reps):
+            fn(ws_[i % len(ws_)], x, n, y, ws)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / reps * 1e3
         wb = weight_bytes(wt, n, k)
         out["formats"][name] = {"us_per_call": round(us, 2), "weight_bytes": wb,
                                 "weight_gbs": round(wb / (us * 1e-6) / 1e9, 1)}
-        del w
+        del w, ws_
     return out
 
 
@@ -267,31 +280,154 @@ def measure_many_rows(gr, torch, wl, rows=(128, 256, 512), reps: int = 20) -> di
     (its down type) shapes: per-call time of the C-ABI call (activation pack and GEMM;
     events on the launch stream) and the useful rate 2 B N K / t against the dense bf16
     MFMA peak.  (The kernel issues twice the useful MFMA work: each activation row is two
-    bf16 rows, hi and lo.)"""
+    bf16 rows, hi and lo.)  Calls rotate over copies of each matrix totalling more than
+    the 256 MB Infinity Cache (cache-cold weights)."""
     import numpy as np
     import synth
-    out = {}
+    out = {"cache": "cold (rotating copies, > 256 MB)"}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for name, wt, n, k in (("gate_up", wl.w_other, 2 * wl.ffn, wl.hidden), ("down", wl.w_down, wl.hidden, wl.ffn)):
         w = torch.from_numpy(synth.weight(np.random.default_rng(77 + wt), wt, n, k)).cuda()
         fn = getattr(gr, WEIGHT_FORMATS[{8: "q8_0", 12: "q4_k", 13: "q5_k", 14: "q6_k"}[wt]][1])
+        ws_ = cold_copies(torch, w)
         for b in rows:
             x = torch.randn(b, k, device="cuda")
             y = torch.empty(b, n, device="cuda")
             ws = gr.workspace(gr.lib().gr_gemm_workspace_size(b, n, k))
-            for _ in range(3):
-                fn(w, x, n, y, ws)
+            for i in range(len(ws_)):
+                fn(ws_[i], x, n, y, ws)
             torch.cuda.synchronize()
             e0.record()
-            for _ in range(reps):
-                fn(w, x, n, y, ws)
+            for i in range(reps):
+                fn(ws_[i % len(ws_)], x, n, y, ws)
             e1.record()
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) / reps * 1e3
             tf = 2.0 * b * n * k / (us * 1e-6) / 1e12
             out[f"{name} {n}x{k} B={b}"] = {"us_per_call": round(us, 1), "useful_tflops": round(tf, 1),
                                             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-        del w
+        del w, ws_
+    return out
+
+
+def measure_stream_ceiling(gr, torch, nbytes: int = 4 << 30, reps: int = 5) -> dict:
+    """The practical read ceiling on this GPU: the library's plain read-only streaming
+    kernel (gr_stream_read: grid-stride, 16-byte loads, eight 1 KB loads in flight per
+    wave) over a buffer of nbytes, best of reps, next to the 8 TB/s peak."""
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(gr.STREAM_READ_WORDS, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps + 1):
+        e0.record()
+        gr.gr_stream_read(buf, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del buf
+    gbs = nbytes / (best * 1e-3) / 1e9
+    return {"kernel": f"stream_read_kernel over {nbytes >> 20} MiB (read-only)", "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def measure_config(gr, torch, name: str, steps: int, warmup: int, cpu: bool) -> dict:
+    """Another workload's whole decode step (its layers, batch, contexts, KV format and
+    page pool; the head when it has one), captured as one graph and replayed: ms/step,
+    algorithmic bytes, GB/s and fraction of 8 TB/s, and the fp64 oracle on a bounded
+    sample of the same step (its first layer at the full batch, scaled by the layer
+    count)."""
+    import numpy as np
+    import synth
+    wl = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    ctx = synth.ctx_lens(wl)
+    max_ctx = int(ctx.max())
+    kv = synth.kv_state(wl, ctx)
+    pm = kv.pages
+    k_dev = [up(p) for p in kv.k_pools]
+    v_dev = [up(p) for p in kv.v_pools]
+    k0, v0 = kv.k_pools[0], kv.v_pools[0]
+    del kv
+    keep, wts, lw0 = [], [], None
+    for layer in range(wl.n_layers):
+        lw = synth.layer_weights(wl, layer)
+        if layer == 0:
+            lw0 = lw
+        t = {k: up(getattr(lw, k)) for k in ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo", "w_gate", "w_up",
+                                              "w_down")}
+        if lw.q_norm is not None:
+            t["q_norm"], t["k_norm"] = up(lw.q_norm), up(lw.k_norm)
+        t.update({k: getattr(lw, k) for k in ("tq", "tk", "tv", "to", "tgate", "tup", "tdown")})
+        keep.append(t)
+        wts.append(gr.layer_weights(t))
+    head_norm = head_w = logits = None
+    if wl.vocab:
+        hn, hw = synth.head_weights(wl)
+        head_norm, head_w = up(hn), up(hw)
+        logits = torch.empty((wl.batch, wl.vocab), dtype=torch.float32, device=dev)
+    x0_host = synth.input_x(wl)
+    x0 = up(x0_host)
+    x = torch.empty_like(x0)
+    bt, cg = up(pm.block_table), up(ctx)
+    cfg = gr.layer_cfg(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.ffn, wl.rms_eps, wl.rope_theta,
+                       wl.rope_style, wl.qk_norm, wl.kv_dtype)
+    sargs = gr.StackArgs(cfg, wts, k_dev, v_dev)
+    ws = gr.workspace(gr.decode_stack_workspace_size(cfg, wl.batch, max_ctx, wl.vocab), dev)
+
+    def step():
+        x.copy_(x0)
+        gr.gr_decode_stack(sargs, pm.num_pages, x, bt, cg, max_ctx, head_norm, head_w, wl.w_head, wl.vocab, logits,
+                           ws=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert torch.isfinite(x).all().item(), f"non-finite decode output ({name})"
+    sb, head_b, pack_b = stage_bytes(wl, ctx, kv_bytes_per_token(wl))
+    step_bytes = wl.n_layers * sum(sb.values()) + head_b + pack_b
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    out = {"workload": f"{wl.name}: {wl.n_layers} layers, hidden {wl.hidden}, B={wl.batch}, ctx {wl.ctx_kind} "
+                       f"{wl.ctx_lo}-{wl.ctx_hi} (mean {ctx.mean():.0f}), kv {['f32', 'f16', 'q8_0'][wl.kv_dtype]}, "
+                       f"pool {wl.pool_kind}" + (f", vocab {wl.vocab}" if wl.vocab else ""),
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(wl.batch / (ms * 1e-3), 1),
+           "step_bytes": int(step_bytes), "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+           "kv_bytes_per_step": int(wl.n_layers * (int(np.sum(ctx.astype(np.int64) + 1)) * kv_bytes_per_token(wl))),
+           "cpu_baseline": None}
+    del graph, ws, keep, wts, k_dev, v_dev
+    torch.cuda.empty_cache()
+    if cpu:
+        import oracle
+        oracle.lib()
+        c0 = time.time()
+        oracle.decode_layer(wl, lw0, k0, v0, x0_host, pm.block_table, ctx)
+        layer_s = time.time() - c0
+        est = layer_s * wl.n_layers
+        sample = f"layer 0 of {wl.n_layers} at B={wl.batch} with the workload's contexts ({layer_s:.1f} s), scaled"
+        if wl.vocab:
+            sample += "; the output head not sampled"
+        out["cpu_baseline"] = {"value": round(wl.batch / est, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
+                               "kind": "oracle", "sample": sample, "seconds_per_step": round(est, 3)}
     return out
 
 
@@ -452,6 +588,8 @@ def main():
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs of this script "
                          "with --copy-calib (no GPU work)")
     ap.add_argument("--cpu-layers", type=int, default=64, help="layers the oracle runs (the rest are scaled)")
+    ap.add_argument("--configs", nargs="*", default=["qwen3_0p6b", "qwen3_8b", "longctx"], metavar="WORKLOAD",
+                    help="other workloads whose whole step is also timed (reported under 'configs')")
     ap.add_argument("--probe-runs", type=int, default=5, help="replays of the probed step per stage")
     ap.add_argument("--probe-reps", type=int, default=1,
                     help="launches of the probed stage per probe (above 1, a repeat may hit in cache)")
@@ -640,6 +778,15 @@ def main():
         formats = measure_weight_formats(gr, torch, wl)
         log("[bench] weight formats: " + json.dumps(formats["formats"]))
 
+    stream = measure_stream_ceiling(gr, torch)
+    log("[bench] stream ceiling: " + json.dumps(stream))
+    configs = {}
+    for name in args.configs:
+        if name == wl.name:
+            continue
+        configs[name] = measure_config(gr, torch, name, args.steps, args.warmup, not args.no_cpu_baseline)
+        log(f"[bench] config {name}: " + json.dumps(configs[name]))
+
     # ---- CPU baseline: the fp64 oracle on one whole step of the same workload (every
     #      layer and the output head), when that is bounded; else on its first layers
     cpu = None
@@ -696,7 +843,9 @@ def main():
         "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "roofline": roofline,
+        "stream_ceiling": stream,
         "cpu_baseline": cpu,
+        "configs": configs or None,
         "stages": stages,
         "sampling": sampling,
         "verify": verify,

@@ -79,6 +79,8 @@ def _load() -> C.CDLL:
     for n in ("gr_q4k_gemm", "gr_q6k_gemm", "gr_q5k_gemm", "gr_q8_0_gemm"):
         getattr(L, n).argtypes = [_p, _p, _p, _i, _i, _i, _p, _sz, _p]
         getattr(L, n).restype = _i
+    L.gr_stream_read.argtypes = [_p, _sz, _p, _p]
+    L.gr_stream_read.restype = _i
     L.gr_paged_decode_attn_workspace_size.argtypes = [C.POINTER(AttnMeta), _i]
     L.gr_paged_decode_attn_workspace_size.restype = _sz
     L.gr_paged_decode_attn.argtypes = [_p, _p, _p, _p, _p, _p, _i, C.POINTER(AttnMeta), _p, _sz, _p]
@@ -122,7 +124,7 @@ def _load() -> C.CDLL:
     L.gr_sample_workspace_size.restype = _sz
     L.gr_sample.argtypes = [_p, _i, _i, _p, _p, _p, _p, _sz, _p]
     L.gr_sample.restype = _i
-    if L.gr_abi_version() != 9:
+    if L.gr_abi_version() != 10:
         raise ImportError("libgr ABI version mismatch")
     _lib = L
     return L
@@ -132,7 +134,7 @@ def lib() -> C.CDLL:
     return _load()
 
 
-EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_bytes", "gr_q4k_dequant",
+EXPORTED = ("gr_abi_version", "gr_status_str", "gr_last_hip_error", "gr_kv_head_bytes", "gr_stream_read", "gr_q4k_dequant",
             "gr_q6k_dequant", "gr_q8_0_dequant", "gr_gemm_workspace_size", "gr_gemm_launch_shape", "gr_q4k_gemm",
             "gr_q6k_gemm", "gr_q5k_gemm", "gr_q8_0_gemm",
             "gr_paged_decode_attn_workspace_size", "gr_paged_decode_attn", "gr_paged_decode_attn_noalloc", "gr_attn_launch_shape", "gr_paged_gather_kv",
@@ -234,6 +236,19 @@ def gr_q8_0_gemm(wblocks, x, n: int, y=None, ws=None):
 
 
 GEMM_EPI_STORE, GEMM_EPI_RESIDUAL, GEMM_EPI_SWIGLU = 0, 1, 2
+
+
+STREAM_READ_WORDS = 2048
+
+
+def gr_stream_read(buf, out=None):
+    """One read-only pass over a device tensor's bytes (the read-ceiling measurement aid);
+    returns the per-workgroup int32 checksums (their XOR covers the whole buffer)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(STREAM_READ_WORDS, dtype=torch.int32, device=buf.device)
+    _check("gr_stream_read", _load().gr_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), _stream()))
+    return out
 
 
 def gr_gemm_launch_shape(wtype: int, rows: int, k: int, b: int, epi: int = GEMM_EPI_STORE) -> dict:

@@ -18,6 +18,7 @@ thread_local ProbeEvents* probe_events = nullptr;
 
 
 hipError_t launch_dequant(int kind, const void* blocks, int64_t n, float* out, hipStream_t st);
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* out, hipStream_t st);
 size_t sample_workspace_bytes(int B, int vocab);
 hipError_t launch_spec_accept(const int32_t* sampled, const int32_t* draft, int B, int T, int32_t* n_accepted,
                               hipStream_t st);
@@ -599,6 +600,15 @@ static gr_status dequant_common(int kind, const void* blocks, int64_t n, float* 
   gr_status s = check_device();
   if (s != GR_OK) return s;
   return check_launch(launch_dequant(kind, blocks, n, out, (hipStream_t)stream));
+}
+gr_status gr_stream_read(const void* p, size_t bytes, uint32_t* out, void* stream) {
+  if (bytes == 0) return GR_OK;
+  if (!p || !out) return GR_ERR_NULL;
+  if (bytes % 16) return GR_ERR_SHAPE;
+  if (!aligned(p, 16) || !aligned(out, 4)) return GR_ERR_ALIGN;
+  gr_status s = check_device();
+  if (s != GR_OK) return s;
+  return check_launch(launch_stream_read(p, bytes, out, (hipStream_t)stream));
 }
 gr_status gr_q4k_dequant(const void* b, int64_t n, float* out, void* s) { return dequant_common(12, b, n, out, s); }
 gr_status gr_q6k_dequant(const void* b, int64_t n, float* out, void* s) { return dequant_common(14, b, n, out, s); }

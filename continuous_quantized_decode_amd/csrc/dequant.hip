@@ -188,4 +188,42 @@ hipError_t launch_gather(int kv_dtype, int D, const void* pool, int is_v, const 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Read-only stream (measurement aid): every workgroup's waves walk the buffer in 8 KB
+// steps (eight 1 KB loads of 16 bytes per lane in flight per wave), grid-stride, and
+// fold what they read into one checksum word per workgroup (plain stores: same-address
+// atomics from every workgroup would serialize and show up in the time): the ceiling a
+// plain streaming read reaches on this GPU, next to which the step's kernels are
+// measured.
+constexpr int kStreamGrid = GR_STREAM_READ_WORDS, kStreamDepth = 8;
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, size_t n16, uint32_t* out) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t step = (size_t)gridDim.x * 4 * kStreamDepth * 64;
+  uint32_t acc = 0;
+  for (size_t base = ((size_t)blockIdx.x * 4 + wave) * kStreamDepth * 64; base < n16; base += step) {
+    u32x4 v[kStreamDepth];
+#pragma unroll
+    for (int d = 0; d < kStreamDepth; ++d) {
+      const size_t i = base + (size_t)d * 64 + lane;
+      v[d] = p[i < n16 ? i : n16 - 1];
+    }
+#pragma unroll
+    for (int d = 0; d < kStreamDepth; ++d)
+      if (base + (size_t)d * 64 + lane < n16) acc ^= v[d].x ^ v[d].w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+  __shared__ uint32_t s_acc[4];
+  if (lane == 0) s_acc[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = s_acc[0] ^ s_acc[1] ^ s_acc[2] ^ s_acc[3];
+}
+
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* out, hipStream_t st) {
+  if (bytes < 16) return hipSuccess;
+  stream_read_kernel<<<dim3(kStreamGrid), 256, 0, st>>>((const u32x4*)p, bytes / 16, out);
+  return hipGetLastError();
+}
+
 }  // namespace gr

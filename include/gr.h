@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GR_ABI_VERSION 9
+#define GR_ABI_VERSION 10
 
 typedef enum {
   GR_OK = 0,
@@ -106,6 +106,15 @@ gr_status gr_q5k_gemm(const void* wblocks, const float* x, float* y, int B, int 
                       size_t ws_bytes, void* stream);
 gr_status gr_q8_0_gemm(const void* wblocks, const float* x, float* y, int B, int N, int K, void* workspace,
                        size_t ws_bytes, void* stream);
+
+/* Measurement aid: one read-only pass over `bytes` bytes at p (16-byte aligned, a
+ * multiple of 16) by a plain streaming kernel of GR_STREAM_READ_WORDS workgroups
+ * (grid-stride, 16-byte loads, eight 1 KB loads in flight per wave).  out[w] (uint32,
+ * GR_STREAM_READ_WORDS of them) receives workgroup w's XOR of the first and last dword
+ * of every 16-byte unit it read; the XOR of all out[w] covers the whole buffer.  Its
+ * rate is the practical read ceiling the decode step's kernels are compared with. */
+#define GR_STREAM_READ_WORDS 2048
+gr_status gr_stream_read(const void* p, size_t bytes, uint32_t* out, void* stream);
 
 /* Launch shape of one fused-dequant GEMM launch (a profiling aid: it names the
  * dispatch a counter or trace row belongs to).  rows: output rows of the launch (for

@@ -37,10 +37,12 @@ def test_host_side_checks_without_gpu():
     """Calls that fail a host check return their status before touching the device."""
     import continuous_quantized_decode_amd as gr
     L = gr.lib()
-    assert L.gr_abi_version() == 9
+    assert L.gr_abi_version() == 10
     assert L.gr_status_str(-6) == b"max_ctx + 1 tokens exceed the block table's pages"
     assert L.gr_kv_head_bytes(2, 128) == 16 * 128 + 16 * 4 * 2
     assert L.gr_kv_head_bytes(7, 128) == -1
+    assert L.gr_stream_read(None, 0, None, None) == 0
+    assert L.gr_stream_read(None, 16, None, None) == -1
     # B == 0 is a no-op; NULL pointers, bad K, bad dtype, capacity are rejected
     assert L.gr_q4k_gemm(None, None, None, 0, 16, 256, None, 0, None) == 0
     assert L.gr_q4k_gemm(None, None, None, 1, 16, 256, None, 0, None) == -1

@@ -265,3 +265,13 @@ def test_page_gather_bit_exact(torch, gr, orc, kv_dtype, d):
         for b, n in enumerate(c):
             assert np.array_equal(got[b, :n].astype(np.float64), want[off:off + n]), (is_v, b)
             off += n
+
+
+@pytest.mark.parametrize("nbytes", [16, 8192 * 3 + 48, (1 << 24) + 16 * 7])
+def test_stream_read_checksum(torch, gr, nbytes):
+    """The read-ceiling kernel reads every 16-byte unit once: its XOR of each unit's
+    first and last dword equals numpy's (sizes below one step, ragged, and many steps)."""
+    a = np.random.default_rng(nbytes).integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    want = np.bitwise_xor.reduce(a.reshape(-1, 4)[:, 0] ^ a.reshape(-1, 4)[:, 3])
+    got = host(gr.gr_stream_read(dev(a.view(np.int32), torch))).view(np.uint32)
+    assert int(np.bitwise_xor.reduce(got)) == int(want)
