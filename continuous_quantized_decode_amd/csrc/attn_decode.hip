@@ -342,8 +342,31 @@ __global__ __launch_bounds__(kAttnDecWaves * 64, 2) void attn_decode_kernel(Attn
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) st.O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool live = 2 * kg < R;  // this lane group holds real heads
-  for (int k = 0; k < ngrp; ++k) {
+  // Every group but the workgroup's last: software-pipelined.  Each page's registers are
+  // refilled with the next group's page as soon as the page is consumed, so the next
+  // group's loads overlap this group's math.  The entries of the group after next are
+  // requested first, so reading them later waits for no page load.  All pages of these
+  // groups hold context.
+  for (int k = 0; k + 1 < ngrp; ++k) {
     const int w0 = pgw + k * PG + wave * PW;  // this wave's first page of the group
+    const int nbt = bt_next;                  // entries of group k + 1
+    const int gp = pgw + (k + 1) * PG;
+    bt_next = load_bt(gp + (k + 2 < ngrp ? PG : 0));
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int pg = w0 + i;
+      if (FUSED && owner && pg == new_page) patch_page<KVDT, D>(r[i], s_knew, s_vnew, new_slot, lane);
+      dec_page<KVDT, D>(r[i], min(kPage, n_tok - pg * kPage), qf, s_p[wave], lane, live, st);
+      // the refill stays behind the page's math (hoisted, it would need a second set
+      // of page registers)
+      __builtin_amdgcn_sched_barrier(0);
+      const u32 npg = (u32)__builtin_amdgcn_readlane(nbt, min(wave * PW + i, n_pages - 1 - gp));
+      load_page<KVDT, D>(r[i], kbase + (size_t)npg * page_bytes, vbase + (size_t)npg * page_bytes, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  {  // the last group (pages past the row's end are skipped)
+    const int w0 = pgw + (ngrp - 1) * PG + wave * PW;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int pg = w0 + i;
@@ -351,12 +374,6 @@ __global__ __launch_bounds__(kAttnDecWaves * 64, 2) void attn_decode_kernel(Attn
         if (FUSED && owner && pg == new_page) patch_page<KVDT, D>(r[i], s_knew, s_vnew, new_slot, lane);
         dec_page<KVDT, D>(r[i], min(kPage, n_tok - pg * kPage), qf, s_p[wave], lane, live, st);
       }
-    }
-    if (k + 1 < ngrp) {
-      bt_lane = bt_next;
-      const int gp = pgw + (k + 1) * PG;
-      load_group(gp);
-      bt_next = load_bt(gp + (k + 2 < ngrp ? PG : 0));
     }
   }
 

@@ -83,9 +83,10 @@ constexpr int kAttnDecWaves = 4;
 constexpr int kAttnDecMaxWg = 256;  // workgroups per (row, KV head) one merge takes
 constexpr int kAttnDecMaxGroups = 8;  // groups of pages per workgroup
 constexpr int kAttnDecWgPerCu = 2;    // resident workgroups per CU (two waves per SIMD)
-// pages per wave: every page in flight at once within two waves' registers per SIMD
+// pages per wave: a group's pages in registers at once, two waves per SIMD (q8_0: six,
+// so the software-pipelined page loop fits the registers without spilling)
 __host__ __device__ constexpr int attn_dec_pages(int kv_dtype) {
-  return kv_dtype == KV_F32_T ? 2 : kv_dtype == KV_F16_T ? 4 : 8;
+  return kv_dtype == KV_F32_T ? 2 : kv_dtype == KV_F16_T ? 4 : 6;
 }
 struct AttnDecPlan {
   int wg_pages;  // pages per workgroup
