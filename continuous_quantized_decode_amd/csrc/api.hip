@@ -312,6 +312,7 @@ AttnPlan layer_attn_plan(int rows, const gr_layer_cfg* c, int max_ctx, int T = 1
   const AttnDecPlan dp = plan_attn_dec(c->kv_dtype, max_ctx + T);
   pl.dec_wg_max = dp.wg_max;
   pl.dec_wg_pages = dp.wg_pages;
+  pl.dec_slots = attn_dec_slots(c->kv_dtype);
   return pl;
 }
 
@@ -368,7 +369,7 @@ AttnSched attn_sched(const LayerBufs& L, const int32_t* ctx, int B, const AttnPl
   z.B = B;
   z.self = 1;
   z.n_kv_heads = L.n_cnt / (B > 0 ? B : 1);
-  z.slots = attn_dec_slots();
+  z.slots = apl.dec_slots;
   z.group_pages = apl.dec_wg_pages;
   z.max_groups = kAttnDecMaxGroups;
   z.list = L.sched;
@@ -802,7 +803,7 @@ static gr_status paged_decode_attn_ws(const float* q, const void* k_pages, const
   sc.B = B;
   sc.self = 0;
   sc.n_kv_heads = m->n_kv_heads;
-  sc.slots = attn_dec_slots();
+  sc.slots = attn_dec_slots(m->kv_dtype);
   sc.group_pages = ap.wg_pages;
   sc.max_groups = kAttnDecMaxGroups;
   sc.list = list;

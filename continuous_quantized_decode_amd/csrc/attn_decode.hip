@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kAttnDecWaves * 64, 2) void attn_decode_kernel(Attn
   if (tid == 0) __hip_atomic_store(p.wg_cnt + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-int attn_dec_slots() {
+int attn_dec_slots(int kv_dtype) {
   static const int cus = [] {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
@@ -471,7 +471,8 @@ int attn_dec_slots() {
     (void)hipGetLastError();
     return 256;
   }();
-  return cus * kAttnDecWgPerCu;
+  (void)kv_dtype;
+  return cus * 2;
 }
 
 AttnDecPlan plan_attn_dec(int kv_dtype, int max_tokens) {

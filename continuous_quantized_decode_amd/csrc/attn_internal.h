@@ -68,7 +68,8 @@ GR_DEV void attn_row_place(const AttnParams& p, int b, int& seq, int& pos) {
 struct AttnPlan {
   int pages_per_split, max_splits;
   int dec_wg_max = 0, dec_wg_pages = 0;  // decode kernel (one token per row): workgroups per
-                                         // (row, KV head), pages per workgroup
+                                         // (row, KV head), pages per workgroup,
+  int dec_slots = 0;                     // resident workgroups (attn_dec_slots)
 };
 
 AttnPlan plan_attn(int B, int n_kv_heads, int max_ctx_tokens);
@@ -80,20 +81,22 @@ hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, in
 // kAttnDecWaves waves take kAttnDecWaves * attn_dec_pages consecutive pages of one (row,
 // KV head); each wave loads its pages all at once.
 constexpr int kAttnDecWaves = 4;
-constexpr int kAttnDecMaxWg = 256;  // workgroups per (row, KV head) one merge takes
+constexpr int kAttnDecMaxWg = 512;  // workgroups per (row, KV head) one merge takes
 constexpr int kAttnDecMaxGroups = 8;  // groups of pages per workgroup
-constexpr int kAttnDecWgPerCu = 2;    // resident workgroups per CU (two waves per SIMD)
-// pages per wave: a group's pages in registers at once, two waves per SIMD (q8_0: six,
-// so the software-pipelined page loop fits the registers without spilling)
+// pages per wave (a group's pages sit in registers at once; measured: f16 two pages
+// 21.2 us per Llama-3-8B layer against 22.8 us for four, whose refills wait a whole
+// group; eight q8_0 pages make the software-pipelined page loop spill)
 __host__ __device__ constexpr int attn_dec_pages(int kv_dtype) {
-  return kv_dtype == KV_F32_T ? 2 : kv_dtype == KV_F16_T ? 4 : 6;
+  return kv_dtype == KV_F32_T ? 2 : kv_dtype == KV_F16_T ? 2 : 6;
 }
 struct AttnDecPlan {
   int wg_pages;  // pages per workgroup
   int wg_max;    // the most workgroups of one (row, KV head); 0: max_tokens too long
 };
 AttnDecPlan plan_attn_dec(int kv_dtype, int max_tokens);
-int attn_dec_slots();  // resident decode-attention workgroups of the device
+// resident decode-attention workgroups of the device for a KV format: two per CU (two
+// waves per SIMD; three per CU for f16 measured no faster)
+int attn_dec_slots(int kv_dtype);
 size_t attn_dec_part_floats(int B, int n_q_heads, int head_dim, int wg_max);
 // fused: the decode layer's variant (QK-norm, RoPE and the KV append of the new token
 // from p.qkv, n_tok = ctx + 1); otherwise q from p.q and ctx tokens already in the pool.

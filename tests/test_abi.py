@@ -168,23 +168,23 @@ def test_mixed_stack_head_rows_host_checks():
 
 def test_attn_launch_shape():
     """The decode attention's plan (host-only call): four waves per workgroup, each with
-    all of its pages in flight (f32 2, f16 4, q8_0 6 pages); the long-context workload's
+    all of its pages in flight (f32 2, f16 2, q8_0 6 pages); the long-context workload's
     rows take more than 64 workgroups, whose states the last one merges; a context past
-    256 workgroups is refused before anything runs, by the decode layer too."""
+    512 workgroups is refused before anything runs, by the decode layer too."""
     import continuous_quantized_decode_amd as gr
     sh = gr.gr_attn_launch_shape(2, 64, 8, 32768 + 1)  # q8_0: 24 pages per workgroup
     assert sh["waves_per_wg"] == 4 and sh["pages_per_wave"] == 6
     assert sh["wg_per_row"] == -(-2049 // 24) > 64
     assert sh["grid_threads"] == 64 * 8 * sh["wg_per_row"] * 256
-    llama = gr.gr_attn_launch_shape(1, 8, 8, 3574)  # f16: 16 pages per workgroup
-    assert llama["pages_per_wave"] == 4 and llama["wg_per_row"] == 14
+    llama = gr.gr_attn_launch_shape(1, 8, 8, 3574)  # f16: 8 pages per workgroup
+    assert llama["pages_per_wave"] == 2 and llama["wg_per_row"] == 28
     assert gr.gr_attn_launch_shape(1, 8, 8, 16)["wg_per_row"] == 1
     assert gr.gr_attn_launch_shape(0, 1, 1, 16 * 8 + 1)["wg_per_row"] == 2  # f32: 8 pages per workgroup
-    assert gr.gr_attn_launch_shape(1, 1, 1, 256 * 16 * 16)["wg_per_row"] == 256
+    assert gr.gr_attn_launch_shape(1, 1, 1, 256 * 16 * 8)["wg_per_row"] == 256
     L = gr.lib()
     v = [ctypes.c_int() for _ in range(3)]
     g = ctypes.c_longlong()
-    too_long = 256 * 16 * 16 + 1  # f16: 256 workgroups of 16 pages
+    too_long = 512 * 16 * 8 + 1  # f16: 512 workgroups of 8 pages
     assert L.gr_attn_launch_shape(1, 1, 1, too_long, *[ctypes.byref(i) for i in v], ctypes.byref(g)) == -6
     # the same limit for a decode layer: max_ctx + 1 tokens
     cfg = gr.layer_cfg(256, 4, 2, 64, 768, 1e-6, 1e4, 0, 0, 1)
