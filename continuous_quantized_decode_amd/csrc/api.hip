@@ -635,10 +635,10 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
   // the choices gemm_run and gemm_swiglu make
   if ((pair || epi == 0) && !use_mm(wtype, B) && use_tile_loop(wtype, tiles, K, B)) {
     const TlPlan tp = plan_gemm_tl(wtype, pair ? 2 : 1, tiles, K, B);
-    *tile_loop = 1;
+    *tile_loop = tp.whole ? 3 : 1;
     *nt = pair ? 2 : 1;
     *btn = tl_btn(B);
-    *maxt = 512;
+    *maxt = tp.whole ? 1024 : 512;
     *grid_threads = tp.grid * tp.waves * 64;
     *block_threads = tp.waves * 64;
     return GR_OK;

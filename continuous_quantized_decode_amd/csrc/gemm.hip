@@ -768,10 +768,28 @@ GR_DEV u32 bf16_dup(float v) {
 // Row n's Q4_K super-block from its staged bytes (rp): the quants of lane group kg, the
 // scales sd[j] = d sc_j, dmin, and the mins m_2kg, m_2kg+1 as the B operand of a K = 16
 // MFMA (each repeated for a bf16 hi / lo pair of the A operand).
+GR_DEV void q4_decode_tl(const Q4Regs& w, int kg, float (&sd)[8], float& dmin, u32x2& bm);
 GR_DEV void q4_load_tl(const lds_u8* rp, int kg, Q4Regs& w, float (&sd)[8], float& dmin, u32x2& bm) {
   w.hdr = *(const __attribute__((address_space(3))) u32x4*)rp;
 #pragma unroll
   for (int c = 0; c < 4; ++c) w.qs[c] = *(const __attribute__((address_space(3))) u32x2*)(rp + 16 + 32 * c + 8 * kg);
+  q4_decode_tl(w, kg, sd, dmin, bm);
+}
+// The same from a whole-tile slot: unit j of the row's block sits at unit (c0 + j) mod U
+// of the row (rowp), c0 = the block's first unit plus the row's rotation.
+GR_DEV void q4_load_tlw(const lds_u8* rowp, int c0, int U, int kg, Q4Regs& w, float (&sd)[8], float& dmin,
+                        u32x2& bm) {
+  auto unit = [&](int j) {
+    const int u = c0 + j;
+    return rowp + 16 * (u >= U ? u - U : u);
+  };
+  w.hdr = *(const __attribute__((address_space(3))) u32x4*)unit(0);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    w.qs[c] = *(const __attribute__((address_space(3))) u32x2*)(unit(1 + 2 * c + (kg >> 1)) + 8 * (kg & 1));
+  q4_decode_tl(w, kg, sd, dmin, bm);
+}
+GR_DEV void q4_decode_tl(const Q4Regs& w, int kg, float (&sd)[8], float& dmin, u32x2& bm) {
   const u32 h0 = w.hdr.x, s0 = w.hdr.y, s1 = w.hdr.z, s2 = w.hdr.w;
   const float d = h2f((u16)(h0 & 0xFFFF));
   dmin = h2f((u16)(h0 >> 16));
@@ -831,6 +849,36 @@ GR_DEV void q4_step_tl(lds_u8* const (&slot)[NT], const u32x4 (&ca)[BTN][8], con
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[t][b][e] = __builtin_fmaf(-dmin[t], corr[e], acc[t][b][e]);
     }
+}
+
+// One Q4_K super-block of one tile from a whole-tile slot (q4_step_tl's arithmetic).
+template <int BTN>
+GR_DEV void q4_step_tlw(const lds_u8* rowp, int c0, int U, const u32x4 (&ca)[BTN][8], const u32x2 (&aS)[BTN],
+                        int lane, float (&acc)[BTN][4]) {
+  const u32x4 neg128 = {kNeg128Bf16, kNeg128Bf16, kNeg128Bf16, kNeg128Bf16};
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int kg = lane >> 4;
+  const u32 M = vconst(0x43004300u);
+  Q4Regs w;
+  float sd[8], dmin;
+  u32x2 bm;
+  q4_load_tlw(rowp, c0, U, kg, w, sd, dmin, bm);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 bq = q4_expand(w.qs[j >> 1], (j & 1) != 0, M);
+#pragma unroll
+    for (int b = 0; b < BTN; ++b) {
+      const f32x4 dd = mfma_bf16_k32(ca[b][j], bq, mfma_bf16_k32(ca[b][j], neg128, z4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[b][e] = __builtin_fmaf(sd[j], dd[e], acc[b][e]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < BTN; ++b) {
+    const f32x4 corr = mfma_bf16_k16(aS[b], bm, z4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[b][e] = __builtin_fmaf(-dmin, corr[e], acc[b][e]);
+  }
 }
 
 // Workgroup barrier for LDS written with ds_write only: the weight loads in flight
@@ -1064,6 +1112,207 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------------
+// Tile loop with whole-tile staging: the Q4_K gate/up pairs (the SwiGLU GEMM) at one
+// activation tile.  The per-wave K slices above load 16 rows x 144 bytes per
+// instruction, many short runs; here the workgroup's waves load each weight tile
+// together, a tile being 16 rows of K / 256 consecutive super-blocks, consecutive in
+// memory, so every 1 KB instruction reads a few long runs (gemm_addr.h: wt_*; each row
+// is rotated in LDS so that one column of 16 rows falls on different banks).  One
+// workgroup per CU, one wave per super-block of K (its activation fragments held in
+// registers for the whole launch), a three-slot ring of whole tiles: two tiles in
+// flight while one is computed.  Stage q is tile q of the workgroup's run (gate and up
+// of pair q / 2); the pairs are split over the grid in proportion (the first
+// workgroups take one more when they do not divide).
+//
+// Step q: wait for this wave's loads of stage q (those of stage q + 1 may stay in
+// flight), then a workgroup barrier (every wave's loads of stage q have landed, and
+// every wave is done reading the slot of stage q - 1), then (even q) the previous
+// pair's epilogue from the reduction buffer, then the loads of stage q + 2 into the
+// freed slot, then stage q's math; after the up tile (odd q) each wave writes its two
+// tiles' partial sums to the reduction buffer, which the next step's barrier publishes.
+// One barrier per tile.  The epilogue's stores go out before the next loads, so waiting
+// for those loads does not wait for stores issued after them.
+constexpr int kTlwSlots = 3;
+
+inline int tlw_waves(int nsb) { return nsb; }
+inline size_t tlw_lds_bytes(int nsb) {
+  return (size_t)kTlwSlots * addr::wt_slot_bytes(nsb) + (size_t)tlw_waves(nsb) * 2 * 128 * sizeof(float);
+}
+
+// One whole-tile staging load (16 bytes per lane into dst + 16 lane).
+GR_DEV void issue_wt(__amdgpu_buffer_rsrc_t rs, lds_u8* dst, u32 voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)dst, 16, voff, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int KWI = addr::kWtInstr;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nwaves = blockDim.x >> 6;  // = nsb: wave w computes super-block w
+  const int n = lane & 15;
+  const int nsb = a.nsb;
+  const int U = addr::wt_units(nsb);
+  const u32 slot_bytes = addr::wt_slot_bytes(nsb);
+  const int kwi = (addr::wt_instrs(nsb) + nwaves - 1) / nwaves;  // loads per wave and tile (<= KWI)
+  lds_u8* const slots = (lds_u8*)lds;
+  float* const red = (float*)(lds + kTlwSlots * (size_t)slot_bytes);  // [waves][2][128]
+
+  if (a.zero_ptr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.0;
+
+  const int g0 = (int)(((long long)blockIdx.x * a.tl_groups) / gridDim.x);
+  const int ng = (int)(((long long)(blockIdx.x + 1) * a.tl_groups) / gridDim.x) - g0;
+  if (ng <= 0) return;  // workgroup-uniform, before any barrier
+  const int nq = 2 * ng;
+  const int rows = a.seg_rows[0];  // gate and up have the same rows
+  const uint8_t* const wg = a.w[0];
+  const uint8_t* const wu = a.w[1];
+  // this lane's source offsets of its loads (the same for every tile; a ragged tile's
+  // descriptor ends at its last row, so the rest read 0)
+  u32 voff[KWI];
+#pragma unroll
+  for (int k = 0; k < KWI; ++k) voff[k] = addr::wt_src(addr::wt_instr(wave, nwaves, k, nsb), lane, nsb);
+  auto issue = [&](int q) {
+    const int lt = g0 + (q >> 1);  // tile within its matrix
+    const uint8_t* base = ((q & 1) ? wu : wg) + (size_t)lt * 16 * a.row_bytes;
+    const int nvalid = min(16, rows - lt * 16);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(u32)((size_t)nvalid * a.row_bytes), kBufDword3);
+    lds_u8* slot = slots + (q % kTlwSlots) * slot_bytes;
+#pragma unroll
+    for (int k = 0; k < KWI; ++k)
+      if (k < kwi) issue_wt(rs, slot + 1024u * (u32)addr::wt_instr(wave, nwaves, k, nsb), voff[k]);
+  };
+  // the loads of one stage are kwi instructions; a wait that leaves the younger stage in
+  // flight allows exactly kwi outstanding
+  auto wait_one_younger = [&]() {
+    if (kwi == 5)
+      wait_vmcnt<5>();
+    else if (kwi == 4)
+      wait_vmcnt<4>();
+    else if (kwi == 3)
+      wait_vmcnt<3>();
+    else if (kwi == 2)
+      wait_vmcnt<2>();
+    else
+      wait_vmcnt<1>();
+  };
+
+  // prologue: RMSNorm partial sums, this wave's activation fragments, then stages 0, 1
+  const int e = threadIdx.x;
+  const int e_brow = 2 * ((e & 127) >> 5) + (e & 1);  // the epilogue element's batch row
+  double sv[16];
+  if (a.ss && wave < 2) {  // the epilogue's threads (e < 128)
+    const int row = min(e_brow, a.B - 1);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sv[q] = a.ss[q * a.B + row];
+  }
+  u32x4 act[1][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) act[0][j] = ((const u32x4*)a.xpack)[((size_t)wave * 8 + j) * 64 + lane];
+  issue(0);
+  if (nq > 1) issue(1);
+  // the activations and partial sums (older than the stages) have landed
+  if (nq > 1) {
+    if (kwi == 5) wait_vmcnt<10>(); else if (kwi == 4) wait_vmcnt<8>(); else if (kwi == 3) wait_vmcnt<6>();
+    else if (kwi == 2) wait_vmcnt<4>(); else wait_vmcnt<2>();
+  } else {
+    wait_one_younger();
+  }
+  float rs = 1.0f;  // 1 / rms of the input row (first, so that the partial sums die early)
+  if (a.ss && e < 128 && e_brow < a.B) {
+    double ssv = 0.0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) ssv += sv[q];
+    rs = 1.0f / sqrtf((float)ssv * a.inv_k + a.eps);
+  }
+  // sub-block sums of the wave's super-block, through its scratch in slot 2 (not loaded
+  // before step 0's barrier)
+  u32x2 aS[1];
+  {
+    const u32x4 ones = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const int m = lane & 15, g = lane >> 4;
+    float* scr = (float*)(slots + 2 * (size_t)slot_bytes) + (size_t)wave * 128;  // [j][row], written once
+    f32x4 sj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sj[j] = mfma_bf16_k32(act[0][j], ones, z4);
+    if (m == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) scr[j * 16 + 4 * g + t] = sj[j][t];
+    }
+    asm volatile("" ::: "memory");  // the reads below see the other lanes' writes
+    u16 h0, l0, h1, l1;
+    split_bf16(scr[(2 * g) * 16 + m], h0, l0);
+    split_bf16(scr[(2 * g + 1) * 16 + m], h1, l1);
+    aS[0] = u32x2{(u32)h0 | ((u32)l0 << 16), (u32)h1 | ((u32)l1 << 16)};
+  }
+
+  // row n of a slot, and the unit column of this wave's super-block in that row
+  const int c0 = [&] {
+    const int c = 9 * wave + addr::wt_rot(n, U);
+    return c >= U ? c - U : c;
+  }();
+  auto epilogue = [&](int pr) {  // pair g0 + pr, from the reduction buffer
+    // the element's indices are recomputed here from an opaque copy of the thread index,
+    // so that they are not held in registers across the main loop
+    int ee = threadIdx.x;
+    asm volatile("" : "+v"(ee));
+    if (ee < 128) {
+      const int erem = ee & 127, elp = erem >> 1;
+      const int brow = 2 * (elp >> 4) + (erem & 1);
+      float v = 0.f, v2 = 0.f;
+      for (int w = 0; w < nwaves; ++w) {
+        v += red[((size_t)w * 2 + 0) * 128 + erem];
+        v2 += red[((size_t)w * 2 + 1) * 128 + erem];
+      }
+      const int col = (g0 + pr) * 16 + (elp & 15);
+      if (brow < a.B && col < rows) {
+        const float gv = rs * v, uv = rs * v2;
+        actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, brow, col, gv / (1.0f + expf(-gv)) * uv);
+      }
+    }
+  };
+
+  float acc[2][1][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[t][0][k] = 0.f;
+
+  for (int pr = 0; pr < ng; ++pr) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int q = 2 * pr + t;
+      if (q + 1 < nq)
+        wait_one_younger();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      if (t == 0 && pr > 0) epilogue(pr - 1);
+      if (q + 2 < nq) issue(q + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const lds_u8* rowp = slots + (q % kTlwSlots) * slot_bytes + (size_t)n * U * 16;
+      q4_step_tlw<1>(rowp, c0, U, act, aS, lane, acc[t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the pair's partial sums: red[wave][t][lane * 2 + k]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float* r = red + ((size_t)wave * 2 + t) * 128 + lane * 2;
+      r[0] = acc[t][0][0] + acc[t][0][1];
+      r[1] = acc[t][0][2] + acc[t][0][3];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[t][0][k] = 0.f;
+    }
+  }
+  lds_barrier();
+  epilogue(ng - 1);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1569,11 +1818,15 @@ TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K, int B) {
   pl.waves = (nsb + 1) / 2;
   pl.ring = tl_ring(wtype, nt, btn);
   const int stage = wtype == 12 ? kQ4Stage : kQ6Stage;
-  pl.lds = (size_t)pl.waves * pl.ring * nt * stage + (size_t)2 * pl.waves * nt * btn * 128 * sizeof(float);
+  pl.whole = wtype == 12 && nt == 2 && btn == 1;  // whole-tile staging (gemm_tlw_kernel)
+  if (pl.whole) pl.waves = tlw_waves(nsb);
+  pl.lds = pl.whole ? tlw_lds_bytes(nsb)
+                    : (size_t)pl.waves * pl.ring * nt * stage + (size_t)2 * pl.waves * nt * btn * 128 * sizeof(float);
   const int per_cu = max(1, kGemmLds / (int)pl.lds);
   int wgs = min(groups, variants().cus * per_cu);
   pl.groups_per_wg = (groups + wgs - 1) / wgs;
-  pl.grid = (groups + pl.groups_per_wg - 1) / pl.groups_per_wg;
+  // whole-tile staging splits the groups over every resident workgroup in proportion
+  pl.grid = pl.whole ? wgs : (groups + pl.groups_per_wg - 1) / pl.groups_per_wg;
   return pl;
 }
 
@@ -1590,18 +1843,25 @@ const void* tl_fn(int nt, int btn) {
 hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st) {
   if (pl.grid <= 0) return hipSuccess;
   const int btn = tl_btn(a.B);
-  if ((nt != 1 && nt != 2) || pl.waves < 2 || pl.waves > 8 || pl.lds > (size_t)kGemmLds || a.B > 16 ||
+  if ((nt != 1 && nt != 2) || pl.waves < 2 || pl.waves > (pl.whole ? 16 : 8) || pl.lds > (size_t)kGemmLds || a.B > 16 ||
       (a.ss && a.ss_slots != 16) || (a.epi == kEpiSwiGLU ? 1 : nt) * 128 * btn > pl.waves * 64)
     return hipErrorInvalidValue;
   const bool aligned = wtype == 12 || a.row_bytes % 16 == 0;
-  const void* fn =
-      wtype == 12 ? tl_fn<12, true>(nt, btn) : aligned ? tl_fn<14, true>(nt, btn) : tl_fn<14, false>(nt, btn);
+  if (pl.whole && (wtype != 12 || nt != 2 || btn != 1 || a.epi != kEpiSwiGLU || a.nsb > 16 || a.nsb < 2 ||
+                   pl.waves != tlw_waves(a.nsb) || addr::kWtInstr * pl.waves < addr::wt_instrs(a.nsb) ||
+                   pl.lds != tlw_lds_bytes(a.nsb)))
+    return hipErrorInvalidValue;
+  const void* fn = pl.whole      ? (const void*)gemm_tlw_kernel
+                   : wtype == 12 ? tl_fn<12, true>(nt, btn)
+                   : aligned     ? tl_fn<14, true>(nt, btn)
+                                 : tl_fn<14, false>(nt, btn);
   static const bool lds_set = [] {
     for (int b = 1; b <= 2; ++b)
       for (int t = 1; t <= 2; ++t) {
         const void* all[] = {tl_fn<12, true>(t, b), tl_fn<14, true>(t, b), tl_fn<14, false>(t, b)};
         for (const void* f : all) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
       }
+    (void)hipFuncSetAttribute((const void*)gemm_tlw_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     (void)hipGetLastError();
     return true;
   }();

@@ -99,6 +99,45 @@ GR_HD uint32_t q6_lds_byte(int r, uint32_t b, uint32_t s16) { return 240u * (uin
 GR_HD uint32_t q4_lds_byte(int r, uint32_t b) { return 144u * (uint32_t)r + b; }
 
 // LDS byte offset, within a stage, where lane `lane`'s load of instruction i lands.
+// Whole-tile staging (the tile loop's Q4_K gate/up pairs): the workgroup's waves load a
+// tile's 16 rows together; row r is the tile's bytes [r row_bytes, (r + 1) row_bytes),
+// U = 9 nsb units of 16 bytes.  LDS unit L = 64 i + lane (load instruction i of the tile)
+// holds row r = L / U's unit c = (L % U - rot) mod U: row r is rotated by rot = r units
+// (2 r for odd U), so that reading one unit column of the 16 rows touches different LDS
+// banks (4 (U r + rot) dwords: 4 (U + 1) r or 4 (U + 2) r mod 64, distinct for r < 16
+// until the rotation wraps; a wrap moves a row by 4 U dwords, a multiple of 64 at
+// K = 4096), and an instruction reads at most a few runs of consecutive bytes.  Units past the tile's last one repeat it;
+// their LDS destination (inside the slot) is never read.  A wave's instruction k is
+// wt_instr(wave, waves, k, nsb); those past the tile's last repeat it.
+constexpr int kWtInstr = 5;  // the most load instructions per wave and tile
+GR_HD int wt_units(int nsb) { return 9 * nsb; }
+// rotation of row r, in units (below U)
+GR_HD int wt_rot(int r, int U) { return ((U & 1) ? 2 * r : r) % U; }
+GR_HD int wt_instrs(int nsb) { return (16 * 9 * nsb + 63) / 64; }
+GR_HD uint32_t wt_slot_bytes(int nsb) { return 1024u * (uint32_t)wt_instrs(nsb); }
+GR_HD int wt_instr(int wave, int nwaves, int k, int nsb) {
+  const int i = wave + nwaves * k, n = wt_instrs(nsb);
+  return i < n ? i : n - 1;
+}
+// byte offset, from the tile's first row, of the unit lane `lane` of instruction i loads
+GR_HD uint32_t wt_src(int i, int lane, int nsb) {
+  const int U = wt_units(nsb);
+  int L = 64 * i + lane;
+  if (L > 16 * U - 1) L = 16 * U - 1;
+  const int r = L / U;
+  int c = L - r * U - wt_rot(r, U);
+  if (c < 0) c += U;
+  return 16u * ((uint32_t)r * (uint32_t)U + (uint32_t)c);
+}
+GR_HD uint32_t wt_lds(int i, int lane) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
+// LDS byte holding byte b (< 16 U) of row r
+GR_HD uint32_t wt_lds_byte(int r, uint32_t b, int nsb) {
+  const int U = wt_units(nsb);
+  int c = (int)(b / 16u) + wt_rot(r, U);
+  if (c >= U) c -= U;
+  return 16u * ((uint32_t)r * (uint32_t)U + (uint32_t)c) + b % 16u;
+}
+
 GR_HD uint32_t q4_lds(int lane, int i) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
 GR_HD uint32_t q6_lds(int lane, int i) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
 

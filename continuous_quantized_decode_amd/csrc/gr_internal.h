@@ -129,6 +129,7 @@ bool use_tile_loop(int wtype, int groups, int K, int B);
 struct TlPlan {
   int waves, grid, groups_per_wg, ring;
   size_t lds;
+  bool whole;  // whole-tile staging (gemm_tlw_kernel: the Q4_K gate/up pairs)
 };
 TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K, int B);
 inline int tl_btn(int B) { return B <= 8 ? 1 : 2; }  // activation tiles of the tile loop

@@ -122,9 +122,11 @@ gr_status gr_stream_read(const void* p, size_t bytes, uint32_t* out, void* strea
  * for a gate/up pair, rows = F).  epi: 0 plain store, 1 residual update, 2 gate/up
  * pair with SwiGLU.  Returns which kernel runs (tile_loop 0: the split-K kernel
  * gemm_kernel<type, nt, btn, maxt, aligned>; 1: the tile-loop kernel
- * gemm_tl_kernel<type, nt, aligned, ring> with btn = 1 and maxt = 512; 2: the many-row
+ * gemm_tl_kernel<type, nt, aligned, ring, btn> with maxt = 512; 2: the many-row
  * kernel gemm_mm_kernel<type, aligned>, 512 threads, nt = 2 tiles per wave and btn = 4
- * (Q4_K) or 2 (Q6_K) activation tiles per workgroup), its template
+ * (Q4_K) or 2 (Q6_K) activation tiles per workgroup; 3: the whole-tile tile loop
+ * gemm_tlw_kernel, Q4_K gate/up pairs at one activation tile, one wave per 256 of K,
+ * maxt = 1024), its template
  * parameters (16-row tiles per workgroup or group nt, 8-row batch tiles btn, launch
  * bound maxt) and the grid and workgroup sizes in threads, as launched by every entry
  * point above for these sizes.  GR_ERR_NULL for a null output pointer, GR_ERR_DTYPE for

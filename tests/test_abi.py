@@ -77,8 +77,9 @@ def test_gemm_launch_shape_names_the_kernel():
     # Llama-3-8B shapes at B = 8: the output head and the gate/up pairs run the tile loop
     head = gr.gr_gemm_launch_shape(q6, 128256, 4096, 8, gr.GEMM_EPI_STORE)
     assert head["tile_loop"] and head["nt"] == 1 and head["kernel"] == "gemm_tl_kernel<14, 1,"
-    gu = gr.gr_gemm_launch_shape(q4, 14336, 4096, 8, gr.GEMM_EPI_SWIGLU)
-    assert gu["tile_loop"] and gu["nt"] == 2 and gu["block_threads"] == 8 * 64
+    gu = gr.gr_gemm_launch_shape(q4, 14336, 4096, 8, gr.GEMM_EPI_SWIGLU)  # whole tiles, a wave per 256 of K
+    assert gu["tile_loop"] and gu["whole_tile"] and gu["nt"] == 2 and gu["block_threads"] == 16 * 64
+    assert gu["kernel"] == "gemm_tlw_kernel" and gu["grid_threads"] == 256 * 16 * 64
     # residual updates and small matrices keep the split-K kernel
     down = gr.gr_gemm_launch_shape(q6, 4096, 14336, 8, gr.GEMM_EPI_RESIDUAL)
     assert not down["tile_loop"] and down["kernel"].startswith("gemm_kernel<14, 1, 1,")

@@ -140,3 +140,89 @@ def test_gemm_staging_loads_stay_in_bounds_and_land_where_read():
         out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
         print(out.stdout)
         assert out.returncode == 0, out.stdout
+
+
+WHOLE_TILE_PROGRAM = r"""
+#include <cstdio>
+#include <vector>
+#include "gemm_addr.h"
+using namespace gr::addr;
+
+static int fails = 0;
+#define CHECK(c, ...) do { if (!(c)) { if (fails++ < 20) { std::printf(__VA_ARGS__); std::printf("\n"); } } } while (0)
+
+// Whole-tile staging of Q4_K tiles: every wave's kWtInstr instructions, every lane.
+int main() {
+  const int rows[] = {1, 2, 15, 16, 17, 31, 33, 48};
+  for (int nsb = 1; nsb <= 16; ++nsb) {
+    // the kernel: one wave per super-block, kwi loads per wave and tile
+    const int waves = nsb, U = wt_units(nsb), kwi = (wt_instrs(nsb) + waves - 1) / waves;
+    const uint32_t row_bytes = 144u * nsb, slot = wt_slot_bytes(nsb);
+    CHECK(16u * (uint32_t)U == row_bytes, "units per row");
+    CHECK(kwi <= kWtInstr, "nsb %d: %d loads per wave", nsb, kwi);
+    for (int N : rows) {
+      const uint64_t total = (uint64_t)N * row_bytes;  // the matrix starts at 0
+      for (int row0 = 0; row0 < N; row0 += 16) {
+        const int nvalid = N - row0 < 16 ? N - row0 : 16;
+        const uint64_t tile = (uint64_t)row0 * row_bytes;
+        const uint64_t desc = (uint64_t)nvalid * row_bytes;  // the descriptor's size: rows past the matrix read 0
+        std::vector<int64_t> held(slot, -1);
+        for (int w = 0; w < waves; ++w)
+          for (int k = 0; k < kwi; ++k) {
+            const int i = wt_instr(w, waves, k, nsb);
+            for (int lane = 0; lane < 64; ++lane) {
+              const uint32_t off = wt_src(i, lane, nsb), lds = wt_lds(i, lane);
+              CHECK(off % 16 == 0 && off + 16 <= 16u * row_bytes, "nsb %d: unit outside the 16 rows", nsb);
+              CHECK(lds + 16 <= slot, "nsb %d: LDS write past the slot", nsb);
+              CHECK(off >= desc || tile + off + 16 <= total, "nsb %d N %d: in-descriptor unit past the matrix", nsb, N);
+              for (int b = 0; b < 16; ++b) {
+                const int64_t v = off + b < desc ? (int64_t)(tile + off + b) : -2;  // -2: reads as zero
+                // two loads of one LDS byte must agree (duplicate units and instructions)
+                CHECK(held[lds + b] == -1 || held[lds + b] == v, "nsb %d: LDS byte %u loaded twice differently", nsb,
+                      lds + b);
+                held[lds + b] = v;
+              }
+            }
+          }
+        for (int r = 0; r < nvalid; ++r)
+          for (uint32_t b = 0; b < row_bytes; ++b)
+            CHECK(held[wt_lds_byte(r, b, nsb)] == (int64_t)(tile + (uint64_t)r * row_bytes + b),
+                  "nsb %d N %d row0 %d row %d byte %u", nsb, N, row0, r, b);
+      }
+    }
+    // reads of one unit column by the 16 rows (64 banks of 4 bytes): distinct banks when
+    // 16 divides U (K = 4096: the rotation's wrap moves a row by a multiple of 64 dwords),
+    // at most four rows per bank otherwise (small K, where the rotation wraps)
+    for (int c = 0; c < U; ++c) {
+      std::vector<int> bank_used(64, 0);
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t dw = wt_lds_byte(r, 16u * c, nsb) / 4;
+        for (int q = 0; q < 4; ++q) bank_used[(dw + q) % 64]++;
+      }
+      const int most = U % 16 == 0 ? 1 : 4;
+      for (int q = 0; q < 64; ++q)
+        CHECK(bank_used[q] <= most, "nsb %d column %d: bank %d used %d times", nsb, c, q, bank_used[q]);
+    }
+  }
+  std::printf("%s (%d failures)\n", fails ? "FAIL" : "ok", fails);
+  return fails ? 1 : 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_whole_tile_staging_in_bounds_and_conflict_free():
+    """The whole-tile staging map (the tile loop's Q4_K gate/up pairs): every wave's
+    loads stay inside the tile's 16 rows and the LDS slot, units past the matrix fall
+    outside the buffer descriptor (they read zeros), every byte of every valid row lands
+    where the compute reads it, and one unit column of the 16 rows sits on 64 distinct
+    LDS banks at K = 4096 (four rows per bank at most otherwise)."""
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "check_wt.cpp")
+        exe = os.path.join(d, "check_wt")
+        with open(src, "w") as f:
+            f.write(WHOLE_TILE_PROGRAM)
+        subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.dirname(HDR), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        print(out.stdout)
+        assert out.returncode == 0, out.stdout

@@ -77,6 +77,14 @@ LAYER_CASES = [
          kv_dtype=synth.KV_Q8_0, qk_norm=True, gu=(False, 2)),
     dict(ctx=[9, 130, 47, 2, 61, 18, 77, 5, 100, 1], batch=10, hidden=2048, ffn=8192, w_other=synth.W_Q6_K,
          kv_dtype=synth.KV_F16, gu=(True, 2)),
+    # Q4_K gate/up pairs at one batch tile: the whole-tile kernel (gu's third entry), one
+    # wave per super-block: K = 4096 (528 pairs over 256 workgroups: two or three each), an
+    # odd unit count per row (hidden 768), and K = 1024
+    dict(ctx=[40, 7, 300, 0, 16, 90, 1, 33], batch=8, hidden=4096, ffn=8448, kv_dtype=synth.KV_F16,
+         gu=(True, 1, True)),
+    dict(ctx=[5, 64, 200, 17, 0], batch=5, hidden=768, ffn=8192, kv_dtype=synth.KV_Q8_0, qk_norm=True,
+         gu=(True, 1, True)),
+    dict(ctx=[31, 1], batch=2, hidden=1024, ffn=9216, gu=(True, 1, True)),
 ]
 
 
@@ -108,7 +116,9 @@ def test_tiny_layer_matches_oracle(torch, gr, orc, case):
         # the gate/up kernel this case exists to cover (so the choice cannot drift unseen)
         sh = gr.gr_gemm_launch_shape(synth.layer_weights(wl, 0).tgate, wl.ffn, wl.hidden, len(ctx), gr.GEMM_EPI_SWIGLU)
         say("  gate/up launch", sh)
-        assert (sh["tile_loop"], sh["btn"]) == gu
+        assert (sh["tile_loop"], sh["btn"]) == gu[:2]
+        if len(gu) > 2:
+            assert sh["whole_tile"] == gu[2]
     got, want, gpools, opools, kv = run_layer_case(torch, gr, orc, wl, ctx)
     assert np.isfinite(got).all()
     err, rerr = rel_l2(got, want), row_rel_l2(got, want)
