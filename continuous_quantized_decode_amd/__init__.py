@@ -260,7 +260,7 @@ def gr_gemm_launch_shape(wtype: int, rows: int, k: int, b: int, epi: int = GEMM_
     if tl == 2:
         name = f"gemm_mm_kernel<{wtype},"
     elif tl == 3:
-        name = "gemm_tlw_kernel"
+        name = f"gemm_tlw_kernel<{'true' if nt == 2 else 'false'}>"
     else:
         name = f"gemm_tl_kernel<{wtype}, {nt}," if tl else f"gemm_kernel<{wtype}, {nt}, {btn}, {maxt},"
     return {"tile_loop": tl in (1, 3), "whole_tile": tl == 3, "many_rows": tl == 2, "nt": nt, "btn": btn,

@@ -129,7 +129,8 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     // kernel (one tile per group)
     int type_cols = 0;
     for (int q = i; q < nmat && types[q] == types[i]; ++q) type_cols += rows[q];
-    const bool tl = ep.kind == kEpiStore && !use_mm(types[i], B) && use_tile_loop(types[i], all_tiles, K, B);
+    const bool tl = ep.kind == kEpiStore && !use_mm(types[i], B) &&
+                    (use_tile_loop(types[i], all_tiles, K, B) || use_tile_loop_whole(types[i], all_tiles, K, B));
     const bool mm = !tl && (ep.kind == kEpiStore ? use_mm_store(types[i], B, type_cols) : use_mm(types[i], B));
     const int group = mm ? mm_group_tiles(false) : tl ? 1 : gemm_group(all_tiles);
     while (j < nmat && types[j] == types[i]) {
@@ -218,7 +219,7 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   a.zero_ptr = zero_ptr;
   a.zero_n = zero_n;
   if (use_mm(wtype, B)) return launch_gemm_mm(wtype, (tiles + mm_group_tiles(true) - 1) / mm_group_tiles(true), a, st);
-  if (use_tile_loop(wtype, tiles, K, B)) {
+  if (use_tile_loop(wtype, tiles, K, B) || use_tile_loop_whole(wtype, tiles, K, B)) {
     a.tl_groups = tiles;
     return launch_gemm_tl(wtype, 2, plan_gemm_tl(wtype, 2, tiles, K, B), a, st);
   }
@@ -633,7 +634,8 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
   const int tiles = (rows + 15) / 16;
   const bool pair = epi == 2;
   // the choices gemm_run and gemm_swiglu make
-  if ((pair || epi == 0) && !use_mm(wtype, B) && use_tile_loop(wtype, tiles, K, B)) {
+  if ((pair || epi == 0) && !use_mm(wtype, B) &&
+      (use_tile_loop(wtype, tiles, K, B) || use_tile_loop_whole(wtype, tiles, K, B))) {
     const TlPlan tp = plan_gemm_tl(wtype, pair ? 2 : 1, tiles, K, B);
     *tile_loop = tp.whole ? 3 : 1;
     *nt = pair ? 2 : 1;

@@ -1139,7 +1139,7 @@ constexpr int kTlwSlots = 3;
 
 inline int tlw_waves(int nsb) { return nsb; }
 inline size_t tlw_lds_bytes(int nsb) {
-  return (size_t)kTlwSlots * addr::wt_slot_bytes(nsb) + (size_t)tlw_waves(nsb) * 2 * 128 * sizeof(float);
+  return (size_t)kTlwSlots * addr::wt_slot_bytes(nsb) + (size_t)2 * tlw_waves(nsb) * 128 * sizeof(float);
 }
 
 // One whole-tile staging load (16 bytes per lane into dst + 16 lane).
@@ -1147,7 +1147,9 @@ GR_DEV void issue_wt(__amdgpu_buffer_rsrc_t rs, lds_u8* dst, u32 voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)dst, 16, voff, 0, 0, 0);
 }
 
+template <bool PAIR>
 __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
+  constexpr int SPG = PAIR ? 2 : 1;  // stages (tiles) per group
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int KWI = addr::kWtInstr;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1158,7 +1160,9 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
   const u32 slot_bytes = addr::wt_slot_bytes(nsb);
   const int kwi = (addr::wt_instrs(nsb) + nwaves - 1) / nwaves;  // loads per wave and tile (<= KWI)
   lds_u8* const slots = (lds_u8*)lds;
-  float* const red = (float*)(lds + kTlwSlots * (size_t)slot_bytes);  // [waves][2][128]
+  // reduction buffer [2][waves][128]: the two tiles of a pair, or (single tiles) two
+  // groups in turn, so a group's partial sums never overwrite ones still being read
+  float* const red = (float*)(lds + kTlwSlots * (size_t)slot_bytes);
 
   if (a.zero_ptr && blockIdx.x == 0)
     for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.0;
@@ -1166,19 +1170,22 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
   const int g0 = (int)(((long long)blockIdx.x * a.tl_groups) / gridDim.x);
   const int ng = (int)(((long long)(blockIdx.x + 1) * a.tl_groups) / gridDim.x) - g0;
   if (ng <= 0) return;  // workgroup-uniform, before any barrier
-  const int nq = 2 * ng;
-  const int rows = a.seg_rows[0];  // gate and up have the same rows
-  const uint8_t* const wg = a.w[0];
-  const uint8_t* const wu = a.w[1];
+  const int nq = SPG * ng;
+  // the matrices (at most three; SwiGLU: gate, up) and the group -> (matrix, tile) map
+  const int off1 = a.seg_tile_off[1], off2 = a.seg_tile_off[2], nseg = a.nseg;
+  auto seg_of = [&](int gi) { return PAIR ? 0 : (nseg > 1 && gi >= off1 ? 1 : 0) + (nseg > 2 && gi >= off2 ? 1 : 0); };
+  auto seg_off = [&](int sg) { return sg == 0 ? 0 : sg == 1 ? off1 : off2; };
   // this lane's source offsets of its loads (the same for every tile; a ragged tile's
   // descriptor ends at its last row, so the rest read 0)
   u32 voff[KWI];
 #pragma unroll
   for (int k = 0; k < KWI; ++k) voff[k] = addr::wt_src(addr::wt_instr(wave, nwaves, k, nsb), lane, nsb);
   auto issue = [&](int q) {
-    const int lt = g0 + (q >> 1);  // tile within its matrix
-    const uint8_t* base = ((q & 1) ? wu : wg) + (size_t)lt * 16 * a.row_bytes;
-    const int nvalid = min(16, rows - lt * 16);
+    const int gi = g0 + q / SPG;
+    const int sg = PAIR ? (q & 1) : seg_of(gi);          // the matrix
+    const int lt = PAIR ? gi : gi - seg_off(sg);         // tile within it
+    const uint8_t* base = (sg == 0 ? a.w[0] : sg == 1 ? a.w[1] : a.w[2]) + (size_t)lt * 16 * a.row_bytes;
+    const int nvalid = min(16, (sg == 0 ? a.seg_rows[0] : sg == 1 ? a.seg_rows[1] : a.seg_rows[2]) - lt * 16);
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(u32)((size_t)nvalid * a.row_bytes), kBufDword3);
     lds_u8* slot = slots + (q % kTlwSlots) * slot_bytes;
@@ -1258,7 +1265,7 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
     const int c = 9 * wave + addr::wt_rot(n, U);
     return c >= U ? c - U : c;
   }();
-  auto epilogue = [&](int pr) {  // pair g0 + pr, from the reduction buffer
+  auto epilogue = [&](int pr) {  // group g0 + pr, from the reduction buffer
     // the element's indices are recomputed here from an opaque copy of the thread index,
     // so that they are not held in registers across the main loop
     int ee = threadIdx.x;
@@ -1266,29 +1273,39 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
     if (ee < 128) {
       const int erem = ee & 127, elp = erem >> 1;
       const int brow = 2 * (elp >> 4) + (erem & 1);
+      const int gi = g0 + pr;
+      const float* r0 = red + (size_t)(PAIR ? 0 : (pr & 1)) * nwaves * 128;
       float v = 0.f, v2 = 0.f;
       for (int w = 0; w < nwaves; ++w) {
-        v += red[((size_t)w * 2 + 0) * 128 + erem];
-        v2 += red[((size_t)w * 2 + 1) * 128 + erem];
+        v += r0[(size_t)w * 128 + erem];
+        if (PAIR) v2 += red[((size_t)nwaves + w) * 128 + erem];
       }
-      const int col = (g0 + pr) * 16 + (elp & 15);
-      if (brow < a.B && col < rows) {
-        const float gv = rs * v, uv = rs * v2;
-        actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, brow, col, gv / (1.0f + expf(-gv)) * uv);
+      if (PAIR) {
+        const int col = gi * 16 + (elp & 15);
+        if (brow < a.B && col < a.seg_rows[0]) {
+          const float gv = rs * v, uv = rs * v2;
+          actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, brow, col, gv / (1.0f + expf(-gv)) * uv);
+        }
+      } else {
+        const int sg = seg_of(gi), lt = gi - seg_off(sg);
+        const int rows_s = sg == 0 ? a.seg_rows[0] : sg == 1 ? a.seg_rows[1] : a.seg_rows[2];
+        const int col_s = sg == 0 ? a.seg_col_off[0] : sg == 1 ? a.seg_col_off[1] : a.seg_col_off[2];
+        const int r = lt * 16 + (elp & 15);
+        if (brow < a.B && r < rows_s) a.y[(size_t)brow * a.ldy + col_s + r] = rs * v;
       }
     }
   };
 
-  float acc[2][1][4];
+  float acc[SPG][1][4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < SPG; ++t)
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc[t][0][k] = 0.f;
 
   for (int pr = 0; pr < ng; ++pr) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int q = 2 * pr + t;
+    for (int t = 0; t < SPG; ++t) {
+      const int q = SPG * pr + t;
       if (q + 1 < nq)
         wait_one_younger();
       else
@@ -1301,10 +1318,10 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
       q4_step_tlw<1>(rowp, c0, U, act, aS, lane, acc[t]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the pair's partial sums: red[wave][t][lane * 2 + k]
+    // the group's partial sums: red[t or pr & 1][wave][lane * 2 + k]
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float* r = red + ((size_t)wave * 2 + t) * 128 + lane * 2;
+    for (int t = 0; t < SPG; ++t) {
+      float* r = red + ((size_t)(PAIR ? t : (pr & 1)) * nwaves + wave) * 128 + lane * 2;
       r[0] = acc[t][0][0] + acc[t][0][1];
       r[1] = acc[t][0][2] + acc[t][0][3];
 #pragma unroll
@@ -1811,6 +1828,12 @@ bool use_tile_loop(int wtype, int groups, int K, int B) {
          groups >= 2 * variants().cus;
 }
 
+// Whole-tile staging (Q4_K, one activation tile) from one group per CU.
+bool use_tile_loop_whole(int wtype, int groups, int K, int B) {
+  const int nsb = K / kQK;
+  return wtype == 12 && B <= 8 && K % kQK == 0 && nsb >= 3 && nsb <= 16 && groups >= variants().cus;
+}
+
 TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K, int B) {
   TlPlan pl{};
   const int nsb = K / kQK;
@@ -1818,7 +1841,7 @@ TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K, int B) {
   pl.waves = (nsb + 1) / 2;
   pl.ring = tl_ring(wtype, nt, btn);
   const int stage = wtype == 12 ? kQ4Stage : kQ6Stage;
-  pl.whole = wtype == 12 && nt == 2 && btn == 1;  // whole-tile staging (gemm_tlw_kernel)
+  pl.whole = wtype == 12 && btn == 1 && nsb >= 3 && nsb <= 16;  // whole-tile staging (gemm_tlw_kernel)
   if (pl.whole) pl.waves = tlw_waves(nsb);
   pl.lds = pl.whole ? tlw_lds_bytes(nsb)
                     : (size_t)pl.waves * pl.ring * nt * stage + (size_t)2 * pl.waves * nt * btn * 128 * sizeof(float);
@@ -1847,11 +1870,11 @@ hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipSt
       (a.ss && a.ss_slots != 16) || (a.epi == kEpiSwiGLU ? 1 : nt) * 128 * btn > pl.waves * 64)
     return hipErrorInvalidValue;
   const bool aligned = wtype == 12 || a.row_bytes % 16 == 0;
-  if (pl.whole && (wtype != 12 || nt != 2 || btn != 1 || a.epi != kEpiSwiGLU || a.nsb > 16 || a.nsb < 2 ||
-                   pl.waves != tlw_waves(a.nsb) || addr::kWtInstr * pl.waves < addr::wt_instrs(a.nsb) ||
+  if (pl.whole && (wtype != 12 || btn != 1 || a.epi != (nt == 2 ? kEpiSwiGLU : kEpiStore) || a.nsb > 16 ||
+                   a.nsb < 2 || pl.waves != tlw_waves(a.nsb) || addr::kWtInstr * pl.waves < addr::wt_instrs(a.nsb) ||
                    pl.lds != tlw_lds_bytes(a.nsb)))
     return hipErrorInvalidValue;
-  const void* fn = pl.whole      ? (const void*)gemm_tlw_kernel
+  const void* fn = pl.whole      ? (nt == 2 ? (const void*)gemm_tlw_kernel<true> : (const void*)gemm_tlw_kernel<false>)
                    : wtype == 12 ? tl_fn<12, true>(nt, btn)
                    : aligned     ? tl_fn<14, true>(nt, btn)
                                  : tl_fn<14, false>(nt, btn);
@@ -1861,7 +1884,8 @@ hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipSt
         const void* all[] = {tl_fn<12, true>(t, b), tl_fn<14, true>(t, b), tl_fn<14, false>(t, b)};
         for (const void* f : all) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
       }
-    (void)hipFuncSetAttribute((const void*)gemm_tlw_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    for (const void* f : {(const void*)gemm_tlw_kernel<true>, (const void*)gemm_tlw_kernel<false>})
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     (void)hipGetLastError();
     return true;
   }();

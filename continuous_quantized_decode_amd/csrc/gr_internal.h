@@ -132,6 +132,7 @@ struct TlPlan {
   bool whole;  // whole-tile staging (gemm_tlw_kernel: the Q4_K gate/up pairs)
 };
 TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K, int B);
+bool use_tile_loop_whole(int wtype, int groups, int K, int B);  // gemm_tlw_kernel's sizes
 inline int tl_btn(int B) { return B <= 8 ? 1 : 2; }  // activation tiles of the tile loop
 hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st);
 hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);

@@ -79,7 +79,9 @@ def test_gemm_launch_shape_names_the_kernel():
     assert head["tile_loop"] and head["nt"] == 1 and head["kernel"] == "gemm_tl_kernel<14, 1,"
     gu = gr.gr_gemm_launch_shape(q4, 14336, 4096, 8, gr.GEMM_EPI_SWIGLU)  # whole tiles, a wave per 256 of K
     assert gu["tile_loop"] and gu["whole_tile"] and gu["nt"] == 2 and gu["block_threads"] == 16 * 64
-    assert gu["kernel"] == "gemm_tlw_kernel" and gu["grid_threads"] == 256 * 16 * 64
+    assert gu["kernel"] == "gemm_tlw_kernel<true>" and gu["grid_threads"] == 256 * 16 * 64
+    qkv = gr.gr_gemm_launch_shape(q4, 6144, 4096, 8, gr.GEMM_EPI_STORE)  # Q4_K store from 256 tiles: whole tiles too
+    assert qkv["whole_tile"] and qkv["nt"] == 1 and qkv["kernel"] == "gemm_tlw_kernel<false>"
     # residual updates and small matrices keep the split-K kernel
     down = gr.gr_gemm_launch_shape(q6, 4096, 14336, 8, gr.GEMM_EPI_RESIDUAL)
     assert not down["tile_loop"] and down["kernel"].startswith("gemm_kernel<14, 1, 1,")

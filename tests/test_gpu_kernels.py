@@ -87,7 +87,7 @@ GEMM_CASES = [
     (synth.W_Q4_K, 1, 16, 256),
     (synth.W_Q4_K, 3, 40, 768),      # ragged row tile
     (synth.W_Q4_K, 8, 256, 4096),
-    (synth.W_Q4_K, 8, 4096, 4096),   # split-K
+    (synth.W_Q4_K, 8, 4096, 4096),   # whole-tile tile loop: one tile per workgroup
     (synth.W_Q4_K, 17, 200, 1024),   # three batch tiles, padded to four
     (synth.W_Q4_K, 32, 512, 2048),
     (synth.W_Q4_K, 64, 64, 512),
@@ -102,7 +102,8 @@ GEMM_CASES = [
     (synth.W_Q6_K, 64, 128, 14336),
     (synth.W_Q4_K, 64, 256, 14336),
     # tile-loop kernel (at least two tile groups per CU, one batch tile, K <= 4096)
-    (synth.W_Q4_K, 8, 8200, 4096),   # 513 tiles, the last ragged; runs of three per workgroup
+    (synth.W_Q4_K, 8, 8200, 4096),   # 513 tiles, the last ragged (whole-tile tile loop, two or three per workgroup)
+    (synth.W_Q4_K, 7, 6144, 4096),   # the QKV shape: 384 tiles, one or two per workgroup
     (synth.W_Q6_K, 5, 9000, 1280),   # 2-byte aligned rows, waves of two and one super-blocks
     (synth.W_Q6_K, 8, 8192, 4096),
     (synth.W_Q4_K, 1, 16384, 256),   # one super-block: too few waves for the tile loop
