@@ -132,7 +132,11 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     const bool tl = ep.kind == kEpiStore && !use_mm(types[i], B) &&
                     (use_tile_loop(types[i], all_tiles, K, B) || use_tile_loop_whole(types[i], all_tiles, K, B));
     const bool mm = !tl && (ep.kind == kEpiStore ? use_mm_store(types[i], B, type_cols) : use_mm(types[i], B));
-    const int group = mm ? mm_group_tiles(false) : tl ? 1 : gemm_group(all_tiles);
+    int n_of_type = 0;
+    for (int q = i; q < nmat && types[q] == types[i]; ++q) ++n_of_type;
+    // a Q6_K residual update (down) at one activation tile: K-chunk staging
+    const bool kc = !tl && !mm && ep.kind == kEpiResidual && use_kcw(types[i], K, B, n_of_type);
+    const int group = mm ? mm_group_tiles(false) : (tl || kc) ? 1 : gemm_group(all_tiles);
     while (j < nmat && types[j] == types[i]) {
       a.w[n] = (const uint8_t*)w[j];
       a.seg_rows[n] = rows[j];
@@ -182,6 +186,8 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     } else if (tl) {
       a.tl_groups = tiles;
       e = launch_gemm_tl(wt, 1, plan_gemm_tl(wt, 1, tiles, K, B), a, st);
+    } else if (kc) {
+      e = launch_gemm_kcw(tiles, a, st);
     } else {
       const GemmPlan pl = plan_gemm(wt, tiles, K, B, group);
       a.sb_per_wave = pl.sb_per_wave;
@@ -643,6 +649,16 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
     *maxt = tp.whole ? 1024 : 512;
     *grid_threads = tp.grid * tp.waves * 64;
     *block_threads = tp.waves * 64;
+    return GR_OK;
+  }
+  if (epi == 1 && !use_mm(wtype, B) && use_kcw(wtype, K, B, 1)) {  // K-chunk staging (gemm_kcw_kernel)
+    const int C = kcw_waves(K / kQK);
+    *tile_loop = 4;
+    *nt = 1;
+    *btn = 1;
+    *maxt = 1024;
+    *grid_threads = tiles * C * 64;
+    *block_threads = C * 64;
     return GR_OK;
   }
   if (epi == 0 ? use_mm_store(wtype, B, rows) : use_mm(wtype, B)) {  // the many-row kernel: 512 threads, activation tile groups x weight tile groups

@@ -464,9 +464,13 @@ constexpr u32 kNeg160Bf16 = 0xC320C320u;  // two bf16 -160.0
 // scales and d).  The window holds block byte b at q6_lds_byte(n, b, s16): the field at
 // block byte C (a multiple of 4) is the dword pair at q6_lds_byte(n, C, s16 & 12)
 // shifted right by s16 & 3 bytes.
+GR_DEV void q6_load_at(const lds_u8* rs, u32 sh, int kg, Q6Regs& w);
 GR_DEV void q6_load_lds(const lds_u8* slot, u32 s16, int n, int kg, Q6Regs& w) {
-  const u32 sh = s16 & 3u;  // bytes (alignbyte's shift operand counts bytes)
-  const lds_u8* rs = slot + addr::q6_lds_byte(n, 0, s16 & 12u);
+  // shift in bytes (alignbyte's shift operand counts bytes)
+  q6_load_at(slot + addr::q6_lds_byte(n, 0, s16 & 12u), s16 & 3u, kg, w);
+}
+// A row's block whose byte 0 sits sh bytes past the 4-byte aligned LDS address rs.
+GR_DEV void q6_load_at(const lds_u8* rs, u32 sh, int kg, Q6Regs& w) {
   const lds_u8* rp = rs + 4 * kg;
 #pragma unroll
   for (int hu = 0; hu < 4; ++hu) {
@@ -531,6 +535,31 @@ GR_DEV void q6_step(const GemmArgs& a, lds_u8* const (&slot)[NT], const u32 (&s1
       }
     }
     // keep the scheduler from hoisting all sixteen sub-blocks' MFMAs at once
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One Q6_K super-block of one tile at one activation tile, its block already in
+// registers (q6_step's arithmetic; ca: the activation fragments of the super-block).
+GR_DEV void q6_step_w(const Q6Regs& w, const u32x4* ca, float (&acc)[4]) {
+  const u32x2 neg160 = {kNeg160Bf16, kNeg160Bf16};
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const u32 E = vconst(0x43434343u);
+  const float dsc = h2f(w.d);
+#pragma unroll
+  for (int hu = 0; hu < 4; ++hu) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sub = 8 * (hu >> 1) + 2 * r + (hu & 1);
+      const u32x4 pr = ca[sub >> 1];
+      const u32x2 av = (sub & 1) ? u32x2{pr.z, pr.w} : u32x2{pr.x, pr.y};
+      const f32x4 cs = mfma_bf16_k16(av, neg160, z4);
+      const u32x2 bq = q6_expand(w.part[hu], r, E);
+      const float sd = dsc * (float)(int)(int8_t)((w.sc[sub >> 2] >> (8 * (sub & 3))) & 0xFF);
+      const f32x4 dd = mfma_bf16_k16(av, bq, cs);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sd, dd[e], acc[e]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1330,6 +1359,182 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
   }
   lds_barrier();
   epilogue(ng - 1);
+}
+
+// ---------------------------------------------------------------------------------
+// K-chunk staging: the Q6_K residual GEMM (down) at one activation tile, rows of a
+// multiple of 16 bytes.  One 16-row tile per workgroup, C waves; stage c is super-blocks
+// [C c, C c + C) of the tile's 16 rows (gemm_addr.h: kc_*), loaded by all waves
+// together as runs of consecutive bytes per row into a three-slot LDS ring; wave w
+// computes super-block C c + w of stage c with its activation fragments one stage ahead
+// in registers.  Load order: a(0), w(0), w(1), then at step c (after the barrier) a(c + 1)
+// and w(c + 2); so before step c's math the loads younger than a(c) and w(c) are exactly
+// w(c + 1) when it exists, and one wait count (one stage) covers every step but the last.
+// The waves' sums meet in LDS for the residual epilogue of gemm_kernel.
+constexpr int kKcwSlots = 3;
+
+inline size_t kcw_lds_bytes(int C) {
+  const size_t ring = (size_t)kKcwSlots * addr::kc_slot_bytes(C);
+  const size_t red = (size_t)C * 128 * sizeof(float) + kSsCap * sizeof(double);
+  return ring > red ? ring : red;
+}
+// Waves (= super-blocks per stage) for K / 256 = nsb: the most, up to 16, that divide
+// nsb and whose three stages fit the LDS; 0 if none (or fewer than two).
+int kcw_waves(int nsb) {
+  for (int c = 16; c >= 2; --c)
+    if (nsb % c == 0 && kcw_lds_bytes(c) <= (size_t)kGemmLds) return c;
+  return 0;
+}
+
+struct KcwAct {
+  u32x4 a[8];
+};
+
+__global__ __launch_bounds__(1024) void gemm_kcw_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int C = blockDim.x >> 6;  // waves = super-blocks per stage
+  const int nch = a.nsb / C;      // stages
+  const int n = lane & 15, kg = lane >> 4;
+  const int tile = blockIdx.x;
+  const u32 slot_bytes = addr::kc_slot_bytes(C);
+  const int stride = addr::kc_stride(C);
+  const int kwi = (addr::kc_instrs(C) + C - 1) / C;  // loads per wave and stage (<= 5)
+  lds_u8* const slots = (lds_u8*)lds;
+
+  if (a.zero_ptr && tile == 0)
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0.0;
+
+  const int rows_n = a.seg_rows[0];
+  const int nvalid = min(16, rows_n - tile * 16);
+  const uint8_t* const tbase = a.w[0] + (size_t)tile * 16 * a.row_bytes;
+  u32 voff[addr::kWtInstr];
+#pragma unroll
+  for (int k = 0; k < addr::kWtInstr; ++k)
+    voff[k] = addr::kc_src(addr::kc_instr(wave, C, k, C), lane, C, (u32)a.row_bytes);
+  auto issue = [&](int c) {
+    const u32 ws = addr::kc_window(C, c);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(tbase + ws), 0, (int)(u32)((size_t)nvalid * a.row_bytes - ws), kBufDword3);
+    lds_u8* slot = slots + (c % kKcwSlots) * slot_bytes;
+#pragma unroll
+    for (int k = 0; k < addr::kWtInstr; ++k)
+      if (k < kwi) issue_wt(rs, slot + 1024u * (u32)addr::kc_instr(wave, C, k, C), voff[k]);
+  };
+  auto load_act = [&](KcwAct& b, int c) {
+    const int sb = c * C + wave;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b.a[j] = ((const u32x4*)a.xpack)[((size_t)sb * 8 + j) * 64 + lane];
+  };
+  auto wait_stage = [&]() {  // leaves one stage's loads in flight
+    if (kwi == 5)
+      wait_vmcnt<5>();
+    else if (kwi == 4)
+      wait_vmcnt<4>();
+    else if (kwi == 3)
+      wait_vmcnt<3>();
+    else if (kwi == 2)
+      wait_vmcnt<2>();
+    else
+      wait_vmcnt<1>();
+  };
+
+  // the epilogue element of this thread (threads < 128): output row brow, column col
+  const int e = threadIdx.x;
+  const int e_nn = (e >> 1) & 15, e_brow = 2 * (e >> 5) + (e & 1);
+  const bool e_live = e < 128 && e_brow < a.B && tile * 16 + e_nn < rows_n;
+  const int e_col = a.seg_col_off[0] + tile * 16 + e_nn;
+  // operands of the epilogue that do not depend on the GEMM, loaded first
+  const double ssp = (a.ss && (int)threadIdx.x < a.ss_slots * a.B) ? a.ss[threadIdx.x] : 0.0;
+  const float pre_x = (e_live && a.epi == kEpiResidual) ? a.y[(size_t)e_brow * a.ldy + e_col] : 0.f;
+  const float pre_g = (e_live && a.epi == kEpiResidual && a.gain) ? a.gain[e_col] : 1.f;
+
+  KcwAct b0, b1;
+  load_act(b0, 0);
+  issue(0);
+  if (nch > 1) issue(1);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto step = [&](int c, const KcwAct& cur, KcwAct& nxt) {
+    if (c + 1 < nch)
+      wait_stage();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (c + 1 < nch) load_act(nxt, c + 1);
+    if (c + 2 < nch) issue(c + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const u32 x0 = addr::kc_s16(C, c) + 210u * (u32)wave;  // the block's first byte in the window
+    const lds_u8* rs = slots + (c % kKcwSlots) * slot_bytes + addr::kc_lds_byte(n, x0 & ~3u, C);
+    Q6Regs w;
+    q6_load_at(rs, x0 & 3u, kg, w);
+    q6_step_w(w, cur.a, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, b0, b1);
+    if (c + 1 < nch) step(c + 1, b1, b0);
+  }
+  (void)stride;
+
+  // the waves' sums (hi + lo parts of each batch row) through LDS, then the epilogue
+  lds_barrier();  // every wave is done with the ring
+  float* red = (float*)lds;  // [waves][128]
+  red[(size_t)wave * 128 + lane * 2] = acc[0] + acc[1];
+  red[(size_t)wave * 128 + lane * 2 + 1] = acc[2] + acc[3];
+  double* s_ss = (double*)(red + (size_t)C * 128);
+  if (a.ss && (int)threadIdx.x < a.ss_slots * a.B) s_ss[threadIdx.x] = ssp;
+  __syncthreads();
+  if (e < 128) {  // waves 0 and 1, whole: the shuffles below see every lane
+    float v = 0.f;
+    for (int w2 = 0; w2 < C; ++w2) v += red[(size_t)w2 * 128 + e];
+    double ssv = 0.0;
+    if (e_live && a.ss)
+      for (int q = 0; q < a.ss_slots; ++q) ssv += s_ss[q * a.B + e_brow];
+    const float rsn = e_live ? (a.ss ? 1.0f / sqrtf((float)ssv * a.inv_k + a.eps) : 1.0f) : 0.f;
+    if (a.epi == kEpiStore) {
+      if (e_live) a.y[(size_t)e_brow * a.ldy + e_col] = rsn * v;
+    } else {
+      float xn = 0.f;
+      if (e_live) {
+        xn = pre_x + rsn * v;
+        a.y[(size_t)e_brow * a.ldy + e_col] = xn;
+        const float pv = xn * pre_g;
+        if (a.pack_out) actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, e_brow, e_col, pv);
+        if (a.pack_out2) actpack_put(a.pack_out2, a.pack_kind2, a.pack_nslices2, e_brow, e_col, pv);
+      }
+      // sum of squares over the tile's 16 columns of each batch row: lanes with the same
+      // (row pair, k2) differ in nn, bits 1..4 of the thread index
+      float sq = xn * xn;
+#pragma unroll
+      for (int o = 2; o <= 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
+      if (e_nn == 0 && e_brow < a.B && a.ss_out)
+        atomicAdd(a.ss_out + (size_t)(tile % a.ss_slots) * a.B + e_brow, (double)sq);
+    }
+  }
+}
+
+// Which GEMMs take it: Q6_K with a residual update or a plain store, one activation
+// tile, rows of a multiple of 16 bytes (K a multiple of 8 super-blocks), one matrix.
+bool use_kcw(int wtype, int K, int B, int nmat) {
+  const int nsb = K / kQK;
+  return wtype == 14 && B <= 8 && nmat == 1 && K % kQK == 0 && nsb % 8 == 0 && kcw_waves(nsb) >= 2;
+}
+
+hipError_t launch_gemm_kcw(int tiles, GemmArgs a, hipStream_t st) {
+  const int C = kcw_waves(a.nsb);
+  if (tiles <= 0) return hipSuccess;
+  if (C < 2 || a.nsb % C || a.B > 8 || a.nseg != 1 || a.row_bytes % 16 || (a.epi != kEpiResidual && a.epi != kEpiStore) ||
+      (a.ss && a.ss_slots * a.B > C * 64) || (a.ss && a.ss_slots * a.B > kSsCap))
+    return hipErrorInvalidValue;
+  static const bool lds_set = [] {
+    (void)hipFuncSetAttribute((const void*)gemm_kcw_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)lds_set;
+  void* kargs[] = {&a};
+  const hipError_t e = launch_fn((const void*)gemm_kcw_kernel, dim3(tiles), dim3(C * 64), kcw_lds_bytes(C), st, kargs);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------

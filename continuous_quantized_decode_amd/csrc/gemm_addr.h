@@ -138,6 +138,38 @@ GR_HD uint32_t wt_lds_byte(int r, uint32_t b, int nsb) {
   return 16u * ((uint32_t)r * (uint32_t)U + (uint32_t)c) + b % 16u;
 }
 
+// K-chunk staging (the Q6_K residual GEMM -- down -- on rows of a multiple of 16 bytes):
+// stage c holds super-blocks [C c, C c + C) of the tile's 16 rows.  Row r's window is
+// kc_units(C) aligned 16-byte units from kc_window(C, c) bytes into the row (the chunk
+// starts kc_s16 bytes in: 2-byte aligned, at most 14, so the window holds it whole).
+// Windows sit kc_stride(C) units apart in LDS, an odd count, so one byte column of the 16
+// rows falls on 16 different banks (4 stride r dwords; odd stride: distinct mod 64 for
+// r < 16); the padding unit repeats the window's last.  LDS unit L = 64 i + lane of load
+// instruction i is row L / stride, window unit min(L % stride, units - 1); units past the
+// stage repeat its last, instructions past it repeat the last.
+GR_HD int kc_units(int C) { return (14 + 210 * C + 15) / 16; }
+GR_HD int kc_stride(int C) { return kc_units(C) | 1; }
+GR_HD int kc_instrs(int C) { return (16 * kc_stride(C) + 63) / 64; }
+GR_HD uint32_t kc_slot_bytes(int C) { return 1024u * (uint32_t)kc_instrs(C); }
+GR_HD uint32_t kc_window(int C, int c) { return (210u * (uint32_t)C * (uint32_t)c) & ~15u; }
+GR_HD uint32_t kc_s16(int C, int c) { return (210u * (uint32_t)C * (uint32_t)c) & 15u; }
+GR_HD int kc_instr(int wave, int waves, int k, int C) {
+  const int i = wave + waves * k, n = kc_instrs(C);
+  return i < n ? i : n - 1;
+}
+// byte offset of the unit lane `lane` of instruction i loads, from row 0's window start
+GR_HD uint32_t kc_src(int i, int lane, int C, uint32_t row_bytes) {
+  const int S = kc_stride(C), U = kc_units(C);
+  int L = 64 * i + lane;
+  if (L > 16 * S - 1) L = 16 * S - 1;
+  const int r = L / S;
+  int col = L - r * S;
+  if (col > U - 1) col = U - 1;
+  return (uint32_t)r * row_bytes + 16u * (uint32_t)col;
+}
+GR_HD uint32_t kc_lds(int i, int lane) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
+GR_HD uint32_t kc_lds_byte(int r, uint32_t b, int C) { return 16u * (uint32_t)kc_stride(C) * (uint32_t)r + b; }
+
 GR_HD uint32_t q4_lds(int lane, int i) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
 GR_HD uint32_t q6_lds(int lane, int i) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
 

@@ -133,6 +133,9 @@ struct TlPlan {
 };
 TlPlan plan_gemm_tl(int wtype, int nt, int groups, int K, int B);
 bool use_tile_loop_whole(int wtype, int groups, int K, int B);  // gemm_tlw_kernel's sizes
+bool use_kcw(int wtype, int K, int B, int nmat);  // gemm_kcw_kernel's sizes (one matrix)
+int kcw_waves(int nsb);
+hipError_t launch_gemm_kcw(int tiles, GemmArgs a, hipStream_t st);
 inline int tl_btn(int B) { return B <= 8 ? 1 : 2; }  // activation tiles of the tile loop
 hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st);
 hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);

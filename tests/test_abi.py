@@ -83,8 +83,9 @@ def test_gemm_launch_shape_names_the_kernel():
     qkv = gr.gr_gemm_launch_shape(q4, 6144, 4096, 8, gr.GEMM_EPI_STORE)  # Q4_K store from 256 tiles: whole tiles too
     assert qkv["whole_tile"] and qkv["nt"] == 1 and qkv["kernel"] == "gemm_tlw_kernel<false>"
     # residual updates and small matrices keep the split-K kernel
-    down = gr.gr_gemm_launch_shape(q6, 4096, 14336, 8, gr.GEMM_EPI_RESIDUAL)
-    assert not down["tile_loop"] and down["kernel"].startswith("gemm_kernel<14, 1, 1,")
+    down = gr.gr_gemm_launch_shape(q6, 4096, 14336, 8, gr.GEMM_EPI_RESIDUAL)  # K-chunk staging: 4 stages of 14
+    assert down["k_chunks"] and down["kernel"] == "gemm_kcw_kernel" and down["block_threads"] == 14 * 64
+    assert gr.gr_gemm_launch_shape(q6, 1024, 3072, 8, gr.GEMM_EPI_RESIDUAL)["kernel"].startswith("gemm_kernel<14, 1, 1,")
     assert not gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_RESIDUAL)["tile_loop"]
     assert gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_STORE)["tile_loop"]
     # the tile loop's epilogue needs two waves (K of three super-blocks or more)

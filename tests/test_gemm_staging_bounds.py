@@ -226,3 +226,93 @@ def test_whole_tile_staging_in_bounds_and_conflict_free():
         out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
         print(out.stdout)
         assert out.returncode == 0, out.stdout
+
+
+KCHUNK_PROGRAM = r"""
+#include <cstdio>
+#include <vector>
+#include "gemm_addr.h"
+using namespace gr::addr;
+
+static int fails = 0;
+#define CHECK(c, ...) do { if (!(c)) { if (fails++ < 20) { std::printf(__VA_ARGS__); std::printf("\n"); } } } while (0)
+
+// K-chunk staging of Q6_K tiles (rows of a multiple of 16 bytes): every wave's loads of
+// every chunk, every lane, and the bytes the compute reads (dword pairs around each
+// 2-byte aligned field of each block).
+int main() {
+  const int nsbs[] = {8, 16, 24, 48, 56};
+  const int rows[] = {1, 15, 16, 17, 33};
+  for (int nsb : nsbs)
+    for (int C = 1; C <= 16; ++C) {
+      if (nsb % C) continue;
+      const int waves = C, nch = nsb / C, kwi = (kc_instrs(C) + waves - 1) / waves;
+      const uint32_t row_bytes = 210u * nsb, slot = kc_slot_bytes(C);
+      CHECK(row_bytes % 16 == 0, "rows of 16 bytes");
+      CHECK(kwi <= 5, "C %d: %d loads per wave", C, kwi);
+      CHECK(kc_stride(C) % 2 == 1 && kc_stride(C) >= kc_units(C), "stride");
+      for (int N : rows)
+        for (int row0 = 0; row0 < N; row0 += 16) {
+          const int nvalid = N - row0 < 16 ? N - row0 : 16;
+          const uint64_t total = (uint64_t)N * row_bytes, tile = (uint64_t)row0 * row_bytes;
+          for (int c = 0; c < nch; ++c) {
+            const uint64_t base = tile + kc_window(C, c);
+            const uint64_t desc = (uint64_t)nvalid * row_bytes - kc_window(C, c);  // descriptor size from base
+            std::vector<int64_t> held(slot, -1);
+            for (int w = 0; w < waves; ++w)
+              for (int k = 0; k < kwi; ++k) {
+                const int i = kc_instr(w, waves, k, C);
+                for (int lane = 0; lane < 64; ++lane) {
+                  const uint32_t off = kc_src(i, lane, C, row_bytes), lds = kc_lds(i, lane);
+                  CHECK(off % 16 == 0, "aligned unit");
+                  CHECK(lds + 16 <= slot, "C %d: LDS write past the slot", C);
+                  CHECK(off >= desc || base + off + 16 <= total, "nsb %d C %d N %d: in-descriptor unit past the matrix",
+                        nsb, C, N);
+                  for (int b = 0; b < 16; ++b) {
+                    const int64_t v = off + b < desc ? (int64_t)(base + off + b) : -2;
+                    CHECK(held[lds + b] == -1 || held[lds + b] == v, "C %d: LDS byte loaded twice differently", C);
+                    held[lds + b] = v;
+                  }
+                }
+              }
+            const uint32_t s16 = kc_s16(C, c);
+            for (int r = 0; r < nvalid; ++r)
+              for (int j = 0; j < C; ++j) {
+                const uint32_t x0 = s16 + 210u * j;  // the block's first byte in the window
+                for (uint32_t b = 0; b < 210; ++b)
+                  CHECK(held[kc_lds_byte(r, x0 + b, C)] == (int64_t)(tile + (uint64_t)r * row_bytes + 210u * (C * c + j) + b),
+                        "nsb %d C %d N %d row0 %d chunk %d row %d block %d byte %u", nsb, C, N, row0, c, r, j, b);
+                // the dword pairs the compute loads around each field stay inside the slot
+                for (uint32_t f = 0; f < 212; f += 4)
+                  CHECK(kc_lds_byte(r, ((x0 + f) & ~3u) + 8, C) <= slot, "C %d: read past the slot", C);
+              }
+          }
+        }
+      // one byte column of the 16 rows: 16 distinct banks
+      for (uint32_t b = 0; b < 16u * kc_units(C); b += 4) {
+        std::vector<int> used(64, 0);
+        for (int r = 0; r < 16; ++r) used[(kc_lds_byte(r, b, C) / 4) % 64]++;
+        for (int q = 0; q < 64; ++q) CHECK(used[q] <= 1, "C %d column %u: bank %d used %d times", C, b, q, used[q]);
+      }
+    }
+  std::printf("%s (%d failures)\n", fails ? "FAIL" : "ok", fails);
+  return fails ? 1 : 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_k_chunk_staging_in_bounds_and_conflict_free():
+    """The K-chunk staging map (the Q6_K down GEMM): every wave's loads of every chunk stay
+    inside the LDS slot and, inside the buffer descriptor, inside the matrix; every byte of
+    every block of every valid row lands where the compute reads it, the dword pairs read
+    around each field stay in the slot, and one byte column of 16 rows sits on 16 banks."""
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "check_kc.cpp")
+        exe = os.path.join(d, "check_kc")
+        with open(src, "w") as f:
+            f.write(KCHUNK_PROGRAM)
+        subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.dirname(HDR), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        print(out.stdout)
+        assert out.returncode == 0, out.stdout

@@ -85,6 +85,11 @@ LAYER_CASES = [
     dict(ctx=[5, 64, 200, 17, 0], batch=5, hidden=768, ffn=8192, kv_dtype=synth.KV_Q8_0, qk_norm=True,
          gu=(True, 1, True)),
     dict(ctx=[31, 1], batch=2, hidden=1024, ffn=9216, gu=(True, 1, True)),
+    # Q6_K down with its residual update at one batch tile: K-chunk staging (dn), K of 56
+    # super-blocks (four stages of 14) and 48 (three of 16)
+    dict(ctx=[40, 7, 300, 0, 16, 90, 1, 33], batch=8, ffn=14336, w_down=synth.W_Q6_K, kv_dtype=synth.KV_F16,
+         dn=True),
+    dict(ctx=[5, 64, 200], batch=3, ffn=12288, w_down=synth.W_Q6_K, qk_norm=True, dn=True),
 ]
 
 
@@ -110,6 +115,7 @@ def test_tiny_layer_matches_oracle(torch, gr, orc, case):
     spec = dict(LAYER_CASES[case])
     ctx = spec.pop("ctx")
     gu = spec.pop("gu", None)
+    dn = spec.pop("dn", None)
     wl = tiny(**spec)
     say("layer case", case, spec, ctx)
     if gu is not None:
@@ -119,6 +125,10 @@ def test_tiny_layer_matches_oracle(torch, gr, orc, case):
         assert (sh["tile_loop"], sh["btn"]) == gu[:2]
         if len(gu) > 2:
             assert sh["whole_tile"] == gu[2]
+    if dn is not None:  # the down launch this case exists to cover
+        sh = gr.gr_gemm_launch_shape(wl.w_down, wl.hidden, wl.ffn, len(ctx), gr.GEMM_EPI_RESIDUAL)
+        say("  down launch", sh)
+        assert sh["k_chunks"] == dn
     got, want, gpools, opools, kv = run_layer_case(torch, gr, orc, wl, ctx)
     assert np.isfinite(got).all()
     err, rerr = rel_l2(got, want), row_rel_l2(got, want)
