@@ -129,8 +129,10 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
     // kernel (one tile per group)
     int type_cols = 0;
     for (int q = i; q < nmat && types[q] == types[i]; ++q) type_cols += rows[q];
-    const bool tl = ep.kind == kEpiStore && !use_mm(types[i], B) &&
-                    (use_tile_loop(types[i], all_tiles, K, B) || use_tile_loop_whole(types[i], all_tiles, K, B));
+    // (the whole-tile kernel also takes residual updates: Wo)
+    const bool tl = !use_mm(types[i], B) &&
+                    ((ep.kind == kEpiStore && use_tile_loop(types[i], all_tiles, K, B)) ||
+                     ((ep.kind == kEpiStore || ep.kind == kEpiResidual) && use_tile_loop_whole(types[i], all_tiles, K, B)));
     const bool mm = !tl && (ep.kind == kEpiStore ? use_mm_store(types[i], B, type_cols) : use_mm(types[i], B));
     int n_of_type = 0;
     for (int q = i; q < nmat && types[q] == types[i]; ++q) ++n_of_type;
@@ -647,6 +649,16 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
     *nt = pair ? 2 : 1;
     *btn = tl_btn(B);
     *maxt = tp.whole ? 1024 : 512;
+    *grid_threads = tp.grid * tp.waves * 64;
+    *block_threads = tp.waves * 64;
+    return GR_OK;
+  }
+  if (epi == 1 && !use_mm(wtype, B) && use_tile_loop_whole(wtype, tiles, K, B)) {  // whole tiles (Wo)
+    const TlPlan tp = plan_gemm_tl(wtype, 1, tiles, K, B);
+    *tile_loop = 3;
+    *nt = 1;
+    *btn = 1;
+    *maxt = 1024;
     *grid_threads = tp.grid * tp.waves * 64;
     *block_threads = tp.waves * 64;
     return GR_OK;

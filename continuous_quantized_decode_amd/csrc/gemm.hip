@@ -1258,6 +1258,18 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
   } else {
     wait_one_younger();
   }
+  // residual update: the first group's residual and gain, loaded while the weights stream
+  float pre_x = 0.f, pre_g = 1.f;
+  if (!PAIR && a.epi == kEpiResidual && e < 128 && ng > 0) {
+    const int sg = seg_of(g0), lt = g0 - seg_off(sg);
+    const int r = lt * 16 + ((e >> 1) & 15);
+    const int rows_s = sg == 0 ? a.seg_rows[0] : sg == 1 ? a.seg_rows[1] : a.seg_rows[2];
+    const int col_s = sg == 0 ? a.seg_col_off[0] : sg == 1 ? a.seg_col_off[1] : a.seg_col_off[2];
+    if (e_brow < a.B && r < rows_s) {
+      pre_x = a.y[(size_t)e_brow * a.ldy + col_s + r];
+      pre_g = a.gain ? a.gain[col_s + r] : 1.f;
+    }
+  }
   float rs = 1.0f;  // 1 / rms of the input row (first, so that the partial sums die early)
   if (a.ss && e < 128 && e_brow < a.B) {
     double ssv = 0.0;
@@ -1320,7 +1332,29 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
         const int rows_s = sg == 0 ? a.seg_rows[0] : sg == 1 ? a.seg_rows[1] : a.seg_rows[2];
         const int col_s = sg == 0 ? a.seg_col_off[0] : sg == 1 ? a.seg_col_off[1] : a.seg_col_off[2];
         const int r = lt * 16 + (elp & 15);
-        if (brow < a.B && r < rows_s) a.y[(size_t)brow * a.ldy + col_s + r] = rs * v;
+        const bool live = brow < a.B && r < rows_s;
+        const size_t yi = (size_t)brow * a.ldy + col_s + r;
+        if (a.epi == kEpiStore) {
+          if (live) a.y[yi] = rs * v;
+        } else {  // residual update: x += rs v, the next input's packs and sum of squares
+          float xn = 0.f;
+          if (live) {
+            const float xv = pr == 0 ? pre_x : a.y[yi];
+            const float gv = pr == 0 ? pre_g : (a.gain ? a.gain[col_s + r] : 1.f);
+            xn = xv + rs * v;
+            a.y[yi] = xn;
+            const float pv = xn * gv;
+            if (a.pack_out) actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, brow, col_s + r, pv);
+            if (a.pack_out2) actpack_put(a.pack_out2, a.pack_kind2, a.pack_nslices2, brow, col_s + r, pv);
+          }
+          // over the tile's 16 columns of each batch row: lanes with the same (row pair,
+          // k2) differ in nn, bits 1..4 of the thread index (waves 0 and 1 whole here)
+          float sq = xn * xn;
+#pragma unroll
+          for (int o = 2; o <= 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
+          if ((elp & 15) == 0 && brow < a.B && a.ss_out)
+            atomicAdd(a.ss_out + (size_t)(gi % a.ss_slots) * a.B + brow, (double)sq);
+        }
       }
     }
   };
@@ -2075,7 +2109,8 @@ hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipSt
       (a.ss && a.ss_slots != 16) || (a.epi == kEpiSwiGLU ? 1 : nt) * 128 * btn > pl.waves * 64)
     return hipErrorInvalidValue;
   const bool aligned = wtype == 12 || a.row_bytes % 16 == 0;
-  if (pl.whole && (wtype != 12 || btn != 1 || a.epi != (nt == 2 ? kEpiSwiGLU : kEpiStore) || a.nsb > 16 ||
+  if (!pl.whole && a.epi == kEpiResidual) return hipErrorInvalidValue;  // only the whole-tile kernel updates
+  if (pl.whole && (wtype != 12 || btn != 1 || (nt == 2) != (a.epi == kEpiSwiGLU) || a.nsb > 16 ||
                    a.nsb < 2 || pl.waves != tlw_waves(a.nsb) || addr::kWtInstr * pl.waves < addr::wt_instrs(a.nsb) ||
                    pl.lds != tlw_lds_bytes(a.nsb)))
     return hipErrorInvalidValue;

@@ -86,7 +86,9 @@ def test_gemm_launch_shape_names_the_kernel():
     down = gr.gr_gemm_launch_shape(q6, 4096, 14336, 8, gr.GEMM_EPI_RESIDUAL)  # K-chunk staging: 4 stages of 14
     assert down["k_chunks"] and down["kernel"] == "gemm_kcw_kernel" and down["block_threads"] == 14 * 64
     assert gr.gr_gemm_launch_shape(q6, 1024, 3072, 8, gr.GEMM_EPI_RESIDUAL)["kernel"].startswith("gemm_kernel<14, 1, 1,")
-    assert not gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_RESIDUAL)["tile_loop"]
+    # a Q4_K residual update from 256 tiles at one batch tile (Wo): whole tiles; at 9 rows: split-K
+    assert gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_RESIDUAL)["kernel"] == "gemm_tlw_kernel<false>"
+    assert not gr.gr_gemm_launch_shape(q4, 8200, 4096, 9, gr.GEMM_EPI_RESIDUAL)["tile_loop"]
     assert gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_STORE)["tile_loop"]
     # the tile loop's epilogue needs two waves (K of three super-blocks or more)
     assert not gr.gr_gemm_launch_shape(q4, 16384, 512, 8, gr.GEMM_EPI_STORE)["tile_loop"]

@@ -90,6 +90,10 @@ LAYER_CASES = [
     dict(ctx=[40, 7, 300, 0, 16, 90, 1, 33], batch=8, ffn=14336, w_down=synth.W_Q6_K, kv_dtype=synth.KV_F16,
          dn=True),
     dict(ctx=[5, 64, 200], batch=3, ffn=12288, w_down=synth.W_Q6_K, qk_norm=True, dn=True),
+    # Wo from 2048 to 4096 (256 tiles) at one batch tile: the whole-tile kernel's residual
+    # update (wo), 16 query heads on 2 KV heads of 128
+    dict(ctx=[60, 3, 250, 17, 0, 99], batch=6, hidden=4096, n_q_heads=16, n_kv_heads=2, head_dim=128, ffn=1024,
+         kv_dtype=synth.KV_F16, wo=True),
 ]
 
 
@@ -116,6 +120,7 @@ def test_tiny_layer_matches_oracle(torch, gr, orc, case):
     ctx = spec.pop("ctx")
     gu = spec.pop("gu", None)
     dn = spec.pop("dn", None)
+    wo = spec.pop("wo", None)
     wl = tiny(**spec)
     say("layer case", case, spec, ctx)
     if gu is not None:
@@ -125,6 +130,11 @@ def test_tiny_layer_matches_oracle(torch, gr, orc, case):
         assert (sh["tile_loop"], sh["btn"]) == gu[:2]
         if len(gu) > 2:
             assert sh["whole_tile"] == gu[2]
+    if wo is not None:  # the Wo launch this case exists to cover
+        sh = gr.gr_gemm_launch_shape(synth.layer_weights(wl, 0).to, wl.hidden, wl.n_q_heads * wl.head_dim, len(ctx),
+                                     gr.GEMM_EPI_RESIDUAL)
+        say("  Wo launch", sh)
+        assert sh["whole_tile"] == wo
     if dn is not None:  # the down launch this case exists to cover
         sh = gr.gr_gemm_launch_shape(wl.w_down, wl.hidden, wl.ffn, len(ctx), gr.GEMM_EPI_RESIDUAL)
         say("  down launch", sh)
