@@ -259,13 +259,14 @@ def gr_gemm_launch_shape(wtype: int, rows: int, k: int, b: int, epi: int = GEMM_
     tl, nt, btn, maxt, grid, block = (i.value for i in v)
     if tl == 2:
         name = f"gemm_mm_kernel<{wtype},"
-    elif tl == 3:
-        name = f"gemm_tlw_kernel<{'true' if nt == 2 else 'false'}>"
+    elif tl in (3, 5):  # whole-tile tile loop: 2 gate/up pairs, 0 plain store, 1 residual update
+        name = f"gemm_tlw_kernel<{2 if nt == 2 else 1 if tl == 5 else 0}>"
     elif tl == 4:
         name = "gemm_kcw_kernel"
     else:
         name = f"gemm_tl_kernel<{wtype}, {nt}," if tl else f"gemm_kernel<{wtype}, {nt}, {btn}, {maxt},"
-    return {"tile_loop": tl in (1, 3), "whole_tile": tl == 3, "k_chunks": tl == 4, "many_rows": tl == 2, "nt": nt, "btn": btn,
+    return {"tile_loop": tl in (1, 3, 5), "whole_tile": tl in (3, 5), "k_chunks": tl == 4, "many_rows": tl == 2,
+            "nt": nt, "btn": btn,
             "maxt": maxt, "grid_threads": grid, "block_threads": block, "kernel": name}
 
 

@@ -655,7 +655,7 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
   }
   if (epi == 1 && !use_mm(wtype, B) && use_tile_loop_whole(wtype, tiles, K, B)) {  // whole tiles (Wo)
     const TlPlan tp = plan_gemm_tl(wtype, 1, tiles, K, B);
-    *tile_loop = 3;
+    *tile_loop = 5;
     *nt = 1;
     *btn = 1;
     *maxt = 1024;

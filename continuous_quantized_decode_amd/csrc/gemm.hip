@@ -1165,6 +1165,7 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
 // One barrier per tile.  The epilogue's stores go out before the next loads, so waiting
 // for those loads does not wait for stores issued after them.
 constexpr int kTlwSlots = 3;
+constexpr int kTlwStore = 0, kTlwResidual = 1, kTlwPair = 2;
 
 inline int tlw_waves(int nsb) { return nsb; }
 inline size_t tlw_lds_bytes(int nsb) {
@@ -1176,8 +1177,11 @@ GR_DEV void issue_wt(__amdgpu_buffer_rsrc_t rs, lds_u8* dst, u32 voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)dst, 16, voff, 0, 0, 0);
 }
 
-template <bool PAIR>
+// MODE: kTlwStore (plain store), kTlwResidual (x += ..., the next input's packs and
+// sum of squares), kTlwPair (gate/up pairs with SwiGLU)
+template <int MODE>
 __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
+  constexpr bool PAIR = MODE == kTlwPair;
   constexpr int SPG = PAIR ? 2 : 1;  // stages (tiles) per group
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int KWI = addr::kWtInstr;
@@ -1260,7 +1264,7 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
   }
   // residual update: the first group's residual and gain, loaded while the weights stream
   float pre_x = 0.f, pre_g = 1.f;
-  if (!PAIR && a.epi == kEpiResidual && e < 128 && ng > 0) {
+  if (MODE == kTlwResidual && e < 128 && ng > 0) {
     const int sg = seg_of(g0), lt = g0 - seg_off(sg);
     const int r = lt * 16 + ((e >> 1) & 15);
     const int rows_s = sg == 0 ? a.seg_rows[0] : sg == 1 ? a.seg_rows[1] : a.seg_rows[2];
@@ -1334,7 +1338,7 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
         const int r = lt * 16 + (elp & 15);
         const bool live = brow < a.B && r < rows_s;
         const size_t yi = (size_t)brow * a.ldy + col_s + r;
-        if (a.epi == kEpiStore) {
+        if (MODE == kTlwStore) {
           if (live) a.y[yi] = rs * v;
         } else {  // residual update: x += rs v, the next input's packs and sum of squares
           float xn = 0.f;
@@ -2114,7 +2118,9 @@ hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipSt
                    a.nsb < 2 || pl.waves != tlw_waves(a.nsb) || addr::kWtInstr * pl.waves < addr::wt_instrs(a.nsb) ||
                    pl.lds != tlw_lds_bytes(a.nsb)))
     return hipErrorInvalidValue;
-  const void* fn = pl.whole      ? (nt == 2 ? (const void*)gemm_tlw_kernel<true> : (const void*)gemm_tlw_kernel<false>)
+  const void* fn = pl.whole      ? (nt == 2                  ? (const void*)gemm_tlw_kernel<kTlwPair>
+                                    : a.epi == kEpiResidual ? (const void*)gemm_tlw_kernel<kTlwResidual>
+                                                            : (const void*)gemm_tlw_kernel<kTlwStore>)
                    : wtype == 12 ? tl_fn<12, true>(nt, btn)
                    : aligned     ? tl_fn<14, true>(nt, btn)
                                  : tl_fn<14, false>(nt, btn);
@@ -2124,7 +2130,8 @@ hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipSt
         const void* all[] = {tl_fn<12, true>(t, b), tl_fn<14, true>(t, b), tl_fn<14, false>(t, b)};
         for (const void* f : all) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
       }
-    for (const void* f : {(const void*)gemm_tlw_kernel<true>, (const void*)gemm_tlw_kernel<false>})
+    for (const void* f : {(const void*)gemm_tlw_kernel<kTlwStore>, (const void*)gemm_tlw_kernel<kTlwResidual>,
+                          (const void*)gemm_tlw_kernel<kTlwPair>})
       (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     (void)hipGetLastError();
     return true;

@@ -125,9 +125,10 @@ gr_status gr_stream_read(const void* p, size_t bytes, uint32_t* out, void* strea
  * gemm_tl_kernel<type, nt, aligned, ring, btn> with maxt = 512; 2: the many-row
  * kernel gemm_mm_kernel<type, aligned>, 512 threads, nt = 2 tiles per wave and btn = 4
  * (Q4_K) or 2 (Q6_K) activation tiles per workgroup; 3: the whole-tile tile loop
- * gemm_tlw_kernel<pair>, Q4_K gate/up pairs or plain stores at one activation tile, one
- * wave per 256 of K, maxt = 1024; 4: the K-chunk kernel gemm_kcw_kernel, a Q6_K
- * residual update at one activation tile, K a multiple of 2048), its template
+ * gemm_tlw_kernel<mode>, Q4_K gate/up pairs (mode 2) or plain stores (mode 0) at one
+ * activation tile, one wave per 256 of K, maxt = 1024; 5: the same for a Q4_K residual
+ * update (mode 1); 4: the K-chunk kernel gemm_kcw_kernel, a Q6_K residual update at one
+ * activation tile, K a multiple of 2048), its template
  * parameters (16-row tiles per workgroup or group nt, 8-row batch tiles btn, launch
  * bound maxt) and the grid and workgroup sizes in threads, as launched by every entry
  * point above for these sizes.  GR_ERR_NULL for a null output pointer, GR_ERR_DTYPE for

@@ -79,15 +79,15 @@ def test_gemm_launch_shape_names_the_kernel():
     assert head["tile_loop"] and head["nt"] == 1 and head["kernel"] == "gemm_tl_kernel<14, 1,"
     gu = gr.gr_gemm_launch_shape(q4, 14336, 4096, 8, gr.GEMM_EPI_SWIGLU)  # whole tiles, a wave per 256 of K
     assert gu["tile_loop"] and gu["whole_tile"] and gu["nt"] == 2 and gu["block_threads"] == 16 * 64
-    assert gu["kernel"] == "gemm_tlw_kernel<true>" and gu["grid_threads"] == 256 * 16 * 64
+    assert gu["kernel"] == "gemm_tlw_kernel<2>" and gu["grid_threads"] == 256 * 16 * 64
     qkv = gr.gr_gemm_launch_shape(q4, 6144, 4096, 8, gr.GEMM_EPI_STORE)  # Q4_K store from 256 tiles: whole tiles too
-    assert qkv["whole_tile"] and qkv["nt"] == 1 and qkv["kernel"] == "gemm_tlw_kernel<false>"
+    assert qkv["whole_tile"] and qkv["nt"] == 1 and qkv["kernel"] == "gemm_tlw_kernel<0>"
     # residual updates and small matrices keep the split-K kernel
     down = gr.gr_gemm_launch_shape(q6, 4096, 14336, 8, gr.GEMM_EPI_RESIDUAL)  # K-chunk staging: 4 stages of 14
     assert down["k_chunks"] and down["kernel"] == "gemm_kcw_kernel" and down["block_threads"] == 14 * 64
     assert gr.gr_gemm_launch_shape(q6, 1024, 3072, 8, gr.GEMM_EPI_RESIDUAL)["kernel"].startswith("gemm_kernel<14, 1, 1,")
     # a Q4_K residual update from 256 tiles at one batch tile (Wo): whole tiles; at 9 rows: split-K
-    assert gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_RESIDUAL)["kernel"] == "gemm_tlw_kernel<false>"
+    assert gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_RESIDUAL)["kernel"] == "gemm_tlw_kernel<1>"
     assert not gr.gr_gemm_launch_shape(q4, 8200, 4096, 9, gr.GEMM_EPI_RESIDUAL)["tile_loop"]
     assert gr.gr_gemm_launch_shape(q4, 8200, 4096, 8, gr.GEMM_EPI_STORE)["tile_loop"]
     # the tile loop's epilogue needs two waves (K of three super-blocks or more)
