@@ -170,7 +170,7 @@ GR_DEV void dec_page(PageRegs<KVDT, D>& cur, int valid, const u32x4 (&qf)[D / 32
 // take PW pages of each group with all of their loads in flight at once (two waves per
 // SIMD), the next group's block-table entries loaded meanwhile.
 template <int KVDT, int D, bool FUSED>
-__global__ __launch_bounds__(kAttnDecWaves * 64, 2) void attn_decode_kernel(AttnParams p) {
+__global__ __launch_bounds__(kAttnDecWaves * 64, KVDT == KV_F32_T ? 2 : 3) void attn_decode_kernel(AttnParams p) {
   constexpr int W = kAttnDecWaves, PW = attn_dec_pages(KVDT), PG = W * PW;
   static_assert(PG <= 64, "one block-table entry per lane");
   constexpr int NS = D / 32;
@@ -471,8 +471,7 @@ int attn_dec_slots(int kv_dtype) {
     (void)hipGetLastError();
     return 256;
   }();
-  (void)kv_dtype;
-  return cus * 2;
+  return cus * (kv_dtype == KV_Q8_T ? 3 : 2);
 }
 
 AttnDecPlan plan_attn_dec(int kv_dtype, int max_tokens) {

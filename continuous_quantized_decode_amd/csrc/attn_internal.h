@@ -85,17 +85,18 @@ constexpr int kAttnDecMaxWg = 512;  // workgroups per (row, KV head) one merge t
 constexpr int kAttnDecMaxGroups = 8;  // groups of pages per workgroup
 // pages per wave (a group's pages sit in registers at once; measured: f16 two pages
 // 21.2 us per Llama-3-8B layer against 22.8 us for four, whose refills wait a whole
-// group; eight q8_0 pages make the software-pipelined page loop spill)
+// group; q8_0 three pages, within the 168 VGPRs of three waves per SIMD, took the
+// Qwen3-8B step from 7.46 ms (six pages, two waves per SIMD) to 6.93 ms)
 __host__ __device__ constexpr int attn_dec_pages(int kv_dtype) {
-  return kv_dtype == KV_F32_T ? 2 : kv_dtype == KV_F16_T ? 2 : 6;
+  return kv_dtype == KV_F32_T ? 2 : kv_dtype == KV_F16_T ? 2 : 3;
 }
 struct AttnDecPlan {
   int wg_pages;  // pages per workgroup
   int wg_max;    // the most workgroups of one (row, KV head); 0: max_tokens too long
 };
 AttnDecPlan plan_attn_dec(int kv_dtype, int max_tokens);
-// resident decode-attention workgroups of the device for a KV format: two per CU (two
-// waves per SIMD; three per CU for f16 measured no faster)
+// resident decode-attention workgroups of the device for a KV format: three per CU for
+// q8_0 (three waves per SIMD), two otherwise (three per CU for f16 measured no faster)
 int attn_dec_slots(int kv_dtype);
 size_t attn_dec_part_floats(int B, int n_q_heads, int head_dim, int wg_max);
 // fused: the decode layer's variant (QK-norm, RoPE and the KV append of the new token

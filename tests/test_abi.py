@@ -174,13 +174,13 @@ def test_mixed_stack_head_rows_host_checks():
 
 def test_attn_launch_shape():
     """The decode attention's plan (host-only call): four waves per workgroup, each with
-    all of its pages in flight (f32 2, f16 2, q8_0 6 pages); the long-context workload's
+    all of its pages in flight (f32 2, f16 2, q8_0 3 pages); the long-context workload's
     rows take more than 64 workgroups, whose states the last one merges; a context past
     512 workgroups is refused before anything runs, by the decode layer too."""
     import continuous_quantized_decode_amd as gr
-    sh = gr.gr_attn_launch_shape(2, 64, 8, 32768 + 1)  # q8_0: 24 pages per workgroup
-    assert sh["waves_per_wg"] == 4 and sh["pages_per_wave"] == 6
-    assert sh["wg_per_row"] == -(-2049 // 24) > 64
+    sh = gr.gr_attn_launch_shape(2, 64, 8, 32768 + 1)  # q8_0: 12 pages per workgroup
+    assert sh["waves_per_wg"] == 4 and sh["pages_per_wave"] == 3
+    assert sh["wg_per_row"] == -(-2049 // 12) > 64
     assert sh["grid_threads"] == 64 * 8 * sh["wg_per_row"] * 256
     llama = gr.gr_attn_launch_shape(1, 8, 8, 3574)  # f16: 8 pages per workgroup
     assert llama["pages_per_wave"] == 2 and llama["wg_per_row"] == 28
