@@ -16,7 +16,7 @@
  *     logical pages (Known limitations), 16-token pages.
  *   - LeatEngine, Run: the q8_0 cache as llama.cpp keeps it (32-element blocks with
  *     an fp16 scale).
- *   - Q5_K and Q8_0 weight rows (the survey's next decoders; public GGUF layouts).
+ *   - Q5_K and Q8_0 weight rows (further GGUF weight formats; public layouts).
  *   - Leone, "What ships": greedy and stochastic sampling (temperature, top-k, top-p)
  *     after the output head, with fixed-point weights so every decision is an
  *     integer one (the readings sit with orc_sample below).
