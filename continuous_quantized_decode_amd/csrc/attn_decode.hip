@@ -488,7 +488,7 @@ size_t attn_dec_part_floats(int B, int n_q_heads, int head_dim, int wg_max) {
 }
 
 __global__ __launch_bounds__(1024) void attn_sched_kernel(AttnSched sc) {
-  __shared__ uint32_t scan[1024 / 64 + 1];
+  __shared__ uint32_t scan[kSchedScratchWords];
   build_attn_sched(sc, scan);
 }
 

@@ -215,20 +215,26 @@ struct RowSel {
 // by its first kernel (one block) and read by every layer's attention.  Pages per
 // workgroup P: a multiple of group_pages, at most max_groups groups, chosen so that the
 // step's workgroups (each row's ceil(pages / P) ranges times the KV heads) about fill
-// `slots` resident workgroups.  The list: [0] its entries, [1] P, then per row b (in
-// order) and range j < ceil(ceil((ctx[b] + self) / 16) / P) the entry
-// {(b << 16) | j, ctx[b]}; and the attention's arrival counters cleared.
+// `slots` resident workgroups.  Row b's ranges j < ceil(ceil((ctx[b] + self) / 16) / P)
+// are listed by the number of page groups they hold, most first (rows, then j, in order
+// within a count), so that when the list needs more than one round of resident
+// workgroups the ones that start late are the short last ranges of rows.  The order is
+// only a schedule: a range's result and the merge order depend on (b, j) alone.  The
+// list: [0] its entries, [1] P, then the entries {(b << 16) | j, ctx[b]}; and the
+// attention's arrival counters cleared.
+constexpr int kSchedMaxGroups = 8;  // groups of pages per range at most
 struct AttnSched {
   const int32_t* ctx = nullptr;
   int B = 0, self = 1;
-  int n_kv_heads = 1, slots = 512, group_pages = 16, max_groups = 8;
+  int n_kv_heads = 1, slots = 512, group_pages = 16, max_groups = kSchedMaxGroups;
   uint32_t* list = nullptr;  // entry i at list[2 + 2 i], list[3 + 2 i]
   uint32_t* cnt = nullptr;   // arrival counters to clear
   int n_cnt = 0;
 };
 // Words of a list for B rows of up to wg_max ranges each.
 inline size_t attn_sched_words(int B, int wg_max) { return 2 + 2 * (size_t)B * wg_max; }
-// The list and the counters by one workgroup of blockDim.x threads (a multiple of 64).
+// LDS words the builder needs for workgroups of up to 1024 threads.
+constexpr int kSchedScratchWords = (2 + 1024 / 64) * (kSchedMaxGroups + 1);
 GR_DEV uint32_t block_sum_u32(uint32_t v, uint32_t* lds_scratch) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -240,52 +246,106 @@ GR_DEV uint32_t block_sum_u32(uint32_t v, uint32_t* lds_scratch) {
   __syncthreads();
   return t;
 }
-GR_DEV void build_attn_sched(const AttnSched& s, uint32_t* lds_scratch /* blockDim.x / 64 + 1 words */) {
-  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+// The list and the counters by one workgroup of blockDim.x <= 1024 threads (a multiple
+// of 64); lds_scratch: kSchedScratchWords words.
+GR_DEV void build_attn_sched(const AttnSched& s, uint32_t* lds_scratch) {
+  constexpr int NB = kSchedMaxGroups + 1;  // bucket k (1 .. G) holds the ranges of k groups
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nthr / 64;
+  // the thread's first row's context, loaded once (rows past the first nthr are read
+  // again in each pass)
+  const int ctx_own = tid < s.B ? s.ctx[tid] : 0;
+  auto ctx_of = [&](int b) { return b == tid ? ctx_own : s.ctx[b]; };
   for (int i = tid; i < s.n_cnt; i += nthr) s.cnt[i] = 0u;
   // pages per workgroup from the step's total
   uint32_t mine = 0;
-  for (int b = tid; b < s.B; b += nthr) mine += (uint32_t)((s.ctx[b] + s.self + 15) / 16);
+  for (int b = tid; b < s.B; b += nthr) mine += (uint32_t)((ctx_of(b) + s.self + 15) / 16);
   const uint64_t total = (uint64_t)block_sum_u32(mine, lds_scratch) * (uint64_t)s.n_kv_heads;
   const uint64_t gp = (uint64_t)s.group_pages;
+  const int maxg = s.max_groups < 1 ? 1 : s.max_groups > kSchedMaxGroups ? kSchedMaxGroups : s.max_groups;
   uint64_t want = (total + (uint64_t)s.slots - 1) / (uint64_t)s.slots;
   want = (want + gp - 1) / gp * gp;
-  const uint32_t wpp = (uint32_t)(want < gp ? gp : want > gp * (uint64_t)s.max_groups ? gp * s.max_groups : want);
-  uint32_t running = 0;
+  const uint32_t wpp = (uint32_t)(want < gp ? gp : want > gp * (uint64_t)maxg ? gp * maxg : want);
+  const uint32_t G = wpp / (uint32_t)gp;  // groups of a whole range
+  // row b: n ranges, the last of kl groups (n = 0 for an empty row past B)
+  auto row_ranges = [&](int b, uint32_t& n, uint32_t& kl) {
+    const uint32_t pages = b < s.B ? (uint32_t)((ctx_of(b) + s.self + 15) / 16) : 0u;
+    n = (pages + wpp - 1) / wpp;
+    kl = n ? (pages - (n - 1) * wpp + (uint32_t)gp - 1) / (uint32_t)gp : 0u;
+  };
+  uint32_t* first = lds_scratch;     // [NB]: the next free entry of each bucket
+  uint32_t* wcnt = lds_scratch + NB;  // [nw + 1][NB]: per wave, then the chunk's totals
+  // bucket sizes, then their first entries (bucket G first)
+  if (tid < NB) first[tid] = 0u;
+  __syncthreads();
+  for (int b = tid; b < s.B; b += nthr) {
+    uint32_t n, kl;
+    row_ranges(b, n, kl);
+    if (n) {
+      if (n > 1) atomicAdd(&first[G], n - 1);
+      atomicAdd(&first[kl], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t n_entries = 0;
+  if (tid == 0) {
+    for (int k = (int)G; k >= 1; --k) {
+      const uint32_t c = first[k];
+      first[k] = n_entries;
+      n_entries += c;
+    }
+  }
+  __syncthreads();
   for (int b0 = 0; b0 < s.B; b0 += nthr) {
     const int b = b0 + tid;
-    const int c = b < s.B ? s.ctx[b] : 0;
-    const uint32_t pages = b < s.B ? (uint32_t)((c + s.self + 15) / 16) : 0u;
-    const uint32_t n = (pages + wpp - 1) / wpp;
-    // inclusive scan of n over the workgroup: within waves, then the wave totals
-    uint32_t v = n;
+    uint32_t n, kl;
+    row_ranges(b, n, kl);
+    const int c = b < s.B ? ctx_of(b) : 0;
+    // bucket G: this row's whole ranges (and its last when that is whole), by an
+    // inclusive scan over the workgroup; the other buckets: one entry, ranked by ballots
+    const uint32_t nG = n ? n - 1 + (kl == G ? 1u : 0u) : 0u;
+    uint32_t v = nG;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t u = __shfl_up(v, o, 64);
       if (lane >= o) v += u;
     }
-    if (lane == 63) lds_scratch[wave] = v;
+    if (lane == 63) wcnt[wave * NB] = v;
+    uint32_t rank = 0;
+    for (int k = 1; k < (int)G; ++k) {
+      const unsigned long long m = __ballot(n != 0 && kl == (uint32_t)k);
+      if (lane == 0) wcnt[wave * NB + k] = (uint32_t)__popcll(m);
+      if (n != 0 && kl == (uint32_t)k) rank = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+    }
     __syncthreads();
-    if (tid == 0) {
+    if (tid < NB) {  // exclusive prefix over the waves per bucket (slot 0: bucket G)
       uint32_t acc = 0;
-      for (int w = 0; w < nthr / 64; ++w) {
-        const uint32_t t = lds_scratch[w];
-        lds_scratch[w] = acc;
+      for (int w = 0; w < nw; ++w) {
+        const uint32_t t = wcnt[w * NB + tid];
+        wcnt[w * NB + tid] = acc;
         acc += t;
       }
-      lds_scratch[nthr / 64] = acc;
+      wcnt[nw * NB + tid] = acc;
     }
     __syncthreads();
-    const uint32_t first = running + lds_scratch[wave] + v - n;
-    for (uint32_t r = 0; r < n; ++r) {
-      s.list[2 + 2 * (first + r)] = ((uint32_t)b << 16) | r;
-      s.list[3 + 2 * (first + r)] = (uint32_t)c;
+    if (n) {
+      const uint32_t fg = first[G] + wcnt[wave * NB] + v - nG;
+      for (uint32_t r = 0; r + 1 < n; ++r) {
+        s.list[2 + 2 * (fg + r)] = ((uint32_t)b << 16) | r;
+        s.list[3 + 2 * (fg + r)] = (uint32_t)c;
+      }
+      const uint32_t at = kl == G ? fg + n - 1 : first[kl] + wcnt[wave * NB + kl] + rank;
+      s.list[2 + 2 * at] = ((uint32_t)b << 16) | (n - 1);
+      s.list[3 + 2 * at] = (uint32_t)c;
     }
-    running += lds_scratch[nthr / 64];
+    __syncthreads();
+    if (tid == 0) {
+      first[G] += wcnt[nw * NB];
+      for (int k = 1; k < (int)G; ++k) first[k] += wcnt[nw * NB + k];
+    }
     __syncthreads();
   }
   if (tid == 0) {
-    s.list[0] = running;
+    s.list[0] = n_entries;
     s.list[1] = wpp;
   }
 }
