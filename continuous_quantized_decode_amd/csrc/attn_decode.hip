@@ -32,6 +32,8 @@
 
 namespace gr {
 
+static_assert(kAttnDecMaxGroups <= kSchedMaxGroups, "the work list's bound on groups per range");
+
 namespace {
 
 GR_DEV void st_agent(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }

@@ -82,7 +82,7 @@ hipError_t launch_attn_merge(const AttnParams& p, float* out, uint16_t* pack, in
 // KV head); each wave loads its pages all at once.
 constexpr int kAttnDecWaves = 4;
 constexpr int kAttnDecMaxWg = 512;  // workgroups per (row, KV head) one merge takes
-constexpr int kAttnDecMaxGroups = 8;  // groups of pages per workgroup
+constexpr int kAttnDecMaxGroups = 12;  // groups of pages per workgroup (8: long-context step 2 % slower)
 // pages per wave (a group's pages sit in registers at once; measured: f16 two pages
 // 21.2 us per Llama-3-8B layer against 22.8 us for four, whose refills wait a whole
 // group; q8_0 three pages, within the 168 VGPRs of three waves per SIMD, took the

@@ -222,7 +222,7 @@ struct RowSel {
 // only a schedule: a range's result and the merge order depend on (b, j) alone.  The
 // list: [0] its entries, [1] P, then the entries {(b << 16) | j, ctx[b]}; and the
 // attention's arrival counters cleared.
-constexpr int kSchedMaxGroups = 8;  // groups of pages per range at most
+constexpr int kSchedMaxGroups = 16;  // groups of pages per range at most
 struct AttnSched {
   const int32_t* ctx = nullptr;
   int B = 0, self = 1;
