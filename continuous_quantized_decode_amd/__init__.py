@@ -263,9 +263,12 @@ def gr_gemm_launch_shape(wtype: int, rows: int, k: int, b: int, epi: int = GEMM_
         name = f"gemm_tlw_kernel<{2 if nt == 2 else 1 if tl == 5 else 0}>"
     elif tl == 4:
         name = "gemm_kcw_kernel"
+    elif tl == 6:  # row-block kernel (gate/up pairs, 17 to 32 rows of Q4_K)
+        name = "gemm_rb_kernel"
     else:
         name = f"gemm_tl_kernel<{wtype}, {nt}," if tl else f"gemm_kernel<{wtype}, {nt}, {btn}, {maxt},"
     return {"tile_loop": tl in (1, 3, 5), "whole_tile": tl in (3, 5), "k_chunks": tl == 4, "many_rows": tl == 2,
+            "row_block": tl == 6,
             "nt": nt, "btn": btn,
             "maxt": maxt, "grid_threads": grid, "block_threads": block, "kernel": name}
 

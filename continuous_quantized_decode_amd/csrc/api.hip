@@ -5,6 +5,7 @@
 // that fails enqueues nothing.  The library keeps no per-row state: continuous
 // batching (Leone, intro; tinyllm, Status: continuous admission, variable-length
 // batched decode) is just a different B, block table and ctx_lens on the next call.
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -203,7 +204,8 @@ hipError_t gemm_run(const void* const* w, const int* types, const int* rows, int
 
 // The SwiGLU GEMM: gate and up (same type, F rows each) paired per 16-column tile.
 hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, int B, const Pack2& xin,
-                       const double* ss, float eps, PackOut out, double* zero_ptr, int zero_n, hipStream_t st) {
+                       const double* ss, float eps, PackOut out, double* zero_ptr, int zero_n, hipStream_t st,
+                       float* part = nullptr, size_t part_cap = 0, uint32_t* rb_cnt = nullptr, int rb_cnt_n = 0) {
   GemmArgs a{};
   a.w[0] = (const uint8_t*)wg;
   a.w[1] = (const uint8_t*)wu;
@@ -227,6 +229,13 @@ hipError_t gemm_swiglu(const void* wg, const void* wu, int wtype, int F, int K, 
   a.zero_ptr = zero_ptr;
   a.zero_n = zero_n;
   if (use_mm(wtype, B)) return launch_gemm_mm(wtype, (tiles + mm_group_tiles(true) - 1) / mm_group_tiles(true), a, st);
+  if (use_rb(wtype, K, B) && rb_fits(tiles, K, true, part_cap, rb_cnt_n)) {
+    a.part = part;
+    a.part_cap = part_cap;
+    a.rb_cnt = rb_cnt;
+    a.rb_cnt_n = rb_cnt_n;
+    return launch_gemm_rb(tiles, a, st);
+  }
   if (use_tile_loop(wtype, tiles, K, B) || use_tile_loop_whole(wtype, tiles, K, B)) {
     a.tl_groups = tiles;
     return launch_gemm_tl(wtype, 2, plan_gemm_tl(wtype, 2, tiles, K, B), a, st);
@@ -250,6 +259,8 @@ struct LayerBufs {
   float* wg_part;     // decode attention: workgroup partial states
   uint32_t* wg_cnt;   // decode attention: arrival counters [B][Hkv], zeroed by the input pack
   int n_cnt;
+  uint32_t* rb_cnt;   // row-block GEMM arrival counters, right after wg_cnt (zeroed with it)
+  int rb_cnt_n;
   uint32_t* sched;    // decode attention: the step's work list, built by the input pack
 };
 
@@ -276,9 +287,17 @@ LayerBufs carve_layer(Carver& c, const gr_layer_cfg* cfg, int B, const AttnPlan&
   L.rope = c.take<double>((size_t)B * cfg->head_dim * sizeof(double));
   L.qbuf = c.take<float>((size_t)B * qd * 4);
   L.part_cap = mm_part_floats(B, qd + 2 * kvd > cfg->hidden ? qd + 2 * kvd : cfg->hidden);
+  // the row-block kernel's partials and counters: the gate/up pairs (Q4_K at 17 to 32 rows)
+  const int gu = (cfg->ffn + 15) / 16;
+  L.rb_cnt_n = 0;
+  if (B > 16 && B <= 32) {
+    L.part_cap = std::max(L.part_cap, rb_part_floats(gu, cfg->hidden, true));
+    L.rb_cnt_n = gu;
+  }
   L.part = L.part_cap ? c.take<float>(L.part_cap * 4) : nullptr;
   L.n_cnt = B * cfg->n_kv_heads;
-  L.wg_cnt = c.take<uint32_t>((size_t)L.n_cnt * 4);
+  L.wg_cnt = c.take<uint32_t>((size_t)(L.n_cnt + L.rb_cnt_n) * 4);
+  L.rb_cnt = L.wg_cnt + L.n_cnt;
   L.wg_part = c.take<float>(attn_dec_part_floats(B, cfg->n_q_heads, cfg->head_dim, ap.dec_wg_max > 1 ? ap.dec_wg_max : 1) * 4);
   L.sched = c.take<uint32_t>(attn_sched_words(B, ap.dec_wg_max > 1 ? ap.dec_wg_max : 1) * 4);
   return L;
@@ -383,7 +402,15 @@ AttnSched attn_sched(const LayerBufs& L, const int32_t* ctx, int B, const AttnPl
   z.max_groups = kAttnDecMaxGroups;
   z.list = L.sched;
   z.cnt = L.wg_cnt;
-  z.n_cnt = L.n_cnt;
+  z.n_cnt = L.n_cnt + L.rb_cnt_n;
+  return z;
+}
+
+// Steps without a decode work list: the input pack clears the arrival counters only.
+AttnSched counters_only(const LayerBufs& L) {
+  AttnSched z;
+  z.cnt = L.wg_cnt;
+  z.n_cnt = L.n_cnt + L.rb_cnt_n;
   return z;
 }
 
@@ -525,7 +552,8 @@ gr_status run_layer(const gr_layer_cfg* c, const gr_layer_weights* w, void* k_pa
   //    attention-norm accumulator for step 6
   s = probed(probe, GR_STAGE_GATE_UP, st, [&] {
     return check_launch(gemm_swiglu(w->w_gate, w->w_up, w->tgate, F, H, B, L.xp, L.ss_ffn, c->rms_eps,
-                                    L.ap.of(w->tdown), L.ss_attn, ss_slots(B) * B, st));
+                                    L.ap.of(w->tdown), L.ss_attn, ss_slots(B) * B, st, L.part, L.part_cap, L.rb_cnt,
+                                    L.rb_cnt_n));
   });
   if (s != GR_OK) return s;
   // 6. x += W_down a; pack x * next_gain for the next consumer
@@ -641,7 +669,18 @@ gr_status gr_gemm_launch_shape(int wtype, int rows, int K, int B, int epi, int* 
   if (mm_required(B) && !mm_supported(wtype)) return GR_ERR_DTYPE;
   const int tiles = (rows + 15) / 16;
   const bool pair = epi == 2;
-  // the choices gemm_run and gemm_swiglu make
+  // the choices gemm_run and gemm_swiglu make (given the workspace the layer and the
+  // standalone GEMM provide)
+  if (pair && !use_mm(wtype, B) && use_rb(wtype, K, B)) {  // row-block kernel (gate/up pairs)
+    const int nkr = rb_ranges(K / kQK), W = K / kQK / nkr;
+    *tile_loop = 6;
+    *nt = 2;
+    *btn = 4;
+    *maxt = 512;
+    *block_threads = W * 64;
+    *grid_threads = rb_grid(K / kQK) * W * 64;
+    return GR_OK;
+  }
   if ((pair || epi == 0) && !use_mm(wtype, B) &&
       (use_tile_loop(wtype, tiles, K, B) || use_tile_loop_whole(wtype, tiles, K, B))) {
     const TlPlan tp = plan_gemm_tl(wtype, pair ? 2 : 1, tiles, K, B);
@@ -1072,7 +1111,7 @@ static gr_status decode_stack_impl(const gr_layer_cfg* c, const gr_layer_weights
   if (n_layers > 0) {
     s = run_input_pack(x, rows, c->hidden, weights[0].attn_norm, qkv_kinds(&weights[0]), L.xp, L.ss_attn, st, probe,
                        rope_table(c, ctx, L, T, rm.pos), RowSel{},
-                       rm.fused() ? attn_sched(L, ctx, rows, apl) : AttnSched{});
+                       rm.fused() ? attn_sched(L, ctx, rows, apl) : counters_only(L));
   } else if (head_w) {
     Kinds k;
     k.add(head_wtype);

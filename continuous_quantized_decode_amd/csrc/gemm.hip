@@ -1402,6 +1402,276 @@ __global__ __launch_bounds__(1024) void gemm_tlw_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
+// Row-block kernel: the Q4_K gate/up pairs (SwiGLU) at 17 to 32 rows (four activation
+// tiles: a 32-row decode step, a four-token verification step).  The split-K kernel's
+// waves read every row's activation fragments from L2 for each weight tile, which at 32
+// rows is 14 times the tile's own bytes.  Here each wave holds the fragments of the four
+// activation tiles for
+// one super-block in registers (128 VGPRs, two waves per SIMD) for the whole launch, so a
+// workgroup of W waves covers a K range of W super-blocks and nkr = K / 256 / W
+// workgroups cover K.  Weight tiles stream as in the whole-tile kernel: the 16 rows of
+// the range, loaded together by the waves (gemm_addr.h: wt_src_rows) into a three-slot
+// LDS ring, two in flight; each expanded weight fragment feeds the four activation
+// tiles' MFMAs.  Per pair the waves' sums meet in LDS as the range's partial sums, which
+// go to memory (agent scope) after the loop.  Then a workgroup counts its arrival on each
+// of its pairs (one agent-scope counter per pair, zero between launches) and, where it
+// arrives last, adds the nkr partials in range order (so the result does not depend on
+// which range came last), applies the SwiGLU epilogue and resets the counter.  With one
+// range (K of at most 8 super-blocks) the epilogue runs straight from LDS.  Measured at
+// Qwen3-8B (32 rows, 768 pairs, K = 4096 in two ranges): 46 us against the split-K
+// kernel's 49 us; it is bound by its math (41 us with the weight loads removed: 68 MFMAs
+// and about 350 other vector instructions per wave and tile at two waves per SIMD), so
+// for QKV and Wo (two or three tiles per workgroup, whose prologue loads 256 KB of
+// activation fragments) it was slower (20.0 and 18.7 us against 18.6 and 14.0).
+// Agent-scope (device-wide) store and load: past the per-XCD L2 (the partial sums of
+// one tile are written and read on different XCDs).
+GR_DEV void gst_agent(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+GR_DEV float gld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kRbBT = 4;          // activation tiles
+constexpr int kRbSlots = 3;       // ring slots: two tiles in flight while one is computed
+constexpr int kRbMaxWaves = 8;    // super-blocks per range (128 activation VGPRs per wave)
+constexpr int kRbMaxRanges = 8;
+constexpr int kRbMaxGroups = 64;  // tile groups per workgroup
+constexpr int kRbElems = kRbBT * 128;  // outputs of one tile: 16 columns x 32 rows
+
+int rb_ranges(int nsb) {
+  for (int nkr = (nsb + kRbMaxWaves - 1) / kRbMaxWaves; nkr <= nsb / 4 && nkr <= kRbMaxRanges; ++nkr)
+    if (nkr >= 1 && nsb % nkr == 0) return nkr;
+  return 0;
+}
+// reduction buffers: [2 (pr & 1)][2 (gate, up)][W][BT][128] floats, then (several ranges)
+// the workgroup's partial sums [ngm][SPG][kRbElems] until they are stored at the end
+inline size_t rb_lds_bytes(int W, int ngm, int spg) {
+  return (size_t)kRbSlots * addr::wt_slot_bytes(W) + (size_t)4 * W * kRbBT * 128 * sizeof(float) +
+         (size_t)ngm * spg * kRbElems * sizeof(float);
+}
+constexpr size_t kRbStaticLds = kSsCap * sizeof(double) + kRbMaxGroups * sizeof(uint32_t);
+
+template <int NK>
+GR_DEV float rb_sum(const float* p, size_t stride) {
+  float v[NK];
+#pragma unroll
+  for (int q = 0; q < NK; ++q) v[q] = gld_agent(p + (size_t)q * stride);
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < NK; ++q) s += v[q];
+  return s;
+}
+// the nk partials p[0], p[stride], ... added in order (all loads issued at once)
+GR_DEV float rb_sum_n(const float* p, size_t stride, int nk) {
+  switch (nk) {
+    case 1: return rb_sum<1>(p, stride);
+    case 2: return rb_sum<2>(p, stride);
+    case 3: return rb_sum<3>(p, stride);
+    case 4: return rb_sum<4>(p, stride);
+    case 5: return rb_sum<5>(p, stride);
+    case 6: return rb_sum<6>(p, stride);
+    case 7: return rb_sum<7>(p, stride);
+    default: return rb_sum<8>(p, stride);
+  }
+}
+
+// Grid: nkr workgroups per slot, workgroup i takes range i % nkr and the (i / nkr)-th
+// share of the gate/up pairs.
+__global__ __launch_bounds__(kRbMaxWaves * 64) void gemm_rb_kernel(GemmArgs a) {
+  constexpr int SPG = 2;  // stages (tiles) per pair: gate, up
+  constexpr int BT = kRbBT, NE = kRbElems;
+  constexpr int KWI = addr::kWtInstr;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ double s_ss[kSsCap];         // the input rows' RMSNorm partial sums
+  __shared__ uint32_t s_last[kRbMaxGroups];  // this workgroup arrived last on group g0 + t
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int W = nthr >> 6;  // super-blocks of the range: wave w computes super-block kr W + w
+  const int n = lane & 15;
+  const int nkr = a.nsb / W;
+  const int kr = (int)blockIdx.x % nkr;
+  const int U = addr::wt_units(W);
+  const u32 slot_bytes = addr::wt_slot_bytes(W);
+  const int kwi = (addr::wt_instrs(W) + W - 1) / W;  // loads per wave and tile (<= KWI)
+  lds_u8* const slots = (lds_u8*)lds;
+  // reduction buffers red[buf][wave][b][128]: buf = 2 (pr & 1) + t, tile t (gate / up, or
+  // the single tile) of group pr, so a group's sums never overwrite ones still being read
+  float* const red = (float*)(lds + kRbSlots * (size_t)slot_bytes);
+  auto red_buf = [&](int pr, int t) { return red + (size_t)(2 * (pr & 1) + t) * W * BT * 128; };
+  float* const outb = red + (size_t)4 * W * BT * 128;  // [ng][SPG][NE]: this range's partials
+
+  if (a.zero_ptr && blockIdx.x == 0)
+    for (int i = tid; i < a.zero_n; i += nthr) a.zero_ptr[i] = 0.0;
+
+  const int G = a.tl_groups, per = (int)gridDim.x / nkr, wi = (int)blockIdx.x / nkr;
+  const int g0 = (int)(((long long)wi * G) / per);
+  const int ng = (int)(((long long)(wi + 1) * G) / per) - g0;
+  if (ng <= 0) return;  // workgroup-uniform, before any barrier
+  const int nq = SPG * ng;
+  const int sbr = kr * W;  // the range's first super-block
+  const u32 rbytes = (u32)a.row_bytes;
+  u32 voff[KWI];
+#pragma unroll
+  for (int k = 0; k < KWI; ++k) voff[k] = addr::wt_src_rows(addr::wt_instr(wave, W, k, W), lane, W, rbytes);
+  auto issue = [&](int q) {  // stage q: tile (gate q even, up q odd) of pair g0 + q / 2
+    const int gi = g0 + q / SPG;
+    const uint8_t* base = ((q & 1) ? a.w[1] : a.w[0]) + (size_t)gi * 16 * a.row_bytes + (size_t)sbr * kQ4KBytes;
+    const int nvalid = min(16, a.seg_rows[0] - gi * 16);
+    // the descriptor ends with the last valid row's range: the rows past it read 0
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)base, 0, (int)((u32)(nvalid - 1) * rbytes + 16u * (u32)U), kBufDword3);
+    lds_u8* slot = slots + (q % kRbSlots) * slot_bytes;
+#pragma unroll
+    for (int k = 0; k < KWI; ++k)
+      if (k < kwi) issue_wt(rs, slot + 1024u * (u32)addr::wt_instr(wave, W, k, W), voff[k]);
+  };
+  auto wait_younger = [&](int y) { wait_vmcnt_n(y * kwi); };
+
+  // prologue: the RMSNorm partial sums, this wave's activation fragments, then stages 0, 1
+  const int n_ss = a.ss ? a.ss_slots * a.B : 0;  // <= kSsCap <= nthr
+  const double ssp = tid < n_ss ? a.ss[tid] : 0.0;
+  const size_t tile_frags = (size_t)a.nsb * 8;
+  u32x4 act[BT][8];
+#pragma unroll
+  for (int b = 0; b < BT; ++b)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      act[b][j] = ((const u32x4*)a.xpack)[((size_t)b * tile_frags + (size_t)(sbr + wave) * 8 + j) * 64 + lane];
+  const int pro = min(kRbSlots - 1, nq);
+  for (int q = 0; q < pro; ++q) issue(q);
+  wait_younger(pro);  // the loads above (older than the stages) have landed
+  if (tid < n_ss) s_ss[tid] = ssp;  // published by step 0's barrier
+  // sub-block sums of the wave's super-block per activation tile, through the wave's part
+  // of the reduction buffer (first written after step 0's barrier)
+  u32x2 aS[BT];
+  {
+    const u32x4 ones = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {
+      float* scr = red + ((size_t)wave * BT + b) * 128;  // [j][row], each written and read once
+      f32x4 sj[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sj[j] = mfma_bf16_k32(act[b][j], ones, z4);
+      if (m == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) scr[j * 16 + 4 * g + t] = sj[j][t];
+      }
+      asm volatile("" ::: "memory");  // the reads below see the other lanes' writes
+      u16 h0, l0, h1, l1;
+      split_bf16(scr[(2 * g) * 16 + m], h0, l0);
+      split_bf16(scr[(2 * g + 1) * 16 + m], h1, l1);
+      aS[b] = u32x2{(u32)h0 | ((u32)l0 << 16), (u32)h1 | ((u32)l1 << 16)};
+    }
+  }
+  const int c0 = [&] {
+    const int c = 9 * wave + addr::wt_rot(n, U);
+    return c >= U ? c - U : c;
+  }();
+
+  // The SwiGLU epilogue of pair gi on the finished sums of element e (gate v, up v2).
+  auto finish = [&](int gi, int e, bool in, float v, float v2) {
+    const int rem = e & 127, lp = rem >> 1;
+    const int brow = 8 * (e >> 7) + 2 * (lp >> 4) + (rem & 1), col = gi * 16 + (lp & 15);
+    if (in && brow < a.B && col < a.seg_rows[0]) {
+      float rs = 1.0f;  // 1 / rms of the input row
+      if (n_ss) {
+        double ssv = 0.0;
+        for (int s = 0; s < a.ss_slots; ++s) ssv += s_ss[s * a.B + brow];
+        rs = 1.0f / sqrtf((float)ssv * a.inv_k + a.eps);
+      }
+      const float gv = rs * v, uv = rs * v2;
+      actpack_put(a.pack_out, a.pack_kind, a.pack_nslices, brow, col, gv / (1.0f + expf(-gv)) * uv);
+    }
+  };
+  // group pr's sums from the reduction buffer: kept in LDS as this range's partials (stored
+  // after the loop, so that no stage's wait waits for them), or (one range) finished at once
+  auto publish = [&](int pr) {
+    const int gi = g0 + pr;
+    for (int e0 = 0; e0 < NE; e0 += nthr) {
+      const int e = e0 + tid;
+      const bool in = e < NE;
+      const int ee = in ? e : 0;
+      const int b = ee >> 7, rem = ee & 127;
+      float v[SPG];
+#pragma unroll
+      for (int t = 0; t < SPG; ++t) {
+        const float* r0 = red_buf(pr, t) + (size_t)b * 128 + rem;  // [wave][b][128]
+        float s = 0.f;
+        for (int w = 0; w < W; ++w) s += r0[(size_t)w * BT * 128];
+        v[t] = s;
+      }
+      if (nkr == 1) {
+        finish(gi, ee, in, v[0], v[1]);
+      } else if (in) {
+#pragma unroll
+        for (int t = 0; t < SPG; ++t) outb[((size_t)pr * SPG + t) * NE + e] = v[t];
+      }
+    }
+  };
+
+  float acc[BT][4];  // one tile's sums: stored to its reduction buffer after its step
+#pragma unroll
+  for (int b = 0; b < BT; ++b)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[b][k] = 0.f;
+
+  for (int pr = 0; pr < ng; ++pr) {
+#pragma unroll
+    for (int t = 0; t < SPG; ++t) {
+      const int q = SPG * pr + t;
+      wait_younger(min(kRbSlots - 2, nq - 1 - q));  // stage q has landed
+      lds_barrier();
+      if (t == 0 && pr > 0) publish(pr - 1);
+      if (q + kRbSlots - 1 < nq) issue(q + kRbSlots - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const lds_u8* rowp = slots + (q % kRbSlots) * slot_bytes + (size_t)n * U * 16;
+      q4_step_tlw<BT>(rowp, c0, U, act, aS, lane, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      // the tile's partial sums: red_buf(pr, t)[wave][b][lane * 2 + k]
+#pragma unroll
+      for (int b = 0; b < BT; ++b) {
+        float* r = red_buf(pr, t) + ((size_t)wave * BT + b) * 128 + lane * 2;
+        r[0] = acc[b][0] + acc[b][1];
+        r[1] = acc[b][2] + acc[b][3];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[b][k] = 0.f;
+      }
+    }
+  }
+  lds_barrier();
+  publish(ng - 1);
+  if (nkr == 1) return;
+
+  // ---- the partials to memory, all at once; they are stored before any arrival is
+  // counted, and the last arriver on a group adds its ranges' partials
+  __syncthreads();
+  for (int i = tid; i < ng * SPG * NE; i += nthr)
+    gst_agent(a.part + ((size_t)kr * G + g0) * SPG * NE + i, outb[i]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid < ng)
+    s_last[tid] = __hip_atomic_fetch_add(a.rb_cnt + g0 + tid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (uint32_t)(nkr - 1);
+  __syncthreads();
+  for (int t = 0; t < ng; ++t) {
+    if (!s_last[t]) continue;  // workgroup-uniform
+    const int gi = g0 + t;
+    const size_t stride = (size_t)G * SPG * NE;  // from one range's partial to the next
+    for (int e0 = 0; e0 < NE; e0 += nthr) {
+      const int e = e0 + tid;
+      const bool in = e < NE;
+      const int ee = in ? e : 0;
+      const float* p0 = a.part + ((size_t)gi * SPG) * NE + ee;
+      finish(gi, ee, in, rb_sum_n(p0, stride, nkr), rb_sum_n(p0 + NE, stride, nkr));
+    }
+    if (tid == 0) __hip_atomic_store(a.rb_cnt + gi, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // K-chunk staging: the Q6_K residual GEMM (down) at one activation tile, rows of a
 // multiple of 16 bytes.  One 16-row tile per workgroup, C waves; stage c is super-blocks
 // [C c, C c + C) of the tile's 16 rows (gemm_addr.h: kc_*), loaded by all waves
@@ -2206,6 +2476,65 @@ hipError_t launch_gemm_mm(int wtype, int groups, GemmArgs a, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess || nsplit <= 1) return e;
   launch_kernel(gemm_mm_finish_kernel, dim3((a.ldp + 255) / 256, a.B), dim3(256), 0, st, a, nsplit);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// row-block plan and launch
+
+// Which GEMMs take it: Q4_K gate/up pairs, 17 to 32 rows, K split into ranges of 4 to 8
+// super-blocks.
+bool use_rb(int wtype, int K, int B) {
+  return wtype == 12 && B > 16 && B <= 32 && K % kQK == 0 && rb_ranges(K / kQK) > 0;
+}
+int rb_slots(int nsb) {
+  const int nkr = rb_ranges(nsb);
+  return nkr > 0 ? variants().cus / nkr : 0;
+}
+int rb_grid(int nsb) { return rb_slots(nsb) * rb_ranges(nsb); }
+size_t rb_part_floats(int groups, int K, bool pair) {
+  const int nkr = rb_ranges(K / kQK);
+  return nkr > 1 ? (size_t)nkr * groups * (pair ? 2 : 1) * kRbElems : 0;
+}
+// groups of the workgroup with the most, and the dynamic LDS of a launch
+int rb_ngm(int groups, int nsb) {
+  const int per = rb_slots(nsb);
+  return per > 0 ? (groups + per - 1) / per : 0;
+}
+size_t rb_lds(int groups, int nsb, bool pair) {
+  const int nkr = rb_ranges(nsb);
+  return rb_lds_bytes(nsb / nkr, nkr > 1 ? rb_ngm(groups, nsb) : 0, pair ? 2 : 1);
+}
+bool rb_fits(int groups, int K, bool pair, size_t part_cap, int cnt_n) {
+  const int nsb = K / kQK, nkr = rb_ranges(nsb);
+  if (nkr < 1) return false;
+  const int ngm = rb_ngm(groups, nsb);
+  if (ngm < 1 || ngm > kRbMaxGroups || rb_lds(groups, nsb, pair) + kRbStaticLds > (size_t)kGemmLds) return false;
+  return nkr == 1 || (rb_part_floats(groups, K, pair) <= part_cap && groups <= cnt_n);
+}
+
+hipError_t launch_gemm_rb(int groups, GemmArgs a, hipStream_t st) {
+  if (groups <= 0) return hipSuccess;
+  const int nkr = rb_ranges(a.nsb);
+  const bool pair = true;
+  if (nkr < 1 || a.B > 32 || a.B < 1 || a.epi != kEpiSwiGLU || a.nseg != 2 || a.seg_rows[0] > groups * 16 ||
+      (a.ss && (a.ss_slots * a.B > kSsCap || a.ss_slots < 1)) ||
+      !rb_fits(groups, a.nsb * kQK, pair, a.part_cap, a.rb_cnt_n) || (nkr > 1 && (!a.part || !a.rb_cnt)))
+    return hipErrorInvalidValue;
+  const int W = a.nsb / nkr;
+  if (W < 4 || W > kRbMaxWaves || addr::kWtInstr * W < addr::wt_instrs(W)) return hipErrorInvalidValue;
+  static const bool lds_set = [] {
+    (void)hipFuncSetAttribute((const void*)gemm_rb_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kGemmLds - (int)kRbStaticLds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)lds_set;
+  a.tl_groups = groups;
+  const void* fn = (const void*)gemm_rb_kernel;
+  void* kargs[] = {&a};
+  const hipError_t e =
+      launch_fn(fn, dim3(rb_grid(a.nsb)), dim3(W * 64), rb_lds(groups, a.nsb, pair), st, kargs);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace gr

@@ -129,6 +129,18 @@ GR_HD uint32_t wt_src(int i, int lane, int nsb) {
   if (c < 0) c += U;
   return 16u * ((uint32_t)r * (uint32_t)U + (uint32_t)c);
 }
+// The same staging for a K range of nsb super-blocks of the tile's 16 rows when the rows
+// are not consecutive in memory: byte offset, from row 0's first byte of the range, of the
+// unit lane `lane` of instruction i loads (row r at r row_bytes); LDS layout as above.
+GR_HD uint32_t wt_src_rows(int i, int lane, int nsb, uint32_t row_bytes) {
+  const int U = wt_units(nsb);
+  int L = 64 * i + lane;
+  if (L > 16 * U - 1) L = 16 * U - 1;
+  const int r = L / U;
+  int c = L - r * U - wt_rot(r, U);
+  if (c < 0) c += U;
+  return (uint32_t)r * row_bytes + 16u * (uint32_t)c;
+}
 GR_HD uint32_t wt_lds(int i, int lane) { return 1024u * (uint32_t)i + 16u * (uint32_t)lane; }
 // LDS byte holding byte b (< 16 U) of row r
 GR_HD uint32_t wt_lds_byte(int r, uint32_t b, int nsb) {

@@ -91,6 +91,10 @@ struct GemmArgs {
   float* part;
   size_t part_cap;      // floats available at part
   int ldp, pcol0;
+  // row-block kernel (17 to 32 rows) over several K ranges: the ranges' partial sums at
+  // part, and one arrival counter per gate/up pair (zero between launches), rb_cnt_n of them
+  uint32_t* rb_cnt;
+  int rb_cnt_n;
 };
 
 // The RMSNorm statistic (per-row sum of squares) that a GEMM epilogue applies is kept
@@ -137,6 +141,15 @@ bool use_kcw(int wtype, int K, int B, int nmat);  // gemm_kcw_kernel's sizes (on
 int kcw_waves(int nsb);
 hipError_t launch_gemm_kcw(int tiles, GemmArgs a, hipStream_t st);
 inline int tl_btn(int B) { return B <= 8 ? 1 : 2; }  // activation tiles of the tile loop
+// The row-block GEMM (gemm_rb_kernel): the Q4_K gate/up pairs at 17 to 32 rows, K in
+// ranges of 4 to 8 super-blocks (rb_ranges of them, 0: not this kernel).  rb_fits:
+// whether the partial-sum floats and counters given suffice for `groups` pairs.
+bool use_rb(int wtype, int K, int B);
+int rb_ranges(int nsb);
+size_t rb_part_floats(int groups, int K, bool pair);
+bool rb_fits(int groups, int K, bool pair, size_t part_cap, int cnt_n);
+int rb_grid(int nsb);  // workgroups of a launch
+hipError_t launch_gemm_rb(int groups, GemmArgs a, hipStream_t st);
 hipError_t launch_gemm_tl(int wtype, int nt, const TlPlan& pl, GemmArgs a, hipStream_t st);
 hipError_t launch_gemm(int wtype, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);
 

@@ -13,17 +13,21 @@ namespace gr {
 constexpr int kPackThreads = 1024;
 
 // grid: 8 * actpack_tiles(B) blocks, one per (padded) batch row, and with a work list to
-// build one more block that builds it; each thread takes four consecutive columns per
-// pass (K % 256 == 0, x rows 16-byte aligned).
+// build or counters to clear one more block that does that; each thread takes four
+// consecutive columns per pass (K % 256 == 0, x rows 16-byte aligned).
 __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const float* __restrict__ x, int ldx, int B, int K,
                                                                  const float* __restrict__ gain, PackOut o1,
                                                                  PackOut o2, double* ss_out, RopeTable rope,
                                                                  RowSel sel, AttnSched sched) {
   const int b = blockIdx.x, tid = threadIdx.x;
-  if (sched.list && b == (int)gridDim.x - 1) {  // the extra last block: the attention's work list
-    __shared__ uint32_t sched_scan[kSchedScratchWords];
-    static_assert(kPackThreads <= 1024, "the work list's scratch");
-    build_attn_sched(sched, sched_scan);
+  if ((sched.list || sched.cnt) && b == (int)gridDim.x - 1) {  // the extra last block
+    if (sched.list) {  // the attention's work list (and the arrival counters cleared)
+      __shared__ uint32_t sched_scan[kSchedScratchWords];
+      static_assert(kPackThreads <= 1024, "the work list's scratch");
+      build_attn_sched(sched, sched_scan);
+    } else {
+      for (int i = tid; i < sched.n_cnt; i += kPackThreads) sched.cnt[i] = 0u;
+    }
     return;
   }
   const int src = (sel.idx && b < B) ? min(max(sel.idx[b], 0), sel.src_rows - 1) : b;
@@ -74,8 +78,9 @@ hipError_t launch_pack_rows(const float* x, int ldx, int B, int K, const float* 
   if (rope.out && (rope.half_d <= 0 || rope.half_d > kPackThreads || (!rope.ctx && !rope.row_pos)))
     return hipErrorInvalidValue;
   if (sel.idx && sel.src_rows <= 0) return hipErrorInvalidValue;
-  launch_kernel(pack_rows_kernel, dim3(8 * actpack_tiles(B) + (sched.list ? 1 : 0)), dim3(kPackThreads), 0, st, x, ldx,
-                B, K, gain, o1, o2, ss_out, rope, sel, sched);
+  const int blocks = 8 * actpack_tiles(B) + (sched.list || sched.cnt ? 1 : 0);
+  launch_kernel(pack_rows_kernel, dim3(blocks), dim3(kPackThreads), 0, st, x, ldx, B, K, gain, o1, o2, ss_out, rope,
+                sel, sched);
   return hipGetLastError();
 }
 

@@ -102,6 +102,16 @@ def test_gemm_launch_shape_names_the_kernel():
     assert not gr.gr_gemm_launch_shape(q4, 16384, 1536, 16, gr.GEMM_EPI_STORE)["tile_loop"]
     assert not gr.gr_gemm_launch_shape(q6, 128256, 4096, 17, gr.GEMM_EPI_STORE)["tile_loop"]
     assert not gr.gr_gemm_launch_shape(q6, 128256, 4352, 8, gr.GEMM_EPI_STORE)["tile_loop"]
+    # 17 to 32 rows: the Q4_K gate/up pairs on the row-block kernel (K = 4096: two ranges of
+    # eight super-blocks, eight waves, 128 workgroups per range), the plain stores not
+    rb = gr.gr_gemm_launch_shape(q4, 12288, 4096, 32, gr.GEMM_EPI_SWIGLU)
+    assert rb["row_block"] and rb["kernel"] == "gemm_rb_kernel" and rb["block_threads"] == 8 * 64
+    assert rb["grid_threads"] == 256 * 8 * 64
+    assert gr.gr_gemm_launch_shape(q4, 12288, 4096, 17, gr.GEMM_EPI_SWIGLU)["row_block"]
+    assert not gr.gr_gemm_launch_shape(q4, 12288, 4096, 16, gr.GEMM_EPI_SWIGLU)["row_block"]
+    assert not gr.gr_gemm_launch_shape(q4, 12288, 4096, 33, gr.GEMM_EPI_SWIGLU)["row_block"]
+    assert not gr.gr_gemm_launch_shape(q4, 6144, 4096, 32, gr.GEMM_EPI_STORE)["row_block"]
+    assert not gr.gr_gemm_launch_shape(q6, 12288, 4096, 32, gr.GEMM_EPI_SWIGLU)["row_block"]
     L = gr.lib()
     out = [ctypes.c_int() for _ in range(6)]
     assert L.gr_gemm_launch_shape(q4, 64, 256, 1, 3, *[ctypes.byref(o) for o in out]) == -2

@@ -316,3 +316,80 @@ def test_k_chunk_staging_in_bounds_and_conflict_free():
         out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
         print(out.stdout)
         assert out.returncode == 0, out.stdout
+
+
+KRANGE_PROGRAM = r"""
+#include <cstdio>
+#include <vector>
+#include "gemm_addr.h"
+using namespace gr::addr;
+
+static int fails = 0;
+#define CHECK(c, ...) do { if (!(c)) { if (fails++ < 20) { std::printf(__VA_ARGS__); std::printf("\n"); } } } while (0)
+
+// Whole-tile staging of K ranges (Q4_K): the matrix's rows are nsb super-blocks long, a
+// range is W = nsb / nkr of them; every wave's loads of every range, every lane.
+int main() {
+  const int rows[] = {1, 15, 16, 17, 33, 48};
+  const int shapes[][2] = {{4, 1}, {5, 1}, {8, 1}, {8, 2}, {12, 2}, {16, 2}, {16, 4}, {20, 4}, {24, 3}, {32, 4}, {56, 7}};
+  for (const auto& sh : shapes) {
+    const int nsb = sh[0], nkr = sh[1], W = nsb / nkr;
+    const int U = wt_units(W), kwi = (wt_instrs(W) + W - 1) / W;
+    const uint32_t row_bytes = 144u * nsb, slot = wt_slot_bytes(W), span = 16u * (uint32_t)U;
+    CHECK(kwi <= kWtInstr, "W %d: %d loads per wave", W, kwi);
+    for (int N : rows) {
+      const uint64_t total = (uint64_t)N * row_bytes;  // the matrix starts at 0
+      for (int row0 = 0; row0 < N; row0 += 16)
+        for (int kr = 0; kr < nkr; ++kr) {
+          const int nvalid = N - row0 < 16 ? N - row0 : 16;
+          const uint64_t base = (uint64_t)row0 * row_bytes + 144u * (uint64_t)(kr * W);
+          // the descriptor ends with the range of the last valid row: rows past the matrix read 0
+          const uint64_t desc = (uint64_t)(nvalid - 1) * row_bytes + span;
+          std::vector<int64_t> held(slot, -1);
+          for (int w = 0; w < W; ++w)
+            for (int k = 0; k < kwi; ++k) {
+              const int i = wt_instr(w, W, k, W);
+              for (int lane = 0; lane < 64; ++lane) {
+                const uint32_t off = wt_src_rows(i, lane, W, row_bytes), lds = wt_lds(i, lane);
+                CHECK(off % 16 == 0, "unaligned unit");
+                CHECK(off % row_bytes + 16 <= span && off / row_bytes < 16, "nsb %d W %d: unit outside the range", nsb, W);
+                CHECK(lds + 16 <= slot, "W %d: LDS write past the slot", W);
+                CHECK(off >= desc || base + off + 16 <= total, "nsb %d N %d: in-descriptor unit past the matrix", nsb, N);
+                CHECK(off >= desc || (int)(off / row_bytes) < nvalid, "in-descriptor unit of a row past the matrix");
+                for (int b = 0; b < 16; ++b) {
+                  const int64_t v = off + b < desc ? (int64_t)(base + off + b) : -2;  // -2: reads as zero
+                  CHECK(held[lds + b] == -1 || held[lds + b] == v, "W %d: LDS byte %u loaded twice differently", W,
+                        lds + b);
+                  held[lds + b] = v;
+                }
+              }
+            }
+          for (int r = 0; r < nvalid; ++r)
+            for (uint32_t b = 0; b < span; ++b)
+              CHECK(held[wt_lds_byte(r, b, W)] == (int64_t)(base + (uint64_t)r * row_bytes + b),
+                    "nsb %d W %d N %d row0 %d kr %d row %d byte %u", nsb, W, N, row0, kr, r, b);
+        }
+    }
+  }
+  std::printf("%s (%d failures)\n", fails ? "FAIL" : "ok", fails);
+  return fails ? 1 : 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_k_range_staging_in_bounds():
+    """Whole-tile staging of a K range (the many-row-block kernel: a tile's 16 rows over
+    W super-blocks of a longer row): every wave's loads stay inside the range of the 16
+    rows and inside the LDS slot, units of rows past the matrix fall outside the buffer
+    descriptor (they read zeros), and every byte of every valid row's range lands where
+    the compute reads it."""
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "check_kr.cpp")
+        exe = os.path.join(d, "check_kr")
+        with open(src, "w") as f:
+            f.write(KRANGE_PROGRAM)
+        subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.dirname(HDR), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        print(out.stdout)
+        assert out.returncode == 0, out.stdout

@@ -101,6 +101,13 @@ GEMM_CASES = [
     (synth.W_Q6_K, 16, 256, 12288),
     (synth.W_Q6_K, 64, 128, 14336),
     (synth.W_Q4_K, 64, 256, 14336),
+    # 17 to 32 rows of Q4_K at K of two, four and seven ranges of the row-block kernel's
+    # (which takes only the gate/up pairs: the plain stores keep the split-K kernel)
+    (synth.W_Q4_K, 32, 6144, 4096),
+    (synth.W_Q4_K, 24, 1000, 4096),
+    (synth.W_Q4_K, 20, 4096, 3072),
+    (synth.W_Q4_K, 17, 2000, 5120),
+    (synth.W_Q4_K, 32, 300, 14336),
     # tile-loop kernel (at least two tile groups per CU, one batch tile, K <= 4096)
     (synth.W_Q4_K, 8, 8200, 4096),   # 513 tiles, the last ragged (whole-tile tile loop, two or three per workgroup)
     (synth.W_Q4_K, 7, 6144, 4096),   # the QKV shape: 384 tiles, one or two per workgroup
@@ -141,7 +148,7 @@ def test_gemm_matches_oracle(torch, gr, orc, wtype, b, n, k):
     rng = np.random.default_rng(1000 + b * 7 + n + k)
     w = synth.weight(rng, wtype, n, k)
     x = rng.standard_normal((b, k), dtype=np.float32)
-    say("gemm", wtype, b, n, k)
+    say("gemm", wtype, b, n, k, gr.gr_gemm_launch_shape(wtype, n, k, b)["kernel"])
     fn = getattr(gr, GEMM_FN[wtype])
     got = host(fn(dev(w, torch), dev(x, torch), n))
     want = orc.gemm(wtype, w, x, n, k)

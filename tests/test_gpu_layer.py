@@ -94,6 +94,14 @@ LAYER_CASES = [
     # update (wo), 16 query heads on 2 KV heads of 128
     dict(ctx=[60, 3, 250, 17, 0, 99], batch=6, hidden=4096, n_q_heads=16, n_kv_heads=2, head_dim=128, ffn=1024,
          kv_dtype=synth.KV_F16, wo=True),
+    # 17 to 32 rows of Q4_K: the gate/up pairs on the row-block kernel (rb), K = 4096 in two
+    # ranges, and at hidden 2048 in one (the epilogue straight from LDS); the other GEMMs
+    # on the split-K kernel
+    dict(ctx=[12, 0, 33, 64, 5, 17, 90, 2, 45, 9, 1, 60, 31, 16, 15, 200, 3, 8, 77, 50, 6, 140, 29, 11], batch=24,
+         hidden=4096, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn=1024, w_down=synth.W_Q4_K,
+         kv_dtype=synth.KV_Q8_0, qk_norm=True, rb=True),
+    dict(ctx=[(37 * i) % 301 for i in range(32)], batch=32, hidden=2048, n_q_heads=16, n_kv_heads=8, head_dim=128,
+         ffn=4096, w_down=synth.W_Q4_K, kv_dtype=synth.KV_F16, rb=True),
 ]
 
 
@@ -121,8 +129,13 @@ def test_tiny_layer_matches_oracle(torch, gr, orc, case):
     gu = spec.pop("gu", None)
     dn = spec.pop("dn", None)
     wo = spec.pop("wo", None)
+    rb = spec.pop("rb", None)
     wl = tiny(**spec)
     say("layer case", case, spec, ctx)
+    if rb:  # the gate/up launch this case exists to cover
+        sh = gr.gr_gemm_launch_shape(synth.W_Q4_K, wl.ffn, wl.hidden, len(ctx), gr.GEMM_EPI_SWIGLU)
+        say("  gate/up launch", sh["kernel"])
+        assert sh["row_block"]
     if gu is not None:
         # the gate/up kernel this case exists to cover (so the choice cannot drift unseen)
         sh = gr.gr_gemm_launch_shape(synth.layer_weights(wl, 0).tgate, wl.ffn, wl.hidden, len(ctx), gr.GEMM_EPI_SWIGLU)
