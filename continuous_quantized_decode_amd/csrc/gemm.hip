@@ -1599,8 +1599,14 @@ __global__ __launch_bounds__(kRbMaxWaves * 64) void gemm_rb_kernel(GemmArgs a) {
 #pragma unroll
       for (int t = 0; t < SPG; ++t) {
         const float* r0 = red_buf(pr, t) + (size_t)b * 128 + rem;  // [wave][b][128]
+        // the W waves' sums in wave order, all eight reads issued at once (a loop over
+        // the run-time W waited for each read before the next)
+        float x[kRbMaxWaves];
+#pragma unroll
+        for (int w = 0; w < kRbMaxWaves; ++w) x[w] = r0[(size_t)min(w, W - 1) * BT * 128];
         float s = 0.f;
-        for (int w = 0; w < W; ++w) s += r0[(size_t)w * BT * 128];
+#pragma unroll
+        for (int w = 0; w < kRbMaxWaves; ++w) s += w < W ? x[w] : 0.f;
         v[t] = s;
       }
       if (nkr == 1) {
