@@ -741,9 +741,22 @@ __global__ __launch_bounds__(MAXT) void gemm_kernel(GemmArgs a) {
     const Elem m = elem(e);
     float v = 0.f, v2 = 0.f;
     if (m.in) {
-      for (int w = 0; w < nwaves; ++w) {
-        v += red[(((size_t)w * NT + m.t) * BTN + m.bt) * 128 + (m.rem % 128)];
-        if (a.epi == kEpiSwiGLU) v2 += red[(((size_t)w * NT + 1) * BTN + m.bt) * 128 + (m.rem % 128)];
+      // the waves' sums in wave order, each tile's reads issued at once (a loop over the
+      // run-time wave count waited for each read before the next)
+      constexpr int MW = MAXT / 64;
+      const size_t ws = (size_t)NT * BTN * 128;  // from one wave's sums to the next
+      float x[MW];
+      const float* r0 = red + ((size_t)m.t * BTN + m.bt) * 128 + (m.rem % 128);
+#pragma unroll
+      for (int w = 0; w < MW; ++w) x[w] = r0[(size_t)min(w, nwaves - 1) * ws];
+#pragma unroll
+      for (int w = 0; w < MW; ++w) v += w < nwaves ? x[w] : 0.f;
+      if (a.epi == kEpiSwiGLU) {
+        const float* r1 = red + ((size_t)1 * BTN + m.bt) * 128 + (m.rem % 128);
+#pragma unroll
+        for (int w = 0; w < MW; ++w) x[w] = r1[(size_t)min(w, nwaves - 1) * ws];
+#pragma unroll
+        for (int w = 0; w < MW; ++w) v2 += w < nwaves ? x[w] : 0.f;
       }
     }
     double ssv = 0.0;
@@ -1146,9 +1159,22 @@ __global__ __launch_bounds__(512) void gemm_tl_kernel(GemmArgs a) {
     lds_barrier();
     if (e < n_elem) {
       float v = 0.f, v2 = 0.f;
-      for (int w = 0; w < nwaves; ++w) {
-        v += rb[(((size_t)w * NT + e_t) * BTN + e_b) * 128 + e_rem];
-        if (a.epi == kEpiSwiGLU) v2 += rb[(((size_t)w * NT + 1) * BTN + e_b) * 128 + e_rem];
+      {  // the waves' sums in wave order, each tile's reads issued at once
+        constexpr int MW = 512 / 64;
+        const size_t ws = (size_t)NT * BTN * 128;
+        float x[MW];
+        const float* r0 = rb + ((size_t)e_t * BTN + e_b) * 128 + e_rem;
+#pragma unroll
+        for (int w = 0; w < MW; ++w) x[w] = r0[(size_t)min(w, nwaves - 1) * ws];
+#pragma unroll
+        for (int w = 0; w < MW; ++w) v += w < nwaves ? x[w] : 0.f;
+        if (a.epi == kEpiSwiGLU) {
+          const float* r1 = rb + ((size_t)1 * BTN + e_b) * 128 + e_rem;
+#pragma unroll
+          for (int w = 0; w < MW; ++w) x[w] = r1[(size_t)min(w, nwaves - 1) * ws];
+#pragma unroll
+          for (int w = 0; w < MW; ++w) v2 += w < nwaves ? x[w] : 0.f;
+        }
       }
       const int lt = a.epi == kEpiSwiGLU ? local : local * NT + e_t;
       const bool live = e_brow < a.B && lt * 16 + e_nn < rows_of(seg);
